@@ -1,0 +1,318 @@
+/*
+ * dspark.h — C ABI of the DSpark per-step sampling and verification engine
+ * (MI355X / gfx950).
+ *
+ * Three hot-path calls:
+ *   dspark_markov_sample  left-to-right low-rank Markov head: turns the parallel
+ *                         draft backbone's block logits into gamma proposals,
+ *                         their full proposal distributions q and their
+ *                         confidence scores.
+ *   dspark_verify         exact verify of the proposals against the target
+ *                         distribution p: greedy contiguous-prefix match, or
+ *                         min(1, p/q) rejection sampling with a max(p-q, 0)
+ *                         residual and a bonus token.
+ *   dspark_accept_stats   training-side analytic acceptance: L1 distance,
+ *                         accept_rate, tau and the position-weighted
+ *                         CE / L1 / BCE loss numerator with report pairs.
+ *
+ * Sources (the pages this engine is built from):
+ *   [FT]  "[2/3] feat(dsv4): implement exact DSpark speculative decoding"
+ *         (FreeToken pull request): sections "End-to-end speculative cycle",
+ *         "Checkpoint-faithful DSpark architecture", "Exact decoding
+ *         semantics" (subsections "Greedy", "Probabilistic").
+ *   [MB]  "DSpark Speculative Decoding (Draft Training) Design"
+ *         (Megatron-Bridge RFC): sections "Semi-autoregressive draft",
+ *         "Training objective", "Acceptance and confidence",
+ *         "Loss return contract", "Memory contract for the full-vocabulary
+ *         terms".
+ *   [PS]  "DeepSeek V4 DSpark NPU Serving Dev Notes" (pypto-serving):
+ *         section "Speculative decoding (K=7)", paragraphs "Programs",
+ *         "Weights", "Acceptance".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  * Every array argument is a caller-owned DEVICE pointer to a dense,
+ *    row-major, contiguous array, unless stated otherwise.  The library never
+ *    allocates, frees or retains device memory; all scratch lives in the
+ *    caller's `workspace` (size from dspark_workspace_size), which must stay
+ *    untouched until the work queued on `stream` has finished.
+ *  * Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns; it never synchronises.  The library keeps no
+ *    global state, so calls on different streams with disjoint workspaces may
+ *    run concurrently.  Two calls that share a workspace must be ordered.
+ *  * Arguments are validated on the host BEFORE anything is enqueued; on any
+ *    error nothing is launched and the outputs are left untouched.  Device
+ *    memory contents are never read on the host, so value problems found on
+ *    the device (NaN logits, a non-positive temperature, zero residual mass)
+ *    never abort: they set bits in the per-row `flags` outputs.
+ *  * bf16 arrays are passed as uint16_t (IEEE binary32 truncated to its upper
+ *    16 bits, i.e. bfloat16).
+ *  * Sizes: B = requests, gamma = proposals per block, V = vocabulary,
+ *    r = Markov rank, d = draft hidden size.  Row k of the target logits
+ *    (k = 0..gamma) is the target distribution after token x_k (x_0 = the
+ *    anchor), so target row k-1 verifies proposal x_k and row gamma is the
+ *    bonus row ([FT] "End-to-end speculative cycle": one target pass over the
+ *    anchor plus the proposals).
+ *
+ * Random numbers
+ * --------------
+ *  Every random decision uses Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ *  "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) with
+ *      key     = (seed & 0xffffffff, seed >> 32)
+ *      counter = (i >> 2, (uint32_t)position, request_id, tag)
+ *  taking 32-bit output word (i & 3), where i is the token index (or chunk
+ *  index) being scored and `position` is the absolute position of the token
+ *  being decided (anchor position + k for proposal / emitted token k).  Tags:
+ *      0 DSPARK_TAG_DRAFT_TOKEN   token-level draft noise
+ *      1 DSPARK_TAG_ACCEPT        accept-test uniform (i = 0)
+ *      2 DSPARK_TAG_TARGET_TOKEN  token-level residual / bonus noise
+ *      3 DSPARK_TAG_DRAFT_CHUNK   chunk-level draft noise
+ *      4 DSPARK_TAG_TARGET_CHUNK  chunk-level residual / bonus noise
+ *  Uniforms: Gumbel u = ((w >> 9) + 0.5) * 2^-23 in (0,1); accept
+ *  u' = (w >> 8) * 2^-24 in [0,1).  Gumbel noise g = -ln(-ln u).
+ *
+ *  Sampling from weights w_v >= 0 is two-level Gumbel-max over chunks of
+ *  DSPARK_CHUNK = 256 consecutive tokens: pick chunk
+ *  c* = argmax_c (ln W_c + g_c) with W_c the chunk's total weight (chunk tag),
+ *  then token v* = argmax_{v in c*} (ln w_v + g_v) (token tag); ties go to the
+ *  lowest index.  P(v*) = (W_c / sum W) (w_v / W_c) = w_v / sum w exactly, and
+ *  no prefix sum over the vocabulary is needed.
+ *
+ * Sampling policy ([FT] "Probabilistic": p and q are both formed after the
+ * request's temperature, top-k and top-p)
+ * --------------------------------------------------------------------
+ *  Sampled rows: z = logits / T; top-k (if 0 < top_k < V) keeps
+ *  {v : z_v >= z_(top_k)} (ties at the boundary kept); top-p (if top_p < 1)
+ *  then keeps, within that set renormalised, every v whose probability is at
+ *  least that of the m-th most probable kept token, m the smallest count whose
+ *  cumulative probability reaches top_p (top_p <= 0 keeps the argmax set).
+ *  The distribution is softmax(z) over the kept set.  Greedy rows use the
+ *  argmax of the unscaled logits (lowest index on ties) and a one-hot
+ *  distribution.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (return value of every call) ------------------------- */
+typedef enum dspark_status {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,     /* a required pointer is NULL or a size is <= 0     */
+  DSPARK_EDTYPE = 2,     /* unknown logits dtype                             */
+  DSPARK_ESHAPE = 3,     /* a size outside the supported range (see below)   */
+  DSPARK_EWORKSPACE = 4, /* workspace NULL or smaller than required          */
+  DSPARK_EDEVICE = 5     /* a HIP launch or runtime call failed              */
+} dspark_status;
+
+/* ---- logits element types ------------------------------------------------ */
+enum { DSPARK_BF16 = 1, DSPARK_F32 = 2 };
+
+/* ---- per-row flag bits (uint8_t flags outputs) ---------------------------
+ * NEAR_THRESHOLD is the device's own diagnostic: a decision whose fp32 margin
+ * was within 1e-6 (relative to max(1, |score|), absolute for accept tests) of
+ * flipping.  The others report value problems.  NONFINITE and EMPTY_ROW are
+ * properties of a row's data and are reported on every row a request owns
+ * (target rows 0..n_draft, every draft row); a request with such a row has
+ * unspecified tokens, lengths and q outputs (logits must be finite or -inf;
+ * -inf excludes a token).  NEAR_THRESHOLD and RESIDUAL_ZERO are reported on
+ * the row where the decision was taken, BAD_POLICY on row 0.               */
+enum {
+  DSPARK_FLAG_NEAR_THRESHOLD = 1u << 0,
+  DSPARK_FLAG_NONFINITE = 1u << 1,      /* the row holds a NaN or +inf      */
+  DSPARK_FLAG_RESIDUAL_ZERO = 1u << 2,  /* max(p-q,0) had zero mass: sampled
+                                           from p instead                     */
+  DSPARK_FLAG_EMPTY_ROW = 1u << 3,      /* no logit above -inf in the row    */
+  DSPARK_FLAG_BAD_POLICY = 1u << 4      /* sampled row with temperature <= 0
+                                           or non-finite: treated as greedy  */
+};
+
+/* ---- Philox stream tags --------------------------------------------------- */
+enum {
+  DSPARK_TAG_DRAFT_TOKEN = 0,
+  DSPARK_TAG_ACCEPT = 1,
+  DSPARK_TAG_TARGET_TOKEN = 2,
+  DSPARK_TAG_DRAFT_CHUNK = 3,
+  DSPARK_TAG_TARGET_CHUNK = 4
+};
+
+/* Tokens per chunk of the two-level Gumbel-max sampler. */
+#define DSPARK_CHUNK 256
+
+/* ---- supported ranges (DSPARK_ESHAPE outside them) ------------------------ */
+#define DSPARK_MAX_GAMMA 16
+#define DSPARK_MAX_RANK 256      /* r must also be a multiple of 16 */
+#define DSPARK_MAX_HIDDEN 65536  /* d                                */
+#define DSPARK_MAX_VOCAB (1 << 30)
+
+/* ---- per-request sampling policy: all DEVICE arrays of length B ----------- */
+typedef struct dspark_policy {
+  const uint8_t* mode;         /* 0 = greedy, 1 = sampled                    */
+  const float* temperature;    /* T > 0 for sampled rows (ignored if greedy) */
+  const int32_t* top_k;        /* 0 or >= V: off                             */
+  const float* top_p;          /* >= 1: off                                  */
+  const uint32_t* request_id;  /* Philox counter word 2                      */
+  const int32_t* position;     /* absolute position of the anchor x_0        */
+} dspark_policy;
+
+/* ---- workspace sizing ------------------------------------------------------ */
+enum { DSPARK_OP_MARKOV = 1, DSPARK_OP_VERIFY = 2, DSPARK_OP_STATS = 3 };
+
+/* Bytes of device workspace one call of `op` needs at these sizes (for
+ * DSPARK_OP_STATS pass N as B; r and d are ignored where they do not apply).
+ * Returns 0 for an unknown op or non-positive sizes.  Host-only. */
+size_t dspark_workspace_size(int op, int32_t B, int32_t gamma, int32_t V,
+                             int32_t r, int32_t d);
+
+/* Human-readable name of a status code (static string).  Host-only. */
+const char* dspark_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch.  Host-only. */
+int dspark_version(void);
+
+/* ---------------------------------------------------------------------------
+ * dspark_markov_sample
+ *
+ * [FT] "Checkpoint-faithful DSpark architecture": the lightweight Markov head
+ * is sampled left to right, proposal k conditioning on proposal k-1 and the
+ * first on the anchor; the full proposal distribution q and the confidence
+ * scores are kept.  [MB] "Semi-autoregressive draft": the Markov head is a
+ * rank-256 token-conditioned additive logit bias, run serially at inference;
+ * the confidence head is c_k = sigmoid(w^T [h_k ; embed(x_{k-1})]).
+ * [PS] "Weights": markov_w1 / markov_w2, confidence head in FP32.
+ *
+ * For k = 1..gamma, in order (x_0 = anchor[b]):
+ *   y_k   = backbone_logits[b, k-1, :] + markov_w1[x_{k-1}, :] . markov_w2^T
+ *           (bias_v = sum_i markov_w1[x_{k-1}, i] * markov_w2[v, i])
+ *   q_k   = policy(y_k); x_k ~ q_k (two-level Gumbel-max, draft tags) for a
+ *           sampled row, x_k = argmax y_k for a greedy row
+ *   c_k   = sigmoid(sum_i conf_w[i] h[b,k-1,i]
+ *                   + sum_i conf_w[d+i] embed[x_{k-1}, i])
+ *
+ * Inputs
+ *   backbone_logits  [B, gamma, V]  logits_dtype; row k-1 = draft position k
+ *   anchor           [B] int32 in [0, V)
+ *   markov_w1        [V, r] bf16: row x is the rank-r code of token x (A)
+ *   markov_w2        [V, r] bf16: row v holds the r weights producing logit v
+ *                    (the [out, in] Linear layout of the rank-r -> V map)
+ *   hidden           [B, gamma, d] bf16: draft hidden state h_k at row k-1
+ *   embed            [V, d] bf16: the shared (target) token embedding
+ *   conf_w           [2d] fp32: confidence weight over [h_k ; embed(x_{k-1})]
+ *   policy, seed     as above
+ * Outputs
+ *   draft_tokens     [B, gamma] int32: x_1..x_gamma
+ *   q_logits         [B, gamma, V] fp32: z = y / T for SAMPLED rows, so that
+ *                    q_v = (z_v >= q_thr) ? exp(z_v - q_lse) : 0.  Rows of
+ *                    greedy requests are not written (q is one-hot at x_k).
+ *   q_lse            [B, gamma] fp32: log-sum-exp of z over the kept set
+ *                    (0 for greedy rows)
+ *   q_thr            [B, gamma] fp32: smallest kept z when top-k / top-p is
+ *                    active, -inf otherwise (0 for greedy rows)
+ *   q_tok            [B, gamma] fp32: q_k(x_k) (1 for greedy rows)
+ *   confidence       [B, gamma] fp32: c_k
+ *   flags            [B, gamma] uint8: DSPARK_FLAG_* per draft row
+ * Errors: EINVAL (NULL pointer, size <= 0), EDTYPE, ESHAPE (gamma >
+ * DSPARK_MAX_GAMMA, r > DSPARK_MAX_RANK or r % 16 != 0, d > DSPARK_MAX_HIDDEN,
+ * V > DSPARK_MAX_VOCAB), EWORKSPACE, EDEVICE.  anchor values outside [0, V)
+ * are clamped into range on the device.
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_markov_sample(
+    const void* backbone_logits, int logits_dtype, const int32_t* anchor,
+    const uint16_t* markov_w1, const uint16_t* markov_w2,
+    const uint16_t* hidden, const uint16_t* embed, const float* conf_w,
+    dspark_policy policy, uint64_t seed, int32_t B, int32_t gamma, int32_t V,
+    int32_t r, int32_t d, int32_t* draft_tokens, float* q_logits,
+    float* q_lse, float* q_thr, float* q_tok, float* confidence,
+    uint8_t* flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dspark_verify
+ *
+ * [FT] "Exact decoding semantics".  Greedy: accept the contiguous prefix of
+ * proposals equal to the target argmax, stop at the first disagreement and
+ * emit the target token there; a later accidental match is never accepted.
+ * Probabilistic: accept x_k with probability min(1, p(x_k)/q(x_k)); at the
+ * first rejection sample from normalised max(p - q, 0); if every proposal
+ * survives, sample a bonus token from the target's next-position
+ * distribution.  [PS] "Acceptance": 1..gamma+1 tokens per step.
+ *
+ * Per request b with n_d = n_draft[b] (gamma if n_draft is NULL; values are
+ * clamped into [0, gamma]):
+ *   greedy : t_k = argmax target[b,k,:] (lowest index); n = first k in
+ *            [1, n_d] with x_k != t_{k-1}, minus 1 (n_d if none);
+ *            out = (x_1..x_n, t_n)
+ *   sampled: p_k = policy(target[b,k,:]); accept x_k iff
+ *            u'_k < p_{k-1}(x_k) / q_k(x_k) (accept iff p > 0 when q = 0);
+ *            first reject j: out = (x_1..x_{j-1}, r), r ~ max(p_{j-1} - q_j, 0)
+ *            (target tags, position anchor+j; zero mass: r ~ p_{j-1} and
+ *            DSPARK_FLAG_RESIDUAL_ZERO); all accepted: out = (x_1..x_{n_d}, r),
+ *            r ~ p_{n_d} (target tags, position anchor+n_d+1).
+ *
+ * Inputs
+ *   target_logits  [B, gamma+1, V] logits_dtype
+ *   draft_tokens   [B, gamma] int32
+ *   q_logits, q_lse, q_thr, q_tok  as written by dspark_markov_sample; the
+ *                  first three may be NULL only if every request is greedy
+ *                  (they are then never read); q_tok may be NULL likewise.
+ *   n_draft        [B] int32 or NULL
+ *   policy, seed   the same policy/seed as the Markov call
+ * Outputs
+ *   accept_len     [B] int32: accepted proposals n in [0, n_d]
+ *   out_tokens     [B, gamma+1] int32: the n+1 emitted tokens, then -1
+ *   flags          [B, gamma+1] uint8: bits per target row
+ * Errors: as dspark_markov_sample (gamma range, V range).
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_verify(
+    const void* target_logits, int logits_dtype, const int32_t* draft_tokens,
+    const float* q_logits, const float* q_lse, const float* q_thr,
+    const float* q_tok, const int32_t* n_draft, dspark_policy policy,
+    uint64_t seed, int32_t B, int32_t gamma, int32_t V, int32_t* accept_len,
+    int32_t* out_tokens, uint8_t* flags, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dspark_accept_stats
+ *
+ * [MB] "Training objective", "Acceptance and confidence", "Loss return
+ * contract".  For every block b in [0, N) and position k = 1..gamma (row k-1),
+ * with P = softmax(draft[b,k-1,:]) and T = softmax(target[b,k-1,:]):
+ *   l1   = sum_v |P_v - T_v|                (raw L1; the 1/2 is only in a)
+ *   a    = clamp(1 - 0.5 * l1, 0, 1)        (accept_rate)
+ *   ce   = logsumexp(draft row) - draft[b,k-1,teacher[b,k-1]]
+ *   bce  = max(c,0) - c*a + log1p(exp(-|c|)),  c = conf_logits[b,k-1]
+ *   tau_b = 1 + sum_k prod_{j<=k} a_{b,j}
+ * and with w_k = exp(-k/gamma) and mask_b = block_mask[b] != 0:
+ *   sums[0]  numerator  = sum_b mask_b sum_k w_k (w_ce ce + w_l1 l1 + w_conf bce)
+ *   sums[1]  num_tokens = gamma * sum_b mask_b
+ *   report pairs [sum, count] over masked positions (blocks for tau):
+ *   sums[2..3] l1, sums[4..5] accept_rate, sums[6..7] tau, sums[8..9] ce,
+ *   sums[10..11] bce.
+ * The numerator is never normalised here: callers divide once by the
+ * globally reduced num_tokens, and form logged ratios as sum/count.
+ *
+ * Inputs : draft_logits, target_logits [N, gamma, V] logits_dtype;
+ *          teacher [N, gamma] int32 (clamped into [0, V)); conf_logits
+ *          [N, gamma] fp32; block_mask [N] uint8 or NULL (all ones);
+ *          w_ce, w_l1, w_conf host scalars (0.1, 0.9, 1.0 in the pages).
+ * Outputs: l1, accept_rate, ce, bce [N, gamma] fp32 (every block, masked or
+ *          not); tau [N] fp32; sums [12] fp32.
+ * Errors : EINVAL, EDTYPE, ESHAPE (gamma, V ranges), EWORKSPACE, EDEVICE.
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_accept_stats(
+    const void* draft_logits, const void* target_logits, int logits_dtype,
+    const int32_t* teacher, const float* conf_logits,
+    const uint8_t* block_mask, int32_t N, int32_t gamma, int32_t V,
+    float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
+    float* ce, float* bce, float* tau, float* sums, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */
