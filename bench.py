@@ -1,0 +1,196 @@
+"""Benchmark of the DSpark sampling / verification hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of the decode-verify
+workload (B = 64 requests, gamma = 5, V = 129280, bf16 logits, Markov rank 256,
+confidence width 4096, sampled at temperature 1 without truncation):
+  dspark_markov_sample  (gamma Markov steps: bias GEMM + sampling + confidence)
+  dspark_verify         (the oracle-free exact sampled verify of those proposals)
+  dspark_accept_stats   (analytic acceptance of the same draft / target rows)
+Inputs are synthetic (workloads.py) and resident in HBM before timing starts.
+
+Prints one JSON line: value = verified rows per second, B (gamma + 1) rows per
+step; the roofline entry is the dominant kernel's algorithmic HBM bytes per
+launch over its average launch time, measured here with HIP events around each
+launch (the library's opt-in profiler, on the launch stream); cpu_baseline is
+the oracle, single-threaded, on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified rows/sec (B×(γ+1)×V logits) at V=129280,B=64,γ=5; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests of the batch the oracle baseline runs on")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_bytes(name, B, g, V, r, d, S, R):
+    """Algorithmic (compulsory) HBM bytes of one launch of each kernel."""
+    C = (V + 255) // 256
+    if name == "markov_step":      # backbone row + q row written + W2 (once per call) + A rows
+        return 2 * B * V + 4 * S * V + (2 * r * V) / g + 2 * B * r
+    if name == "markov_finalize":  # chunk partials + h and embedding rows + chosen-chunk z
+        return 16 * B * C + 4 * B * d + 4 * 256 * S
+    if name == "verify_rows":      # every target row once
+        return 2 * B * (g + 1) * V
+    if name == "verify_decide":    # the proposal row of each rejecting request
+        return 4 * V * R
+    if name == "stats_rows":       # draft + target row pairs
+        return 2 * 2 * B * g * V
+    if name == "stats_reduce":
+        return 16 * B * g
+    return 0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dspark_draft_sampling_amd as ds
+    from workloads import decode_inputs
+
+    t0 = time.time()
+    inp = decode_inputs("decode")
+    B, g, V, r, d = inp["B"], inp["gamma"], inp["V"], inp["r"], inp["d"]
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    backbone, target = bf(inp["backbone"]), bf(inp["target"])
+    w1, w2, hidden, embed = bf(inp["w1"]), bf(inp["w2"]), bf(inp["hidden"]), bf(inp["embed"])
+    anchor = torch.from_numpy(inp["anchor"]).to(dev)
+    conf_w = torch.from_numpy(inp["conf_w"]).to(dev)
+    pol = ds.Policy(mode=torch.from_numpy(inp["mode"]).to(dev),
+                    temperature=torch.from_numpy(inp["temperature"]).to(dev),
+                    top_k=torch.from_numpy(inp["top_k"]).to(dev),
+                    top_p=torch.from_numpy(inp["top_p"]).to(dev),
+                    request_id=torch.from_numpy(inp["request_id"].view(np.int32)).to(dev),
+                    position=torch.from_numpy(inp["position"]).to(dev))
+    # the accept stats read the same rows: draft logits and the first gamma target rows
+    tgt_rows = target[:, :g].contiguous()
+    rng = np.random.default_rng(1234)
+    teacher = torch.from_numpy(rng.integers(0, V, (B, g)).astype(np.int32)).to(dev)
+    conf_logits = torch.from_numpy(rng.standard_normal((B, g)).astype(np.float32)).to(dev)
+
+    mk_out = ds.dspark_markov_sample(backbone, anchor, w1, w2, hidden, embed, conf_w, pol, seed=0)
+    vf_out = ds.dspark_verify(target, mk_out["draft_tokens"], pol, mk_out["q_logits"],
+                              mk_out["q_lse"], mk_out["q_thr"], mk_out["q_tok"], seed=0)
+    st_out = ds.dspark_accept_stats(backbone, tgt_rows, teacher, conf_logits)
+
+    def step():
+        ds.dspark_markov_sample(backbone, anchor, w1, w2, hidden, embed, conf_w, pol, seed=0,
+                                out=mk_out)
+        ds.dspark_verify(target, mk_out["draft_tokens"], pol, mk_out["q_logits"],
+                         mk_out["q_lse"], mk_out["q_thr"], mk_out["q_tok"], seed=0, out=vf_out)
+        ds.dspark_accept_stats(backbone, tgt_rows, teacher, conf_logits, out=st_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    value = B * (g + 1) * args.steps / (ms_total / 1e3)
+    print(f"# {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall:.3f}s",
+          file=sys.stderr, flush=True)
+
+    # per-kernel launch durations, same launch configuration, HIP events on the launch stream
+    prof_steps = max(10, min(args.steps, 50))
+    ds.profile_enable(True)
+    for _ in range(prof_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = ds.profile_summary()
+    ds.profile_enable(False)
+    S = int((inp["mode"] != 0).sum())
+    R = int((vf_out["accept_len"] < g).sum().item())
+    kernels = {}
+    for name, (n, ms) in prof.items():
+        avg_us = ms / n * 1e3
+        nbytes = kernel_bytes(name, B, g, V, r, d, S, R)
+        kernels[name] = dict(launches_per_step=n / prof_steps, avg_us=round(avg_us, 3),
+                             alg_bytes=int(nbytes), gbs=round(nbytes / (avg_us * 1e-6) / 1e9, 1))
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+    ach = kernels[dom]["gbs"]
+    roofline = dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, args.cpu_requests)
+
+    line = dict(metric=METRIC, value=round(value, 1), unit="rows/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(ms_per_step, 5), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="decode verify: Markov sample + sampled verify + accept stats",
+                            B=B, gamma=g, V=V, r=r, d=d, logits="bf16", temperature=1.0,
+                            truncation="none", mode="sampled"),
+                roofline=roofline, cpu_baseline=cpu,
+                step=dict(alg_bytes=int(step_bytes),
+                          alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                          accept_rate=round(float(vf_out["accept_len"].float().mean().item()) / g, 4),
+                          kernels=kernels))
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, nreq):
+    """The oracle on the first nreq requests of the batch, single-threaded."""
+    from oracle import oracle as O
+    from workloads import decode_inputs
+
+    reqs = list(range(nreq))
+    sub = decode_inputs("decode", requests=reqs, with_embed=False)
+    sub["embed"] = inp["embed"]
+    g = sub["gamma"]
+    t = time.perf_counter()
+    mk = O.markov_sample(sub)
+    q = dict(q_z=mk["q_z"].astype(np.float32), q_lse=mk["q_lse"].astype(np.float32),
+             q_thr=mk["q_thr"].astype(np.float32), q_tok=mk["q_tok"].astype(np.float32))
+    O.verify(sub, mk["draft_tokens"], **q)
+    st = dict(draft=sub["backbone"], target=np.ascontiguousarray(sub["target"][:, :g]),
+              teacher=np.zeros((nreq, g), np.int32), conf_logits=np.zeros((nreq, g), np.float32),
+              block_mask=None, N=nreq, gamma=g, V=sub["V"], dtype=sub["dtype"])
+    O.accept_stats(st)
+    sec = time.perf_counter() - t
+    return dict(value=round(nreq * (g + 1) / sec, 2), unit="rows/s", cores=1, kind="oracle",
+                sample=f"{nreq} of the 64 requests (Markov sample + verify + accept stats), "
+                       f"{sec:.1f}s single-threaded")
+
+
+if __name__ == "__main__":
+    main()

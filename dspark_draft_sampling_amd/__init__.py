@@ -1,0 +1,267 @@
+"""Python binding of the DSpark sampling / verification library (libdspark.so).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the stream (the current stream of the
+tensors' device).  The functions carry the C ABI's names:
+
+  dspark_markov_sample  Markov draft sampler + confidence head
+  dspark_verify         exact greedy / sampled verify
+  dspark_accept_stats   training-side analytic acceptance statistics
+
+Outputs are allocated with torch on the inputs' device (or passed in through
+`out=`).  A status other than DSPARK_OK raises DSparkError.  There is no CPU
+fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_ESHAPE, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(6)
+DSPARK_BF16, DSPARK_F32 = 1, 2
+DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS = 1, 2, 3
+FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
+
+__all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
+           "dspark_accept_stats", "dspark_workspace_size", "profile_enable", "profile_summary"]
+
+
+class DSparkError(RuntimeError):
+    pass
+
+
+class dspark_policy(C.Structure):
+    _fields_ = [("mode", C.c_void_p), ("temperature", C.c_void_p), ("top_k", C.c_void_p),
+                ("top_p", C.c_void_p), ("request_id", C.c_void_p), ("position", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdspark.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DSparkError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        P, i32, u64, f32, sz = C.c_void_p, C.c_int32, C.c_uint64, C.c_float, C.c_size_t
+        L.dspark_workspace_size.argtypes = [C.c_int, i32, i32, i32, i32, i32]
+        L.dspark_workspace_size.restype = sz
+        L.dspark_status_string.argtypes = [C.c_int]
+        L.dspark_status_string.restype = C.c_char_p
+        L.dspark_version.restype = C.c_int
+        L.dspark_markov_sample.argtypes = [P, C.c_int, P, P, P, P, P, P, dspark_policy, u64, i32,
+                                           i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+        L.dspark_markov_sample.restype = C.c_int
+        L.dspark_verify.argtypes = [P, C.c_int, P, P, P, P, P, P, dspark_policy, u64, i32, i32,
+                                    i32, P, P, P, P, sz, P]
+        L.dspark_verify.restype = C.c_int
+        L.dspark_accept_stats.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32, f32,
+                                          P, P, P, P, P, P, P, sz, P]
+        L.dspark_accept_stats.restype = C.c_int
+        L.dspark_profile_enable.argtypes = [C.c_int]
+        L.dspark_profile_enable.restype = C.c_int
+        L.dspark_profile_summary.argtypes = [C.c_char_p, sz]
+        L.dspark_profile_summary.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != DSPARK_OK:
+        raise DSparkError(f"dspark status {rc}: {lib().dspark_status_string(rc).decode()}")
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise DSparkError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise DSparkError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise DSparkError(f"{name} must be contiguous")
+    return t
+
+
+def _logits_dtype(t, name):
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    raise DSparkError(f"{name} must be bfloat16 or float32")
+
+
+_ws = {}
+
+
+def _workspace(op, device, nbytes):
+    """A cached per-(device, op) scratch buffer of at least nbytes."""
+    key = (device, op)
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def dspark_workspace_size(op, B, gamma, V, r=0, d=0):
+    return int(lib().dspark_workspace_size(op, B, gamma, V, r, d))
+
+
+@dataclass
+class Policy:
+    """Per-request sampling policy as device tensors of length B."""
+
+    mode: torch.Tensor          # uint8: 0 greedy, 1 sampled
+    temperature: torch.Tensor   # float32
+    top_k: torch.Tensor         # int32 (0 = off)
+    top_p: torch.Tensor         # float32 (>= 1 = off)
+    request_id: torch.Tensor    # int32 holding the uint32 request ids
+    position: torch.Tensor      # int32: absolute position of the anchor
+
+    def c(self):
+        _dev_tensor(self.mode, torch.uint8, "mode")
+        _dev_tensor(self.temperature, torch.float32, "temperature")
+        _dev_tensor(self.top_k, torch.int32, "top_k")
+        _dev_tensor(self.top_p, torch.float32, "top_p")
+        _dev_tensor(self.request_id, torch.int32, "request_id")
+        _dev_tensor(self.position, torch.int32, "position")
+        return dspark_policy(self.mode.data_ptr(), self.temperature.data_ptr(),
+                             self.top_k.data_ptr(), self.top_p.data_ptr(),
+                             self.request_id.data_ptr(), self.position.data_ptr())
+
+
+def _stream(device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dspark_markov_sample(backbone, anchor, markov_w1, markov_w2, hidden, embed, conf_w,
+                         policy: Policy, seed=0, out=None):
+    """Markov draft sampling; returns a dict of device tensors
+    draft_tokens [B,g] int32, q_logits [B,g,V] f32, q_lse, q_thr, q_tok,
+    confidence [B,g] f32, flags [B,g] uint8."""
+    dt = _logits_dtype(backbone, "backbone")
+    _dev_tensor(backbone, backbone.dtype, "backbone")
+    B, g, V = backbone.shape
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1")
+    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2")
+    _dev_tensor(hidden, torch.bfloat16, "hidden")
+    _dev_tensor(embed, torch.bfloat16, "embed")
+    _dev_tensor(conf_w, torch.float32, "conf_w")
+    _dev_tensor(anchor, torch.int32, "anchor")
+    r = markov_w1.shape[1]
+    d = hidden.shape[2]
+    if markov_w1.shape != (V, r) or markov_w2.shape != (V, r) or hidden.shape != (B, g, d) \
+            or embed.shape != (V, d) or conf_w.shape != (2 * d,) or anchor.shape != (B,):
+        raise DSparkError("markov_sample: inconsistent shapes")
+    dev = backbone.device
+    if out is None:
+        out = dict(draft_tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
+                   q_logits=torch.empty((B, g, V), dtype=torch.float32, device=dev),
+                   q_lse=torch.empty((B, g), dtype=torch.float32, device=dev),
+                   q_thr=torch.empty((B, g), dtype=torch.float32, device=dev),
+                   q_tok=torch.empty((B, g), dtype=torch.float32, device=dev),
+                   confidence=torch.empty((B, g), dtype=torch.float32, device=dev),
+                   flags=torch.empty((B, g), dtype=torch.uint8, device=dev))
+    nb = dspark_workspace_size(DSPARK_OP_MARKOV, B, g, V, r, d)
+    ws = _workspace(DSPARK_OP_MARKOV, dev, nb)
+    rc = lib().dspark_markov_sample(
+        _p(backbone), dt, _p(anchor), _p(markov_w1), _p(markov_w2), _p(hidden), _p(embed),
+        _p(conf_w), policy.c(), int(seed), B, g, V, r, d, _p(out["draft_tokens"]),
+        _p(out["q_logits"]), _p(out["q_lse"]), _p(out["q_thr"]), _p(out["q_tok"]),
+        _p(out["confidence"]), _p(out["flags"]), _p(ws), ws.numel(), _stream(dev))
+    _check(rc)
+    return out
+
+
+def dspark_verify(target, draft_tokens, policy: Policy, q_logits=None, q_lse=None, q_thr=None,
+                  q_tok=None, n_draft=None, seed=0, out=None):
+    """Exact verify; returns dict accept_len [B] int32, out_tokens [B,g+1]
+    int32, flags [B,g+1] uint8 (device tensors)."""
+    dt = _logits_dtype(target, "target")
+    _dev_tensor(target, target.dtype, "target")
+    B, g1, V = target.shape
+    g = g1 - 1
+    _dev_tensor(draft_tokens, torch.int32, "draft_tokens")
+    if draft_tokens.shape != (B, g):
+        raise DSparkError("verify: draft_tokens must be [B, gamma]")
+    for name, t, shape in [("q_logits", q_logits, (B, g, V)), ("q_lse", q_lse, (B, g)),
+                           ("q_thr", q_thr, (B, g)), ("q_tok", q_tok, (B, g))]:
+        if t is not None:
+            _dev_tensor(t, torch.float32, name)
+            if tuple(t.shape) != shape:
+                raise DSparkError(f"verify: {name} must be {shape}")
+    if n_draft is not None:
+        _dev_tensor(n_draft, torch.int32, "n_draft")
+    dev = target.device
+    if out is None:
+        out = dict(accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, g1), dtype=torch.int32, device=dev),
+                   flags=torch.empty((B, g1), dtype=torch.uint8, device=dev))
+    nb = dspark_workspace_size(DSPARK_OP_VERIFY, B, g, V)
+    ws = _workspace(DSPARK_OP_VERIFY, dev, nb)
+    rc = lib().dspark_verify(_p(target), dt, _p(draft_tokens), _p(q_logits), _p(q_lse),
+                             _p(q_thr), _p(q_tok), _p(n_draft), policy.c(), int(seed), B, g, V,
+                             _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["flags"]),
+                             _p(ws), ws.numel(), _stream(dev))
+    _check(rc)
+    return out
+
+
+def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_ce=0.1,
+                        w_l1=0.9, w_conf=1.0, out=None):
+    """Acceptance statistics; returns dict l1, accept_rate, ce, bce [N,g],
+    tau [N], sums [12] (float32 device tensors)."""
+    dt = _logits_dtype(draft, "draft")
+    _dev_tensor(draft, draft.dtype, "draft")
+    _dev_tensor(target, draft.dtype, "target")
+    N, g, V = draft.shape
+    if target.shape != draft.shape:
+        raise DSparkError("accept_stats: draft and target shapes differ")
+    _dev_tensor(teacher, torch.int32, "teacher")
+    _dev_tensor(conf_logits, torch.float32, "conf_logits")
+    if block_mask is not None:
+        _dev_tensor(block_mask, torch.uint8, "block_mask")
+    dev = draft.device
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        out = dict(l1=torch.empty((N, g), **f), accept_rate=torch.empty((N, g), **f),
+                   ce=torch.empty((N, g), **f), bce=torch.empty((N, g), **f),
+                   tau=torch.empty((N,), **f), sums=torch.empty((12,), **f))
+    nb = dspark_workspace_size(DSPARK_OP_STATS, N, g, V)
+    ws = _workspace(DSPARK_OP_STATS, dev, nb) if nb > 0 else None
+    rc = lib().dspark_accept_stats(_p(draft), _p(target), dt, _p(teacher), _p(conf_logits),
+                                   _p(block_mask), N, g, V, float(w_ce), float(w_l1),
+                                   float(w_conf), _p(out["l1"]), _p(out["accept_rate"]),
+                                   _p(out["ce"]), _p(out["bce"]), _p(out["tau"]),
+                                   _p(out["sums"]), _p(ws), 0 if ws is None else ws.numel(),
+                                   _stream(dev))
+    _check(rc)
+    return out
+
+
+def profile_enable(on=True):
+    lib().dspark_profile_enable(1 if on else 0)
+
+
+def profile_summary():
+    """{kernel: (launches, total_ms)} of the launches recorded since the last call."""
+    buf = C.create_string_buffer(1 << 16)
+    _check(lib().dspark_profile_summary(buf, len(buf)))
+    res = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        res[name] = (int(n), float(ms))
+    return res

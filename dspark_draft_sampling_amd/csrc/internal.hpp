@@ -1,0 +1,96 @@
+// internal.hpp — host-side plumbing shared by the library's translation units:
+// workspace layout and the per-operation launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+// Per (row, slice) partial of the vocabulary-streaming row pass.
+struct RowPart {
+  float m;      // maximum logit of the slice (-inf if none)
+  float s;      // sum of exp((l - m) / T) over the slice (sampled rows)
+  int32_t arg;  // lowest index of the maximum (INT32_MAX if none)
+  uint32_t flags;
+};
+
+// Per (request, slice) best chunk of a two-level Gumbel-max draw.
+struct Pick {
+  float v1;     // best score
+  int32_t i1;   // its chunk
+  float v2;     // second-best score
+  uint32_t pad;
+};
+
+// Per (request, chunk) partial of the Markov step's fused GEMM epilogue.
+struct ChunkPart {
+  float m;      // max of z over the chunk
+  float s;      // sum of exp(z - m) over the chunk
+  int32_t arg;  // lowest index of the max of z (greedy rows: of y)
+  uint32_t flags;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Brackets one kernel launch with HIP events while profiling is enabled
+// (dspark_profile_enable); a no-op otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t st);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t a_;
+};
+
+// Vocabulary slicing of the verify row pass.
+struct VerifyPlan {
+  int vec;        // 1: 16-byte vector loads, 0: scalar loads
+  int slice_len;  // elements per row slice
+  int S;          // row slices
+  int S2;         // chunk slices of the residual / bonus pass
+  int cps;        // chunks per chunk slice
+  size_t off_part, off_pick, off_cnt, bytes;
+};
+VerifyPlan plan_verify(int logits_dtype, int32_t B, int32_t gamma, int32_t V, bool aligned);
+
+struct MarkovPlan {
+  int C;  // chunks per row
+  size_t off_part, bytes;
+};
+MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d);
+
+struct StatsPlan {
+  size_t off_sums, bytes;
+};
+StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
+
+hipError_t launch_verify(const void* target, int dtype, const int32_t* draft, const float* q_z,
+                         const float* q_lse, const float* q_thr, const float* q_tok,
+                         const int32_t* n_draft, dspark_policy pol, uint64_t seed, int32_t B,
+                         int32_t gamma, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                         uint8_t* flags, void* ws, const VerifyPlan& plan, hipStream_t st);
+
+hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
+                         const uint16_t* w1, const uint16_t* w2, const uint16_t* hidden,
+                         const uint16_t* embed, const float* conf_w, dspark_policy pol,
+                         uint64_t seed, int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d,
+                         int32_t* draft_tokens, float* q_z, float* q_lse, float* q_thr,
+                         float* q_tok, float* confidence, uint8_t* flags, void* ws,
+                         const MarkovPlan& plan, hipStream_t st);
+
+hipError_t launch_stats(const void* draft, const void* target, int dtype, const int32_t* teacher,
+                        const float* conf_logits, const uint8_t* block_mask, int32_t N,
+                        int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
+                        float* accept_rate, float* ce, float* bce, float* tau, float* sums,
+                        void* ws, const StatsPlan& plan, hipStream_t st);
+
+}  // namespace dspark

@@ -1,0 +1,273 @@
+// stats.hip — training-side analytic acceptance statistics on gfx950.
+//
+// Semantics ("DSpark Speculative Decoding (Draft Training) Design", sections
+// "Training objective", "Acceptance and confidence", "Loss return contract"):
+// per block b and position k, with P = softmax(draft row) and T = softmax(target
+// row): l1 = sum |P - T| (raw), a = clamp(1 - l1 / 2, 0, 1), ce = lse(draft) -
+// draft[teacher], bce = BCE-with-logits(c, a); per block tau = 1 + sum_k
+// prod_{j<=k} a_j; the position-weighted loss numerator (weights exp(-k/gamma))
+// and [sum, count] report pairs are returned unnormalised.
+//
+// stats_rows: one workgroup per row pair.  Pass 1 streams both rows once with
+// 16-byte loads and keeps an online (max, sum exp) per thread; pass 2 streams
+// them again (the pair was just read, so it is served from the caches) for
+// the L1 term.  stats_reduce: one workgroup computes tau and the sums in fp64
+// in a fixed order, so the sums are deterministic.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dspark {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;
+
+template <typename T, bool VEC>
+struct Vec8;
+
+template <>
+struct Vec8<uint16_t, true> {
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* o) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    o[0] = bf_lo(u.x);
+    o[1] = bf_hi(u.x);
+    o[2] = bf_lo(u.y);
+    o[3] = bf_hi(u.y);
+    o[4] = bf_lo(u.z);
+    o[5] = bf_hi(u.z);
+    o[6] = bf_lo(u.w);
+    o[7] = bf_hi(u.w);
+  }
+};
+template <>
+struct Vec8<float, true> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* o) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    o[0] = u.x;
+    o[1] = u.y;
+    o[2] = u.z;
+    o[3] = u.w;
+  }
+};
+template <typename T>
+struct Vec8<T, false> {
+  static constexpr int N = 1;
+  __device__ static void load(const T* p, float* o) { o[0] = load_logit(p, 0); }
+};
+
+__device__ __forceinline__ void online(float& m, float& s, const float* x, int n) {
+  float mx = x[0];
+  for (int j = 1; j < n; ++j) mx = fmaxf(mx, x[j]);
+  if (mx > m) {
+    s = (m > neg_inf()) ? s * __builtin_amdgcn_exp2f((m - mx) * kLog2e) : 0.0f;
+    m = mx;
+  }
+  if (m > neg_inf())
+    for (int j = 0; j < n; ++j) s += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void stats_rows_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, const int32_t* __restrict__ teacher,
+    const float* __restrict__ conf_logits, int32_t V, float* __restrict__ l1,
+    float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
+  using L = Vec8<T, VEC>;
+  constexpr int EPL = L::N;
+  __shared__ float shv[kWaves];
+  const size_t row = blockIdx.x;
+  const T* dr = draft + row * V;
+  const T* tr = target + row * V;
+  const int step = kThreads * EPL;
+
+  // pass 1: online normalisers of both rows
+  float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
+  int e = threadIdx.x * EPL;
+  for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
+    float xd[kUnroll][EPL], xt[kUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      L::load(dr + e + u * step, xd[u]);
+      L::load(tr + e + u * step, xt[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      online(md, sd, xd[u], EPL);
+      online(mt, st, xt[u], EPL);
+    }
+  }
+  for (; e < V; e += step) {
+    float xd[EPL], xt[EPL];
+    L::load(dr + e, xd);
+    L::load(tr + e, xt);
+    online(md, sd, xd, EPL);
+    online(mt, st, xt, EPL);
+  }
+  const float Md = block_max<kWaves>(md, shv);
+  const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
+  const float Mt = block_max<kWaves>(mt, shv);
+  const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
+  const float isd = 1.0f / Sd, ist = 1.0f / St;
+
+  // pass 2: L1 = sum |P - T|
+  float acc = 0.0f;
+  e = threadIdx.x * EPL;
+  for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
+    float xd[kUnroll][EPL], xt[kUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      L::load(dr + e + u * step, xd[u]);
+      L::load(tr + e + u * step, xt[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        acc += fabsf(__builtin_amdgcn_exp2f((xd[u][j] - Md) * kLog2e) * isd -
+                     __builtin_amdgcn_exp2f((xt[u][j] - Mt) * kLog2e) * ist);
+  }
+  for (; e < V; e += step) {
+    float xd[EPL], xt[EPL];
+    L::load(dr + e, xd);
+    L::load(tr + e, xt);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      acc += fabsf(__builtin_amdgcn_exp2f((xd[j] - Md) * kLog2e) * isd -
+                   __builtin_amdgcn_exp2f((xt[j] - Mt) * kLog2e) * ist);
+  }
+  const float L1 = block_sum<kWaves>(acc, shv);
+
+  if (threadIdx.x == 0) {
+    const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+    const int32_t tch = clamp_token(teacher[row], V);
+    const float lse_d = Md + logf(Sd);
+    const float c = conf_logits[row];
+    l1[row] = L1;
+    accept_rate[row] = a;
+    ce[row] = lse_d - load_logit(dr, tch);
+    bce[row] = fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
+  }
+}
+
+// One workgroup: per-block tau and the loss / report sums, in fp64, in a fixed
+// order (thread t owns blocks t, t + 256, ...; then a fixed tree).
+__global__ __launch_bounds__(kThreads) void stats_reduce_kernel(
+    const float* __restrict__ l1, const float* __restrict__ accept_rate,
+    const float* __restrict__ ce, const float* __restrict__ bce,
+    const uint8_t* __restrict__ block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,
+    float w_conf, float* __restrict__ tau, float* __restrict__ sums) {
+  __shared__ double sh[kThreads];
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // num, tokens, l1, acc, tau, blocks, ce, bce
+  for (int b = threadIdx.x; b < N; b += kThreads) {
+    const bool m = block_mask ? block_mask[b] != 0 : true;
+    double cum = 1.0, t = 1.0;
+    for (int k = 1; k <= gamma; ++k) {
+      const size_t i = static_cast<size_t>(b) * gamma + (k - 1);
+      const double a = accept_rate[i];
+      cum *= a;
+      t += cum;
+      if (m) {
+        const double wk = exp(-static_cast<double>(k) / gamma);
+        acc[0] += wk * (w_ce * static_cast<double>(ce[i]) + w_l1 * static_cast<double>(l1[i]) +
+                        w_conf * static_cast<double>(bce[i]));
+        acc[1] += 1.0;
+        acc[2] += l1[i];
+        acc[3] += a;
+        acc[6] += ce[i];
+        acc[7] += bce[i];
+      }
+    }
+    tau[b] = static_cast<float>(t);
+    if (m) {
+      acc[4] += t;
+      acc[5] += 1.0;
+    }
+  }
+  double tot[8];
+  for (int q = 0; q < 8; ++q) {
+    sh[threadIdx.x] = acc[q];
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+      if (static_cast<int>(threadIdx.x) < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+      __syncthreads();
+    }
+    tot[q] = sh[0];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double n = tot[1];
+    sums[0] = static_cast<float>(tot[0]);
+    sums[1] = static_cast<float>(n);
+    sums[2] = static_cast<float>(tot[2]);
+    sums[3] = static_cast<float>(n);
+    sums[4] = static_cast<float>(tot[3]);
+    sums[5] = static_cast<float>(n);
+    sums[6] = static_cast<float>(tot[4]);
+    sums[7] = static_cast<float>(tot[5]);
+    sums[8] = static_cast<float>(tot[6]);
+    sums[9] = static_cast<float>(n);
+    sums[10] = static_cast<float>(tot[7]);
+    sums[11] = static_cast<float>(n);
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
+                        const float* conf_logits, const uint8_t* block_mask, int32_t N,
+                        int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
+                        float* accept_rate, float* ce, float* bce, float* tau, float* sums,
+                        hipStream_t st) {
+  const int epl = sizeof(T) == 2 ? 8 : 4;
+  const bool vec = (V % epl == 0) && reinterpret_cast<uintptr_t>(draft) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(target) % 16 == 0;
+  const dim3 grid(static_cast<unsigned>(static_cast<size_t>(N) * gamma));
+  {
+  ProfScope ps("stats_rows", st);
+  if (N == 0) {
+    // no rows: the reduction still writes the (zero) sums
+  } else if (vec)
+    hipLaunchKernelGGL((stats_rows_kernel<T, true>), grid, dim3(kThreads), 0, st, draft, target,
+                       teacher, conf_logits, V, l1, accept_rate, ce, bce);
+  else
+    hipLaunchKernelGGL((stats_rows_kernel<T, false>), grid, dim3(kThreads), 0, st, draft, target,
+                       teacher, conf_logits, V, l1, accept_rate, ce, bce);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ProfScope ps("stats_reduce", st);
+  hipLaunchKernelGGL(stats_reduce_kernel, dim3(1), dim3(kThreads), 0, st, l1, accept_rate, ce, bce,
+                     block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
+  (void)N;
+  (void)gamma;
+  (void)V;
+  StatsPlan p{};
+  p.off_sums = 0;
+  p.bytes = 0;
+  return p;
+}
+
+hipError_t launch_stats(const void* draft, const void* target, int dtype, const int32_t* teacher,
+                        const float* conf_logits, const uint8_t* block_mask, int32_t N,
+                        int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
+                        float* accept_rate, float* ce, float* bce, float* tau, float* sums,
+                        void* ws, const StatsPlan& plan, hipStream_t st) {
+  (void)ws;
+  (void)plan;
+  if (dtype == DSPARK_BF16)
+    return launch_typed(static_cast<const uint16_t*>(draft), static_cast<const uint16_t*>(target),
+                        teacher, conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf, l1,
+                        accept_rate, ce, bce, tau, sums, st);
+  return launch_typed(static_cast<const float*>(draft), static_cast<const float*>(target), teacher,
+                      conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf, l1, accept_rate,
+                      ce, bce, tau, sums, st);
+}
+
+}  // namespace dspark

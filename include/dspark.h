@@ -175,6 +175,15 @@ const char* dspark_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch.  Host-only. */
 int dspark_version(void);
 
+/* Diagnostics: per-kernel timing with HIP events (off by default; the only
+ * process-wide state of the library).  While enabled, every kernel the library
+ * launches is bracketed by two events recorded on its stream.
+ * dspark_profile_summary waits for the recorded events, writes one line
+ * "<kernel> <launches> <total_ms>" per kernel name into buf (NUL-terminated,
+ * truncated to n bytes), forgets the records, and returns 0 or DSPARK_EDEVICE. */
+int dspark_profile_enable(int on);
+int dspark_profile_summary(char* buf, size_t n);
+
 /* ---------------------------------------------------------------------------
  * dspark_markov_sample
  *

@@ -1,0 +1,232 @@
+"""GPU parity of the HIP library against the CPU oracle (needs an MI355X).
+
+Every input comes from the seeded generator (workloads.py) or from the oracle
+itself (the verify's proposals and q are the oracle Markov's, rounded to fp32);
+nothing the GPU computes is fed back to the oracle.
+
+Bars: tokens, accept lengths and integer flags bit-exact, except where the
+oracle flags a decision within 1e-6 of its threshold (then the rest of that
+chain is not compared); floating-point outputs within 1e-4 relative.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from oracle import oracle as O  # noqa: E402
+from tests import _gpu as G  # noqa: E402
+from tests._cases import decode_case, stats_case  # noqa: E402
+from workloads import decode_inputs, stats_inputs  # noqa: E402
+
+RTOL = 1e-4
+DATA_FLAGS = O.F_NONFINITE | O.F_EMPTY
+
+
+def first_flag(flags):
+    """Per request, index of the first row the oracle flags NEAR (g if none)."""
+    near = (flags & O.F_NEAR) != 0
+    g = flags.shape[1]
+    return np.where(near.any(1), near.argmax(1), g)
+
+
+def check_markov(inp, got, ref, rows=None):
+    B, g = ref["draft_tokens"].shape
+    ff = first_flag(ref["flags"])
+    sampled = (inp["mode"] != 0)
+    n_cmp = 0
+    for b in range(B):
+        for k in range(g):
+            if k > ff[b]:
+                break  # chain may legitimately diverge after a flagged draw
+            # quantities that depend only on x_{k-1}: compare up to the flagged row
+            assert np.isclose(got["confidence"][b, k], ref["confidence"][b, k], rtol=RTOL, atol=1e-6), (b, k)
+            if sampled[b]:
+                gz, rz = got["q_logits"][b, k], ref["q_z"][b, k]
+                assert np.allclose(gz, rz, rtol=RTOL, atol=1e-5), (b, k, np.abs(gz - rz).max())
+                assert np.isclose(got["q_lse"][b, k], ref["q_lse"][b, k], rtol=RTOL, atol=1e-6), (b, k)
+            if k == ff[b]:
+                break
+            assert got["draft_tokens"][b, k] == ref["draft_tokens"][b, k], (b, k)
+            assert np.isclose(got["q_tok"][b, k], ref["q_tok"][b, k], rtol=RTOL, atol=1e-12), (b, k)
+            assert (got["flags"][b, k] & DATA_FLAGS) == (ref["flags"][b, k] & DATA_FLAGS), (b, k)
+            n_cmp += 1
+    return n_cmp
+
+
+def check_verify(got, ref):
+    flagged = (ref["flags"] & O.F_NEAR).any(1)
+    ok = ~flagged
+    assert np.array_equal(got["accept_len"][ok], ref["accept_len"][ok])
+    assert np.array_equal(got["out_tokens"][ok], ref["out_tokens"][ok])
+    assert np.array_equal(got["flags"][ok] & (DATA_FLAGS | O.F_RESID_ZERO | O.F_BAD_POLICY),
+                          ref["flags"][ok] & (DATA_FLAGS | O.F_RESID_ZERO | O.F_BAD_POLICY))
+    return int(flagged.sum())
+
+
+# ------------------------------------------------------------------ tiny ----
+@pytest.mark.parametrize("mode", ["greedy", "sampled"])
+def test_markov_tiny(mode):
+    inp = decode_inputs("tiny", mode=mode)
+    ref = O.markov_sample(inp)
+    got = G.markov(inp)
+    assert check_markov(inp, got, ref) >= inp["B"] * inp["gamma"] - 2
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sampled"])
+def test_verify_tiny(mode):
+    inp = decode_inputs("tiny", mode=mode)
+    mk = O.markov_sample(inp)
+    q = G.q_of(mk) if mode == "sampled" else None
+    ref = O.verify(inp, mk["draft_tokens"], **(q or {}))
+    got = G.verify(inp, mk["draft_tokens"], q)
+    assert check_verify(got, ref) == 0
+
+
+def test_stats_tiny_f32_and_bf16_masked():
+    for dtype, mask in [("f32", 0), ("bf16", 3)]:
+        si = stats_inputs(dict(seed=11, N=9, gamma=5, V=1024, dtype=dtype, draft_std=2.0,
+                               noise_std=0.5), mask_every=mask)
+        ref = O.accept_stats(si)
+        got = G.stats(si)
+        for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
+            assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
+        assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
+
+
+# --------------------------------------------------------- decode, full V ----
+@pytest.fixture(scope="module")
+def decode_full():
+    inp = decode_inputs("decode")
+    return inp
+
+
+def test_markov_decode_full_size(decode_full):
+    inp = decode_full
+    got = G.markov(inp)
+    reqs = [0, 37, 63]
+    sub = decode_inputs("decode", requests=reqs, with_embed=False)
+    sub["embed"] = inp["embed"]
+    ref = O.markov_sample(sub)
+    gsub = {k: v[reqs] for k, v in got.items()}
+    assert check_markov(sub, gsub, ref) >= len(reqs) * inp["gamma"] - 1
+    # every request: tokens in range, q normalised at the drawn token, flags clean
+    assert np.all((got["draft_tokens"] >= 0) & (got["draft_tokens"] < inp["V"]))
+    assert np.all((got["q_tok"] > 0) & (got["q_tok"] <= 1))
+    assert np.all((got["flags"] & DATA_FLAGS) == 0)
+
+
+def test_verify_decode_full_size(decode_full):
+    inp = decode_full
+    mk = O.markov_sample(inp)  # all 64 requests: the proposals come from the oracle
+    q = G.q_of(mk)
+    ref = O.verify(inp, mk["draft_tokens"], **q)
+    got = G.verify(inp, mk["draft_tokens"], q)
+    assert check_verify(got, ref) <= 1
+    rate = ref["accept_len"].mean() / inp["gamma"]
+    assert 0.2 < rate < 0.95
+
+
+def test_verify_wide_greedy_full_size():
+    inp = decode_inputs("wide_greedy", with_embed=False)
+    from workloads import bf16_to_f32
+
+    # proposals: the draft rows' own argmax (input preparation, not the method)
+    draft = bf16_to_f32(inp["backbone"]).argmax(-1).astype(np.int32)
+    ref = O.verify(inp, draft)
+    got = G.verify(inp, draft)
+    assert check_verify(got, ref) == 0
+    emitted = (got["out_tokens"] >= 0).sum(1)
+    assert np.all((emitted >= 1) & (emitted <= 8))
+
+
+def test_stats_full_vocab():
+    si = stats_inputs(blocks=list(range(16)), mask_every=8)
+    ref = O.accept_stats(si)
+    got = G.stats(si)
+    for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
+        assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
+    assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
+
+
+# ---------------------------------------------------------- flag rate -------
+def test_flag_rate_many_draws():
+    """Sampled Markov + verify over ~1e5 draws on the tiny shape: unflagged
+    draws bit-exact, flagged share below 1e-4."""
+    inp = decode_inputs("tiny", B=8192, mode="sampled", with_embed=True)
+    ref = O.markov_sample(inp)
+    got = G.markov(inp)
+    check_markov(inp, got, ref)
+    vref = O.verify(inp, ref["draft_tokens"], **G.q_of(ref))
+    vgot = G.verify(inp, ref["draft_tokens"], G.q_of(ref))
+    check_verify(vgot, vref)
+    draws = inp["B"] * inp["gamma"] + int((vref["accept_len"] + 1).sum())
+    flagged = int(((ref["flags"] & O.F_NEAR) != 0).sum() + ((vref["flags"] & O.F_NEAR) != 0).sum())
+    assert draws > 60000
+    assert flagged / draws < 1e-4
+
+
+# ---------------------------------------------------------- edge cases ------
+def test_empty_batch():
+    import dspark_draft_sampling_amd as ds
+
+    inp = decode_inputs("tiny", B=0, with_embed=True)
+    out = G.verify(inp, np.zeros((0, inp["gamma"]), np.int32))
+    assert out["accept_len"].shape == (0,)
+    si = stats_case(np.zeros((0, 3, 16), np.float32), np.zeros((0, 3, 16), np.float32))
+    got = G.stats(si)
+    assert np.all(got["sums"] == 0)
+    assert ds.dspark_workspace_size(ds.DSPARK_OP_VERIFY, 0, 5, 1024) >= 0
+
+
+@pytest.mark.parametrize("V,dtype,B", [(999, "f32", 5), (1000, "bf16", 70), (1, "f32", 2)])
+def test_ragged_shapes(V, dtype, B):
+    cfg = dict(seed=77, B=B, gamma=3, V=V, r=16, d=24, dtype=dtype, draft_std=2.0,
+               noise_std=0.5, w_std=0.3, mode="mixed")
+    inp = decode_inputs(cfg)
+    ref = O.markov_sample(inp)
+    got = G.markov(inp)
+    check_markov(inp, got, ref)
+    vref = O.verify(inp, ref["draft_tokens"], **G.q_of(ref))
+    vgot = G.verify(inp, ref["draft_tokens"], G.q_of(ref))
+    assert check_verify(vgot, vref) <= 1
+
+
+def test_n_draft_and_bad_rows():
+    rng = np.random.default_rng(5)
+    B, g, V = 6, 4, 700
+    tgt = rng.normal(0, 2, (B, g + 1, V)).astype(np.float32)
+    tgt[1, 2, 10] = np.nan         # request 1: NaN in row 2
+    tgt[2, 0, :] = -np.inf         # request 2: empty row 0
+    tgt[3, 1, 5] = np.inf          # request 3: +inf in row 1
+    tgt[4, :, 7] = 50.0            # request 4: a clear argmax
+    inp = decode_case(None, tgt, B=B, gamma=g, V=V, mode=[0, 0, 0, 1, 0, 1])
+    draft = rng.integers(0, V, (B, g)).astype(np.int32)
+    draft[4] = 7
+    n_draft = np.array([4, 3, 2, 4, 1, 0], np.int32)
+    kq, zq, lq, tq, _ = O.policy_row(np.zeros(V), 1.0, 0, 1.0)
+    q = dict(q_z=np.zeros((B, g, V), np.float32), q_lse=np.full((B, g), lq, np.float32),
+             q_thr=np.full((B, g), -np.inf, np.float32), q_tok=np.full((B, g), 1.0 / V, np.float32))
+    ref = O.verify(inp, draft, n_draft=n_draft, **q)
+    got = G.verify(inp, draft, q, n_draft=n_draft)
+    assert np.array_equal(got["flags"] & DATA_FLAGS, ref["flags"] & DATA_FLAGS)
+    clean = [0, 4, 5]  # requests without a bad row
+    assert np.array_equal(got["accept_len"][clean], ref["accept_len"][clean])
+    assert np.array_equal(got["out_tokens"][clean], ref["out_tokens"][clean])
+    assert got["accept_len"][4] == 1 and got["out_tokens"][4, 1] == 7
+
+
+def test_greedy_ties_lowest_index():
+    V = 20000  # three row slices in the fp32 vector path
+    tgt = np.zeros((2, 3, V), np.float32)
+    tgt[:, :, [17000, 9000, 3000, 17]] = 5.0  # equal maxima in different slices
+    inp = decode_case(None, tgt, B=2, gamma=2, V=V, mode=0)
+    got = G.verify(inp, np.array([[17, 17], [3000, 17]], np.int32))
+    assert list(got["out_tokens"][0]) == [17, 17, 17]
+    assert list(got["out_tokens"][1]) == [17, -1, -1]

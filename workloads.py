@@ -21,6 +21,9 @@ available.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 __all__ = [
@@ -119,7 +122,8 @@ def decode_inputs(name_or_cfg="tiny", requests=None, with_embed=True, **override
     temperature = np.empty(n, np.float32)
     top_k = np.empty(n, np.int32)
     top_p = np.empty(n, np.float32)
-    for i, b in enumerate(reqs):
+    def one(i):
+        b = reqs[i]
         draft = _rng(s, 1, b).standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(cfg["draft_std"])
         tgt = draft + _rng(s, 2, b).standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(cfg["noise_std"])
         if cfg.get("zipf"):
@@ -134,6 +138,9 @@ def decode_inputs(name_or_cfg="tiny", requests=None, with_embed=True, **override
         hidden[i] = to_bf16(_rng(s, 3, b).standard_normal((gamma, d), dtype=np.float32))
         anchor[i] = _rng(s, 4, b).integers(0, V)
         mode[i], temperature[i], top_k[i], top_p[i] = _policy(cfg, b)
+
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(one, range(n)))
     out = dict(
         backbone=backbone, target=target, anchor=anchor, hidden=hidden,
         w1=to_bf16(_rng(s, 10).standard_normal((V, r), dtype=np.float32) * np.float32(cfg["w_std"])),
@@ -151,16 +158,27 @@ def decode_inputs(name_or_cfg="tiny", requests=None, with_embed=True, **override
 
 
 def embed_table(cfg) -> np.ndarray:
-    """Shared token embedding [V, d] bf16 of a decode config."""
+    """Shared token embedding [V, d] bf16 of a decode config.
+
+    Rows are drawn in blocks of 1024, block j from its own stream (config seed,
+    12, j), so the table is the same whatever the number of worker threads."""
     cfg = dict(DECODE_CONFIGS[cfg]) if isinstance(cfg, str) else cfg
     V, d = cfg["V"], cfg["d"]
     out = np.empty((V, d), np.uint16)
-    g = _rng(cfg["seed"], 12)
-    step = max(1, (1 << 24) // max(d, 1))
-    for lo in range(0, V, step):
-        hi = min(V, lo + step)
-        out[lo:hi] = to_bf16(g.standard_normal((hi - lo, d), dtype=np.float32))
+    rows = 1024
+
+    def fill(j):
+        lo, hi = j * rows, min(V, (j + 1) * rows)
+        out[lo:hi] = to_bf16(_rng(cfg["seed"], 12, j).standard_normal((hi - lo, d), dtype=np.float32))
+
+    nblk = (V + rows - 1) // rows
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(fill, range(nblk)))
     return out
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def stats_inputs(cfg=None, blocks=None, mask_every=0, **overrides) -> dict:
@@ -182,7 +200,8 @@ def stats_inputs(cfg=None, blocks=None, mask_every=0, **overrides) -> dict:
     target = np.empty((n, gamma, V), edt)
     teacher = np.empty((n, gamma), np.int32)
     conf = np.empty((n, gamma), np.float32)
-    for i, b in enumerate(blks):
+    def one(i):
+        b = blks[i]
         dr = _rng(s, 1, b).standard_normal((gamma, V), dtype=np.float32) * np.float32(cfg["draft_std"])
         tg = dr + _rng(s, 2, b).standard_normal((gamma, V), dtype=np.float32) * np.float32(cfg["noise_std"])
         if bf:
@@ -194,6 +213,9 @@ def stats_inputs(cfg=None, blocks=None, mask_every=0, **overrides) -> dict:
             target[i] = tg
             teacher[i] = np.argmax(tg, axis=1)
         conf[i] = _rng(s, 4, b).standard_normal(gamma, dtype=np.float32)
+
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(one, range(n)))
     mask = np.ones(n, np.uint8)
     if mask_every > 0:
         mask[np.asarray(blks) % mask_every == mask_every - 1] = 0
