@@ -40,7 +40,23 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device copy of MIB MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for counter calibration."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes_read=n * 4, copy_bytes_written=n * 4, launches=3)), flush=True)
 
 
 def kernel_bytes(name, B, g, V, r, d, S, R):
@@ -63,6 +79,9 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the sharding design is described in DESIGN.md)", file=sys.stderr)
