@@ -89,20 +89,46 @@ __device__ __forceinline__ bool near_gap(float best, float second) {
 }
 
 // ---- wave64 reductions --------------------------------------------------------
+// Butterfly inside each row of 16 lanes with DPP (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror), then the four row results
+// are read with v_readlane and combined in a fixed order, so every lane gets
+// the same, deterministic result.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
+  int x = static_cast<int>(v);
+  x |= dpp_i<kDppXor1>(x);
+  x |= dpp_i<kDppXor2>(x);
+  x |= dpp_i<kDppHalfMirror>(x);
+  x |= dpp_i<kDppMirror>(x);
+  return static_cast<uint32_t>(lane_i(x, 0) | lane_i(x, 16) | lane_i(x, 32) | lane_i(x, 48));
 }
 
 // (value, index) maximum: larger value wins, the lower index on equal values.
@@ -114,13 +140,20 @@ struct ArgMax {
 __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
   return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
 }
+template <int CTRL>
+__device__ __forceinline__ ArgMax dpp_step(ArgMax a) {
+  return better(a, ArgMax{dpp_f<CTRL>(a.v), dpp_i<CTRL>(a.i)});
+}
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ArgMax b{__shfl_xor(a.v, o, 64), __shfl_xor(a.i, o, 64)};
-    a = better(a, b);
-  }
-  return a;
+  a = dpp_step<kDppXor1>(a);
+  a = dpp_step<kDppXor2>(a);
+  a = dpp_step<kDppHalfMirror>(a);
+  a = dpp_step<kDppMirror>(a);
+  ArgMax r{lane_f(a.v, 0), lane_i(a.i, 0)};
+  r = better(r, ArgMax{lane_f(a.v, 16), lane_i(a.i, 16)});
+  r = better(r, ArgMax{lane_f(a.v, 32), lane_i(a.i, 32)});
+  r = better(r, ArgMax{lane_f(a.v, 48), lane_i(a.i, 48)});
+  return r;
 }
 
 // Top-2 scores with the argmax: (best, index, second best).
@@ -142,13 +175,48 @@ __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
   }
   return r;
 }
+template <int CTRL>
+__device__ __forceinline__ Top2 dpp_step(Top2 a) {
+  return top2_merge(a, Top2{dpp_f<CTRL>(a.v1), dpp_i<CTRL>(a.i1), dpp_f<CTRL>(a.v2)});
+}
 __device__ __forceinline__ Top2 wave_top2(Top2 a) {
+  a = dpp_step<kDppXor1>(a);
+  a = dpp_step<kDppXor2>(a);
+  a = dpp_step<kDppHalfMirror>(a);
+  a = dpp_step<kDppMirror>(a);
+  Top2 r{lane_f(a.v1, 0), lane_i(a.i1, 0), lane_f(a.v2, 0)};
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Top2 b{__shfl_xor(a.v1, o, 64), __shfl_xor(a.i1, o, 64), __shfl_xor(a.v2, o, 64)};
-    a = top2_merge(a, b);
-  }
-  return a;
+  for (int l = 16; l < 64; l += 16) r = top2_merge(r, Top2{lane_f(a.v1, l), lane_i(a.i1, l), lane_f(a.v2, l)});
+  return r;
+}
+
+// Cross-workgroup hand-off without whole-cache maintenance: values are written
+// through to the device-coherent level (agent-scope relaxed atomic stores, sc1)
+// and read from it (agent-scope relaxed atomic loads); publish() waits for the
+// writer's stores to complete before its ticket increment is issued.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait for every outstanding memory operation of this wave (s_waitcnt 0),
+// then increment the ticket; returns the ticket's previous value.
+__device__ __forceinline__ uint32_t publish(uint32_t* ticket) {
+  __builtin_amdgcn_s_waitcnt(0);
+  return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge of log-sum-exp partials (m, s) meaning s * exp(m): returns the pair

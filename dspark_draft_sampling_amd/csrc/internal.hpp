@@ -2,6 +2,7 @@
 // workspace layout and the per-operation launchers behind the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -36,20 +37,34 @@ struct ChunkPart {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Brackets one kernel launch with HIP events while profiling is enabled
-// (dspark_profile_enable); a no-op otherwise.
+// Holds the start / stop events of one kernel launch while profiling is
+// enabled (dspark_profile_enable); inactive otherwise.  The launch records the
+// events at the kernel's own start and end (hipExtLaunchKernelGGL).
 class ProfScope {
  public:
-  ProfScope(const char* name, hipStream_t st);
+  explicit ProfScope(const char* name);
   ~ProfScope();
   ProfScope(const ProfScope&) = delete;
   ProfScope& operator=(const ProfScope&) = delete;
+  bool active() const { return a_ != nullptr; }
+  hipEvent_t start() const { return a_; }
+  hipEvent_t stop() const { return b_; }
 
  private:
   const char* name_;
-  hipStream_t st_;
-  hipEvent_t a_;
+  hipEvent_t a_, b_;
 };
+
+// Launch `kernel` (parenthesise template kernels) and, while profiling, time it.
+#define DSPARK_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                         \
+  do {                                                                                      \
+    ::dspark::ProfScope dspark_ps_(name);                                                   \
+    if (dspark_ps_.active())                                                                \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, dspark_ps_.start(),         \
+                            dspark_ps_.stop(), 0, __VA_ARGS__);                             \
+    else                                                                                    \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                  \
+  } while (0)
 
 // Vocabulary slicing of the verify row pass.
 struct VerifyPlan {

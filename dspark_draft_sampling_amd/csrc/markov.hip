@@ -349,26 +349,20 @@ hipError_t launch_typed(const T* backbone, const int32_t* anchor, const uint16_t
   for (int k = 1; k <= gamma; ++k) {
     const int32_t* xp = k == 1 ? anchor : draft_tokens + (k - 2);
     const int32_t xs = k == 1 ? 1 : gamma;
-    {
-    ProfScope ps("markov_step", st);
     if (vec)
-      hipLaunchKernelGGL((markov_step_kernel<T, true>), g_step, dim3(kStepThreads), 0, st,
-                         backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
-                         pl.C, q_z, part);
+      DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, true>), g_step, dim3(kStepThreads), 0,
+                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
+                    pl.C, q_z, part);
     else
-      hipLaunchKernelGGL((markov_step_kernel<T, false>), g_step, dim3(kStepThreads), 0, st,
-                         backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
-                         pl.C, q_z, part);
-    }
+      DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, false>), g_step, dim3(kStepThreads), 0,
+                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
+                    pl.C, q_z, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    {
-    ProfScope ps("markov_finalize", st);
-    hipLaunchKernelGGL(markov_finalize_kernel, dim3(B), dim3(kFinThreads), 0, st, xp, xs, hidden,
-                       embed, conf_w, pol.mode, pol.temperature, pol.request_id, pol.position,
-                       seed, gamma, k, V, d, pl.C, part, q_z, draft_tokens, q_lse, q_thr, q_tok,
-                       confidence, flags);
-    }
+    DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel, dim3(B), dim3(kFinThreads), 0, st, xp,
+                  xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
+                  pol.position, seed, gamma, k, V, d, pl.C, part, q_z, draft_tokens, q_lse, q_thr,
+                  q_tok, confidence, flags);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,7 +1,8 @@
 // profile.hip — opt-in per-kernel timing with HIP events.
 //
-// When enabled, every kernel launch of the library is bracketed by two events
-// recorded on the launch stream; dspark_profile_summary synchronises them and
+// When enabled, every kernel launch of the library records two events at the
+// kernel's own start and end (hipExtLaunchKernelGGL); dspark_profile_summary
+// synchronises them and
 // reports, per kernel name, the launch count and the summed duration.  This is
 // the only process-wide state of the library and it is off by default.
 #include <hip/hip_runtime.h>
@@ -31,25 +32,23 @@ std::vector<Rec> g_recs;
 
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t st) : name_(name), st_(st), a_(nullptr) {
+ProfScope::ProfScope(const char* name) : name_(name), a_(nullptr), b_(nullptr) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   if (hipEventCreate(&a_) != hipSuccess) {
     a_ = nullptr;
     return;
   }
-  (void)hipEventRecord(a_, st_);
+  if (hipEventCreate(&b_) != hipSuccess) {
+    (void)hipEventDestroy(a_);
+    a_ = nullptr;
+    b_ = nullptr;
+  }
 }
 
 ProfScope::~ProfScope() {
   if (!a_) return;
-  hipEvent_t b = nullptr;
-  if (hipEventCreate(&b) != hipSuccess) {
-    (void)hipEventDestroy(a_);
-    return;
-  }
-  (void)hipEventRecord(b, st_);
   std::lock_guard<std::mutex> lk(g_mu);
-  g_recs.push_back(Rec{name_, a_, b});
+  g_recs.push_back(Rec{name_, a_, b_});
 }
 
 }  // namespace dspark

@@ -223,22 +223,18 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
   const bool vec = (V % epl == 0) && reinterpret_cast<uintptr_t>(draft) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(target) % 16 == 0;
   const dim3 grid(static_cast<unsigned>(static_cast<size_t>(N) * gamma));
-  {
-  ProfScope ps("stats_rows", st);
-  if (N == 0) {
-    // no rows: the reduction still writes the (zero) sums
-  } else if (vec)
-    hipLaunchKernelGGL((stats_rows_kernel<T, true>), grid, dim3(kThreads), 0, st, draft, target,
-                       teacher, conf_logits, V, l1, accept_rate, ce, bce);
-  else
-    hipLaunchKernelGGL((stats_rows_kernel<T, false>), grid, dim3(kThreads), 0, st, draft, target,
-                       teacher, conf_logits, V, l1, accept_rate, ce, bce);
+  if (N > 0) {
+    if (vec)
+      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, true>), grid, dim3(kThreads), 0, st, draft,
+                    target, teacher, conf_logits, V, l1, accept_rate, ce, bce);
+    else
+      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, false>), grid, dim3(kThreads), 0, st,
+                    draft, target, teacher, conf_logits, V, l1, accept_rate, ce, bce);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ProfScope ps("stats_reduce", st);
-  hipLaunchKernelGGL(stats_reduce_kernel, dim3(1), dim3(kThreads), 0, st, l1, accept_rate, ce, bce,
-                     block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums);
+  DSPARK_LAUNCH("stats_reduce", stats_reduce_kernel, dim3(1), dim3(kThreads), 0, st, l1,
+                accept_rate, ce, bce, block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums);
   return hipGetLastError();
 }
 

@@ -9,15 +9,22 @@
 // distribution when every proposal survives.  Target row k - 1 verifies x_k.
 //
 // Two launches:
-//  1. verify_rows   grid (row slices, B (gamma+1) rows).  Each workgroup pulls
-//     one slice of one target row into registers with 16-byte loads, then
-//     reduces max / lowest argmax / sum exp((l - max) / T) over it.
+//  1. verify_rows   grid (row segments / 4, B (gamma+1) rows), 4 waves.  Each
+//     wave pulls one 2048-token segment of one target row into registers with
+//     16-byte loads and reduces it to (max, lowest argmax, sum) with wave
+//     shuffles only: no LDS, no barrier.
 //  2. verify_decide grid (chunk slices, B).  Every workgroup of a request
-//     combines the row partials and replays the (cheap, deterministic) accept
-//     scan, so all of them agree on the row to sample from.  Each then scores
-//     its slice of 256-token chunks for the two-level Gumbel-max draw; the last
-//     workgroup to finish (atomic ticket) picks the chunk and the token inside
-//     it and writes the outputs.  The tickets are armed by the first launch.
+//     combines the segment partials of its rows and replays the accept scan
+//     (one thread per proposal, first reject by ballot), so all of them agree
+//     on the row to sample from.  Each then scores its slice of 256-token
+//     chunks for the two-level Gumbel-max draw; the last workgroup to finish
+//     (atomic ticket, armed by launch 1) picks the chunk and the token inside
+//     it and writes the outputs.
+//
+// Sums use an integer base-2 shift: s = sum 2^(l cT - M2), cT = log2(e) / T,
+// M2 = floor(max(l) cT).  Partials with different shifts combine by exact
+// powers of two, and p(x) = 2^(l_x cT - M2) / s uses the very expression each
+// term of s used.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -26,167 +33,197 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kVecIters = 8;      // 16-byte loads per thread per row slice
-constexpr int kScalarIters = 32;  // scalar loads per thread per row slice
-constexpr int kMaxSlices2 = 8;    // chunk slices per request in the decide pass
+constexpr int kVecIters = 4;       // 16-byte loads per lane per segment
+constexpr int kScalarIters = 32;   // scalar loads per lane per segment
+constexpr int kChunksPerWave = 8;  // chunks one wave scores in the decide pass
+constexpr int kChunksPerWG = kChunksPerWave * kWaves;
 
+// One 16-byte load per lane per iteration (vector path: 8 bf16 or 4 fp32
+// logits kept packed in a uint4), or one scalar logit (scalar path).  Lanes
+// past the row end hold -inf.
 template <typename T, bool VEC>
 struct RowLoad;
 
-template <>
-struct RowLoad<uint16_t, true> {
-  static constexpr int EPL = 8;
-  __device__ static void load(const uint16_t* row, int e, int hi, float* o) {
-    if (e < hi) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + e);
-      o[0] = bf_lo(u.x);
-      o[1] = bf_hi(u.x);
-      o[2] = bf_lo(u.y);
-      o[3] = bf_hi(u.y);
-      o[4] = bf_lo(u.z);
-      o[5] = bf_hi(u.z);
-      o[6] = bf_lo(u.w);
-      o[7] = bf_hi(u.w);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = neg_inf();
-    }
-  }
-};
-
-template <>
-struct RowLoad<float, true> {
-  static constexpr int EPL = 4;
-  __device__ static void load(const float* row, int e, int hi, float* o) {
-    if (e < hi) {
-      const float4 u = *reinterpret_cast<const float4*>(row + e);
-      o[0] = u.x;
-      o[1] = u.y;
-      o[2] = u.z;
-      o[3] = u.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = neg_inf();
-    }
-  }
+template <typename T>
+struct RowLoad<T, true> {
+  using Raw = uint4;
+  static constexpr int EPL = 16 / sizeof(T);
+  static constexpr uint32_t kNegInfBits = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
+  __device__ static Raw load(const T* row, int e) { return *reinterpret_cast<const uint4*>(row + e); }
+  __device__ static Raw neg() { return make_uint4(kNegInfBits, kNegInfBits, kNegInfBits, kNegInfBits); }
 };
 
 template <typename T>
 struct RowLoad<T, false> {
+  using Raw = float;
   static constexpr int EPL = 1;
-  __device__ static void load(const T* row, int e, int hi, float* o) {
-    o[0] = e < hi ? load_logit(row, e) : neg_inf();
-  }
+  __device__ static Raw load(const T* row, int e) { return load_logit(row, e); }
+  __device__ static Raw neg() { return neg_inf(); }
 };
+
+// element j of a packed vector
+__device__ __forceinline__ float elem(const uint4& u, int j, uint16_t) {
+  const uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
+  return (j & 1) ? bf_hi(w) : bf_lo(w);
+}
+__device__ __forceinline__ float elem(const uint4& u, int j, float) {
+  return __uint_as_float(j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w);
+}
+__device__ __forceinline__ float elem(float x, int, uint16_t) { return x; }
+__device__ __forceinline__ float elem(float x, int, float) { return x; }
+
+template <typename T, bool VEC>
+constexpr int seg_len() {
+  return (VEC ? kVecIters : kScalarIters) * 64 * RowLoad<T, VEC>::EPL;
+}
 
 __device__ __forceinline__ int32_t n_draft_of(const int32_t* n_draft, int b, int gamma) {
   int nd = n_draft ? n_draft[b] : gamma;
   return nd < 0 ? 0 : (nd > gamma ? gamma : nd);
 }
 
+// integer base-2 shift of a row (or segment) whose largest logit is m
+__device__ __forceinline__ float shift_of(float m, float cT) { return floorf(m * cT); }
+
 // ---------------------------------------------------------------------------
-// Pass 1: per (row, slice) max, lowest argmax and sum of exp((l - max) / T).
+// Pass 1: per (row, segment) max, lowest argmax and sum 2^(l cT - M2).
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
-    const T* __restrict__ target, int32_t V, int32_t gamma, int32_t slice_len, int32_t S,
+    const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P,
     const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
     const int32_t* __restrict__ n_draft, RowPart* __restrict__ part,
     uint32_t* __restrict__ counters, int32_t B) {
   using L = RowLoad<T, VEC>;
   constexpr int ITERS = VEC ? kVecIters : kScalarIters;
   constexpr int EPL = L::EPL;
-  constexpr int N = ITERS * EPL;
-  __shared__ float shv[kWaves];
-  __shared__ int32_t shi[kWaves];
-  __shared__ uint32_t shu[kWaves];
+  constexpr int SEG = seg_len<T, VEC>();
 
   const int G1 = gamma + 1;
-  const int s = blockIdx.x, row = blockIdx.y;
+  const int row = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * kWaves + (threadIdx.x >> 6);
   // arm the per-request tickets of the decide pass (which starts after this
   // launch completes on the same stream)
-  if (s == 0 && row == 0)
+  if (blockIdx.x == 0 && row == 0)
     for (int i = threadIdx.x; i < B; i += kThreads) counters[i] = 0u;
   const int b = row / G1, k = row - b * G1;
-  if (k > n_draft_of(n_draft, b, gamma)) return;  // never consulted
+  if (seg >= P || k > n_draft_of(n_draft, b, gamma)) return;  // wave-uniform
   const T* rp = target + static_cast<size_t>(row) * V;
-  const int lo = s * slice_len;
-  const int hi = min(V, lo + slice_len);
+  const int lo = seg * SEG;
+  const int hi = min(V, lo + SEG);
 
-  float v[N];
+  typename L::Raw u[ITERS];
+  if (hi - lo == SEG) {  // full segment: no bounds checks
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it)
-    L::load(rp, lo + (it * kThreads + static_cast<int>(threadIdx.x)) * EPL, hi, v + it * EPL);
+    for (int it = 0; it < ITERS; ++it) u[it] = L::load(rp, lo + (it * 64 + lane) * EPL);
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int e = lo + (it * 64 + lane) * EPL;
+      u[it] = e < hi ? L::load(rp, e) : L::neg();
+    }
+  }
 
   const float Tb = temperature[b];
   const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
-
+  uint32_t fl = 0;
   float m = neg_inf();
   int32_t arg = INT32_MAX;
-  uint32_t nan = 0;
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float x = v[it * EPL + e];
-      if (x > m) {
-        m = x;
-        arg = lo + (it * kThreads + static_cast<int>(threadIdx.x)) * EPL + e;
-      }
-      if (!sampled) nan |= (x != x) ? 1u : 0u;
-    }
-  }
-  const ArgMax am = block_argmax<kWaves>(ArgMax{m, arg}, shv, shi);
-
   float sum = 0.0f;
-  if (sampled && am.v > neg_inf()) {
-    const float cT = kLog2e / Tb;
+  if (!sampled) {
+    uint32_t nan = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) sum += __builtin_amdgcn_exp2f((v[j] - am.v) * cT);
-    sum = block_sum<kWaves>(sum, shv);
+    for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = elem(u[it], e, T{});
+        if (x > m) {
+          m = x;
+          arg = lo + (it * 64 + lane) * EPL + e;
+        }
+        nan |= (x != x) ? 1u : 0u;
+      }
+    }
+    const ArgMax am = wave_argmax(ArgMax{m, arg});
+    m = am.v;
+    arg = am.i;
+    if (wave_or(nan) || m == pos_inf()) fl |= DSPARK_FLAG_NONFINITE;
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m = fmaxf(m, elem(u[it], e, T{}));
+    m = wave_max(m);
+    if (m > neg_inf()) {
+      const float cT = kLog2e / Tb;
+      const float M2 = shift_of(m, cT);
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          sum += __builtin_amdgcn_exp2f(fmaf(elem(u[it], e, T{}), cT, -M2));
+      sum = wave_sum(sum);
+    }
+    if (m == pos_inf() || !(sum < pos_inf())) fl |= DSPARK_FLAG_NONFINITE;
   }
-  if (!sampled) nan = block_or<kWaves>(nan, shu);
-  if (threadIdx.x == 0) {
-    uint32_t fl = 0;
-    if (nan || am.v == pos_inf() || (sampled && !(sum < pos_inf()))) fl |= DSPARK_FLAG_NONFINITE;
-    part[static_cast<size_t>(row) * S + s] = RowPart{am.v, sum, am.i, fl};
-  }
+  if (lane == 0) part[static_cast<size_t>(row) * P + seg] = RowPart{m, sum, arg, fl};
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: decision, chunk scores of the residual / bonus draw, final pick.
 struct Decision {
-  int kind;      // 0 greedy, 1 residual at j, 2 bonus
-  int n;         // accepted proposals
-  int srow;      // target row sampled from (kind 1, 2)
-  int qrow;      // proposal row of the residual (kind 1)
-  uint32_t near; // bit k: NEAR on target row k
-  int32_t token; // greedy: the emitted target token
+  int kind;       // 0 greedy, 1 residual at j, 2 bonus
+  int n;          // accepted proposals
+  int srow;       // target row sampled from (kind 1, 2)
+  uint32_t near;  // bit k: NEAR on target row k
+  int32_t token;  // greedy: the emitted target token
 };
 
-template <typename T>
-__device__ __forceinline__ float draw_weight(int kind, const T* trow, const float* qrow, int v,
-                                             float m, float cT, float inv_s, float lse_q,
-                                             float thr_q) {
-  const float l = load_logit(trow, v);
-  const float e = __builtin_amdgcn_exp2f((l - m) * cT);
+__device__ __forceinline__ float draw_weight(int kind, float l, float zq, float cT, float M2,
+                                             float inv_s, float lse_q, float thr_q) {
+  if (!(l > neg_inf())) return 0.0f;
+  const float e = __builtin_amdgcn_exp2f(fmaf(l, cT, -M2));
   if (kind != 1) return e;  // bonus / fallback: unnormalised p
-  const float zq = qrow[v];
-  const float q = (zq >= thr_q && zq > neg_inf()) ? __builtin_amdgcn_exp2f((zq - lse_q) * kLog2e) : 0.0f;
+  const float q =
+      (zq >= thr_q && zq > neg_inf()) ? __builtin_amdgcn_exp2f((zq - lse_q) * kLog2e) : 0.0f;
   return fmaxf(e * inv_s - q, 0.0f);
 }
 
-template <typename T>
+// Four consecutive logits v0..v0+3 (v0 a multiple of 4) of a row, -inf past V.
+template <typename T, bool VEC4>
+__device__ __forceinline__ void load4(const T* row, int v0, int V, float* o) {
+  if (VEC4 && v0 + 3 < V) {
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(row + v0);
+      o[0] = bf_lo(u.x);
+      o[1] = bf_hi(u.x);
+      o[2] = bf_lo(u.y);
+      o[3] = bf_hi(u.y);
+    } else {
+      const float4 u = *reinterpret_cast<const float4*>(row + v0);
+      o[0] = u.x;
+      o[1] = u.y;
+      o[2] = u.z;
+      o[3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? load_logit(row, v0 + e) : neg_inf();
+  }
+}
+
+template <typename T, bool VEC4>
 __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     const T* __restrict__ target, const int32_t* __restrict__ draft,
     const float* __restrict__ q_z, const float* __restrict__ q_lse,
     const float* __restrict__ q_thr, const float* __restrict__ q_tok,
     const int32_t* __restrict__ n_draft, const uint8_t* __restrict__ mode,
     const float* __restrict__ temperature, const uint32_t* __restrict__ request_id,
-    const int32_t* __restrict__ position, uint64_t seed, int32_t gamma, int32_t V, int32_t S,
-    int32_t S2, int32_t cps, const RowPart* __restrict__ part, Pick* __restrict__ picks,
+    const int32_t* __restrict__ position, uint64_t seed, int32_t gamma, int32_t V, int32_t P,
+    int32_t S2, const RowPart* __restrict__ part, Pick* __restrict__ picks,
     uint32_t* __restrict__ counters, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ out_tokens, uint8_t* __restrict__ flags) {
-  __shared__ float rm[DSPARK_MAX_GAMMA + 1], rs[DSPARK_MAX_GAMMA + 1];
+  __shared__ float rm[DSPARK_MAX_GAMMA + 1], rs[DSPARK_MAX_GAMMA + 1], rM2[DSPARK_MAX_GAMMA + 1];
   __shared__ int32_t rarg[DSPARK_MAX_GAMMA + 1];
   __shared__ uint32_t rfl[DSPARK_MAX_GAMMA + 1];
   __shared__ Decision dec;
@@ -204,168 +241,204 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   const bool sampled = want_sampled && q_z && q_lse && q_thr && q_tok;
   const float cT = sampled ? kLog2e / Tb : kLog2e;
   const int C = (V + kChunk - 1) / kChunk;
+  const uint32_t req = request_id[b];
+  const int32_t pos0 = position[b];
 
-  // 1. combine the row partials of rows 0..n_d
-  if (tid <= nd) {
-    const RowPart* p = part + static_cast<size_t>(b * G1 + tid) * S;
-    float m = neg_inf(), s = 0.0f;
-    int32_t arg = INT32_MAX;
-    uint32_t fl = 0;
-    for (int i = 0; i < S; ++i) {
-      const RowPart q = p[i];
-      fl |= q.flags;
-      const ArgMax a = better(ArgMax{m, arg}, ArgMax{q.m, q.arg});
-      if (sampled) {
-        if (q.m > m) {
-          s = s * __builtin_amdgcn_exp2f((m - q.m) * cT) + q.s;
-        } else if (q.m > neg_inf()) {
-          s += q.s * __builtin_amdgcn_exp2f((q.m - m) * cT);
-        }
-      }
-      m = a.v;
-      arg = a.i;
+  // proposal-side values of the accept scan, fetched up front (thread k-1
+  // owns proposal k)
+  int32_t xk = 0;
+  float lx = neg_inf(), qk = 0.0f;
+  if (tid < nd) {
+    xk = clamp_token(draft[b * gamma + tid], V);
+    if (sampled) {
+      lx = load_logit(target, static_cast<size_t>(b * G1 + tid) * V + xk);
+      qk = q_tok[b * gamma + tid];
     }
-    if (!(m > neg_inf())) fl |= DSPARK_FLAG_EMPTY_ROW;
-    rm[tid] = m;
-    rs[tid] = s;
-    rarg[tid] = arg;
-    rfl[tid] = fl;
+  }
+
+  // 1. combine the segment partials of rows 0..n_d (wave w: rows w, w+4, ...)
+  for (int r = wave; r <= nd; r += kWaves) {
+    const RowPart* p = part + static_cast<size_t>(b * G1 + r) * P;
+    ArgMax am{neg_inf(), INT32_MAX};
+    uint32_t fl = 0;
+    for (int i = lane; i < P; i += 64) {
+      const RowPart q = p[i];
+      am = better(am, ArgMax{q.m, q.arg});
+      fl |= q.flags;
+    }
+    am = wave_argmax(am);
+    fl = wave_or(fl);
+    const float M2 = (am.v > neg_inf() && am.v < pos_inf()) ? shift_of(am.v, cT) : 0.0f;
+    float s = 0.0f;
+    if (sampled && am.v > neg_inf()) {
+      for (int i = lane; i < P; i += 64) {
+        const RowPart q = p[i];
+        if (q.m > neg_inf()) s += q.s * __builtin_amdgcn_exp2f(shift_of(q.m, cT) - M2);
+      }
+      s = wave_sum(s);
+    }
+    if (lane == 0) {
+      if (!(am.v > neg_inf())) fl |= DSPARK_FLAG_EMPTY_ROW;
+      rm[r] = am.v;
+      rs[r] = s;
+      rM2[r] = M2;
+      rarg[r] = am.i;
+      rfl[r] = fl;
+    }
   }
   __syncthreads();
 
-  // 2. the decision (identical in every workgroup of the request)
-  if (tid == 0) {
-    Decision d{};
-    d.near = 0;
-    if (!sampled) {
-      int n = nd;
-      for (int k = 1; k <= nd; ++k) {
-        const int32_t x = clamp_token(draft[b * gamma + k - 1], V);
-        const int32_t t = rarg[k - 1] == INT32_MAX ? 0 : rarg[k - 1];
-        if (x != t) {
-          n = k - 1;
-          break;
-        }
-      }
-      d.kind = 0;
-      d.n = n;
-      d.token = rarg[n] == INT32_MAX ? 0 : rarg[n];
-    } else {
-      const uint32_t req = request_id[b];
-      const int32_t pos0 = position[b];
-      int j = 0;
-      for (int k = 1; k <= nd; ++k) {
-        const int32_t x = clamp_token(draft[b * gamma + k - 1], V);
-        const float lx = load_logit(target, static_cast<size_t>(b * G1 + k - 1) * V + x);
-        const float p = (lx > neg_inf() && rs[k - 1] > 0.0f)
-                            ? expf((lx - rm[k - 1]) / Tb) / rs[k - 1]
+  // 2. the decision (identical in every workgroup of the request), in wave 0
+  if (wave == 0) {
+    bool stop = false, near = false;
+    if (lane < nd) {
+      if (!sampled) {
+        const int32_t t = rarg[lane] == INT32_MAX ? 0 : rarg[lane];
+        stop = xk != t;
+      } else {
+        const float s = rs[lane];
+        const float p = (lx > neg_inf() && s > 0.0f)
+                            ? __builtin_amdgcn_exp2f(fmaf(lx, cT, -rM2[lane])) / s
                             : 0.0f;
-        const float q = q_tok[b * gamma + k - 1];
-        const float u = accept_uniform(seed, pos0 + k, req);
-        bool acc;
-        if (q > 0.0f) {
-          const float rho = p / q;
-          acc = u < rho;
-          if (fabsf(u - rho) <= kNearEps) d.near |= 1u << (k - 1);
+        const float u = accept_uniform(seed, pos0 + lane + 1, req);
+        if (qk > 0.0f) {
+          const float rho = p / qk;
+          stop = !(u < rho);
+          near = fabsf(u - rho) <= kNearEps;
         } else {
-          acc = p > 0.0f;
-        }
-        if (!acc) {
-          j = k;
-          break;
+          stop = !(p > 0.0f);
         }
       }
-      if (j > 0) {
+    }
+    const uint64_t stops = __ballot(stop);
+    const uint64_t nears = __ballot(near);
+    if (lane == 0) {
+      Decision d{};
+      const int j = stops ? __builtin_ctzll(stops) + 1 : 0;  // first reject, 1-based
+      // only accept tests that were reached (proposals 1..j) can be NEAR
+      const uint64_t reached = j ? ((1ull << j) - 1ull) : ~0ull;
+      d.near = static_cast<uint32_t>(nears & reached);
+      if (!sampled) {
+        d.kind = 0;
+        d.n = j ? j - 1 : nd;
+        d.token = rarg[d.n] == INT32_MAX ? 0 : rarg[d.n];
+        d.near = 0;
+      } else if (j) {
         d.kind = 1;
         d.n = j - 1;
         d.srow = j - 1;
-        d.qrow = j - 1;
       } else {
         d.kind = 2;
         d.n = nd;
         d.srow = nd;
-        d.qrow = 0;
       }
-      d.token = 0;
+      dec = d;
     }
-    dec = d;
   }
   __syncthreads();
   const Decision d = dec;
 
+  // threads 0..G1-1 write one row each
   auto write_outputs = [&](int32_t emitted, uint32_t extra_row_flags, int extra_row) {
-    // thread 0 only
-    int32_t* out = out_tokens + static_cast<size_t>(b) * G1;
-    for (int i = 0; i < G1; ++i) {
-      int32_t t = -1;
-      if (i < d.n) t = clamp_token(draft[b * gamma + i], V);
-      else if (i == d.n) t = emitted;
-      out[i] = t;
-      uint32_t fl = 0;
-      if (i <= nd) {
-        fl = rfl[i] & (DSPARK_FLAG_NONFINITE | DSPARK_FLAG_EMPTY_ROW);
-        if (d.near & (1u << i)) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
-        if (i == extra_row) fl |= extra_row_flags;
-      }
-      if (i == 0 && mode[b] != 0 && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
-      flags[static_cast<size_t>(b) * G1 + i] = static_cast<uint8_t>(fl);
+    const int i = tid;
+    if (i >= G1) return;
+    int32_t t = -1;
+    if (i < d.n) t = clamp_token(draft[b * gamma + i], V);
+    else if (i == d.n) t = emitted;
+    out_tokens[static_cast<size_t>(b) * G1 + i] = t;
+    uint32_t fl = 0;
+    if (i <= nd) {
+      fl = rfl[i] & (DSPARK_FLAG_NONFINITE | DSPARK_FLAG_EMPTY_ROW);
+      if (d.near & (1u << i)) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
+      if (i == extra_row) fl |= extra_row_flags;
     }
-    accept_len[b] = d.n;
+    if (i == 0 && mode[b] != 0 && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
+    flags[static_cast<size_t>(b) * G1 + i] = static_cast<uint8_t>(fl);
+    if (i == 0) accept_len[b] = d.n;
   };
 
   if (d.kind == 0) {
-    if (s2 == 0 && tid == 0) write_outputs(d.token, 0, -1);
+    if (s2 == 0) write_outputs(d.token, 0, -1);
     return;
   }
 
   // 3. chunk scores of this workgroup's chunk slice
-  const uint32_t req = request_id[b];
-  const int32_t pos = position[b] + (d.kind == 1 ? d.n + 1 : nd + 1);
+  const int32_t pos = pos0 + (d.kind == 1 ? d.n + 1 : nd + 1);
   const T* trow = target + static_cast<size_t>(b * G1 + d.srow) * V;
-  const float* qrow = d.kind == 1 ? q_z + static_cast<size_t>(b * gamma + d.qrow) * V : nullptr;
-  const float m = rm[d.srow];
+  const size_t qoff = static_cast<size_t>(b * gamma + d.srow) * V;  // q row j-1 (kind 1)
+  const float M2 = rM2[d.srow];
   const float inv_s = rs[d.srow] > 0.0f ? 1.0f / rs[d.srow] : 0.0f;
-  const float lse_q = d.kind == 1 ? q_lse[b * gamma + d.qrow] : 0.0f;
-  const float thr_q = d.kind == 1 ? q_thr[b * gamma + d.qrow] : 0.0f;
+  const float lse_q = d.kind == 1 ? q_lse[b * gamma + d.srow] : 0.0f;
+  const float thr_q = d.kind == 1 ? q_thr[b * gamma + d.srow] : 0.0f;
 
-  auto chunk_scores = [&](int kind, int c_lo, int c_hi) -> Top2 {
-    Top2 best{neg_inf(), INT32_MAX, neg_inf()};
-    for (int c = c_lo + wave; c < c_hi; c += kWaves) {
+  // wave-level best of chunks c0 + wave + 4 i (i < kChunksPerWave)
+  auto wave_chunks = [&](int kind, int c0) -> Top2 {
+    float l[kChunksPerWave][4], zq[kChunksPerWave][4];
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+      const int c = c0 + wave + kWaves * i;
+      const int v0 = c * kChunk + lane * 4;
+      if (c < C) {
+        load4<T, VEC4>(trow, v0, V, l[i]);
+        if (kind == 1) load4<float, VEC4>(q_z + qoff, v0, V, zq[i]);
+        else
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zq[i][e] = neg_inf();
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[i][e] = zq[i][e] = neg_inf();
+      }
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
       float w = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = c * kChunk + lane * 4 + e;
-        if (v < V) w += draw_weight(kind, trow, qrow, v, m, cT, inv_s, lse_q, thr_q);
-      }
+      for (int e = 0; e < 4; ++e)
+        w += draw_weight(kind, l[i][e], zq[i][e], cT, M2, inv_s, lse_q, thr_q);
       w = wave_sum(w);
-      const float sc = w > 0.0f ? logf(w) + gumbel(seed, static_cast<uint32_t>(c), pos, req,
-                                                   DSPARK_TAG_TARGET_CHUNK)
-                                : neg_inf();
-      best = top2_merge(best, Top2{sc, w > 0.0f ? c : INT32_MAX, neg_inf()});
+      if (lane == i) mine = w;  // lane i scores chunk i of this wave
     }
-    return block_top2<kWaves>(best, shv, shi, shv2);
+    Top2 t{neg_inf(), INT32_MAX, neg_inf()};
+    const int c = c0 + wave + kWaves * lane;
+    if (lane < kChunksPerWave && c < C && mine > 0.0f)
+      t = Top2{logf(mine) + gumbel(seed, static_cast<uint32_t>(c), pos, req,
+                                   DSPARK_TAG_TARGET_CHUNK),
+               c, neg_inf()};
+    return wave_top2(t);
   };
 
-  const int c_lo = s2 * cps, c_hi = min(C, c_lo + cps);
-  const Top2 mine = chunk_scores(d.kind, c_lo, c_hi);
+  Top2 mine{neg_inf(), INT32_MAX, neg_inf()};
+  {
+    const Top2 w = wave_chunks(d.kind, s2 * kChunksPerWG);
+    if (lane == 0) {
+      shv[wave] = w.v1;
+      shi[wave] = w.i1;
+      shv2[wave] = w.v2;
+    }
+    __syncthreads();
+    for (int i = 0; i < kWaves; ++i) mine = top2_merge(mine, Top2{shv[i], shi[i], shv2[i]});
+  }
   if (tid == 0) {
-    picks[static_cast<size_t>(b) * S2 + s2] = Pick{mine.v1, mine.i1, mine.v2, 0u};
-    __threadfence();
-    const uint32_t prev = atomicAdd(&counters[b], 1u);
+    Pick* pk = picks + static_cast<size_t>(b) * S2 + s2;
+    store_coherent(&pk->v1, mine.v1);
+    store_coherent(&pk->i1, mine.i1);
+    store_coherent(&pk->v2, mine.v2);
+    const uint32_t prev = publish(&counters[b]);
     sh_last = (prev == static_cast<uint32_t>(S2 - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
 
   // 4. last workgroup of the request: pick the chunk, then the token
-  __threadfence();
-  if (tid == 0) {
-    Top2 best{neg_inf(), INT32_MAX, neg_inf()};
-    for (int i = 0; i < S2; ++i) {
-      const Pick p = picks[static_cast<size_t>(b) * S2 + i];
-      best = top2_merge(best, Top2{p.v1, p.i1, p.v2});
+  {
+    Top2 t{neg_inf(), INT32_MAX, neg_inf()};
+    for (int i = tid; i < S2; i += kThreads) {
+      const Pick* pk = picks + static_cast<size_t>(b) * S2 + i;
+      t = top2_merge(t, Top2{load_coherent(&pk->v1), load_coherent(&pk->i1), load_coherent(&pk->v2)});
     }
-    sh_best = best;
+    t = block_top2<kWaves>(t, shv, shi, shv2);
+    if (tid == 0) sh_best = t;
   }
   __syncthreads();
   Top2 best = sh_best;
@@ -375,7 +448,9 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     // max(p - q, 0) has no mass (only reachable by rounding): draw from p
     kind = 3;
     row_flags |= DSPARK_FLAG_RESIDUAL_ZERO;
-    best = chunk_scores(3, 0, C);
+    Top2 t{neg_inf(), INT32_MAX, neg_inf()};
+    for (int c0 = 0; c0 < C; c0 += kChunksPerWG) t = top2_merge(t, wave_chunks(3, c0));
+    best = block_top2<kWaves>(t, shv, shi, shv2);
   }
   if (best.i1 != INT32_MAX && best.v2 > neg_inf() && near_gap(best.v1, best.v2))
     row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
@@ -384,13 +459,13 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   if (best.i1 != INT32_MAX) {
     const int v = best.i1 * kChunk + tid;
     if (v < V) {
-      float lw;
+      const float l = load_logit(trow, v);
+      float lw = neg_inf();
       if (kind == 1) {
-        const float w = draw_weight(1, trow, qrow, v, m, cT, inv_s, lse_q, thr_q);
+        const float w = draw_weight(1, l, q_z[qoff + v], cT, M2, inv_s, lse_q, thr_q);
         lw = w > 0.0f ? logf(w) : neg_inf();
-      } else {
-        const float l = load_logit(trow, v);
-        lw = l > neg_inf() ? (l - m) / Tb : neg_inf();
+      } else if (l > neg_inf()) {
+        lw = (l - rm[d.srow]) / Tb;
       }
       if (lw > neg_inf())
         tok = Top2{lw + gumbel(seed, static_cast<uint32_t>(v), pos, req, DSPARK_TAG_TARGET_TOKEN),
@@ -398,12 +473,9 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     }
   }
   tok = block_top2<kWaves>(tok, shv, shi, shv2);
-  if (tid == 0) {
-    if (tok.i1 != INT32_MAX && tok.v2 > neg_inf() && near_gap(tok.v1, tok.v2))
-      row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
-    const int32_t emitted = tok.i1 == INT32_MAX ? 0 : tok.i1;
-    write_outputs(emitted, row_flags, d.srow);
-  }
+  if (tok.i1 != INT32_MAX && tok.v2 > neg_inf() && near_gap(tok.v1, tok.v2))
+    row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
+  write_outputs(tok.i1 == INT32_MAX ? 0 : tok.i1, row_flags, d.srow);
 }
 
 template <typename T>
@@ -416,24 +488,27 @@ hipError_t launch_typed(const T* target, const int32_t* draft, const float* q_z,
   RowPart* part = reinterpret_cast<RowPart*>(w + pl.off_part);
   Pick* picks = reinterpret_cast<Pick*>(w + pl.off_pick);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
-  const dim3 g1(pl.S, B * (gamma + 1));
-  {
-  ProfScope ps("verify_rows", st);
+  const dim3 g1((pl.S + kWaves - 1) / kWaves, B * (gamma + 1));
   if (pl.vec)
-    hipLaunchKernelGGL((verify_rows_kernel<T, true>), g1, dim3(kThreads), 0, st, target, V, gamma,
-                       pl.slice_len, pl.S, pol.mode, pol.temperature, n_draft, part, cnt, B);
+    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, true>), g1, dim3(kThreads), 0, st, target,
+                  V, gamma, pl.S, pol.mode, pol.temperature, n_draft, part, cnt, B);
   else
-    hipLaunchKernelGGL((verify_rows_kernel<T, false>), g1, dim3(kThreads), 0, st, target, V,
-                       gamma, pl.slice_len, pl.S, pol.mode, pol.temperature, n_draft, part, cnt,
-                       B);
-  }
+    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, false>), g1, dim3(kThreads), 0, st,
+                  target, V, gamma, pl.S, pol.mode, pol.temperature, n_draft, part, cnt, B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ProfScope ps("verify_decide", st);
-  hipLaunchKernelGGL((verify_decide_kernel<T>), dim3(pl.S2, B), dim3(kThreads), 0, st, target,
-                     draft, q_z, q_lse, q_thr, q_tok, n_draft, pol.mode, pol.temperature,
-                     pol.request_id, pol.position, seed, gamma, V, pl.S, pl.S2, pl.cps, part,
-                     picks, cnt, accept_len, out_tokens, flags);
+  const bool vec4 = V % 4 == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(q_z) % 16 == 0;
+  if (vec4)
+    DSPARK_LAUNCH("verify_decide", (verify_decide_kernel<T, true>), dim3(pl.S2, B),
+                  dim3(kThreads), 0, st, target, draft, q_z, q_lse, q_thr, q_tok, n_draft,
+                  pol.mode, pol.temperature, pol.request_id, pol.position, seed, gamma, V, pl.S,
+                  pl.S2, part, picks, cnt, accept_len, out_tokens, flags);
+  else
+    DSPARK_LAUNCH("verify_decide", (verify_decide_kernel<T, false>), dim3(pl.S2, B),
+                  dim3(kThreads), 0, st, target, draft, q_z, q_lse, q_thr, q_tok, n_draft,
+                  pol.mode, pol.temperature, pol.request_id, pol.position, seed, gamma, V, pl.S,
+                  pl.S2, part, picks, cnt, accept_len, out_tokens, flags);
   return hipGetLastError();
 }
 
@@ -441,14 +516,13 @@ hipError_t launch_typed(const T* target, const int32_t* draft, const float* q_z,
 
 VerifyPlan plan_verify(int dtype, int32_t B, int32_t gamma, int32_t V, bool aligned) {
   VerifyPlan p{};
-  const int epl16 = dtype == DSPARK_BF16 ? 8 : 4;
-  p.vec = (aligned && V % epl16 == 0) ? 1 : 0;
-  const int epl = p.vec ? epl16 : 1;
-  p.slice_len = (p.vec ? kVecIters : kScalarIters) * kThreads * epl;
-  p.S = (V + p.slice_len - 1) / p.slice_len;
+  const bool bf = dtype == DSPARK_BF16;
+  p.vec = (aligned && V % (bf ? 8 : 4) == 0) ? 1 : 0;
+  p.slice_len = bf ? (p.vec ? seg_len<uint16_t, true>() : seg_len<uint16_t, false>())
+                   : (p.vec ? seg_len<float, true>() : seg_len<float, false>());
+  p.S = (V + p.slice_len - 1) / p.slice_len;  // row segments (one wave each)
   const int C = (V + kChunk - 1) / kChunk;
-  const int S2 = C < kMaxSlices2 ? C : kMaxSlices2;
-  p.cps = (C + S2 - 1) / S2;
+  p.cps = kChunksPerWG;
   p.S2 = (C + p.cps - 1) / p.cps;
   size_t off = 0;
   p.off_part = off;
