@@ -29,10 +29,11 @@ struct Pick {
 
 // Per (request, chunk) partial of the Markov step's fused GEMM epilogue.
 struct ChunkPart {
-  float m;      // max of z over the chunk
-  float s;      // sum of exp(z - m) over the chunk
-  int32_t arg;  // lowest index of the max of z (greedy rows: of y)
-  uint32_t flags;
+  float m;          // max of z over the chunk (-inf if none)
+  float s;          // sum of exp(z - m) over the chunk
+  float score;      // sampled rows: ln(chunk mass) + chunk Gumbel noise (-inf if none)
+  uint32_t arg_nf;  // bits 0..30: lowest index of the max (0x7fffffff: none);
+                    // bit 31: a NaN or +inf was seen
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

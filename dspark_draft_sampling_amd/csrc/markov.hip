@@ -37,35 +37,39 @@ constexpr int kPad = 8;            // bf16 padding per staged W1 row (bank sprea
 constexpr int kFinThreads = 256;
 constexpr int kFinWaves = kFinThreads / 64;
 
-template <typename T, bool VEC>
-struct Quad;  // four consecutive logits starting at a multiple of 4
-
-template <>
-struct Quad<uint16_t, true> {
-  __device__ static void load(const uint16_t* p, float* o) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    o[0] = bf_lo(u.x);
-    o[1] = bf_hi(u.x);
-    o[2] = bf_lo(u.y);
-    o[3] = bf_hi(u.y);
-  }
-};
-template <>
-struct Quad<float, true> {
-  __device__ static void load(const float* p, float* o) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    o[0] = u.x;
-    o[1] = u.y;
-    o[2] = u.z;
-    o[3] = u.w;
-  }
-};
+// Four consecutive logits starting at a multiple of 4, kept packed (bf16:
+// 8 bytes, fp32: 16 bytes) until the epilogue unpacks them.
 template <typename T>
-struct Quad<T, false> {
-  __device__ static void load(const T* p, float* o) {
+struct QuadRaw;
+template <>
+struct QuadRaw<uint16_t> {
+  uint2 u;
+  __device__ void load(const uint16_t* p, bool vec, int n) {
+    if (vec && n >= 4) {
+      u = *reinterpret_cast<const uint2*>(p);
+    } else {
+      uint32_t h[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = load_logit(p, i);
+      for (int i = 0; i < 4; ++i) h[i] = i < n ? p[i] : 0u;
+      u = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
   }
+  __device__ float at(int i) const {
+    const uint32_t w = i < 2 ? u.x : u.y;
+    return (i & 1) ? bf_hi(w) : bf_lo(w);
+  }
+};
+template <>
+struct QuadRaw<float> {
+  float4 u;
+  __device__ void load(const float* p, bool vec, int n) {
+    if (vec && n >= 4) {
+      u = *reinterpret_cast<const float4*>(p);
+    } else {
+      u = make_float4(n > 0 ? p[0] : 0.f, n > 1 ? p[1] : 0.f, n > 2 ? p[2] : 0.f, n > 3 ? p[3] : 0.f);
+    }
+  }
+  __device__ float at(int i) const { return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w; }
 };
 
 __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
@@ -76,8 +80,9 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
     const T* __restrict__ backbone, const int32_t* __restrict__ xprev, int32_t xstride,
     const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
-    const uint8_t* __restrict__ mode, const float* __restrict__ temperature, int32_t B,
-    int32_t gamma, int32_t k, int32_t V, int32_t r, int32_t C, float* __restrict__ q_z,
+    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
+    const uint32_t* __restrict__ request_id, const int32_t* __restrict__ position, uint64_t seed,
+    int32_t B, int32_t gamma, int32_t k, int32_t V, int32_t r, int32_t C, float* __restrict__ q_z,
     ChunkPart* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[kTile * (kMaxR + kPad)];
   __shared__ float red_m[kStepWaves][kTile], red_s[kStepWaves][kTile];
@@ -106,17 +111,48 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
     }
   }
 
-  // stage the gathered W1 rows of the tile's requests (MFMA B operand)
-  const int pieces = kpad / 8;
-  for (int idx = tid; idx < kTile * pieces; idx += kStepThreads) {
-    const int row = idx / pieces, pc = idx - row * pieces;
-    const int b = b0 + row;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (b < B && pc * 8 < r) {
-      const int32_t x = clamp_token(xprev[static_cast<size_t>(b) * xstride], V);
-      val = *reinterpret_cast<const uint4*>(w1 + static_cast<size_t>(x) * r + pc * 8);
+  // prefetch this lane's backbone values (tokens vb + ms*16 + 4*(lane>>4) + i of
+  // request ns*16 + (lane&15)) so their latency overlaps the product
+  QuadRaw<T> bbv[4][2];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int b = b0 + ns * 16 + (lane & 15);
+    const size_t rowoff = (static_cast<size_t>(b < B ? b : 0) * gamma + (k - 1)) * V;
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+      const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+      const int n = b < B ? (V - v0 < 4 ? (V - v0 > 0 ? V - v0 : 0) : 4) : 0;
+      bbv[ns][ms].load(backbone + rowoff + (n > 0 ? v0 : 0), VEC, n);
     }
-    *reinterpret_cast<uint4*>(a_lds + row * ld + pc * 8) = val;
+  }
+
+  // stage the gathered W1 rows of the tile's requests (MFMA B operand): the
+  // 64 tokens first, then every 16-byte piece load issued back to back
+  __shared__ int32_t xs_lds[kTile];
+  if (tid < kTile) {
+    const int b = b0 + tid;
+    xs_lds[tid] = b < B ? clamp_token(xprev[static_cast<size_t>(b) * xstride], V) : -1;
+  }
+  __syncthreads();
+  const int pieces = kpad / 8;
+  constexpr int kMaxPieces = kTile * (kMaxR / 8) / kStepThreads;  // 4
+  uint4 stage[kMaxPieces];
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) {
+    const int idx = tid + j * kStepThreads;
+    const int row = idx / pieces, pc = idx - row * pieces;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (row < kTile && pc * 8 < r) {
+      const int32_t x = xs_lds[row];
+      if (x >= 0) val = *reinterpret_cast<const uint4*>(w1 + static_cast<size_t>(x) * r + pc * 8);
+    }
+    stage[j] = val;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) {
+    const int idx = tid + j * kStepThreads;
+    const int row = idx / pieces, pc = idx - row * pieces;
+    if (row < kTile) *reinterpret_cast<uint4*>(a_lds + row * ld + pc * 8) = stage[j];
   }
   __syncthreads();
 
@@ -158,19 +194,12 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) {
       const int v0 = vb + ms * 16 + 4 * (lane >> 4);
-      float bb[4] = {0.f, 0.f, 0.f, 0.f};
+      const QuadRaw<T>& bb = bbv[ns][ms];
       const bool full = bvalid && v0 + 3 < V;
-      if (full) {
-        Quad<T, VEC>::load(backbone + rowoff + v0, bb);
-      } else if (bvalid) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v0 + i < V) bb[i] = load_logit(backbone, rowoff + v0 + i);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool in = bvalid && v0 + i < V;
-        z[ms * 4 + i] = in ? (acc[ms][ns][i] + bb[i]) * invT : neg_inf();
+        z[ms * 4 + i] = in ? (acc[ms][ns][i] + bb.at(i)) * invT : neg_inf();
         zi[ms * 4 + i] = v0 + i;
       }
       if (sampled) {
@@ -221,6 +250,7 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
   }
   __syncthreads();
   if (tid < kTile && b0 + tid < B) {
+    const int b = b0 + tid;
     float m = red_m[0][tid], s = red_s[0][tid];
     ArgMax a{red_m[0][tid], red_i[0][tid]};
     uint32_t bad = red_f[0][tid];
@@ -230,109 +260,209 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
       a = better(a, ArgMax{red_m[w][tid], red_i[w][tid]});
       bad |= red_f[w][tid];
     }
-    part[static_cast<size_t>(b0 + tid) * C + c] =
-        ChunkPart{m, s, a.i, bad ? static_cast<uint32_t>(DSPARK_FLAG_NONFINITE) : 0u};
+    // chunk level of the two-level Gumbel-max draw: ln(mass) + chunk noise
+    float score = neg_inf();
+    const float Tb = temperature[b];
+    if (mode[b] != 0 && !bad_temperature(Tb) && m > neg_inf() && m < pos_inf() && s > 0.0f)
+      score = m + logf(s) + gumbel(seed, static_cast<uint32_t>(c), position[b] + k, request_id[b],
+                                   DSPARK_TAG_DRAFT_CHUNK);
+    part[static_cast<size_t>(b) * C + c] =
+        ChunkPart{m, s, score, (static_cast<uint32_t>(a.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)};
   }
 }
 
+// One workgroup per request.  All waves combine the chunk partials; then wave
+// 0 draws the token inside the chosen chunk (lane l scores tokens 4l..4l+3 with
+// one Philox block) while waves 1-3 evaluate the confidence head.
+template <bool VEC>
 __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
     const int32_t* __restrict__ xprev, int32_t xstride, const uint16_t* __restrict__ hidden,
     const uint16_t* __restrict__ embed, const float* __restrict__ conf_w,
     const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
     const uint32_t* __restrict__ request_id, const int32_t* __restrict__ position,
-    uint64_t seed, int32_t gamma, int32_t k, int32_t V, int32_t d, int32_t C,
+    uint64_t seed, int32_t gamma, int32_t k, int32_t V, int32_t d, int32_t C, int32_t cvec,
     const ChunkPart* __restrict__ part, const float* __restrict__ q_z,
     int32_t* __restrict__ draft_tokens, float* __restrict__ q_lse, float* __restrict__ q_thr,
     float* __restrict__ q_tok, float* __restrict__ confidence, uint8_t* __restrict__ flags) {
-  __shared__ float shv[kFinWaves], shv2[kFinWaves];
-  __shared__ int32_t shi[kFinWaves];
-  __shared__ uint32_t shu[kFinWaves];
-  __shared__ float sh_zx;
+  __shared__ float sh_m[kFinWaves], sh_s[kFinWaves], sh_am[kFinWaves], sh_v1[kFinWaves],
+      sh_v2[kFinWaves], sh_dot[kFinWaves];
+  __shared__ int32_t sh_ai[kFinWaves], sh_i1[kFinWaves];
+  __shared__ uint32_t sh_bad[kFinWaves];
+  __shared__ float fin_M, fin_S, fin_zx;
+  __shared__ int32_t fin_x;
+  __shared__ uint32_t fin_fl;
 
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
   const float Tb = temperature[b];
   const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
   const uint32_t req = request_id[b];
   const int32_t pos = position[b] + k;
 
+  // 1. combine the chunk partials
   float m = neg_inf(), s = 0.0f;
   ArgMax am{neg_inf(), INT32_MAX};
-  uint32_t fl = 0;
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
+  uint32_t bad = 0;
   for (int c = tid; c < C; c += kFinThreads) {
     const ChunkPart p = part[static_cast<size_t>(b) * C + c];
-    fl |= p.flags;
-    am = better(am, ArgMax{p.m, p.arg});
+    const int32_t arg = static_cast<int32_t>(p.arg_nf & 0x7fffffffu);
+    bad |= p.arg_nf >> 31;
+    am = better(am, ArgMax{p.m, arg == 0x7fffffff ? INT32_MAX : arg});
     lse_merge(m, s, p.m, p.s);
-    if (sampled && p.m > neg_inf() && p.s > 0.0f) {
-      const float sc = p.m + logf(p.s) +
-                       gumbel(seed, static_cast<uint32_t>(c), pos, req, DSPARK_TAG_DRAFT_CHUNK);
-      best = top2_merge(best, Top2{sc, c, neg_inf()});
+    if (p.score > neg_inf()) best = top2_merge(best, Top2{p.score, c, neg_inf()});
+  }
+  {
+    const float wm = wave_max(m);
+    const float ws = wave_sum((m > neg_inf() && wm < pos_inf()) ? s * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
+    const ArgMax wa = wave_argmax(am);
+    const Top2 wb = wave_top2(best);
+    const uint32_t wbad = wave_or(bad);
+    if (lane == 0) {
+      sh_m[wave] = wm;
+      sh_s[wave] = ws;
+      sh_am[wave] = wa.v;
+      sh_ai[wave] = wa.i;
+      sh_v1[wave] = wb.v1;
+      sh_i1[wave] = wb.i1;
+      sh_v2[wave] = wb.v2;
+      sh_bad[wave] = wbad;
     }
   }
-  am = block_argmax<kFinWaves>(am, shv, shi);
-  const float M = block_max<kFinWaves>(m, shv);
-  const float S = block_sum<kFinWaves>(
-      (m > neg_inf() && M < pos_inf()) ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f, shv);
-  fl = block_or<kFinWaves>(fl, shu);
+  __syncthreads();
+  float M = sh_m[0], S = sh_s[0];
+  ArgMax A{sh_am[0], sh_ai[0]};
+  Top2 Bst{sh_v1[0], sh_i1[0], sh_v2[0]};
+  uint32_t fl = sh_bad[0] ? DSPARK_FLAG_NONFINITE : 0u;
+#pragma unroll
+  for (int w = 1; w < kFinWaves; ++w) {
+    lse_merge(M, S, sh_m[w], sh_s[w]);
+    A = better(A, ArgMax{sh_am[w], sh_ai[w]});
+    Bst = top2_merge(Bst, Top2{sh_v1[w], sh_i1[w], sh_v2[w]});
+    if (sh_bad[w]) fl |= DSPARK_FLAG_NONFINITE;
+  }
 
-  int32_t x = 0;
-  uint32_t near = 0;
-  if (!sampled) {
-    if (am.i == INT32_MAX) fl |= DSPARK_FLAG_EMPTY_ROW;
-    else x = am.i;
-  } else {
-    best = block_top2<kFinWaves>(best, shv, shi, shv2);
-    if (best.i1 == INT32_MAX) {
+  if (wave == 0) {
+    // 2a. the draw
+    int32_t x = 0;
+    float zx = neg_inf();
+    uint32_t near = 0;
+    if (!sampled) {
+      if (A.i == INT32_MAX) fl |= DSPARK_FLAG_EMPTY_ROW;
+      else x = A.i;
+    } else if (Bst.i1 == INT32_MAX) {
       fl |= DSPARK_FLAG_EMPTY_ROW;
     } else {
-      if (best.v2 > neg_inf() && near_gap(best.v1, best.v2)) near = 1;
-      const int v = best.i1 * kChunk + tid;
-      Top2 tok{neg_inf(), INT32_MAX, neg_inf()};
-      if (v < V) {
-        const float z = q_z[row * V + v];
-        if (z > neg_inf())
-          tok = Top2{z + gumbel(seed, static_cast<uint32_t>(v), pos, req, DSPARK_TAG_DRAFT_TOKEN),
-                     v, neg_inf()};
+      if (Bst.v2 > neg_inf() && near_gap(Bst.v1, Bst.v2)) near = 1;
+      const int v0 = Bst.i1 * kChunk + 4 * lane;
+      float z[4];
+      if (VEC && v0 + 3 < V) {
+        const float4 u = *reinterpret_cast<const float4*>(q_z + row * V + v0);
+        z[0] = u.x;
+        z[1] = u.y;
+        z[2] = u.z;
+        z[3] = u.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = v0 + e < V ? q_z[row * V + v0 + e] : neg_inf();
       }
-      tok = block_top2<kFinWaves>(tok, shv, shi, shv2);
-      if (tok.i1 == INT32_MAX) {
+      // tokens v0..v0+3 share Philox counter (v0 / 4, pos, req, tag)
+      uint32_t c0 = static_cast<uint32_t>(v0) >> 2, c1 = static_cast<uint32_t>(pos), c2 = req,
+               c3 = DSPARK_TAG_DRAFT_TOKEN;
+      philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+      const uint32_t wv[4] = {c0, c1, c2, c3};
+      Top2 t{neg_inf(), INT32_MAX, neg_inf()};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (z[e] > neg_inf()) t = top2_merge(t, Top2{z[e] + gumbel_of(wv[e]), v0 + e, neg_inf()});
+      t = wave_top2(t);
+      if (t.i1 == INT32_MAX) {
         fl |= DSPARK_FLAG_EMPTY_ROW;
       } else {
-        x = tok.i1;
-        if (tok.v2 > neg_inf() && near_gap(tok.v1, tok.v2)) near = 1;
+        x = t.i1;
+        if (t.v2 > neg_inf() && near_gap(t.v1, t.v2)) near = 1;
+        zx = q_z[row * V + x];
       }
     }
+    if (near) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
+    if (lane == 0) {
+      fin_x = x;
+      fin_zx = zx;
+      fin_M = M;
+      fin_S = S;
+      fin_fl = fl;
+    }
+  } else {
+    // 2b. confidence head on [h_k ; embed(x_{k-1})]: 8 elements per 16-byte
+    // load, every load of a thread issued before the first use
+    const int32_t xp = clamp_token(xprev[static_cast<size_t>(b) * xstride], V);
+    const uint16_t* h = hidden + row * d;
+    const uint16_t* e = embed + static_cast<size_t>(xp) * d;
+    const int t = tid - 64;
+    constexpr int kConfThreads = kFinThreads - 64;
+    float dot = 0.0f;
+    if (cvec) {
+      constexpr int kU = 4;  // vectors per thread per round
+      for (int base = 0; base < d; base += kConfThreads * 8 * kU) {
+        uint4 hv[kU], ev[kU];
+        float4 wh[kU][2], we[kU][2];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + (t + u * kConfThreads) * 8;
+          if (i < d) {
+            hv[u] = *reinterpret_cast<const uint4*>(h + i);
+            ev[u] = *reinterpret_cast<const uint4*>(e + i);
+            wh[u][0] = *reinterpret_cast<const float4*>(conf_w + i);
+            wh[u][1] = *reinterpret_cast<const float4*>(conf_w + i + 4);
+            we[u][0] = *reinterpret_cast<const float4*>(conf_w + d + i);
+            we[u][1] = *reinterpret_cast<const float4*>(conf_w + d + i + 4);
+          } else {
+            hv[u] = ev[u] = make_uint4(0u, 0u, 0u, 0u);
+            wh[u][0] = wh[u][1] = we[u][0] = we[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const float hx[8] = {bf_lo(hv[u].x), bf_hi(hv[u].x), bf_lo(hv[u].y), bf_hi(hv[u].y),
+                               bf_lo(hv[u].z), bf_hi(hv[u].z), bf_lo(hv[u].w), bf_hi(hv[u].w)};
+          const float ex[8] = {bf_lo(ev[u].x), bf_hi(ev[u].x), bf_lo(ev[u].y), bf_hi(ev[u].y),
+                               bf_lo(ev[u].z), bf_hi(ev[u].z), bf_lo(ev[u].w), bf_hi(ev[u].w)};
+          const float whx[8] = {wh[u][0].x, wh[u][0].y, wh[u][0].z, wh[u][0].w,
+                                wh[u][1].x, wh[u][1].y, wh[u][1].z, wh[u][1].w};
+          const float wex[8] = {we[u][0].x, we[u][0].y, we[u][0].z, we[u][0].w,
+                                we[u][1].x, we[u][1].y, we[u][1].z, we[u][1].w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dot += whx[j] * hx[j] + wex[j] * ex[j];
+        }
+      }
+    } else {
+      for (int i = t; i < d; i += kConfThreads)
+        dot += conf_w[i] * load_logit(h, i) + conf_w[d + i] * load_logit(e, i);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) sh_dot[wave] = dot;
   }
-
-  // confidence head on [h_k ; embed(x_{k-1})]
-  const int32_t xp = clamp_token(xprev[static_cast<size_t>(b) * xstride], V);
-  const uint16_t* h = hidden + row * d;
-  const uint16_t* e = embed + static_cast<size_t>(xp) * d;
-  float dot = 0.0f;
-  for (int i = tid; i < d; i += kFinThreads)
-    dot += conf_w[i] * load_logit(h, i) + conf_w[d + i] * load_logit(e, i);
-  dot = block_sum<kFinWaves>(dot, shv);
-
+  __syncthreads();
   if (tid == 0) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int w = 1; w < kFinWaves; ++w) dot += sh_dot[w];
+    const int32_t x = fin_x;
     draft_tokens[row] = x;
     if (sampled) {
-      const float zx = q_z[row * V + x];
-      q_lse[row] = M + logf(S);
+      q_lse[row] = fin_M + logf(fin_S);
       q_thr[row] = neg_inf();
-      q_tok[row] = (zx > neg_inf() && S > 0.0f) ? expf(zx - M) / S : 0.0f;
+      q_tok[row] = (fin_zx > neg_inf() && fin_S > 0.0f) ? expf(fin_zx - fin_M) / fin_S : 0.0f;
     } else {
       q_lse[row] = 0.0f;
       q_thr[row] = 0.0f;
       q_tok[row] = 1.0f;
     }
     confidence[row] = 1.0f / (1.0f + expf(-dot));
-    if (near) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
-    if (mode[b] != 0 && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
-    flags[row] = static_cast<uint8_t>(fl);
+    uint32_t f = fin_fl;
+    if (mode[b] != 0 && !sampled) f |= DSPARK_FLAG_BAD_POLICY;
+    flags[row] = static_cast<uint8_t>(f);
   }
-  (void)sh_zx;
 }
 
 template <typename T>
@@ -346,23 +476,33 @@ hipError_t launch_typed(const T* backbone, const int32_t* anchor, const uint16_t
   const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(backbone) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(q_z) % 16 == 0);
   const dim3 g_step(pl.C, (B + kTile - 1) / kTile);
+  // 16-byte loads of the confidence head's rows and weights
+  const int32_t cvec = (d % 8 == 0) && reinterpret_cast<uintptr_t>(hidden) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(embed) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(conf_w) % 16 == 0;
   for (int k = 1; k <= gamma; ++k) {
     const int32_t* xp = k == 1 ? anchor : draft_tokens + (k - 2);
     const int32_t xs = k == 1 ? 1 : gamma;
     if (vec)
       DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, true>), g_step, dim3(kStepThreads), 0,
-                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
-                    pl.C, q_z, part);
+                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, pol.request_id,
+                    pol.position, seed, B, gamma, k, V, r, pl.C, q_z, part);
     else
       DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, false>), g_step, dim3(kStepThreads), 0,
-                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, B, gamma, k, V, r,
-                    pl.C, q_z, part);
+                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, pol.request_id,
+                    pol.position, seed, B, gamma, k, V, r, pl.C, q_z, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel, dim3(B), dim3(kFinThreads), 0, st, xp,
-                  xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
-                  pol.position, seed, gamma, k, V, d, pl.C, part, q_z, draft_tokens, q_lse, q_thr,
-                  q_tok, confidence, flags);
+    if (vec)
+      DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<true>, dim3(B), dim3(kFinThreads), 0,
+                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
+                    pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
+                    q_lse, q_thr, q_tok, confidence, flags);
+    else
+      DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<false>, dim3(B), dim3(kFinThreads), 0,
+                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
+                    pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
+                    q_lse, q_thr, q_tok, confidence, flags);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -152,31 +152,46 @@ __global__ __launch_bounds__(kThreads) void stats_rows_kernel(
 }
 
 // One workgroup: per-block tau and the loss / report sums, in fp64, in a fixed
-// order (thread t owns blocks t, t + 256, ...; then a fixed tree).
+// order (thread t owns blocks t, t + 256, ...; then one fixed tree over the
+// eight sums at once).  Every load of a block is issued before its first use.
 __global__ __launch_bounds__(kThreads) void stats_reduce_kernel(
     const float* __restrict__ l1, const float* __restrict__ accept_rate,
     const float* __restrict__ ce, const float* __restrict__ bce,
     const uint8_t* __restrict__ block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,
     float w_conf, float* __restrict__ tau, float* __restrict__ sums) {
-  __shared__ double sh[kThreads];
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // num, tokens, l1, acc, tau, blocks, ce, bce
+  constexpr int Q = 8;  // num, tokens, l1, accept, tau, blocks, ce, bce
+  __shared__ double sh[Q][kThreads];
+  double acc[Q] = {0, 0, 0, 0, 0, 0, 0, 0};
+  double wk[DSPARK_MAX_GAMMA];
+#pragma unroll
+  for (int k = 0; k < DSPARK_MAX_GAMMA; ++k) wk[k] = exp(-static_cast<double>(k + 1) / gamma);
   for (int b = threadIdx.x; b < N; b += kThreads) {
+    float a[DSPARK_MAX_GAMMA], c[DSPARK_MAX_GAMMA], l[DSPARK_MAX_GAMMA], x[DSPARK_MAX_GAMMA];
+    const size_t base = static_cast<size_t>(b) * gamma;
+#pragma unroll
+    for (int k = 0; k < DSPARK_MAX_GAMMA; ++k) {
+      const bool in = k < gamma;
+      a[k] = in ? accept_rate[base + k] : 0.0f;
+      c[k] = in ? ce[base + k] : 0.0f;
+      l[k] = in ? l1[base + k] : 0.0f;
+      x[k] = in ? bce[base + k] : 0.0f;
+    }
     const bool m = block_mask ? block_mask[b] != 0 : true;
     double cum = 1.0, t = 1.0;
-    for (int k = 1; k <= gamma; ++k) {
-      const size_t i = static_cast<size_t>(b) * gamma + (k - 1);
-      const double a = accept_rate[i];
-      cum *= a;
-      t += cum;
-      if (m) {
-        const double wk = exp(-static_cast<double>(k) / gamma);
-        acc[0] += wk * (w_ce * static_cast<double>(ce[i]) + w_l1 * static_cast<double>(l1[i]) +
-                        w_conf * static_cast<double>(bce[i]));
-        acc[1] += 1.0;
-        acc[2] += l1[i];
-        acc[3] += a;
-        acc[6] += ce[i];
-        acc[7] += bce[i];
+#pragma unroll
+    for (int k = 0; k < DSPARK_MAX_GAMMA; ++k) {
+      if (k < gamma) {
+        cum *= a[k];
+        t += cum;
+        if (m) {
+          acc[0] += wk[k] * (w_ce * static_cast<double>(c[k]) + w_l1 * static_cast<double>(l[k]) +
+                             w_conf * static_cast<double>(x[k]));
+          acc[1] += 1.0;
+          acc[2] += l[k];
+          acc[3] += a[k];
+          acc[6] += c[k];
+          acc[7] += x[k];
+        }
       }
     }
     tau[b] = static_cast<float>(t);
@@ -185,30 +200,28 @@ __global__ __launch_bounds__(kThreads) void stats_reduce_kernel(
       acc[5] += 1.0;
     }
   }
-  double tot[8];
-  for (int q = 0; q < 8; ++q) {
-    sh[threadIdx.x] = acc[q];
-    __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-      if (static_cast<int>(threadIdx.x) < o) sh[threadIdx.x] += sh[threadIdx.x + o];
-      __syncthreads();
-    }
-    tot[q] = sh[0];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) sh[q][threadIdx.x] = acc[q];
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) sh[q][threadIdx.x] += sh[q][threadIdx.x + o];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double n = tot[1];
-    sums[0] = static_cast<float>(tot[0]);
+    const double n = sh[1][0];
+    sums[0] = static_cast<float>(sh[0][0]);
     sums[1] = static_cast<float>(n);
-    sums[2] = static_cast<float>(tot[2]);
+    sums[2] = static_cast<float>(sh[2][0]);
     sums[3] = static_cast<float>(n);
-    sums[4] = static_cast<float>(tot[3]);
+    sums[4] = static_cast<float>(sh[3][0]);
     sums[5] = static_cast<float>(n);
-    sums[6] = static_cast<float>(tot[4]);
-    sums[7] = static_cast<float>(tot[5]);
-    sums[8] = static_cast<float>(tot[6]);
+    sums[6] = static_cast<float>(sh[4][0]);
+    sums[7] = static_cast<float>(sh[5][0]);
+    sums[8] = static_cast<float>(sh[6][0]);
     sums[9] = static_cast<float>(n);
-    sums[10] = static_cast<float>(tot[7]);
+    sums[10] = static_cast<float>(sh[7][0]);
     sums[11] = static_cast<float>(n);
   }
 }
