@@ -6,7 +6,10 @@ confidence width 4096, sampled at temperature 1 without truncation):
   dspark_markov_sample  (gamma Markov steps: bias GEMM + sampling + confidence)
   dspark_verify         (the oracle-free exact sampled verify of those proposals)
   dspark_accept_stats   (analytic acceptance of the same draft / target rows)
-Inputs are synthetic (workloads.py) and resident in HBM before timing starts.
+Inputs are synthetic (workloads.py) and resident in HBM before timing starts;
+successive steps cycle through --rotate independent copies of the batch and
+weights (about 1.5 GB each), so no step is served from the Infinity Cache by
+an earlier step's reads.
 
 Prints one JSON line: value = verified rows per second, B (gamma + 1) rows per
 step; the roofline entry is the dominant kernel's algorithmic HBM bytes per
@@ -37,6 +40,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="independent copies of the batch (logits and weights) cycled step by "
+                         "step, so that no step finds its inputs in the 256 MB Infinity Cache")
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -102,8 +108,14 @@ def main():
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    backbone, target = bf(inp["backbone"]), bf(inp["target"])
-    w1, w2, hidden, embed = bf(inp["w1"]), bf(inp["w2"]), bf(inp["hidden"]), bf(inp["embed"])
+    # --rotate independent device copies of every per-step input and weight
+    # (the same values; distinct memory), used round-robin by successive steps
+    sets = []
+    for _ in range(max(1, args.rotate)):
+        backbone, target = bf(inp["backbone"]), bf(inp["target"])
+        sets.append(dict(backbone=backbone, target=target, tgt_rows=target[:, :g].contiguous(),
+                         w1=bf(inp["w1"]), w2=bf(inp["w2"]), hidden=bf(inp["hidden"]),
+                         embed=bf(inp["embed"])))
     anchor = torch.from_numpy(inp["anchor"]).to(dev)
     conf_w = torch.from_numpy(inp["conf_w"]).to(dev)
     pol = ds.Policy(mode=torch.from_numpy(inp["mode"]).to(dev),
@@ -113,22 +125,27 @@ def main():
                     request_id=torch.from_numpy(inp["request_id"].view(np.int32)).to(dev),
                     position=torch.from_numpy(inp["position"]).to(dev))
     # the accept stats read the same rows: draft logits and the first gamma target rows
-    tgt_rows = target[:, :g].contiguous()
     rng = np.random.default_rng(1234)
     teacher = torch.from_numpy(rng.integers(0, V, (B, g)).astype(np.int32)).to(dev)
     conf_logits = torch.from_numpy(rng.standard_normal((B, g)).astype(np.float32)).to(dev)
 
-    mk_out = ds.dspark_markov_sample(backbone, anchor, w1, w2, hidden, embed, conf_w, pol, seed=0)
-    vf_out = ds.dspark_verify(target, mk_out["draft_tokens"], pol, mk_out["q_logits"],
-                              mk_out["q_lse"], mk_out["q_thr"], mk_out["q_tok"], seed=0)
-    st_out = ds.dspark_accept_stats(backbone, tgt_rows, teacher, conf_logits)
+    s0 = sets[0]
+    mk_out = [ds.dspark_markov_sample(s0["backbone"], anchor, s0["w1"], s0["w2"], s0["hidden"],
+                                      s0["embed"], conf_w, pol, seed=0) for _ in sets]
+    vf_out = ds.dspark_verify(s0["target"], mk_out[0]["draft_tokens"], pol, mk_out[0]["q_logits"],
+                              mk_out[0]["q_lse"], mk_out[0]["q_thr"], mk_out[0]["q_tok"], seed=0)
+    st_out = ds.dspark_accept_stats(s0["backbone"], s0["tgt_rows"], teacher, conf_logits)
+    it = [0]
 
     def step():
-        ds.dspark_markov_sample(backbone, anchor, w1, w2, hidden, embed, conf_w, pol, seed=0,
-                                out=mk_out)
-        ds.dspark_verify(target, mk_out["draft_tokens"], pol, mk_out["q_logits"],
-                         mk_out["q_lse"], mk_out["q_thr"], mk_out["q_tok"], seed=0, out=vf_out)
-        ds.dspark_accept_stats(backbone, tgt_rows, teacher, conf_logits, out=st_out)
+        i = it[0] % len(sets)
+        it[0] += 1
+        x, mo = sets[i], mk_out[i]
+        ds.dspark_markov_sample(x["backbone"], anchor, x["w1"], x["w2"], x["hidden"], x["embed"],
+                                conf_w, pol, seed=0, out=mo)
+        ds.dspark_verify(x["target"], mo["draft_tokens"], pol, mo["q_logits"], mo["q_lse"],
+                         mo["q_thr"], mo["q_tok"], seed=0, out=vf_out)
+        ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
 
     for _ in range(args.warmup):
         step()
@@ -178,7 +195,7 @@ def main():
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload="decode verify: Markov sample + sampled verify + accept stats",
                             B=B, gamma=g, V=V, r=r, d=d, logits="bf16", temperature=1.0,
-                            truncation="none", mode="sampled"),
+                            truncation="none", mode="sampled", rotated_batches=len(sets)),
                 roofline=roofline, cpu_baseline=cpu,
                 step=dict(alg_bytes=int(step_bytes),
                           alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

@@ -301,6 +301,15 @@ __device__ __forceinline__ Top2 block_top2(Top2 a, float* shv, int32_t* shi, flo
   return r;
 }
 
+// Byte i of a byte array, read through the aligned 32-bit word that holds it,
+// so that a wave-uniform index becomes a scalar (SMEM) load.  The word never
+// leaves the 4-byte-aligned block of the byte itself.
+__device__ __forceinline__ uint32_t load_u8_word(const uint8_t* __restrict__ p, int i) {
+  const int off = static_cast<int>(reinterpret_cast<uintptr_t>(p + i) & 3u);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p + (i - off));
+  return (w >> (8 * off)) & 0xffu;
+}
+
 __device__ __forceinline__ bool bad_temperature(float T) {
   return !(T > 0.0f) || !(T < pos_inf());
 }

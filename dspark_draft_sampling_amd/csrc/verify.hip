@@ -9,10 +9,10 @@
 // distribution when every proposal survives.  Target row k - 1 verifies x_k.
 //
 // Two launches:
-//  1. verify_rows   grid (row segments / 4, B (gamma+1) rows), 4 waves.  Each
-//     wave pulls one 2048-token segment of one target row into registers with
-//     16-byte loads and reduces it to (max, lowest argmax, sum) with wave
-//     shuffles only: no LDS, no barrier.
+//  1. verify_rows   grid-stride over (target row, 2048-token segment) items,
+//     one wave per item: 16-byte loads into registers, reduced to (max, lowest
+//     argmax, sum) with DPP only (no LDS, no barrier); the next item's loads
+//     are in flight while the current one is reduced.
 //  2. verify_decide grid (chunk slices, B).  Every workgroup of a request
 //     combines the segment partials of its rows and replays the accept scan
 //     (one thread per proposal, first reject by ballot), so all of them agree
@@ -25,6 +25,8 @@
 // M2 = floor(max(l) cT).  Partials with different shifts combine by exact
 // powers of two, and p(x) = 2^(l_x cT - M2) / s uses the very expression each
 // term of s used.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -37,6 +39,7 @@ constexpr int kVecIters = 4;       // 16-byte loads per lane per segment
 constexpr int kScalarIters = 32;   // scalar loads per lane per segment
 constexpr int kChunksPerWave = 8;  // chunks one wave scores in the decide pass
 constexpr int kChunksPerWG = kChunksPerWave * kWaves;
+constexpr int kRowsMaxWGs = 1024;  // grid of the row pass: 4 waves per SIMD
 
 // One 16-byte load per lane per iteration (vector path: 8 bf16 or 4 fp32
 // logits kept packed in a uint4), or one scalar logit (scalar path).  Lanes
@@ -87,45 +90,47 @@ __device__ __forceinline__ float shift_of(float m, float cT) { return floorf(m *
 
 // ---------------------------------------------------------------------------
 // Pass 1: per (row, segment) max, lowest argmax and sum 2^(l cT - M2).
+// Grid-stride over (row, segment) items, one item per wave at a time; the
+// next item's loads are issued before the current item is reduced, so memory
+// and arithmetic overlap within every wave.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_rows_kernel(
-    const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P,
-    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
-    const int32_t* __restrict__ n_draft, RowPart* __restrict__ part,
-    uint32_t* __restrict__ counters, int32_t B) {
+__device__ __forceinline__ void rows_load(const T* __restrict__ target, int32_t V, int32_t P,
+                                          int item, int lane, typename RowLoad<T, VEC>::Raw* u) {
   using L = RowLoad<T, VEC>;
   constexpr int ITERS = VEC ? kVecIters : kScalarIters;
   constexpr int EPL = L::EPL;
   constexpr int SEG = seg_len<T, VEC>();
-
-  const int G1 = gamma + 1;
-  const int row = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int seg = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  // arm the per-request tickets of the decide pass (which starts after this
-  // launch completes on the same stream)
-  if (blockIdx.x == 0 && row == 0)
-    for (int i = threadIdx.x; i < B; i += kThreads) counters[i] = 0u;
-  const int b = row / G1, k = row - b * G1;
-  if (seg >= P || k > n_draft_of(n_draft, b, gamma)) return;  // wave-uniform
+  const int row = item / P, seg = item - row * P;
   const T* rp = target + static_cast<size_t>(row) * V;
   const int lo = seg * SEG;
-  const int hi = min(V, lo + SEG);
+  // every load is issued; past the row end the address is clamped to the
+  // row's last vector and rows_reduce masks those elements
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it)
+    u[it] = L::load(rp, min(lo + (it * 64 + lane) * EPL, V - EPL));
+}
 
-  typename L::Raw u[ITERS];
-  if (hi - lo == SEG) {  // full segment: no bounds checks
+template <typename T, bool VEC>
+__device__ __forceinline__ void rows_reduce(typename RowLoad<T, VEC>::Raw* u, int item,
+                                            int32_t P, int32_t G1, int32_t vlen, int lane,
+                                            const uint8_t* __restrict__ mode,
+                                            const float* __restrict__ temperature,
+                                            RowPart* __restrict__ part) {
+  using L = RowLoad<T, VEC>;
+  constexpr int ITERS = VEC ? kVecIters : kScalarIters;
+  constexpr int EPL = L::EPL;
+  constexpr int SEG = seg_len<T, VEC>();
+  const int row = item / P, seg = item - row * P;
+  const int b = row / G1;
+  const int lo = seg * SEG;
+  const int V = vlen;
+  if (V - lo < SEG) {  // partial segment (wave-uniform): mask the clamped loads
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) u[it] = L::load(rp, lo + (it * 64 + lane) * EPL);
-  } else {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int e = lo + (it * 64 + lane) * EPL;
-      u[it] = e < hi ? L::load(rp, e) : L::neg();
-    }
+    for (int it = 0; it < ITERS; ++it)
+      if (lo + (it * 64 + lane) * EPL >= V) u[it] = L::neg();
   }
-
   const float Tb = temperature[b];
-  const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
+  const bool sampled = load_u8_word(mode, b) != 0 && !bad_temperature(Tb);
   uint32_t fl = 0;
   float m = neg_inf();
   int32_t arg = INT32_MAX;
@@ -167,6 +172,55 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     if (m == pos_inf() || !(sum < pos_inf())) fl |= DSPARK_FLAG_NONFINITE;
   }
   if (lane == 0) part[static_cast<size_t>(row) * P + seg] = RowPart{m, sum, arg, fl};
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_rows_kernel(
+    const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P, int32_t items,
+    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
+    const int32_t* __restrict__ n_draft, RowPart* __restrict__ part,
+    uint32_t* __restrict__ counters, int32_t B) {
+  using L = RowLoad<T, VEC>;
+  constexpr int ITERS = VEC ? kVecIters : kScalarIters;
+  const int G1 = gamma + 1;
+  const int lane = threadIdx.x & 63;
+  // arm the per-request tickets of the decide pass (which starts after this
+  // launch completes on the same stream)
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < B; i += kThreads) counters[i] = 0u;
+  const int nwaves = gridDim.x * kWaves;
+  // next item at or after i whose row the decision can consult (rows past
+  // n_draft are skipped); returns `items` when there is none
+  auto next_live = [&](int i) {
+    for (; i < items; i += nwaves) {
+      const int row = i / P;
+      const int b = row / G1, k = row - b * G1;
+      if (k <= n_draft_of(n_draft, b, gamma)) break;
+    }
+    return i;
+  };
+  // the item index is wave-uniform: keep it (and every address derived from
+  // it) in scalar registers, so per-request scalars come through the scalar
+  // cache and never wait behind the vector loads in flight
+  int item = next_live(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6)));
+  if (item >= items) return;  // wave-uniform
+  // two register buffers used alternately; the prefetch is unconditional (an
+  // exhausted wave re-reads its last item), so the compiler can wait for
+  // exactly the older buffer's loads
+  typename L::Raw ua[ITERS], ub[ITERS];
+  rows_load<T, VEC>(target, V, P, item, lane, ua);
+  while (true) {
+    const int n1 = __builtin_amdgcn_readfirstlane(next_live(item + nwaves));
+    rows_load<T, VEC>(target, V, P, n1 < items ? n1 : item, lane, ub);
+    rows_reduce<T, VEC>(ua, item, P, G1, V, lane, mode, temperature, part);
+    if (n1 >= items) break;
+    const int n2 = __builtin_amdgcn_readfirstlane(next_live(n1 + nwaves));
+    rows_load<T, VEC>(target, V, P, n2 < items ? n2 : n1, lane, ua);
+    rows_reduce<T, VEC>(ub, n1, P, G1, V, lane, mode, temperature, part);
+    if (n2 >= items) break;
+    item = n2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -488,13 +542,14 @@ hipError_t launch_typed(const T* target, const int32_t* draft, const float* q_z,
   RowPart* part = reinterpret_cast<RowPart*>(w + pl.off_part);
   Pick* picks = reinterpret_cast<Pick*>(w + pl.off_pick);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
-  const dim3 g1((pl.S + kWaves - 1) / kWaves, B * (gamma + 1));
+  const int items = B * (gamma + 1) * pl.S;
+  const int wgs = std::min(kRowsMaxWGs, (items + kWaves - 1) / kWaves);
   if (pl.vec)
-    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, true>), g1, dim3(kThreads), 0, st, target,
-                  V, gamma, pl.S, pol.mode, pol.temperature, n_draft, part, cnt, B);
+    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, true>), dim3(wgs), dim3(kThreads), 0, st,
+                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, n_draft, part, cnt, B);
   else
-    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, false>), g1, dim3(kThreads), 0, st,
-                  target, V, gamma, pl.S, pol.mode, pol.temperature, n_draft, part, cnt, B);
+    DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, false>), dim3(wgs), dim3(kThreads), 0, st,
+                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, n_draft, part, cnt, B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool vec4 = V % 4 == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
