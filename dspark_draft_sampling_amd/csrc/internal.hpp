@@ -19,6 +19,13 @@ struct RowPart {
   uint32_t flags;
 };
 
+// Per target row of a truncated policy: smallest kept logit and the kept
+// weight sum (same base-2 shift as the row's partial sums).
+struct RowTrunc {
+  float thr;
+  float s_kept;
+};
+
 // Per (request, slice) best chunk of a two-level Gumbel-max draw.
 struct Pick {
   float v1;     // best score
@@ -74,7 +81,7 @@ struct VerifyPlan {
   int S;          // row slices
   int S2;         // chunk slices of the residual / bonus pass
   int cps;        // chunks per chunk slice
-  size_t off_part, off_pick, off_cnt, bytes;
+  size_t off_part, off_pick, off_cnt, off_trunc, off_cmax, bytes;
 };
 VerifyPlan plan_verify(int logits_dtype, int32_t B, int32_t gamma, int32_t V, bool aligned);
 
@@ -85,7 +92,9 @@ struct MarkovPlan {
 MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d);
 
 struct StatsPlan {
-  size_t off_sums, bytes;
+  int sliced;  // 1: (row pair, segment) item kernels; 0: one workgroup per row pair
+  int P;       // segments per row pair
+  size_t off_part, off_l1, off_lse, bytes;
 };
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 

@@ -22,6 +22,7 @@
 //    evaluates the confidence head.
 #include "common.hpp"
 #include "internal.hpp"
+#include "truncate.hpp"
 
 namespace dspark {
 namespace {
@@ -274,11 +275,78 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
 // One workgroup per request.  All waves combine the chunk partials; then wave
 // 0 draws the token inside the chosen chunk (lane l scores tokens 4l..4l+3 with
 // one Philox block) while waves 1-3 evaluate the confidence head.
+// One proposal row of scaled logits z (fp32), 4 tokens per load.
+struct QzRow {
+  const float* p;
+  int V;
+  bool vec4;
+  __device__ float operator()(int v) const { return p[v]; }
+  __device__ void load4(int v0, float* o) const {
+    if (vec4 && v0 + 3 < V) {
+      const float4 u = *reinterpret_cast<const float4*>(p + v0);
+      o[0] = u.x;
+      o[1] = u.y;
+      o[2] = u.z;
+      o[3] = u.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? p[v0 + e] : neg_inf();
+    }
+  }
+};
+
+// Level-1 scores of the two-level draw restricted to the kept set
+// (z >= thr): for each listed chunk (list[j], or j itself without a list)
+// holding kept tokens, log of its kept mass plus the chunk's Gumbel.  Wave w
+// takes entries w, w + 4, ...; four chunks' loads are issued together.
+// Returns the wave's best two (score, chunk).
+__device__ Top2 kept_chunk_scores(const QzRow& qr, int n, const int* list, float thr,
+                                  uint64_t seed, int32_t pos, uint32_t req) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Top2 best{neg_inf(), INT32_MAX, neg_inf()};
+  constexpr int kU = 4;
+  for (int j0 = wave * kU; j0 < n; j0 += kFinWaves * kU) {
+    float z[kU][4];
+    int cs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u;
+      cs[u] = j < n ? (list ? list[j] : j) : -1;
+      if (cs[u] >= 0) {
+        qr.load4(cs[u] * kChunk + 4 * lane, z[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[u][e] = neg_inf();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (cs[u] < 0) continue;  // wave-uniform
+      float mc = neg_inf();
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (z[u][e] >= thr) mc = fmaxf(mc, z[u][e]);
+      mc = wave_max(mc);
+      if (!(mc > neg_inf())) continue;
+      float w = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (z[u][e] >= thr) w += __builtin_amdgcn_exp2f((z[u][e] - mc) * kLog2e);
+      w = wave_sum(w);
+      const float score = mc + logf(w) +
+                          gumbel(seed, static_cast<uint32_t>(cs[u]), pos, req, DSPARK_TAG_DRAFT_CHUNK);
+      best = top2_merge(best, Top2{score, cs[u], neg_inf()});
+    }
+  }
+  return best;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
     const int32_t* __restrict__ xprev, int32_t xstride, const uint16_t* __restrict__ hidden,
     const uint16_t* __restrict__ embed, const float* __restrict__ conf_w,
     const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
     const uint32_t* __restrict__ request_id, const int32_t* __restrict__ position,
     uint64_t seed, int32_t gamma, int32_t k, int32_t V, int32_t d, int32_t C, int32_t cvec,
     const ChunkPart* __restrict__ part, const float* __restrict__ q_z,
@@ -291,6 +359,7 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
   __shared__ float fin_M, fin_S, fin_zx;
   __shared__ int32_t fin_x;
   __shared__ uint32_t fin_fl;
+  __shared__ TruncLds U;
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
@@ -342,6 +411,55 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
     if (sh_bad[w]) fl |= DSPARK_FLAG_NONFINITE;
   }
 
+  // 1b. truncated rows (top-k / top-p on z): the kept set's smallest value
+  // thr and weight, then the level-1 choice over kept chunks only
+  // Kept weights are 2^(z log2e - M2) with the integer shift M2, so that the
+  // drawn token's weight and the kept sum round alike (one kept token: q = 1).
+  float thr = neg_inf(), s_kept = 0.0f, M2 = 0.0f;
+  const int tk_raw = top_k[b];
+  const float tp = top_p[b];
+  const bool trunc_row = sampled && truncated(tk_raw, tp, V) && M > neg_inf() && M < pos_inf();
+  if (trunc_row) {
+    const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
+    M2 = floorf(M * kLog2e);
+    const float wa = kLog2e, wb = -M2;
+    const float total = S * __builtin_amdgcn_exp2f(fmaf(M, kLog2e, -M2));
+    const QzRow qr{q_z + row * V, V, VEC};
+    const ChunkPart* pb = part + static_cast<size_t>(b) * C;
+    auto chunk_max = [pb](int c) { return pb[c].m; };
+    bool cand = false;
+    if (chunk_bound(chunk_max, C, tk, tp, wa, wb, total, U.c)) {
+      gather_candidates(qr, V, U.c);
+      exact_cut(tk, tp, wa, wb, total, U.c);
+      cand = U.c.ok != 0;
+    }
+    int nlist = C;
+    const int* list = nullptr;
+    if (cand) {
+      thr = U.c.thr;
+      s_kept = U.c.s_kept;
+      // the kept tokens lie in the chunks whose maximum reaches thr: a
+      // prefix of the sorted chunk list
+      nlist = count_at_least(U.c.cm, U.c.nchunks, thr, U.c.cnt);
+      list = U.c.ci;
+    } else {
+      const SelResult r = select_threshold(qr, V, 32, tk, tp, wa, wb, U.s);
+      thr = r.thr;
+      s_kept = static_cast<float>(r.s_kept);
+    }
+    const Top2 tb = wave_top2(kept_chunk_scores(qr, nlist, list, thr, seed, pos, req));
+    __syncthreads();
+    if (lane == 0) {
+      sh_v1[wave] = tb.v1;
+      sh_i1[wave] = tb.i1;
+      sh_v2[wave] = tb.v2;
+    }
+    __syncthreads();
+    Bst = Top2{sh_v1[0], sh_i1[0], sh_v2[0]};
+#pragma unroll
+    for (int w = 1; w < kFinWaves; ++w) Bst = top2_merge(Bst, Top2{sh_v1[w], sh_i1[w], sh_v2[w]});
+  }
+
   if (wave == 0) {
     // 2a. the draw
     int32_t x = 0;
@@ -374,7 +492,8 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
       Top2 t{neg_inf(), INT32_MAX, neg_inf()};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (z[e] > neg_inf()) t = top2_merge(t, Top2{z[e] + gumbel_of(wv[e]), v0 + e, neg_inf()});
+        if (z[e] > neg_inf() && z[e] >= thr)
+          t = top2_merge(t, Top2{z[e] + gumbel_of(wv[e]), v0 + e, neg_inf()});
       t = wave_top2(t);
       if (t.i1 == INT32_MAX) {
         fl |= DSPARK_FLAG_EMPTY_ROW;
@@ -450,9 +569,17 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
     const int32_t x = fin_x;
     draft_tokens[row] = x;
     if (sampled) {
-      q_lse[row] = fin_M + logf(fin_S);
-      q_thr[row] = neg_inf();
-      q_tok[row] = (fin_zx > neg_inf() && fin_S > 0.0f) ? expf(fin_zx - fin_M) / fin_S : 0.0f;
+      if (trunc_row) {
+        q_lse[row] = M2 * kLn2 + logf(s_kept);
+        q_thr[row] = thr;
+        q_tok[row] = (fin_zx > neg_inf() && fin_zx >= thr && s_kept > 0.0f)
+                         ? __builtin_amdgcn_exp2f(fmaf(fin_zx, kLog2e, -M2)) / s_kept
+                         : 0.0f;
+      } else {
+        q_lse[row] = fin_M + logf(fin_S);
+        q_thr[row] = neg_inf();
+        q_tok[row] = (fin_zx > neg_inf() && fin_S > 0.0f) ? expf(fin_zx - fin_M) / fin_S : 0.0f;
+      }
     } else {
       q_lse[row] = 0.0f;
       q_thr[row] = 0.0f;
@@ -495,12 +622,14 @@ hipError_t launch_typed(const T* backbone, const int32_t* anchor, const uint16_t
     if (e != hipSuccess) return e;
     if (vec)
       DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<true>, dim3(B), dim3(kFinThreads), 0,
-                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
+                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.top_k,
+                    pol.top_p, pol.request_id,
                     pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
                     q_lse, q_thr, q_tok, confidence, flags);
     else
       DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<false>, dim3(B), dim3(kFinThreads), 0,
-                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.request_id,
+                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.top_k,
+                    pol.top_p, pol.request_id,
                     pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
                     q_lse, q_thr, q_tok, confidence, flags);
     e = hipGetLastError();

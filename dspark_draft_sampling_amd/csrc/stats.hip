@@ -13,6 +13,8 @@
 // them again (the pair was just read, so it is served from the caches) for
 // the L1 term.  stats_reduce: one workgroup computes tau and the sums in fp64
 // in a fixed order, so the sums are deterministic.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -22,6 +24,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;
+constexpr int kItemMaxWGs = 1024;      // grid of the sliced item kernels
+constexpr int kSlicedMaxPairs = 2048;  // row pairs below which the sliced path is used
 
 template <typename T, bool VEC>
 struct Vec8;
@@ -151,6 +155,212 @@ __global__ __launch_bounds__(kThreads) void stats_rows_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sliced path for small batches: (row pair, 2048-token segment) items, one
+// wave each, so that a few hundred row pairs still fill the GPU.
+//   stats_part1  per item: (max, sum) of both rows, sums with an integer
+//                base-2 shift (s = sum 2^(x log2e - floor(m log2e)))
+//   stats_part2  per item: the pair's normalisers from all its part1
+//                records, then the item's share of sum |P - T|; the second
+//                read of the pair follows the first within one call, so it
+//                is served by the Infinity Cache
+//   stats_pairs  per pair: L1, accept_rate, CE, BCE
+// Both item kernels keep the next item's loads in flight while reducing the
+// current one (two register buffers, unconditional clamped loads).
+constexpr int kSegIters = 4;  // 16-byte loads per lane per row per segment
+
+struct StatPart {
+  float md, sd, mt, st;
+};
+
+template <typename T>
+constexpr int stat_seg() {
+  return kSegIters * 64 * (16 / static_cast<int>(sizeof(T)));
+}
+
+__device__ __forceinline__ float elem16(const uint4& u, int j, uint16_t) {
+  const uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
+  return (j & 1) ? bf_hi(w) : bf_lo(w);
+}
+__device__ __forceinline__ float elem16(const uint4& u, int j, float) {
+  return __uint_as_float(j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w);
+}
+
+template <typename T>
+__device__ __forceinline__ void seg_load(const T* __restrict__ draft, const T* __restrict__ target,
+                                         int32_t V, int32_t P, int item, int lane, uint4* ud,
+                                         uint4* ut) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int SEG = stat_seg<T>();
+  const int pair = item / P, seg = item - pair * P;
+  const size_t off = static_cast<size_t>(pair) * V;
+  const int lo = seg * SEG;
+#pragma unroll
+  for (int it = 0; it < kSegIters; ++it) {
+    const int e = min(lo + (it * 64 + lane) * EPL, V - EPL);
+    ud[it] = *reinterpret_cast<const uint4*>(draft + off + e);
+    ut[it] = *reinterpret_cast<const uint4*>(target + off + e);
+  }
+}
+
+// mask the clamped loads of a partial segment with -inf
+template <typename T>
+__device__ __forceinline__ void seg_mask(int32_t V, int lo, int lane, uint4* ud, uint4* ut) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr uint32_t kNeg = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
+  if (V - lo < stat_seg<T>()) {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+      if (lo + (it * 64 + lane) * EPL >= V) ud[it] = ut[it] = make_uint4(kNeg, kNeg, kNeg, kNeg);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void seg_stats(const uint4* u, float& m, float& s) {
+  constexpr int EPL = 16 / sizeof(T);
+  m = neg_inf();
+#pragma unroll
+  for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) m = fmaxf(m, elem16(u[it], j, T{}));
+  m = wave_max(m);
+  s = 0.0f;
+  if (m > neg_inf()) {
+    const float M2 = floorf(m * kLog2e);
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) s += __builtin_amdgcn_exp2f(fmaf(elem16(u[it], j, T{}), kLog2e, -M2));
+    s = wave_sum(s);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_part1_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
+    int32_t items, StatPart* __restrict__ part) {
+  constexpr int SEG = stat_seg<T>();
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * kWaves;
+  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                            (threadIdx.x >> 6));
+  if (item >= items) return;
+  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  auto reduce = [&](uint4* ud, uint4* ut, int it_) {
+    const int seg = it_ - (it_ / P) * P;
+    seg_mask<T>(V, seg * SEG, lane, ud, ut);
+    StatPart r;
+    seg_stats<T>(ud, r.md, r.sd);
+    seg_stats<T>(ut, r.mt, r.st);
+    if (lane == 0) part[it_] = r;
+  };
+  seg_load<T>(draft, target, V, P, item, lane, ad, at);
+  while (true) {
+    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
+    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
+    reduce(ad, at, item);
+    if (n1 >= items) break;
+    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
+    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
+    reduce(bd, bt, n1);
+    if (n2 >= items) break;
+    item = n2;
+  }
+}
+
+// combine a pair's part1 records: the base-2 shift M2 of the pair and the sum
+// relative to it, for the draft (d) and target (t) rows
+__device__ __forceinline__ void pair_norm(const StatPart* __restrict__ rec, int P, int lane,
+                                          float& M2d, float& Sd, float& M2t, float& St) {
+  float md = neg_inf(), mt = neg_inf();
+  for (int i = lane; i < P; i += 64) {
+    md = fmaxf(md, rec[i].md);
+    mt = fmaxf(mt, rec[i].mt);
+  }
+  md = wave_max(md);
+  mt = wave_max(mt);
+  M2d = md > neg_inf() ? floorf(md * kLog2e) : 0.0f;
+  M2t = mt > neg_inf() ? floorf(mt * kLog2e) : 0.0f;
+  float sd = 0.0f, st = 0.0f;
+  for (int i = lane; i < P; i += 64) {
+    const StatPart r = rec[i];
+    if (r.md > neg_inf()) sd += r.sd * __builtin_amdgcn_exp2f(floorf(r.md * kLog2e) - M2d);
+    if (r.mt > neg_inf()) st += r.st * __builtin_amdgcn_exp2f(floorf(r.mt * kLog2e) - M2t);
+  }
+  Sd = wave_sum(sd);
+  St = wave_sum(st);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_part2_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
+    int32_t items, const StatPart* __restrict__ part, float* __restrict__ l1part,
+    float2* __restrict__ lse_pair) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int SEG = stat_seg<T>();
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * kWaves;
+  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                            (threadIdx.x >> 6));
+  if (item >= items) return;
+  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  auto reduce = [&](uint4* ud, uint4* ut, int it_) {
+    const int pair = it_ / P, seg = it_ - pair * P;
+    seg_mask<T>(V, seg * SEG, lane, ud, ut);
+    float M2d, Sd, M2t, St;
+    pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
+    const float isd = 1.0f / Sd, ist = 1.0f / St;
+    float acc = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        acc += fabsf(__builtin_amdgcn_exp2f(fmaf(elem16(ud[it], j, T{}), kLog2e, -M2d)) * isd -
+                     __builtin_amdgcn_exp2f(fmaf(elem16(ut[it], j, T{}), kLog2e, -M2t)) * ist);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      l1part[it_] = acc;
+      if (seg == 0) lse_pair[pair] = make_float2(M2d * kLn2 + logf(Sd), M2t * kLn2 + logf(St));
+    }
+  };
+  seg_load<T>(draft, target, V, P, item, lane, ad, at);
+  while (true) {
+    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
+    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
+    reduce(ad, at, item);
+    if (n1 >= items) break;
+    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
+    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
+    reduce(bd, bt, n1);
+    if (n2 >= items) break;
+    item = n2;
+  }
+}
+
+// one wave per row pair: L1 from the item partials, then the pair's outputs
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_pairs_kernel(
+    const T* __restrict__ draft, const int32_t* __restrict__ teacher,
+    const float* __restrict__ conf_logits, int32_t V, int32_t P, int32_t npairs,
+    const float* __restrict__ l1part, const float2* __restrict__ lse_pair, float* __restrict__ l1,
+    float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
+  const int lane = threadIdx.x & 63;
+  const int pair = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (pair >= npairs) return;
+  float acc = 0.0f;
+  for (int i = lane; i < P; i += 64) acc += l1part[static_cast<size_t>(pair) * P + i];
+  const float L1 = wave_sum(acc);
+  if (lane == 0) {
+    const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+    const int32_t tch = clamp_token(teacher[pair], V);
+    const float c = conf_logits[pair];
+    l1[pair] = L1;
+    accept_rate[pair] = a;
+    ce[pair] = lse_pair[pair].x - load_logit(draft + static_cast<size_t>(pair) * V, tch);
+    bce[pair] = fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
+  }
+}
+
 // One workgroup: per-block tau and the loss / report sums, in fp64, in a fixed
 // order (thread t owns blocks t, t + 256, ...; then one fixed tree over the
 // eight sums at once).  Every load of a block is issued before its first use.
@@ -231,12 +441,27 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                         const float* conf_logits, const uint8_t* block_mask, int32_t N,
                         int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
                         float* accept_rate, float* ce, float* bce, float* tau, float* sums,
-                        hipStream_t st) {
+                        void* ws, const StatsPlan& pl, hipStream_t st) {
   const int epl = sizeof(T) == 2 ? 8 : 4;
   const bool vec = (V % epl == 0) && reinterpret_cast<uintptr_t>(draft) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(target) % 16 == 0;
-  const dim3 grid(static_cast<unsigned>(static_cast<size_t>(N) * gamma));
-  if (N > 0) {
+  const int npairs = N * gamma;
+  if (npairs > 0 && vec && pl.sliced) {
+    char* w = static_cast<char*>(ws);
+    StatPart* part = reinterpret_cast<StatPart*>(w + pl.off_part);
+    float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
+    float2* lse = reinterpret_cast<float2*>(w + pl.off_lse);
+    const int items = npairs * pl.P;
+    const int wgs = std::min(kItemMaxWGs, (items + kWaves - 1) / kWaves);
+    DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
+                  target, V, pl.P, items, part);
+    DSPARK_LAUNCH("stats_part2", (stats_part2_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
+                  target, V, pl.P, items, part, l1part, lse);
+    DSPARK_LAUNCH("stats_pairs", (stats_pairs_kernel<T>), dim3((npairs + kWaves - 1) / kWaves),
+                  dim3(kThreads), 0, st, draft, teacher, conf_logits, V, pl.P, npairs, l1part, lse,
+                  l1, accept_rate, ce, bce);
+  } else if (npairs > 0) {
+    const dim3 grid(static_cast<unsigned>(npairs));
     if (vec)
       DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, true>), grid, dim3(kThreads), 0, st, draft,
                     target, teacher, conf_logits, V, l1, accept_rate, ce, bce);
@@ -254,12 +479,24 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
 }  // namespace
 
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
-  (void)N;
-  (void)gamma;
-  (void)V;
   StatsPlan p{};
-  p.off_sums = 0;
-  p.bytes = 0;
+  const int64_t npairs = static_cast<int64_t>(N) * gamma;
+  // bf16 segments are the larger: size the workspace for them
+  p.P = (V + stat_seg<uint16_t>() - 1) / stat_seg<uint16_t>();
+  const int Pf = (V + stat_seg<float>() - 1) / stat_seg<float>();
+  const int Pmax = p.P > Pf ? p.P : Pf;
+  p.sliced = npairs > 0 && npairs < kSlicedMaxPairs;
+  size_t off = 0;
+  if (p.sliced) {
+    const size_t items = static_cast<size_t>(npairs) * Pmax;
+    p.off_part = off;
+    off = align_up(off + items * sizeof(StatPart), 256);
+    p.off_l1 = off;
+    off = align_up(off + items * sizeof(float), 256);
+    p.off_lse = off;
+    off = align_up(off + static_cast<size_t>(npairs) * sizeof(float2), 256);
+  }
+  p.bytes = off;
   return p;
 }
 
@@ -268,15 +505,18 @@ hipError_t launch_stats(const void* draft, const void* target, int dtype, const 
                         int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
                         float* accept_rate, float* ce, float* bce, float* tau, float* sums,
                         void* ws, const StatsPlan& plan, hipStream_t st) {
-  (void)ws;
-  (void)plan;
-  if (dtype == DSPARK_BF16)
+  if (dtype == DSPARK_BF16) {
+    StatsPlan pl = plan;
+    pl.P = (V + stat_seg<uint16_t>() - 1) / stat_seg<uint16_t>();
     return launch_typed(static_cast<const uint16_t*>(draft), static_cast<const uint16_t*>(target),
                         teacher, conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf, l1,
-                        accept_rate, ce, bce, tau, sums, st);
+                        accept_rate, ce, bce, tau, sums, ws, pl, st);
+  }
+  StatsPlan pl = plan;
+  pl.P = (V + stat_seg<float>() - 1) / stat_seg<float>();
   return launch_typed(static_cast<const float*>(draft), static_cast<const float*>(target), teacher,
                       conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf, l1, accept_rate,
-                      ce, bce, tau, sums, st);
+                      ce, bce, tau, sums, ws, pl, st);
 }
 
 }  // namespace dspark

@@ -1,0 +1,443 @@
+// truncate.hpp — top-k / top-p thresholds of one logits row, computed by one
+// 256-thread workgroup with a radix select over order-preserving float keys.
+//
+// Policy ("[2/3] feat(dsv4): implement exact DSpark speculative decoding",
+// "Exact decoding semantics", "Probabilistic": temperature, top-k and top-p
+// shape both p and q), with the library's reading of order and ties:
+//   top-k keeps every token whose value is >= the k-th largest value (ties
+//   with it kept); top-p then keeps, on the renormalised top-k set, every
+//   value group whose strictly-larger groups hold less than top_p of the mass
+//   (top_p <= 0 keeps the largest group).
+//
+// Keys: a float maps to a 32-bit key whose unsigned order is the float order.
+// Each histogram level bins the keys that share the bits chosen so far by the
+// next 11 (or 10 / 5) bits, counting elements (top-k) or summing their
+// weights in fp64 (top-p).  bf16 rows resolve in two levels (16 key bits),
+// fp32 rows in three.
+#pragma once
+
+#include "common.hpp"
+
+namespace dspark {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelBins = 2048;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+struct SelLds {
+  uint32_t cnt[kSelBins];
+  double mass[kSelBins];
+  uint32_t tc[kSelThreads];
+  double tm[kSelThreads];
+  int bin;
+  uint32_t above_c;
+  double above_m;
+  double total_m;
+  uint32_t total_c;
+};
+
+struct SelResult {
+  float thr;      // smallest kept value
+  double s_kept;  // total weight of the kept tokens
+};
+
+// One histogram level over the row: tokens with key >= kmin whose key bits at
+// and above `top` equal `prefix` are binned by key bits [shift, top).
+template <class Row>
+__device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int shift, uint32_t kmin,
+                          float wa, float wb, SelLds& S) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kSelBins; i += kSelThreads) {
+    S.cnt[i] = 0u;
+    S.mass[i] = 0.0;
+  }
+  if (tid == 0) S.total_m = 0.0;
+  __syncthreads();
+  const uint32_t mask = (1u << (top - shift)) - 1u;
+  double local = 0.0;
+  for (int v = tid; v < V; v += kSelThreads) {
+    const float x = row(v);
+    if (!(x > neg_inf()) || x != x) continue;
+    const uint32_t k = order_key(x);
+    if (k < kmin) continue;
+    if (top < 32 && (k >> top) != prefix) continue;
+    const int bin = static_cast<int>((k >> shift) & mask);
+    const double w = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, wa, wb)));
+    atomicAdd(&S.cnt[bin], 1u);
+    atomicAdd(&S.mass[bin], w);
+    local += w;
+  }
+  atomicAdd(&S.total_m, local);  // the level's total weight
+  __syncthreads();
+}
+
+// First bin, scanning from the largest keys down, at which the running count
+// (by_mass = false) or weight (true) including the bin reaches `target`; if
+// the whole level holds less, the smallest non-empty bin.  Leaves the bin and
+// the count / weight strictly above it in S.
+__device__ void sel_find(SelLds& S, int nbins, bool by_mass, double target) {
+  const int tid = threadIdx.x;
+  constexpr int per = kSelBins / kSelThreads;  // 8 bins per thread, descending
+  uint32_t c = 0;
+  double m = 0.0;
+  for (int j = 0; j < per; ++j) {
+    const int bin = nbins - 1 - (tid * per + j);
+    if (bin >= 0) {
+      c += S.cnt[bin];
+      m += S.mass[bin];
+    }
+  }
+  S.tc[tid] = c;
+  S.tm[tid] = m;
+  __syncthreads();
+  if (tid == 0) {
+    // exclusive scan in descending-key order
+    uint32_t ac = 0;
+    double am = 0.0;
+    for (int t = 0; t < kSelThreads; ++t) {
+      const uint32_t xc = S.tc[t];
+      const double xm = S.tm[t];
+      S.tc[t] = ac;
+      S.tm[t] = am;
+      ac += xc;
+      am += xm;
+    }
+    S.total_c = ac;
+    S.total_m = am;
+    S.bin = -1;
+  }
+  __syncthreads();
+  const double total = by_mass ? S.total_m : static_cast<double>(S.total_c);
+  const double tgt = target < total ? target : total;
+  uint32_t ac = S.tc[tid];
+  double am = S.tm[tid];
+  for (int j = 0; j < per; ++j) {
+    const int bin = nbins - 1 - (tid * per + j);
+    if (bin < 0) break;
+    const uint32_t bc = S.cnt[bin];
+    const double bm = S.mass[bin];
+    const double before = by_mass ? am : static_cast<double>(ac);
+    const double incl = by_mass ? am + bm : static_cast<double>(ac + bc);
+    if (bc > 0 && before < tgt && incl >= tgt) {
+      S.bin = bin;
+      S.above_c = ac;
+      S.above_m = am;
+    }
+    ac += bc;
+    am += bm;
+  }
+  __syncthreads();
+}
+
+// Thresholds of a row.  `row(v)` returns the value the policy orders by
+// (logit or scaled logit); the weight of a token is exp2(value * wa + wb).
+// keybits = 16 for bf16 rows (their key's low 16 bits are determined by the
+// sign), 32 otherwise.
+template <class Row>
+__device__ SelResult select_threshold(const Row& row, int V, int keybits, int top_k, float top_p,
+                                      float wa, float wb, SelLds& S) {
+  const int nlev = keybits == 16 ? 2 : 3;
+  const int tops[3] = {32, 21, 10};
+  const int shifts16[2] = {21, 16};
+  const int shifts32[3] = {21, 10, 0};
+  uint32_t kmin = 0u;
+  uint32_t key = 0u;
+  double s_kept = 0.0;
+  const bool use_k = top_k > 0 && top_k < V;
+  if (use_k) {
+    uint32_t prefix = 0u;
+    double need = static_cast<double>(top_k);
+    for (int l = 0; l < nlev; ++l) {
+      const int top = tops[l];
+      const int shift = keybits == 16 ? shifts16[l] : shifts32[l];
+      sel_level(row, V, prefix, top, shift, 0u, wa, wb, S);
+      sel_find(S, 1 << (top - shift), false, need);
+      const int bin = S.bin < 0 ? 0 : S.bin;
+      need -= static_cast<double>(S.above_c);
+      s_kept += S.above_m;
+      if (l == nlev - 1) s_kept += S.mass[bin];
+      prefix = (prefix << (top - shift)) | static_cast<uint32_t>(bin);
+      __syncthreads();
+    }
+    key = keybits == 16 ? ((prefix << 16) | ((prefix & 0x8000u) ? 0u : 0xffffu)) : prefix;
+    kmin = key;
+  }
+  if (top_p < 1.0f) {
+    uint32_t prefix = 0u;
+    double target = 0.0;
+    s_kept = 0.0;
+    for (int l = 0; l < nlev; ++l) {
+      const int top = tops[l];
+      const int shift = keybits == 16 ? shifts16[l] : shifts32[l];
+      sel_level(row, V, prefix, top, shift, kmin, wa, wb, S);
+      if (l == 0) {
+        // top_p applies to the renormalised (top-k) set; top_p <= 0 keeps
+        // only the largest group: the first bin with weight
+        target = top_p > 0.0f ? static_cast<double>(top_p) * S.total_m : 1e-300;
+      }
+      sel_find(S, 1 << (top - shift), true, target);
+      const int bin = S.bin < 0 ? 0 : S.bin;
+      target -= S.above_m;
+      s_kept += S.above_m;
+      if (l == nlev - 1) s_kept += S.mass[bin];
+      prefix = (prefix << (top - shift)) | static_cast<uint32_t>(bin);
+      __syncthreads();
+    }
+    key = keybits == 16 ? ((prefix << 16) | ((prefix & 0x8000u) ? 0u : 0xffffu)) : prefix;
+  }
+  return SelResult{key_value(key), s_kept};
+}
+
+__device__ __forceinline__ bool truncated(int top_k, float top_p, int V) {
+  return (top_k > 0 && top_k < V) || top_p < 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Candidate path.  Per 256-token chunk maxima bound the kept set from below:
+//  * top-k: the k-th largest chunk maximum is <= the k-th largest value (the
+//    maxima of the k best chunks are k distinct tokens);
+//  * top-p: any tau whose chunks' maxima alone carry top_p of the weight has
+//    mass(x >= tau) >= top_p * total, so the cut lies at or above tau.
+// Tokens of the chunks whose maximum reaches tau are gathered into LDS,
+// sorted, and the exact cut is taken there.  The caller falls back to
+// select_threshold when the bound cannot be formed or the candidates
+// overflow.
+constexpr int kMaxChunksSorted = 1024;  // chunk maxima sorted in LDS
+constexpr int kCandCap = 4096;          // candidate tokens held in LDS
+
+struct CandLds {
+  float cm[kMaxChunksSorted];  // chunk maxima, sorted descending
+  int ci[kMaxChunksSorted];    // their chunk indices
+  float cv[kCandCap];          // candidate values, sorted descending
+  float pw[kCandCap];          // running weight sums (inclusive)
+  float wtot[kSelThreads / 64];
+  int n;        // candidates gathered (> kCandCap: overflow)
+  int nchunks;  // chunks whose maximum reaches tau
+  int idx;      // scratch index (block maximum)
+  int cnt;      // scratch count
+  float tau;
+  float thr;
+  float s_kept;
+  int nkept;
+  int ok;  // the cut lies inside the candidates
+};
+
+// Either the candidate state or the radix-select state: they are never live
+// at the same time.
+union TruncLds {
+  CandLds c;
+  SelLds s;
+};
+
+// Bitonic sort of n2 (a power of two) values, descending; with IX the
+// indices travel along (ascending index among equal values).  All threads of
+// the workgroup take part.
+template <bool IX>
+__device__ void sort_desc(float* v, int* ix, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += kSelThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool desc = (i & k) == 0;
+          const float a = v[i], b = v[l];
+          bool a_first = a > b;
+          if constexpr (IX) a_first = a_first || (a == b && ix[i] < ix[l]);
+          else a_first = a_first || a == b;
+          if (desc != a_first) {
+            v[i] = b;
+            v[l] = a;
+            if constexpr (IX) {
+              const int t = ix[i];
+              ix[i] = ix[l];
+              ix[l] = t;
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// In-place inclusive prefix sum of a[0 .. n) (LDS), all threads.
+__device__ void block_scan_incl(float* a, int n, float* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int lo = tid * per, hi = min(n, lo + per);
+  float s = 0.0f;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  float x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  float run = x - s;
+  for (int w = 0; w < wave; ++w) run += wtot[w];
+  for (int i = lo; i < hi; ++i) {
+    run += a[i];
+    a[i] = run;
+  }
+  __syncthreads();
+}
+
+// Number of v[0 .. n) that are >= t (v sorted descending), all threads.
+__device__ int count_at_least(const float* v, int n, float t, int& slot) {
+  if (threadIdx.x == 0) slot = 0;
+  __syncthreads();
+  int c = 0;
+  for (int i = threadIdx.x; i < n; i += kSelThreads) c += v[i] >= t ? 1 : 0;
+  c = static_cast<int>(wave_sum(static_cast<float>(c)));
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(&slot, c);
+  __syncthreads();
+  const int r = slot;
+  __syncthreads();
+  return r;
+}
+
+// Sort the C chunk maxima (cmax(c)) and set L.tau and L.nchunks; returns
+// false when the bound cannot be formed.  wa, wb: the weight of a value x is
+// exp2(x wa + wb); total: the row's total weight.
+template <class ChunkMax>
+__device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p, float wa,
+                            float wb, float total, CandLds& L) {
+  if (C > kMaxChunksSorted) return false;
+  const int n2 = pow2_at_least(C);
+  for (int i = threadIdx.x; i < n2; i += kSelThreads) {
+    L.cm[i] = i < C ? cmax(i) : neg_inf();
+    L.ci[i] = i;
+  }
+  __syncthreads();
+  sort_desc<true>(L.cm, L.ci, n2);
+  float tau = neg_inf();
+  if (top_k > 0) {
+    if (top_k <= C && top_k <= kCandCap) tau = L.cm[top_k - 1];
+  } else if (top_p < 1.0f) {
+    // running weight of the sorted maxima; tau = the first maximum at which
+    // it reaches top_p * total (with a margin against rounding)
+    for (int i = threadIdx.x; i < C; i += kSelThreads)
+      L.cv[i] = L.cm[i] > neg_inf() ? __builtin_amdgcn_exp2f(fmaf(L.cm[i], wa, wb)) : 0.0f;
+    __syncthreads();
+    block_scan_incl(L.cv, C, L.wtot);
+    const float target = (top_p > 0.0f ? top_p : 0.0f) * total * 1.0009765625f;
+    if (threadIdx.x == 0) L.idx = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < C; i += kSelThreads)
+      if (L.cm[i] > neg_inf() && L.cv[i] >= target && (i == 0 || L.cv[i - 1] < target))
+        L.idx = i;  // unique: the running sum is monotone
+    __syncthreads();
+    if (L.idx >= 0) tau = L.cm[L.idx];
+  }
+  if (!(tau > neg_inf())) {
+    __syncthreads();
+    return false;
+  }
+  const int nc = count_at_least(L.cm, C, tau, L.cnt);
+  if (threadIdx.x == 0) {
+    L.tau = tau;
+    L.nchunks = nc;
+    L.n = 0;
+  }
+  __syncthreads();
+  return true;
+}
+
+// Gather every token >= tau of the chunks L.ci[0 .. L.nchunks) (wave w takes
+// chunks w, w+4, ...; lane l the 4 tokens 4l..4l+3).  Sets L.n (possibly
+// above kCandCap: overflow, nothing beyond the cap is stored).
+template <class Row>
+__device__ void gather_candidates(const Row& row, int V, CandLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float tau = L.tau;
+  for (int j = wave; j < L.nchunks; j += kSelThreads / 64) {
+    const int c = L.ci[j];
+    const int v0 = c * kChunk + lane * 4;
+    float x[4];
+    row.load4(v0, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool take = v0 + e < V && x[e] >= tau;
+      const uint64_t mask = __ballot(take);
+      int base = 0;
+      if (lane == 0 && mask) base = atomicAdd(&L.n, __popcll(mask));
+      base = __shfl(base, 0, 64);
+      if (take) {
+        const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+        if (slot < kCandCap) L.cv[slot] = x[e];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Exact cut on the gathered candidates: sorts them, applies top-k (ties
+// kept) and then top-p on the renormalised set (the first value group always
+// kept, a later group kept iff the weight strictly above it is below top_p of
+// the set's weight).  total: the row's total weight (the set's weight when
+// top-k is off).  Sets L.thr (smallest kept value), L.s_kept (kept weight),
+// L.nkept and L.ok (0: the cut is not decided by the candidates).
+__device__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds& L) {
+  const int n = L.n;
+  if (n > kCandCap || n < 1 || (top_k > 0 && top_k > n)) {
+    __syncthreads();
+    if (threadIdx.x == 0) L.ok = 0;
+    __syncthreads();
+    return;
+  }
+  const int n2 = pow2_at_least(n);
+  for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += kSelThreads) L.cv[i] = neg_inf();
+  __syncthreads();
+  sort_desc<false>(L.cv, nullptr, n2);
+  for (int i = threadIdx.x; i < n; i += kSelThreads)
+    L.pw[i] = __builtin_amdgcn_exp2f(fmaf(L.cv[i], wa, wb));
+  __syncthreads();
+  block_scan_incl(L.pw, n, L.wtot);
+  int nk = n;
+  float set_total = total;
+  if (top_k > 0) {
+    nk = count_at_least(L.cv, n, L.cv[top_k - 1], L.cnt);
+    set_total = L.pw[nk - 1];
+  }
+  int cut = nk;
+  if (top_p < 1.0f) {
+    const float target = (top_p > 0.0f ? top_p : 0.0f) * set_total;
+    if (threadIdx.x == 0) L.idx = 0;
+    __syncthreads();
+    // the last group start whose strictly-larger weight is below target
+    int best = 0;
+    for (int i = threadIdx.x; i < nk; i += kSelThreads)
+      if (i > 0 && L.cv[i] != L.cv[i - 1] && L.pw[i - 1] < target) best = i;
+    if (best > 0) atomicMax(&L.idx, best);
+    __syncthreads();
+    cut = count_at_least(L.cv, nk, L.cv[L.idx], L.cnt);
+  }
+  if (threadIdx.x == 0) {
+    L.nkept = cut;
+    L.thr = L.cv[cut - 1];
+    L.s_kept = L.pw[cut - 1];
+    // with top-k the set is all candidates' business; top-p alone needs the
+    // candidates to carry the target weight, else the cut may lie below tau
+    bool ok = true;
+    if (top_k <= 0 && top_p < 1.0f) ok = L.pw[n - 1] >= (top_p > 0.0f ? top_p : 0.0f) * total;
+    L.ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+}
+
+}  // namespace dspark

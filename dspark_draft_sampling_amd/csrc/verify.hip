@@ -29,6 +29,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "truncate.hpp"
 
 namespace dspark {
 namespace {
@@ -110,12 +111,45 @@ __device__ __forceinline__ void rows_load(const T* __restrict__ target, int32_t 
     u[it] = L::load(rp, min(lo + (it * 64 + lane) * EPL, V - EPL));
 }
 
+// Per 256-token chunk maxima of one segment (vector paths only: a chunk is
+// 32 lanes x 8 bf16 or 64 lanes x 4 fp32 of one load iteration).
+template <typename T, bool VEC>
+__device__ __forceinline__ void rows_chunk_max(const typename RowLoad<T, VEC>::Raw* u, int lo,
+                                               int V, int C, int lane, float* __restrict__ cmax) {
+  if constexpr (VEC) {
+    constexpr int ITERS = kVecIters;
+    constexpr int EPL = RowLoad<T, VEC>::EPL;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      float m = neg_inf();
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m = fmaxf(m, elem(u[it], e, T{}));
+      m = fmaxf(m, dpp_f<kDppXor1>(m));
+      m = fmaxf(m, dpp_f<kDppXor2>(m));
+      m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+      m = fmaxf(m, dpp_f<kDppMirror>(m));
+      const float r0 = lane_f(m, 0), r1 = lane_f(m, 16), r2 = lane_f(m, 32), r3 = lane_f(m, 48);
+      if (lane == 0) {
+        const int c0 = (lo + it * 64 * EPL) >> 8;  // first chunk of this iteration
+        if (EPL == 8) {
+          if (c0 < C) cmax[c0] = fmaxf(r0, r1);
+          if (c0 + 1 < C) cmax[c0 + 1] = fmaxf(r2, r3);
+        } else {
+          if (c0 < C) cmax[c0] = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+        }
+      }
+    }
+  }
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void rows_reduce(typename RowLoad<T, VEC>::Raw* u, int item,
                                             int32_t P, int32_t G1, int32_t vlen, int lane,
                                             const uint8_t* __restrict__ mode,
                                             const float* __restrict__ temperature,
-                                            RowPart* __restrict__ part) {
+                                            const int32_t* __restrict__ top_k,
+                                            const float* __restrict__ top_p,
+                                            float* __restrict__ cmax, RowPart* __restrict__ part) {
   using L = RowLoad<T, VEC>;
   constexpr int ITERS = VEC ? kVecIters : kScalarIters;
   constexpr int EPL = L::EPL;
@@ -170,6 +204,10 @@ __device__ __forceinline__ void rows_reduce(typename RowLoad<T, VEC>::Raw* u, in
       sum = wave_sum(sum);
     }
     if (m == pos_inf() || !(sum < pos_inf())) fl |= DSPARK_FLAG_NONFINITE;
+    if (truncated(top_k[b], top_p[b], V)) {
+      const int C = (V + kChunk - 1) / kChunk;
+      rows_chunk_max<T, VEC>(u, lo, V, C, lane, cmax + static_cast<size_t>(row) * C);
+    }
   }
   if (lane == 0) part[static_cast<size_t>(row) * P + seg] = RowPart{m, sum, arg, fl};
 }
@@ -178,7 +216,8 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
     const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P, int32_t items,
     const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
-    const int32_t* __restrict__ n_draft, RowPart* __restrict__ part,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
+    const int32_t* __restrict__ n_draft, RowPart* __restrict__ part, float* __restrict__ cmax,
     uint32_t* __restrict__ counters, int32_t B) {
   using L = RowLoad<T, VEC>;
   constexpr int ITERS = VEC ? kVecIters : kScalarIters;
@@ -213,13 +252,98 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   while (true) {
     const int n1 = __builtin_amdgcn_readfirstlane(next_live(item + nwaves));
     rows_load<T, VEC>(target, V, P, n1 < items ? n1 : item, lane, ub);
-    rows_reduce<T, VEC>(ua, item, P, G1, V, lane, mode, temperature, part);
+    rows_reduce<T, VEC>(ua, item, P, G1, V, lane, mode, temperature, top_k, top_p, cmax, part);
     if (n1 >= items) break;
     const int n2 = __builtin_amdgcn_readfirstlane(next_live(n1 + nwaves));
     rows_load<T, VEC>(target, V, P, n2 < items ? n2 : n1, lane, ua);
-    rows_reduce<T, VEC>(ub, n1, P, G1, V, lane, mode, temperature, part);
+    rows_reduce<T, VEC>(ub, n1, P, G1, V, lane, mode, temperature, top_k, top_p, cmax, part);
     if (n2 >= items) break;
     item = n2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Truncation pass: one workgroup per target row of a sampled request whose
+// policy has top-k or top-p; every other workgroup returns at once.  Finds the
+// smallest kept logit and the kept weight sum 2^(l cT - M2) (same shift M2 as
+// the row pass) by radix selection.
+template <typename T>
+struct LogitRow {
+  const T* p;
+  int V;
+  bool vec4;  // 4 consecutive logits per aligned load
+  __device__ float operator()(int v) const { return load_logit(p, v); }
+  __device__ void load4(int v0, float* o) const {
+    if (vec4 && v0 + 3 < V) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p + v0);
+        o[0] = bf_lo(u.x);
+        o[1] = bf_hi(u.x);
+        o[2] = bf_lo(u.y);
+        o[3] = bf_hi(u.y);
+      } else {
+        const float4 u = *reinterpret_cast<const float4*>(p + v0);
+        o[0] = u.x;
+        o[1] = u.y;
+        o[2] = u.z;
+        o[3] = u.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? load_logit(p, v0 + e) : neg_inf();
+    }
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
+    const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P, int32_t have_cmax,
+    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
+    const int32_t* __restrict__ n_draft, const RowPart* __restrict__ part,
+    const float* __restrict__ cmax, RowTrunc* __restrict__ trunc) {
+  __shared__ TruncLds U;
+  __shared__ float sh_m[kSelThreads / 64], sh_s[kSelThreads / 64];
+  const int G1 = gamma + 1;
+  const int row = blockIdx.x, b = row / G1, k = row - b * G1;
+  const float Tb = temperature[b];
+  const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
+  const int tk_raw = top_k[b];
+  const float tp = top_p[b];
+  if (!sampled || !truncated(tk_raw, tp, V) || k > n_draft_of(n_draft, b, gamma)) return;
+  const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
+  // row maximum, its base-2 shift and the total weight, from the row pass
+  const float cT = kLog2e / Tb;
+  float m = neg_inf();
+  for (int i = threadIdx.x; i < P; i += kSelThreads)
+    m = fmaxf(m, part[static_cast<size_t>(row) * P + i].m);
+  m = block_max<kSelThreads / 64>(m, sh_m);
+  const float M2 = (m > neg_inf() && m < pos_inf()) ? shift_of(m, cT) : 0.0f;
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < P; i += kSelThreads) {
+    const RowPart q = part[static_cast<size_t>(row) * P + i];
+    if (q.m > neg_inf()) s += q.s * __builtin_amdgcn_exp2f(shift_of(q.m, cT) - M2);
+  }
+  const float total = block_sum<kSelThreads / 64>(s, sh_s);
+  const T* rp = target + static_cast<size_t>(row) * V;
+  const LogitRow<T> lr{rp, V, (V % 4 == 0) && reinterpret_cast<uintptr_t>(target) % 16 == 0};
+  const int C = (V + kChunk - 1) / kChunk;
+  bool done = false;
+  if (have_cmax) {
+    const float* cm = cmax + static_cast<size_t>(row) * C;
+    auto chunk_max = [cm](int c) { return cm[c]; };
+    if (chunk_bound(chunk_max, C, tk, tp, cT, -M2, total, U.c)) {
+      gather_candidates(lr, V, U.c);
+      exact_cut(tk, tp, cT, -M2, total, U.c);
+      if (U.c.ok) {
+        if (threadIdx.x == 0) trunc[row] = RowTrunc{U.c.thr, U.c.s_kept};
+        done = true;
+      }
+    }
+  }
+  if (!done) {  // radix selection over the whole row
+    const SelResult r = select_threshold(lr, V, sizeof(T) == 2 ? 16 : 32, tk, tp, cT, -M2, U.s);
+    if (threadIdx.x == 0) trunc[row] = RowTrunc{r.thr, static_cast<float>(r.s_kept)};
   }
 }
 
@@ -234,8 +358,8 @@ struct Decision {
 };
 
 __device__ __forceinline__ float draw_weight(int kind, float l, float zq, float cT, float M2,
-                                             float inv_s, float lse_q, float thr_q) {
-  if (!(l > neg_inf())) return 0.0f;
+                                             float inv_s, float lse_q, float thr_q, float thr_p) {
+  if (!(l > neg_inf()) || !(l >= thr_p)) return 0.0f;
   const float e = __builtin_amdgcn_exp2f(fmaf(l, cT, -M2));
   if (kind != 1) return e;  // bonus / fallback: unnormalised p
   const float q =
@@ -272,12 +396,15 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     const float* __restrict__ q_z, const float* __restrict__ q_lse,
     const float* __restrict__ q_thr, const float* __restrict__ q_tok,
     const int32_t* __restrict__ n_draft, const uint8_t* __restrict__ mode,
-    const float* __restrict__ temperature, const uint32_t* __restrict__ request_id,
+    const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const uint32_t* __restrict__ request_id,
     const int32_t* __restrict__ position, uint64_t seed, int32_t gamma, int32_t V, int32_t P,
-    int32_t S2, const RowPart* __restrict__ part, Pick* __restrict__ picks,
+    int32_t S2, const RowPart* __restrict__ part, const RowTrunc* __restrict__ trunc,
+    Pick* __restrict__ picks,
     uint32_t* __restrict__ counters, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ out_tokens, uint8_t* __restrict__ flags) {
-  __shared__ float rm[DSPARK_MAX_GAMMA + 1], rs[DSPARK_MAX_GAMMA + 1], rM2[DSPARK_MAX_GAMMA + 1];
+  __shared__ float rm[DSPARK_MAX_GAMMA + 1], rs[DSPARK_MAX_GAMMA + 1], rM2[DSPARK_MAX_GAMMA + 1],
+      rthr[DSPARK_MAX_GAMMA + 1];
   __shared__ int32_t rarg[DSPARK_MAX_GAMMA + 1];
   __shared__ uint32_t rfl[DSPARK_MAX_GAMMA + 1];
   __shared__ Decision dec;
@@ -297,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   const int C = (V + kChunk - 1) / kChunk;
   const uint32_t req = request_id[b];
   const int32_t pos0 = position[b];
+  const bool trunc_row = sampled && truncated(top_k[b], top_p[b], V);
 
   // proposal-side values of the accept scan, fetched up front (thread k-1
   // owns proposal k)
@@ -333,6 +461,13 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     }
     if (lane == 0) {
       if (!(am.v > neg_inf())) fl |= DSPARK_FLAG_EMPTY_ROW;
+      float thr = neg_inf();
+      if (trunc_row) {  // kept set of the truncated policy
+        const RowTrunc t = trunc[b * G1 + r];
+        thr = t.thr;
+        s = t.s_kept;
+      }
+      rthr[r] = thr;
       rm[r] = am.v;
       rs[r] = s;
       rM2[r] = M2;
@@ -351,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
         stop = xk != t;
       } else {
         const float s = rs[lane];
-        const float p = (lx > neg_inf() && s > 0.0f)
+        const float p = (lx > neg_inf() && lx >= rthr[lane] && s > 0.0f)
                             ? __builtin_amdgcn_exp2f(fmaf(lx, cT, -rM2[lane])) / s
                             : 0.0f;
         const float u = accept_uniform(seed, pos0 + lane + 1, req);
@@ -424,6 +559,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   const float inv_s = rs[d.srow] > 0.0f ? 1.0f / rs[d.srow] : 0.0f;
   const float lse_q = d.kind == 1 ? q_lse[b * gamma + d.srow] : 0.0f;
   const float thr_q = d.kind == 1 ? q_thr[b * gamma + d.srow] : 0.0f;
+  const float thr_p = rthr[d.srow];
 
   // wave-level best of chunks c0 + wave + 4 i (i < kChunksPerWave)
   auto wave_chunks = [&](int kind, int c0) -> Top2 {
@@ -449,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
       float w = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w += draw_weight(kind, l[i][e], zq[i][e], cT, M2, inv_s, lse_q, thr_q);
+        w += draw_weight(kind, l[i][e], zq[i][e], cT, M2, inv_s, lse_q, thr_q, thr_p);
       w = wave_sum(w);
       if (lane == i) mine = w;  // lane i scores chunk i of this wave
     }
@@ -516,9 +652,9 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
       const float l = load_logit(trow, v);
       float lw = neg_inf();
       if (kind == 1) {
-        const float w = draw_weight(1, l, q_z[qoff + v], cT, M2, inv_s, lse_q, thr_q);
+        const float w = draw_weight(1, l, q_z[qoff + v], cT, M2, inv_s, lse_q, thr_q, thr_p);
         lw = w > 0.0f ? logf(w) : neg_inf();
-      } else if (l > neg_inf()) {
+      } else if (l > neg_inf() && l >= thr_p) {
         lw = (l - rm[d.srow]) / Tb;
       }
       if (lw > neg_inf())
@@ -544,26 +680,37 @@ hipError_t launch_typed(const T* target, const int32_t* draft, const float* q_z,
   uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
   const int items = B * (gamma + 1) * pl.S;
   const int wgs = std::min(kRowsMaxWGs, (items + kWaves - 1) / kWaves);
+  float* cmax = reinterpret_cast<float*>(w + pl.off_cmax);
   if (pl.vec)
     DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, true>), dim3(wgs), dim3(kThreads), 0, st,
-                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, n_draft, part, cnt, B);
+                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, pol.top_k, pol.top_p,
+                  n_draft, part, cmax, cnt, B);
   else
     DSPARK_LAUNCH("verify_rows", (verify_rows_kernel<T, false>), dim3(wgs), dim3(kThreads), 0, st,
-                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, n_draft, part, cnt, B);
+                  target, V, gamma, pl.S, items, pol.mode, pol.temperature, pol.top_k, pol.top_p,
+                  n_draft, part, cmax, cnt, B);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RowTrunc* trunc = reinterpret_cast<RowTrunc*>(w + pl.off_trunc);
+  DSPARK_LAUNCH("verify_select", (verify_select_kernel<T>), dim3(B * (gamma + 1)),
+                dim3(kSelThreads), 0, st, target, V, gamma, pl.S, pl.vec, pol.mode,
+                pol.temperature, pol.top_k, pol.top_p, n_draft, part, cmax, trunc);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool vec4 = V % 4 == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(q_z) % 16 == 0;
   if (vec4)
     DSPARK_LAUNCH("verify_decide", (verify_decide_kernel<T, true>), dim3(pl.S2, B),
                   dim3(kThreads), 0, st, target, draft, q_z, q_lse, q_thr, q_tok, n_draft,
-                  pol.mode, pol.temperature, pol.request_id, pol.position, seed, gamma, V, pl.S,
-                  pl.S2, part, picks, cnt, accept_len, out_tokens, flags);
+                  pol.mode, pol.temperature, pol.top_k, pol.top_p, pol.request_id, pol.position,
+                  seed, gamma, V, pl.S, pl.S2, part, trunc, picks, cnt, accept_len, out_tokens,
+                  flags);
   else
     DSPARK_LAUNCH("verify_decide", (verify_decide_kernel<T, false>), dim3(pl.S2, B),
                   dim3(kThreads), 0, st, target, draft, q_z, q_lse, q_thr, q_tok, n_draft,
-                  pol.mode, pol.temperature, pol.request_id, pol.position, seed, gamma, V, pl.S,
-                  pl.S2, part, picks, cnt, accept_len, out_tokens, flags);
+                  pol.mode, pol.temperature, pol.top_k, pol.top_p, pol.request_id, pol.position,
+                  seed, gamma, V, pl.S, pl.S2, part, trunc, picks, cnt, accept_len, out_tokens,
+                  flags);
   return hipGetLastError();
 }
 
@@ -586,6 +733,10 @@ VerifyPlan plan_verify(int dtype, int32_t B, int32_t gamma, int32_t V, bool alig
   off = align_up(off + static_cast<size_t>(B) * p.S2 * sizeof(Pick), 256);
   p.off_cnt = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(uint32_t), 256);
+  p.off_trunc = off;
+  off = align_up(off + static_cast<size_t>(B) * (gamma + 1) * sizeof(RowTrunc), 256);
+  p.off_cmax = off;
+  off = align_up(off + static_cast<size_t>(B) * (gamma + 1) * C * sizeof(float), 256);
   p.bytes = off;
   return p;
 }
