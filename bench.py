@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="instead of the benchmark, write the rocprofv3 summary of the "
+                         "profiling run under DIR to profiles/")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -76,15 +79,132 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
         return 2 * B * (g + 1) * V
     if name == "verify_decide":    # the proposal row of each rejecting request
         return 4 * V * R
-    if name == "stats_rows":       # draft + target row pairs
+    if name == "verify_select":    # second look at truncated rows (cached): not compulsory
+        return 0
+    if name in ("stats_rows", "stats_part1"):  # draft + target row pairs, first look
         return 2 * 2 * B * g * V
-    if name == "stats_reduce":
+    if name == "stats_part2":      # second look at the same rows: not compulsory
+        return 0
+    if name in ("stats_pairs", "stats_reduce"):
         return 16 * B * g
     return 0
 
 
+PROFILE = os.path.join(ROOT, "profiles", "decode_step_B64_g5_V129280.md")
+CSRC = os.path.join(ROOT, "dspark_draft_sampling_amd", "csrc")
+
+
+def source_digest():
+    """sha256 over the kernel sources (file names and contents, sorted)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (copy-calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary was
+    taken on other kernel sources."""
+    try:
+        text = open(PROFILE).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return int(k["read_bytes"] + k["write_bytes"])
+
+
+def summarize_profile(base, out):
+    """Write the rocprofv3 summary (kernel trace + copy-calibrated HBM
+    counters) of a profiling run whose outputs are under `base`."""
+    import collections
+    import csv
+
+    def agg(path):
+        d = collections.defaultdict(list)
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in d.items()}
+
+    ours = ("markov", "verify", "stats")
+    with open(f"{base}/prof_kt/kt_kernel_stats.csv") as fh:
+        stats = [r for r in csv.DictReader(fh) if r["Name"].startswith(ours)]
+    fetch = agg(f"{base}/prof_FETCH_SIZE/p_counter_collection.csv")
+    write = agg(f"{base}/prof_WRITE_SIZE/p_counter_collection.csv")
+    copy = "__amd_rocclr_copyBuffer"
+    cf = agg(f"{base}/prof_copy_FETCH_SIZE/p_counter_collection.csv")[copy]
+    cw = agg(f"{base}/prof_copy_WRITE_SIZE/p_counter_collection.csv")[copy]
+    true_kib = 256 * 1024
+    sf, sw = true_kib / cf, true_kib / cw
+    cmd = "python3 bench.py"
+    lines = [
+        "# Decode step (Markov sample + verify + accept stats), B=64, gamma=5, V=129280, bf16, sampled",
+        "",
+        "Commands, from the repository root after `cd /tmp && export TMPDIR=/tmp` (paths "
+        "absolute on the run; `python3 bench.py --summarize-profile gpurun_out` wrote this file):",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats -T -f csv -d gpurun_out/prof_kt -o kt -- {cmd} --steps 50 --warmup 5 --no-cpu",
+        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
+        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d gpurun_out/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
+        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
+        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d gpurun_out/prof_copy_WRITE_SIZE -o p -- {cmd} --copy-calibration 256",
+        "```",
+        "",
+        "## Kernel time (`--kernel-trace --stats`)",
+        "",
+        "| kernel | calls | average µs | min µs | max µs | share % |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in stats:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    lines += [
+        "",
+        "## HBM bytes per dispatch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)",
+        "",
+        f"Calibration: a 256 MiB device copy (`{copy}`) reads {cf:.0f} KiB of FETCH_SIZE and "
+        f"{cw:.0f} KiB of WRITE_SIZE per dispatch against {true_kib} KiB moved each way, so "
+        f"FETCH_SIZE is scaled by {sf:.3f} and WRITE_SIZE by {sw:.3f}.",
+        "",
+        "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+        "|---|---|---|---|---|",
+    ]
+    rec = dict(source_sha256=source_digest(), fetch_scale=sf, write_scale=sw, kernels={})
+    for k in sorted(fetch):
+        if not k.startswith(ours):
+            continue
+        rd, wr = fetch[k] * sf * 1024, write.get(k, 0.0) * sw * 1024
+        name = k.replace("_kernel", "")
+        avg = next((float(r["AverageNs"]) / 1e3 for r in stats if r["Name"] == k), None)
+        rec["kernels"][name] = dict(read_bytes=round(rd), write_bytes=round(wr), avg_us=avg)
+        lines.append(f"| {k} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+    lines += ["", "Machine-readable copy (bench.py fills `roofline.traffic` from it while the "
+              "kernel sources still hash to `source_sha256`):", "", "```json",
+              json.dumps(rec, indent=1), "```"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, PROFILE)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -183,7 +303,8 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
     ach = kernels[dom]["gbs"]
     roofline = dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(ach / HBM_PEAK_GBS, 4),
+                    traffic=counter_traffic(dom))
     step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
 
     cpu = None
