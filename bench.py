@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--markov-plan", choices=["auto", "per-step"], default="auto",
+                    help="Markov launch plan: one cooperative launch when it fits (auto) or "
+                         "two launches per step")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="instead of the benchmark, write the rocprofv3 summary of the "
                          "profiling run under DIR to profiles/")
@@ -71,10 +74,14 @@ def copy_calibration(mib):
 def kernel_bytes(name, B, g, V, r, d, S, R):
     """Algorithmic (compulsory) HBM bytes of one launch of each kernel."""
     C = (V + 255) // 256
+    if name == "markov_fused":     # one launch for all gamma steps: backbone, q, W2 once, A rows
+        return 2 * B * g * V + 4 * S * g * V + 2 * r * V + 2 * B * g * r
     if name == "markov_step":      # backbone row + q row written + W2 (once per call) + A rows
         return 2 * B * V + 4 * S * V + (2 * r * V) / g + 2 * B * r
-    if name == "markov_finalize":  # chunk partials + h and embedding rows + chosen-chunk z
-        return 16 * B * C + 4 * B * d + 4 * 256 * S
+    if name == "markov_confidence":  # h row + embedding row per draft row, w once
+        return 4 * B * g * d + 8 * d
+    if name == "markov_finalize":  # chunk partials + chosen-chunk z
+        return 16 * B * C + 4 * 256 * S
     if name == "verify_rows":      # every target row once
         return 2 * B * (g + 1) * V
     if name == "verify_decide":    # the proposal row of each rejecting request
@@ -218,6 +225,7 @@ def main():
     import dspark_draft_sampling_amd as ds
     from workloads import decode_inputs
 
+    ds.markov_plan(ds.MARKOV_AUTO if args.markov_plan == "auto" else ds.MARKOV_PER_STEP)
     t0 = time.time()
     inp = decode_inputs("decode")
     B, g, V, r, d = inp["B"], inp["gamma"], inp["V"], inp["r"], inp["d"]
@@ -316,7 +324,8 @@ def main():
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload="decode verify: Markov sample + sampled verify + accept stats",
                             B=B, gamma=g, V=V, r=r, d=d, logits="bf16", temperature=1.0,
-                            truncation="none", mode="sampled", rotated_batches=len(sets)),
+                            truncation="none", mode="sampled", rotated_batches=len(sets),
+                            markov_plan=args.markov_plan),
                 roofline=roofline, cpu_baseline=cpu,
                 step=dict(alg_bytes=int(step_bytes),
                           alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

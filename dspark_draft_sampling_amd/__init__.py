@@ -70,6 +70,8 @@ def lib():
         L.dspark_accept_stats.restype = C.c_int
         L.dspark_profile_enable.argtypes = [C.c_int]
         L.dspark_profile_enable.restype = C.c_int
+        L.dspark_markov_plan.argtypes = [C.c_int]
+        L.dspark_markov_plan.restype = C.c_int
         L.dspark_profile_summary.argtypes = [C.c_char_p, sz]
         L.dspark_profile_summary.restype = C.c_int
         _lib = L
@@ -254,6 +256,18 @@ def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_
 
 def profile_enable(on=True):
     lib().dspark_profile_enable(1 if on else 0)
+
+
+MARKOV_AUTO, MARKOV_PER_STEP = 0, 1
+
+
+def markov_plan(plan):
+    """Set the Markov launch plan (MARKOV_AUTO or MARKOV_PER_STEP, process-wide);
+    returns the previous one."""
+    prev = lib().dspark_markov_plan(int(plan))
+    if prev < 0:
+        raise DSparkError(f"unknown Markov plan {plan}")
+    return prev
 
 
 def profile_summary():

@@ -96,7 +96,7 @@ dspark_status dspark_markov_sample(
   const hipError_t e = dspark::launch_markov(
       backbone_logits, logits_dtype, anchor, markov_w1, markov_w2, hidden, embed, conf_w, policy,
       seed, B, gamma, V, r, d, draft_tokens, q_logits, q_lse, q_thr, q_tok, confidence, flags,
-      workspace, plan, static_cast<hipStream_t>(stream));
+      workspace, plan, dspark::markov_plan_mode(), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "dspark.h"
@@ -87,7 +89,7 @@ VerifyPlan plan_verify(int logits_dtype, int32_t B, int32_t gamma, int32_t V, bo
 
 struct MarkovPlan {
   int C;  // chunks per row
-  size_t off_part, bytes;
+  size_t off_part, off_sync, bytes;
 };
 MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d);
 
@@ -110,7 +112,10 @@ hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
                          uint64_t seed, int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d,
                          int32_t* draft_tokens, float* q_z, float* q_lse, float* q_thr,
                          float* q_tok, float* confidence, uint8_t* flags, void* ws,
-                         const MarkovPlan& plan, hipStream_t st);
+                         const MarkovPlan& plan, int plan_mode, hipStream_t st);
+
+// Launch plan of the Markov sampler (DSPARK_MARKOV_AUTO / _PER_STEP).
+int markov_plan_mode();
 
 hipError_t launch_stats(const void* draft, const void* target, int dtype, const int32_t* teacher,
                         const float* conf_logits, const uint8_t* block_mask, int32_t N,

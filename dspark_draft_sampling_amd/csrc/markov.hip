@@ -7,19 +7,33 @@
 // anchor), q_k = policy(y_k), x_k ~ q_k (argmax for greedy requests); the full
 // q_k and the confidence c_k = sigmoid(w . [h_k ; embed(x_{k-1})]) are kept.
 //
-// Each step k is two launches:
-//  * markov_step: one workgroup per (256-token chunk, 64-request tile).  The
-//    bias tile bias[v, b] = sum_i W2[v, i] W1[x_{k-1}(b), i] is a bf16 MFMA
-//    product (v_mfma_f32_16x16x32_bf16) with the vocabulary as the M side, so
-//    each lane's accumulators hold 4 consecutive tokens of one request and the
+// Every step has two phases:
+//  * stream: per (16 MS-token group, 64-request tile) of one wave, the bias tile
+//    bias[v, b] = sum_i W2[v, i] W1[x_{k-1}(b), i] is a bf16 MFMA product
+//    (v_mfma_f32_16x16x32_bf16) with the vocabulary as the M side, so each
+//    lane's accumulators hold 4 consecutive tokens of one request and the
 //    epilogue reads the backbone with 8-byte loads and writes z = y / T with
-//    16-byte stores.  The epilogue also reduces each request's chunk to
-//    (max z, lowest argmax, sum exp(z - max)) for the sampler.
-//  * markov_finalize: one workgroup per request.  Combines the chunk partials
-//    into the log-normaliser, picks the chunk by Gumbel-max over the chunk
-//    log-masses and the token inside it by Gumbel-max over its 256 z values
-//    (two-level Gumbel-max: exact, no prefix sum over the vocabulary), and
-//    evaluates the confidence head.
+//    16-byte stores.  The epilogue reduces each request's 256-token chunk to
+//    (max z, lowest argmax, sum exp(z - max), ln mass + chunk Gumbel).
+//  * finalize, per request: combines the chunk partials into the
+//    log-normaliser, picks the chunk by Gumbel-max over the chunk log-masses
+//    and the token inside it by Gumbel-max over its 256 z values (two-level
+//    Gumbel-max: exact, no prefix sum over the vocabulary), and applies
+//    top-k / top-p when the request truncates.
+// The confidence head needs only x_{k-1}, so one kernel evaluates it for every
+// row after the last step.
+//
+// Two launch plans run these phases:
+//  * fused: one cooperative launch for all gamma steps.  Workgroup g owns the
+//    512 tokens [512 g, 512 g + 512) and keeps their W2 rows in registers (the
+//    MFMA A fragments) for the whole call, so the rank-r factor is read from
+//    HBM once per call rather than once per step.  Grid barriers separate the
+//    phases; everything that crosses workgroups inside the launch (chunk
+//    partials, z rows read by the draw, x_k) is stored and loaded at device
+//    scope (sc1), so the barriers need no L2 writeback or invalidate.
+//  * per step: 2 gamma launches (stream kernel over all chunks, finalize
+//    kernel over all requests), used when the fused grid cannot be resident
+//    at once (V above 512 tokens per compute unit).
 #include "common.hpp"
 #include "internal.hpp"
 #include "truncate.hpp"
@@ -30,13 +44,39 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;          // requests per workgroup tile (MFMA N side)
-constexpr int kStepThreads = 512;  // 8 waves, 32 tokens each
-constexpr int kStepWaves = kStepThreads / 64;
+constexpr int kTile = 64;           // requests per tile (MFMA N side)
+constexpr int kStepThreads = 512;   // per-step stream kernel: 8 waves x 32 tokens, one chunk
+constexpr int kFusedThreads = 512;  // fused kernel: 8 waves x 64 tokens, two chunks
+constexpr int kStepMS = 2;          // 16-token MFMA row blocks per wave (per-step kernel)
+constexpr int kFusedMS = 4;         // 16-token MFMA row blocks per wave (fused kernel)
+constexpr int kFusedTokens = kFusedThreads / 64 * 16 * kFusedMS;
 constexpr int kMaxR = DSPARK_MAX_RANK;
-constexpr int kPad = 8;            // bf16 padding per staged W1 row (bank spread)
-constexpr int kFinThreads = 256;
-constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kPad = 8;             // bf16 padding per staged W1 row (bank spread)
+constexpr int kFinThreads = 256;    // per-step finalize kernel
+constexpr uint32_t kSpinLimit = 1u << 22;  // grid-barrier polls (~1 us each) before giving up
+
+// Everything one Markov call reads and writes.
+struct MarkovArgs {
+  const void* backbone;
+  const int32_t* anchor;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const uint16_t* hidden;
+  const uint16_t* embed;
+  const float* conf_w;
+  dspark_policy pol;
+  uint64_t seed;
+  int32_t B, gamma, V, r, d, C, cvec;
+  int32_t* draft_tokens;
+  float* q_z;
+  float* q_lse;
+  float* q_thr;
+  float* q_tok;
+  float* confidence;
+  uint8_t* flags;
+  ChunkPart* part;
+  uint32_t* sync;  // fused plan: barrier counters and timeout word (kSyncWords)
+};
 
 // Four consecutive logits starting at a multiple of 4, kept packed (bf16:
 // 8 bytes, fp32: 16 bytes) until the epilogue unpacks them.
@@ -77,31 +117,87 @@ __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
-    const T* __restrict__ backbone, const int32_t* __restrict__ xprev, int32_t xstride,
-    const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
-    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
-    const uint32_t* __restrict__ request_id, const int32_t* __restrict__ position, uint64_t seed,
-    int32_t B, int32_t gamma, int32_t k, int32_t V, int32_t r, int32_t C, float* __restrict__ q_z,
-    ChunkPart* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[kTile * (kMaxR + kPad)];
-  __shared__ float red_m[kStepWaves][kTile], red_s[kStepWaves][kTile];
-  __shared__ int32_t red_i[kStepWaves][kTile];
-  __shared__ uint32_t red_f[kStepWaves][kTile];
+// Device-scope 16-byte store (written through to memory): z values that a
+// workgroup of the same launch reads later.
+__device__ __forceinline__ void store4_coherent(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 
-  const int c = blockIdx.x;
-  const int b0 = blockIdx.y * kTile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kpad = (r + 31) & ~31;
-  const int ld = kpad + kPad;
-  const int ksteps = kpad / 32;
+template <bool COH>
+__device__ __forceinline__ float ld_f(const float* p) {
+  if constexpr (COH) return load_coherent(p);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ int32_t ld_i(const int32_t* p) {
+  if constexpr (COH) return load_coherent(p);
+  else return *p;
+}
 
-  // W2 fragments of this wave's 32 tokens (MFMA A operand: token rows, K slices)
-  const int vb = c * kChunk + wave * 32;
-  bf16x8 af[2][kMaxR / 32];
+// Device-scope 16-byte load (bypassing stale cached copies); the wait for its
+// data is part of the instruction sequence.
+__device__ __forceinline__ f32x4 load4_coherent(const void* p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
+               : "=v"(v)
+               : "v"(p)
+               : "memory");
+  return v;
+}
+
+template <bool COH>
+__device__ __forceinline__ ChunkPart load_part(const ChunkPart* p) {
+  if constexpr (COH) {
+    const f32x4 v = load4_coherent(p);
+    return ChunkPart{v[0], v[1], v[2], __float_as_uint(v[3])};
+  } else {
+    return *p;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ void store_part(ChunkPart* p, ChunkPart v) {
+  if constexpr (COH) {
+    store4_coherent(reinterpret_cast<float*>(p), f32x4{v.m, v.s, v.score, __uint_as_float(v.arg_nf)});
+  } else {
+    *p = v;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ void store_flag(uint8_t* p, uint8_t v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+// The thread index, opaque to the optimiser: the phases of the one-launch plan
+// recompute their lane-derived addresses instead of keeping them live (in
+// registers) across the whole step loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Stream phase.
+
+template <int NT>
+struct StreamLds {
+  static constexpr int NW = NT / 64;
+  __attribute__((aligned(16))) uint16_t a[kTile * (kMaxR + kPad)];  // staged W1 rows
+  float red_m[NW][kTile], red_s[NW][kTile];  // per (wave, request)
+  int32_t red_i[NW][kTile];
+  uint32_t red_f[NW][kTile];
+  int32_t xs[kTile];
+};
+
+// W2 fragments of the 16 MS tokens [vb, vb + 16 MS) (MFMA A operand: token
+// rows, K slices of 32).
+template <int MS>
+__device__ __forceinline__ void load_w2(bf16x8 (&af)[MS][kMaxR / 32], const uint16_t* w2, int vb,
+                                        int V, int r, int lane) {
+  const int ksteps = ((r + 31) & ~31) / 32;
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms) {
+  for (int ms = 0; ms < MS; ++ms) {
     const int v = vb + ms * 16 + (lane & 15);
 #pragma unroll
     for (int ks = 0; ks < kMaxR / 32; ++ks) {
@@ -111,178 +207,234 @@ __global__ __launch_bounds__(kStepThreads) void markov_step_kernel(
       af[ms][ks] = f;
     }
   }
+}
 
-  // prefetch this lane's backbone values (tokens vb + ms*16 + 4*(lane>>4) + i of
-  // request ns*16 + (lane&15)) so their latency overlaps the product
-  QuadRaw<T> bbv[4][2];
+// Backbone values of this lane for the request blocks [ns0, ns0 + NSP) of the
+// tile: tokens vb + ms*16 + 4*(lane>>4) + i of request b0 + ns*16 + (lane&15).
+template <typename T, bool VEC, int MS, int NSP>
+__device__ __forceinline__ void load_backbone(QuadRaw<T> (&bbv)[NSP][MS], const T* backbone,
+                                              int B, int gamma, int V, int k, int b0, int ns0,
+                                              int vb, int lane) {
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int b = b0 + ns * 16 + (lane & 15);
+  for (int j = 0; j < NSP; ++j) {
+    const int b = b0 + (ns0 + j) * 16 + (lane & 15);
     const size_t rowoff = (static_cast<size_t>(b < B ? b : 0) * gamma + (k - 1)) * V;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+    for (int ms = 0; ms < MS; ++ms) {
       const int v0 = vb + ms * 16 + 4 * (lane >> 4);
       const int n = b < B ? (V - v0 < 4 ? (V - v0 > 0 ? V - v0 : 0) : 4) : 0;
-      bbv[ns][ms].load(backbone + rowoff + (n > 0 ? v0 : 0), VEC, n);
+      bbv[j][ms].load(backbone + rowoff + (n > 0 ? v0 : 0), VEC, n);
     }
   }
+}
 
-  // stage the gathered W1 rows of the tile's requests (MFMA B operand): the
-  // 64 tokens first, then every 16-byte piece load issued back to back
-  __shared__ int32_t xs_lds[kTile];
+// Step k for requests [b0, b0 + 64) over the workgroup's tokens [tok0, tok0 +
+// 16 MS NW): wave w takes the 16 MS tokens at vb = tok0 + 16 MS w with its W2
+// fragments af, and the 64 requests in NH passes of 64 / NH.  Writes z of
+// sampled requests and one ChunkPart per (request, chunk of the workgroup).
+// COH: z and the partials are read by other workgroups of the same launch.
+template <typename T, bool VEC, int NT, int MS, int NH, bool COH>
+__device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&af)[MS][kMaxR / 32], int tok0,
+                            int b0, int k, StreamLds<NT>& L) {
+  constexpr int NW = NT / 64;
+  constexpr int NSP = 4 / NH;         // 16-request blocks per pass
+  constexpr int TPW = 16 * MS;        // tokens per wave
+  constexpr int WPC = kChunk / TPW;   // waves per chunk
+  const T* __restrict__ backbone = static_cast<const T*>(a.backbone);
+  const int B = a.B, gamma = a.gamma, V = a.V, r = a.r;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int vb = tok0 + wave * TPW;
+  const int kpad = (r + 31) & ~31;
+  const int ld = kpad + kPad;
+  const int ksteps = kpad / 32;
+
+  // the tile's tokens x_{k-1} are requested first (loads complete in order),
+  // then every pass's backbone values, so that their latency overlaps the W1
+  // staging and the products
+  int32_t xv = -1;
   if (tid < kTile) {
     const int b = b0 + tid;
-    xs_lds[tid] = b < B ? clamp_token(xprev[static_cast<size_t>(b) * xstride], V) : -1;
+    if (b < B)
+      xv = clamp_token(k == 1 ? a.anchor[b] : ld_i<COH>(a.draft_tokens + static_cast<size_t>(b) * gamma + (k - 2)), V);
   }
+  QuadRaw<T> bbv[NH][NSP][MS];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    load_backbone<T, VEC, MS, NSP>(bbv[h], backbone, B, gamma, V, k, b0, h * NSP, vb, lane);
+
+  // stage the gathered W1 rows of the tile's requests (MFMA B operand): every
+  // 16-byte piece load issued back to back
+  if (tid < kTile) L.xs[tid] = xv;
   __syncthreads();
   const int pieces = kpad / 8;
-  constexpr int kMaxPieces = kTile * (kMaxR / 8) / kStepThreads;  // 4
+  constexpr int kMaxPieces = kTile * (kMaxR / 8) / NT;
   uint4 stage[kMaxPieces];
 #pragma unroll
   for (int j = 0; j < kMaxPieces; ++j) {
-    const int idx = tid + j * kStepThreads;
+    const int idx = tid + j * NT;
     const int row = idx / pieces, pc = idx - row * pieces;
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
     if (row < kTile && pc * 8 < r) {
-      const int32_t x = xs_lds[row];
-      if (x >= 0) val = *reinterpret_cast<const uint4*>(w1 + static_cast<size_t>(x) * r + pc * 8);
+      const int32_t x = L.xs[row];
+      if (x >= 0) val = *reinterpret_cast<const uint4*>(a.w1 + static_cast<size_t>(x) * r + pc * 8);
     }
     stage[j] = val;
   }
 #pragma unroll
   for (int j = 0; j < kMaxPieces; ++j) {
-    const int idx = tid + j * kStepThreads;
+    const int idx = tid + j * NT;
     const int row = idx / pieces, pc = idx - row * pieces;
-    if (row < kTile) *reinterpret_cast<uint4*>(a_lds + row * ld + pc * 8) = stage[j];
+    if (row < kTile) *reinterpret_cast<uint4*>(L.a + row * ld + pc * 8) = stage[j];
   }
   __syncthreads();
 
-  f32x4 acc[2][4];
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
+  for (int h = 0; h < NH; ++h) {
+  f32x4 acc[MS][NSP];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int j = 0; j < NSP; ++j) acc[ms][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < kMaxR / 32; ++ks) {
     if (ks < ksteps) {
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
+      for (int j = 0; j < NSP; ++j) {
+        const int ns = h * NSP + j;
         const bf16x8 bfr =
-            load_frag(a_lds + (ns * 16 + (lane & 15)) * ld + ks * 32 + (lane >> 4) * 8);
+            load_frag(L.a + (ns * 16 + (lane & 15)) * ld + ks * 32 + (lane >> 4) * 8);
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-          acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms][ns], 0, 0, 0);
+        for (int ms = 0; ms < MS; ++ms)
+          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms][j], 0, 0, 0);
       }
     }
   }
 
   // epilogue: lane holds tokens vb + ms*16 + 4*(lane>>4) + i of request ns*16 + (lane&15)
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
+  for (int j = 0; j < NSP; ++j) {
+    const int ns = h * NSP + j;
     const int n = ns * 16 + (lane & 15);
     const int b = b0 + n;
     const bool bvalid = b < B;
     float invT = 1.0f;
     bool sampled = false;
     if (bvalid) {
-      const float Tb = temperature[b];
-      sampled = mode[b] != 0 && !bad_temperature(Tb);
+      const float Tb = a.pol.temperature[b];
+      sampled = a.pol.mode[b] != 0 && !bad_temperature(Tb);
       if (sampled) invT = 1.0f / Tb;
     }
     const size_t rowoff = (static_cast<size_t>(bvalid ? b : 0) * gamma + (k - 1)) * V;
-    float z[8];
-    int32_t zi[8];
+    float z[4 * MS];
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+    for (int ms = 0; ms < MS; ++ms) {
       const int v0 = vb + ms * 16 + 4 * (lane >> 4);
-      const QuadRaw<T>& bb = bbv[ns][ms];
+      const QuadRaw<T>& bb = bbv[h][j][ms];
       const bool full = bvalid && v0 + 3 < V;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool in = bvalid && v0 + i < V;
-        z[ms * 4 + i] = in ? (acc[ms][ns][i] + bb.at(i)) * invT : neg_inf();
-        zi[ms * 4 + i] = v0 + i;
+        z[ms * 4 + i] = in ? (acc[ms][j][i] + bb.at(i)) * invT : neg_inf();
       }
       if (sampled) {
-        float* dst = q_z + rowoff + v0;
+        float* dst = a.q_z + rowoff + v0;
         if (VEC && full) {
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]);
+          const f32x4 zv{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+          if constexpr (COH) store4_coherent(dst, zv);
+          else *reinterpret_cast<f32x4*>(dst) = zv;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (v0 + i < V) dst[i] = z[ms * 4 + i];
+            if (v0 + i < V) {
+              if constexpr (COH) store_coherent(dst + i, z[ms * 4 + i]);
+              else dst[i] = z[ms * 4 + i];
+            }
         }
       }
     }
-    // reduce over this lane's 8 tokens, then over the 4 lane groups sharing n
-    float m = neg_inf();
-    int32_t arg = INT32_MAX;
-    uint32_t bad = 0;
+    // reduce over this lane's 4 MS tokens, then over the 4 lane groups
+    // sharing n: max, lowest argmax, and a NaN / +inf detector (the sum of z
+    // is NaN iff some z is NaN or +inf meets -inf; +inf alone shows as max)
+    float m = neg_inf(), zsum = 0.0f;
+    int32_t ej = -1;  // element of the lane's first maximum
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (z[j] > m) {
-        m = z[j];
-        arg = zi[j];
+    for (int e = 0; e < 4 * MS; ++e) {
+      if (z[e] > m) {
+        m = z[e];
+        ej = e;
       }
-      bad |= (z[j] != z[j] || z[j] == pos_inf()) ? 1u : 0u;
+      zsum += z[e];
     }
+    int32_t arg = ej < 0 ? INT32_MAX : vb + (ej >> 2) * 16 + 4 * (lane >> 4) + (ej & 3);
+    uint32_t bad = (zsum != zsum || m == pos_inf()) ? 1u : 0u;
 #pragma unroll
     for (int o = 16; o < 64; o <<= 1) {
       const ArgMax other{__shfl_xor(m, o, 64), __shfl_xor(arg, o, 64)};
-      const ArgMax a = better(ArgMax{m, arg}, other);
-      m = a.v;
-      arg = a.i;
+      const ArgMax am = better(ArgMax{m, arg}, other);
+      m = am.v;
+      arg = am.i;
       bad |= __shfl_xor(bad, o, 64);
     }
+    // sum of 2^(z log2e - m log2e) relative to the 4 lanes' maximum
     float s = 0.0f;
     if (m > neg_inf() && m < pos_inf()) {
+      const float mb = m * kLog2e;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2e);
+      for (int e = 0; e < 4 * MS; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[e], kLog2e, -mb));
     }
 #pragma unroll
     for (int o = 16; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
     if (lane < 16) {
-      red_m[wave][n] = m;
-      red_s[wave][n] = s;
-      red_i[wave][n] = arg;
-      red_f[wave][n] = bad;
+      L.red_m[wave][n] = m;
+      L.red_s[wave][n] = s;
+      L.red_i[wave][n] = arg;
+      L.red_f[wave][n] = bad;
     }
   }
+  }
   __syncthreads();
-  if (tid < kTile && b0 + tid < B) {
-    const int b = b0 + tid;
-    float m = red_m[0][tid], s = red_s[0][tid];
-    ArgMax a{red_m[0][tid], red_i[0][tid]};
-    uint32_t bad = red_f[0][tid];
+  // one ChunkPart per (request, chunk): the chunk's waves combined
+  constexpr int kChunksPerWG = NW / WPC;
+  for (int idx = tid; idx < kChunksPerWG * kTile; idx += NT) {
+    const int h = idx / kTile, n = idx - h * kTile;
+    const int c = tok0 / kChunk + h;
+    const int b = b0 + n;
+    if (c >= a.C || b >= B) continue;
+    const int w0 = h * WPC;
+    float m = L.red_m[w0][n], s = L.red_s[w0][n];
+    ArgMax am{L.red_m[w0][n], L.red_i[w0][n]};
+    uint32_t bad = L.red_f[w0][n];
 #pragma unroll
-    for (int w = 1; w < kStepWaves; ++w) {
-      lse_merge(m, s, red_m[w][tid], red_s[w][tid]);
-      a = better(a, ArgMax{red_m[w][tid], red_i[w][tid]});
-      bad |= red_f[w][tid];
+    for (int w = 1; w < WPC; ++w) {
+      lse_merge(m, s, L.red_m[w0 + w][n], L.red_s[w0 + w][n]);
+      am = better(am, ArgMax{L.red_m[w0 + w][n], L.red_i[w0 + w][n]});
+      bad |= L.red_f[w0 + w][n];
     }
     // chunk level of the two-level Gumbel-max draw: ln(mass) + chunk noise
     float score = neg_inf();
-    const float Tb = temperature[b];
-    if (mode[b] != 0 && !bad_temperature(Tb) && m > neg_inf() && m < pos_inf() && s > 0.0f)
-      score = m + logf(s) + gumbel(seed, static_cast<uint32_t>(c), position[b] + k, request_id[b],
-                                   DSPARK_TAG_DRAFT_CHUNK);
-    part[static_cast<size_t>(b) * C + c] =
-        ChunkPart{m, s, score, (static_cast<uint32_t>(a.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)};
+    const float Tb = a.pol.temperature[b];
+    if (a.pol.mode[b] != 0 && !bad_temperature(Tb) && m > neg_inf() && m < pos_inf() && s > 0.0f)
+      score = m + logf(s) + gumbel(a.seed, static_cast<uint32_t>(c), a.pol.position[b] + k,
+                                   a.pol.request_id[b], DSPARK_TAG_DRAFT_CHUNK);
+    store_part<COH>(a.part + static_cast<size_t>(b) * a.C + c,
+                    ChunkPart{m, s, score,
+                              (static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)});
   }
+  __syncthreads();  // the LDS tile is reused by the next call
 }
 
-// One workgroup per request.  All waves combine the chunk partials; then wave
-// 0 draws the token inside the chosen chunk (lane l scores tokens 4l..4l+3 with
-// one Philox block) while waves 1-3 evaluate the confidence head.
+// ---------------------------------------------------------------------------
+// Finalize phase.
+
 // One proposal row of scaled logits z (fp32), 4 tokens per load.
+template <bool COH>
 struct QzRow {
   const float* p;
   int V;
   bool vec4;
-  __device__ float operator()(int v) const { return p[v]; }
+  __device__ float operator()(int v) const { return ld_f<COH>(p + v); }
   __device__ void load4(int v0, float* o) const {
-    if (vec4 && v0 + 3 < V) {
+    if (!COH && vec4 && v0 + 3 < V) {
       const float4 u = *reinterpret_cast<const float4*>(p + v0);
       o[0] = u.x;
       o[1] = u.y;
@@ -290,7 +442,7 @@ struct QzRow {
       o[3] = u.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? p[v0 + e] : neg_inf();
+      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? ld_f<COH>(p + v0 + e) : neg_inf();
     }
   }
 };
@@ -298,14 +450,16 @@ struct QzRow {
 // Level-1 scores of the two-level draw restricted to the kept set
 // (z >= thr): for each listed chunk (list[j], or j itself without a list)
 // holding kept tokens, log of its kept mass plus the chunk's Gumbel.  Wave w
-// takes entries w, w + 4, ...; four chunks' loads are issued together.
+// takes entries w, w + NW, ...; four chunks' loads are issued together.
 // Returns the wave's best two (score, chunk).
-__device__ Top2 kept_chunk_scores(const QzRow& qr, int n, const int* list, float thr,
+template <int NT, bool COH>
+__device__ __forceinline__ Top2 kept_chunk_scores(const QzRow<COH>& qr, int n, const int* list, float thr,
                                   uint64_t seed, int32_t pos, uint32_t req) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
   constexpr int kU = 4;
-  for (int j0 = wave * kU; j0 < n; j0 += kFinWaves * kU) {
+  for (int j0 = wave * kU; j0 < n; j0 += NW * kU) {
     float z[kU][4];
     int cs[kU];
 #pragma unroll
@@ -341,40 +495,42 @@ __device__ Top2 kept_chunk_scores(const QzRow& qr, int n, const int* list, float
   return best;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
-    const int32_t* __restrict__ xprev, int32_t xstride, const uint16_t* __restrict__ hidden,
-    const uint16_t* __restrict__ embed, const float* __restrict__ conf_w,
-    const uint8_t* __restrict__ mode, const float* __restrict__ temperature,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
-    const uint32_t* __restrict__ request_id, const int32_t* __restrict__ position,
-    uint64_t seed, int32_t gamma, int32_t k, int32_t V, int32_t d, int32_t C, int32_t cvec,
-    const ChunkPart* __restrict__ part, const float* __restrict__ q_z,
-    int32_t* __restrict__ draft_tokens, float* __restrict__ q_lse, float* __restrict__ q_thr,
-    float* __restrict__ q_tok, float* __restrict__ confidence, uint8_t* __restrict__ flags) {
-  __shared__ float sh_m[kFinWaves], sh_s[kFinWaves], sh_am[kFinWaves], sh_v1[kFinWaves],
-      sh_v2[kFinWaves], sh_dot[kFinWaves];
-  __shared__ int32_t sh_ai[kFinWaves], sh_i1[kFinWaves];
-  __shared__ uint32_t sh_bad[kFinWaves];
-  __shared__ float fin_M, fin_S, fin_zx;
-  __shared__ int32_t fin_x;
-  __shared__ uint32_t fin_fl;
-  __shared__ TruncLds U;
+template <int NT>
+struct FinLds {
+  static constexpr int NW = NT / 64;
+  float sh_m[NW], sh_s[NW], sh_am[NW], sh_v1[NW], sh_v2[NW];
+  int32_t sh_ai[NW], sh_i1[NW];
+  uint32_t sh_bad[NW];
+  float fin_M, fin_S, fin_zx;
+  int32_t fin_x;
+  uint32_t fin_fl;
+  TruncLds<NT> U;
+};
 
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Finalize step k of request b with the whole workgroup.  All waves combine
+// the chunk partials (and cut the kept set of a truncating request); then
+// wave 0 draws the token inside the chosen chunk (lane l scores tokens
+// 4l..4l+3 with one Philox block).  COH: the partials and z were written by
+// other workgroups of the same launch, and x_k is read by them.
+template <int NT, bool VEC, bool COH>
+__device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int k, FinLds<NT>& F) {
+  constexpr int NW = NT / 64;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int V = a.V, C = a.C, gamma = a.gamma;
   const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
-  const float Tb = temperature[b];
-  const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
-  const uint32_t req = request_id[b];
-  const int32_t pos = position[b] + k;
+  const float Tb = a.pol.temperature[b];
+  const bool sampled = a.pol.mode[b] != 0 && !bad_temperature(Tb);
+  const uint32_t req = a.pol.request_id[b];
+  const int32_t pos = a.pol.position[b] + k;
+  const ChunkPart* pb = a.part + static_cast<size_t>(b) * C;
 
   // 1. combine the chunk partials
   float m = neg_inf(), s = 0.0f;
   ArgMax am{neg_inf(), INT32_MAX};
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
   uint32_t bad = 0;
-  for (int c = tid; c < C; c += kFinThreads) {
-    const ChunkPart p = part[static_cast<size_t>(b) * C + c];
+  for (int c = tid; c < C; c += NT) {
+    const ChunkPart p = load_part<COH>(pb + c);
     const int32_t arg = static_cast<int32_t>(p.arg_nf & 0x7fffffffu);
     bad |= p.arg_nf >> 31;
     am = better(am, ArgMax{p.m, arg == 0x7fffffff ? INT32_MAX : arg});
@@ -388,76 +544,75 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
     const Top2 wb = wave_top2(best);
     const uint32_t wbad = wave_or(bad);
     if (lane == 0) {
-      sh_m[wave] = wm;
-      sh_s[wave] = ws;
-      sh_am[wave] = wa.v;
-      sh_ai[wave] = wa.i;
-      sh_v1[wave] = wb.v1;
-      sh_i1[wave] = wb.i1;
-      sh_v2[wave] = wb.v2;
-      sh_bad[wave] = wbad;
+      F.sh_m[wave] = wm;
+      F.sh_s[wave] = ws;
+      F.sh_am[wave] = wa.v;
+      F.sh_ai[wave] = wa.i;
+      F.sh_v1[wave] = wb.v1;
+      F.sh_i1[wave] = wb.i1;
+      F.sh_v2[wave] = wb.v2;
+      F.sh_bad[wave] = wbad;
     }
   }
   __syncthreads();
-  float M = sh_m[0], S = sh_s[0];
-  ArgMax A{sh_am[0], sh_ai[0]};
-  Top2 Bst{sh_v1[0], sh_i1[0], sh_v2[0]};
-  uint32_t fl = sh_bad[0] ? DSPARK_FLAG_NONFINITE : 0u;
+  float M = F.sh_m[0], S = F.sh_s[0];
+  ArgMax A{F.sh_am[0], F.sh_ai[0]};
+  Top2 Bst{F.sh_v1[0], F.sh_i1[0], F.sh_v2[0]};
+  uint32_t fl = F.sh_bad[0] ? DSPARK_FLAG_NONFINITE : 0u;
 #pragma unroll
-  for (int w = 1; w < kFinWaves; ++w) {
-    lse_merge(M, S, sh_m[w], sh_s[w]);
-    A = better(A, ArgMax{sh_am[w], sh_ai[w]});
-    Bst = top2_merge(Bst, Top2{sh_v1[w], sh_i1[w], sh_v2[w]});
-    if (sh_bad[w]) fl |= DSPARK_FLAG_NONFINITE;
+  for (int w = 1; w < NW; ++w) {
+    lse_merge(M, S, F.sh_m[w], F.sh_s[w]);
+    A = better(A, ArgMax{F.sh_am[w], F.sh_ai[w]});
+    Bst = top2_merge(Bst, Top2{F.sh_v1[w], F.sh_i1[w], F.sh_v2[w]});
+    if (F.sh_bad[w]) fl |= DSPARK_FLAG_NONFINITE;
   }
 
   // 1b. truncated rows (top-k / top-p on z): the kept set's smallest value
-  // thr and weight, then the level-1 choice over kept chunks only
-  // Kept weights are 2^(z log2e - M2) with the integer shift M2, so that the
-  // drawn token's weight and the kept sum round alike (one kept token: q = 1).
+  // thr and weight, then the level-1 choice over kept chunks only.  Kept
+  // weights are 2^(z log2e - M2) with the integer shift M2, so that the drawn
+  // token's weight and the kept sum round alike (one kept token: q = 1).
   float thr = neg_inf(), s_kept = 0.0f, M2 = 0.0f;
-  const int tk_raw = top_k[b];
-  const float tp = top_p[b];
+  const int tk_raw = a.pol.top_k[b];
+  const float tp = a.pol.top_p[b];
   const bool trunc_row = sampled && truncated(tk_raw, tp, V) && M > neg_inf() && M < pos_inf();
+  const QzRow<COH> qr{a.q_z + row * V, V, VEC};
   if (trunc_row) {
     const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
     M2 = floorf(M * kLog2e);
     const float wa = kLog2e, wb = -M2;
     const float total = S * __builtin_amdgcn_exp2f(fmaf(M, kLog2e, -M2));
-    const QzRow qr{q_z + row * V, V, VEC};
-    const ChunkPart* pb = part + static_cast<size_t>(b) * C;
-    auto chunk_max = [pb](int c) { return pb[c].m; };
+    auto chunk_max = [pb](int c) { return load_part<COH>(pb + c).m; };
     bool cand = false;
-    if (chunk_bound(chunk_max, C, tk, tp, wa, wb, total, U.c)) {
-      gather_candidates(qr, V, U.c);
-      exact_cut(tk, tp, wa, wb, total, U.c);
-      cand = U.c.ok != 0;
+    if (chunk_bound(chunk_max, C, tk, tp, wa, wb, total, F.U.c)) {
+      gather_candidates(qr, V, F.U.c);
+      exact_cut(tk, tp, wa, wb, total, F.U.c);
+      cand = F.U.c.ok != 0;
     }
     int nlist = C;
     const int* list = nullptr;
     if (cand) {
-      thr = U.c.thr;
-      s_kept = U.c.s_kept;
+      thr = F.U.c.thr;
+      s_kept = F.U.c.s_kept;
       // the kept tokens lie in the chunks whose maximum reaches thr: a
       // prefix of the sorted chunk list
-      nlist = count_at_least(U.c.cm, U.c.nchunks, thr, U.c.cnt);
-      list = U.c.ci;
+      nlist = count_at_least<NT>(F.U.c.cm, F.U.c.nchunks, thr, F.U.c.cnt);
+      list = F.U.c.ci;
     } else {
-      const SelResult r = select_threshold(qr, V, 32, tk, tp, wa, wb, U.s);
-      thr = r.thr;
-      s_kept = static_cast<float>(r.s_kept);
+      const SelResult sr = select_threshold(qr, V, 32, tk, tp, wa, wb, F.U.s);
+      thr = sr.thr;
+      s_kept = static_cast<float>(sr.s_kept);
     }
-    const Top2 tb = wave_top2(kept_chunk_scores(qr, nlist, list, thr, seed, pos, req));
+    const Top2 tb = wave_top2(kept_chunk_scores<NT, COH>(qr, nlist, list, thr, a.seed, pos, req));
     __syncthreads();
     if (lane == 0) {
-      sh_v1[wave] = tb.v1;
-      sh_i1[wave] = tb.i1;
-      sh_v2[wave] = tb.v2;
+      F.sh_v1[wave] = tb.v1;
+      F.sh_i1[wave] = tb.i1;
+      F.sh_v2[wave] = tb.v2;
     }
     __syncthreads();
-    Bst = Top2{sh_v1[0], sh_i1[0], sh_v2[0]};
+    Bst = Top2{F.sh_v1[0], F.sh_i1[0], F.sh_v2[0]};
 #pragma unroll
-    for (int w = 1; w < kFinWaves; ++w) Bst = top2_merge(Bst, Top2{sh_v1[w], sh_i1[w], sh_v2[w]});
+    for (int w = 1; w < NW; ++w) Bst = top2_merge(Bst, Top2{F.sh_v1[w], F.sh_i1[w], F.sh_v2[w]});
   }
 
   if (wave == 0) {
@@ -474,20 +629,12 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
       if (Bst.v2 > neg_inf() && near_gap(Bst.v1, Bst.v2)) near = 1;
       const int v0 = Bst.i1 * kChunk + 4 * lane;
       float z[4];
-      if (VEC && v0 + 3 < V) {
-        const float4 u = *reinterpret_cast<const float4*>(q_z + row * V + v0);
-        z[0] = u.x;
-        z[1] = u.y;
-        z[2] = u.z;
-        z[3] = u.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = v0 + e < V ? q_z[row * V + v0 + e] : neg_inf();
-      }
+      qr.load4(v0, z);
       // tokens v0..v0+3 share Philox counter (v0 / 4, pos, req, tag)
       uint32_t c0 = static_cast<uint32_t>(v0) >> 2, c1 = static_cast<uint32_t>(pos), c2 = req,
                c3 = DSPARK_TAG_DRAFT_TOKEN;
-      philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+      philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(a.seed),
+                    static_cast<uint32_t>(a.seed >> 32));
       const uint32_t wv[4] = {c0, c1, c2, c3};
       Top2 t{neg_inf(), INT32_MAX, neg_inf()};
 #pragma unroll
@@ -500,142 +647,272 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(
       } else {
         x = t.i1;
         if (t.v2 > neg_inf() && near_gap(t.v1, t.v2)) near = 1;
-        zx = q_z[row * V + x];
+        // the winner's z, from the lane that loaded it
+        const int owner = (x - Bst.i1 * kChunk) >> 2;
+        const float zo = (x & 3) == 0 ? z[0] : (x & 3) == 1 ? z[1] : (x & 3) == 2 ? z[2] : z[3];
+        zx = __shfl(zo, owner, 64);
       }
     }
     if (near) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
     if (lane == 0) {
-      fin_x = x;
-      fin_zx = zx;
-      fin_M = M;
-      fin_S = S;
-      fin_fl = fl;
+      F.fin_x = x;
+      F.fin_zx = zx;
+      F.fin_M = M;
+      F.fin_S = S;
+      F.fin_fl = fl;
     }
-  } else {
-    // 2b. confidence head on [h_k ; embed(x_{k-1})]: 8 elements per 16-byte
-    // load, every load of a thread issued before the first use
-    const int32_t xp = clamp_token(xprev[static_cast<size_t>(b) * xstride], V);
-    const uint16_t* h = hidden + row * d;
-    const uint16_t* e = embed + static_cast<size_t>(xp) * d;
-    const int t = tid - 64;
-    constexpr int kConfThreads = kFinThreads - 64;
-    float dot = 0.0f;
-    if (cvec) {
-      constexpr int kU = 4;  // vectors per thread per round
-      for (int base = 0; base < d; base += kConfThreads * 8 * kU) {
-        uint4 hv[kU], ev[kU];
-        float4 wh[kU][2], we[kU][2];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int i = base + (t + u * kConfThreads) * 8;
-          if (i < d) {
-            hv[u] = *reinterpret_cast<const uint4*>(h + i);
-            ev[u] = *reinterpret_cast<const uint4*>(e + i);
-            wh[u][0] = *reinterpret_cast<const float4*>(conf_w + i);
-            wh[u][1] = *reinterpret_cast<const float4*>(conf_w + i + 4);
-            we[u][0] = *reinterpret_cast<const float4*>(conf_w + d + i);
-            we[u][1] = *reinterpret_cast<const float4*>(conf_w + d + i + 4);
-          } else {
-            hv[u] = ev[u] = make_uint4(0u, 0u, 0u, 0u);
-            wh[u][0] = wh[u][1] = we[u][0] = we[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const float hx[8] = {bf_lo(hv[u].x), bf_hi(hv[u].x), bf_lo(hv[u].y), bf_hi(hv[u].y),
-                               bf_lo(hv[u].z), bf_hi(hv[u].z), bf_lo(hv[u].w), bf_hi(hv[u].w)};
-          const float ex[8] = {bf_lo(ev[u].x), bf_hi(ev[u].x), bf_lo(ev[u].y), bf_hi(ev[u].y),
-                               bf_lo(ev[u].z), bf_hi(ev[u].z), bf_lo(ev[u].w), bf_hi(ev[u].w)};
-          const float whx[8] = {wh[u][0].x, wh[u][0].y, wh[u][0].z, wh[u][0].w,
-                                wh[u][1].x, wh[u][1].y, wh[u][1].z, wh[u][1].w};
-          const float wex[8] = {we[u][0].x, we[u][0].y, we[u][0].z, we[u][0].w,
-                                we[u][1].x, we[u][1].y, we[u][1].z, we[u][1].w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dot += whx[j] * hx[j] + wex[j] * ex[j];
-        }
-      }
-    } else {
-      for (int i = t; i < d; i += kConfThreads)
-        dot += conf_w[i] * load_logit(h, i) + conf_w[d + i] * load_logit(e, i);
-    }
-    dot = wave_sum(dot);
-    if (lane == 0) sh_dot[wave] = dot;
   }
   __syncthreads();
   if (tid == 0) {
-    float dot = 0.0f;
-#pragma unroll
-    for (int w = 1; w < kFinWaves; ++w) dot += sh_dot[w];
-    const int32_t x = fin_x;
-    draft_tokens[row] = x;
-    if (sampled) {
-      if (trunc_row) {
-        q_lse[row] = M2 * kLn2 + logf(s_kept);
-        q_thr[row] = thr;
-        q_tok[row] = (fin_zx > neg_inf() && fin_zx >= thr && s_kept > 0.0f)
-                         ? __builtin_amdgcn_exp2f(fmaf(fin_zx, kLog2e, -M2)) / s_kept
+    const int32_t x = F.fin_x;
+    if constexpr (COH) store_coherent(a.draft_tokens + row, x);
+    else a.draft_tokens[row] = x;
+    const float zx = F.fin_zx;
+    if (!sampled) {
+      a.q_lse[row] = 0.0f;
+      a.q_thr[row] = 0.0f;
+      a.q_tok[row] = 1.0f;
+    } else if (trunc_row) {
+      a.q_lse[row] = M2 * kLn2 + logf(s_kept);
+      a.q_thr[row] = thr;
+      a.q_tok[row] = (zx > neg_inf() && zx >= thr && s_kept > 0.0f)
+                         ? __builtin_amdgcn_exp2f(fmaf(zx, kLog2e, -M2)) / s_kept
                          : 0.0f;
-      } else {
-        q_lse[row] = fin_M + logf(fin_S);
-        q_thr[row] = neg_inf();
-        q_tok[row] = (fin_zx > neg_inf() && fin_S > 0.0f) ? expf(fin_zx - fin_M) / fin_S : 0.0f;
-      }
     } else {
-      q_lse[row] = 0.0f;
-      q_thr[row] = 0.0f;
-      q_tok[row] = 1.0f;
+      const float fM = F.fin_M, fS = F.fin_S;
+      a.q_lse[row] = fM + logf(fS);
+      a.q_thr[row] = neg_inf();
+      a.q_tok[row] = (zx > neg_inf() && fS > 0.0f) ? expf(zx - fM) / fS : 0.0f;
     }
-    confidence[row] = 1.0f / (1.0f + expf(-dot));
-    uint32_t f = fin_fl;
-    if (mode[b] != 0 && !sampled) f |= DSPARK_FLAG_BAD_POLICY;
-    flags[row] = static_cast<uint8_t>(f);
+    uint32_t f = F.fin_fl;
+    if (a.pol.mode[b] != 0 && !sampled) f |= DSPARK_FLAG_BAD_POLICY;
+    store_flag<COH>(a.flags + row, static_cast<uint8_t>(f));
+  }
+  __syncthreads();  // F is reused by the next request
+}
+
+// Confidence head of every draft row (b, k): c = sigmoid(w . [h_k ;
+// embed(x_{k-1})]), one workgroup per row, run after the last step (x_{k-1}
+// is the anchor for k = 1, else draft token k-1).  8 elements per 16-byte
+// load, every load of a thread issued before the first use.
+constexpr int kConfThreads = 256;
+
+__global__ __launch_bounds__(kConfThreads) void markov_confidence_kernel(MarkovArgs a) {
+  __shared__ float sh[kConfThreads / 64];
+  const int row = blockIdx.x;
+  const int b = row / a.gamma, k = row - b * a.gamma + 1;
+  const int d = a.d, V = a.V, t = threadIdx.x;
+  const int32_t xp =
+      clamp_token(k == 1 ? a.anchor[b] : a.draft_tokens[static_cast<size_t>(b) * a.gamma + (k - 2)], V);
+  const uint16_t* h = a.hidden + static_cast<size_t>(row) * d;
+  const uint16_t* e = a.embed + static_cast<size_t>(xp) * d;
+  const float* cw = a.conf_w;
+  float dot = 0.0f;
+  if (a.cvec) {
+    constexpr int kU = 2;  // vectors per thread per round
+    for (int base = 0; base < d; base += kConfThreads * 8 * kU) {
+      uint4 hv[kU], ev[kU];
+      float4 wh[kU][2], we[kU][2];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + (t + u * kConfThreads) * 8;
+        if (i < d) {
+          hv[u] = *reinterpret_cast<const uint4*>(h + i);
+          ev[u] = *reinterpret_cast<const uint4*>(e + i);
+          wh[u][0] = *reinterpret_cast<const float4*>(cw + i);
+          wh[u][1] = *reinterpret_cast<const float4*>(cw + i + 4);
+          we[u][0] = *reinterpret_cast<const float4*>(cw + d + i);
+          we[u][1] = *reinterpret_cast<const float4*>(cw + d + i + 4);
+        } else {
+          hv[u] = ev[u] = make_uint4(0u, 0u, 0u, 0u);
+          wh[u][0] = wh[u][1] = we[u][0] = we[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float hx[8] = {bf_lo(hv[u].x), bf_hi(hv[u].x), bf_lo(hv[u].y), bf_hi(hv[u].y),
+                             bf_lo(hv[u].z), bf_hi(hv[u].z), bf_lo(hv[u].w), bf_hi(hv[u].w)};
+        const float ex[8] = {bf_lo(ev[u].x), bf_hi(ev[u].x), bf_lo(ev[u].y), bf_hi(ev[u].y),
+                             bf_lo(ev[u].z), bf_hi(ev[u].z), bf_lo(ev[u].w), bf_hi(ev[u].w)};
+        const float whx[8] = {wh[u][0].x, wh[u][0].y, wh[u][0].z, wh[u][0].w,
+                              wh[u][1].x, wh[u][1].y, wh[u][1].z, wh[u][1].w};
+        const float wex[8] = {we[u][0].x, we[u][0].y, we[u][0].z, we[u][0].w,
+                              we[u][1].x, we[u][1].y, we[u][1].z, we[u][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot += whx[j] * hx[j] + wex[j] * ex[j];
+      }
+    }
+  } else {
+    for (int i = t; i < d; i += kConfThreads)
+      dot += cw[i] * load_logit(h, i) + cw[d + i] * load_logit(e, i);
+  }
+  dot = block_sum<kConfThreads / 64>(dot, sh);
+  if (t == 0) a.confidence[row] = 1.0f / (1.0f + expf(-dot));
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kStepThreads) void markov_step_kernel(MarkovArgs a, int32_t k) {
+  __shared__ StreamLds<kStepThreads> L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * kChunk;
+  bf16x8 af[kStepMS][kMaxR / 32];
+  load_w2<kStepMS>(af, a.w2, tok0 + wave * 16 * kStepMS, a.V, a.r, lane);
+  stream_tile<T, VEC, kStepThreads, kStepMS, 1, false>(a, af, tok0, blockIdx.y * kTile, k, L);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(MarkovArgs a, int32_t k) {
+  __shared__ FinLds<kFinThreads> F;
+  finalize_request<kFinThreads, VEC, false>(a, blockIdx.x, k, F);
+}
+
+// Grid-wide barrier of the fused launch (every workgroup resident).  Arrival
+// is two-level, because device-scope atomics on one address serialise (tens
+// of ns each): workgroup g counts on group counter g mod 8 (each on its own
+// 64-byte line), and the last arrival of each group counts on the global
+// counter, which every workgroup polls.  Counters only grow (barrier n ends
+// when the global counter reaches n x groups); the reset kernel clears them
+// before each launch.  Each wave first drains its own memory operations, so
+// everything stored before the barrier (device-scope) is visible after it.
+// A poll limit bounds the wait; on expiry the timeout word is set and the
+// launch runs on to its end (its rows are then flagged).
+constexpr int kSyncGroups = 8;
+constexpr int kSyncStride = 16;                                 // words per group line
+constexpr int kSyncGlobal = kSyncGroups * kSyncStride;          // global counter word
+constexpr int kSyncTimeout = kSyncGlobal + kSyncStride;         // timeout word
+constexpr int kSyncWords = kSyncTimeout + kSyncStride;
+
+__device__ __forceinline__ void grid_sync(uint32_t* sync, uint32_t gen) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x, g = blockIdx.x, j = g % kSyncGroups;
+    const uint32_t size_j = (G - j + kSyncGroups - 1) / kSyncGroups;
+    const uint32_t groups = G < static_cast<uint32_t>(kSyncGroups) ? G : kSyncGroups;
+    const uint32_t old = __hip_atomic_fetch_add(sync + j * kSyncStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gen * size_j - 1u)
+      __hip_atomic_fetch_add(sync + kSyncGlobal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = gen * groups;
+    uint32_t polls = 0;
+    while (__hip_atomic_load(sync + kSyncGlobal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++polls > kSpinLimit) {
+        __hip_atomic_store(sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ void markov_sync_reset_kernel(uint32_t* sync) {
+  for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) sync[i] = 0u;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs a) {
+  __shared__ StreamLds<kFusedThreads> SL;
+  __shared__ FinLds<kFusedThreads> FL;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = g * kFusedTokens;
+  bf16x8 af[kFusedMS][kMaxR / 32];  // resident for the whole call
+  load_w2<kFusedMS>(af, a.w2, tok0 + wave * 16 * kFusedMS, a.V, a.r, lane);
+  uint32_t gen = 0;
+  for (int k = 1; k <= a.gamma; ++k) {
+    for (int b0 = 0; b0 < a.B; b0 += kTile)
+      stream_tile<T, VEC, kFusedThreads, kFusedMS, 4, true>(a, af, tok0, b0, k, SL);
+    grid_sync(a.sync, ++gen);
+    for (int b = g; b < a.B; b += G) finalize_request<kFusedThreads, VEC, true>(a, b, k, FL);
+    if (k < a.gamma) grid_sync(a.sync, ++gen);
+  }
+  // after a barrier timeout, mark the rows this workgroup finalized
+  if (threadIdx.x == 0 &&
+      __hip_atomic_load(a.sync + kSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    for (int b = g; b < a.B; b += G)
+      for (int k = 0; k < a.gamma; ++k) {
+        uint8_t* f = a.flags + static_cast<size_t>(b) * a.gamma + k;
+        *f = static_cast<uint8_t>(*f | DSPARK_FLAG_SYNC_TIMEOUT);
+      }
   }
 }
 
-template <typename T>
-hipError_t launch_typed(const T* backbone, const int32_t* anchor, const uint16_t* w1,
-                        const uint16_t* w2, const uint16_t* hidden, const uint16_t* embed,
-                        const float* conf_w, dspark_policy pol, uint64_t seed, int32_t B,
-                        int32_t gamma, int32_t V, int32_t r, int32_t d, int32_t* draft_tokens,
-                        float* q_z, float* q_lse, float* q_thr, float* q_tok, float* confidence,
-                        uint8_t* flags, void* ws, const MarkovPlan& pl, hipStream_t st) {
-  ChunkPart* part = reinterpret_cast<ChunkPart*>(static_cast<char*>(ws) + pl.off_part);
-  const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(backbone) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(q_z) % 16 == 0);
-  const dim3 g_step(pl.C, (B + kTile - 1) / kTile);
-  // 16-byte loads of the confidence head's rows and weights
-  const int32_t cvec = (d % 8 == 0) && reinterpret_cast<uintptr_t>(hidden) % 16 == 0 &&
-                       reinterpret_cast<uintptr_t>(embed) % 16 == 0 &&
-                       reinterpret_cast<uintptr_t>(conf_w) % 16 == 0;
-  for (int k = 1; k <= gamma; ++k) {
-    const int32_t* xp = k == 1 ? anchor : draft_tokens + (k - 2);
-    const int32_t xs = k == 1 ? 1 : gamma;
-    if (vec)
-      DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, true>), g_step, dim3(kStepThreads), 0,
-                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, pol.request_id,
-                    pol.position, seed, B, gamma, k, V, r, pl.C, q_z, part);
-    else
-      DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, false>), g_step, dim3(kStepThreads), 0,
-                    st, backbone, xp, xs, w1, w2, pol.mode, pol.temperature, pol.request_id,
-                    pol.position, seed, B, gamma, k, V, r, pl.C, q_z, part);
+// Resident workgroups per compute unit of a fused instantiation and the
+// device's compute units (0 if cooperative launch is unavailable), cached per
+// device: a property of the device and the code object only.
+struct FusedFit {
+  int blocks_per_cu;
+  int cus;
+};
+
+template <typename T, bool VEC>
+FusedFit fused_fit() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];  // (blocks << 16 | cus) + 1; 0 = unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FusedFit{0, 0};
+  if (dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return FusedFit{(c - 1) >> 16, (c - 1) & 0xffff};
+  }
+  int coop = 0, cus = 0, nb = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, markov_fused_kernel<T, VEC>, kFusedThreads,
+                                                   0) != hipSuccess)
+    nb = 0;
+  FusedFit f{coop ? nb : 0, cus};
+  if (f.blocks_per_cu < 0 || f.blocks_per_cu > 0x7fff || cus < 0 || cus > 0xffff) f = FusedFit{0, 0};
+  if (dev < kMaxDev) cache[dev].store(((f.blocks_per_cu << 16) | f.cus) + 1, std::memory_order_relaxed);
+  return f;
+}
+
+template <typename T, bool VEC>
+hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
+  if (fused) {
+    DSPARK_LAUNCH("markov_sync_reset", markov_sync_reset_kernel, dim3(1), dim3(256), 0, st, a.sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (vec)
-      DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<true>, dim3(B), dim3(kFinThreads), 0,
-                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.top_k,
-                    pol.top_p, pol.request_id,
-                    pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
-                    q_lse, q_thr, q_tok, confidence, flags);
-    else
-      DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<false>, dim3(B), dim3(kFinThreads), 0,
-                    st, xp, xs, hidden, embed, conf_w, pol.mode, pol.temperature, pol.top_k,
-                    pol.top_p, pol.request_id,
-                    pol.position, seed, gamma, k, V, d, pl.C, cvec, part, q_z, draft_tokens,
-                    q_lse, q_thr, q_tok, confidence, flags);
-    e = hipGetLastError();
+    const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
+    MarkovArgs arg = a;
+    void* params[] = {&arg};
+    ProfScope ps("markov_fused");
+    if (ps.active()) (void)hipEventRecord(ps.start(), st);
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>),
+                                   dim3(G), dim3(kFusedThreads), params, 0, st);
+    if (ps.active()) (void)hipEventRecord(ps.stop(), st);
     if (e != hipSuccess) return e;
+  } else {
+    const dim3 g_step(a.C, (a.B + kTile - 1) / kTile);
+    for (int k = 1; k <= a.gamma; ++k) {
+      DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, VEC>), g_step, dim3(kStepThreads), 0, st,
+                    a, k);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      DSPARK_LAUNCH("markov_finalize", markov_finalize_kernel<VEC>, dim3(a.B), dim3(kFinThreads),
+                    0, st, a, k);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
-  return hipSuccess;
+  DSPARK_LAUNCH("markov_confidence", markov_confidence_kernel, dim3(a.B * a.gamma),
+                dim3(kConfThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, bool VEC>
+hipError_t launch_typed(const MarkovArgs& a, int plan_mode, hipStream_t st) {
+  // fused when its grid (one workgroup per 512 tokens) is resident at once
+  const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
+  bool fused = false;
+  if (plan_mode != DSPARK_MARKOV_PER_STEP) {
+    const FusedFit f = fused_fit<T, VEC>();
+    fused = f.blocks_per_cu > 0 && G <= f.blocks_per_cu * f.cus;
+  }
+  return launch_plan<T, VEC>(a, fused ? 1 : 0, st);
 }
 
 }  // namespace
@@ -647,7 +924,10 @@ MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d
   MarkovPlan p{};
   p.C = (V + kChunk - 1) / kChunk;
   p.off_part = 0;
-  p.bytes = align_up(static_cast<size_t>(B) * p.C * sizeof(ChunkPart), 256);
+  size_t off = align_up(static_cast<size_t>(B) * p.C * sizeof(ChunkPart), 256);
+  p.off_sync = off;
+  off += align_up(kSyncWords * sizeof(uint32_t), 256);
+  p.bytes = off;
   return p;
 }
 
@@ -657,14 +937,43 @@ hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
                          uint64_t seed, int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d,
                          int32_t* draft_tokens, float* q_z, float* q_lse, float* q_thr,
                          float* q_tok, float* confidence, uint8_t* flags, void* ws,
-                         const MarkovPlan& plan, hipStream_t st) {
+                         const MarkovPlan& plan, int plan_mode, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  MarkovArgs a{};
+  a.backbone = backbone;
+  a.anchor = anchor;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.hidden = hidden;
+  a.embed = embed;
+  a.conf_w = conf_w;
+  a.pol = pol;
+  a.seed = seed;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.d = d;
+  a.C = plan.C;
+  // 16-byte loads of the confidence head's rows and weights
+  a.cvec = (d % 8 == 0) && reinterpret_cast<uintptr_t>(hidden) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(embed) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(conf_w) % 16 == 0;
+  a.draft_tokens = draft_tokens;
+  a.q_z = q_z;
+  a.q_lse = q_lse;
+  a.q_thr = q_thr;
+  a.q_tok = q_tok;
+  a.confidence = confidence;
+  a.flags = flags;
+  a.part = reinterpret_cast<ChunkPart*>(w + plan.off_part);
+  a.sync = reinterpret_cast<uint32_t*>(w + plan.off_sync);
+  const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(backbone) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(q_z) % 16 == 0);
   if (dtype == DSPARK_BF16)
-    return launch_typed(static_cast<const uint16_t*>(backbone), anchor, w1, w2, hidden, embed,
-                        conf_w, pol, seed, B, gamma, V, r, d, draft_tokens, q_z, q_lse, q_thr,
-                        q_tok, confidence, flags, ws, plan, st);
-  return launch_typed(static_cast<const float*>(backbone), anchor, w1, w2, hidden, embed, conf_w,
-                      pol, seed, B, gamma, V, r, d, draft_tokens, q_z, q_lse, q_thr, q_tok,
-                      confidence, flags, ws, plan, st);
+    return vec ? launch_typed<uint16_t, true>(a, plan_mode, st)
+               : launch_typed<uint16_t, false>(a, plan_mode, st);
+  return vec ? launch_typed<float, true>(a, plan_mode, st) : launch_typed<float, false>(a, plan_mode, st);
 }
 
 }  // namespace dspark

@@ -1,4 +1,5 @@
-// profile.hip — opt-in per-kernel timing with HIP events.
+// profile.hip — opt-in per-kernel timing with HIP events, and the Markov
+// launch-plan switch (the library's only process-wide settings).
 //
 // When enabled, every kernel launch of the library records two events at the
 // kernel's own start and end (hipExtLaunchKernelGGL); dspark_profile_summary
@@ -27,10 +28,13 @@ struct Rec {
 };
 
 std::atomic<int> g_on{0};
+std::atomic<int> g_markov_plan{DSPARK_MARKOV_AUTO};
 std::mutex g_mu;
 std::vector<Rec> g_recs;
 
 }  // namespace
+
+int markov_plan_mode() { return g_markov_plan.load(std::memory_order_relaxed); }
 
 ProfScope::ProfScope(const char* name) : name_(name), a_(nullptr), b_(nullptr) {
   if (!g_on.load(std::memory_order_relaxed)) return;
@@ -54,6 +58,11 @@ ProfScope::~ProfScope() {
 }  // namespace dspark
 
 extern "C" {
+
+int dspark_markov_plan(int plan) {
+  if (plan != DSPARK_MARKOV_AUTO && plan != DSPARK_MARKOV_PER_STEP) return -1;
+  return dspark::g_markov_plan.exchange(plan);
+}
 
 int dspark_profile_enable(int on) {
   dspark::g_on.store(on ? 1 : 0);

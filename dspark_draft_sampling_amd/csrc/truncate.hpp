@@ -1,5 +1,7 @@
 // truncate.hpp — top-k / top-p thresholds of one logits row, computed by one
-// 256-thread workgroup with a radix select over order-preserving float keys.
+// workgroup of NT threads (a multiple of 64 dividing 2048): an exact cut on
+// candidates bounded by chunk maxima, and a radix select over order-preserving
+// float keys as the fallback.
 //
 // Policy ("[2/3] feat(dsv4): implement exact DSpark speculative decoding",
 // "Exact decoding semantics", "Probabilistic": temperature, top-k and top-p
@@ -20,7 +22,7 @@
 
 namespace dspark {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;  // workgroup size of the verify select
 constexpr int kSelBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -31,11 +33,12 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+template <int NT>
 struct SelLds {
   uint32_t cnt[kSelBins];
   double mass[kSelBins];
-  uint32_t tc[kSelThreads];
-  double tm[kSelThreads];
+  uint32_t tc[NT];
+  double tm[NT];
   int bin;
   uint32_t above_c;
   double above_m;
@@ -50,11 +53,11 @@ struct SelResult {
 
 // One histogram level over the row: tokens with key >= kmin whose key bits at
 // and above `top` equal `prefix` are binned by key bits [shift, top).
-template <class Row>
+template <int NT, class Row>
 __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int shift, uint32_t kmin,
-                          float wa, float wb, SelLds& S) {
+                          float wa, float wb, SelLds<NT>& S) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kSelBins; i += kSelThreads) {
+  for (int i = tid; i < kSelBins; i += NT) {
     S.cnt[i] = 0u;
     S.mass[i] = 0.0;
   }
@@ -62,7 +65,7 @@ __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int s
   __syncthreads();
   const uint32_t mask = (1u << (top - shift)) - 1u;
   double local = 0.0;
-  for (int v = tid; v < V; v += kSelThreads) {
+  for (int v = tid; v < V; v += NT) {
     const float x = row(v);
     if (!(x > neg_inf()) || x != x) continue;
     const uint32_t k = order_key(x);
@@ -82,9 +85,10 @@ __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int s
 // (by_mass = false) or weight (true) including the bin reaches `target`; if
 // the whole level holds less, the smallest non-empty bin.  Leaves the bin and
 // the count / weight strictly above it in S.
-__device__ void sel_find(SelLds& S, int nbins, bool by_mass, double target) {
+template <int NT>
+__device__ void sel_find(SelLds<NT>& S, int nbins, bool by_mass, double target) {
   const int tid = threadIdx.x;
-  constexpr int per = kSelBins / kSelThreads;  // 8 bins per thread, descending
+  constexpr int per = kSelBins / NT;  // bins per thread, descending
   uint32_t c = 0;
   double m = 0.0;
   for (int j = 0; j < per; ++j) {
@@ -101,7 +105,7 @@ __device__ void sel_find(SelLds& S, int nbins, bool by_mass, double target) {
     // exclusive scan in descending-key order
     uint32_t ac = 0;
     double am = 0.0;
-    for (int t = 0; t < kSelThreads; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const uint32_t xc = S.tc[t];
       const double xm = S.tm[t];
       S.tc[t] = ac;
@@ -140,9 +144,9 @@ __device__ void sel_find(SelLds& S, int nbins, bool by_mass, double target) {
 // (logit or scaled logit); the weight of a token is exp2(value * wa + wb).
 // keybits = 16 for bf16 rows (their key's low 16 bits are determined by the
 // sign), 32 otherwise.
-template <class Row>
+template <int NT, class Row>
 __device__ SelResult select_threshold(const Row& row, int V, int keybits, int top_k, float top_p,
-                                      float wa, float wb, SelLds& S) {
+                                      float wa, float wb, SelLds<NT>& S) {
   const int nlev = keybits == 16 ? 2 : 3;
   const int tops[3] = {32, 21, 10};
   const int shifts16[2] = {21, 16};
@@ -212,12 +216,13 @@ __device__ __forceinline__ bool truncated(int top_k, float top_p, int V) {
 constexpr int kMaxChunksSorted = 1024;  // chunk maxima sorted in LDS
 constexpr int kCandCap = 4096;          // candidate tokens held in LDS
 
+template <int NT>
 struct CandLds {
   float cm[kMaxChunksSorted];  // chunk maxima, sorted descending
   int ci[kMaxChunksSorted];    // their chunk indices
   float cv[kCandCap];          // candidate values, sorted descending
   float pw[kCandCap];          // running weight sums (inclusive)
-  float wtot[kSelThreads / 64];
+  float wtot[NT / 64];
   int n;        // candidates gathered (> kCandCap: overflow)
   int nchunks;  // chunks whose maximum reaches tau
   int idx;      // scratch index (block maximum)
@@ -231,19 +236,20 @@ struct CandLds {
 
 // Either the candidate state or the radix-select state: they are never live
 // at the same time.
+template <int NT>
 union TruncLds {
-  CandLds c;
-  SelLds s;
+  CandLds<NT> c;
+  SelLds<NT> s;
 };
 
 // Bitonic sort of n2 (a power of two) values, descending; with IX the
 // indices travel along (ascending index among equal values).  All threads of
 // the workgroup take part.
-template <bool IX>
+template <int NT, bool IX>
 __device__ void sort_desc(float* v, int* ix, int n2) {
   for (int k = 2; k <= n2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += kSelThreads) {
+      for (int i = threadIdx.x; i < n2; i += NT) {
         const int l = i ^ j;
         if (l > i) {
           const bool desc = (i & k) == 0;
@@ -274,9 +280,10 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 }
 
 // In-place inclusive prefix sum of a[0 .. n) (LDS), all threads.
+template <int NT>
 __device__ void block_scan_incl(float* a, int n, float* wtot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
   float s = 0.0f;
   for (int i = lo; i < hi; ++i) s += a[i];
@@ -298,11 +305,12 @@ __device__ void block_scan_incl(float* a, int n, float* wtot) {
 }
 
 // Number of v[0 .. n) that are >= t (v sorted descending), all threads.
+template <int NT>
 __device__ int count_at_least(const float* v, int n, float t, int& slot) {
   if (threadIdx.x == 0) slot = 0;
   __syncthreads();
   int c = 0;
-  for (int i = threadIdx.x; i < n; i += kSelThreads) c += v[i] >= t ? 1 : 0;
+  for (int i = threadIdx.x; i < n; i += NT) c += v[i] >= t ? 1 : 0;
   c = static_cast<int>(wave_sum(static_cast<float>(c)));
   if ((threadIdx.x & 63) == 0 && c) atomicAdd(&slot, c);
   __syncthreads();
@@ -314,31 +322,31 @@ __device__ int count_at_least(const float* v, int n, float t, int& slot) {
 // Sort the C chunk maxima (cmax(c)) and set L.tau and L.nchunks; returns
 // false when the bound cannot be formed.  wa, wb: the weight of a value x is
 // exp2(x wa + wb); total: the row's total weight.
-template <class ChunkMax>
+template <int NT, class ChunkMax>
 __device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p, float wa,
-                            float wb, float total, CandLds& L) {
+                            float wb, float total, CandLds<NT>& L) {
   if (C > kMaxChunksSorted) return false;
   const int n2 = pow2_at_least(C);
-  for (int i = threadIdx.x; i < n2; i += kSelThreads) {
+  for (int i = threadIdx.x; i < n2; i += NT) {
     L.cm[i] = i < C ? cmax(i) : neg_inf();
     L.ci[i] = i;
   }
   __syncthreads();
-  sort_desc<true>(L.cm, L.ci, n2);
+  sort_desc<NT, true>(L.cm, L.ci, n2);
   float tau = neg_inf();
   if (top_k > 0) {
     if (top_k <= C && top_k <= kCandCap) tau = L.cm[top_k - 1];
   } else if (top_p < 1.0f) {
     // running weight of the sorted maxima; tau = the first maximum at which
     // it reaches top_p * total (with a margin against rounding)
-    for (int i = threadIdx.x; i < C; i += kSelThreads)
+    for (int i = threadIdx.x; i < C; i += NT)
       L.cv[i] = L.cm[i] > neg_inf() ? __builtin_amdgcn_exp2f(fmaf(L.cm[i], wa, wb)) : 0.0f;
     __syncthreads();
-    block_scan_incl(L.cv, C, L.wtot);
+    block_scan_incl<NT>(L.cv, C, L.wtot);
     const float target = (top_p > 0.0f ? top_p : 0.0f) * total * 1.0009765625f;
     if (threadIdx.x == 0) L.idx = -1;
     __syncthreads();
-    for (int i = threadIdx.x; i < C; i += kSelThreads)
+    for (int i = threadIdx.x; i < C; i += NT)
       if (L.cm[i] > neg_inf() && L.cv[i] >= target && (i == 0 || L.cv[i - 1] < target))
         L.idx = i;  // unique: the running sum is monotone
     __syncthreads();
@@ -348,7 +356,7 @@ __device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p,
     __syncthreads();
     return false;
   }
-  const int nc = count_at_least(L.cm, C, tau, L.cnt);
+  const int nc = count_at_least<NT>(L.cm, C, tau, L.cnt);
   if (threadIdx.x == 0) {
     L.tau = tau;
     L.nchunks = nc;
@@ -361,11 +369,11 @@ __device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p,
 // Gather every token >= tau of the chunks L.ci[0 .. L.nchunks) (wave w takes
 // chunks w, w+4, ...; lane l the 4 tokens 4l..4l+3).  Sets L.n (possibly
 // above kCandCap: overflow, nothing beyond the cap is stored).
-template <class Row>
-__device__ void gather_candidates(const Row& row, int V, CandLds& L) {
+template <int NT, class Row>
+__device__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float tau = L.tau;
-  for (int j = wave; j < L.nchunks; j += kSelThreads / 64) {
+  for (int j = wave; j < L.nchunks; j += NT / 64) {
     const int c = L.ci[j];
     const int v0 = c * kChunk + lane * 4;
     float x[4];
@@ -392,7 +400,8 @@ __device__ void gather_candidates(const Row& row, int V, CandLds& L) {
 // the set's weight).  total: the row's total weight (the set's weight when
 // top-k is off).  Sets L.thr (smallest kept value), L.s_kept (kept weight),
 // L.nkept and L.ok (0: the cut is not decided by the candidates).
-__device__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds& L) {
+template <int NT>
+__device__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds<NT>& L) {
   const int n = L.n;
   if (n > kCandCap || n < 1 || (top_k > 0 && top_k > n)) {
     __syncthreads();
@@ -401,17 +410,17 @@ __device__ void exact_cut(int top_k, float top_p, float wa, float wb, float tota
     return;
   }
   const int n2 = pow2_at_least(n);
-  for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += kSelThreads) L.cv[i] = neg_inf();
+  for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += NT) L.cv[i] = neg_inf();
   __syncthreads();
-  sort_desc<false>(L.cv, nullptr, n2);
-  for (int i = threadIdx.x; i < n; i += kSelThreads)
+  sort_desc<NT, false>(L.cv, nullptr, n2);
+  for (int i = threadIdx.x; i < n; i += NT)
     L.pw[i] = __builtin_amdgcn_exp2f(fmaf(L.cv[i], wa, wb));
   __syncthreads();
-  block_scan_incl(L.pw, n, L.wtot);
+  block_scan_incl<NT>(L.pw, n, L.wtot);
   int nk = n;
   float set_total = total;
   if (top_k > 0) {
-    nk = count_at_least(L.cv, n, L.cv[top_k - 1], L.cnt);
+    nk = count_at_least<NT>(L.cv, n, L.cv[top_k - 1], L.cnt);
     set_total = L.pw[nk - 1];
   }
   int cut = nk;
@@ -421,11 +430,11 @@ __device__ void exact_cut(int top_k, float top_p, float wa, float wb, float tota
     __syncthreads();
     // the last group start whose strictly-larger weight is below target
     int best = 0;
-    for (int i = threadIdx.x; i < nk; i += kSelThreads)
+    for (int i = threadIdx.x; i < nk; i += NT)
       if (i > 0 && L.cv[i] != L.cv[i - 1] && L.pw[i - 1] < target) best = i;
     if (best > 0) atomicMax(&L.idx, best);
     __syncthreads();
-    cut = count_at_least(L.cv, nk, L.cv[L.idx], L.cnt);
+    cut = count_at_least<NT>(L.cv, nk, L.cv[L.idx], L.cnt);
   }
   if (threadIdx.x == 0) {
     L.nkept = cut;

@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
     const int32_t* __restrict__ n_draft, const RowPart* __restrict__ part,
     const float* __restrict__ cmax, RowTrunc* __restrict__ trunc) {
-  __shared__ TruncLds U;
+  __shared__ TruncLds<kSelThreads> U;
   __shared__ float sh_m[kSelThreads / 64], sh_s[kSelThreads / 64];
   const int G1 = gamma + 1;
   const int row = blockIdx.x, b = row / G1, k = row - b * G1;

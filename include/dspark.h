@@ -128,8 +128,13 @@ enum {
   DSPARK_FLAG_RESIDUAL_ZERO = 1u << 2,  /* max(p-q,0) had zero mass: sampled
                                            from p instead                     */
   DSPARK_FLAG_EMPTY_ROW = 1u << 3,      /* no logit above -inf in the row    */
-  DSPARK_FLAG_BAD_POLICY = 1u << 4      /* sampled row with temperature <= 0
+  DSPARK_FLAG_BAD_POLICY = 1u << 4,     /* sampled row with temperature <= 0
                                            or non-finite: treated as greedy  */
+  DSPARK_FLAG_SYNC_TIMEOUT = 1u << 5    /* dspark_markov_sample only: a
+                                           device-wide barrier of the one-launch
+                                           plan gave up waiting (other work held
+                                           the device's compute units); every
+                                           output of the call is unspecified  */
 };
 
 /* ---- Philox stream tags --------------------------------------------------- */
@@ -183,6 +188,20 @@ int dspark_version(void);
  * truncated to n bytes), forgets the records, and returns 0 or DSPARK_EDEVICE. */
 int dspark_profile_enable(int on);
 int dspark_profile_summary(char* buf, size_t n);
+
+/* Launch plan of dspark_markov_sample (process-wide, like the profiler
+ * switch; read when a call is enqueued).
+ *   DSPARK_MARKOV_AUTO (default): one cooperative launch for all gamma steps
+ *     whenever its grid (one workgroup per 512 tokens of the vocabulary) can
+ *     be resident at once; each workgroup then keeps its slice of markov_w2
+ *     in registers for the whole call.  Otherwise, or if cooperative launch
+ *     is unavailable, 2 gamma launches as below.
+ *   DSPARK_MARKOV_PER_STEP: 2 gamma launches (one stream kernel over all
+ *     chunks and one finalize kernel over all requests per step).
+ * Both plans compute identical results.  Returns the previous plan, or -1
+ * (leaving it unchanged) for an unknown value. */
+enum { DSPARK_MARKOV_AUTO = 0, DSPARK_MARKOV_PER_STEP = 1 };
+int dspark_markov_plan(int plan);
 
 /* ---------------------------------------------------------------------------
  * dspark_markov_sample

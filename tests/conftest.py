@@ -18,3 +18,18 @@ def oracle():
 
     O.lib()
     return O
+
+
+# Full-size decode inputs (seeded; generated once per session, on first use).
+@pytest.fixture(scope="session")
+def decode_full():
+    from workloads import decode_inputs
+
+    return decode_inputs("decode")
+
+
+@pytest.fixture(scope="session")
+def truncated_full():
+    from workloads import decode_inputs
+
+    return decode_inputs("truncated")

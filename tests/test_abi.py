@@ -115,3 +115,14 @@ def test_binding_refuses_cpu_tensors(L):
     with pytest.raises(ds.DSparkError):
         ds.dspark_accept_stats(torch.zeros(1, 1, 4), torch.zeros(1, 1, 4),
                                torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, 1))
+
+
+def test_markov_plan_switch(L):
+    prev = L.dspark_markov_plan(1)
+    try:
+        assert prev in (0, 1)
+        assert L.dspark_markov_plan(0) == 1
+        assert L.dspark_markov_plan(7) == -1      # unknown: refused, unchanged
+        assert L.dspark_markov_plan(0) == 0
+    finally:
+        L.dspark_markov_plan(prev)

@@ -104,12 +104,6 @@ def test_stats_tiny_f32_and_bf16_masked():
 
 
 # --------------------------------------------------------- decode, full V ----
-@pytest.fixture(scope="module")
-def decode_full():
-    inp = decode_inputs("decode")
-    return inp
-
-
 def test_markov_decode_full_size(decode_full):
     inp = decode_full
     got = G.markov(inp)
@@ -247,3 +241,28 @@ def test_stats_paths(N, gamma, V, dtype):
     for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
         assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
     assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
+
+
+@pytest.mark.parametrize("config", ["decode", "truncated"])
+def test_markov_plans_agree(config, decode_full, truncated_full):
+    """The one-launch plan (W2 resident, grid barriers) and the per-step plan
+    agree at full size: tokens, flags, z and thresholds bit for bit; the
+    log-normalisers up to the order of their fp32 partial sums (the plans
+    combine chunk partials over different workgroup shapes)."""
+    import dspark_draft_sampling_amd as ds
+
+    inp = decode_full if config == "decode" else truncated_full
+    prev = ds.markov_plan(ds.MARKOV_AUTO)
+    try:
+        fused = G.markov(inp)
+        ds.markov_plan(ds.MARKOV_PER_STEP)
+        step = G.markov(inp)
+    finally:
+        ds.markov_plan(prev)
+    samp = inp["mode"] != 0
+    for k in ("draft_tokens", "q_thr", "confidence", "flags"):
+        assert np.array_equal(fused[k], step[k]), k
+    for k in ("q_lse", "q_tok"):
+        assert np.allclose(fused[k], step[k], rtol=1e-6, atol=0), k
+    assert np.array_equal(fused["q_logits"][samp], step["q_logits"][samp])
+    assert not np.any(fused["flags"] & (1 << 5))  # no barrier gave up

@@ -85,11 +85,6 @@ def _pol(inp):
     return [(0 < k < V) or p < 1.0 for k, p in zip(inp["top_k"], inp["top_p"])]
 
 
-@pytest.fixture(scope="module")
-def truncated_full():
-    return decode_inputs("truncated")
-
-
 def _coverage_requests(inp):
     """Requests covering each sampled policy kind (top-k only, top-p only,
     both, neither) plus two greedy ones."""
