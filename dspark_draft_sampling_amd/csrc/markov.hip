@@ -27,13 +27,17 @@
 //  * fused: one cooperative launch for all gamma steps.  Workgroup g owns the
 //    512 tokens [512 g, 512 g + 512) and keeps their W2 rows in registers (the
 //    MFMA A fragments) for the whole call, so the rank-r factor is read from
-//    HBM once per call rather than once per step.  Grid barriers separate the
-//    phases; everything that crosses workgroups inside the launch (chunk
-//    partials, z rows read by the draw, x_k) is stored and loaded at device
-//    scope (sc1), so the barriers need no L2 writeback or invalidate.
+//    HBM once per call rather than once per step.  A grid barrier separates
+//    each stream phase from its finalize; the finalize hands x_k to the next
+//    stream phase through draft_tokens (cleared to -1 before the launch).
+//    Everything that crosses workgroups inside the launch (chunk partials, z
+//    rows read by the draw, x_k) is stored and loaded at device scope (sc1),
+//    so no L2 writeback or invalidate is needed.
 //  * per step: 2 gamma launches (stream kernel over all chunks, finalize
 //    kernel over all requests), used when the fused grid cannot be resident
 //    at once (V above 512 tokens per compute unit).
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "truncate.hpp"
@@ -54,6 +58,16 @@ constexpr int kMaxR = DSPARK_MAX_RANK;
 constexpr int kPad = 8;             // bf16 padding per staged W1 row (bank spread)
 constexpr int kFinThreads = 256;    // per-step finalize kernel
 constexpr uint32_t kSpinLimit = 1u << 22;  // grid-barrier polls (~1 us each) before giving up
+
+// Words of the one-launch plan's synchronisation area (each group's counter
+// and release word on its own 256-byte line, then the global counter and the
+// timeout word).
+constexpr int kSyncGroups = 8;
+constexpr int kSyncStride = 64;                                 // words per group line
+constexpr int kSyncRelease = kSyncStride / 2;                   // release word within a line
+constexpr int kSyncGlobal = kSyncGroups * kSyncStride;          // global counter word
+constexpr int kSyncTimeout = kSyncGlobal + kSyncStride;         // timeout word
+constexpr int kSyncWords = kSyncTimeout + kSyncStride;
 
 // Everything one Markov call reads and writes.
 struct MarkovArgs {
@@ -254,8 +268,25 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
   int32_t xv = -1;
   if (tid < kTile) {
     const int b = b0 + tid;
-    if (b < B)
-      xv = clamp_token(k == 1 ? a.anchor[b] : ld_i<COH>(a.draft_tokens + static_cast<size_t>(b) * gamma + (k - 2)), V);
+    if (b < B) {
+      if (k == 1) {
+        xv = a.anchor[b];
+      } else if constexpr (COH) {
+        // one-launch plan: x_{k-1} is -1 until its finalize stores it
+        const int32_t* xp = a.draft_tokens + static_cast<size_t>(b) * gamma + (k - 2);
+        uint32_t polls = 0;
+        while ((xv = load_coherent(xp)) < 0) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++polls > kSpinLimit) {
+            __hip_atomic_store(a.sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      } else {
+        xv = a.draft_tokens[static_cast<size_t>(b) * gamma + (k - 2)];
+      }
+      xv = clamp_token(xv, V);
+    }
   }
   QuadRaw<T> bbv[NH][NSP][MS];
 #pragma unroll
@@ -771,19 +802,29 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(MarkovArgs
 
 // Grid-wide barrier of the fused launch (every workgroup resident).  Arrival
 // is two-level, because device-scope atomics on one address serialise (tens
-// of ns each): workgroup g counts on group counter g mod 8 (each on its own
-// 64-byte line), and the last arrival of each group counts on the global
-// counter, which every workgroup polls.  Counters only grow (barrier n ends
-// when the global counter reaches n x groups); the reset kernel clears them
-// before each launch.  Each wave first drains its own memory operations, so
-// everything stored before the barrier (device-scope) is visible after it.
-// A poll limit bounds the wait; on expiry the timeout word is set and the
-// launch runs on to its end (its rows are then flagged).
-constexpr int kSyncGroups = 8;
-constexpr int kSyncStride = 16;                                 // words per group line
-constexpr int kSyncGlobal = kSyncGroups * kSyncStride;          // global counter word
-constexpr int kSyncTimeout = kSyncGlobal + kSyncStride;         // timeout word
-constexpr int kSyncWords = kSyncTimeout + kSyncStride;
+// of ns each): workgroup g counts on group counter g mod 8 (each group on its
+// own 256-byte line), and the last arrival of each group counts on the global
+// counter.  Only those group leaders poll the global counter; each then
+// releases its group by storing the barrier number on the group's line, which
+// the other members poll (polling spread over the groups' lines, with a
+// pause between polls, keeps any one memory channel lightly loaded).
+// Counters only grow; the reset kernel clears them before each launch.  Each
+// wave first drains its own memory operations, so everything stored before
+// the barrier (device-scope) is visible after it.  A poll limit bounds every
+// wait; on expiry the timeout word is set and the launch runs on to its end
+// (its rows are then flagged).
+
+__device__ __forceinline__ bool poll_until(uint32_t* w, uint32_t target, uint32_t* timeout) {
+  uint32_t polls = 0;
+  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++polls > kSpinLimit) {
+      __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  return true;
+}
 
 __device__ __forceinline__ void grid_sync(uint32_t* sync, uint32_t gen) {
   __builtin_amdgcn_s_waitcnt(0);
@@ -792,24 +833,24 @@ __device__ __forceinline__ void grid_sync(uint32_t* sync, uint32_t gen) {
     const uint32_t G = gridDim.x, g = blockIdx.x, j = g % kSyncGroups;
     const uint32_t size_j = (G - j + kSyncGroups - 1) / kSyncGroups;
     const uint32_t groups = G < static_cast<uint32_t>(kSyncGroups) ? G : kSyncGroups;
-    const uint32_t old = __hip_atomic_fetch_add(sync + j * kSyncStride, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gen * size_j - 1u)
+    uint32_t* line = sync + j * kSyncStride;
+    const uint32_t old = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gen * size_j - 1u) {  // last of its group: the group's leader
       __hip_atomic_fetch_add(sync + kSyncGlobal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = gen * groups;
-    uint32_t polls = 0;
-    while (__hip_atomic_load(sync + kSyncGlobal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++polls > kSpinLimit) {
-        __hip_atomic_store(sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
+      poll_until(sync + kSyncGlobal, gen * groups, sync + kSyncTimeout);
+      __hip_atomic_store(line + kSyncRelease, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      poll_until(line + kSyncRelease, gen, sync + kSyncTimeout);
     }
   }
   __syncthreads();
 }
 
-__global__ void markov_sync_reset_kernel(uint32_t* sync) {
-  for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) sync[i] = 0u;
+// Clears the barrier words and marks every draft token as not yet drawn.
+__global__ void markov_sync_reset_kernel(uint32_t* sync, int32_t* draft_tokens, int32_t n) {
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
+  for (int i = i0; i < kSyncWords; i += step) sync[i] = 0u;
+  for (int i = i0; i < n; i += step) draft_tokens[i] = -1;
 }
 
 template <typename T, bool VEC>
@@ -826,8 +867,9 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs 
     for (int b0 = 0; b0 < a.B; b0 += kTile)
       stream_tile<T, VEC, kFusedThreads, kFusedMS, 4, true>(a, af, tok0, b0, k, SL);
     grid_sync(a.sync, ++gen);
+    // x_k reaches the next step's stream phase through draft_tokens itself
+    // (-1 until stored), so no second barrier is needed
     for (int b = g; b < a.B; b += G) finalize_request<kFusedThreads, VEC, true>(a, b, k, FL);
-    if (k < a.gamma) grid_sync(a.sync, ++gen);
   }
   // after a barrier timeout, mark the rows this workgroup finalized
   if (threadIdx.x == 0 &&
@@ -873,7 +915,10 @@ FusedFit fused_fit() {
 template <typename T, bool VEC>
 hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
   if (fused) {
-    DSPARK_LAUNCH("markov_sync_reset", markov_sync_reset_kernel, dim3(1), dim3(256), 0, st, a.sync);
+    const int ntok = a.B * a.gamma;
+    DSPARK_LAUNCH("markov_sync_reset", markov_sync_reset_kernel,
+                  dim3(std::min(64, (std::max(ntok, kSyncWords) + 255) / 256)), dim3(256), 0, st,
+                  a.sync, a.draft_tokens, ntok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
