@@ -3,7 +3,8 @@
 One step is one pass of the whole path over one batch of the decode-verify
 workload (B = 64 requests, gamma = 5, V = 129280, bf16 logits, Markov rank 256,
 confidence width 4096, sampled at temperature 1 without truncation):
-  dspark_markov_sample  (gamma Markov steps: bias GEMM + sampling + confidence)
+  dspark_markov_sample  (gamma Markov steps: bias GEMM + sampling + confidence;
+                        one cooperative launch by default, --markov-plan)
   dspark_verify         (the oracle-free exact sampled verify of those proposals)
   dspark_accept_stats   (analytic acceptance of the same draft / target rows)
 Inputs are synthetic (workloads.py) and resident in HBM before timing starts;
@@ -14,8 +15,11 @@ an earlier step's reads.
 Prints one JSON line: value = verified rows per second, B (gamma + 1) rows per
 step; the roofline entry is the dominant kernel's algorithmic HBM bytes per
 launch over its average launch time, measured here with HIP events around each
-launch (the library's opt-in profiler, on the launch stream); cpu_baseline is
-the oracle, single-threaded, on a bounded sample of the same batch.
+launch (the library's opt-in profiler, on the launch stream; for the
+cooperative Markov launch the event pair also brackets its dispatch), and its
+counter-measured traffic from the committed rocprofv3 summary while the kernel
+sources match it; cpu_baseline is the oracle, single-threaded, on a bounded
+sample of the same batch.
 """
 
 from __future__ import annotations
@@ -43,7 +47,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent copies of the batch (logits and weights) cycled step by "
                          "step, so that no step finds its inputs in the 256 MB Infinity Cache")
-    ap.add_argument("--cpu-requests", type=int, default=16,
+    ap.add_argument("--cpu-requests", type=int, default=64,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--markov-plan", choices=["auto", "per-step"], default="auto",

@@ -262,9 +262,14 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
   const int ld = kpad + kPad;
   const int ksteps = kpad / 32;
 
-  // the tile's tokens x_{k-1} are requested first (loads complete in order),
-  // then every pass's backbone values, so that their latency overlaps the W1
-  // staging and the products
+  // every pass's backbone values are requested first (they do not depend on
+  // x_{k-1}), so that their transfer overlaps the wait for the tile's tokens
+  // x_{k-1}, the W1 staging and the products
+  QuadRaw<T> bbv[NH][NSP][MS];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    load_backbone<T, VEC, MS, NSP>(bbv[h], backbone, B, gamma, V, k, b0, h * NSP, vb, lane);
+
   int32_t xv = -1;
   if (tid < kTile) {
     const int b = b0 + tid;
@@ -288,10 +293,6 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       xv = clamp_token(xv, V);
     }
   }
-  QuadRaw<T> bbv[NH][NSP][MS];
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-    load_backbone<T, VEC, MS, NSP>(bbv[h], backbone, B, gamma, V, k, b0, h * NSP, vb, lane);
 
   // stage the gathered W1 rows of the tile's requests (MFMA B operand): every
   // 16-byte piece load issued back to back
