@@ -19,6 +19,9 @@ constexpr int kChunk = DSPARK_CHUNK;  // tokens per chunk of two-level Gumbel-ma
 constexpr float kNearEps = 1e-6f;     // margin of the NEAR_THRESHOLD diagnostic
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Words between ticket counters: each on its own 256-byte line, because
+// device-scope atomics to one line are performed one at a time.
+constexpr int kTicketStride = 64;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_inff(); }

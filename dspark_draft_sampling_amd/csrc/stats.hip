@@ -161,10 +161,10 @@ __global__ __launch_bounds__(kThreads) void stats_rows_kernel(
 //   stats_part1  per item: (max, sum) of both rows, sums with an integer
 //                base-2 shift (s = sum 2^(x log2e - floor(m log2e)))
 //   stats_part2  per item: the pair's normalisers from all its part1
-//                records, then the item's share of sum |P - T|; the second
-//                read of the pair follows the first within one call, so it
-//                is served by the Infinity Cache
-//   stats_pairs  per pair: L1, accept_rate, CE, BCE
+//                records, then the item's share of sum |P - T| (a second
+//                read of the pair), with a ticket per pair: the pair's last
+//                item writes L1, accept_rate, CE and BCE, and the wave
+//                finishing the last pair writes tau and the sums
 // Both item kernels keep the next item's loads in flight while reducing the
 // current one (two register buffers, unconditional clamped loads).
 constexpr int kSegIters = 4;  // 16-byte loads per lane per row per segment
@@ -238,9 +238,13 @@ __device__ __forceinline__ void seg_stats(const uint4* u, float& m, float& s) {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_part1_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
-    int32_t items, StatPart* __restrict__ part) {
+    int32_t items, StatPart* __restrict__ part, uint32_t* __restrict__ counters,
+    int32_t ncounters) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
+  // the ticket counters of stats_part2 start at zero
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ncounters; i += kThreads) counters[i * kTicketStride] = 0u;
   const int nwaves = gridDim.x * kWaves;
   int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
                                             (threadIdx.x >> 6));
@@ -291,24 +295,109 @@ __device__ __forceinline__ void pair_norm(const StatPart* __restrict__ rec, int 
   St = wave_sum(st);
 }
 
+// Per-block tau and the loss / report sums by one wave, in fp64 and a fixed
+// order (lane l owns blocks l, l + 64, ...; then a fixed butterfly), so the
+// sums are deterministic.  The per-position values were stored by other
+// waves of the same launch (device-scope loads).
+__device__ void wave_batch_reduce(const float* __restrict__ l1, const float* __restrict__ accept_rate,
+                                  const float* __restrict__ ce, const float* __restrict__ bce,
+                                  const uint8_t* __restrict__ block_mask, int32_t N,
+                                  int32_t gamma, float w_ce, float w_l1, float w_conf,
+                                  float* __restrict__ tau, float* __restrict__ sums) {
+  constexpr int Q = 8;  // num, tokens, l1, accept, tau, blocks, ce, bce
+  const int lane = threadIdx.x & 63;
+  // w_k = exp(-k / gamma) = r^k (k 1-based), r to fp32 accuracy
+  const double r = static_cast<double>(expf(-1.0f / static_cast<float>(gamma)));
+  double acc[Q] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int b = lane; b < N; b += 64) {
+    const size_t base = static_cast<size_t>(b) * gamma;
+    const bool m = block_mask ? block_mask[b] != 0 : true;
+    double cum = 1.0, t = 1.0, wk = 1.0;
+    for (int k = 0; k < gamma; ++k) {
+      const float a = load_coherent(accept_rate + base + k);
+      const float c = load_coherent(ce + base + k);
+      const float l = load_coherent(l1 + base + k);
+      const float x = load_coherent(bce + base + k);
+      cum *= a;
+      t += cum;
+      wk *= r;
+      if (m) {
+        acc[0] += wk * (w_ce * static_cast<double>(c) + w_l1 * static_cast<double>(l) +
+                        w_conf * static_cast<double>(x));
+        acc[1] += 1.0;
+        acc[2] += l;
+        acc[3] += a;
+        acc[6] += c;
+        acc[7] += x;
+      }
+    }
+    tau[b] = static_cast<float>(t);
+    if (m) {
+      acc[4] += t;
+      acc[5] += 1.0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc[q] += __shfl_xor(acc[q], o, 64);
+  if (lane == 0) {
+    const double n = acc[1];
+    sums[0] = static_cast<float>(acc[0]);
+    sums[1] = static_cast<float>(n);
+    sums[2] = static_cast<float>(acc[2]);
+    sums[3] = static_cast<float>(n);
+    sums[4] = static_cast<float>(acc[3]);
+    sums[5] = static_cast<float>(n);
+    sums[6] = static_cast<float>(acc[4]);
+    sums[7] = static_cast<float>(acc[5]);
+    sums[8] = static_cast<float>(acc[6]);
+    sums[9] = static_cast<float>(n);
+    sums[10] = static_cast<float>(acc[7]);
+    sums[11] = static_cast<float>(n);
+  }
+}
+
+struct StatsOut {
+  const int32_t* teacher;
+  const float* conf_logits;
+  const uint8_t* block_mask;
+  int32_t N, gamma;
+  float w_ce, w_l1, w_conf;
+  float* l1;
+  float* accept_rate;
+  float* ce;
+  float* bce;
+  float* tau;
+  float* sums;
+  uint32_t* counters;  // per pair: segments done; then pairs done (kTicketStride apart)
+};
+
+// Per item: the pair's normalisers from all its part1 records, then the
+// item's share of sum |P - T|, with a ticket on the pair: the pair's last
+// item writes L1, accept_rate, CE and BCE, and the wave finishing the last
+// pair writes tau and the sums.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
-    int32_t items, const StatPart* __restrict__ part, float* __restrict__ l1part,
-    float2* __restrict__ lse_pair) {
+    int32_t items, const StatPart* __restrict__ part, float* __restrict__ l1part, StatsOut o) {
   constexpr int EPL = 16 / sizeof(T);
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
-  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
-                                            (threadIdx.x >> 6));
-  if (item >= items) return;
-  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
-  auto reduce = [&](uint4* ud, uint4* ut, int it_) {
+  const int npairs = items / P;
+  // one item at a time per wave (its ticket waits for its own stores, so no
+  // later item's loads may be in flight); the other waves of the CU cover
+  // the latency
+  for (int item = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6); item < items;
+       item += nwaves) {
+    const int it_ = __builtin_amdgcn_readfirstlane(item);
     const int pair = it_ / P, seg = it_ - pair * P;
-    seg_mask<T>(V, seg * SEG, lane, ud, ut);
+    uint4 ud[kSegIters], ut[kSegIters];
+    seg_load<T>(draft, target, V, P, it_, lane, ud, ut);
     float M2d, Sd, M2t, St;
     pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
+    seg_mask<T>(V, seg * SEG, lane, ud, ut);
     const float isd = 1.0f / Sd, ist = 1.0f / St;
     float acc = 0.0f;
 #pragma unroll
@@ -318,46 +407,35 @@ __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
         acc += fabsf(__builtin_amdgcn_exp2f(fmaf(elem16(ud[it], j, T{}), kLog2e, -M2d)) * isd -
                      __builtin_amdgcn_exp2f(fmaf(elem16(ut[it], j, T{}), kLog2e, -M2t)) * ist);
     acc = wave_sum(acc);
+    uint32_t ticket = 0;
     if (lane == 0) {
-      l1part[it_] = acc;
-      if (seg == 0) lse_pair[pair] = make_float2(M2d * kLn2 + logf(Sd), M2t * kLn2 + logf(St));
+      store_coherent(l1part + it_, acc);
+      ticket = publish(o.counters + static_cast<size_t>(pair) * kTicketStride);
     }
-  };
-  seg_load<T>(draft, target, V, P, item, lane, ad, at);
-  while (true) {
-    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
-    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
-    reduce(ad, at, item);
-    if (n1 >= items) break;
-    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
-    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
-    reduce(bd, bt, n1);
-    if (n2 >= items) break;
-    item = n2;
-  }
-}
-
-// one wave per row pair: L1 from the item partials, then the pair's outputs
-template <typename T>
-__global__ __launch_bounds__(kThreads) void stats_pairs_kernel(
-    const T* __restrict__ draft, const int32_t* __restrict__ teacher,
-    const float* __restrict__ conf_logits, int32_t V, int32_t P, int32_t npairs,
-    const float* __restrict__ l1part, const float2* __restrict__ lse_pair, float* __restrict__ l1,
-    float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
-  const int lane = threadIdx.x & 63;
-  const int pair = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (pair >= npairs) return;
-  float acc = 0.0f;
-  for (int i = lane; i < P; i += 64) acc += l1part[static_cast<size_t>(pair) * P + i];
-  const float L1 = wave_sum(acc);
-  if (lane == 0) {
-    const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
-    const int32_t tch = clamp_token(teacher[pair], V);
-    const float c = conf_logits[pair];
-    l1[pair] = L1;
-    accept_rate[pair] = a;
-    ce[pair] = lse_pair[pair].x - load_logit(draft + static_cast<size_t>(pair) * V, tch);
-    bce[pair] = fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket != static_cast<uint32_t>(P - 1)) continue;
+    // the pair's last item: L1 from the item shares (fixed order), outputs
+    float L1 = 0.0f;
+    for (int i = lane; i < P; i += 64) L1 += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
+    L1 = wave_sum(L1);
+    uint32_t last = 0;
+    if (lane == 0) {
+      const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+      const int32_t tch = clamp_token(o.teacher[pair], V);
+      const float c = o.conf_logits[pair];
+      const float lse_d = M2d * kLn2 + logf(Sd);
+      store_coherent(o.l1 + pair, L1);
+      store_coherent(o.accept_rate + pair, a);
+      store_coherent(o.ce + pair, lse_d - load_logit(draft + static_cast<size_t>(pair) * V, tch));
+      store_coherent(o.bce + pair, fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c))));
+      last = publish(o.counters + static_cast<size_t>(npairs) * kTicketStride) ==
+                     static_cast<uint32_t>(npairs - 1)
+                 ? 1u
+                 : 0u;
+    }
+    if (__builtin_amdgcn_readfirstlane(last))
+      wave_batch_reduce(o.l1, o.accept_rate, o.ce, o.bce, o.block_mask, o.N, o.gamma, o.w_ce,
+                        o.w_l1, o.w_conf, o.tau, o.sums);
   }
 }
 
@@ -450,16 +528,16 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
     char* w = static_cast<char*>(ws);
     StatPart* part = reinterpret_cast<StatPart*>(w + pl.off_part);
     float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
-    float2* lse = reinterpret_cast<float2*>(w + pl.off_lse);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
     const int items = npairs * pl.P;
     const int wgs = std::min(kItemMaxWGs, (items + kWaves - 1) / kWaves);
     DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
-                  target, V, pl.P, items, part);
+                  target, V, pl.P, items, part, cnt, npairs + 1);
+    const StatsOut o{teacher, conf_logits, block_mask, N, gamma, w_ce, w_l1, w_conf,
+                     l1, accept_rate, ce, bce, tau, sums, cnt};
     DSPARK_LAUNCH("stats_part2", (stats_part2_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
-                  target, V, pl.P, items, part, l1part, lse);
-    DSPARK_LAUNCH("stats_pairs", (stats_pairs_kernel<T>), dim3((npairs + kWaves - 1) / kWaves),
-                  dim3(kThreads), 0, st, draft, teacher, conf_logits, V, pl.P, npairs, l1part, lse,
-                  l1, accept_rate, ce, bce);
+                  target, V, pl.P, items, part, l1part, o);
+    return hipGetLastError();
   } else if (npairs > 0) {
     const dim3 grid(static_cast<unsigned>(npairs));
     if (vec)
@@ -493,8 +571,8 @@ StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
     off = align_up(off + items * sizeof(StatPart), 256);
     p.off_l1 = off;
     off = align_up(off + items * sizeof(float), 256);
-    p.off_lse = off;
-    off = align_up(off + static_cast<size_t>(npairs) * sizeof(float2), 256);
+    p.off_cnt = off;
+    off = align_up(off + (static_cast<size_t>(npairs) + 1) * kTicketStride * sizeof(uint32_t), 256);
   }
   p.bytes = off;
   return p;

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
   // arm the per-request tickets of the decide pass (which starts after this
   // launch completes on the same stream)
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < B; i += kThreads) counters[i] = 0u;
+    for (int i = threadIdx.x; i < B; i += kThreads) counters[i * kTicketStride] = 0u;
   const int nwaves = gridDim.x * kWaves;
   // next item at or after i whose row the decision can consult (rows past
   // n_draft are skipped); returns `items` when there is none
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     store_coherent(&pk->v1, mine.v1);
     store_coherent(&pk->i1, mine.i1);
     store_coherent(&pk->v2, mine.v2);
-    const uint32_t prev = publish(&counters[b]);
+    const uint32_t prev = publish(&counters[b * kTicketStride]);
     sh_last = (prev == static_cast<uint32_t>(S2 - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -732,7 +732,7 @@ VerifyPlan plan_verify(int dtype, int32_t B, int32_t gamma, int32_t V, bool alig
   p.off_pick = off;
   off = align_up(off + static_cast<size_t>(B) * p.S2 * sizeof(Pick), 256);
   p.off_cnt = off;
-  off = align_up(off + static_cast<size_t>(B) * sizeof(uint32_t), 256);
+  off = align_up(off + static_cast<size_t>(B) * kTicketStride * sizeof(uint32_t), 256);
   p.off_trunc = off;
   off = align_up(off + static_cast<size_t>(B) * (gamma + 1) * sizeof(RowTrunc), 256);
   p.off_cmax = off;
