@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=64,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "stats"],
+                    default="decode",
+                    help="decode (default: the benchmark line); the other configurations "
+                         "are measured the same way for reference")
     ap.add_argument("--markov-plan", choices=["auto", "per-step"], default="auto",
                     help="Markov launch plan: one cooperative launch when it fits (auto) or "
                          "two launches per step")
@@ -211,6 +215,49 @@ def summarize_profile(base, out):
     print("\n".join(lines))
 
 
+def _timed(step, args, torch):
+    """W untimed steps, then K timed steps bracketed by synchronisation;
+    returns (ms_total, wall_s)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1), time.perf_counter() - t_wall
+
+
+def _kernels(step, args, torch, ds, bytes_of):
+    """Per-kernel launch durations over a second pass in the same launch
+    configuration (HIP events on the launch stream)."""
+    prof_steps = max(10, min(args.steps, 50))
+    ds.profile_enable(True)
+    for _ in range(prof_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = ds.profile_summary()
+    ds.profile_enable(False)
+    kernels = {}
+    for name, (n, ms) in prof.items():
+        avg_us = ms / n * 1e3
+        nbytes = bytes_of(name)
+        kernels[name] = dict(launches_per_step=n / prof_steps, avg_us=round(avg_us, 3),
+                             alg_bytes=int(nbytes), gbs=round(nbytes / (avg_us * 1e-6) / 1e9, 1))
+    return kernels
+
+
+def _roofline(kernels, headline):
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+    ach = kernels[dom]["gbs"]
+    return dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4),
+                traffic=counter_traffic(dom) if headline else None)
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -227,11 +274,32 @@ def main():
     import torch
 
     import dspark_draft_sampling_amd as ds
-    from workloads import decode_inputs
 
     ds.markov_plan(ds.MARKOV_AUTO if args.markov_plan == "auto" else ds.MARKOV_PER_STEP)
+    if args.workload == "stats":
+        line = run_stats(args, torch, ds)
+    else:
+        line = run_decode(args, torch, ds)
+    print(json.dumps(line), flush=True)
+
+
+DECODE_WORKLOADS = {
+    # name: (generator config, description)
+    "decode": ("decode", "decode verify: Markov sample + sampled verify + accept stats"),
+    "truncated": ("truncated", "truncated sampling at max batch: B=256, mixed greedy/sampled, "
+                               "per-request T, top-k, top-p; Markov + verify + accept stats"),
+    "wide_greedy": ("wide_greedy", "wide greedy tile: 64 requests x 8 rows, greedy Markov + verify "
+                                   "+ accept stats"),
+}
+
+
+def run_decode(args, torch, ds):
+    from workloads import decode_inputs
+
+    cfg_name, desc = DECODE_WORKLOADS[args.workload]
+    headline = args.workload == "decode"
     t0 = time.time()
-    inp = decode_inputs("decode")
+    inp = decode_inputs(cfg_name)
     B, g, V, r, d = inp["B"], inp["gamma"], inp["V"], inp["r"], inp["d"]
     print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
@@ -279,72 +347,94 @@ def main():
                          mo["q_thr"], mo["q_tok"], seed=0, out=vf_out)
         ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total, wall = _timed(step, args, torch)
     ms_per_step = ms_total / args.steps
     value = B * (g + 1) * args.steps / (ms_total / 1e3)
     print(f"# {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall:.3f}s",
           file=sys.stderr, flush=True)
 
-    # per-kernel launch durations, same launch configuration, HIP events on the launch stream
-    prof_steps = max(10, min(args.steps, 50))
-    ds.profile_enable(True)
-    for _ in range(prof_steps):
-        step()
-    torch.cuda.synchronize()
-    prof = ds.profile_summary()
-    ds.profile_enable(False)
     S = int((inp["mode"] != 0).sum())
     R = int((vf_out["accept_len"] < g).sum().item())
-    kernels = {}
-    for name, (n, ms) in prof.items():
-        avg_us = ms / n * 1e3
-        nbytes = kernel_bytes(name, B, g, V, r, d, S, R)
-        kernels[name] = dict(launches_per_step=n / prof_steps, avg_us=round(avg_us, 3),
-                             alg_bytes=int(nbytes), gbs=round(nbytes / (avg_us * 1e-6) / 1e9, 1))
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
-    ach = kernels[dom]["gbs"]
-    roofline = dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4),
-                    traffic=counter_traffic(dom))
+    kernels = _kernels(step, args, torch, ds, lambda n: kernel_bytes(n, B, g, V, r, d, S, R))
+    roofline = _roofline(kernels, headline)
     step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(inp, args.cpu_requests)
+        cpu = cpu_baseline(inp, min(args.cpu_requests, B) if headline else min(16, B), cfg_name)
 
-    line = dict(metric=METRIC, value=round(value, 1), unit="rows/s", n_gpus=1, steps=args.steps,
+    metric = METRIC if headline else f"verified rows/sec (B×(γ+1)×V logits) at {args.workload} (V={V},B={B},γ={g})"
+    modes = "sampled" if S == B else ("greedy" if S == 0 else "mixed")
+    truncation = "none" if not np.any((inp["top_k"] > 0) | (inp["top_p"] < 1.0)) else "top-k/top-p per request"
+    return dict(metric=metric, value=round(value, 1), unit="rows/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms_per_step, 5), higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-                config=dict(workload="decode verify: Markov sample + sampled verify + accept stats",
-                            B=B, gamma=g, V=V, r=r, d=d, logits="bf16", temperature=1.0,
-                            truncation="none", mode="sampled", rotated_batches=len(sets),
-                            markov_plan=args.markov_plan),
+                config=dict(workload=desc, B=B, gamma=g, V=V, r=r, d=d, logits="bf16",
+                            temperature=1.0 if headline else "per request", truncation=truncation,
+                            mode=modes, rotated_batches=len(sets), markov_plan=args.markov_plan),
                 roofline=roofline, cpu_baseline=cpu,
                 step=dict(alg_bytes=int(step_bytes),
                           alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                           accept_rate=round(float(vf_out["accept_len"].float().mean().item()) / g, 4),
                           kernels=kernels))
-    print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(inp, nreq):
+def run_stats(args, torch, ds):
+    """Training-side acceptance statistics alone: 2048 blocks x gamma 7."""
+    from workloads import stats_inputs
+
+    t0 = time.time()
+    inp = stats_inputs()
+    N, g, V = inp["N"], inp["gamma"], inp["V"]
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = [dict(draft=bf(inp["draft"]), target=bf(inp["target"])) for _ in range(max(1, min(args.rotate, 2)))]
+    teacher = torch.from_numpy(inp["teacher"]).to(dev)
+    conf = torch.from_numpy(inp["conf_logits"]).to(dev)
+    out = ds.dspark_accept_stats(sets[0]["draft"], sets[0]["target"], teacher, conf)
+    it = [0]
+
+    def step():
+        x = sets[it[0] % len(sets)]
+        it[0] += 1
+        ds.dspark_accept_stats(x["draft"], x["target"], teacher, conf, out=out)
+
+    ms_total, wall = _timed(step, args, torch)
+    ms_per_step = ms_total / args.steps
+    value = N * g * args.steps / (ms_total / 1e3)
+    kernels = _kernels(step, args, torch, ds, lambda n: kernel_bytes(n, N, g, V, 0, 0, 0, 0))
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as O
+
+        nb = 4
+        sub = stats_inputs(blocks=list(range(nb)))
+        t = time.perf_counter()
+        O.accept_stats(sub)
+        sec = time.perf_counter() - t
+        cpu = dict(value=round(nb * g / sec, 2), unit="rows/s", cores=1, kind="oracle",
+                   sample=f"{nb} of the {N} blocks, {sec:.1f}s single-threaded")
+    return dict(metric=f"stats rows/sec (N×γ row pairs) at V={V},N={N},γ={g}", value=round(value, 1),
+                unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="training acceptance statistics", N=N, gamma=g, V=V,
+                            logits="bf16", rotated_batches=len(sets)),
+                roofline=_roofline(kernels, False), cpu_baseline=cpu,
+                step=dict(kernels=kernels))
+
+
+def cpu_baseline(inp, nreq, cfg_name="decode"):
     """The oracle on the first nreq requests of the batch, single-threaded."""
     from oracle import oracle as O
     from workloads import decode_inputs
 
     reqs = list(range(nreq))
-    sub = decode_inputs("decode", requests=reqs, with_embed=False)
+    sub = decode_inputs(cfg_name, requests=reqs, with_embed=False)
     sub["embed"] = inp["embed"]
     g = sub["gamma"]
     t = time.perf_counter()
@@ -358,8 +448,8 @@ def cpu_baseline(inp, nreq):
     O.accept_stats(st)
     sec = time.perf_counter() - t
     return dict(value=round(nreq * (g + 1) / sec, 2), unit="rows/s", cores=1, kind="oracle",
-                sample=f"{nreq} of the 64 requests (Markov sample + verify + accept stats), "
-                       f"{sec:.1f}s single-threaded")
+                sample=f"{nreq} of the {inp['B']} requests (Markov sample + verify + accept "
+                       f"stats), {sec:.1f}s single-threaded")
 
 
 if __name__ == "__main__":

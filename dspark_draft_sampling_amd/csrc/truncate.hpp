@@ -52,7 +52,8 @@ struct SelResult {
 };
 
 // One histogram level over the row: tokens with key >= kmin whose key bits at
-// and above `top` equal `prefix` are binned by key bits [shift, top).
+// and above `top` equal `prefix` are binned by key bits [shift, top).  The row
+// functor provides load4(v0, x[4]) for v0 a multiple of 4 (-inf past V).
 template <int NT, class Row>
 __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int shift, uint32_t kmin,
                           float wa, float wb, SelLds<NT>& S) {
@@ -65,17 +66,27 @@ __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int s
   __syncthreads();
   const uint32_t mask = (1u << (top - shift)) - 1u;
   double local = 0.0;
-  for (int v = tid; v < V; v += NT) {
-    const float x = row(v);
-    if (!(x > neg_inf()) || x != x) continue;
-    const uint32_t k = order_key(x);
-    if (k < kmin) continue;
-    if (top < 32 && (k >> top) != prefix) continue;
-    const int bin = static_cast<int>((k >> shift) & mask);
-    const double w = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, wa, wb)));
-    atomicAdd(&S.cnt[bin], 1u);
-    atomicAdd(&S.mass[bin], w);
-    local += w;
+  // eight groups of four tokens per thread per round, all loads issued first
+  constexpr int U = 8;
+  for (int base = tid * 4; base < V; base += NT * 4 * U) {
+    float x[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) row.load4(base + u * NT * 4, x[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xv = x[u][e];  // -inf past the row end
+        if (!(xv > neg_inf()) || xv != xv) continue;
+        const uint32_t k = order_key(xv);
+        if (k < kmin) continue;
+        if (top < 32 && (k >> top) != prefix) continue;
+        const int bin = static_cast<int>((k >> shift) & mask);
+        const double w = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xv, wa, wb)));
+        atomicAdd(&S.cnt[bin], 1u);
+        atomicAdd(&S.mass[bin], w);
+        local += w;
+      }
   }
   atomicAdd(&S.total_m, local);  // the level's total weight
   __syncthreads();
@@ -367,29 +378,39 @@ __device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p,
 }
 
 // Gather every token >= tau of the chunks L.ci[0 .. L.nchunks) (wave w takes
-// chunks w, w+4, ...; lane l the 4 tokens 4l..4l+3).  Sets L.n (possibly
-// above kCandCap: overflow, nothing beyond the cap is stored).
+// groups of four chunks, the group's loads issued together; lane l the 4
+// tokens 4l..4l+3 of each chunk).  Sets L.n (possibly above kCandCap:
+// overflow, nothing beyond the cap is stored).
 template <int NT, class Row>
 __device__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
+  constexpr int NW = NT / 64;
+  constexpr int CU = 4;  // chunks whose loads a wave issues together
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float tau = L.tau;
-  for (int j = wave; j < L.nchunks; j += NT / 64) {
-    const int c = L.ci[j];
-    const int v0 = c * kChunk + lane * 4;
-    float x[4];
-    row.load4(v0, x);
+  const int nch = L.nchunks;
+  for (int j0 = wave * CU; j0 < nch; j0 += NW * CU) {
+    float x[CU][4];
+    int v0[CU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool take = v0 + e < V && x[e] >= tau;
-      const uint64_t mask = __ballot(take);
-      int base = 0;
-      if (lane == 0 && mask) base = atomicAdd(&L.n, __popcll(mask));
-      base = __shfl(base, 0, 64);
-      if (take) {
-        const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-        if (slot < kCandCap) L.cv[slot] = x[e];
-      }
+    for (int u = 0; u < CU; ++u) {
+      const int j = j0 + u;
+      v0[u] = j < nch ? L.ci[j] * kChunk + lane * 4 : V;  // V: nothing to load
+      row.load4(v0[u], x[u]);
     }
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool take = v0[u] + e < V && x[u][e] >= tau;
+        const uint64_t mask = __ballot(take);
+        int base = 0;
+        if (lane == 0 && mask) base = atomicAdd(&L.n, __popcll(mask));
+        base = __shfl(base, 0, 64);
+        if (take) {
+          const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+          if (slot < kCandCap) L.cv[slot] = x[u][e];
+        }
+      }
   }
   __syncthreads();
 }
