@@ -137,17 +137,6 @@ __device__ __forceinline__ void store4_coherent(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
-template <bool COH>
-__device__ __forceinline__ float ld_f(const float* p) {
-  if constexpr (COH) return load_coherent(p);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ int32_t ld_i(const int32_t* p) {
-  if constexpr (COH) return load_coherent(p);
-  else return *p;
-}
-
 // Device-scope 16-byte load (bypassing stale cached copies); the wait for its
 // data is part of the instruction sequence.
 __device__ __forceinline__ f32x4 load4_coherent(const void* p) {
@@ -458,23 +447,34 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
 // ---------------------------------------------------------------------------
 // Finalize phase.
 
-// One proposal row of scaled logits z (fp32), 4 tokens per load.
+// One proposal row of scaled logits z (fp32), 4 tokens per load, read through
+// a buffer resource over the row (reads past the row return 0, never fault).
+// COH: the row was written by other workgroups of the same launch, so every
+// load carries the sc1 policy (served by the device-coherent level, not a
+// possibly stale cache line); the compiler still batches them.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <bool COH>
 struct QzRow {
-  const float* p;
+  static constexpr int kPolicy = COH ? 16 : 0;  // cache policy bits: sc1
+  __amdgpu_buffer_rsrc_t rs;
   int V;
   bool vec4;
-  __device__ float operator()(int v) const { return ld_f<COH>(p + v); }
+  __device__ QzRow(const float* p, int V_, bool vec) : V(V_), vec4(vec) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), static_cast<short>(0), V_ * 4,
+                                           kBufferWord3);
+  }
   __device__ void load4(int v0, float* o) const {
-    if (!COH && vec4 && v0 + 3 < V) {
-      const float4 u = *reinterpret_cast<const float4*>(p + v0);
-      o[0] = u.x;
-      o[1] = u.y;
-      o[2] = u.z;
-      o[3] = u.w;
+    if (vec4 && v0 + 3 < V) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, v0 * 4, 0, kPolicy);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(u[e]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? ld_f<COH>(p + v0 + e) : neg_inf();
+      for (int e = 0; e < 4; ++e)
+        o[e] = v0 + e < V ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (v0 + e) * 4, 0, kPolicy))
+                          : neg_inf();
     }
   }
 };
@@ -527,6 +527,25 @@ __device__ __forceinline__ Top2 kept_chunk_scores(const QzRow<COH>& qr, int n, c
   return best;
 }
 
+// Level-1 scores from the histogram cut's kept chunk weights (fixed point,
+// 2^-40 units of the shifted frame 2^(z log2e - M2)): ln of the chunk's kept
+// mass plus the chunk's Gumbel.  Returns the thread's best two.
+template <int NT>
+__device__ __forceinline__ Top2 hist_chunk_scores(const HistLds<NT>& H, float M2, uint64_t seed,
+                                                  int32_t pos, uint32_t req) {
+  Top2 best{neg_inf(), INT32_MAX, neg_inf()};
+  const float off = (M2 - 40.0f) * kLn2;
+  for (int j = threadIdx.x; j < H.nl; j += NT) {
+    const int c = H.cl[j];
+    const fix_t w = H.cw[c];
+    if (w == 0) continue;
+    const float score = logf(static_cast<float>(w)) + off +
+                        gumbel(seed, static_cast<uint32_t>(c), pos, req, DSPARK_TAG_DRAFT_CHUNK);
+    best = top2_merge(best, Top2{score, c, neg_inf()});
+  }
+  return best;
+}
+
 template <int NT>
 struct FinLds {
   static constexpr int NW = NT / 64;
@@ -536,8 +555,74 @@ struct FinLds {
   float fin_M, fin_S, fin_zx;
   int32_t fin_x;
   uint32_t fin_fl;
+  float cm[kMaxChunksBound];  // chunk maxima of the row (truncated rows)
   TruncLds<NT> U;
 };
+
+// Kept set of a truncated row (smallest kept z, kept weight in units of
+// 2^(z log2e - M2)) and the level-1 choice over its chunks: candidates under
+// the chunk-maxima bound; else, for top-p alone, the weight histogram; else
+// radix selection over the row.  Kept out of line: only truncated rows pay
+// for its registers.  All threads of the workgroup call it.
+struct TruncOut {
+  float thr, s_kept;
+  Top2 best;
+};
+
+__device__ __forceinline__ int uni_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int NT, bool COH>
+__device__ __noinline__ TruncOut truncate_row(const float* zrow, int V, int vec, int C, int tk, float tp,
+                                              float M, float M2, float total, uint64_t seed, int32_t pos,
+                                              uint32_t req, FinLds<NT>& F) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // every argument is uniform: keep the row's buffer resource scalar
+  const uint64_t pz = reinterpret_cast<uint64_t>(zrow);
+  const float* zr = reinterpret_cast<const float*>(
+      (static_cast<uint64_t>(static_cast<uint32_t>(uni_i(static_cast<int>(pz >> 32)))) << 32) |
+      static_cast<uint32_t>(uni_i(static_cast<int>(pz))));
+  V = uni_i(V);
+  C = uni_i(C);
+  const QzRow<COH> qr(zr, V, uni_i(vec) != 0);
+  const float wa = kLog2e, wb = -M2;
+  int path = 0;
+  if (C <= kMaxChunksBound && chunk_bound(F.cm, C, tk, tp, wa, wb, total, F.U.c)) {
+    gather_candidates(qr, V, F.U.c);
+    exact_cut(tk, tp, wa, wb, total, F.U.c);
+    if (F.U.c.ok) path = 1;
+  }
+  if (path == 0 && tk == 0 && C <= kMaxChunksBound && hist_cut(qr, V, F.cm, C, M, total, wa, wb, tp, F.U.h))
+    path = 2;
+  TruncOut o;
+  Top2 tb;
+  if (path == 1) {
+    o.thr = F.U.c.thr;
+    o.s_kept = F.U.c.s_kept;
+    tb = kept_chunk_scores<NT, COH>(qr, F.U.c.nchunks, F.U.c.ci, o.thr, seed, pos, req);
+  } else if (path == 2) {
+    o.thr = F.U.h.thr;
+    o.s_kept = F.U.h.s_kept;
+    tb = hist_chunk_scores<NT>(F.U.h, M2, seed, pos, req);
+  } else {
+    const SelResult sr = select_threshold(qr, V, 32, tk, tp, wa, wb, F.U.s);
+    o.thr = sr.thr;
+    o.s_kept = static_cast<float>(sr.s_kept);
+    tb = kept_chunk_scores<NT, COH>(qr, C, nullptr, o.thr, seed, pos, req);
+  }
+  tb = wave_top2(tb);
+  __syncthreads();
+  if (lane == 0) {
+    F.sh_v1[wave] = tb.v1;
+    F.sh_i1[wave] = tb.i1;
+    F.sh_v2[wave] = tb.v2;
+  }
+  __syncthreads();
+  o.best = Top2{F.sh_v1[0], F.sh_i1[0], F.sh_v2[0]};
+#pragma unroll
+  for (int w = 1; w < NW; ++w) o.best = top2_merge(o.best, Top2{F.sh_v1[w], F.sh_i1[w], F.sh_v2[w]});
+  return o;
+}
 
 // Finalize step k of request b with the whole workgroup.  All waves combine
 // the chunk partials (and cut the kept set of a truncating request); then
@@ -561,8 +646,12 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   ArgMax am{neg_inf(), INT32_MAX};
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
   uint32_t bad = 0;
+  const float tp = a.pol.top_p[b];
+  const int tk_raw = a.pol.top_k[b];
+  const bool want_cm = sampled && truncated(tk_raw, tp, V) && C <= kMaxChunksBound;
   for (int c = tid; c < C; c += NT) {
     const ChunkPart p = load_part<COH>(pb + c);
+    if (want_cm) F.cm[c] = p.m;
     const int32_t arg = static_cast<int32_t>(p.arg_nf & 0x7fffffffu);
     bad |= p.arg_nf >> 31;
     am = better(am, ArgMax{p.m, arg == 0x7fffffff ? INT32_MAX : arg});
@@ -604,47 +693,17 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   // weights are 2^(z log2e - M2) with the integer shift M2, so that the drawn
   // token's weight and the kept sum round alike (one kept token: q = 1).
   float thr = neg_inf(), s_kept = 0.0f, M2 = 0.0f;
-  const int tk_raw = a.pol.top_k[b];
-  const float tp = a.pol.top_p[b];
   const bool trunc_row = sampled && truncated(tk_raw, tp, V) && M > neg_inf() && M < pos_inf();
-  const QzRow<COH> qr{a.q_z + row * V, V, VEC};
+  const QzRow<COH> qr(a.q_z + row * V, V, VEC);
   if (trunc_row) {
     const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
     M2 = floorf(M * kLog2e);
-    const float wa = kLog2e, wb = -M2;
     const float total = S * __builtin_amdgcn_exp2f(fmaf(M, kLog2e, -M2));
-    auto chunk_max = [pb](int c) { return load_part<COH>(pb + c).m; };
-    bool cand = false;
-    if (chunk_bound(chunk_max, C, tk, tp, wa, wb, total, F.U.c)) {
-      gather_candidates(qr, V, F.U.c);
-      exact_cut(tk, tp, wa, wb, total, F.U.c);
-      cand = F.U.c.ok != 0;
-    }
-    int nlist = C;
-    const int* list = nullptr;
-    if (cand) {
-      thr = F.U.c.thr;
-      s_kept = F.U.c.s_kept;
-      // the kept tokens lie in the chunks whose maximum reaches thr: a
-      // prefix of the sorted chunk list
-      nlist = count_at_least<NT>(F.U.c.cm, F.U.c.nchunks, thr, F.U.c.cnt);
-      list = F.U.c.ci;
-    } else {
-      const SelResult sr = select_threshold(qr, V, 32, tk, tp, wa, wb, F.U.s);
-      thr = sr.thr;
-      s_kept = static_cast<float>(sr.s_kept);
-    }
-    const Top2 tb = wave_top2(kept_chunk_scores<NT, COH>(qr, nlist, list, thr, a.seed, pos, req));
-    __syncthreads();
-    if (lane == 0) {
-      F.sh_v1[wave] = tb.v1;
-      F.sh_i1[wave] = tb.i1;
-      F.sh_v2[wave] = tb.v2;
-    }
-    __syncthreads();
-    Bst = Top2{F.sh_v1[0], F.sh_i1[0], F.sh_v2[0]};
-#pragma unroll
-    for (int w = 1; w < NW; ++w) Bst = top2_merge(Bst, Top2{F.sh_v1[w], F.sh_i1[w], F.sh_v2[w]});
+    const TruncOut o = truncate_row<NT, COH>(a.q_z + row * V, V, VEC ? 1 : 0, C, tk, tp, M, M2, total,
+                                              a.seed, pos, req, F);
+    thr = o.thr;
+    s_kept = o.s_kept;
+    Bst = o.best;
   }
 
   if (wave == 0) {

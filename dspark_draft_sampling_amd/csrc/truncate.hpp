@@ -221,23 +221,22 @@ __device__ __forceinline__ bool truncated(int top_k, float top_p, int V) {
 //  * top-p: any tau whose chunks' maxima alone carry top_p of the weight has
 //    mass(x >= tau) >= top_p * total, so the cut lies at or above tau.
 // Tokens of the chunks whose maximum reaches tau are gathered into LDS,
-// sorted, and the exact cut is taken there.  The caller falls back to
-// select_threshold when the bound cannot be formed or the candidates
-// overflow.
-constexpr int kMaxChunksSorted = 1024;  // chunk maxima sorted in LDS
-constexpr int kCandCap = 4096;          // candidate tokens held in LDS
+// sorted, and the exact cut is taken there.  The caller falls back when the
+// bound cannot be formed or the candidates overflow.
+constexpr int kMaxChunksBound = 1024;  // chunk maxima a bound looks at
+constexpr int kCandCap = 4096;         // candidate tokens held in LDS
 
 template <int NT>
 struct CandLds {
-  float cm[kMaxChunksSorted];  // chunk maxima, sorted descending
-  int ci[kMaxChunksSorted];    // their chunk indices
-  float cv[kCandCap];          // candidate values, sorted descending
-  float pw[kCandCap];          // running weight sums (inclusive)
+  int ci[kMaxChunksBound];  // chunks whose maximum reaches tau (any order)
+  float cv[kCandCap];       // candidate values, sorted descending
+  float pw[kCandCap];       // running weight sums (inclusive)
   float wtot[NT / 64];
-  int n;        // candidates gathered (> kCandCap: overflow)
-  int nchunks;  // chunks whose maximum reaches tau
-  int idx;      // scratch index (block maximum)
-  int cnt;      // scratch count
+  uint32_t key;  // order key of tau (0: no bound)
+  int n;         // candidates gathered (> kCandCap: overflow)
+  int nchunks;   // chunks whose maximum reaches tau
+  int idx;       // scratch index
+  int cnt;       // scratch count
   float tau;
   float thr;
   float s_kept;
@@ -245,13 +244,55 @@ struct CandLds {
   int ok;  // the cut lies inside the candidates
 };
 
-// Either the candidate state or the radix-select state: they are never live
+// Weight-histogram path for top-p without top-k (its state is HistLds below).
+// Weights are summed in fixed point, units of 2^-40 of the row's shifted
+// frame (the maximum weighs [1, 2)): integer sums are exact and independent
+// of order.
+using fix_t = unsigned long long;
+constexpr float kFix = 1099511627776.0f;  // 2^40
+constexpr int kHistBins = 2048;
+constexpr int kHistCap = 512;  // tokens of the cut's bin range held in LDS
+
+template <int NT>
+struct HistLds {
+  fix_t hw[kHistBins];        // weight per bin
+  fix_t cw[kMaxChunksBound];  // per chunk: its kept weight
+  int cl[kMaxChunksBound];    // chunks whose maximum lies in the window
+  float cv[kHistCap];         // tokens of the cut's bin: values, sorted descending,
+  int ct[kHistCap];           // their token indices,
+  fix_t pw[kHistCap];         // and the running weight from the row's top (inclusive)
+  fix_t wt[NT / 64];
+  fix_t above;  // weight of the bins before the cut's bin
+  int nl;       // listed chunks
+  int n;        // tokens of the cut's bin (> kHistCap: overflow)
+  int jc;       // the cut's bin
+  int cs;       // start of the cut group in cv
+  float thr;
+  float s_kept;
+};
+
+// Either the candidate, the histogram or the radix-select state: never live
 // at the same time.
 template <int NT>
 union TruncLds {
   CandLds<NT> c;
+  HistLds<NT> h;
   SelLds<NT> s;
 };
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kDppXor1>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
+  return (lane_i(v, 0) + lane_i(v, 16)) + (lane_i(v, 32) + lane_i(v, 48));
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 // Bitonic sort of n2 (a power of two) values, descending; with IX the
 // indices travel along (ascending index among equal values).  All threads of
@@ -330,48 +371,80 @@ __device__ int count_at_least(const float* v, int n, float t, int& slot) {
   return r;
 }
 
-// Sort the C chunk maxima (cmax(c)) and set L.tau and L.nchunks; returns
-// false when the bound cannot be formed.  wa, wb: the weight of a value x is
-// exp2(x wa + wb); total: the row's total weight.
-template <int NT, class ChunkMax>
-__device__ bool chunk_bound(const ChunkMax& cmax, int C, int top_k, float top_p, float wa,
-                            float wb, float total, CandLds<NT>& L) {
-  if (C > kMaxChunksSorted) return false;
-  const int n2 = pow2_at_least(C);
-  for (int i = threadIdx.x; i < n2; i += NT) {
-    L.cm[i] = i < C ? cmax(i) : neg_inf();
-    L.ci[i] = i;
+// tau of the chunk-maxima bound and the chunks whose maximum reaches it.
+// cm: the C chunk maxima (LDS; -inf or NaN: no finite token).  Wave 0 finds
+// tau by bisection over the maxima's order keys: top-k, the largest key with
+// at least top_k maxima at or above it (the k-th largest maximum); top-p, the
+// largest key whose maxima at or above it weigh top_p * total (with a margin
+// against rounding).  Sets L.tau, L.ci / L.nchunks (any order) and L.n = 0;
+// returns false when there is no bound.  wa, wb: a value x weighs
+// exp2(x wa + wb); total: the row's weight.
+template <int NT>
+__device__ bool chunk_bound(const float* cm, int C, int top_k, float top_p, float wa, float wb,
+                            float total, CandLds<NT>& L) {
+  if (C > kMaxChunksBound) return false;
+  if (threadIdx.x < 64) {
+    constexpr int PER = kMaxChunksBound / 64;
+    const int lane = threadIdx.x;
+    const bool byk = top_k > 0;
+    uint32_t key[PER];
+    float w[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = lane + 64 * j;
+      const float x = c < C ? cm[c] : neg_inf();
+      const bool fin = x > neg_inf();  // false for NaN
+      key[j] = fin ? order_key(x) : 0u;
+      w[j] = (!byk && fin) ? __builtin_amdgcn_exp2f(fmaf(x, wa, wb)) : 0.0f;
+    }
+    uint32_t t = 0u;
+    if (byk) {
+      if (top_k <= C && top_k <= kCandCap) {
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = t | (1u << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) cnt += key[j] >= cand ? 1 : 0;
+          if (wave_sum_i(cnt) >= top_k) t = cand;
+        }
+      }
+    } else if (top_p < 1.0f) {
+      const float target = (top_p > 0.0f ? top_p : 0.0f) * total * 1.0009765625f;
+      float all = 0.0f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) all += w[j];
+      if (wave_sum(all) >= target) {
+        // the masked sums only grow as the key falls (rounding is monotone)
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = t | (1u << bit);
+          float ws = 0.0f;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) ws += key[j] >= cand ? w[j] : 0.0f;
+          if (wave_sum(ws) >= target) t = cand;
+        }
+      }
+    }
+    if (lane == 0) {
+      L.key = t;
+      L.tau = t ? key_value(t) : neg_inf();
+      L.nchunks = 0;
+      L.n = 0;
+    }
   }
   __syncthreads();
-  sort_desc<NT, true>(L.cm, L.ci, n2);
-  float tau = neg_inf();
-  if (top_k > 0) {
-    if (top_k <= C && top_k <= kCandCap) tau = L.cm[top_k - 1];
-  } else if (top_p < 1.0f) {
-    // running weight of the sorted maxima; tau = the first maximum at which
-    // it reaches top_p * total (with a margin against rounding)
-    for (int i = threadIdx.x; i < C; i += NT)
-      L.cv[i] = L.cm[i] > neg_inf() ? __builtin_amdgcn_exp2f(fmaf(L.cm[i], wa, wb)) : 0.0f;
-    __syncthreads();
-    block_scan_incl<NT>(L.cv, C, L.wtot);
-    const float target = (top_p > 0.0f ? top_p : 0.0f) * total * 1.0009765625f;
-    if (threadIdx.x == 0) L.idx = -1;
-    __syncthreads();
-    for (int i = threadIdx.x; i < C; i += NT)
-      if (L.cm[i] > neg_inf() && L.cv[i] >= target && (i == 0 || L.cv[i - 1] < target))
-        L.idx = i;  // unique: the running sum is monotone
-    __syncthreads();
-    if (L.idx >= 0) tau = L.cm[L.idx];
-  }
-  if (!(tau > neg_inf())) {
+  if (L.key == 0u) {
     __syncthreads();
     return false;
   }
-  const int nc = count_at_least<NT>(L.cm, C, tau, L.cnt);
-  if (threadIdx.x == 0) {
-    L.tau = tau;
-    L.nchunks = nc;
-    L.n = 0;
+  const float tau = L.tau;
+  for (int c0 = 0; c0 < C; c0 += NT) {
+    const int c = c0 + static_cast<int>(threadIdx.x);
+    const bool take = c < C && cm[c] >= tau;
+    const uint64_t mask = __ballot(take);
+    int base = 0;
+    if ((threadIdx.x & 63) == 0 && mask) base = atomicAdd(&L.nchunks, __popcll(mask));
+    base = __shfl(base, 0, 64);
+    if (take) L.ci[base + __popcll(mask & ((1ull << (threadIdx.x & 63)) - 1ull))] = c;
   }
   __syncthreads();
   return true;
@@ -468,6 +541,242 @@ __device__ void exact_cut(int top_k, float top_p, float wa, float wb, float tota
     L.ok = ok ? 1 : 0;
   }
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Histogram path: top-p without top-k, for rows whose kept set spreads over
+// too many chunks for the maxima bound.  A value x weighs 2^u, u = x wa + wb
+// (the row maximum M has u in [0, 1)), taken in fixed point.
+//
+// Window: the smallest kept value thr has w(thr) > (1 - top_p) total / V (the
+// tokens at or below thr weigh more than (1 - top_p) of the total and number
+// at most V), so no token with u below ulo = log2 of that bound, less one for
+// rounding, is kept; ulo is also held within 64 of umax (the bound itself
+// lies within 55 of it).  The window [ulo, umax] is cut into kHistBins bins
+// of equal width by (umax - u), a non-increasing function of x: equal values
+// share a bin and a larger value never lies in a later bin.
+//  pass A: the weight of every bin, over the chunks whose maximum lies in
+//    the window (their list kept);
+//  the cut's bin jc: the first non-empty bin at which the running weight
+//    reaches top_p * total.  The running sums are exact, so every group
+//    before jc is kept (its weight from the top stays below the target),
+//    every group after jc is not, and jc's first group is kept;
+//  pass B: per listed chunk reaching jc, the weight of its tokens before jc;
+//    jc's tokens into LDS;
+//  cut: jc's tokens sorted, their running weight from the weight before jc,
+//    the top-p rule group by group.
+// Leaves H.thr, H.s_kept (kept weight, 2^u units) and H.cw[c] = chunk c's
+// kept weight (fixed point) for the chunks H.cl[0 .. H.nl) (the others hold
+// no kept token).  Returns false when jc's tokens overflow LDS or the window
+// does not reach the target (then nothing is decided).
+__device__ __forceinline__ fix_t to_fix(float w) { return static_cast<fix_t>(w * kFix); }
+
+struct HistMap {
+  float wa, wb, umax, ulo, inv;
+  // bin of value x (-1 below the window, NaN and -inf included) and its weight
+  __device__ __forceinline__ int bin(float x, float& w) const {
+    const float u = fmaf(x, wa, wb);
+    if (!(u >= ulo)) return -1;
+    w = __builtin_amdgcn_exp2f(u);
+    const int j = static_cast<int>((umax - u) * inv);
+    return j < 0 ? 0 : (j < kHistBins ? j : kHistBins - 1);
+  }
+};
+
+// In-place inclusive prefix sum of a[0 .. n) (LDS) plus base, all threads.
+template <int NT>
+__device__ void block_scan_fix(fix_t* a, int n, fix_t base, fix_t* wt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + NT - 1) / NT;
+  const int lo = tid * per, hi = min(n, lo + per);
+  fix_t s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  fix_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const fix_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wt[wave] = x;
+  __syncthreads();
+  fix_t run = base + x - s;
+  for (int w = 0; w < wave; ++w) run += wt[w];
+  for (int i = lo; i < hi; ++i) {
+    run += a[i];
+    a[i] = run;
+  }
+  __syncthreads();
+}
+
+template <int NT, class Row>
+__device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M, float total,
+                         float wa, float wb, float top_p, HistLds<NT>& H) {
+  constexpr int NW = NT / 64, CU = 8, PB = kHistBins / NT;
+  static_assert(kHistBins % NT == 0, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (C > kMaxChunksBound || !(total > 0.0f) || !(total < pos_inf())) return false;
+  const float p = top_p > 0.0f ? top_p : 0.0f;
+  HistMap hm;
+  hm.wa = wa;
+  hm.wb = wb;
+  hm.umax = fmaf(M, wa, wb);
+  hm.ulo = fmaxf(__log2f((1.0f - p) * total / static_cast<float>(V)) - 1.0f, hm.umax - 64.0f);
+  hm.inv = static_cast<float>(kHistBins) / (hm.umax - hm.ulo);
+  // a group is kept iff the weight above it is < p * total: for the integer
+  // sums, iff it is < T = ceil(p * total * 2^40)
+  const fix_t T = static_cast<fix_t>(ceil(static_cast<double>(p) * static_cast<double>(total) *
+                                          static_cast<double>(kFix)));
+  for (int i = tid; i < kHistBins; i += NT) H.hw[i] = 0;
+  for (int c = tid; c < C; c += NT) H.cw[c] = 0;
+  if (tid == 0) {
+    H.nl = 0;
+    H.n = 0;
+    H.jc = INT32_MAX;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < C; c0 += NT) {
+    const int c = c0 + tid;
+    float w;
+    const bool take = c < C && hm.bin(cm[c], w) >= 0;
+    const uint64_t mask = __ballot(take);
+    int base = 0;
+    if (lane == 0 && mask) base = atomicAdd(&H.nl, __popcll(mask));
+    base = __shfl(base, 0, 64);
+    if (take) H.cl[base + __popcll(mask & ((1ull << lane) - 1ull))] = c;
+  }
+  __syncthreads();
+  const int nl = H.nl;
+  // pass A: wave w takes listed chunks in groups of CU, the group's loads
+  // issued together; lane l the tokens 4l .. 4l+3 of each chunk
+  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
+    float x[CU][4];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = j0 + u;
+      row.load4(j < nl ? H.cl[j] * kChunk + 4 * lane : V, x[u]);  // V: nothing loaded
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float w;
+        const int b = hm.bin(x[u][e], w);
+        if (b >= 0) atomicAdd(&H.hw[b], to_fix(w));
+      }
+  }
+  __syncthreads();
+  // the cut's bin: thread t owns bins t*PB .. t*PB+PB-1
+  fix_t own = 0;
+#pragma unroll
+  for (int i = 0; i < PB; ++i) own += H.hw[tid * PB + i];
+  fix_t incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const fix_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) H.wt[wave] = incl;
+  __syncthreads();
+  fix_t run = incl - own;
+  for (int w = 0; w < wave; ++w) run += H.wt[w];
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    const int j = tid * PB + i;
+    const fix_t h = H.hw[j];
+    if (h && run + h >= T) {  // this thread's first such bin; the smallest wins
+      atomicMin(&H.jc, j);
+      break;
+    }
+    run += h;
+  }
+  __syncthreads();
+  const int jc = H.jc;
+  if (jc == INT32_MAX) {  // the window holds less than the target
+    __syncthreads();
+    return false;
+  }
+  // weight before jc: the owner of jc knows it
+  {
+    fix_t r = incl - own;
+    for (int w = 0; w < wave; ++w) r += H.wt[w];
+    if (jc / PB == tid) {
+      for (int j = tid * PB; j < jc; ++j) r += H.hw[j];
+      H.above = r;
+    }
+  }
+  // pass B over the listed chunks whose maximum reaches jc
+  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
+    float x[CU][4];
+    int c[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = j0 + u;
+      float w;
+      c[u] = (j < nl && hm.bin(cm[H.cl[j]], w) <= jc) ? H.cl[j] : -1;
+      row.load4(c[u] >= 0 ? c[u] * kChunk + 4 * lane : V, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (c[u] < 0) continue;  // wave-uniform
+      fix_t a = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float w = 0.0f;
+        const int b = hm.bin(x[u][e], w);
+        if (b >= 0 && b < jc) a += to_fix(w);
+        const bool take = b == jc;
+        const uint64_t mask = __ballot(take);
+        if (mask) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&H.n, __popcll(mask));
+          base = __shfl(base, 0, 64);
+          const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+          if (take && slot < kHistCap) {
+            H.cv[slot] = x[u][e];
+            H.ct[slot] = c[u] * kChunk + 4 * lane + e;
+          }
+        }
+      }
+      a = wave_sum_u64(a);
+      if (lane == 0) H.cw[c[u]] = a;
+    }
+  }
+  __syncthreads();
+  const int n = H.n;
+  if (n > kHistCap || n < 1) {
+    __syncthreads();
+    return false;
+  }
+  // the cut inside jc
+  const int n2 = pow2_at_least(n);
+  for (int i = n + tid; i < n2; i += NT) {
+    H.cv[i] = neg_inf();
+    H.ct[i] = INT32_MAX;
+  }
+  __syncthreads();
+  sort_desc<NT, true>(H.cv, H.ct, n2);
+  for (int i = tid; i < n; i += NT) H.pw[i] = to_fix(__builtin_amdgcn_exp2f(fmaf(H.cv[i], wa, wb)));
+  if (tid == 0) H.cs = 0;  // jc's first group is kept
+  __syncthreads();
+  block_scan_fix<NT>(H.pw, n, H.above, H.wt);
+  int best = 0;
+  for (int i = tid; i < n; i += NT)
+    if (i > 0 && H.cv[i] != H.cv[i - 1] && H.pw[i - 1] < T) best = i;
+  if (best > 0) atomicMax(&H.cs, best);
+  __syncthreads();
+  const float thr = H.cv[H.cs];
+  // the cut group ends where the values fall below thr; its kept tokens add
+  // to their chunks' weight
+  for (int i = tid; i < n; i += NT)
+    if (H.cv[i] >= thr) {
+      atomicAdd(&H.cw[H.ct[i] / kChunk], to_fix(__builtin_amdgcn_exp2f(fmaf(H.cv[i], wa, wb))));
+      if (i + 1 == n || H.cv[i + 1] < thr) {
+        H.thr = thr;
+        H.s_kept = static_cast<float>(H.pw[i]) * (1.0f / kFix);
+      }
+    }
+  __syncthreads();
+  return true;
 }
 
 }  // namespace dspark

@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
     const int32_t* __restrict__ n_draft, const RowPart* __restrict__ part,
     const float* __restrict__ cmax, RowTrunc* __restrict__ trunc) {
   __shared__ TruncLds<kSelThreads> U;
+  __shared__ float cms[kMaxChunksBound];
   __shared__ float sh_m[kSelThreads / 64], sh_s[kSelThreads / 64];
   const int G1 = gamma + 1;
   const int row = blockIdx.x, b = row / G1, k = row - b * G1;
@@ -329,16 +330,23 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
   const LogitRow<T> lr{rp, V, (V % 4 == 0) && reinterpret_cast<uintptr_t>(target) % 16 == 0};
   const int C = (V + kChunk - 1) / kChunk;
   bool done = false;
-  if (have_cmax) {
+  if (have_cmax && C <= kMaxChunksBound) {
+    // candidates under the chunk-maxima bound; else, for top-p alone, the
+    // weight histogram
     const float* cm = cmax + static_cast<size_t>(row) * C;
-    auto chunk_max = [cm](int c) { return cm[c]; };
-    if (chunk_bound(chunk_max, C, tk, tp, cT, -M2, total, U.c)) {
+    for (int c = threadIdx.x; c < C; c += kSelThreads) cms[c] = cm[c];
+    __syncthreads();
+    if (chunk_bound(cms, C, tk, tp, cT, -M2, total, U.c)) {
       gather_candidates(lr, V, U.c);
       exact_cut(tk, tp, cT, -M2, total, U.c);
       if (U.c.ok) {
         if (threadIdx.x == 0) trunc[row] = RowTrunc{U.c.thr, U.c.s_kept};
         done = true;
       }
+    }
+    if (!done && tk == 0 && hist_cut(lr, V, cms, C, m, total, cT, -M2, tp, U.h)) {
+      if (threadIdx.x == 0) trunc[row] = RowTrunc{U.h.thr, U.h.s_kept};
+      done = true;
     }
   }
   if (!done) {  // radix selection over the whole row
