@@ -23,6 +23,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 // device-scope atomics to one line are performed one at a time.
 constexpr int kTicketStride = 64;
 
+// Raw buffer resources (loads bounds-checked against the resource's size:
+// reads past it return 0).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Index of the calling wave in its workgroup, as a scalar (the compiler
+// cannot tell that threadIdx.x / 64 is uniform across the wave).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
+// A value the caller knows to be the same on every lane, as a scalar.
+__device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
 

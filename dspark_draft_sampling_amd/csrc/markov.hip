@@ -452,9 +452,6 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
 // COH: the row was written by other workgroups of the same launch, so every
 // load carries the sc1 policy (served by the device-coherent level, not a
 // possibly stale cache line); the compiler still batches them.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-
 template <bool COH>
 struct QzRow {
   static constexpr int kPolicy = COH ? 16 : 0;  // cache policy bits: sc1
@@ -465,11 +462,15 @@ struct QzRow {
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), static_cast<short>(0), V_ * 4,
                                            kBufferWord3);
   }
+  // one 16-byte load (row 16-byte aligned, v0 a multiple of 4; 0 past V)
+  __device__ void load4u(int v0, float* o) const {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, v0 * 4, 0, kPolicy);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(u[e]);
+  }
   __device__ void load4(int v0, float* o) const {
     if (vec4 && v0 + 3 < V) {
-      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, v0 * 4, 0, kPolicy);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(u[e]);
+      load4u(v0, o);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -488,7 +489,7 @@ template <int NT, bool COH>
 __device__ __forceinline__ Top2 kept_chunk_scores(const QzRow<COH>& qr, int n, const int* list, float thr,
                                   uint64_t seed, int32_t pos, uint32_t req) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
   constexpr int kU = 4;
   for (int j0 = wave * kU; j0 < n; j0 += NW * kU) {
@@ -497,7 +498,7 @@ __device__ __forceinline__ Top2 kept_chunk_scores(const QzRow<COH>& qr, int n, c
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int j = j0 + u;
-      cs[u] = j < n ? (list ? list[j] : j) : -1;
+      cs[u] = j < n ? (list ? uniform_i(list[j]) : j) : -1;
       if (cs[u] >= 0) {
         qr.load4(cs[u] * kChunk + 4 * lane, z[u]);
       } else {
@@ -569,8 +570,6 @@ struct TruncOut {
   Top2 best;
 };
 
-__device__ __forceinline__ int uni_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 template <int NT, bool COH>
 __device__ __noinline__ TruncOut truncate_row(const float* zrow, int V, int vec, int C, int tk, float tp,
                                               float M, float M2, float total, uint64_t seed, int32_t pos,
@@ -580,11 +579,11 @@ __device__ __noinline__ TruncOut truncate_row(const float* zrow, int V, int vec,
   // every argument is uniform: keep the row's buffer resource scalar
   const uint64_t pz = reinterpret_cast<uint64_t>(zrow);
   const float* zr = reinterpret_cast<const float*>(
-      (static_cast<uint64_t>(static_cast<uint32_t>(uni_i(static_cast<int>(pz >> 32)))) << 32) |
-      static_cast<uint32_t>(uni_i(static_cast<int>(pz))));
-  V = uni_i(V);
-  C = uni_i(C);
-  const QzRow<COH> qr(zr, V, uni_i(vec) != 0);
+      (static_cast<uint64_t>(static_cast<uint32_t>(uniform_i(static_cast<int>(pz >> 32)))) << 32) |
+      static_cast<uint32_t>(uniform_i(static_cast<int>(pz))));
+  V = uniform_i(V);
+  C = uniform_i(C);
+  const QzRow<COH> qr(zr, V, uniform_i(vec) != 0);
   const float wa = kLog2e, wb = -M2;
   int path = 0;
   if (C <= kMaxChunksBound && chunk_bound(F.cm, C, tk, tp, wa, wb, total, F.U.c)) {
@@ -592,7 +591,7 @@ __device__ __noinline__ TruncOut truncate_row(const float* zrow, int V, int vec,
     exact_cut(tk, tp, wa, wb, total, F.U.c);
     if (F.U.c.ok) path = 1;
   }
-  if (path == 0 && tk == 0 && C <= kMaxChunksBound && hist_cut(qr, V, F.cm, C, M, total, wa, wb, tp, F.U.h))
+  if (path == 0 && tk == 0 && C <= kMaxChunksBound && hist_cut<NT, true>(qr, V, F.cm, C, M, total, wa, wb, tp, F.U.h))
     path = 2;
   TruncOut o;
   Top2 tb;

@@ -55,7 +55,7 @@ struct SelResult {
 // and above `top` equal `prefix` are binned by key bits [shift, top).  The row
 // functor provides load4(v0, x[4]) for v0 a multiple of 4 (-inf past V).
 template <int NT, class Row>
-__device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int shift, uint32_t kmin,
+__device__ __forceinline__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int shift, uint32_t kmin,
                           float wa, float wb, SelLds<NT>& S) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kSelBins; i += NT) {
@@ -97,7 +97,7 @@ __device__ void sel_level(const Row& row, int V, uint32_t prefix, int top, int s
 // the whole level holds less, the smallest non-empty bin.  Leaves the bin and
 // the count / weight strictly above it in S.
 template <int NT>
-__device__ void sel_find(SelLds<NT>& S, int nbins, bool by_mass, double target) {
+__device__ __forceinline__ void sel_find(SelLds<NT>& S, int nbins, bool by_mass, double target) {
   const int tid = threadIdx.x;
   constexpr int per = kSelBins / NT;  // bins per thread, descending
   uint32_t c = 0;
@@ -156,7 +156,7 @@ __device__ void sel_find(SelLds<NT>& S, int nbins, bool by_mass, double target) 
 // keybits = 16 for bf16 rows (their key's low 16 bits are determined by the
 // sign), 32 otherwise.
 template <int NT, class Row>
-__device__ SelResult select_threshold(const Row& row, int V, int keybits, int top_k, float top_p,
+__device__ __forceinline__ SelResult select_threshold(const Row& row, int V, int keybits, int top_k, float top_p,
                                       float wa, float wb, SelLds<NT>& S) {
   const int nlev = keybits == 16 ? 2 : 3;
   const int tops[3] = {32, 21, 10};
@@ -288,17 +288,64 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return (lane_i(v, 0) + lane_i(v, 16)) + (lane_i(v, 32) + lane_i(v, 48));
 }
 
+// Integer sum over the wave (same butterfly as wave_sum, on both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(lane_i(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(lane_i(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_u64<kDppXor1>(v);
+  v += dpp_u64<kDppXor2>(v);
+  v += dpp_u64<kDppHalfMirror>(v);
+  v += dpp_u64<kDppMirror>(v);
+  return (lane_u64(v, 0) + lane_u64(v, 16)) + (lane_u64(v, 32) + lane_u64(v, 48));
+}
+
+// Rank sort of v[0 .. n) descending (LDS, n <= NT), ties by ascending ix
+// (IX) or by position; tv / ti: scratch of n entries.  For the small sets
+// where a bitonic network would spend most of its time in barriers.
+template <int NT, bool IX>
+__device__ __forceinline__ void rank_sort_desc(float* v, int* ix, int n, float* tv, int* ti) {
+  const int i = threadIdx.x;
+  float x = 0.0f;
+  int id = 0, r = 0;
+  if (i < n) {
+    x = v[i];
+    if constexpr (IX) id = ix[i];
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) {
+      const float y = v[j];
+      bool before = y > x;
+      if constexpr (IX) before = before || (y == x && ix[j] < id);
+      else before = before || (y == x && j < i);
+      r += before ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (i < n) {
+    tv[r] = x;
+    if constexpr (IX) ti[r] = id;
+  }
+  __syncthreads();
+  if (i < n) {
+    v[i] = tv[i];
+    if constexpr (IX) ix[i] = ti[i];
+  }
+  __syncthreads();
 }
 
 // Bitonic sort of n2 (a power of two) values, descending; with IX the
 // indices travel along (ascending index among equal values).  All threads of
 // the workgroup take part.
 template <int NT, bool IX>
-__device__ void sort_desc(float* v, int* ix, int n2) {
+__device__ __forceinline__ void sort_desc(float* v, int* ix, int n2) {
   for (int k = 2; k <= n2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < n2; i += NT) {
@@ -333,7 +380,7 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 
 // In-place inclusive prefix sum of a[0 .. n) (LDS), all threads.
 template <int NT>
-__device__ void block_scan_incl(float* a, int n, float* wtot) {
+__device__ __forceinline__ void block_scan_incl(float* a, int n, float* wtot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
@@ -358,7 +405,7 @@ __device__ void block_scan_incl(float* a, int n, float* wtot) {
 
 // Number of v[0 .. n) that are >= t (v sorted descending), all threads.
 template <int NT>
-__device__ int count_at_least(const float* v, int n, float t, int& slot) {
+__device__ __forceinline__ int count_at_least(const float* v, int n, float t, int& slot) {
   if (threadIdx.x == 0) slot = 0;
   __syncthreads();
   int c = 0;
@@ -380,7 +427,7 @@ __device__ int count_at_least(const float* v, int n, float t, int& slot) {
 // returns false when there is no bound.  wa, wb: a value x weighs
 // exp2(x wa + wb); total: the row's weight.
 template <int NT>
-__device__ bool chunk_bound(const float* cm, int C, int top_k, float top_p, float wa, float wb,
+__device__ __forceinline__ bool chunk_bound(const float* cm, int C, int top_k, float top_p, float wa, float wb,
                             float total, CandLds<NT>& L) {
   if (C > kMaxChunksBound) return false;
   if (threadIdx.x < 64) {
@@ -455,19 +502,19 @@ __device__ bool chunk_bound(const float* cm, int C, int top_k, float top_p, floa
 // tokens 4l..4l+3 of each chunk).  Sets L.n (possibly above kCandCap:
 // overflow, nothing beyond the cap is stored).
 template <int NT, class Row>
-__device__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
+__device__ __forceinline__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
   constexpr int NW = NT / 64;
   constexpr int CU = 4;  // chunks whose loads a wave issues together
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const float tau = L.tau;
-  const int nch = L.nchunks;
+  const int nch = uniform_i(L.nchunks);
   for (int j0 = wave * CU; j0 < nch; j0 += NW * CU) {
     float x[CU][4];
     int v0[CU];
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       const int j = j0 + u;
-      v0[u] = j < nch ? L.ci[j] * kChunk + lane * 4 : V;  // V: nothing to load
+      v0[u] = j < nch ? uniform_i(L.ci[j]) * kChunk + lane * 4 : V;  // V: nothing to load
       row.load4(v0[u], x[u]);
     }
 #pragma unroll
@@ -495,7 +542,7 @@ __device__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
 // top-k is off).  Sets L.thr (smallest kept value), L.s_kept (kept weight),
 // L.nkept and L.ok (0: the cut is not decided by the candidates).
 template <int NT>
-__device__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds<NT>& L) {
+__device__ __forceinline__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds<NT>& L) {
   const int n = L.n;
   if (n > kCandCap || n < 1 || (top_k > 0 && top_k > n)) {
     __syncthreads();
@@ -503,10 +550,14 @@ __device__ void exact_cut(int top_k, float top_p, float wa, float wb, float tota
     __syncthreads();
     return;
   }
-  const int n2 = pow2_at_least(n);
-  for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += NT) L.cv[i] = neg_inf();
-  __syncthreads();
-  sort_desc<NT, false>(L.cv, nullptr, n2);
+  if (n <= NT) {
+    rank_sort_desc<NT, false>(L.cv, nullptr, n, L.pw, nullptr);
+  } else {
+    const int n2 = pow2_at_least(n);
+    for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += NT) L.cv[i] = neg_inf();
+    __syncthreads();
+    sort_desc<NT, false>(L.cv, nullptr, n2);
+  }
   for (int i = threadIdx.x; i < n; i += NT)
     L.pw[i] = __builtin_amdgcn_exp2f(fmaf(L.cv[i], wa, wb));
   __syncthreads();
@@ -569,10 +620,23 @@ __device__ void exact_cut(int top_k, float top_p, float wa, float wb, float tota
 // kept weight (fixed point) for the chunks H.cl[0 .. H.nl) (the others hold
 // no kept token).  Returns false when jc's tokens overflow LDS or the window
 // does not reach the target (then nothing is decided).
-__device__ __forceinline__ fix_t to_fix(float w) { return static_cast<fix_t>(w * kFix); }
+// w * 2^40 truncated to an integer, for w in [0, 2) with w >= 2^-64 or 0:
+// w = m 2^(E - 150) (m the 24-bit significand, E the biased exponent), so
+// w 2^40 = (m 2^24) >> (134 - E); shifts past 63 leave less than one unit.
+__device__ __forceinline__ fix_t to_fix(float w) {
+  const uint32_t b = __float_as_uint(w);
+  const uint32_t sh = min(134u - (b >> 23), 63u);
+  const fix_t m = static_cast<fix_t>((b & 0x7fffffu) | 0x800000u) << 24;
+  return m >> sh;
+}
 
 struct HistMap {
   float wa, wb, umax, ulo, inv;
+  // bin of u = x wa + wb, for u >= ulo (u <= umax: the row maximum's)
+  __device__ __forceinline__ int bin_of(float u) const {
+    const int j = static_cast<int>((umax - u) * inv);
+    return j < 0 ? 0 : (j < kHistBins ? j : kHistBins - 1);
+  }
   // bin of value x (-1 below the window, NaN and -inf included) and its weight
   __device__ __forceinline__ int bin(float x, float& w) const {
     const float u = fmaf(x, wa, wb);
@@ -585,7 +649,7 @@ struct HistMap {
 
 // In-place inclusive prefix sum of a[0 .. n) (LDS) plus base, all threads.
 template <int NT>
-__device__ void block_scan_fix(fix_t* a, int n, fix_t base, fix_t* wt) {
+__device__ __forceinline__ void block_scan_fix(fix_t* a, int n, fix_t base, fix_t* wt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
@@ -608,8 +672,115 @@ __device__ void block_scan_fix(fix_t* a, int n, fix_t base, fix_t* wt) {
   __syncthreads();
 }
 
-template <int NT, class Row>
-__device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M, float total,
+// Four tokens v0 .. v0+3 of a listed chunk (v0 a multiple of 4, -inf past
+// V): VL rows (V a multiple of 4, aligned) take one vector load, masked as a
+// whole; others the row's checked path.
+template <bool VL, class Row>
+__device__ __forceinline__ void hist_load(const Row& row, int v0, int V, float* x) {
+  if constexpr (VL) {
+    row.load4u(v0, x);
+    const bool in = v0 < V;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = in ? x[e] : neg_inf();
+  } else {
+    row.load4(v0, x);
+  }
+}
+
+// Pass A: the weight of every bin over the listed chunks (wave w takes groups
+// of CU chunks, the group's loads issued together; lane l the tokens 4l ..
+// 4l+3 of each chunk).
+template <int NT, int CU, bool VL, class Row>
+__device__ __forceinline__ void hist_pass_a(const Row& row, int V, const HistMap& hm, const int* cl, int nl,
+                                            fix_t* hw) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
+    float x[CU][4];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = j0 + u;
+      const int cc = j < nl ? uniform_i(cl[j]) : -1;
+      hist_load<VL>(row, cc >= 0 ? cc * kChunk + 4 * lane : V, V, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float uu = fmaf(x[u][e], hm.wa, hm.wb);
+        const int b = hm.bin_of(uu);
+        const fix_t f = to_fix(__builtin_amdgcn_exp2f(uu));
+        if (uu >= hm.ulo) atomicAdd(&hw[b], f);
+      }
+  }
+}
+
+// Appends the lanes' token (value xv, index tok) where take holds to jc's
+// tokens (H.cv / H.ct; H.n counts past the cap).  All lanes call it.
+template <int NT>
+__device__ __forceinline__ void hist_append(bool take, float xv, int tok, HistLds<NT>& H) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t mask = __ballot(take);
+  if (!mask) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&H.n, __popcll(mask));
+  base = __shfl(base, 0, 64);
+  const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+  if (take && slot < kHistCap) {
+    H.cv[slot] = xv;
+    H.ct[slot] = tok;
+  }
+}
+
+// Pass B over the listed chunks reaching the cut's bin jc: jc's tokens into
+// H.cv / H.ct and, with CW, each chunk's weight of tokens before jc added to
+// H.cw (integer LDS atomics: few tokens lie before jc, and the sums do not
+// depend on order).
+template <int NT, int CU, bool VL, bool CW, class Row>
+__device__ __forceinline__ void hist_pass_b(const Row& row, int V, const HistMap& hm, int jc, const float* cm,
+                                            HistLds<NT>& H) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int nl = uniform_i(H.nl);
+  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
+    float x[CU][4];
+    int c[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = j0 + u;
+      int cc = -1;
+      if (j < nl) {
+        cc = uniform_i(H.cl[j]);
+        float w;
+        if (uniform_i(hm.bin(cm[cc], w)) > jc) cc = -1;  // every token of the chunk lies past jc
+      }
+      c[u] = cc;
+      hist_load<VL>(row, cc >= 0 ? cc * kChunk + 4 * lane : V, V, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (c[u] < 0) continue;  // wave-uniform
+      uint32_t at = 0;  // bit e: token 4 lane + e lies in jc
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float uu = fmaf(x[u][e], hm.wa, hm.wb);
+        const bool inw = uu >= hm.ulo;
+        const int b = hm.bin_of(uu);
+        if constexpr (CW) {
+          if (inw && b < jc) atomicAdd(&H.cw[c[u]], to_fix(__builtin_amdgcn_exp2f(uu)));
+        }
+        at |= (inw && b == jc) ? (1u << e) : 0u;
+      }
+      if (__ballot(at != 0)) {  // rare: the chunk holds tokens of jc
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hist_append((at >> e) & 1u, x[u][e], c[u] * kChunk + 4 * lane + e, H);
+      }
+    }
+  }
+}
+
+template <int NT, bool CW, class Row>
+__device__ __forceinline__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M, float total,
                          float wa, float wb, float top_p, HistLds<NT>& H) {
   constexpr int NW = NT / 64, CU = 8, PB = kHistBins / NT;
   static_assert(kHistBins % NT == 0, "bins per thread");
@@ -645,25 +816,9 @@ __device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M,
     if (take) H.cl[base + __popcll(mask & ((1ull << lane) - 1ull))] = c;
   }
   __syncthreads();
-  const int nl = H.nl;
-  // pass A: wave w takes listed chunks in groups of CU, the group's loads
-  // issued together; lane l the tokens 4l .. 4l+3 of each chunk
-  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
-    float x[CU][4];
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const int j = j0 + u;
-      row.load4(j < nl ? H.cl[j] * kChunk + 4 * lane : V, x[u]);  // V: nothing loaded
-    }
-#pragma unroll
-    for (int u = 0; u < CU; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float w;
-        const int b = hm.bin(x[u][e], w);
-        if (b >= 0) atomicAdd(&H.hw[b], to_fix(w));
-      }
-  }
+  const int nl = uniform_i(H.nl);
+  if (row.vec4) hist_pass_a<NT, CU, true>(row, V, hm, H.cl, nl, H.hw);
+  else hist_pass_a<NT, CU, false>(row, V, hm, H.cl, nl, H.hw);
   __syncthreads();
   // the cut's bin: thread t owns bins t*PB .. t*PB+PB-1
   fix_t own = 0;
@@ -690,7 +845,7 @@ __device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M,
     run += h;
   }
   __syncthreads();
-  const int jc = H.jc;
+  const int jc = uniform_i(H.jc);
   if (jc == INT32_MAX) {  // the window holds less than the target
     __syncthreads();
     return false;
@@ -704,57 +859,28 @@ __device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M,
       H.above = r;
     }
   }
-  // pass B over the listed chunks whose maximum reaches jc
-  for (int j0 = wave * CU; j0 < nl; j0 += NW * CU) {
-    float x[CU][4];
-    int c[CU];
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      const int j = j0 + u;
-      float w;
-      c[u] = (j < nl && hm.bin(cm[H.cl[j]], w) <= jc) ? H.cl[j] : -1;
-      row.load4(c[u] >= 0 ? c[u] * kChunk + 4 * lane : V, x[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < CU; ++u) {
-      if (c[u] < 0) continue;  // wave-uniform
-      fix_t a = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float w = 0.0f;
-        const int b = hm.bin(x[u][e], w);
-        if (b >= 0 && b < jc) a += to_fix(w);
-        const bool take = b == jc;
-        const uint64_t mask = __ballot(take);
-        if (mask) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&H.n, __popcll(mask));
-          base = __shfl(base, 0, 64);
-          const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-          if (take && slot < kHistCap) {
-            H.cv[slot] = x[u][e];
-            H.ct[slot] = c[u] * kChunk + 4 * lane + e;
-          }
-        }
-      }
-      a = wave_sum_u64(a);
-      if (lane == 0) H.cw[c[u]] = a;
-    }
-  }
+  __syncthreads();  // H.hw is read above; H.cw is added to below
+  if (row.vec4) hist_pass_b<NT, CU, true, CW>(row, V, hm, jc, cm, H);
+  else hist_pass_b<NT, CU, false, CW>(row, V, hm, jc, cm, H);
   __syncthreads();
   const int n = H.n;
   if (n > kHistCap || n < 1) {
     __syncthreads();
     return false;
   }
-  // the cut inside jc
-  const int n2 = pow2_at_least(n);
-  for (int i = n + tid; i < n2; i += NT) {
-    H.cv[i] = neg_inf();
-    H.ct[i] = INT32_MAX;
+  // the cut inside jc (the bins are no longer needed: sort scratch)
+  if (n <= NT) {
+    rank_sort_desc<NT, true>(H.cv, H.ct, n, reinterpret_cast<float*>(H.hw),
+                             reinterpret_cast<int*>(H.hw) + kHistCap);
+  } else {
+    const int n2 = pow2_at_least(n);
+    for (int i = n + tid; i < n2; i += NT) {
+      H.cv[i] = neg_inf();
+      H.ct[i] = INT32_MAX;
+    }
+    __syncthreads();
+    sort_desc<NT, true>(H.cv, H.ct, n2);
   }
-  __syncthreads();
-  sort_desc<NT, true>(H.cv, H.ct, n2);
   for (int i = tid; i < n; i += NT) H.pw[i] = to_fix(__builtin_amdgcn_exp2f(fmaf(H.cv[i], wa, wb)));
   if (tid == 0) H.cs = 0;  // jc's first group is kept
   __syncthreads();
@@ -769,7 +895,7 @@ __device__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M,
   // to their chunks' weight
   for (int i = tid; i < n; i += NT)
     if (H.cv[i] >= thr) {
-      atomicAdd(&H.cw[H.ct[i] / kChunk], to_fix(__builtin_amdgcn_exp2f(fmaf(H.cv[i], wa, wb))));
+      if constexpr (CW) atomicAdd(&H.cw[H.ct[i] / kChunk], to_fix(__builtin_amdgcn_exp2f(fmaf(H.cv[i], wa, wb))));
       if (i + 1 == n || H.cv[i + 1] < thr) {
         H.thr = thr;
         H.s_kept = static_cast<float>(H.pw[i]) * (1.0f / kFix);

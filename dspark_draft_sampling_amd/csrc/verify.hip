@@ -269,28 +269,39 @@ __global__ __launch_bounds__(kThreads) void verify_rows_kernel(
 // the row pass) by radix selection.
 template <typename T>
 struct LogitRow {
-  const T* p;
+  __amdgpu_buffer_rsrc_t rs;  // over the row (reads past it return 0)
   int V;
   bool vec4;  // 4 consecutive logits per aligned load
-  __device__ float operator()(int v) const { return load_logit(p, v); }
+  __device__ LogitRow(const T* p, int V_, bool vec) : V(V_), vec4(vec) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), static_cast<short>(0),
+                                           V_ * static_cast<int>(sizeof(T)), kBufferWord3);
+  }
+  __device__ float one(int v) const {
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, v * 2, 0, 0)) << 16);
+    else
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, v * 4, 0, 0));
+  }
+  // four logits in one load (v0 a multiple of 4, the row aligned)
+  __device__ void load4u(int v0, float* o) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, v0 * 2, 0, 0));
+      o[0] = bf_lo(u.x);
+      o[1] = bf_hi(u.x);
+      o[2] = bf_lo(u.y);
+      o[3] = bf_hi(u.y);
+    } else {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, v0 * 4, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(u[e]);
+    }
+  }
   __device__ void load4(int v0, float* o) const {
     if (vec4 && v0 + 3 < V) {
-      if constexpr (sizeof(T) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p + v0);
-        o[0] = bf_lo(u.x);
-        o[1] = bf_hi(u.x);
-        o[2] = bf_lo(u.y);
-        o[3] = bf_hi(u.y);
-      } else {
-        const float4 u = *reinterpret_cast<const float4*>(p + v0);
-        o[0] = u.x;
-        o[1] = u.y;
-        o[2] = u.z;
-        o[3] = u.w;
-      }
+      load4u(v0, o);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? load_logit(p, v0 + e) : neg_inf();
+      for (int e = 0; e < 4; ++e) o[e] = v0 + e < V ? one(v0 + e) : neg_inf();
     }
   }
 };
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
   }
   const float total = block_sum<kSelThreads / 64>(s, sh_s);
   const T* rp = target + static_cast<size_t>(row) * V;
-  const LogitRow<T> lr{rp, V, (V % 4 == 0) && reinterpret_cast<uintptr_t>(target) % 16 == 0};
+  const LogitRow<T> lr(rp, V, (V % 4 == 0) && reinterpret_cast<uintptr_t>(target) % 16 == 0);
   const int C = (V + kChunk - 1) / kChunk;
   bool done = false;
   if (have_cmax && C <= kMaxChunksBound) {
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
         done = true;
       }
     }
-    if (!done && tk == 0 && hist_cut(lr, V, cms, C, m, total, cT, -M2, tp, U.h)) {
+    if (!done && tk == 0 && hist_cut<kSelThreads, false>(lr, V, cms, C, m, total, cT, -M2, tp, U.h)) {
       if (threadIdx.x == 0) trunc[row] = RowTrunc{U.h.thr, U.h.s_kept};
       done = true;
     }
