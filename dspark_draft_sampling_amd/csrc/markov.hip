@@ -553,9 +553,6 @@ struct FinLds {
   float sh_m[NW], sh_s[NW], sh_am[NW], sh_v1[NW], sh_v2[NW];
   int32_t sh_ai[NW], sh_i1[NW];
   uint32_t sh_bad[NW];
-  float fin_M, fin_S, fin_zx;
-  int32_t fin_x;
-  uint32_t fin_fl;
   float cm[kMaxChunksBound];  // chunk maxima of the row (truncated rows)
   TruncLds<NT> U;
 };
@@ -648,6 +645,13 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   const float tp = a.pol.top_p[b];
   const int tk_raw = a.pol.top_k[b];
   const bool want_cm = sampled && truncated(tk_raw, tp, V) && C <= kMaxChunksBound;
+  // a sampled row without truncation draws inside its best-scoring chunk:
+  // each wave fetches its own best chunk while the waves' results merge, and
+  // the wave holding the row's best draws from registers
+  const bool spec = sampled && !truncated(tk_raw, tp, V);
+  const QzRow<COH> qr(a.q_z + row * V, V, VEC);
+  Top2 wbest;
+  float zpre[4];
   for (int c = tid; c < C; c += NT) {
     const ChunkPart p = load_part<COH>(pb + c);
     if (want_cm) F.cm[c] = p.m;
@@ -662,6 +666,7 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
     const float ws = wave_sum((m > neg_inf() && wm < pos_inf()) ? s * __builtin_amdgcn_exp2f((m - wm) * kLog2e) : 0.0f);
     const ArgMax wa = wave_argmax(am);
     const Top2 wb = wave_top2(best);
+    wbest = wb;
     const uint32_t wbad = wave_or(bad);
     if (lane == 0) {
       F.sh_m[wave] = wm;
@@ -674,6 +679,7 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
       F.sh_bad[wave] = wbad;
     }
   }
+  if (spec && wbest.i1 != INT32_MAX) qr.load4(wbest.i1 * kChunk + 4 * lane, zpre);
   __syncthreads();
   float M = F.sh_m[0], S = F.sh_s[0];
   ArgMax A{F.sh_am[0], F.sh_ai[0]};
@@ -693,7 +699,6 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   // token's weight and the kept sum round alike (one kept token: q = 1).
   float thr = neg_inf(), s_kept = 0.0f, M2 = 0.0f;
   const bool trunc_row = sampled && truncated(tk_raw, tp, V) && M > neg_inf() && M < pos_inf();
-  const QzRow<COH> qr(a.q_z + row * V, V, VEC);
   if (trunc_row) {
     const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
     M2 = floorf(M * kLog2e);
@@ -705,7 +710,9 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
     Bst = o.best;
   }
 
-  if (wave == 0) {
+  // the drawing wave: the holder of the best chunk's prefetched z, else wave 0
+  const bool pre = spec && Bst.i1 != INT32_MAX && wbest.i1 == Bst.i1;
+  if (spec && Bst.i1 != INT32_MAX ? pre : wave == 0) {
     // 2a. the draw
     int32_t x = 0;
     float zx = neg_inf();
@@ -719,7 +726,12 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
       if (Bst.v2 > neg_inf() && near_gap(Bst.v1, Bst.v2)) near = 1;
       const int v0 = Bst.i1 * kChunk + 4 * lane;
       float z[4];
-      qr.load4(v0, z);
+      if (pre) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = zpre[e];
+      } else {
+        qr.load4(v0, z);
+      }
       // tokens v0..v0+3 share Philox counter (v0 / 4, pos, req, tag)
       uint32_t c0 = static_cast<uint32_t>(v0) >> 2, c1 = static_cast<uint32_t>(pos), c2 = req,
                c3 = DSPARK_TAG_DRAFT_TOKEN;
@@ -744,39 +756,29 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
       }
     }
     if (near) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
+    // the drawing wave writes the row's outputs, x_k first: the next step's
+    // workgroups wait for it
     if (lane == 0) {
-      F.fin_x = x;
-      F.fin_zx = zx;
-      F.fin_M = M;
-      F.fin_S = S;
-      F.fin_fl = fl;
+      if constexpr (COH) store_coherent(a.draft_tokens + row, x);
+      else a.draft_tokens[row] = x;
+      if (!sampled) {
+        a.q_lse[row] = 0.0f;
+        a.q_thr[row] = 0.0f;
+        a.q_tok[row] = 1.0f;
+      } else if (trunc_row) {
+        a.q_lse[row] = M2 * kLn2 + logf(s_kept);
+        a.q_thr[row] = thr;
+        a.q_tok[row] = (zx > neg_inf() && zx >= thr && s_kept > 0.0f)
+                           ? __builtin_amdgcn_exp2f(fmaf(zx, kLog2e, -M2)) / s_kept
+                           : 0.0f;
+      } else {
+        a.q_lse[row] = M + logf(S);
+        a.q_thr[row] = neg_inf();
+        a.q_tok[row] = (zx > neg_inf() && S > 0.0f) ? expf(zx - M) / S : 0.0f;
+      }
+      if (a.pol.mode[b] != 0 && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
+      store_flag<COH>(a.flags + row, static_cast<uint8_t>(fl));
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int32_t x = F.fin_x;
-    if constexpr (COH) store_coherent(a.draft_tokens + row, x);
-    else a.draft_tokens[row] = x;
-    const float zx = F.fin_zx;
-    if (!sampled) {
-      a.q_lse[row] = 0.0f;
-      a.q_thr[row] = 0.0f;
-      a.q_tok[row] = 1.0f;
-    } else if (trunc_row) {
-      a.q_lse[row] = M2 * kLn2 + logf(s_kept);
-      a.q_thr[row] = thr;
-      a.q_tok[row] = (zx > neg_inf() && zx >= thr && s_kept > 0.0f)
-                         ? __builtin_amdgcn_exp2f(fmaf(zx, kLog2e, -M2)) / s_kept
-                         : 0.0f;
-    } else {
-      const float fM = F.fin_M, fS = F.fin_S;
-      a.q_lse[row] = fM + logf(fS);
-      a.q_thr[row] = neg_inf();
-      a.q_tok[row] = (zx > neg_inf() && fS > 0.0f) ? expf(zx - fM) / fS : 0.0f;
-    }
-    uint32_t f = F.fin_fl;
-    if (a.pol.mode[b] != 0 && !sampled) f |= DSPARK_FLAG_BAD_POLICY;
-    store_flag<COH>(a.flags + row, static_cast<uint8_t>(f));
   }
   __syncthreads();  // F is reused by the next request
 }
