@@ -4,7 +4,7 @@ One step is one pass of the whole path over one batch of the decode-verify
 workload (B = 64 requests, gamma = 5, V = 129280, bf16 logits, Markov rank 256,
 confidence width 4096, sampled at temperature 1 without truncation):
   dspark_markov_sample  (gamma Markov steps: bias GEMM + sampling + confidence;
-                        one cooperative launch by default, --markov-plan)
+                        one launch for all steps by default, --markov-plan)
   dspark_verify         (the oracle-free exact sampled verify of those proposals)
   dspark_accept_stats   (analytic acceptance of the same draft / target rows)
 Inputs are synthetic (workloads.py) and resident in HBM before timing starts;
@@ -54,7 +54,7 @@ def parse():
                     default="decode",
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
-    ap.add_argument("--markov-plan", choices=["auto", "per-step"], default="auto",
+    ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative"], default="auto",
                     help="Markov launch plan: one cooperative launch when it fits (auto) or "
                          "two launches per step")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -275,7 +275,8 @@ def main():
 
     import dspark_draft_sampling_amd as ds
 
-    ds.markov_plan(ds.MARKOV_AUTO if args.markov_plan == "auto" else ds.MARKOV_PER_STEP)
+    ds.markov_plan({"auto": ds.MARKOV_AUTO, "per-step": ds.MARKOV_PER_STEP,
+                    "cooperative": ds.MARKOV_COOPERATIVE}[args.markov_plan])
     if args.workload == "stats":
         line = run_stats(args, torch, ds)
     else:

@@ -258,12 +258,12 @@ def profile_enable(on=True):
     lib().dspark_profile_enable(1 if on else 0)
 
 
-MARKOV_AUTO, MARKOV_PER_STEP = 0, 1
+MARKOV_AUTO, MARKOV_PER_STEP, MARKOV_COOPERATIVE = 0, 1, 2
 
 
 def markov_plan(plan):
-    """Set the Markov launch plan (MARKOV_AUTO or MARKOV_PER_STEP, process-wide);
-    returns the previous one."""
+    """Set the Markov launch plan (MARKOV_AUTO, MARKOV_PER_STEP or
+    MARKOV_COOPERATIVE, process-wide); returns the previous one."""
     prev = lib().dspark_markov_plan(int(plan))
     if prev < 0:
         raise DSparkError(f"unknown Markov plan {plan}")

@@ -37,6 +37,7 @@
 //    kernel over all requests), used when the fused grid cannot be resident
 //    at once (V above 512 tokens per compute unit).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -943,23 +944,24 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs 
   }
 }
 
-// Resident workgroups per compute unit of a fused instantiation and the
-// device's compute units (0 if cooperative launch is unavailable), cached per
+// Resident workgroups per compute unit of a fused instantiation, the
+// device's compute units and whether it offers cooperative launch, cached per
 // device: a property of the device and the code object only.
 struct FusedFit {
   int blocks_per_cu;
   int cus;
+  bool coop;
 };
 
 template <typename T, bool VEC>
 FusedFit fused_fit() {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev];  // (blocks << 16 | cus) + 1; 0 = unknown
+  static std::atomic<int> cache[kMaxDev];  // (coop << 30 | blocks << 16 | cus) + 1; 0 = unknown
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FusedFit{0, 0};
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FusedFit{0, 0, false};
   if (dev < kMaxDev) {
     const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c) return FusedFit{(c - 1) >> 16, (c - 1) & 0xffff};
+    if (c) return FusedFit{((c - 1) >> 16) & 0x3fff, (c - 1) & 0xffff, ((c - 1) >> 30) != 0};
   }
   int coop = 0, cus = 0, nb = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
@@ -967,12 +969,35 @@ FusedFit fused_fit() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, markov_fused_kernel<T, VEC>, kFusedThreads,
                                                    0) != hipSuccess)
     nb = 0;
-  FusedFit f{coop ? nb : 0, cus};
-  if (f.blocks_per_cu < 0 || f.blocks_per_cu > 0x7fff || cus < 0 || cus > 0xffff) f = FusedFit{0, 0};
-  if (dev < kMaxDev) cache[dev].store(((f.blocks_per_cu << 16) | f.cus) + 1, std::memory_order_relaxed);
+  FusedFit f{nb, cus, coop != 0};
+  if (f.blocks_per_cu < 0 || f.blocks_per_cu > 0x3fff || cus < 0 || cus > 0xffff) f = FusedFit{0, 0, false};
+  if (dev < kMaxDev)
+    cache[dev].store(((f.coop ? 1 << 30 : 0) | (f.blocks_per_cu << 16) | f.cus) + 1, std::memory_order_relaxed);
   return f;
 }
 
+// Compute units the stream's queue may use (its CU mask), or all of them.
+int stream_cus(hipStream_t st, int cus) {
+  uint32_t mask[32] = {};
+  const int words = (cus + 31) / 32;
+  if (words > 32 || hipExtStreamGetCUMask(st, static_cast<uint32_t>(words), mask) != hipSuccess) return cus;
+  int n = 0;
+  for (int w = 0; w < words; ++w) n += __builtin_popcount(mask[w]);
+  return n > 0 && n < cus ? n : cus;
+}
+
+// An ordinary launch of the fused grid relies on all of it being resident at
+// once, which an occupancy-sized grid is unless another such grid holds part
+// of the device: fused launches on one device are therefore chained, each
+// waiting for the previous one's completion event whatever its stream
+// (not inside a stream capture, where the caller orders the work).
+struct FusedChain {
+  std::mutex mu;
+  hipEvent_t ev[64] = {};
+};
+FusedChain g_chain;
+
+// fused: 0 per-step kernels, 1 one ordinary launch, 2 one cooperative launch
 template <typename T, bool VEC>
 hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
   if (fused) {
@@ -984,13 +1009,42 @@ hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
     MarkovArgs arg = a;
-    void* params[] = {&arg};
-    ProfScope ps("markov_fused");
-    if (ps.active()) (void)hipEventRecord(ps.start(), st);
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>),
-                                   dim3(G), dim3(kFusedThreads), params, 0, st);
-    if (ps.active()) (void)hipEventRecord(ps.stop(), st);
-    if (e != hipSuccess) return e;
+    if (fused == 2) {
+      void* params[] = {&arg};
+      ProfScope ps("markov_fused");
+      if (ps.active()) (void)hipEventRecord(ps.start(), st);
+      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>),
+                                     dim3(G), dim3(kFusedThreads), params, 0, st);
+      if (ps.active()) (void)hipEventRecord(ps.stop(), st);
+      if (e != hipSuccess) return e;
+    } else {
+      int dev = 0;
+      e = hipGetDevice(&dev);
+      if (e != hipSuccess) return e;
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(st, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+      const bool chain = cs == hipStreamCaptureStatusNone && dev >= 0 && dev < 64;
+      std::unique_lock<std::mutex> lk(g_chain.mu, std::defer_lock);
+      if (chain) {
+        lk.lock();
+        hipEvent_t& ev = g_chain.ev[dev];
+        if (!ev) {
+          e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+          if (e != hipSuccess) return e;
+        } else {
+          e = hipStreamWaitEvent(st, ev, 0);
+          if (e != hipSuccess) return e;
+        }
+      }
+      DSPARK_LAUNCH("markov_fused", (markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st,
+                    arg);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (chain) {
+        e = hipEventRecord(g_chain.ev[dev], st);
+        if (e != hipSuccess) return e;
+      }
+    }
   } else {
     const dim3 g_step(a.C, (a.B + kTile - 1) / kTile);
     for (int k = 1; k <= a.gamma; ++k) {
@@ -1013,12 +1067,15 @@ template <typename T, bool VEC>
 hipError_t launch_typed(const MarkovArgs& a, int plan_mode, hipStream_t st) {
   // fused when its grid (one workgroup per 512 tokens) is resident at once
   const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
-  bool fused = false;
-  if (plan_mode != DSPARK_MARKOV_PER_STEP) {
+  int fused = 0;
+  if (plan_mode == DSPARK_MARKOV_AUTO) {
     const FusedFit f = fused_fit<T, VEC>();
-    fused = f.blocks_per_cu > 0 && G <= f.blocks_per_cu * f.cus;
+    if (f.blocks_per_cu > 0 && G <= f.blocks_per_cu * stream_cus(st, f.cus)) fused = 1;
+  } else if (plan_mode == DSPARK_MARKOV_COOPERATIVE) {
+    const FusedFit f = fused_fit<T, VEC>();
+    if (f.coop && f.blocks_per_cu > 0 && G <= f.blocks_per_cu * f.cus) fused = 2;
   }
-  return launch_plan<T, VEC>(a, fused ? 1 : 0, st);
+  return launch_plan<T, VEC>(a, fused, st);
 }
 
 }  // namespace

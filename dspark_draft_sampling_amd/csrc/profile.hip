@@ -60,7 +60,8 @@ ProfScope::~ProfScope() {
 extern "C" {
 
 int dspark_markov_plan(int plan) {
-  if (plan != DSPARK_MARKOV_AUTO && plan != DSPARK_MARKOV_PER_STEP) return -1;
+  if (plan != DSPARK_MARKOV_AUTO && plan != DSPARK_MARKOV_PER_STEP && plan != DSPARK_MARKOV_COOPERATIVE)
+    return -1;
   return dspark::g_markov_plan.exchange(plan);
 }
 

@@ -191,16 +191,26 @@ int dspark_profile_summary(char* buf, size_t n);
 
 /* Launch plan of dspark_markov_sample (process-wide, like the profiler
  * switch; read when a call is enqueued).
- *   DSPARK_MARKOV_AUTO (default): one cooperative launch for all gamma steps
- *     whenever its grid (one workgroup per 512 tokens of the vocabulary) can
- *     be resident at once; each workgroup then keeps its slice of markov_w2
- *     in registers for the whole call.  Otherwise, or if cooperative launch
- *     is unavailable, 2 gamma launches as below.
+ *   DSPARK_MARKOV_AUTO (default): one launch for all gamma steps whenever its
+ *     grid (one workgroup per 512 tokens of the vocabulary) fits the compute
+ *     units the stream may use, resident at once; each workgroup then keeps
+ *     its slice of markov_w2 in registers for the whole call and the steps
+ *     meet at device-wide barriers.  It is an ordinary launch: the library
+ *     chains its own such launches on a device (each waits for the previous
+ *     one's completion event, whatever the stream; not inside a stream
+ *     capture), and residency otherwise relies on no other kernel holding
+ *     compute units indefinitely.  Every barrier wait is bounded: on expiry
+ *     the call ends and flags its rows DSPARK_FLAG_SYNC_TIMEOUT.  Otherwise
+ *     2 gamma launches as below.
  *   DSPARK_MARKOV_PER_STEP: 2 gamma launches (one stream kernel over all
  *     chunks and one finalize kernel over all requests per step).
- * Both plans compute identical results.  Returns the previous plan, or -1
+ *   DSPARK_MARKOV_COOPERATIVE: as AUTO, but through cooperative launch (the
+ *     runtime guarantees residency, at the price of synchronising its
+ *     separate queue with the stream before and after the launch).
+ *     Without cooperative launch, as PER_STEP.
+ * All plans compute identical results.  Returns the previous plan, or -1
  * (leaving it unchanged) for an unknown value. */
-enum { DSPARK_MARKOV_AUTO = 0, DSPARK_MARKOV_PER_STEP = 1 };
+enum { DSPARK_MARKOV_AUTO = 0, DSPARK_MARKOV_PER_STEP = 1, DSPARK_MARKOV_COOPERATIVE = 2 };
 int dspark_markov_plan(int plan);
 
 /* ---------------------------------------------------------------------------

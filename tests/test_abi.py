@@ -120,8 +120,10 @@ def test_binding_refuses_cpu_tensors(L):
 def test_markov_plan_switch(L):
     prev = L.dspark_markov_plan(1)
     try:
-        assert prev in (0, 1)
+        assert prev in (0, 1, 2)
         assert L.dspark_markov_plan(0) == 1
+        assert L.dspark_markov_plan(2) == 0       # cooperative launch
+        assert L.dspark_markov_plan(0) == 2
         assert L.dspark_markov_plan(7) == -1      # unknown: refused, unchanged
         assert L.dspark_markov_plan(0) == 0
     finally:

@@ -245,24 +245,56 @@ def test_stats_paths(N, gamma, V, dtype):
 
 @pytest.mark.parametrize("config", ["decode", "truncated"])
 def test_markov_plans_agree(config, decode_full, truncated_full):
-    """The one-launch plan (W2 resident, grid barriers) and the per-step plan
-    agree at full size: tokens, flags, z and thresholds bit for bit; the
-    log-normalisers up to the order of their fp32 partial sums (the plans
-    combine chunk partials over different workgroup shapes)."""
+    """The one-launch plans (W2 resident, grid barriers; ordinary and
+    cooperative launch) and the per-step plan agree at full size: tokens,
+    flags, z and thresholds bit for bit; the log-normalisers up to the order
+    of their fp32 partial sums (the plans combine chunk partials over
+    different workgroup shapes)."""
     import dspark_draft_sampling_amd as ds
 
     inp = decode_full if config == "decode" else truncated_full
     prev = ds.markov_plan(ds.MARKOV_AUTO)
     try:
         fused = G.markov(inp)
+        ds.markov_plan(ds.MARKOV_COOPERATIVE)
+        coop = G.markov(inp)
         ds.markov_plan(ds.MARKOV_PER_STEP)
         step = G.markov(inp)
     finally:
         ds.markov_plan(prev)
     samp = inp["mode"] != 0
+    for k in ("draft_tokens", "q_thr", "confidence", "flags", "q_lse", "q_tok"):
+        assert np.array_equal(fused[k], coop[k]), k  # the same kernel
     for k in ("draft_tokens", "q_thr", "confidence", "flags"):
         assert np.array_equal(fused[k], step[k]), k
     for k in ("q_lse", "q_tok"):
         assert np.allclose(fused[k], step[k], rtol=1e-6, atol=0), k
     assert np.array_equal(fused["q_logits"][samp], step["q_logits"][samp])
+    assert np.array_equal(fused["q_logits"][samp], coop["q_logits"][samp])
     assert not np.any(fused["flags"] & (1 << 5))  # no barrier gave up
+
+
+def test_markov_concurrent_streams(decode_full):
+    """Two one-launch Markov calls enqueued at once on two streams: the
+    library chains its fused launches on the device, so neither grid waits
+    on compute units the other holds; both end with a lone call's results and
+    no barrier gives up."""
+    import dspark_draft_sampling_amd as ds
+
+    inp = decode_full
+    ref = G.markov(inp)
+    args = (G.logits(inp["backbone"], inp["dtype"]), G.i32(inp["anchor"]), G.bf(inp["w1"]),
+            G.bf(inp["w2"]), G.bf(inp["hidden"]), G.bf(inp["embed"]), G.f32(inp["conf_w"]),
+            G.policy(inp))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        o1 = ds.dspark_markov_sample(*args, seed=inp["seed"])
+    with torch.cuda.stream(s2):
+        o2 = ds.dspark_markov_sample(*args, seed=inp["seed"])
+    torch.cuda.synchronize()
+    for o in (o1, o2):
+        got = {k: v.cpu().numpy() for k, v in o.items()}
+        for k in ("draft_tokens", "q_thr", "confidence", "flags", "q_lse", "q_tok"):
+            assert np.array_equal(got[k], ref[k]), k
+        assert not np.any(got["flags"] & (1 << 5))
