@@ -989,11 +989,13 @@ int stream_cus(hipStream_t st, int cus) {
 // An ordinary launch of the fused grid relies on all of it being resident at
 // once, which an occupancy-sized grid is unless another such grid holds part
 // of the device: fused launches on one device are therefore chained, each
-// waiting for the previous one's completion event whatever its stream
-// (not inside a stream capture, where the caller orders the work).
+// waiting for the previous one's completion event when that one went to
+// another stream (one stream orders its own launches), not inside a stream
+// capture (where the caller orders the work).
 struct FusedChain {
   std::mutex mu;
   hipEvent_t ev[64] = {};
+  hipStream_t last[64] = {};
 };
 FusedChain g_chain;
 
@@ -1029,21 +1031,29 @@ hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
         lk.lock();
         hipEvent_t& ev = g_chain.ev[dev];
         if (!ev) {
-          e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+          e = hipEventCreate(&ev);
           if (e != hipSuccess) return e;
-        } else {
+        } else if (g_chain.last[dev] != st) {
           e = hipStreamWaitEvent(st, ev, 0);
           if (e != hipSuccess) return e;
         }
       }
-      DSPARK_LAUNCH("markov_fused", (markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st,
-                    arg);
+      // the chain's event rides on the kernel's own dispatch (no marker
+      // packet between it and the next kernel of the stream)
+      ProfScope ps("markov_fused");
+      if (ps.active()) {
+        hipExtLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, ps.start(),
+                              ps.stop(), 0, arg);
+        if (chain) (void)hipEventRecord(g_chain.ev[dev], st);
+      } else if (chain) {
+        hipExtLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, nullptr,
+                              g_chain.ev[dev], 0, arg);
+      } else {
+        hipLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, arg);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
-      if (chain) {
-        e = hipEventRecord(g_chain.ev[dev], st);
-        if (e != hipSuccess) return e;
-      }
+      if (chain) g_chain.last[dev] = st;
     }
   } else {
     const dim3 g_step(a.C, (a.B + kTile - 1) / kTile);
