@@ -24,7 +24,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;
-constexpr int kItemMaxWGs = 1024;      // grid of the sliced item kernels
+constexpr int kItemMaxWGs = 2048;      // grid of the sliced item kernels
 constexpr int kSlicedMaxPairs = 2048;  // row pairs below which the sliced path is used
 
 template <typename T, bool VEC>

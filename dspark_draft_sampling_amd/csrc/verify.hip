@@ -40,7 +40,7 @@ constexpr int kVecIters = 4;       // 16-byte loads per lane per segment
 constexpr int kScalarIters = 32;   // scalar loads per lane per segment
 constexpr int kChunksPerWave = 8;  // chunks one wave scores in the decide pass
 constexpr int kChunksPerWG = kChunksPerWave * kWaves;
-constexpr int kRowsMaxWGs = 1024;  // grid of the row pass: 4 waves per SIMD
+constexpr int kRowsMaxWGs = 4096;  // grid of the row pass: up to 16 waves per SIMD
 
 // One 16-byte load per lane per iteration (vector path: 8 bf16 or 4 fp32
 // logits kept packed in a uint4), or one scalar logit (scalar path).  Lanes
