@@ -24,15 +24,16 @@
 // row after the last step.
 //
 // Two launch plans run these phases:
-//  * fused: one cooperative launch for all gamma steps.  Workgroup g owns the
-//    512 tokens [512 g, 512 g + 512) and keeps their W2 rows in registers (the
-//    MFMA A fragments) for the whole call, so the rank-r factor is read from
-//    HBM once per call rather than once per step.  A grid barrier separates
-//    each stream phase from its finalize; the finalize hands x_k to the next
-//    stream phase through draft_tokens (cleared to -1 before the launch).
-//    Everything that crosses workgroups inside the launch (chunk partials, z
-//    rows read by the draw, x_k) is stored and loaded at device scope (sc1),
-//    so no L2 writeback or invalidate is needed.
+//  * fused: one launch for all gamma steps (its whole grid resident at once).
+//    Workgroup g owns the 512 tokens [512 g, 512 g + 512) and keeps their W2
+//    rows in registers (the MFMA A fragments) for the whole call, so the
+//    rank-r factor is read from HBM once per call rather than once per step.
+//    A finalize starts when its request's chunk records of the step are all
+//    stored (polled, no grid barrier) and hands x_k to the next stream phase
+//    through draft_tokens (both cleared before the launch).  Everything that
+//    crosses workgroups inside the launch (chunk records, z rows read by the
+//    draw, x_k) is stored and loaded at device scope (sc1), so no L2
+//    writeback or invalidate is needed.
 //  * per step: 2 gamma launches (stream kernel over all chunks, finalize
 //    kernel over all requests), used when the fused grid cannot be resident
 //    at once (V above 512 tokens per compute unit).
@@ -58,17 +59,12 @@ constexpr int kFusedTokens = kFusedThreads / 64 * 16 * kFusedMS;
 constexpr int kMaxR = DSPARK_MAX_RANK;
 constexpr int kPad = 8;             // bf16 padding per staged W1 row (bank spread)
 constexpr int kFinThreads = 256;    // per-step finalize kernel
-constexpr uint32_t kSpinLimit = 1u << 22;  // grid-barrier polls (~1 us each) before giving up
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls (~1 us each) of one wait before giving up
 
-// Words of the one-launch plan's synchronisation area (each group's counter
-// and release word on its own 256-byte line, then the global counter and the
-// timeout word).
-constexpr int kSyncGroups = 8;
-constexpr int kSyncStride = 64;                                 // words per group line
-constexpr int kSyncRelease = kSyncStride / 2;                   // release word within a line
-constexpr int kSyncGlobal = kSyncGroups * kSyncStride;          // global counter word
-constexpr int kSyncTimeout = kSyncGlobal + kSyncStride;         // timeout word
-constexpr int kSyncWords = kSyncTimeout + kSyncStride;
+// The one-launch plan's synchronisation area: the timeout word, alone on its
+// 256-byte line.
+constexpr int kSyncTimeout = 0;
+constexpr int kSyncWords = 64;
 
 // Everything one Markov call reads and writes.
 struct MarkovArgs {
@@ -90,7 +86,7 @@ struct MarkovArgs {
   float* confidence;
   uint8_t* flags;
   ChunkPart* part;
-  uint32_t* sync;  // fused plan: barrier counters and timeout word (kSyncWords)
+  uint32_t* sync;  // fused plan: timeout word (kSyncWords)
 };
 
 // Four consecutive logits starting at a multiple of 4, kept packed (bf16:
@@ -417,11 +413,17 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
   __syncthreads();
   // one ChunkPart per (request, chunk): the chunk's waves combined
   constexpr int kChunksPerWG = NW / WPC;
-  for (int idx = tid; idx < kChunksPerWG * kTile; idx += NT) {
+  constexpr int kRecPerThread = (kChunksPerWG * kTile + NT - 1) / NT;
+  ChunkPart rec[kRecPerThread];
+  ChunkPart* dst[kRecPerThread];
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j) {
+    dst[j] = nullptr;
+    const int idx = tid + j * NT;
     const int h = idx / kTile, n = idx - h * kTile;
     const int c = tok0 / kChunk + h;
     const int b = b0 + n;
-    if (c >= a.C || b >= B) continue;
+    if (idx >= kChunksPerWG * kTile || c >= a.C || b >= B) continue;
     const int w0 = h * WPC;
     float m = L.red_m[w0][n], s = L.red_s[w0][n];
     ArgMax am{L.red_m[w0][n], L.red_i[w0][n]};
@@ -438,10 +440,18 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
     if (a.pol.mode[b] != 0 && !bad_temperature(Tb) && m > neg_inf() && m < pos_inf() && s > 0.0f)
       score = m + logf(s) + gumbel(a.seed, static_cast<uint32_t>(c), a.pol.position[b] + k,
                                    a.pol.request_id[b], DSPARK_TAG_DRAFT_CHUNK);
-    store_part<COH>(a.part + static_cast<size_t>(b) * a.C + c,
-                    ChunkPart{m, s, score,
-                              (static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)});
+    rec[j] = ChunkPart{m, s, score, (static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)};
+    dst[j] = a.part + (static_cast<size_t>(k - 1) * B + b) * a.C + c;
   }
+  if constexpr (COH) {
+    // a record, once visible, vouches for every z of the step this
+    // workgroup stored: all waves' stores complete before any record is
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < kRecPerThread; ++j)
+    if (dst[j]) store_part<COH>(dst[j], rec[j]);
   __syncthreads();  // the LDS tile is reused by the next call
 }
 
@@ -636,7 +646,7 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   const bool sampled = a.pol.mode[b] != 0 && !bad_temperature(Tb);
   const uint32_t req = a.pol.request_id[b];
   const int32_t pos = a.pol.position[b] + k;
-  const ChunkPart* pb = a.part + static_cast<size_t>(b) * C;
+  const ChunkPart* pb = a.part + (static_cast<size_t>(k - 1) * a.B + b) * C;
 
   // 1. combine the chunk partials
   float m = neg_inf(), s = 0.0f;
@@ -654,7 +664,20 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   Top2 wbest;
   float zpre[4];
   for (int c = tid; c < C; c += NT) {
-    const ChunkPart p = load_part<COH>(pb + c);
+    ChunkPart p = load_part<COH>(pb + c);
+    if constexpr (COH) {
+      // the fused plan's records start as s = -1 (a stored s is >= 0 or NaN)
+      uint32_t polls = 0;
+      while (p.s < 0.0f) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++polls > kSpinLimit) {
+          __hip_atomic_store(a.sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          p = ChunkPart{neg_inf(), 0.0f, neg_inf(), 0x7fffffffu};
+          break;
+        }
+        p = load_part<COH>(pb + c);
+      }
+    }
     if (want_cm) F.cm[c] = p.m;
     const int32_t arg = static_cast<int32_t>(p.arg_nf & 0x7fffffffu);
     bad |= p.arg_nf >> 31;
@@ -862,57 +885,28 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(MarkovArgs
   finalize_request<kFinThreads, VEC, false>(a, blockIdx.x, k, F);
 }
 
-// Grid-wide barrier of the fused launch (every workgroup resident).  Arrival
-// is two-level, because device-scope atomics on one address serialise (tens
-// of ns each): workgroup g counts on group counter g mod 8 (each group on its
-// own 256-byte line), and the last arrival of each group counts on the global
-// counter.  Only those group leaders poll the global counter; each then
-// releases its group by storing the barrier number on the group's line, which
-// the other members poll (polling spread over the groups' lines, with a
-// pause between polls, keeps any one memory channel lightly loaded).
-// Counters only grow; the reset kernel clears them before each launch.  Each
-// wave first drains its own memory operations, so everything stored before
-// the barrier (device-scope) is visible after it.  A poll limit bounds every
-// wait; on expiry the timeout word is set and the launch runs on to its end
-// (its rows are then flagged).
+// One-launch plan.  Every workgroup streams its vocabulary slice for every
+// request and step; workgroup g also finalizes requests g, g + G, ...  The
+// steps meet through the data itself, without a grid-wide barrier:
+//  * each step's chunk records have their own slice of the workspace, reset
+//    to s = -1 before the launch; a workgroup stores its records of step k
+//    only after all of its waves' stores of step k completed, so a record
+//    that is visible vouches for the z values behind it, and a finalizer
+//    polls its request's records until none is -1;
+//  * x_k reaches the next step's stream phase through draft_tokens (-1
+//    until its finalizer stores it).
+// A poll limit bounds every wait; on expiry the timeout word is set and the
+// launch runs on to its end (its rows are then flagged).
 
-__device__ __forceinline__ bool poll_until(uint32_t* w, uint32_t target, uint32_t* timeout) {
-  uint32_t polls = 0;
-  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++polls > kSpinLimit) {
-      __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-  }
-  return true;
-}
-
-__device__ __forceinline__ void grid_sync(uint32_t* sync, uint32_t gen) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t G = gridDim.x, g = blockIdx.x, j = g % kSyncGroups;
-    const uint32_t size_j = (G - j + kSyncGroups - 1) / kSyncGroups;
-    const uint32_t groups = G < static_cast<uint32_t>(kSyncGroups) ? G : kSyncGroups;
-    uint32_t* line = sync + j * kSyncStride;
-    const uint32_t old = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gen * size_j - 1u) {  // last of its group: the group's leader
-      __hip_atomic_fetch_add(sync + kSyncGlobal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      poll_until(sync + kSyncGlobal, gen * groups, sync + kSyncTimeout);
-      __hip_atomic_store(line + kSyncRelease, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      poll_until(line + kSyncRelease, gen, sync + kSyncTimeout);
-    }
-  }
-  __syncthreads();
-}
-
-// Clears the barrier words and marks every draft token as not yet drawn.
-__global__ void markov_sync_reset_kernel(uint32_t* sync, int32_t* draft_tokens, int32_t n) {
-  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
-  for (int i = i0; i < kSyncWords; i += step) sync[i] = 0u;
-  for (int i = i0; i < n; i += step) draft_tokens[i] = -1;
+// Clears the timeout word, marks every draft token as not yet drawn and every
+// chunk record (nrec of them) as not yet stored.
+__global__ void markov_sync_reset_kernel(uint32_t* sync, int32_t* draft_tokens, size_t n, ChunkPart* part,
+                                         size_t nrec) {
+  const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t step = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = i0; i < kSyncWords; i += step) sync[i] = 0u;
+  for (size_t i = i0; i < n; i += step) draft_tokens[i] = -1;
+  for (size_t i = i0; i < nrec; i += step) part[i] = ChunkPart{neg_inf(), -1.0f, neg_inf(), 0x7fffffffu};
 }
 
 template <typename T, bool VEC>
@@ -924,16 +918,12 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs 
   const int tok0 = g * kFusedTokens;
   bf16x8 af[kFusedMS][kMaxR / 32];  // resident for the whole call
   load_w2<kFusedMS>(af, a.w2, tok0 + wave * 16 * kFusedMS, a.V, a.r, lane);
-  uint32_t gen = 0;
   for (int k = 1; k <= a.gamma; ++k) {
     for (int b0 = 0; b0 < a.B; b0 += kTile)
       stream_tile<T, VEC, kFusedThreads, kFusedMS, 4, true>(a, af, tok0, b0, k, SL);
-    grid_sync(a.sync, ++gen);
-    // x_k reaches the next step's stream phase through draft_tokens itself
-    // (-1 until stored), so no second barrier is needed
     for (int b = g; b < a.B; b += G) finalize_request<kFusedThreads, VEC, true>(a, b, k, FL);
   }
-  // after a barrier timeout, mark the rows this workgroup finalized
+  // after a timed-out wait, mark the rows this workgroup finalized
   if (threadIdx.x == 0 &&
       __hip_atomic_load(a.sync + kSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
     for (int b = g; b < a.B; b += G)
@@ -1003,10 +993,12 @@ FusedChain g_chain;
 template <typename T, bool VEC>
 hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
   if (fused) {
-    const int ntok = a.B * a.gamma;
+    const size_t ntok = static_cast<size_t>(a.B) * a.gamma;
+    const size_t nrec = ntok * static_cast<size_t>(a.C);
+    const size_t most = std::max({ntok, nrec, static_cast<size_t>(kSyncWords)});
     DSPARK_LAUNCH("markov_sync_reset", markov_sync_reset_kernel,
-                  dim3(std::min(64, (std::max(ntok, kSyncWords) + 255) / 256)), dim3(256), 0, st,
-                  a.sync, a.draft_tokens, ntok);
+                  dim3(static_cast<unsigned>(std::min<size_t>(1024, (most + 255) / 256))), dim3(256), 0, st,
+                  a.sync, a.draft_tokens, ntok, a.part, nrec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
@@ -1091,13 +1083,12 @@ hipError_t launch_typed(const MarkovArgs& a, int plan_mode, hipStream_t st) {
 }  // namespace
 
 MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d) {
-  (void)gamma;
   (void)r;
   (void)d;
   MarkovPlan p{};
   p.C = (V + kChunk - 1) / kChunk;
-  p.off_part = 0;
-  size_t off = align_up(static_cast<size_t>(B) * p.C * sizeof(ChunkPart), 256);
+  p.off_part = 0;  // one slice of B x C records per step
+  size_t off = align_up(static_cast<size_t>(gamma) * B * p.C * sizeof(ChunkPart), 256);
   p.off_sync = off;
   off += align_up(kSyncWords * sizeof(uint32_t), 256);
   p.bytes = off;
