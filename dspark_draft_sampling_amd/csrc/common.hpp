@@ -170,6 +170,41 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   return r;
 }
 
+// ArgMax over the four 16-lane rows (see rows_combine).
+__device__ __forceinline__ ArgMax rows_argmax(ArgMax a) {
+  const auto v1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+  const auto i1 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(a.i), static_cast<uint32_t>(a.i), false, false);
+  a = better(ArgMax{__uint_as_float(v1[0]), static_cast<int32_t>(i1[0])},
+             ArgMax{__uint_as_float(v1[1]), static_cast<int32_t>(i1[1])});
+  const auto v2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+  const auto i2 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(a.i), static_cast<uint32_t>(a.i), false, false);
+  return better(ArgMax{__uint_as_float(v2[0]), static_cast<int32_t>(i2[0])},
+                ArgMax{__uint_as_float(v2[1]), static_cast<int32_t>(i2[1])});
+}
+
+// ---- reductions over the four 16-lane rows of a wave -------------------------
+// Lanes l, l^16, l^32, l^48 combined in registers with the gfx950 lane swaps
+// (v_permlane16_swap: rows 1 and 3 of the first operand trade places with
+// rows 0 and 2 of the second; v_permlane32_swap: the upper half of the first
+// with the lower half of the second).  Swapping a value with itself leaves a
+// lane holding its own value and its partner row's (or half's) in the two
+// results, so op(r0, r1) is the pairwise combination on every lane.
+template <class Op>
+__device__ __forceinline__ uint32_t rows_combine(uint32_t x, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  return __uint_as_float(rows_combine(__float_as_uint(v), [](uint32_t p, uint32_t q) {
+    return __float_as_uint(__uint_as_float(p) + __uint_as_float(q));
+  }));
+}
+__device__ __forceinline__ uint32_t rows_or(uint32_t v) {
+  return rows_combine(v, [](uint32_t p, uint32_t q) { return p | q; });
+}
+
 // Top-2 scores with the argmax: (best, index, second best).
 struct Top2 {
   float v1;

@@ -384,14 +384,11 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       zsum += z[e];
     }
     int32_t arg = ej < 0 ? INT32_MAX : vb + (ej >> 2) * 16 + 4 * (lane >> 4) + (ej & 3);
-    uint32_t bad = (zsum != zsum || m == pos_inf()) ? 1u : 0u;
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-      const ArgMax other{__shfl_xor(m, o, 64), __shfl_xor(arg, o, 64)};
-      const ArgMax am = better(ArgMax{m, arg}, other);
+    const uint32_t bad = rows_or((zsum != zsum || m == pos_inf()) ? 1u : 0u);
+    {
+      const ArgMax am = rows_argmax(ArgMax{m, arg});
       m = am.v;
       arg = am.i;
-      bad |= __shfl_xor(bad, o, 64);
     }
     // sum of 2^(z log2e - m log2e) relative to the 4 lanes' maximum
     float s = 0.0f;
@@ -400,8 +397,7 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
 #pragma unroll
       for (int e = 0; e < 4 * MS; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[e], kLog2e, -mb));
     }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+    s = rows_sum(s);
     if (lane < 16) {
       L.red_m[wave][n] = m;
       L.red_s[wave][n] = s;
