@@ -230,8 +230,8 @@ template <int NT>
 struct CandLds {
   int ci[kMaxChunksBound];  // chunks whose maximum reaches tau (any order)
   float cv[kCandCap];       // candidate values, sorted descending
-  float pw[kCandCap];       // running weight sums (inclusive)
-  float wtot[NT / 64];
+  float tmp[kCandCap];      // sort scratch
+  unsigned long long wt[NT / 64];
   uint32_t key;  // order key of tau (0: no bound)
   int n;         // candidates gathered (> kCandCap: overflow)
   int nchunks;   // chunks whose maximum reaches tau
@@ -250,6 +250,17 @@ struct CandLds {
 // of order.
 using fix_t = unsigned long long;
 constexpr float kFix = 1099511627776.0f;  // 2^40
+
+// w * 2^40 truncated to an integer, for w in [0, 2) with w >= 2^-64 or 0:
+// w = m 2^(E - 150) (m the 24-bit significand, E the biased exponent), so
+// w 2^40 = (m 2^24) >> (134 - E); shifts past 63 leave less than one unit.
+__device__ __forceinline__ fix_t to_fix(float w) {
+  const uint32_t b = __float_as_uint(w);
+  const uint32_t sh = min(134u - (b >> 23), 63u);
+  const fix_t m = static_cast<fix_t>((b & 0x7fffffu) | 0x800000u) << 24;
+  return m >> sh;
+}
+
 constexpr int kHistBins = 2048;
 constexpr int kHistCap = 512;  // tokens of the cut's bin range held in LDS
 
@@ -376,31 +387,6 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   int p = 1;
   while (p < n) p <<= 1;
   return p;
-}
-
-// In-place inclusive prefix sum of a[0 .. n) (LDS), all threads.
-template <int NT>
-__device__ __forceinline__ void block_scan_incl(float* a, int n, float* wtot) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + NT - 1) / NT;
-  const int lo = tid * per, hi = min(n, lo + per);
-  float s = 0.0f;
-  for (int i = lo; i < hi; ++i) s += a[i];
-  float x = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wtot[wave] = x;
-  __syncthreads();
-  float run = x - s;
-  for (int w = 0; w < wave; ++w) run += wtot[w];
-  for (int i = lo; i < hi; ++i) {
-    run += a[i];
-    a[i] = run;
-  }
-  __syncthreads();
 }
 
 // Number of v[0 .. n) that are >= t (v sorted descending), all threads.
@@ -535,12 +521,53 @@ __device__ __forceinline__ void gather_candidates(const Row& row, int V, CandLds
   __syncthreads();
 }
 
+// Sum of one fixed-point value per thread over the workgroup (all threads).
+template <int NT>
+__device__ __forceinline__ fix_t block_sum_fix(fix_t v, fix_t* wt) {
+  v = wave_sum_u64(v);
+  if ((threadIdx.x & 63) == 0) wt[threadIdx.x >> 6] = v;
+  __syncthreads();
+  fix_t all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) all += wt[w];
+  __syncthreads();
+  return all;
+}
+
+// Exclusive prefix of one fixed-point value per thread in thread order, and
+// the total (all threads).
+template <int NT>
+__device__ __forceinline__ fix_t block_excl_scan_fix(fix_t own, fix_t* wt, fix_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  fix_t x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const fix_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wt[wave] = x;
+  __syncthreads();
+  fix_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const fix_t t = wt[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + x - own;
+}
+
 // Exact cut on the gathered candidates: sorts them, applies top-k (ties
 // kept) and then top-p on the renormalised set (the first value group always
 // kept, a later group kept iff the weight strictly above it is below top_p of
-// the set's weight).  total: the row's total weight (the set's weight when
-// top-k is off).  Sets L.thr (smallest kept value), L.s_kept (kept weight),
-// L.nkept and L.ok (0: the cut is not decided by the candidates).
+// the set's weight).  Weights are summed in 2^-40 fixed point (exact, in any
+// order): thread t owns a contiguous stretch of the sorted candidates and the
+// running weight at each of them is its stretch's prefix plus the weight of
+// the stretches before.  total: the row's total weight (the set's weight
+// when top-k is off).  Sets L.thr (smallest kept value), L.s_kept (kept
+// weight), L.nkept and L.ok (0: the cut is not decided by the candidates).
 template <int NT>
 __device__ __forceinline__ void exact_cut(int top_k, float top_p, float wa, float wb, float total, CandLds<NT>& L) {
   const int n = L.n;
@@ -551,44 +578,59 @@ __device__ __forceinline__ void exact_cut(int top_k, float top_p, float wa, floa
     return;
   }
   if (n <= NT) {
-    rank_sort_desc<NT, false>(L.cv, nullptr, n, L.pw, nullptr);
+    rank_sort_desc<NT, false>(L.cv, nullptr, n, L.tmp, nullptr);
   } else {
     const int n2 = pow2_at_least(n);
     for (int i = n + static_cast<int>(threadIdx.x); i < n2; i += NT) L.cv[i] = neg_inf();
     __syncthreads();
     sort_desc<NT, false>(L.cv, nullptr, n2);
   }
-  for (int i = threadIdx.x; i < n; i += NT)
-    L.pw[i] = __builtin_amdgcn_exp2f(fmaf(L.cv[i], wa, wb));
-  __syncthreads();
-  block_scan_incl<NT>(L.pw, n, L.wtot);
+  const int tid = threadIdx.x;
+  const int per = (n + NT - 1) / NT, lo = min(n, tid * per), hi = min(n, lo + per);
+  auto wfix = [&](int i) { return to_fix(__builtin_amdgcn_exp2f(fmaf(L.cv[i], wa, wb))); };
+  // weight of this thread's share of the first m candidates
+  auto share = [&](int m) {
+    fix_t v = 0;
+    for (int i = lo; i < hi && i < m; ++i) v += wfix(i);
+    return v;
+  };
+  fix_t own = share(n), all;
+  const fix_t before = block_excl_scan_fix<NT>(own, L.wt, all);
   int nk = n;
-  float set_total = total;
+  fix_t set_w = 0;
   if (top_k > 0) {
     nk = count_at_least<NT>(L.cv, n, L.cv[top_k - 1], L.cnt);
-    set_total = L.pw[nk - 1];
+    set_w = block_sum_fix<NT>(share(nk), L.wt);
   }
   int cut = nk;
+  bool ok = true;
   if (top_p < 1.0f) {
-    const float target = (top_p > 0.0f ? top_p : 0.0f) * set_total;
-    if (threadIdx.x == 0) L.idx = 0;
+    // a group is kept iff the weight above it is < p * (set weight): for
+    // the integer sums, iff it is < T = ceil(p * set weight)
+    const double p = top_p > 0.0f ? static_cast<double>(top_p) : 0.0;
+    const double set_d = top_k > 0 ? static_cast<double>(set_w) : static_cast<double>(total) * static_cast<double>(kFix);
+    const fix_t T = static_cast<fix_t>(ceil(p * set_d));
+    if (tid == 0) L.idx = 0;
     __syncthreads();
-    // the last group start whose strictly-larger weight is below target
+    // the last group start whose strictly-larger weight is below T
     int best = 0;
-    for (int i = threadIdx.x; i < nk; i += NT)
-      if (i > 0 && L.cv[i] != L.cv[i - 1] && L.pw[i - 1] < target) best = i;
+    fix_t run = before;
+    for (int i = lo; i < hi; ++i) {
+      if (i > 0 && i < nk && L.cv[i] != L.cv[i - 1] && run < T) best = i;
+      run += wfix(i);
+    }
     if (best > 0) atomicMax(&L.idx, best);
     __syncthreads();
     cut = count_at_least<NT>(L.cv, nk, L.cv[L.idx], L.cnt);
+    // top-p alone: the candidates must carry the target, else the cut may
+    // lie below tau
+    if (top_k <= 0) ok = all >= T;
   }
-  if (threadIdx.x == 0) {
+  const fix_t kept = block_sum_fix<NT>(share(cut), L.wt);
+  if (tid == 0) {
     L.nkept = cut;
     L.thr = L.cv[cut - 1];
-    L.s_kept = L.pw[cut - 1];
-    // with top-k the set is all candidates' business; top-p alone needs the
-    // candidates to carry the target weight, else the cut may lie below tau
-    bool ok = true;
-    if (top_k <= 0 && top_p < 1.0f) ok = L.pw[n - 1] >= (top_p > 0.0f ? top_p : 0.0f) * total;
+    L.s_kept = static_cast<float>(kept) * (1.0f / kFix);
     L.ok = ok ? 1 : 0;
   }
   __syncthreads();
@@ -620,16 +662,6 @@ __device__ __forceinline__ void exact_cut(int top_k, float top_p, float wa, floa
 // kept weight (fixed point) for the chunks H.cl[0 .. H.nl) (the others hold
 // no kept token).  Returns false when jc's tokens overflow LDS or the window
 // does not reach the target (then nothing is decided).
-// w * 2^40 truncated to an integer, for w in [0, 2) with w >= 2^-64 or 0:
-// w = m 2^(E - 150) (m the 24-bit significand, E the biased exponent), so
-// w 2^40 = (m 2^24) >> (134 - E); shifts past 63 leave less than one unit.
-__device__ __forceinline__ fix_t to_fix(float w) {
-  const uint32_t b = __float_as_uint(w);
-  const uint32_t sh = min(134u - (b >> 23), 63u);
-  const fix_t m = static_cast<fix_t>((b & 0x7fffffu) | 0x800000u) << 24;
-  return m >> sh;
-}
-
 struct HistMap {
   float wa, wb, umax, ulo, inv;
   // bin of u = x wa + wb, for u >= ulo (u <= umax: the row maximum's)
