@@ -130,11 +130,12 @@ enum {
   DSPARK_FLAG_EMPTY_ROW = 1u << 3,      /* no logit above -inf in the row    */
   DSPARK_FLAG_BAD_POLICY = 1u << 4,     /* sampled row with temperature <= 0
                                            or non-finite: treated as greedy  */
-  DSPARK_FLAG_SYNC_TIMEOUT = 1u << 5    /* dspark_markov_sample only: a
-                                           device-wide barrier of the one-launch
-                                           plan gave up waiting (other work held
-                                           the device's compute units); every
-                                           output of the call is unspecified  */
+  DSPARK_FLAG_SYNC_TIMEOUT = 1u << 5    /* dspark_markov_sample only: a wait
+                                           of the one-launch plan for another
+                                           workgroup's data gave up (other work
+                                           held the device's compute units);
+                                           every output of the call is
+                                           unspecified                        */
 };
 
 /* ---- Philox stream tags --------------------------------------------------- */
@@ -194,12 +195,13 @@ int dspark_profile_summary(char* buf, size_t n);
  *   DSPARK_MARKOV_AUTO (default): one launch for all gamma steps whenever its
  *     grid (one workgroup per 512 tokens of the vocabulary) fits the compute
  *     units the stream may use, resident at once; each workgroup then keeps
- *     its slice of markov_w2 in registers for the whole call and the steps
- *     meet at device-wide barriers.  It is an ordinary launch: the library
+ *     its slice of markov_w2 in registers for the whole call, and the steps
+ *     hand their results to one another through the workspace (polled, no
+ *     device-wide barrier).  It is an ordinary launch: the library
  *     chains its own such launches on a device (each waits for the previous
  *     one's completion event, whatever the stream; not inside a stream
  *     capture), and residency otherwise relies on no other kernel holding
- *     compute units indefinitely.  Every barrier wait is bounded: on expiry
+ *     compute units indefinitely.  Every such wait is bounded: on expiry
  *     the call ends and flags its rows DSPARK_FLAG_SYNC_TIMEOUT.  Otherwise
  *     2 gamma launches as below.
  *   DSPARK_MARKOV_PER_STEP: 2 gamma launches (one stream kernel over all

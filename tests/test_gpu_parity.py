@@ -245,11 +245,11 @@ def test_stats_paths(N, gamma, V, dtype):
 
 @pytest.mark.parametrize("config", ["decode", "truncated"])
 def test_markov_plans_agree(config, decode_full, truncated_full):
-    """The one-launch plans (W2 resident, grid barriers; ordinary and
-    cooperative launch) and the per-step plan agree at full size: tokens,
-    flags, z and thresholds bit for bit; the log-normalisers up to the order
-    of their fp32 partial sums (the plans combine chunk partials over
-    different workgroup shapes)."""
+    """The one-launch plans (W2 resident, steps handed off through polled
+    records; ordinary and cooperative launch) and the per-step plan agree at
+    full size: tokens, flags, z and thresholds bit for bit; the
+    log-normalisers up to the order of their fp32 partial sums (the plans
+    combine chunk partials over different workgroup shapes)."""
     import dspark_draft_sampling_amd as ds
 
     inp = decode_full if config == "decode" else truncated_full
@@ -271,14 +271,14 @@ def test_markov_plans_agree(config, decode_full, truncated_full):
         assert np.allclose(fused[k], step[k], rtol=1e-6, atol=0), k
     assert np.array_equal(fused["q_logits"][samp], step["q_logits"][samp])
     assert np.array_equal(fused["q_logits"][samp], coop["q_logits"][samp])
-    assert not np.any(fused["flags"] & (1 << 5))  # no barrier gave up
+    assert not np.any(fused["flags"] & (1 << 5))  # no wait gave up
 
 
 def test_markov_concurrent_streams(decode_full):
     """Two one-launch Markov calls enqueued at once on two streams: the
     library chains its fused launches on the device, so neither grid waits
     on compute units the other holds; both end with a lone call's results and
-    no barrier gives up."""
+    no wait gives up."""
     import dspark_draft_sampling_amd as ds
 
     inp = decode_full
