@@ -22,7 +22,7 @@
 
 namespace dspark {
 
-constexpr int kSelThreads = 256;  // workgroup size of the verify select
+constexpr int kSelThreads = 512;  // workgroup size of the verify select
 constexpr int kSelBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -483,15 +483,32 @@ __device__ __forceinline__ bool chunk_bound(const float* cm, int C, int top_k, f
   return true;
 }
 
-// Gather every token >= tau of the chunks L.ci[0 .. L.nchunks) (wave w takes
-// groups of four chunks, the group's loads issued together; lane l the 4
-// tokens 4l..4l+3 of each chunk).  Sets L.n (possibly above kCandCap:
-// overflow, nothing beyond the cap is stored).
-template <int NT, class Row>
-__device__ __forceinline__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
+// Four tokens v0 .. v0+3 of a listed chunk (v0 a multiple of 4, -inf past
+// V): VL rows (V a multiple of 4, aligned) take one vector load, masked as a
+// whole; others the row's checked path.
+template <bool VL, class Row>
+__device__ __forceinline__ void hist_load(const Row& row, int v0, int V, float* x) {
+  if constexpr (VL) {
+    row.load4u(v0, x);
+    const bool in = v0 < V;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = in ? x[e] : neg_inf();
+  } else {
+    row.load4(v0, x);
+  }
+}
+
+// Gather every token >= tau of the chunks L.ci[0 .. L.nchunks): wave w
+// takes groups of CU chunks, the group's loads issued together (lane l the
+// tokens 4l .. 4l+3 of each chunk); one LDS atomic reserves the group's
+// slots, and each token's slot follows from the ballots before it.  Sets
+// L.n (possibly above kCandCap: overflow, nothing beyond the cap is stored).
+template <int NT, bool VL, class Row>
+__device__ __forceinline__ void gather_group(const Row& row, int V, CandLds<NT>& L) {
   constexpr int NW = NT / 64;
-  constexpr int CU = 4;  // chunks whose loads a wave issues together
+  constexpr int CU = 8;
   const int lane = threadIdx.x & 63, wave = wave_id();
+  const uint64_t below = (1ull << lane) - 1ull;
   const float tau = L.tau;
   const int nch = uniform_i(L.nchunks);
   for (int j0 = wave * CU; j0 < nch; j0 += NW * CU) {
@@ -501,23 +518,34 @@ __device__ __forceinline__ void gather_candidates(const Row& row, int V, CandLds
     for (int u = 0; u < CU; ++u) {
       const int j = j0 + u;
       v0[u] = j < nch ? uniform_i(L.ci[j]) * kChunk + lane * 4 : V;  // V: nothing to load
-      row.load4(v0[u], x[u]);
+      hist_load<VL>(row, v0[u], V, x[u]);
     }
+    int total = 0;
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) total += __popcll(__ballot(x[u][e] >= tau));
+    if (total == 0) continue;  // wave-uniform
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&L.n, total);
+    base = uniform_i(base);
 #pragma unroll
     for (int u = 0; u < CU; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool take = v0[u] + e < V && x[u][e] >= tau;
-        const uint64_t mask = __ballot(take);
-        int base = 0;
-        if (lane == 0 && mask) base = atomicAdd(&L.n, __popcll(mask));
-        base = __shfl(base, 0, 64);
-        if (take) {
-          const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-          if (slot < kCandCap) L.cv[slot] = x[u][e];
-        }
+        const bool take = x[u][e] >= tau;  // -inf past V never passes
+        const uint64_t m = __ballot(take);
+        const int slot = base + __popcll(m & below);
+        if (take && slot < kCandCap) L.cv[slot] = x[u][e];
+        base += __popcll(m);
       }
   }
+}
+
+template <int NT, class Row>
+__device__ __forceinline__ void gather_candidates(const Row& row, int V, CandLds<NT>& L) {
+  if (row.vec4) gather_group<NT, true>(row, V, L);
+  else gather_group<NT, false>(row, V, L);
   __syncthreads();
 }
 
@@ -702,21 +730,6 @@ __device__ __forceinline__ void block_scan_fix(fix_t* a, int n, fix_t base, fix_
     a[i] = run;
   }
   __syncthreads();
-}
-
-// Four tokens v0 .. v0+3 of a listed chunk (v0 a multiple of 4, -inf past
-// V): VL rows (V a multiple of 4, aligned) take one vector load, masked as a
-// whole; others the row's checked path.
-template <bool VL, class Row>
-__device__ __forceinline__ void hist_load(const Row& row, int v0, int V, float* x) {
-  if constexpr (VL) {
-    row.load4u(v0, x);
-    const bool in = v0 < V;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = in ? x[e] : neg_inf();
-  } else {
-    row.load4(v0, x);
-  }
 }
 
 // Pass A: the weight of every bin over the listed chunks (wave w takes groups

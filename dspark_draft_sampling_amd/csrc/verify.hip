@@ -306,6 +306,67 @@ struct LogitRow {
   }
 };
 
+// Workgroup w of the select grid takes the w-th row of an order that starts
+// the slowest cuts first: the rows of sampled requests with top-p alone (a
+// spread row takes the weight histogram), then of sampled requests with
+// top-k, then the rest (which return at once); requests keep their order
+// within a class.  All threads call it; returns the row.
+template <int NT>
+__device__ __forceinline__ int slow_first_row(int w, int B, int G1, int V, const uint8_t* __restrict__ mode,
+                                              const float* __restrict__ temperature,
+                                              const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
+                                              int* sh) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto cls = [&](int b) {
+    if (mode[b] == 0 || bad_temperature(temperature[b])) return 2;
+    const int tk = top_k[b];
+    if (!truncated(tk, top_p[b], V)) return 2;
+    return (tk > 0 && tk < V) ? 1 : 0;
+  };
+  const int per = (B + NT - 1) / NT, lo = min(B, tid * per), hi = min(B, lo + per);
+  int cnt[3] = {0, 0, 0};
+  for (int b = lo; b < hi; ++b) ++cnt[cls(b)];
+  // class totals
+  int n0 = wave_sum_i(cnt[0]), n1 = wave_sum_i(cnt[1]);
+  if (lane == 0) {
+    sh[wave] = n0;
+    sh[NW + wave] = n1;
+  }
+  __syncthreads();
+  n0 = 0;
+  n1 = 0;
+  for (int i = 0; i < NW; ++i) {
+    n0 += sh[i];
+    n1 += sh[NW + i];
+  }
+  __syncthreads();
+  const int r = w / G1, k = w - r * G1;
+  const int c = r < n0 ? 0 : (r < n0 + n1 ? 1 : 2);
+  const int rank = r - (c >= 1 ? n0 : 0) - (c == 2 ? n1 : 0);
+  // the rank-th request of class c: exclusive scan of the threads' counts
+  const int own = cnt[c];
+  int x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = x - own;
+  for (int i = 0; i < wave; ++i) before += sh[i];
+  if (rank >= before && rank < before + own) {
+    int seen = before;
+    for (int b = lo; b < hi; ++b)
+      if (cls(b) == c && seen++ == rank) sh[2 * NW] = b;
+  }
+  __syncthreads();
+  const int b = sh[2 * NW];
+  __syncthreads();
+  return b * G1 + k;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
     const T* __restrict__ target, int32_t V, int32_t gamma, int32_t P, int32_t have_cmax,
@@ -316,8 +377,11 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
   __shared__ TruncLds<kSelThreads> U;
   __shared__ float cms[kMaxChunksBound];
   __shared__ float sh_m[kSelThreads / 64], sh_s[kSelThreads / 64];
+  __shared__ int sh_o[2 * (kSelThreads / 64) + 1];
   const int G1 = gamma + 1;
-  const int row = blockIdx.x, b = row / G1, k = row - b * G1;
+  const int B = static_cast<int>(gridDim.x) / G1;
+  const int row = slow_first_row<kSelThreads>(blockIdx.x, B, G1, V, mode, temperature, top_k, top_p, sh_o);
+  const int b = row / G1, k = row - b * G1;
   const float Tb = temperature[b];
   const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
   const int tk_raw = top_k[b];
