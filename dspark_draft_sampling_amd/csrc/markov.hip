@@ -535,6 +535,65 @@ __device__ __forceinline__ Top2 kept_chunk_scores(const QzRow<COH>& qr, int n, c
   return best;
 }
 
+// Level-1 scores over the listed chunks list[0 .. n) (n <= kMaxChunksBound)
+// for the kept set z >= thr, as kept_chunk_scores computes them, in two
+// stages: the waves reduce eight chunks at a time (their loads issued
+// together) to each chunk's kept maximum and weight in smc / sw (LDS, n
+// entries each); then thread t scores the chunks t, t + NT, ... (one Philox
+// noise per thread rather than per wave).  Returns the thread's best two.
+template <int NT, bool COH>
+__device__ __forceinline__ Top2 kept_list_scores(const QzRow<COH>& qr, int n, const int* list, float thr,
+                                                 uint64_t seed, int32_t pos, uint32_t req, float* smc, float* sw) {
+  constexpr int NW = NT / 64;
+  constexpr int kU = 8;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  for (int j0 = wave * kU; j0 < n; j0 += NW * kU) {
+    float z[kU][4];
+    int cs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u;
+      cs[u] = j < n ? uniform_i(list[j]) : -1;
+      if (cs[u] >= 0) {
+        qr.load4(cs[u] * kChunk + 4 * lane, z[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[u][e] = neg_inf();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (cs[u] < 0) continue;  // wave-uniform
+      float mc = neg_inf();
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (z[u][e] >= thr) mc = fmaxf(mc, z[u][e]);
+      mc = wave_max(mc);
+      float w = 0.0f;
+      if (mc > neg_inf()) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (z[u][e] >= thr) w += __builtin_amdgcn_exp2f((z[u][e] - mc) * kLog2e);
+        w = wave_sum(w);
+      }
+      if (lane == 0) {
+        smc[j0 + u] = mc;
+        sw[j0 + u] = w;
+      }
+    }
+  }
+  __syncthreads();
+  Top2 best{neg_inf(), INT32_MAX, neg_inf()};
+  for (int j = threadIdx.x; j < n; j += NT) {
+    const float mc = smc[j];
+    if (!(mc > neg_inf())) continue;
+    const int c = list[j];
+    const float score = mc + logf(sw[j]) + gumbel(seed, static_cast<uint32_t>(c), pos, req, DSPARK_TAG_DRAFT_CHUNK);
+    best = top2_merge(best, Top2{score, c, neg_inf()});
+  }
+  return best;
+}
+
 // Level-1 scores from the histogram cut's kept chunk weights (fixed point,
 // 2^-40 units of the shifted frame 2^(z log2e - M2)): ln of the chunk's kept
 // mass plus the chunk's Gumbel.  Returns the thread's best two.
@@ -602,7 +661,9 @@ __device__ __noinline__ TruncOut truncate_row(const float* zrow, int V, int vec,
   if (path == 1) {
     o.thr = F.U.c.thr;
     o.s_kept = F.U.c.s_kept;
-    tb = kept_chunk_scores<NT, COH>(qr, F.U.c.nchunks, F.U.c.ci, o.thr, seed, pos, req);
+    // the sort scratch is free once the cut is taken
+    tb = kept_list_scores<NT, COH>(qr, F.U.c.nchunks, F.U.c.ci, o.thr, seed, pos, req, F.U.c.tmp,
+                                   F.U.c.tmp + kMaxChunksBound);
   } else if (path == 2) {
     o.thr = F.U.h.thr;
     o.s_kept = F.U.h.s_kept;
