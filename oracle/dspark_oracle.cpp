@@ -738,4 +738,52 @@ int32_t oracle_accept_stats(const void* draft, const void* target,
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Confidence-scheduled draft width ([FT] "Scope and limitations" and the
+// author's reply on hardware-aware width: a measured choice over 0..5
+// proposals that declines or shortens speculation when the measured draft
+// plus verify cost D + V(k) does not pay; [MB] "Overview": the confidence
+// head predicts per-position acceptance so that the server can schedule its
+// verify budget).  Reading: c_j is the predicted probability that proposal j
+// is accepted given proposals 1..j-1 were, so verifying the first w
+// proposals emits E(w) = 1 + sum_{k<=w} prod_{j<=k} c_j tokens in
+// expectation (the accepted prefix plus the one token the target always
+// emits; E(gamma) is the tau of the acceptance statistics with c for a),
+// at cost D + V(w).  Per request, the width w in 0..gamma with the largest
+// E(w) / (D + V(w)); ties go to the smaller w; a width whose cost is not a
+// finite positive number is not eligible, and with none eligible w = 0.
+// c_j is clamped to [0, 1] (NaN -> 0).  cost = {D, V(0), ..., V(gamma)}.
+// Evaluated in binary64 in this order: p_k = p_{k-1} c_k, E_k = E_{k-1} + p_k,
+// den = D + V(w), ratio = E / den, compared with a strict >.
+int32_t oracle_select_width(const float* confidence, const float* cost, int32_t B,
+                            int32_t gamma, int32_t* n_draft, double* expected) {
+  if (B < 0 || gamma < 1) return 1;
+  const double D = static_cast<double>(cost[0]);
+  for (int32_t b = 0; b < B; ++b) {
+    double p = 1.0, E = 1.0;
+    double best = kNegInf, best_E = 1.0;
+    int32_t best_w = 0;
+    for (int32_t w = 0; w <= gamma; ++w) {
+      if (w >= 1) {
+        double c = static_cast<double>(confidence[static_cast<size_t>(b) * gamma + (w - 1)]);
+        if (!(c > 0.0)) c = 0.0;  // NaN and non-positive
+        if (c > 1.0) c = 1.0;
+        p = p * c;
+        E = E + p;
+      }
+      const double den = D + static_cast<double>(cost[1 + w]);
+      if (!(den > 0.0) || !std::isfinite(den)) continue;
+      const double ratio = E / den;
+      if (ratio > best) {
+        best = ratio;
+        best_w = w;
+        best_E = E;
+      }
+    }
+    n_draft[b] = best_w;
+    expected[b] = best_E;
+  }
+  return 0;
+}
+
 }  // extern "C"

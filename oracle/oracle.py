@@ -65,6 +65,8 @@ def _declare(L):
     L.oracle_accept_stats.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, f64,
                                       f64, P, P, P, P, P, P]
     L.oracle_accept_stats.restype = i32
+    L.oracle_select_width.argtypes = [P, P, i32, i32, P, P]
+    L.oracle_select_width.restype = i32
 
 
 def _p(a):
@@ -204,3 +206,23 @@ def accept_stats(inp, w_ce=0.1, w_l1=0.9, w_conf=1.0):
                                    _p(out["tau"]), _p(out["sums"]))
     assert rc == 0
     return out
+
+
+def select_width(confidence, cost):
+    """Oracle of the confidence-scheduled draft width.
+
+    confidence: [B, gamma] per-proposal acceptance predictions; cost: the
+    gamma + 2 values {D, V(0), ..., V(gamma)}.  Returns (n_draft int32 [B],
+    expected float64 [B]).
+    """
+    c = _c(confidence, np.float32)
+    assert c.ndim == 2
+    B, g = c.shape
+    co = _c(cost, np.float32)
+    assert co.shape == (g + 2,)
+    n = np.zeros(B, np.int32)
+    e = np.zeros(B)
+    rc = lib().oracle_select_width(_p(c), _p(co), B, g, _p(n), _p(e))
+    assert rc == 0
+    return n, e
+

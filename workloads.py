@@ -33,6 +33,7 @@ __all__ = [
     "STATS_CONFIG",
     "decode_inputs",
     "stats_inputs",
+    "width_inputs",
 ]
 
 
@@ -221,3 +222,33 @@ def stats_inputs(cfg=None, blocks=None, mask_every=0, **overrides) -> dict:
         mask[np.asarray(blks) % mask_every == mask_every - 1] = 0
     return dict(draft=draft, target=target, teacher=teacher, conf_logits=conf,
                 block_mask=mask, N=n, gamma=gamma, V=V, dtype=cfg["dtype"])
+
+
+# Draft-width selection: per-proposal acceptance predictions and a cost table
+# {D, V(0), ..., V(gamma)} in arbitrary time units.  Confidences of request b
+# decay along the block (c_j = s_b * u_j^(j / gamma), s_b ~ U[0.3, 1], u_j ~
+# U[0.5, 1]) so that the chosen widths spread over 0..gamma; the costs model a
+# fixed draft pass and a verify pass that grows with the rows it checks.
+WIDTH_CONFIG = dict(seed=1006, B=64, gamma=5, draft_cost=1.0, verify_base=3.0,
+                    verify_per_row=0.45)
+
+
+def width_inputs(B=None, gamma=None, cfg=None, **overrides) -> dict:
+    cfg = dict(WIDTH_CONFIG if cfg is None else cfg)
+    cfg.update(overrides)
+    if B is not None:
+        cfg["B"] = B
+    if gamma is not None:
+        cfg["gamma"] = gamma
+    B, g = cfg["B"], cfg["gamma"]
+    conf = np.empty((B, g), np.float32)
+    for b in range(B):
+        r = _rng(cfg["seed"], 1, b)
+        s_b = r.uniform(0.3, 1.0)
+        u = r.uniform(0.5, 1.0, g)
+        conf[b] = s_b * u ** (np.arange(1, g + 1) / g)
+    cost = np.empty(g + 2, np.float32)
+    cost[0] = cfg["draft_cost"]
+    cost[1:] = cfg["verify_base"] + cfg["verify_per_row"] * (np.arange(g + 1) + 1)
+    return dict(B=B, gamma=g, confidence=conf, cost=cost)
+
