@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=64,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "stats"],
+    ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "adaptive", "stats"],
                     default="decode",
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
@@ -102,6 +102,8 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
         return 0
     if name in ("stats_pairs", "stats_reduce"):
         return 16 * B * g
+    if name == "select_width":     # confidences in, widths and expectations out
+        return 4 * B * g + 4 * (g + 2) + 8 * B
     return 0
 
 
@@ -291,7 +293,14 @@ DECODE_WORKLOADS = {
                                "per-request T, top-k, top-p; Markov + verify + accept stats"),
     "wide_greedy": ("wide_greedy", "wide greedy tile: 64 requests x 8 rows, greedy Markov + verify "
                                    "+ accept stats"),
+    "adaptive": ("decode", "decode verify with confidence-scheduled width: Markov + width choice + "
+                           "verify of the chosen proposals + accept stats"),
 }
+
+# Draft-width cost table of the adaptive workload, in microseconds: a fixed
+# draft pass and a verify pass that grows with the rows it checks (synthetic
+# values of the order of this step's own kernels, not a live calibration).
+ADAPTIVE_COST_US = dict(draft=140.0, verify_base=40.0, verify_per_row=12.0)
 
 
 def run_decode(args, torch, ds):
@@ -336,6 +345,12 @@ def run_decode(args, torch, ds):
     vf_out = ds.dspark_verify(s0["target"], mk_out[0]["draft_tokens"], pol, mk_out[0]["q_logits"],
                               mk_out[0]["q_lse"], mk_out[0]["q_thr"], mk_out[0]["q_tok"], seed=0)
     st_out = ds.dspark_accept_stats(s0["backbone"], s0["tgt_rows"], teacher, conf_logits)
+    adaptive = args.workload == "adaptive"
+    if adaptive:
+        c = ADAPTIVE_COST_US
+        cost = torch.tensor([c["draft"]] + [c["verify_base"] + c["verify_per_row"] * (w + 1)
+                                            for w in range(g + 1)], dtype=torch.float32, device=dev)
+        wd_out = ds.dspark_select_width(mk_out[0]["confidence"], cost)
     it = [0]
 
     def step():
@@ -344,8 +359,12 @@ def run_decode(args, torch, ds):
         x, mo = sets[i], mk_out[i]
         ds.dspark_markov_sample(x["backbone"], anchor, x["w1"], x["w2"], x["hidden"], x["embed"],
                                 conf_w, pol, seed=0, out=mo)
+        nd = None
+        if adaptive:
+            ds.dspark_select_width(mo["confidence"], cost, out=wd_out)
+            nd = wd_out["n_draft"]
         ds.dspark_verify(x["target"], mo["draft_tokens"], pol, mo["q_logits"], mo["q_lse"],
-                         mo["q_thr"], mo["q_tok"], seed=0, out=vf_out)
+                         mo["q_thr"], mo["q_tok"], n_draft=nd, seed=0, out=vf_out)
         ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
 
     ms_total, wall = _timed(step, args, torch)
@@ -377,6 +396,8 @@ def run_decode(args, torch, ds):
                 step=dict(alg_bytes=int(step_bytes),
                           alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                           accept_rate=round(float(vf_out["accept_len"].float().mean().item()) / g, 4),
+                          **(dict(mean_width=round(float(wd_out["n_draft"].float().mean().item()), 3),
+                                  cost_us=ADAPTIVE_COST_US) if adaptive else {}),
                           kernels=kernels))
 
 

@@ -30,7 +30,8 @@ DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS = 1, 2, 3
 FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
 
 __all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
-           "dspark_accept_stats", "dspark_workspace_size", "profile_enable", "profile_summary"]
+           "dspark_accept_stats", "dspark_select_width", "dspark_workspace_size", "profile_enable",
+           "profile_summary"]
 
 
 class DSparkError(RuntimeError):
@@ -68,6 +69,8 @@ def lib():
         L.dspark_accept_stats.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32, f32,
                                           P, P, P, P, P, P, P, sz, P]
         L.dspark_accept_stats.restype = C.c_int
+        L.dspark_select_width.argtypes = [P, P, i32, i32, P, P, P]
+        L.dspark_select_width.restype = C.c_int
         L.dspark_profile_enable.argtypes = [C.c_int]
         L.dspark_profile_enable.restype = C.c_int
         L.dspark_markov_plan.argtypes = [C.c_int]
@@ -250,6 +253,28 @@ def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_
                                    _p(out["ce"]), _p(out["bce"]), _p(out["tau"]),
                                    _p(out["sums"]), _p(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev))
+    _check(rc)
+    return out
+
+
+def dspark_select_width(confidence, cost, want_expected=True, out=None):
+    """Confidence-scheduled draft width; returns dict n_draft int32 [B] and
+    expected float32 [B] (or None) as device tensors.  cost is the device
+    float32 table {D, V(0), ..., V(gamma)}."""
+    _dev_tensor(confidence, torch.float32, "confidence")
+    _dev_tensor(cost, torch.float32, "cost")
+    if confidence.dim() != 2:
+        raise DSparkError("select_width: confidence must be [B, gamma]")
+    B, g = confidence.shape
+    if cost.shape != (g + 2,):
+        raise DSparkError("select_width: cost must hold gamma + 2 values")
+    dev = confidence.device
+    if out is None:
+        out = dict(n_draft=torch.empty((B,), dtype=torch.int32, device=dev),
+                   expected=torch.empty((B,), dtype=torch.float32, device=dev)
+                   if want_expected else None)
+    rc = lib().dspark_select_width(_p(confidence), _p(cost), B, g, _p(out["n_draft"]),
+                                   _p(out["expected"]), _stream(dev))
     _check(rc)
     return out
 

@@ -147,4 +147,16 @@ dspark_status dspark_accept_stats(const void* draft_logits, const void* target_l
   return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
 }
 
+dspark_status dspark_select_width(const float* confidence, const float* cost, int32_t B,
+                                  int32_t gamma, int32_t* n_draft, float* expected, void* stream) {
+  if (B < 0 || gamma <= 0) return DSPARK_EINVAL;
+  if (gamma > DSPARK_MAX_GAMMA) return DSPARK_ESHAPE;
+  if (!cost) return DSPARK_EINVAL;
+  if (B == 0) return DSPARK_OK;
+  if (!confidence || !n_draft) return DSPARK_EINVAL;
+  const hipError_t e = dspark::launch_select_width(confidence, cost, B, gamma, n_draft, expected,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
+}
+
 }  // extern "C"

@@ -106,6 +106,10 @@ hipError_t launch_verify(const void* target, int dtype, const int32_t* draft, co
                          int32_t gamma, int32_t V, int32_t* accept_len, int32_t* out_tokens,
                          uint8_t* flags, void* ws, const VerifyPlan& plan, hipStream_t st);
 
+// Confidence-scheduled draft width (width.hip).
+hipError_t launch_select_width(const float* confidence, const float* cost, int32_t B, int32_t gamma,
+                               int32_t* n_draft, float* expected, hipStream_t st);
+
 hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
                          const uint16_t* w1, const uint16_t* w2, const uint16_t* hidden,
                          const uint16_t* embed, const float* conf_w, dspark_policy pol,

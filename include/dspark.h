@@ -351,6 +351,41 @@ dspark_status dspark_accept_stats(
     float* ce, float* bce, float* tau, float* sums, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * dspark_select_width
+ *
+ * [FT] scope notes and the author's reply on hardware-aware width: a measured
+ * choice over 0..gamma proposals that declines or shortens speculation when
+ * the draft plus verify cost D + V(k) does not pay.  [MB] "Overview": the
+ * confidence head predicts per-position acceptance so that the server can
+ * schedule its verify budget.  Per request b, with c_j = confidence[b, j-1]
+ * clamped to [0, 1] (NaN -> 0) read as the probability that proposal j is
+ * accepted once 1..j-1 were:
+ *   E(w)       = 1 + sum_{k<=w} prod_{j<=k} c_j   (expected tokens emitted when
+ *                the first w proposals are verified; E(gamma) is tau of
+ *                dspark_accept_stats with c for a)
+ *   n_draft[b] = the w in [0, gamma] with the largest E(w) / (D + V(w)); the
+ *                smaller w on ties; a w whose D + V(w) is not a finite
+ *                positive number is skipped (none left: 0)
+ * evaluated in binary64 in the order p_k = p_{k-1} c_k, E_k = E_{k-1} + p_k,
+ * E / (D + V(w)), every operation rounded separately (no fused multiply-add),
+ * so the choice is exact and reproducible.  n_draft feeds dspark_verify.
+ *
+ * Inputs
+ *   confidence [B, gamma] float32 (as written by dspark_markov_sample)
+ *   cost       [gamma + 2] float32, device memory: {D, V(0), ..., V(gamma)}
+ *              in one time unit of the caller's choice
+ * Outputs
+ *   n_draft    [B] int32
+ *   expected   [B] float32 or NULL: E(n_draft[b])
+ * No workspace.  Errors: EINVAL (NULL confidence, cost or n_draft; B < 0;
+ * gamma <= 0), ESHAPE (gamma > DSPARK_MAX_GAMMA), EDEVICE.  B = 0 is a no-op
+ * (cost must still be given).
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_select_width(const float* confidence, const float* cost,
+                                  int32_t B, int32_t gamma, int32_t* n_draft,
+                                  float* expected, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,21 @@ def stats(L, N=4, gamma=5, V=1024, dtype=1, sums=FAKE):
                                  FAKE, FAKE, FAKE, FAKE, FAKE, sums, None, 0, None)
 
 
+def width(L, B=4, gamma=5, conf=FAKE, cost=FAKE, out=FAKE):
+    return L.dspark_select_width(conf, cost, B, gamma, out, None, None)
+
+
+def test_select_width_validation(L):
+    assert width(L, B=-1) == ds.DSPARK_EINVAL
+    assert width(L, gamma=0) == ds.DSPARK_EINVAL
+    assert width(L, gamma=17) == ds.DSPARK_ESHAPE
+    assert width(L, conf=None) == ds.DSPARK_EINVAL
+    assert width(L, cost=None) == ds.DSPARK_EINVAL
+    assert width(L, out=None) == ds.DSPARK_EINVAL
+    assert width(L, B=0, conf=None, out=None) == ds.DSPARK_OK  # empty batch: no-op
+    assert width(L, B=0, cost=None) == ds.DSPARK_EINVAL
+
+
 def test_verify_validation(L):
     assert verify(L, B=-1) == ds.DSPARK_EINVAL
     assert verify(L, gamma=0) == ds.DSPARK_EINVAL
