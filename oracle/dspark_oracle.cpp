@@ -739,6 +739,72 @@ int32_t oracle_accept_stats(const void* draft, const void* target,
 }
 
 // ---------------------------------------------------------------------------
+// Gradient of the acceptance statistics' loss numerator ([MB] "Training
+// objective": the draft is trained by 0.1 CE + 0.9 raw L1, and the BCE term
+// trains the confidence head against the acceptance label; the target's
+// distribution is detached; "Memory contract for the full-vocabulary terms":
+// the terms' row chunks are recomputed in the backward).  With the
+// numerator of oracle_accept_stats scaled by `scale`, per block b (mask m_b)
+// and position k (row k-1), w_k = exp(-k/gamma), P = softmax(draft row),
+// T = softmax(target row), a = clamp(1 - L1/2, 0, 1):
+//   d/d draft_v = scale m_b w_k [ w_ce (P_v - [v == teacher])
+//                                + w_l1 P_v (s_v - sum_u s_u P_u) ]
+//   d/d c       = scale m_b w_k w_conf (sigmoid(c) - a)
+// with s_u = sign(P_u - T_u) and sign(0) = 0 (the subgradient of |x| that
+// vanishes at 0).  Readings: the label a is held fixed in the BCE (it is the
+// confidence head's regression target), so the BCE sends no gradient into
+// the draft logits; -inf logits have P = 0 and get gradient 0 (teacher
+// aside).  sigmoid(c) = 1 / (1 + exp(-c)).
+int32_t oracle_accept_stats_backward(const void* draft, const void* target, int32_t dtype,
+                                     const int32_t* teacher, const float* conf_logits,
+                                     const uint8_t* block_mask, int32_t N, int32_t gamma,
+                                     int32_t V, double w_ce, double w_l1, double w_conf,
+                                     double scale, double* grad_draft, double* grad_conf) {
+  if (N < 0 || gamma < 1 || V < 1) return 1;
+  std::vector<double> dl, tl, P, T;
+  P.resize(V);
+  T.resize(V);
+  for (int32_t b = 0; b < N; ++b) {
+    const double m = (block_mask ? block_mask[b] != 0 : true) ? 1.0 : 0.0;
+    for (int32_t k = 1; k <= gamma; ++k) {
+      const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
+      bool nf = false;
+      load_row(draft, dtype, row * V, V, &dl, &nf);
+      load_row(target, dtype, row * V, V, &tl, &nf);
+      double md = kNegInf, mt = kNegInf;
+      for (int32_t v = 0; v < V; ++v) {
+        md = std::max(md, dl[v]);
+        mt = std::max(mt, tl[v]);
+      }
+      double sd = 0.0, st = 0.0;
+      for (int32_t v = 0; v < V; ++v) {
+        if (dl[v] != kNegInf) sd += std::exp(dl[v] - md);
+        if (tl[v] != kNegInf) st += std::exp(tl[v] - mt);
+      }
+      double l1 = 0.0, S = 0.0;
+      for (int32_t v = 0; v < V; ++v) {
+        P[v] = (dl[v] == kNegInf) ? 0.0 : std::exp(dl[v] - md) / sd;
+        T[v] = (tl[v] == kNegInf) ? 0.0 : std::exp(tl[v] - mt) / st;
+        l1 += std::fabs(P[v] - T[v]);
+        const double sg = P[v] > T[v] ? 1.0 : (P[v] < T[v] ? -1.0 : 0.0);
+        S += sg * P[v];
+      }
+      const double a = std::min(1.0, std::max(0.0, 1.0 - 0.5 * l1));
+      const double alpha = scale * m * std::exp(-static_cast<double>(k) / gamma);
+      const int32_t tch = clamp_token(teacher[row], V);
+      for (int32_t v = 0; v < V; ++v) {
+        const double sg = P[v] > T[v] ? 1.0 : (P[v] < T[v] ? -1.0 : 0.0);
+        const double ce_g = P[v] - (v == tch ? 1.0 : 0.0);
+        grad_draft[row * V + v] = alpha * (w_ce * ce_g + w_l1 * P[v] * (sg - S));
+      }
+      const double c = static_cast<double>(conf_logits[row]);
+      grad_conf[row] = alpha * w_conf * (1.0 / (1.0 + std::exp(-c)) - a);
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
 // Confidence-scheduled draft width ([FT] "Scope and limitations" and the
 // author's reply on hardware-aware width: a measured choice over 0..5
 // proposals that declines or shortens speculation when the measured draft

@@ -65,6 +65,9 @@ def _declare(L):
     L.oracle_accept_stats.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, f64,
                                       f64, P, P, P, P, P, P]
     L.oracle_accept_stats.restype = i32
+    L.oracle_accept_stats_backward.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, f64,
+                                               f64, f64, P, P]
+    L.oracle_accept_stats_backward.restype = i32
     L.oracle_select_width.argtypes = [P, P, i32, i32, P, P]
     L.oracle_select_width.restype = i32
 
@@ -204,6 +207,24 @@ def accept_stats(inp, w_ce=0.1, w_l1=0.9, w_conf=1.0):
                                    _p(bm), N, g, V, w_ce, w_l1, w_conf, _p(out["l1"]),
                                    _p(out["accept_rate"]), _p(out["ce"]), _p(out["bce"]),
                                    _p(out["tau"]), _p(out["sums"]))
+    assert rc == 0
+    return out
+
+
+def accept_stats_backward(inp, w_ce=0.1, w_l1=0.9, w_conf=1.0, scale=1.0):
+    """Oracle of the gradient of the statistics' loss numerator (times
+    scale): dict grad_draft [N,g,V] and grad_conf [N,g], binary64."""
+    N, g, V = inp["N"], inp["gamma"], inp["V"]
+    dr = _logits(inp["draft"], inp["dtype"])
+    tg = _logits(inp["target"], inp["dtype"])
+    assert dr.shape == (N, g, V) and tg.shape == (N, g, V)
+    te = _c(inp["teacher"], np.int32)
+    cl = _c(inp["conf_logits"], np.float32)
+    bm = _c(inp.get("block_mask"), np.uint8)
+    out = dict(grad_draft=np.zeros((N, g, V)), grad_conf=np.zeros((N, g)))
+    rc = lib().oracle_accept_stats_backward(_p(dr), _p(tg), DTYPES[inp["dtype"]], _p(te), _p(cl),
+                                            _p(bm), N, g, V, w_ce, w_l1, w_conf, scale,
+                                            _p(out["grad_draft"]), _p(out["grad_conf"]))
     assert rc == 0
     return out
 
