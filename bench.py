@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=64,
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "adaptive", "stats"],
+    ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "adaptive", "stats",
+                                           "train"],
                     default="decode",
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
@@ -102,6 +103,12 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
         return 0
     if name in ("stats_pairs", "stats_reduce"):
         return 16 * B * g
+    if name == "stats_grad_rows":  # row pair read once, gradient row written once (bf16)
+        return 3 * 2 * B * g * V
+    if name == "stats_grad_write":  # the gradient row written (its reads are the third look)
+        return 2 * B * g * V
+    if name == "stats_grad_part2":  # second look: not compulsory
+        return 0
     if name == "select_width":     # confidences in, widths and expectations out
         return 4 * B * g + 4 * (g + 2) + 8 * B
     return 0
@@ -279,7 +286,7 @@ def main():
 
     ds.markov_plan({"auto": ds.MARKOV_AUTO, "per-step": ds.MARKOV_PER_STEP,
                     "cooperative": ds.MARKOV_COOPERATIVE}[args.markov_plan])
-    if args.workload == "stats":
+    if args.workload in ("stats", "train"):
         line = run_stats(args, torch, ds)
     else:
         line = run_decode(args, torch, ds)
@@ -402,7 +409,9 @@ def run_decode(args, torch, ds):
 
 
 def run_stats(args, torch, ds):
-    """Training-side acceptance statistics alone: 2048 blocks x gamma 7."""
+    """Training-side acceptance statistics: 2048 blocks x gamma 7; with
+    --workload train also their gradient (the forward and backward of the
+    loss terms)."""
     from workloads import stats_inputs
 
     t0 = time.time()
@@ -418,12 +427,21 @@ def run_stats(args, torch, ds):
     teacher = torch.from_numpy(inp["teacher"]).to(dev)
     conf = torch.from_numpy(inp["conf_logits"]).to(dev)
     out = ds.dspark_accept_stats(sets[0]["draft"], sets[0]["target"], teacher, conf)
+    train = args.workload == "train"
+    if train:
+        # the loss is the numerator over its token count: the upstream gradient
+        scale = (1.0 / out["sums"][1:2]).contiguous()
+        gout = ds.dspark_accept_stats_backward(sets[0]["draft"], sets[0]["target"], teacher, conf,
+                                               grad_scale=scale)
     it = [0]
 
     def step():
         x = sets[it[0] % len(sets)]
         it[0] += 1
         ds.dspark_accept_stats(x["draft"], x["target"], teacher, conf, out=out)
+        if train:
+            ds.dspark_accept_stats_backward(x["draft"], x["target"], teacher, conf, grad_scale=scale,
+                                            out=gout)
 
     ms_total, wall = _timed(step, args, torch)
     ms_per_step = ms_total / args.steps
@@ -440,11 +458,13 @@ def run_stats(args, torch, ds):
         sec = time.perf_counter() - t
         cpu = dict(value=round(nb * g / sec, 2), unit="rows/s", cores=1, kind="oracle",
                    sample=f"{nb} of the {N} blocks, {sec:.1f}s single-threaded")
-    return dict(metric=f"stats rows/sec (N×γ row pairs) at V={V},N={N},γ={g}", value=round(value, 1),
+    what = "stats forward + backward" if train else "stats"
+    return dict(metric=f"{what} rows/sec (N×γ row pairs) at V={V},N={N},γ={g}", value=round(value, 1),
                 unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                 ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak",
                 vs_baseline=None, dtype="bf16", data="synthetic",
-                config=dict(workload="training acceptance statistics", N=N, gamma=g, V=V,
+                config=dict(workload="training acceptance statistics" +
+                            (" and their gradient" if train else ""), N=N, gamma=g, V=V,
                             logits="bf16", rotated_batches=len(sets)),
                 roofline=_roofline(kernels, False), cpu_baseline=cpu,
                 step=dict(kernels=kernels))

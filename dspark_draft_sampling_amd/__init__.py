@@ -26,11 +26,11 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_ESHAPE, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(6)
 DSPARK_BF16, DSPARK_F32 = 1, 2
-DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS = 1, 2, 3
+DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS, DSPARK_OP_STATS_BACKWARD = 1, 2, 3, 4
 FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
 
 __all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
-           "dspark_accept_stats", "dspark_select_width", "dspark_workspace_size", "profile_enable",
+           "dspark_accept_stats", "dspark_accept_stats_backward", "dspark_select_width", "dspark_workspace_size", "profile_enable",
            "profile_summary"]
 
 
@@ -69,6 +69,9 @@ def lib():
         L.dspark_accept_stats.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32, f32,
                                           P, P, P, P, P, P, P, sz, P]
         L.dspark_accept_stats.restype = C.c_int
+        L.dspark_accept_stats_backward.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32,
+                                                   f32, P, P, P, P, sz, P]
+        L.dspark_accept_stats_backward.restype = C.c_int
         L.dspark_select_width.argtypes = [P, P, i32, i32, P, P, P]
         L.dspark_select_width.restype = C.c_int
         L.dspark_profile_enable.argtypes = [C.c_int]
@@ -253,6 +256,40 @@ def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_
                                    _p(out["ce"]), _p(out["bce"]), _p(out["tau"]),
                                    _p(out["sums"]), _p(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev))
+    _check(rc)
+    return out
+
+
+def dspark_accept_stats_backward(draft, target, teacher, conf_logits, block_mask=None, w_ce=0.1,
+                                 w_l1=0.9, w_conf=1.0, grad_scale=None, out=None):
+    """Gradient of grad_scale x the statistics' loss numerator; returns dict
+    grad_draft [N,g,V] (the logits dtype) and grad_conf [N,g] float32 (device
+    tensors).  grad_scale: a one-element float32 device tensor or None (1)."""
+    dt = _logits_dtype(draft, "draft")
+    _dev_tensor(draft, draft.dtype, "draft")
+    _dev_tensor(target, draft.dtype, "target")
+    N, g, V = draft.shape
+    if target.shape != draft.shape:
+        raise DSparkError("accept_stats_backward: draft and target shapes differ")
+    _dev_tensor(teacher, torch.int32, "teacher")
+    _dev_tensor(conf_logits, torch.float32, "conf_logits")
+    if block_mask is not None:
+        _dev_tensor(block_mask, torch.uint8, "block_mask")
+    if grad_scale is not None:
+        _dev_tensor(grad_scale, torch.float32, "grad_scale")
+        if grad_scale.numel() != 1:
+            raise DSparkError("accept_stats_backward: grad_scale must hold one value")
+    dev = draft.device
+    if out is None:
+        out = dict(grad_draft=torch.empty((N, g, V), dtype=draft.dtype, device=dev),
+                   grad_conf=torch.empty((N, g), dtype=torch.float32, device=dev))
+    nb = dspark_workspace_size(DSPARK_OP_STATS_BACKWARD, N, g, V)
+    ws = _workspace(DSPARK_OP_STATS_BACKWARD, dev, nb) if nb > 0 else None
+    rc = lib().dspark_accept_stats_backward(_p(draft), _p(target), dt, _p(teacher), _p(conf_logits),
+                                            _p(block_mask), N, g, V, float(w_ce), float(w_l1),
+                                            float(w_conf), _p(grad_scale), _p(out["grad_draft"]),
+                                            _p(out["grad_conf"]), _p(ws),
+                                            0 if ws is None else ws.numel(), _stream(dev))
     _check(rc)
     return out
 

@@ -47,6 +47,8 @@ size_t dspark_workspace_size(int op, int32_t B, int32_t gamma, int32_t V, int32_
     }
     case DSPARK_OP_STATS:
       return dspark::plan_stats(B, gamma, V).bytes;
+    case DSPARK_OP_STATS_BACKWARD:
+      return dspark::plan_stats_backward(B, gamma, V).bytes;
     default:
       return 0;
   }
@@ -144,6 +146,28 @@ dspark_status dspark_accept_stats(const void* draft_logits, const void* target_l
       draft_logits, target_logits, logits_dtype, teacher, conf_logits, block_mask, N, gamma, V,
       w_ce, w_l1, w_conf, l1, accept_rate, ce, bce, tau, sums, workspace, plan,
       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
+}
+
+dspark_status dspark_accept_stats_backward(const void* draft_logits, const void* target_logits,
+                                           int logits_dtype, const int32_t* teacher,
+                                           const float* conf_logits, const uint8_t* block_mask,
+                                           int32_t N, int32_t gamma, int32_t V, float w_ce,
+                                           float w_l1, float w_conf, const float* grad_scale,
+                                           void* grad_draft, float* grad_conf, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (N < 0) return DSPARK_EINVAL;
+  dspark_status s = check_common(logits_dtype, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if (N == 0) return DSPARK_OK;
+  if (!draft_logits || !target_logits || !teacher || !conf_logits || !grad_draft || !grad_conf)
+    return DSPARK_EINVAL;
+  if (static_cast<int64_t>(N) * gamma > 0x7fffffffLL) return DSPARK_ESHAPE;
+  const dspark::StatsGradPlan plan = dspark::plan_stats_backward(N, gamma, V);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return DSPARK_EWORKSPACE;
+  const hipError_t e = dspark::launch_stats_backward(
+      draft_logits, target_logits, logits_dtype, teacher, conf_logits, block_mask, N, gamma, V, w_ce,
+      w_l1, w_conf, grad_scale, grad_draft, grad_conf, workspace, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
 }
 

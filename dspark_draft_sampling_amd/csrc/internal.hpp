@@ -100,6 +100,19 @@ struct StatsPlan {
 };
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 
+// Gradient of the statistics' loss numerator (stats.hip).
+struct StatsGradPlan {
+  int sliced;  // 1: (row pair, segment) item kernels; 0: one workgroup per row pair
+  int P;       // segments per row pair
+  size_t off_part, off_l1, off_s, off_rows, off_cnt, bytes;
+};
+StatsGradPlan plan_stats_backward(int32_t N, int32_t gamma, int32_t V);
+hipError_t launch_stats_backward(const void* draft, const void* target, int dtype, const int32_t* teacher,
+                                 const float* conf_logits, const uint8_t* block_mask, int32_t N,
+                                 int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf,
+                                 const float* grad_scale, void* grad_draft, float* grad_conf, void* ws,
+                                 const StatsGradPlan& plan, hipStream_t st);
+
 hipError_t launch_verify(const void* target, int dtype, const int32_t* draft, const float* q_z,
                          const float* q_lse, const float* q_thr, const float* q_tok,
                          const int32_t* n_draft, dspark_policy pol, uint64_t seed, int32_t B,

@@ -514,6 +514,236 @@ __global__ __launch_bounds__(kThreads) void stats_reduce_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward: the gradient of scale x the loss numerator (definition in
+// include/dspark.h).  Per row pair, three looks: the normalisers; then
+// L1 = sum |P - T| and S = sum_u sign(P_u - T_u) P_u; then the gradient row
+//   g_v = a_ce (P_v - [v == teacher]) + a_l1 P_v (s_v - S),
+// a_ce = scale m_b w_k w_ce, a_l1 = scale m_b w_k w_l1 (the only write).  The
+// sliced path runs the looks as item kernels (the first is stats_part1); the
+// row path keeps one workgroup per pair for all three, its second and third
+// looks served by the caches.
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// A pair's coefficients: P_v = 2^(x log2e - shd) isd, T_v likewise.
+struct GradRow {
+  float shd, isd, sht, ist;
+  float S, a_ce, a_l1;
+  int32_t teacher;
+};
+
+struct GradArgs {
+  const int32_t* teacher;
+  const float* conf_logits;
+  const uint8_t* block_mask;
+  const float* scale;  // device scalar or NULL (1)
+  int32_t gamma;
+  float w_ce, w_l1, w_conf;
+  float* grad_conf;
+  GradRow* rows;
+  uint32_t* counters;
+};
+
+// the pair's coefficients from its normalisers, L1 and S; writes the
+// confidence-logit gradient scale m_b w_k w_conf (sigmoid(c) - a)
+__device__ __forceinline__ GradRow grad_row(const GradArgs& g, int pair, float shd, float Sd, float sht,
+                                            float St, float L1, float S, int32_t V) {
+  const int k = pair % g.gamma + 1, b = pair / g.gamma;
+  const bool m = g.block_mask ? g.block_mask[b] != 0 : true;
+  const float sc = g.scale ? *g.scale : 1.0f;
+  const float alpha = m ? sc * expf(-static_cast<float>(k) / static_cast<float>(g.gamma)) : 0.0f;
+  const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+  const float c = g.conf_logits[pair];
+  g.grad_conf[pair] = alpha * g.w_conf * (1.0f / (1.0f + expf(-c)) - a);
+  return GradRow{shd, 1.0f / Sd, sht, 1.0f / St, S, alpha * g.w_ce, alpha * g.w_l1,
+                 clamp_token(g.teacher[pair], V)};
+}
+
+__device__ __forceinline__ void l1_and_s(float x, float y, float shd, float isd, float sht, float ist,
+                                         float& l1, float& s) {
+  const float P = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -shd)) * isd;
+  const float T = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -sht)) * ist;
+  l1 += fabsf(P - T);
+  s += P > T ? P : (P < T ? -P : 0.0f);
+}
+
+__device__ __forceinline__ float grad_elem(const GradRow& r, float x, float y, int v) {
+  const float P = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r.shd)) * r.isd;
+  const float T = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -r.sht)) * r.ist;
+  const float sg = P > T ? 1.0f : (P < T ? -1.0f : 0.0f);
+  return r.a_ce * (P - (v == r.teacher ? 1.0f : 0.0f)) + r.a_l1 * P * (sg - r.S);
+}
+
+// Sliced second look: per item the pair's normalisers (its part1 records)
+// and the item's shares of L1 and S; the pair's last item (ticket) sums the
+// shares in a fixed order and stores the pair's GradRow.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_grad_part2_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P, int32_t items,
+    const StatPart* __restrict__ part, float* __restrict__ l1part, float* __restrict__ spart,
+    GradArgs o) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int SEG = stat_seg<T>();
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * kWaves;
+  for (int item = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6); item < items;
+       item += nwaves) {
+    const int it_ = __builtin_amdgcn_readfirstlane(item);
+    const int pair = it_ / P, seg = it_ - pair * P;
+    uint4 ud[kSegIters], ut[kSegIters];
+    seg_load<T>(draft, target, V, P, it_, lane, ud, ut);
+    float M2d, Sd, M2t, St;
+    pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
+    seg_mask<T>(V, seg * SEG, lane, ud, ut);
+    const float isd = 1.0f / Sd, ist = 1.0f / St;
+    float l1 = 0.0f, sv = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        l1_and_s(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}), M2d, isd, M2t, ist, l1, sv);
+    l1 = wave_sum(l1);
+    sv = wave_sum(sv);
+    uint32_t ticket = 0;
+    if (lane == 0) {
+      store_coherent(l1part + it_, l1);
+      store_coherent(spart + it_, sv);
+      ticket = publish(o.counters + static_cast<size_t>(pair) * kTicketStride);
+    }
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket != static_cast<uint32_t>(P - 1)) continue;
+    float L1 = 0.0f, S = 0.0f;
+    for (int i = lane; i < P; i += 64) {
+      L1 += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
+      S += load_coherent(spart + static_cast<size_t>(pair) * P + i);
+    }
+    L1 = wave_sum(L1);
+    S = wave_sum(S);
+    if (lane == 0) o.rows[pair] = grad_row(o, pair, M2d, Sd, M2t, St, L1, S, V);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const float* g);
+template <>
+__device__ __forceinline__ void store16<uint16_t>(uint16_t* p, const float* g) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(bf16_rne(g[2 * i])) | (static_cast<uint32_t>(bf16_rne(g[2 * i + 1])) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ void store16<float>(float* p, const float* g) {
+  *reinterpret_cast<float4*>(p) = make_float4(g[0], g[1], g[2], g[3]);
+}
+
+// Sliced third look: per item the gradient of its segment (the next item's
+// loads in flight while the current one is computed and stored).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_grad_write_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P, int32_t items,
+    const GradRow* __restrict__ rows, T* __restrict__ grad) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int SEG = stat_seg<T>();
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * kWaves;
+  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6));
+  if (item >= items) return;
+  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  auto write = [&](const uint4* ud, const uint4* ut, int it_) {
+    const int pair = it_ / P, seg = it_ - pair * P;
+    const GradRow r = rows[pair];
+    const size_t off = static_cast<size_t>(pair) * V;
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it) {
+      const int e = seg * SEG + (it * 64 + lane) * EPL;
+      if (e >= V) continue;  // a clamped load past the row
+      float g[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, elem16(ud[it], j, T{}), elem16(ut[it], j, T{}), e + j);
+      store16<T>(grad + off + e, g);
+    }
+  };
+  seg_load<T>(draft, target, V, P, item, lane, ad, at);
+  while (true) {
+    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
+    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
+    write(ad, at, item);
+    if (n1 >= items) break;
+    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
+    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
+    write(bd, bt, n1);
+    if (n2 >= items) break;
+    item = n2;
+  }
+}
+
+// Row path: one workgroup per row pair, the three looks in turn.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void stats_grad_rows_kernel(const T* __restrict__ draft,
+                                                                   const T* __restrict__ target,
+                                                                   int32_t V, GradArgs o,
+                                                                   T* __restrict__ grad) {
+  using L = Vec8<T, VEC>;
+  constexpr int EPL = L::N;
+  __shared__ float shv[kWaves];
+  const size_t row = blockIdx.x;
+  const T* dr = draft + row * V;
+  const T* tr = target + row * V;
+  T* gr = grad + row * V;
+  const int step = kThreads * EPL;
+
+  float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
+  for (int e = threadIdx.x * EPL; e < V; e += step) {
+    float xd[EPL], xt[EPL];
+    L::load(dr + e, xd);
+    L::load(tr + e, xt);
+    online(md, sd, xd, EPL);
+    online(mt, st, xt, EPL);
+  }
+  const float Md = block_max<kWaves>(md, shv);
+  const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
+  const float Mt = block_max<kWaves>(mt, shv);
+  const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
+  const float shd = Md > neg_inf() ? Md * kLog2e : 0.0f, sht = Mt > neg_inf() ? Mt * kLog2e : 0.0f;
+  const float isd = 1.0f / Sd, ist = 1.0f / St;
+
+  float l1 = 0.0f, sv = 0.0f;
+  for (int e = threadIdx.x * EPL; e < V; e += step) {
+    float xd[EPL], xt[EPL];
+    L::load(dr + e, xd);
+    L::load(tr + e, xt);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) l1_and_s(xd[j], xt[j], shd, isd, sht, ist, l1, sv);
+  }
+  const float L1 = block_sum<kWaves>(l1, shv);
+  const float S = block_sum<kWaves>(sv, shv);
+  __shared__ GradRow shr;
+  if (threadIdx.x == 0) shr = grad_row(o, static_cast<int>(row), shd, Sd, sht, St, L1, S, V);
+  __syncthreads();
+  const GradRow r = shr;
+
+  for (int e = threadIdx.x * EPL; e < V; e += step) {
+    float xd[EPL], xt[EPL], g[EPL];
+    L::load(dr + e, xd);
+    L::load(tr + e, xt);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[j], xt[j], e + j);
+    if constexpr (VEC) {
+      store16<T>(gr + e, g);
+    } else {
+      if constexpr (sizeof(T) == 2) gr[e] = bf16_rne(g[0]);
+      else gr[e] = g[0];
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                         const float* conf_logits, const uint8_t* block_mask, int32_t N,
@@ -554,7 +784,87 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int32_t gamma, int32_t V,
+                                 GradArgs o, T* grad, void* ws, const StatsGradPlan& pl,
+                                 hipStream_t st) {
+  const int epl = 16 / static_cast<int>(sizeof(T));
+  const bool vec = (V % epl == 0) && reinterpret_cast<uintptr_t>(draft) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(grad) % 16 == 0;
+  const int npairs = N * gamma;
+  if (npairs == 0) return hipSuccess;
+  if (vec && pl.sliced) {
+    char* w = static_cast<char*>(ws);
+    StatPart* part = reinterpret_cast<StatPart*>(w + pl.off_part);
+    float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
+    float* spart = reinterpret_cast<float*>(w + pl.off_s);
+    o.rows = reinterpret_cast<GradRow*>(w + pl.off_rows);
+    o.counters = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
+    const int items = npairs * pl.P;
+    const int wgs = std::min(kItemMaxWGs, (items + kWaves - 1) / kWaves);
+    DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
+                  target, V, pl.P, items, part, o.counters, npairs);
+    DSPARK_LAUNCH("stats_grad_part2", (stats_grad_part2_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
+                  draft, target, V, pl.P, items, part, l1part, spart, o);
+    DSPARK_LAUNCH("stats_grad_write", (stats_grad_write_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
+                  draft, target, V, pl.P, items, o.rows, grad);
+  } else {
+    const dim3 grid(static_cast<unsigned>(npairs));
+    if (vec)
+      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, true>), grid, dim3(kThreads), 0, st,
+                    draft, target, V, o, grad);
+    else
+      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, false>), grid, dim3(kThreads), 0, st,
+                    draft, target, V, o, grad);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+StatsGradPlan plan_stats_backward(int32_t N, int32_t gamma, int32_t V) {
+  StatsGradPlan p{};
+  const int64_t npairs = static_cast<int64_t>(N) * gamma;
+  p.P = (V + stat_seg<uint16_t>() - 1) / stat_seg<uint16_t>();
+  const int Pf = (V + stat_seg<float>() - 1) / stat_seg<float>();
+  const int Pmax = p.P > Pf ? p.P : Pf;
+  p.sliced = npairs > 0 && npairs < kSlicedMaxPairs;
+  size_t off = 0;
+  if (p.sliced) {
+    const size_t items = static_cast<size_t>(npairs) * Pmax;
+    p.off_part = off;
+    off = align_up(off + items * sizeof(StatPart), 256);
+    p.off_l1 = off;
+    off = align_up(off + items * sizeof(float), 256);
+    p.off_s = off;
+    off = align_up(off + items * sizeof(float), 256);
+    p.off_rows = off;
+    off = align_up(off + static_cast<size_t>(npairs) * sizeof(GradRow), 256);
+    p.off_cnt = off;
+    off = align_up(off + static_cast<size_t>(npairs) * kTicketStride * sizeof(uint32_t), 256);
+  }
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_stats_backward(const void* draft, const void* target, int dtype, const int32_t* teacher,
+                                 const float* conf_logits, const uint8_t* block_mask, int32_t N,
+                                 int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf,
+                                 const float* grad_scale, void* grad_draft, float* grad_conf, void* ws,
+                                 const StatsGradPlan& plan, hipStream_t st) {
+  GradArgs o{teacher, conf_logits, block_mask, grad_scale, gamma, w_ce, w_l1, w_conf, grad_conf,
+             nullptr, nullptr};
+  StatsGradPlan pl = plan;
+  if (dtype == DSPARK_BF16) {
+    pl.P = (V + stat_seg<uint16_t>() - 1) / stat_seg<uint16_t>();
+    return launch_backward_typed(static_cast<const uint16_t*>(draft), static_cast<const uint16_t*>(target),
+                                 N, gamma, V, o, static_cast<uint16_t*>(grad_draft), ws, pl, st);
+  }
+  pl.P = (V + stat_seg<float>() - 1) / stat_seg<float>();
+  return launch_backward_typed(static_cast<const float*>(draft), static_cast<const float*>(target), N,
+                               gamma, V, o, static_cast<float*>(grad_draft), ws, pl, st);
+}
 
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
   StatsPlan p{};

@@ -167,7 +167,7 @@ typedef struct dspark_policy {
 } dspark_policy;
 
 /* ---- workspace sizing ------------------------------------------------------ */
-enum { DSPARK_OP_MARKOV = 1, DSPARK_OP_VERIFY = 2, DSPARK_OP_STATS = 3 };
+enum { DSPARK_OP_MARKOV = 1, DSPARK_OP_VERIFY = 2, DSPARK_OP_STATS = 3, DSPARK_OP_STATS_BACKWARD = 4 };
 
 /* Bytes of device workspace one call of `op` needs at these sizes (for
  * DSPARK_OP_STATS pass N as B; r and d are ignored where they do not apply).
@@ -349,6 +349,43 @@ dspark_status dspark_accept_stats(
     const uint8_t* block_mask, int32_t N, int32_t gamma, int32_t V,
     float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
     float* ce, float* bce, float* tau, float* sums, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dspark_accept_stats_backward
+ *
+ * [MB] "Training objective" (the draft is trained by w_ce CE + w_l1 raw L1;
+ * the BCE term trains the confidence head against the acceptance label; the
+ * target distribution is detached) and "Memory contract for the
+ * full-vocabulary terms" (the row chunks are recomputed in the backward).
+ * The gradient of scale * sums[0] of dspark_accept_stats (same inputs and
+ * weights), with the label a held fixed in the BCE:
+ *   grad_draft[b,k-1,v] = scale m_b w_k [ w_ce (P_v - [v == teacher])
+ *                                        + w_l1 P_v (s_v - sum_u s_u P_u) ]
+ *   grad_conf[b,k-1]    = scale m_b w_k w_conf (sigmoid(c) - a)
+ * with P, T, a, w_k, m_b as in dspark_accept_stats, s_u = sign(P_u - T_u)
+ * and sign(0) = 0 (the subgradient of |x| that vanishes at 0).  No gradient
+ * is produced for the target rows.  Each row pair is read three times
+ * (normalisers; L1 and S; the gradient row), the gradient written once.
+ *
+ * Inputs
+ *   draft_logits, target_logits, teacher, conf_logits, block_mask, N, gamma,
+ *   V, w_ce, w_l1, w_conf   as dspark_accept_stats
+ *   grad_scale  device float32 scalar or NULL (1): the upstream gradient of
+ *               the numerator (for example 1 / num_tokens of the loss)
+ * Outputs
+ *   grad_draft  [N, gamma, V] in logits_dtype (bf16: rounded to nearest even)
+ *   grad_conf   [N, gamma] float32
+ * Workspace: dspark_workspace_size(DSPARK_OP_STATS_BACKWARD, N, gamma, V, 0, 0)
+ * (0 is valid when it returns 0).  Errors: as dspark_accept_stats.  N = 0 is
+ * a no-op.
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_accept_stats_backward(
+    const void* draft_logits, const void* target_logits, int logits_dtype,
+    const int32_t* teacher, const float* conf_logits,
+    const uint8_t* block_mask, int32_t N, int32_t gamma, int32_t V,
+    float w_ce, float w_l1, float w_conf, const float* grad_scale,
+    void* grad_draft, float* grad_conf, void* workspace,
     size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

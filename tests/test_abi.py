@@ -59,6 +59,25 @@ def stats(L, N=4, gamma=5, V=1024, dtype=1, sums=FAKE):
                                  FAKE, FAKE, FAKE, FAKE, FAKE, sums, None, 0, None)
 
 
+def stats_bwd(L, N=4, gamma=5, V=1024, dtype=1, grad=FAKE, ws=FAKE, wsb=1 << 30):
+    return L.dspark_accept_stats_backward(FAKE, FAKE, dtype, FAKE, FAKE, None, N, gamma, V, 0.1, 0.9,
+                                          1.0, None, grad, FAKE, ws, wsb, None)
+
+
+def test_stats_backward_validation(L):
+    assert stats_bwd(L, N=-1) == ds.DSPARK_EINVAL
+    assert stats_bwd(L, gamma=0) == ds.DSPARK_EINVAL
+    assert stats_bwd(L, dtype=9) == ds.DSPARK_EDTYPE
+    assert stats_bwd(L, gamma=17) == ds.DSPARK_ESHAPE
+    assert stats_bwd(L, grad=None) == ds.DSPARK_EINVAL
+    assert stats_bwd(L, ws=None) == ds.DSPARK_EWORKSPACE
+    assert stats_bwd(L, wsb=16) == ds.DSPARK_EWORKSPACE
+    assert stats_bwd(L, N=0, grad=None, ws=None) == ds.DSPARK_OK
+    # the row path (many pairs) needs no workspace
+    assert ds.dspark_workspace_size(ds.DSPARK_OP_STATS_BACKWARD, 2048, 7, 129280) == 0
+    assert ds.dspark_workspace_size(ds.DSPARK_OP_STATS_BACKWARD, 64, 5, 129280) > 0
+
+
 def width(L, B=4, gamma=5, conf=FAKE, cost=FAKE, out=FAKE):
     return L.dspark_select_width(conf, cost, B, gamma, out, None, None)
 
