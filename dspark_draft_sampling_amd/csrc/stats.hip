@@ -14,6 +14,7 @@
 // the L1 term.  stats_reduce: one workgroup computes tau and the sums in fp64
 // in a fixed order, so the sums are deterministic.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -23,6 +24,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// Row path: one workgroup of kRowThreads per compute unit, each looping over
+// row pairs, so that the pairs being read at once (one per CU, 0.5 MB each at
+// V = 129280 in bf16) stay within the 256 MB Infinity Cache and the later
+// looks at a pair are served from it rather than from HBM.
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kUnroll = 4;
 constexpr int kItemMaxWGs = 2048;      // grid of the sliced item kernels
 constexpr int kSlicedMaxPairs = 2048;  // row pairs below which the sliced path is used
@@ -74,14 +81,16 @@ __device__ __forceinline__ void online(float& m, float& s, const float* x, int n
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void stats_rows_kernel(
+__global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, const int32_t* __restrict__ teacher,
-    const float* __restrict__ conf_logits, int32_t V, float* __restrict__ l1,
+    const float* __restrict__ conf_logits, int32_t V, int32_t npairs, float* __restrict__ l1,
     float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
   using L = Vec8<T, VEC>;
   constexpr int EPL = L::N;
+  constexpr int kThreads = kRowThreads, kWaves = kRowWaves;
   __shared__ float shv[kWaves];
-  const size_t row = blockIdx.x;
+  for (int rr = blockIdx.x; rr < npairs; rr += gridDim.x) {
+  const size_t row = static_cast<size_t>(rr);
   const T* dr = draft + row * V;
   const T* tr = target + row * V;
   const int step = kThreads * EPL;
@@ -152,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void stats_rows_kernel(
     accept_rate[row] = a;
     ce[row] = lse_d - load_logit(dr, tch);
     bce[row] = fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
+  }
   }
 }
 
@@ -684,64 +694,133 @@ __global__ __launch_bounds__(kThreads) void stats_grad_write_kernel(
   }
 }
 
-// Row path: one workgroup per row pair, the three looks in turn.
+// Row path: one persistent workgroup per compute unit, the three looks of
+// each of its row pairs in turn.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void stats_grad_rows_kernel(const T* __restrict__ draft,
-                                                                   const T* __restrict__ target,
-                                                                   int32_t V, GradArgs o,
-                                                                   T* __restrict__ grad) {
+__global__ __launch_bounds__(kRowThreads) void stats_grad_rows_kernel(const T* __restrict__ draft,
+                                                                      const T* __restrict__ target,
+                                                                      int32_t V, int32_t npairs, GradArgs o,
+                                                                      T* __restrict__ grad) {
   using L = Vec8<T, VEC>;
   constexpr int EPL = L::N;
+  constexpr int kWaves = kRowWaves;
   __shared__ float shv[kWaves];
-  const size_t row = blockIdx.x;
-  const T* dr = draft + row * V;
-  const T* tr = target + row * V;
-  T* gr = grad + row * V;
-  const int step = kThreads * EPL;
-
-  float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
-  for (int e = threadIdx.x * EPL; e < V; e += step) {
-    float xd[EPL], xt[EPL];
-    L::load(dr + e, xd);
-    L::load(tr + e, xt);
-    online(md, sd, xd, EPL);
-    online(mt, st, xt, EPL);
-  }
-  const float Md = block_max<kWaves>(md, shv);
-  const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
-  const float Mt = block_max<kWaves>(mt, shv);
-  const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
-  const float shd = Md > neg_inf() ? Md * kLog2e : 0.0f, sht = Mt > neg_inf() ? Mt * kLog2e : 0.0f;
-  const float isd = 1.0f / Sd, ist = 1.0f / St;
-
-  float l1 = 0.0f, sv = 0.0f;
-  for (int e = threadIdx.x * EPL; e < V; e += step) {
-    float xd[EPL], xt[EPL];
-    L::load(dr + e, xd);
-    L::load(tr + e, xt);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) l1_and_s(xd[j], xt[j], shd, isd, sht, ist, l1, sv);
-  }
-  const float L1 = block_sum<kWaves>(l1, shv);
-  const float S = block_sum<kWaves>(sv, shv);
   __shared__ GradRow shr;
-  if (threadIdx.x == 0) shr = grad_row(o, static_cast<int>(row), shd, Sd, sht, St, L1, S, V);
-  __syncthreads();
-  const GradRow r = shr;
+  const int step = kRowThreads * EPL;
+  for (int rr = blockIdx.x; rr < npairs; rr += gridDim.x) {
+    const size_t row = static_cast<size_t>(rr);
+    const T* dr = draft + row * V;
+    const T* tr = target + row * V;
+    T* gr = grad + row * V;
 
-  for (int e = threadIdx.x * EPL; e < V; e += step) {
-    float xd[EPL], xt[EPL], g[EPL];
-    L::load(dr + e, xd);
-    L::load(tr + e, xt);
+    float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
+    int e = threadIdx.x * EPL;
+    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
+      float xd[kUnroll][EPL], xt[kUnroll][EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[j], xt[j], e + j);
-    if constexpr (VEC) {
-      store16<T>(gr + e, g);
-    } else {
-      if constexpr (sizeof(T) == 2) gr[e] = bf16_rne(g[0]);
-      else gr[e] = g[0];
+      for (int u = 0; u < kUnroll; ++u) {
+        L::load(dr + e + u * step, xd[u]);
+        L::load(tr + e + u * step, xt[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        online(md, sd, xd[u], EPL);
+        online(mt, st, xt[u], EPL);
+      }
+    }
+    for (; e < V; e += step) {
+      float xd[EPL], xt[EPL];
+      L::load(dr + e, xd);
+      L::load(tr + e, xt);
+      online(md, sd, xd, EPL);
+      online(mt, st, xt, EPL);
+    }
+    const float Md = block_max<kWaves>(md, shv);
+    const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
+    const float Mt = block_max<kWaves>(mt, shv);
+    const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
+    const float shd = Md > neg_inf() ? Md * kLog2e : 0.0f, sht = Mt > neg_inf() ? Mt * kLog2e : 0.0f;
+    const float isd = 1.0f / Sd, ist = 1.0f / St;
+
+    float l1 = 0.0f, sv = 0.0f;
+    e = threadIdx.x * EPL;
+    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
+      float xd[kUnroll][EPL], xt[kUnroll][EPL];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        L::load(dr + e + u * step, xd[u]);
+        L::load(tr + e + u * step, xt[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) l1_and_s(xd[u][j], xt[u][j], shd, isd, sht, ist, l1, sv);
+    }
+    for (; e < V; e += step) {
+      float xd[EPL], xt[EPL];
+      L::load(dr + e, xd);
+      L::load(tr + e, xt);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) l1_and_s(xd[j], xt[j], shd, isd, sht, ist, l1, sv);
+    }
+    const float L1 = block_sum<kWaves>(l1, shv);
+    const float S = block_sum<kWaves>(sv, shv);
+    if (threadIdx.x == 0) shr = grad_row(o, static_cast<int>(row), shd, Sd, sht, St, L1, S, V);
+    __syncthreads();
+    const GradRow r = shr;
+
+    e = threadIdx.x * EPL;
+    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
+      float xd[kUnroll][EPL], xt[kUnroll][EPL];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        L::load(dr + e + u * step, xd[u]);
+        L::load(tr + e + u * step, xt[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float g[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[u][j], xt[u][j], e + u * step + j);
+        if constexpr (VEC) {
+          store16<T>(gr + e + u * step, g);
+        } else {
+          if constexpr (sizeof(T) == 2) gr[e + u * step] = bf16_rne(g[0]);
+          else gr[e + u * step] = g[0];
+        }
+      }
+    }
+    for (; e < V; e += step) {
+      float xd[EPL], xt[EPL], g[EPL];
+      L::load(dr + e, xd);
+      L::load(tr + e, xt);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[j], xt[j], e + j);
+      if constexpr (VEC) {
+        store16<T>(gr + e, g);
+      } else {
+        if constexpr (sizeof(T) == 2) gr[e] = bf16_rne(g[0]);
+        else gr[e] = g[0];
+      }
     }
   }
+}
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < kMaxDev) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 template <typename T>
@@ -769,13 +848,13 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                   target, V, pl.P, items, part, l1part, o);
     return hipGetLastError();
   } else if (npairs > 0) {
-    const dim3 grid(static_cast<unsigned>(npairs));
+    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus())));
     if (vec)
-      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, true>), grid, dim3(kThreads), 0, st, draft,
-                    target, teacher, conf_logits, V, l1, accept_rate, ce, bce);
+      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, true>), grid, dim3(kRowThreads), 0, st, draft,
+                    target, teacher, conf_logits, V, npairs, l1, accept_rate, ce, bce);
     else
-      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, false>), grid, dim3(kThreads), 0, st,
-                    draft, target, teacher, conf_logits, V, l1, accept_rate, ce, bce);
+      DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, false>), grid, dim3(kRowThreads), 0, st,
+                    draft, target, teacher, conf_logits, V, npairs, l1, accept_rate, ce, bce);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -810,13 +889,13 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
     DSPARK_LAUNCH("stats_grad_write", (stats_grad_write_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
                   draft, target, V, pl.P, items, o.rows, grad);
   } else {
-    const dim3 grid(static_cast<unsigned>(npairs));
+    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus())));
     if (vec)
-      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, true>), grid, dim3(kThreads), 0, st,
-                    draft, target, V, o, grad);
+      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, true>), grid, dim3(kRowThreads), 0, st,
+                    draft, target, V, npairs, o, grad);
     else
-      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, false>), grid, dim3(kThreads), 0, st,
-                    draft, target, V, o, grad);
+      DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, false>), grid, dim3(kRowThreads), 0,
+                    st, draft, target, V, npairs, o, grad);
   }
   return hipGetLastError();
 }
