@@ -540,9 +540,11 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// A pair's coefficients: P_v = 2^(x log2e - shd) isd, T_v likewise.
+// A pair's coefficients: P_v = 2^(x log2e - shd) isd, and
+// log2 P_v - log2 T_v = (x - y) log2e - lr (lr: the pair's log2 ratio of the
+// two normalisers), so the sign of P_v - T_v needs no second exponential.
 struct GradRow {
-  float shd, isd, sht, ist;
+  float shd, isd, lr;
   float S, a_ce, a_l1;
   int32_t teacher;
 };
@@ -570,8 +572,9 @@ __device__ __forceinline__ GradRow grad_row(const GradArgs& g, int pair, float s
   const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
   const float c = g.conf_logits[pair];
   g.grad_conf[pair] = alpha * g.w_conf * (1.0f / (1.0f + expf(-c)) - a);
-  return GradRow{shd, 1.0f / Sd, sht, 1.0f / St, S, alpha * g.w_ce, alpha * g.w_l1,
-                 clamp_token(g.teacher[pair], V)};
+  // log2 P_v - log2 T_v = (x - y) log2e - [(shd + log2 Sd) - (sht + log2 St)]
+  const float lr = (shd + __log2f(Sd)) - (sht + __log2f(St));
+  return GradRow{shd, 1.0f / Sd, lr, S, alpha * g.w_ce, alpha * g.w_l1, clamp_token(g.teacher[pair], V)};
 }
 
 __device__ __forceinline__ void l1_and_s(float x, float y, float shd, float isd, float sht, float ist,
@@ -584,8 +587,8 @@ __device__ __forceinline__ void l1_and_s(float x, float y, float shd, float isd,
 
 __device__ __forceinline__ float grad_elem(const GradRow& r, float x, float y, int v) {
   const float P = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r.shd)) * r.isd;
-  const float T = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -r.sht)) * r.ist;
-  const float sg = P > T ? 1.0f : (P < T ? -1.0f : 0.0f);
+  const float dl = fmaf(x - y, kLog2e, -r.lr);  // NaN (both -inf: P = 0) gives sign 0
+  const float sg = dl > 0.0f ? 1.0f : (dl < 0.0f ? -1.0f : 0.0f);
   return r.a_ce * (P - (v == r.teacher ? 1.0f : 0.0f)) + r.a_l1 * P * (sg - r.S);
 }
 
