@@ -115,6 +115,15 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
 
 
 PROFILE = os.path.join(ROOT, "profiles", "decode_step_B64_g5_V129280.md")
+# profile summaries per workload: (file, title, bench arguments of the run)
+PROFILES = {
+    "decode": (PROFILE, "Decode step (Markov sample + verify + accept stats), B=64, gamma=5, "
+                        "V=129280, bf16, sampled", ""),
+    "train": (os.path.join(ROOT, "profiles", "stats_train_N2048_g7_V129280.md"),
+              "Training statistics and their gradient (dspark_accept_stats + "
+              "dspark_accept_stats_backward), 2048 blocks x gamma 7, V=129280, bf16",
+              " --workload train"),
+}
 CSRC = os.path.join(ROOT, "dspark_draft_sampling_amd", "csrc")
 
 
@@ -149,9 +158,10 @@ def counter_traffic(kernel):
     return int(k["read_bytes"] + k["write_bytes"])
 
 
-def summarize_profile(base, out):
+def summarize_profile(base, workload="decode"):
     """Write the rocprofv3 summary (kernel trace + copy-calibrated HBM
-    counters) of a profiling run whose outputs are under `base`."""
+    counters) of a profiling run of `workload` whose outputs are under
+    `base`."""
     import collections
     import csv
 
@@ -162,7 +172,8 @@ def summarize_profile(base, out):
                 d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in d.items()}
 
-    ours = ("markov", "verify", "stats")
+    out, title, wl = PROFILES[workload]
+    ours = ("markov", "verify", "stats", "select_width")
     with open(f"{base}/prof_kt/kt_kernel_stats.csv") as fh:
         stats = [r for r in csv.DictReader(fh) if r["Name"].startswith(ours)]
     fetch = agg(f"{base}/prof_FETCH_SIZE/p_counter_collection.csv")
@@ -172,15 +183,16 @@ def summarize_profile(base, out):
     cw = agg(f"{base}/prof_copy_WRITE_SIZE/p_counter_collection.csv")[copy]
     true_kib = 256 * 1024
     sf, sw = true_kib / cf, true_kib / cw
-    cmd = "python3 bench.py"
+    cmd = "python3 bench.py" + wl
+    steps = " --steps 10 --warmup 2" if workload == "train" else " --steps 50 --warmup 5"
     lines = [
-        "# Decode step (Markov sample + verify + accept stats), B=64, gamma=5, V=129280, bf16, sampled",
+        f"# {title}",
         "",
         "Commands, from the repository root after `cd /tmp && export TMPDIR=/tmp` (paths "
-        "absolute on the run; `python3 bench.py --summarize-profile gpurun_out` wrote this file):",
+        f"absolute on the run; `python3 bench.py{wl} --summarize-profile gpurun_out` wrote this file):",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats -T -f csv -d gpurun_out/prof_kt -o kt -- {cmd} --steps 50 --warmup 5 --no-cpu",
+        f"rocprofv3 --kernel-trace --stats -T -f csv -d gpurun_out/prof_kt -o kt -- {cmd}{steps} --no-cpu",
         f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
         f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d gpurun_out/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
         f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
@@ -270,7 +282,7 @@ def _roofline(kernels, headline):
 def main():
     args = parse()
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, PROFILE)
+        summarize_profile(args.summarize_profile, "train" if args.workload == "train" else "decode")
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
