@@ -61,8 +61,10 @@ double bf16_to_double(uint16_t h) {
 }
 
 // logits element `i` of an array of dtype 1 = bf16, 2 = fp32
+// dtype 1: bf16 bits, 2: float32, 3: binary64 (oracle-side rows only)
 double logit_at(const void* p, int dtype, size_t i) {
   if (dtype == 1) return bf16_to_double(static_cast<const uint16_t*>(p)[i]);
+  if (dtype == 3) return static_cast<const double*>(p)[i];
   return static_cast<double>(static_cast<const float*>(p)[i]);
 }
 
@@ -669,6 +671,14 @@ int32_t oracle_verify(const void* target, int32_t dtype,
 // supervised positions (reading); the mask is per block (reading).
 // sums[12] = {numerator, num_tokens, l1 sum, count, accept sum, count,
 //             tau sum, block count, ce sum, count, bce sum, count}.
+int32_t oracle_accept_stats2(const void* draft, int32_t ddtype, const void* target,
+                             int32_t dtype, const int32_t* teacher,
+                             const float* conf_logits, const uint8_t* block_mask,
+                             int32_t N, int32_t gamma, int32_t V, double w_ce,
+                             double w_l1, double w_conf, double* l1,
+                             double* accept_rate, double* ce, double* bce,
+                             double* tau, double* sums);
+
 int32_t oracle_accept_stats(const void* draft, const void* target,
                             int32_t dtype, const int32_t* teacher,
                             const float* conf_logits, const uint8_t* block_mask,
@@ -676,6 +686,18 @@ int32_t oracle_accept_stats(const void* draft, const void* target,
                             double w_l1, double w_conf, double* l1,
                             double* accept_rate, double* ce, double* bce,
                             double* tau, double* sums) {
+  return oracle_accept_stats2(draft, dtype, target, dtype, teacher, conf_logits, block_mask, N,
+                              gamma, V, w_ce, w_l1, w_conf, l1, accept_rate, ce, bce, tau, sums);
+}
+
+// The same statistics with the draft rows in their own dtype (ddtype).
+int32_t oracle_accept_stats2(const void* draft, int32_t ddtype, const void* target,
+                             int32_t dtype, const int32_t* teacher,
+                             const float* conf_logits, const uint8_t* block_mask,
+                             int32_t N, int32_t gamma, int32_t V, double w_ce,
+                             double w_l1, double w_conf, double* l1,
+                             double* accept_rate, double* ce, double* bce,
+                             double* tau, double* sums) {
   if (N < 0 || gamma < 1 || V < 1) return 1;
   for (int i = 0; i < 12; ++i) sums[i] = 0.0;
   std::vector<double> dl, tl;
@@ -685,7 +707,7 @@ int32_t oracle_accept_stats(const void* draft, const void* target,
     for (int32_t k = 1; k <= gamma; ++k) {
       const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
       bool nf = false;
-      load_row(draft, dtype, row * V, V, &dl, &nf);
+      load_row(draft, ddtype, row * V, V, &dl, &nf);
       load_row(target, dtype, row * V, V, &tl, &nf);
       double md = kNegInf, mt = kNegInf;
       for (int32_t v = 0; v < V; ++v) {
@@ -736,6 +758,47 @@ int32_t oracle_accept_stats(const void* draft, const void* target,
     }
   }
   return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance statistics of the teacher-forced Markov draft ([MB]
+// "Semi-autoregressive draft": the sequential head adds a low-rank,
+// token-conditioned bias to the parallel logits and is teacher-forced with
+// the previous block tokens at training time; "Training objective").  The
+// draft row of block b at position k is
+//   backbone[b,k-1,:] + W1[x_{k-1}] . W2^T,
+// x_0 = anchor[b] and x_{k-1} = teacher[b,k-2] for k >= 2 (the true token
+// before position k; teacher[b,k-1] is the CE target of position k), both
+// clamped into [0, V); -inf backbone logits stay -inf.  The statistics are
+// then those of oracle_accept_stats on these rows (binary64 throughout).
+int32_t oracle_accept_stats_markov(const void* backbone, const void* target, int32_t dtype,
+                                   const int32_t* anchor, const uint16_t* A,
+                                   const uint16_t* Bt, int32_t r, const int32_t* teacher,
+                                   const float* conf_logits, const uint8_t* block_mask,
+                                   int32_t N, int32_t gamma, int32_t V, double w_ce,
+                                   double w_l1, double w_conf, double* l1,
+                                   double* accept_rate, double* ce, double* bce,
+                                   double* tau, double* sums) {
+  if (N < 0 || gamma < 1 || V < 1 || r < 0) return 1;
+  std::vector<double> draft(static_cast<size_t>(N) * gamma * V);
+  std::vector<double> a(r), bb;
+  for (int32_t b = 0; b < N; ++b)
+    for (int32_t k = 1; k <= gamma; ++k) {
+      const size_t row = static_cast<size_t>(b) * gamma + (k - 1);
+      const int32_t x = clamp_token(k == 1 ? anchor[b] : teacher[row - 1], V);
+      for (int32_t i = 0; i < r; ++i) a[i] = bf16_to_double(A[static_cast<size_t>(x) * r + i]);
+      bool nf = false;
+      load_row(backbone, dtype, row * V, V, &bb, &nf);
+      for (int32_t v = 0; v < V; ++v) {
+        double bias = 0.0;
+        for (int32_t i = 0; i < r; ++i)
+          bias += a[i] * bf16_to_double(Bt[static_cast<size_t>(v) * r + i]);
+        draft[row * V + v] = (bb[v] == kNegInf) ? kNegInf : bb[v] + bias;
+      }
+    }
+  return oracle_accept_stats2(draft.data(), 3, target, dtype, teacher, conf_logits, block_mask,
+                              N, gamma, V, w_ce, w_l1, w_conf, l1, accept_rate, ce, bce, tau,
+                              sums);
 }
 
 // ---------------------------------------------------------------------------

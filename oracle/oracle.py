@@ -65,6 +65,12 @@ def _declare(L):
     L.oracle_accept_stats.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, f64,
                                       f64, P, P, P, P, P, P]
     L.oracle_accept_stats.restype = i32
+    L.oracle_accept_stats2.argtypes = [P, i32, P, i32, P, P, P, i32, i32, i32, f64, f64, f64,
+                                       P, P, P, P, P, P]
+    L.oracle_accept_stats2.restype = i32
+    L.oracle_accept_stats_markov.argtypes = [P, P, i32, P, P, P, i32, P, P, P, i32, i32, i32, f64,
+                                             f64, f64, P, P, P, P, P, P]
+    L.oracle_accept_stats_markov.restype = i32
     L.oracle_accept_stats_backward.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, f64,
                                                f64, f64, P, P]
     L.oracle_accept_stats_backward.restype = i32
@@ -207,6 +213,47 @@ def accept_stats(inp, w_ce=0.1, w_l1=0.9, w_conf=1.0):
                                    _p(bm), N, g, V, w_ce, w_l1, w_conf, _p(out["l1"]),
                                    _p(out["accept_rate"]), _p(out["ce"]), _p(out["bce"]),
                                    _p(out["tau"]), _p(out["sums"]))
+    assert rc == 0
+    return out
+
+
+def _stats_out(N, g):
+    return dict(l1=np.zeros((N, g)), accept_rate=np.zeros((N, g)), ce=np.zeros((N, g)),
+                bce=np.zeros((N, g)), tau=np.zeros(N), sums=np.zeros(12))
+
+
+def accept_stats_f64_draft(draft64, inp, w_ce=0.1, w_l1=0.9, w_conf=1.0):
+    """The statistics with binary64 draft rows (test helper: feeds rows the
+    oracle itself produced, such as Markov z rows, without rounding)."""
+    N, g, V = inp["N"], inp["gamma"], inp["V"]
+    dr = np.ascontiguousarray(draft64, np.float64)
+    assert dr.shape == (N, g, V)
+    tg = _logits(inp["target"], inp["dtype"])
+    out = _stats_out(N, g)
+    rc = lib().oracle_accept_stats2(_p(dr), 3, _p(tg), DTYPES[inp["dtype"]], _p(_c(inp["teacher"], np.int32)),
+                                    _p(_c(inp["conf_logits"], np.float32)),
+                                    _p(_c(inp.get("block_mask"), np.uint8)), N, g, V, w_ce, w_l1,
+                                    w_conf, _p(out["l1"]), _p(out["accept_rate"]), _p(out["ce"]),
+                                    _p(out["bce"]), _p(out["tau"]), _p(out["sums"]))
+    assert rc == 0
+    return out
+
+
+def accept_stats_markov(inp, w_ce=0.1, w_l1=0.9, w_conf=1.0):
+    """Oracle of the statistics of the teacher-forced Markov draft: inp holds
+    backbone (the parallel logits, in place of draft), target, anchor, w1, w2,
+    r, teacher, conf_logits, block_mask, N, gamma, V, dtype."""
+    N, g, V, r = inp["N"], inp["gamma"], inp["V"], inp["r"]
+    bb = _logits(inp["backbone"], inp["dtype"])
+    tg = _logits(inp["target"], inp["dtype"])
+    assert bb.shape == (N, g, V) and tg.shape == (N, g, V)
+    out = _stats_out(N, g)
+    rc = lib().oracle_accept_stats_markov(
+        _p(bb), _p(tg), DTYPES[inp["dtype"]], _p(_c(inp["anchor"], np.int32)),
+        _p(_c(inp["w1"], np.uint16)), _p(_c(inp["w2"], np.uint16)), r,
+        _p(_c(inp["teacher"], np.int32)), _p(_c(inp["conf_logits"], np.float32)),
+        _p(_c(inp.get("block_mask"), np.uint8)), N, g, V, w_ce, w_l1, w_conf, _p(out["l1"]),
+        _p(out["accept_rate"]), _p(out["ce"]), _p(out["bce"]), _p(out["tau"]), _p(out["sums"]))
     assert rc == 0
     return out
 

@@ -34,6 +34,7 @@ __all__ = [
     "decode_inputs",
     "stats_inputs",
     "width_inputs",
+    "stats_markov_inputs",
 ]
 
 
@@ -251,4 +252,23 @@ def width_inputs(B=None, gamma=None, cfg=None, **overrides) -> dict:
     cost[0] = cfg["draft_cost"]
     cost[1:] = cfg["verify_base"] + cfg["verify_per_row"] * (np.arange(g + 1) + 1)
     return dict(B=B, gamma=g, confidence=conf, cost=cost)
+
+
+def stats_markov_inputs(cfg=None, blocks=None, r=256, w_std=0.02, mask_every=0, **overrides) -> dict:
+    """Inputs of the statistics of the teacher-forced Markov draft: the
+    statistics' rows, with the draft rows renamed `backbone` (the parallel
+    logits the Markov bias is added to), plus per block an anchor token and
+    the rank-r factors W1, W2 [V, r] (bf16, N(0, w_std^2)), drawn from
+    streams keyed like the rest."""
+    cfg = dict(STATS_CONFIG if cfg is None else cfg)
+    cfg.update(overrides)
+    inp = stats_inputs(cfg, blocks=blocks, mask_every=mask_every)
+    s, V = cfg["seed"], cfg["V"]
+    blks = list(range(cfg["N"])) if blocks is None else [int(b) for b in blocks]
+    inp["backbone"] = inp.pop("draft")
+    inp["anchor"] = np.array([_rng(s, 6, b).integers(0, V) for b in blks], np.int32)
+    inp["w1"] = to_bf16(_rng(s, 7).standard_normal((V, r), dtype=np.float32) * np.float32(w_std))
+    inp["w2"] = to_bf16(_rng(s, 8).standard_normal((V, r), dtype=np.float32) * np.float32(w_std))
+    inp["r"] = r
+    return inp
 
