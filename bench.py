@@ -51,7 +51,7 @@ def parse():
                     help="requests of the batch the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--workload", choices=["decode", "truncated", "wide_greedy", "adaptive", "stats",
-                                           "train"],
+                                           "train", "markov_stats"],
                     default="decode",
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
@@ -103,6 +103,10 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
         return 0
     if name in ("stats_pairs", "stats_reduce"):
         return 16 * B * g
+    if name == "stats_markov_look1":  # backbone + target rows, W2 once per token slice
+        return 2 * 2 * B * g * V + 2 * r * V
+    if name == "stats_markov_look2":  # second look: not compulsory
+        return 0
     if name == "stats_grad_rows":  # row pair read once, gradient row written once (bf16)
         return 3 * 2 * B * g * V
     if name == "stats_grad_write":  # the gradient row written (its reads are the third look)
@@ -298,7 +302,9 @@ def main():
 
     ds.markov_plan({"auto": ds.MARKOV_AUTO, "per-step": ds.MARKOV_PER_STEP,
                     "cooperative": ds.MARKOV_COOPERATIVE}[args.markov_plan])
-    if args.workload in ("stats", "train"):
+    if args.workload == "markov_stats":
+        line = run_markov_stats(args, torch, ds)
+    elif args.workload in ("stats", "train"):
         line = run_stats(args, torch, ds)
     else:
         line = run_decode(args, torch, ds)
@@ -480,6 +486,53 @@ def run_stats(args, torch, ds):
                             logits="bf16", rotated_batches=len(sets)),
                 roofline=_roofline(kernels, False), cpu_baseline=cpu,
                 step=dict(kernels=kernels))
+
+
+def run_markov_stats(args, torch, ds):
+    """Statistics of the teacher-forced Markov draft: 2048 blocks x gamma 7,
+    V = 129280, rank 256 (the bias formed on MFMA inside both looks)."""
+    from workloads import stats_markov_inputs
+
+    t0 = time.time()
+    inp = stats_markov_inputs()
+    N, g, V, r = inp["N"], inp["gamma"], inp["V"], inp["r"]
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = [dict(backbone=bf(inp["backbone"]), target=bf(inp["target"]))
+            for _ in range(max(1, min(args.rotate, 2)))]
+    anchor = torch.from_numpy(inp["anchor"]).to(dev)
+    w1, w2 = bf(inp["w1"]), bf(inp["w2"])
+    teacher = torch.from_numpy(inp["teacher"]).to(dev)
+    conf = torch.from_numpy(inp["conf_logits"]).to(dev)
+    out = ds.dspark_accept_stats_markov(sets[0]["backbone"], sets[0]["target"], anchor, w1, w2, teacher,
+                                        conf)
+    it = [0]
+
+    def step():
+        x = sets[it[0] % len(sets)]
+        it[0] += 1
+        ds.dspark_accept_stats_markov(x["backbone"], x["target"], anchor, w1, w2, teacher, conf, out=out)
+
+    ms_total, wall = _timed(step, args, torch)
+    ms_per_step = ms_total / args.steps
+    value = N * g * args.steps / (ms_total / 1e3)
+    kernels = _kernels(step, args, torch, ds, lambda n: kernel_bytes(n, N, g, V, r, 0, 0, 0))
+    flops = 2.0 * N * g * V * r  # the bias of one look
+    for name in ("stats_markov_look1", "stats_markov_look2"):
+        if name in kernels:
+            kernels[name]["mfma_tflops"] = round(flops / (kernels[name]["avg_us"] * 1e-6) / 1e12, 1)
+    return dict(metric=f"teacher-forced Markov stats rows/sec (N×γ row pairs) at V={V},N={N},γ={g},r={r}",
+                value=round(value, 1), unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="acceptance statistics of the teacher-forced Markov draft", N=N,
+                            gamma=g, V=V, r=r, logits="bf16", rotated_batches=len(sets)),
+                roofline=_roofline(kernels, False), cpu_baseline=None,
+                step=dict(kernels=kernels, bias_gflop_per_look=round(flops / 1e9, 1)))
 
 
 def cpu_baseline(inp, nreq, cfg_name="decode"):

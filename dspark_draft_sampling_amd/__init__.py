@@ -27,10 +27,12 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_ESHAPE, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(6)
 DSPARK_BF16, DSPARK_F32 = 1, 2
 DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS, DSPARK_OP_STATS_BACKWARD = 1, 2, 3, 4
+DSPARK_OP_STATS_MARKOV = 5
 FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
 
 __all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
-           "dspark_accept_stats", "dspark_accept_stats_backward", "dspark_select_width", "dspark_workspace_size", "profile_enable",
+           "dspark_accept_stats", "dspark_accept_stats_backward", "dspark_accept_stats_markov",
+           "dspark_select_width", "dspark_workspace_size", "profile_enable",
            "profile_summary"]
 
 
@@ -69,6 +71,9 @@ def lib():
         L.dspark_accept_stats.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32, f32,
                                           P, P, P, P, P, P, P, sz, P]
         L.dspark_accept_stats.restype = C.c_int
+        L.dspark_accept_stats_markov.argtypes = [P, P, C.c_int, P, P, P, i32, P, P, P, i32, i32, i32,
+                                                 f32, f32, f32, P, P, P, P, P, P, P, sz, P]
+        L.dspark_accept_stats_markov.restype = C.c_int
         L.dspark_accept_stats_backward.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32,
                                                    f32, P, P, P, P, sz, P]
         L.dspark_accept_stats_backward.restype = C.c_int
@@ -256,6 +261,46 @@ def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_
                                    _p(out["ce"]), _p(out["bce"]), _p(out["tau"]),
                                    _p(out["sums"]), _p(ws), 0 if ws is None else ws.numel(),
                                    _stream(dev))
+    _check(rc)
+    return out
+
+
+def dspark_accept_stats_markov(backbone, target, anchor, markov_w1, markov_w2, teacher, conf_logits,
+                               block_mask=None, w_ce=0.1, w_l1=0.9, w_conf=1.0, out=None):
+    """Statistics of the teacher-forced Markov draft (backbone + W1[x] W2^T,
+    x the anchor then the teacher tokens); returns the same dict as
+    dspark_accept_stats."""
+    dt = _logits_dtype(backbone, "backbone")
+    _dev_tensor(backbone, backbone.dtype, "backbone")
+    _dev_tensor(target, backbone.dtype, "target")
+    N, g, V = backbone.shape
+    if target.shape != backbone.shape:
+        raise DSparkError("accept_stats_markov: backbone and target shapes differ")
+    _dev_tensor(anchor, torch.int32, "anchor")
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1")
+    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2")
+    r = markov_w1.shape[1]
+    if markov_w1.shape != (V, r) or markov_w2.shape != (V, r):
+        raise DSparkError("accept_stats_markov: markov_w1 and markov_w2 must be [V, r]")
+    _dev_tensor(teacher, torch.int32, "teacher")
+    _dev_tensor(conf_logits, torch.float32, "conf_logits")
+    if block_mask is not None:
+        _dev_tensor(block_mask, torch.uint8, "block_mask")
+    dev = backbone.device
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        out = dict(l1=torch.empty((N, g), **f), accept_rate=torch.empty((N, g), **f),
+                   ce=torch.empty((N, g), **f), bce=torch.empty((N, g), **f),
+                   tau=torch.empty((N,), **f), sums=torch.empty((12,), **f))
+    nb = dspark_workspace_size(DSPARK_OP_STATS_MARKOV, N, g, V, r)
+    ws = _workspace(DSPARK_OP_STATS_MARKOV, dev, nb) if nb > 0 else None
+    rc = lib().dspark_accept_stats_markov(_p(backbone), _p(target), dt, _p(anchor), _p(markov_w1),
+                                          _p(markov_w2), r, _p(teacher), _p(conf_logits),
+                                          _p(block_mask), N, g, V, float(w_ce), float(w_l1),
+                                          float(w_conf), _p(out["l1"]), _p(out["accept_rate"]),
+                                          _p(out["ce"]), _p(out["bce"]), _p(out["tau"]),
+                                          _p(out["sums"]), _p(ws), 0 if ws is None else ws.numel(),
+                                          _stream(dev))
     _check(rc)
     return out
 

@@ -49,6 +49,8 @@ size_t dspark_workspace_size(int op, int32_t B, int32_t gamma, int32_t V, int32_
       return dspark::plan_stats(B, gamma, V).bytes;
     case DSPARK_OP_STATS_BACKWARD:
       return dspark::plan_stats_backward(B, gamma, V).bytes;
+    case DSPARK_OP_STATS_MARKOV:
+      return dspark::plan_stats_markov(B, gamma, V).bytes;
     default:
       return 0;
   }
@@ -146,6 +148,35 @@ dspark_status dspark_accept_stats(const void* draft_logits, const void* target_l
       draft_logits, target_logits, logits_dtype, teacher, conf_logits, block_mask, N, gamma, V,
       w_ce, w_l1, w_conf, l1, accept_rate, ce, bce, tau, sums, workspace, plan,
       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
+}
+
+dspark_status dspark_accept_stats_markov(const void* backbone_logits, const void* target_logits,
+                                         int logits_dtype, const int32_t* anchor,
+                                         const uint16_t* markov_w1, const uint16_t* markov_w2,
+                                         int32_t r, const int32_t* teacher, const float* conf_logits,
+                                         const uint8_t* block_mask, int32_t N, int32_t gamma,
+                                         int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
+                                         float* accept_rate, float* ce, float* bce, float* tau,
+                                         float* sums, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  if (N < 0) return DSPARK_EINVAL;
+  dspark_status s = check_common(logits_dtype, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if (r <= 0) return DSPARK_EINVAL;
+  if (r > DSPARK_MAX_RANK || r % 16 != 0) return DSPARK_ESHAPE;
+  if (!sums) return DSPARK_EINVAL;
+  if (N > 0 && (!backbone_logits || !target_logits || !anchor || !markov_w1 || !markov_w2 ||
+                !teacher || !conf_logits || !l1 || !accept_rate || !ce || !bce || !tau))
+    return DSPARK_EINVAL;
+  if (N > 0 && (!aligned16(markov_w1) || !aligned16(markov_w2))) return DSPARK_EINVAL;
+  if (static_cast<int64_t>(N) * gamma > 0x7fffffffLL) return DSPARK_ESHAPE;
+  const dspark::StatsMarkovPlan plan = dspark::plan_stats_markov(N, gamma, V);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return DSPARK_EWORKSPACE;
+  const hipError_t e = dspark::launch_stats_markov(
+      backbone_logits, target_logits, logits_dtype, anchor, markov_w1, markov_w2, r, teacher,
+      conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf, l1, accept_rate, ce, bce, tau, sums,
+      workspace, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
 }
 

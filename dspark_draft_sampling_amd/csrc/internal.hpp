@@ -100,6 +100,25 @@ struct StatsPlan {
 };
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 
+// Batch reduction of the per-position statistics (tau and the sums), shared by
+// the statistics calls (stats.hip).
+hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,
+                               const uint8_t* block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,
+                               float w_conf, float* tau, float* sums, hipStream_t st);
+
+// Statistics of the teacher-forced Markov draft (stats_markov.hip).
+struct StatsMarkovPlan {
+  int G;  // token slices (workgroups of the look kernels)
+  size_t off_rec, off_norm, off_l1, off_dt, bytes;
+};
+StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V);
+hipError_t launch_stats_markov(const void* backbone, const void* target, int dtype, const int32_t* anchor,
+                               const uint16_t* w1, const uint16_t* w2, int32_t r, const int32_t* teacher,
+                               const float* conf_logits, const uint8_t* block_mask, int32_t N, int32_t gamma,
+                               int32_t V, float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
+                               float* ce, float* bce, float* tau, float* sums, void* ws,
+                               const StatsMarkovPlan& pl, hipStream_t st);
+
 // Gradient of the statistics' loss numerator (stats.hip).
 struct StatsGradPlan {
   int sliced;  // 1: (row pair, segment) item kernels; 0: one workgroup per row pair

@@ -905,6 +905,14 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
 
 }  // namespace
 
+hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,
+                               const uint8_t* block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,
+                               float w_conf, float* tau, float* sums, hipStream_t st) {
+  DSPARK_LAUNCH("stats_reduce", stats_reduce_kernel, dim3(1), dim3(kThreads), 0, st, l1, accept_rate, ce, bce,
+                block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums);
+  return hipGetLastError();
+}
+
 StatsGradPlan plan_stats_backward(int32_t N, int32_t gamma, int32_t V) {
   StatsGradPlan p{};
   const int64_t npairs = static_cast<int64_t>(N) * gamma;

@@ -1,0 +1,430 @@
+// stats_markov.hip — acceptance statistics of the teacher-forced Markov draft
+// on gfx950.
+//
+// Semantics ("DSpark Speculative Decoding (Draft Training) Design",
+// "Semi-autoregressive draft": the Markov head adds a low-rank,
+// token-conditioned bias to the parallel logits and is teacher-forced with
+// the previous block tokens at training time; "Training objective",
+// "Acceptance and confidence"): the draft row of block b at position k is
+// backbone[b,k-1,:] + W1[x_{k-1}] . W2^T, x_0 the block's anchor and x_{k-1}
+// the teacher token of position k-1; the statistics are those of
+// dspark_accept_stats on these rows (definition in include/dspark.h).
+//
+// The bias is a dense contraction: per look 2 N gamma V r flops (949 GFLOP at
+// 2048 x 7 blocks, V = 129280, r = 256), on v_mfma_f32_16x16x32_bf16 with the
+// vocabulary as the M side.  As in the one-launch Markov sampler, workgroup g
+// owns 512 tokens and keeps their W2 rows in registers (the MFMA A
+// fragments) for the whole launch; it walks the rows in tiles of 64 (the N
+// side), staging the tile's W1 rows (selected by the forced tokens) in LDS,
+// and adds the bias to the backbone values it streams.  Two looks:
+//  * look 1: per (row, workgroup) the (max, sum exp) of the draft and target
+//    values of its tokens, and the draft value at the row's teacher token;
+//  * rows: the per-row normalisers from those records;
+//  * look 2: the bias again, and per (row, workgroup) the share of
+//    sum |P - T|;
+//  * final: per row L1, accept_rate, CE, BCE; then the batch reduction of
+//    the plain statistics.
+#include <algorithm>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dspark {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSmThreads = 512;  // 8 waves x 64 tokens
+constexpr int kSmWaves = kSmThreads / 64;
+constexpr int kSmMS = 4;         // 16-token MFMA row blocks per wave
+constexpr int kSmTokens = kSmWaves * 16 * kSmMS;
+constexpr int kSmTile = 64;      // rows per tile (MFMA N side)
+constexpr int kSmMaxR = DSPARK_MAX_RANK;
+constexpr int kSmPad = 8;
+
+struct SmRec {
+  float md, sd, mt, st;  // max and sum exp(x - max) of the draft and target values
+};
+
+struct SmArgs {
+  const void* backbone;
+  const void* target;
+  const int32_t* anchor;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const int32_t* teacher;
+  int32_t rows, gamma, V, r;
+  SmRec* rec;       // [rows][G] (look 1)
+  float* dteach;    // [rows]: the draft value at the teacher token (look 1)
+  SmRec* norm;      // [rows]: per-row normalisers (after look 1)
+  float* l1part;    // [rows][G] (look 2)
+};
+
+struct SmLds {
+  __attribute__((aligned(16))) uint16_t a[kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
+  float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];              // per (array, wave, row)
+};
+
+__device__ __forceinline__ float rows_max(float v) {
+  return __uint_as_float(rows_combine(__float_as_uint(v), [](uint32_t p, uint32_t q) {
+    return __float_as_uint(fmaxf(__uint_as_float(p), __uint_as_float(q)));
+  }));
+}
+
+template <typename T>
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+  uint2 u;
+  // vec: 4-aligned rows (one 8-byte load for a full quad)
+  __device__ void load(const uint16_t* p, int n, bool vec) {
+    if (vec && n >= 4) {
+      u = *reinterpret_cast<const uint2*>(p);
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = i < n ? p[i] : 0u;
+      u = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
+  __device__ float at(int i) const {
+    const uint32_t w = i < 2 ? u.x : u.y;
+    return (i & 1) ? bf_hi(w) : bf_lo(w);
+  }
+};
+template <>
+struct Quad<float> {
+  float4 u;
+  __device__ void load(const float* p, int n, bool vec) {
+    if (vec && n >= 4) u = *reinterpret_cast<const float4*>(p);
+    else u = make_float4(n > 0 ? p[0] : 0.f, n > 1 ? p[1] : 0.f, n > 2 ? p[2] : 0.f, n > 3 ? p[3] : 0.f);
+  }
+  __device__ float at(int i) const { return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w; }
+};
+
+// The forced token before row `row` (flattened b gamma + k - 1).
+__device__ __forceinline__ int32_t forced_token(const SmArgs& a, int row) {
+  const int k = row % a.gamma;  // k - 1
+  const int32_t x = k == 0 ? a.anchor[row / a.gamma] : a.teacher[row - 1];
+  return clamp_token(x, a.V);
+}
+
+// One look over the row tile [row0, row0 + 64) for the workgroup's tokens:
+// stages the W1 rows, forms the bias tile on MFMA, adds the backbone values
+// and calls epi(pass h, lane's row, d[16], t[16], token of element 0 of each
+// quad) for every 16-row pass.
+template <typename T, bool VEC, class Epi>
+__device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
+                                        int row0, SmLds& L, Epi&& epi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vb = tok0 + wave * 16 * kSmMS;
+  const int V = a.V, r = a.r;
+  const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
+  const T* bb = static_cast<const T*>(a.backbone);
+  const T* tg = static_cast<const T*>(a.target);
+
+  // stage the tile's W1 rows (MFMA B operand), four 16-byte pieces per
+  // thread and round; the pieces are L2-resident after the first tiles
+  const int pieces = kpad / 8;
+  constexpr int kRound = 4;
+  constexpr int kMaxPieces = kSmTile * (kSmMaxR / 8) / kSmThreads;
+  static_assert(kMaxPieces % kRound == 0, "staging rounds");
+#pragma unroll
+  for (int j0 = 0; j0 < kMaxPieces; j0 += kRound) {
+    uint4 stage[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int idx = tid + (j0 + j) * kSmThreads;
+      const int rt = idx / pieces, pc = idx - rt * pieces;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (rt < kSmTile && pc * 8 < r && row0 + rt < a.rows) {
+        const int32_t x = forced_token(a, row0 + rt);
+        val = *reinterpret_cast<const uint4*>(a.w1 + static_cast<size_t>(x) * r + pc * 8);
+      }
+      stage[j] = val;
+    }
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int idx = tid + (j0 + j) * kSmThreads;
+      const int rt = idx / pieces, pc = idx - rt * pieces;
+      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a + rt * ld + pc * 8) = stage[j];
+    }
+  }
+
+  // every pass's backbone and target values, in flight during the products
+  Quad<T> qd[4][kSmMS], qt[4][kSmMS];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int row = row0 + h * 16 + (lane & 15);
+    const size_t off = static_cast<size_t>(row < a.rows ? row : 0) * V;
+#pragma unroll
+    for (int ms = 0; ms < kSmMS; ++ms) {
+      const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+      const int n = row < a.rows ? (V - v0 < 4 ? (V - v0 > 0 ? V - v0 : 0) : 4) : 0;
+      qd[h][ms].load(bb + off + (n > 0 ? v0 : 0), n, VEC);
+      qt[h][ms].load(tg + off + (n > 0 ? v0 : 0), n, VEC);
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f32x4 acc[kSmMS];
+#pragma unroll
+    for (int ms = 0; ms < kSmMS; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
+      if (ks < ksteps) {
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a + (h * 16 + (lane & 15)) * ld + ks * 32 +
+                                                           (lane >> 4) * 8);
+#pragma unroll
+        for (int ms = 0; ms < kSmMS; ++ms)
+          acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms], 0, 0, 0);
+      }
+    }
+    // lane: tokens vb + ms 16 + 4 (lane >> 4) + i of row row0 + h 16 + (lane & 15)
+    float d[4 * kSmMS], t[4 * kSmMS];
+#pragma unroll
+    for (int ms = 0; ms < kSmMS; ++ms) {
+      const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = v0 + i < V;
+        d[ms * 4 + i] = in ? qd[h][ms].at(i) + acc[ms][i] : neg_inf();
+        t[ms * 4 + i] = in ? qt[h][ms].at(i) : neg_inf();
+      }
+    }
+    epi(h, row0 + h * 16 + (lane & 15), d, t, vb + 4 * (lane >> 4));
+  }
+}
+
+// W2 fragments of the wave's 16 MS tokens [vb, vb + 16 MS) (A operand).
+__device__ __forceinline__ void sm_load_w2(bf16x8 (&af)[kSmMS][kSmMaxR / 32], const uint16_t* w2, int vb, int V,
+                                           int r, int lane) {
+  const int ksteps = ((r + 31) & ~31) / 32;
+#pragma unroll
+  for (int ms = 0; ms < kSmMS; ++ms) {
+    const int v = vb + ms * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
+      const int k0 = ks * 32 + (lane >> 4) * 8;
+      bf16x8 f = {};
+      if (ks < ksteps && v < V && k0 < r) f = *reinterpret_cast<const bf16x8*>(w2 + static_cast<size_t>(v) * r + k0);
+      af[ms][ks] = f;
+    }
+  }
+}
+
+// Look 1: per (row, workgroup) record of the draft and target values'
+// (max, sum exp), and the draft value at the row's teacher token.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a) {
+  __shared__ SmLds L;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = g * kSmTokens;
+  bf16x8 af[kSmMS][kSmMaxR / 32];
+  sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
+  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
+    sm_tile<T, VEC>(a, af, tok0, row0, L, [&](int h, int row, const float* d, const float* t, int v00) {
+      // the teacher token's draft value, from the lane that holds it
+      if (row < a.rows) {
+        const int32_t tch = clamp_token(a.teacher[row], a.V);
+#pragma unroll
+        for (int ms = 0; ms < kSmMS; ++ms)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v00 + ms * 16 + i == tch) a.dteach[row] = d[ms * 4 + i];
+      }
+      float md = neg_inf(), mt = neg_inf();
+#pragma unroll
+      for (int e = 0; e < 4 * kSmMS; ++e) {
+        md = fmaxf(md, d[e]);
+        mt = fmaxf(mt, t[e]);
+      }
+      md = rows_max(md);
+      mt = rows_max(mt);
+      float sd = 0.0f, st = 0.0f;
+      if (md > neg_inf())
+#pragma unroll
+        for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f((d[e] - md) * kLog2e);
+      if (mt > neg_inf())
+#pragma unroll
+        for (int e = 0; e < 4 * kSmMS; ++e) st += __builtin_amdgcn_exp2f((t[e] - mt) * kLog2e);
+      sd = rows_sum(sd);
+      st = rows_sum(st);
+      if (lane < 16) {
+        const int n = h * 16 + lane;
+        L.m[0][wave][n] = md;
+        L.s[0][wave][n] = sd;
+        L.m[1][wave][n] = mt;
+        L.s[1][wave][n] = st;
+      }
+    });
+    __syncthreads();
+    if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
+      const int n = threadIdx.x;
+      float M[2], S[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float m = neg_inf();
+#pragma unroll
+        for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[q][w][n]);
+        float s = 0.0f;
+        if (m > neg_inf())
+#pragma unroll
+          for (int w = 0; w < kSmWaves; ++w)
+            if (L.m[q][w][n] > neg_inf()) s += L.s[q][w][n] * __builtin_amdgcn_exp2f((L.m[q][w][n] - m) * kLog2e);
+        M[q] = m;
+        S[q] = s;
+      }
+      a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{M[0], S[0], M[1], S[1]};
+    }
+    __syncthreads();  // the LDS tile is reused by the next tile
+  }
+}
+
+// Per row: the normalisers from the row's G look-1 records.
+__global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_t G) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const SmRec* rc = a.rec + static_cast<size_t>(row) * G;
+  float md = neg_inf(), mt = neg_inf();
+  for (int i = lane; i < G; i += 64) {
+    md = fmaxf(md, rc[i].md);
+    mt = fmaxf(mt, rc[i].mt);
+  }
+  md = wave_max(md);
+  mt = wave_max(mt);
+  float sd = 0.0f, st = 0.0f;
+  for (int i = lane; i < G; i += 64) {
+    const SmRec q = rc[i];
+    if (q.md > neg_inf()) sd += q.sd * __builtin_amdgcn_exp2f((q.md - md) * kLog2e);
+    if (q.mt > neg_inf()) st += q.st * __builtin_amdgcn_exp2f((q.mt - mt) * kLog2e);
+  }
+  sd = wave_sum(sd);
+  st = wave_sum(st);
+  if (lane == 0) a.norm[row] = SmRec{md, sd, mt, st};
+}
+
+// Look 2: per (row, workgroup) share of sum |P - T|.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a) {
+  __shared__ SmLds L;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = g * kSmTokens;
+  bf16x8 af[kSmMS][kSmMaxR / 32];
+  sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
+  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
+    sm_tile<T, VEC>(a, af, tok0, row0, L, [&](int h, int row, const float* d, const float* t, int) {
+      float l1 = 0.0f;
+      if (row < a.rows) {
+        const SmRec nr = a.norm[row];
+        const float isd = 1.0f / nr.sd, ist = 1.0f / nr.st;
+#pragma unroll
+        for (int e = 0; e < 4 * kSmMS; ++e)
+          l1 += fabsf(__builtin_amdgcn_exp2f((d[e] - nr.md) * kLog2e) * isd -
+                      __builtin_amdgcn_exp2f((t[e] - nr.mt) * kLog2e) * ist);
+      }
+      l1 = rows_sum(l1);
+      if (lane < 16) L.s[0][wave][h * 16 + lane] = l1;
+    });
+    __syncthreads();
+    if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSmWaves; ++w) s += L.s[0][w][threadIdx.x];
+      a.l1part[static_cast<size_t>(row0 + threadIdx.x) * G + g] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// Per row: L1 from its G shares, then accept_rate, CE and BCE.
+__global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32_t G, const float* conf_logits,
+                                                                 float* l1, float* accept_rate, float* ce,
+                                                                 float* bce) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  float s = 0.0f;
+  for (int i = lane; i < G; i += 64) s += a.l1part[static_cast<size_t>(row) * G + i];
+  s = wave_sum(s);
+  if (lane == 0) {
+    const SmRec nr = a.norm[row];
+    const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * s));
+    const float c = conf_logits[row];
+    l1[row] = s;
+    accept_rate[row] = av;
+    ce[row] = nr.md + logf(nr.sd) - a.dteach[row];
+    bce[row] = fmaxf(c, 0.0f) - c * av + log1pf(expf(-fabsf(c)));
+  }
+}
+
+template <typename T>
+hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, const uint8_t* block_mask,
+                           int32_t N, float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
+                           float* ce, float* bce, float* tau, float* sums, hipStream_t st) {
+  const unsigned rb = static_cast<unsigned>((a.rows + 3) / 4);
+  const bool vec = a.V % 4 == 0 && reinterpret_cast<uintptr_t>(a.backbone) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
+  if (vec)
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true>), dim3(G), dim3(kSmThreads), 0, st, a);
+  else
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, false>), dim3(G), dim3(kSmThreads), 0, st, a);
+  DSPARK_LAUNCH("stats_markov_rows", stats_markov_rows_kernel, dim3(rb), dim3(256), 0, st, a, G);
+  if (vec)
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true>), dim3(G), dim3(kSmThreads), 0, st, a);
+  else
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, false>), dim3(G), dim3(kSmThreads), 0, st, a);
+  DSPARK_LAUNCH("stats_markov_final", stats_markov_final_kernel, dim3(rb), dim3(256), 0, st, a, G,
+                conf_logits, l1, accept_rate, ce, bce);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_stats_reduce(l1, accept_rate, ce, bce, block_mask, N, a.gamma, w_ce, w_l1, w_conf, tau, sums,
+                             st);
+}
+
+}  // namespace
+
+StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V) {
+  StatsMarkovPlan p{};
+  const size_t rows = static_cast<size_t>(N) * gamma;
+  p.G = (V + kSmTokens - 1) / kSmTokens;
+  size_t off = 0;
+  p.off_rec = off;
+  off = align_up(off + rows * p.G * sizeof(SmRec), 256);
+  p.off_norm = off;
+  off = align_up(off + rows * sizeof(SmRec), 256);
+  p.off_l1 = off;
+  off = align_up(off + rows * p.G * sizeof(float), 256);
+  p.off_dt = off;
+  off = align_up(off + rows * sizeof(float), 256);
+  p.bytes = rows > 0 ? off : 0;
+  return p;
+}
+
+hipError_t launch_stats_markov(const void* backbone, const void* target, int dtype, const int32_t* anchor,
+                               const uint16_t* w1, const uint16_t* w2, int32_t r, const int32_t* teacher,
+                               const float* conf_logits, const uint8_t* block_mask, int32_t N, int32_t gamma,
+                               int32_t V, float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
+                               float* ce, float* bce, float* tau, float* sums, void* ws,
+                               const StatsMarkovPlan& pl, hipStream_t st) {
+  const int32_t rows = N * gamma;
+  if (rows == 0)
+    return launch_stats_reduce(l1, accept_rate, ce, bce, block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums, st);
+  char* w = static_cast<char*>(ws);
+  SmArgs a{backbone, target, anchor, w1, w2, teacher, rows, gamma, V, r,
+           reinterpret_cast<SmRec*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
+           reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1)};
+  if (dtype == DSPARK_BF16)
+    return launch_sm_typed<uint16_t>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate,
+                                     ce, bce, tau, sums, st);
+  return launch_sm_typed<float>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate, ce,
+                                bce, tau, sums, st);
+}
+
+}  // namespace dspark

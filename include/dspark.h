@@ -167,7 +167,13 @@ typedef struct dspark_policy {
 } dspark_policy;
 
 /* ---- workspace sizing ------------------------------------------------------ */
-enum { DSPARK_OP_MARKOV = 1, DSPARK_OP_VERIFY = 2, DSPARK_OP_STATS = 3, DSPARK_OP_STATS_BACKWARD = 4 };
+enum {
+  DSPARK_OP_MARKOV = 1,
+  DSPARK_OP_VERIFY = 2,
+  DSPARK_OP_STATS = 3,
+  DSPARK_OP_STATS_BACKWARD = 4,
+  DSPARK_OP_STATS_MARKOV = 5
+};
 
 /* Bytes of device workspace one call of `op` needs at these sizes (for
  * DSPARK_OP_STATS pass N as B; r and d are ignored where they do not apply).
@@ -346,6 +352,42 @@ dspark_status dspark_verify(
 dspark_status dspark_accept_stats(
     const void* draft_logits, const void* target_logits, int logits_dtype,
     const int32_t* teacher, const float* conf_logits,
+    const uint8_t* block_mask, int32_t N, int32_t gamma, int32_t V,
+    float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
+    float* ce, float* bce, float* tau, float* sums, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dspark_accept_stats_markov
+ *
+ * [MB] "Semi-autoregressive draft" (the Markov head adds a low-rank,
+ * token-conditioned bias to the parallel logits; at training time it is
+ * teacher-forced with the previous block tokens) and the statistics of
+ * dspark_accept_stats.  The draft row of block b at position k is formed on
+ * the device, never stored:
+ *   draft[b,k-1,:] = backbone[b,k-1,:] + W1[x_{k-1}] . W2^T
+ *   x_0 = anchor[b],  x_{k-1} = teacher[b,k-2] for k >= 2  (clamped to [0,V))
+ * and l1, accept_rate, ce, bce, tau and sums are those of dspark_accept_stats
+ * on these rows and target_logits.  The bias is an MFMA contraction of
+ * 2 N gamma V r flops per look at the rows (two looks).
+ *
+ * Inputs
+ *   backbone_logits [N, gamma, V] logits_dtype (the parallel draft logits)
+ *   target_logits   [N, gamma, V] logits_dtype
+ *   anchor          [N] int32
+ *   markov_w1, markov_w2  [V, r] bf16 (16-byte aligned), r as in
+ *                   dspark_markov_sample
+ *   teacher, conf_logits, block_mask, N, gamma, V, w_ce, w_l1, w_conf
+ *                   as dspark_accept_stats
+ * Outputs: as dspark_accept_stats.
+ * Workspace: dspark_workspace_size(DSPARK_OP_STATS_MARKOV, N, gamma, V, r, 0).
+ * Errors: as dspark_accept_stats, plus EINVAL (NULL anchor or factors,
+ * r <= 0, misaligned factors) and ESHAPE (r > DSPARK_MAX_RANK or r % 16 != 0).
+ * ------------------------------------------------------------------------- */
+dspark_status dspark_accept_stats_markov(
+    const void* backbone_logits, const void* target_logits, int logits_dtype,
+    const int32_t* anchor, const uint16_t* markov_w1, const uint16_t* markov_w2,
+    int32_t r, const int32_t* teacher, const float* conf_logits,
     const uint8_t* block_mask, int32_t N, int32_t gamma, int32_t V,
     float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
     float* ce, float* bce, float* tau, float* sums, void* workspace,

@@ -78,6 +78,26 @@ def test_stats_backward_validation(L):
     assert ds.dspark_workspace_size(ds.DSPARK_OP_STATS_BACKWARD, 64, 5, 129280) > 0
 
 
+def stats_mk(L, N=4, gamma=5, V=1024, r=16, w1=FAKE, anchor=FAKE, ws=FAKE, wsb=1 << 30):
+    return L.dspark_accept_stats_markov(FAKE, FAKE, 1, anchor, w1, FAKE, r, FAKE, FAKE, None, N, gamma,
+                                        V, 0.1, 0.9, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
+                                        None)
+
+
+def test_stats_markov_validation(L):
+    assert stats_mk(L, N=-1) == ds.DSPARK_EINVAL
+    assert stats_mk(L, r=0) == ds.DSPARK_EINVAL
+    assert stats_mk(L, r=24) == ds.DSPARK_ESHAPE
+    assert stats_mk(L, r=512) == ds.DSPARK_ESHAPE
+    assert stats_mk(L, gamma=17) == ds.DSPARK_ESHAPE
+    assert stats_mk(L, anchor=None) == ds.DSPARK_EINVAL
+    assert stats_mk(L, w1=None) == ds.DSPARK_EINVAL
+    assert stats_mk(L, w1=C.c_void_p(4098)) == ds.DSPARK_EINVAL  # misaligned factor
+    assert stats_mk(L, ws=None) == ds.DSPARK_EWORKSPACE
+    assert stats_mk(L, wsb=16) == ds.DSPARK_EWORKSPACE
+    assert ds.dspark_workspace_size(ds.DSPARK_OP_STATS_MARKOV, 4, 5, 1024, 16) > 0
+
+
 def width(L, B=4, gamma=5, conf=FAKE, cost=FAKE, out=FAKE):
     return L.dspark_select_width(conf, cost, B, gamma, out, None, None)
 
