@@ -64,6 +64,8 @@ struct SmArgs {
 struct SmLds {
   __attribute__((aligned(16))) uint16_t a[kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
   float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];              // per (array, wave, row)
+  SmRec meta[kSmTile];  // per row of the tile: look 1 the teacher token (in md), look 2 the normalisers
+  float dt[kSmTile];    // look 1: the draft value at the row's teacher token, if in this slice
 };
 
 __device__ __forceinline__ float rows_max(float v) {
@@ -110,10 +112,11 @@ __device__ __forceinline__ int32_t forced_token(const SmArgs& a, int row) {
   return clamp_token(x, a.V);
 }
 
-// One look over the row tile [row0, row0 + 64) for the workgroup's tokens:
-// stages the W1 rows, forms the bias tile on MFMA, adds the backbone values
-// and calls epi(pass h, lane's row, d[16], t[16], token of element 0 of each
-// quad) for every 16-row pass.
+// One look over the row tile [row0, row0 + 64) for the workgroup's tokens
+// (any row alignment): stages the W1 rows, forms the bias tile on MFMA, adds
+// the backbone values and calls epi(pass h, d[16], t[16], token of element 0)
+// for every 16-row pass, element e of the lane's 16 being token
+// v00 + (e / 4) 16 + e % 4 of row row0 + h 16 + lane % 16.
 template <typename T, bool VEC, class Epi>
 __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
                                         int row0, SmLds& L, Epi&& epi) {
@@ -195,7 +198,141 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
         t[ms * 4 + i] = in ? qt[h][ms].at(i) : neg_inf();
       }
     }
-    epi(h, row0 + h * 16 + (lane & 15), d, t, vb + 4 * (lane >> 4));
+    epi(h, d, t, vb + 4 * (lane >> 4));
+  }
+}
+
+// Buffer resources over the backbone and target rows [row0, rows): loads
+// past them return zeros, so every load of a tile is unconditional and the
+// compiler's wait counts stay exact.
+template <typename T>
+struct TileRs {
+  __amdgpu_buffer_rsrc_t d, t;
+};
+template <typename T>
+__device__ __forceinline__ TileRs<T> tile_rs(const SmArgs& a, int row0) {
+  const size_t base = static_cast<size_t>(row0) * a.V;
+  const size_t left = (static_cast<size_t>(a.rows) - row0) * a.V * sizeof(T);
+  const int bytes = static_cast<int>(left > 0x7fffffffull ? 0x7fffffffull : left);
+  return TileRs<T>{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(a.backbone) + base),
+                                                     static_cast<short>(0), bytes, kBufferWord3),
+                   __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(a.target) + base),
+                                                     static_cast<short>(0), bytes, kBufferWord3)};
+}
+
+// The backbone and target quads of passes h0, h0 + 1 (16 rows each) of a tile.
+template <typename T>
+__device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)[2][kSmMS], const TileRs<T>& rs,
+                                          int h0, int vb, int lane, int V) {
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint32_t n = static_cast<uint32_t>((h0 + hh) * 16 + (lane & 15));
+#pragma unroll
+    for (int ms = 0; ms < kSmMS; ++ms) {
+      const uint32_t v0 = static_cast<uint32_t>(vb + ms * 16 + 4 * (lane >> 4));
+      const uint32_t off = (n * static_cast<uint32_t>(V) + v0) * sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        qd[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.d, off, 0, 0));
+        qt[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.t, off, 0, 0));
+      } else {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs.d, off, 0, 0);
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rs.t, off, 0, 0);
+        qd[hh][ms].u = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                                   __uint_as_float(x[3]));
+        qt[hh][ms].u = make_float4(__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
+                                   __uint_as_float(y[3]));
+      }
+    }
+  }
+}
+
+// All row tiles of one look, for 4-aligned rows.  Per tile: the rows'
+// metadata (meta(row) -> LDS) and W1 rows are staged; the second half of
+// the tile's values is requested before the first half is used, and the
+// next tile's first half before the second half is used, so the workgroup
+// always has loads in flight.  epi as for sm_tile; merge(row0) after each
+// tile's passes (LDS partials complete).
+template <typename T, class Meta, class Epi, class Merge>
+__device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
+                                            SmLds& L, Meta&& meta, Epi&& epi, Merge&& merge) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vb = tok0 + wave * 16 * kSmMS;
+  const int V = a.V, r = a.r;
+  const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
+  const int pieces = kpad / 8;
+  constexpr int kMaxPieces = kSmTile * (kSmMaxR / 8) / kSmThreads;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
+  Quad<T> qA[2][kSmMS], tA[2][kSmMS], qB[2][kSmMS], tB[2][kSmMS];
+  load_half<T>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
+  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
+    if (tid < kSmTile) L.meta[tid] = meta(row0 + tid);
+    // W1 rows of the tile's forced tokens
+    int32_t xs[kMaxPieces];
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int idx = tid + j * kSmThreads;
+      const int row = row0 + idx / pieces;
+      const int rr = row < a.rows ? row : 0;
+      const int k = rr % a.gamma;
+      xs[j] = *(k == 0 ? a.anchor + rr / a.gamma : a.teacher + (rr - 1));  // one load, no branch
+    }
+    uint4 stage[kMaxPieces];
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int idx = tid + j * kSmThreads;
+      const int rt = idx / pieces, pc = idx - rt * pieces;
+      const uint32_t off = (pc * 8 < r && row0 + rt < a.rows)
+                               ? static_cast<uint32_t>((clamp_token(xs[j], V) * r + pc * 8) * 2)
+                               : 0xfffffff0u;
+      stage[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int idx = tid + j * kSmThreads;
+      const int rt = idx / pieces, pc = idx - rt * pieces;
+      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a + rt * ld + pc * 8) = stage[j];
+    }
+    __syncthreads();
+    load_half<T>(qB, tB, tile_rs<T>(a, row0), 2, vb, lane, V);
+
+    auto pass = [&](int h, const Quad<T> (&qd)[kSmMS], const Quad<T> (&qt)[kSmMS]) {
+      f32x4 acc[kSmMS];
+#pragma unroll
+      for (int ms = 0; ms < kSmMS; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
+        if (ks < ksteps) {
+          const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a + (h * 16 + (lane & 15)) * ld + ks * 32 +
+                                                             (lane >> 4) * 8);
+#pragma unroll
+          for (int ms = 0; ms < kSmMS; ++ms)
+            acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms], 0, 0, 0);
+        }
+      }
+      float d[4 * kSmMS], t[4 * kSmMS];
+#pragma unroll
+      for (int ms = 0; ms < kSmMS; ++ms) {
+        const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool in = v0 + i < V;
+          d[ms * 4 + i] = in ? qd[ms].at(i) + acc[ms][i] : neg_inf();
+          t[ms * 4 + i] = in ? qt[ms].at(i) : neg_inf();
+        }
+      }
+      epi(h, d, t, vb + 4 * (lane >> 4));
+    };
+    pass(0, qA[0], tA[0]);
+    pass(1, qA[1], tA[1]);
+    // unconditional (past the last tile the resource is empty and the loads
+    // return zeros), so that both paths reach the next waits alike
+    load_half<T>(qA, tA, tile_rs<T>(a, min(row0 + kSmTile, a.rows)), 0, vb, lane, V);
+    pass(2, qB[0], tB[0]);
+    pass(3, qB[1], tB[1]);
+    __syncthreads();
+    merge(row0);
+    __syncthreads();  // the LDS tile is reused by the next tile
   }
 }
 
@@ -226,43 +363,43 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-    sm_tile<T, VEC>(a, af, tok0, row0, L, [&](int h, int row, const float* d, const float* t, int v00) {
-      // the teacher token's draft value, from the lane that holds it
-      if (row < a.rows) {
-        const int32_t tch = clamp_token(a.teacher[row], a.V);
+  auto meta = [&](int row) {
+    const int32_t t = row < a.rows ? clamp_token(a.teacher[row], a.V) : -1;
+    return SmRec{__int_as_float(t), 0.0f, 0.0f, 0.0f};
+  };
+  auto epi = [&](int h, const float* d, const float* t, int v00) {
+    // the teacher token's draft value, from the lane that holds it (to LDS:
+    // a global store here would blur the wait counts of the loads in flight)
+    const int32_t tch = __float_as_int(L.meta[h * 16 + (lane & 15)].md);
 #pragma unroll
-        for (int ms = 0; ms < kSmMS; ++ms)
+    for (int e = 0; e < 4 * kSmMS; ++e)
+      if (v00 + (e >> 2) * 16 + (e & 3) == tch) L.dt[h * 16 + (lane & 15)] = d[e];
+    float md = neg_inf(), mt = neg_inf();
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (v00 + ms * 16 + i == tch) a.dteach[row] = d[ms * 4 + i];
-      }
-      float md = neg_inf(), mt = neg_inf();
+    for (int e = 0; e < 4 * kSmMS; ++e) {
+      md = fmaxf(md, d[e]);
+      mt = fmaxf(mt, t[e]);
+    }
+    md = rows_max(md);
+    mt = rows_max(mt);
+    float sd = 0.0f, st = 0.0f;
+    if (md > neg_inf())
 #pragma unroll
-      for (int e = 0; e < 4 * kSmMS; ++e) {
-        md = fmaxf(md, d[e]);
-        mt = fmaxf(mt, t[e]);
-      }
-      md = rows_max(md);
-      mt = rows_max(mt);
-      float sd = 0.0f, st = 0.0f;
-      if (md > neg_inf())
+      for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f((d[e] - md) * kLog2e);
+    if (mt > neg_inf())
 #pragma unroll
-        for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f((d[e] - md) * kLog2e);
-      if (mt > neg_inf())
-#pragma unroll
-        for (int e = 0; e < 4 * kSmMS; ++e) st += __builtin_amdgcn_exp2f((t[e] - mt) * kLog2e);
-      sd = rows_sum(sd);
-      st = rows_sum(st);
-      if (lane < 16) {
-        const int n = h * 16 + lane;
-        L.m[0][wave][n] = md;
-        L.s[0][wave][n] = sd;
-        L.m[1][wave][n] = mt;
-        L.s[1][wave][n] = st;
-      }
-    });
-    __syncthreads();
+      for (int e = 0; e < 4 * kSmMS; ++e) st += __builtin_amdgcn_exp2f((t[e] - mt) * kLog2e);
+    sd = rows_sum(sd);
+    st = rows_sum(st);
+    if (lane < 16) {
+      const int n = h * 16 + lane;
+      L.m[0][wave][n] = md;
+      L.s[0][wave][n] = sd;
+      L.m[1][wave][n] = mt;
+      L.s[1][wave][n] = st;
+    }
+  };
+  auto merge = [&](int row0) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       const int n = threadIdx.x;
       float M[2], S[2];
@@ -280,8 +417,20 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
         S[q] = s;
       }
       a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{M[0], S[0], M[1], S[1]};
+      const int32_t tch = __float_as_int(L.meta[n].md);
+      if (tch >= tok0 && tch < tok0 + kSmTokens) a.dteach[row0 + n] = L.dt[n];
     }
-    __syncthreads();  // the LDS tile is reused by the next tile
+  };
+  if constexpr (VEC) {
+    sm_look_vec<T>(a, af, tok0, L, meta, epi, merge);
+  } else {
+    for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
+      if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
+      sm_tile<T, VEC>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
+      __syncthreads();
+      merge(row0);
+      __syncthreads();  // the LDS tile is reused by the next tile
+    }
   }
 }
 
@@ -318,28 +467,36 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-    sm_tile<T, VEC>(a, af, tok0, row0, L, [&](int h, int row, const float* d, const float* t, int) {
-      float l1 = 0.0f;
-      if (row < a.rows) {
-        const SmRec nr = a.norm[row];
-        const float isd = 1.0f / nr.sd, ist = 1.0f / nr.st;
+  auto meta = [&](int row) { return row < a.rows ? a.norm[row] : SmRec{0.0f, 1.0f, 0.0f, 1.0f}; };
+  auto epi = [&](int h, const float* d, const float* t, int) {
+    const SmRec nr = L.meta[h * 16 + (lane & 15)];
+    const float isd = 1.0f / nr.sd, ist = 1.0f / nr.st;
+    float l1 = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4 * kSmMS; ++e)
-          l1 += fabsf(__builtin_amdgcn_exp2f((d[e] - nr.md) * kLog2e) * isd -
-                      __builtin_amdgcn_exp2f((t[e] - nr.mt) * kLog2e) * ist);
-      }
-      l1 = rows_sum(l1);
-      if (lane < 16) L.s[0][wave][h * 16 + lane] = l1;
-    });
-    __syncthreads();
+    for (int e = 0; e < 4 * kSmMS; ++e)
+      l1 += fabsf(__builtin_amdgcn_exp2f((d[e] - nr.md) * kLog2e) * isd -
+                  __builtin_amdgcn_exp2f((t[e] - nr.mt) * kLog2e) * ist);
+    l1 = rows_sum(l1);
+    if (lane < 16) L.s[0][wave][h * 16 + lane] = l1;
+  };
+  auto merge = [&](int row0) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < kSmWaves; ++w) s += L.s[0][w][threadIdx.x];
       a.l1part[static_cast<size_t>(row0 + threadIdx.x) * G + g] = s;
     }
-    __syncthreads();
+  };
+  if constexpr (VEC) {
+    sm_look_vec<T>(a, af, tok0, L, meta, epi, merge);
+  } else {
+    for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
+      if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
+      sm_tile<T, VEC>(a, af, tok0, row0, L, epi);
+      __syncthreads();
+      merge(row0);
+      __syncthreads();
+    }
   }
 }
 
@@ -369,8 +526,11 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
                            int32_t N, float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
                            float* ce, float* bce, float* tau, float* sums, hipStream_t st) {
   const unsigned rb = static_cast<unsigned>((a.rows + 3) / 4);
+  // the aligned path addresses a tile's rows with 32-bit byte offsets
   const bool vec = a.V % 4 == 0 && reinterpret_cast<uintptr_t>(a.backbone) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
+                   reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
+                   static_cast<uint64_t>(kSmTile) * a.V * sizeof(T) < 0x7fffffffull &&
+                   static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull;
   if (vec)
     DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true>), dim3(G), dim3(kSmThreads), 0, st, a);
   else
