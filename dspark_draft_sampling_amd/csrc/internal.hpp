@@ -100,6 +100,9 @@ struct StatsPlan {
 };
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 
+// Compute units of the current device (cached per device; stats.hip).
+int device_cus();
+
 // Batch reduction of the per-position statistics (tau and the sums), shared by
 // the statistics calls (stats.hip).
 hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,

@@ -810,7 +810,7 @@ __global__ __launch_bounds__(kRowThreads) void stats_grad_rows_kernel(const T* _
 }
 
 // Compute units of the current device, cached per device.
-int device_cus() {
+int device_cus_cached() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
   int dev = 0;
@@ -851,7 +851,7 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                   target, V, pl.P, items, part, l1part, o);
     return hipGetLastError();
   } else if (npairs > 0) {
-    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus())));
+    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus_cached())));
     if (vec)
       DSPARK_LAUNCH("stats_rows", (stats_rows_kernel<T, true>), grid, dim3(kRowThreads), 0, st, draft,
                     target, teacher, conf_logits, V, npairs, l1, accept_rate, ce, bce);
@@ -892,7 +892,7 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
     DSPARK_LAUNCH("stats_grad_write", (stats_grad_write_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
                   draft, target, V, pl.P, items, o.rows, grad);
   } else {
-    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus())));
+    const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus_cached())));
     if (vec)
       DSPARK_LAUNCH("stats_grad_rows", (stats_grad_rows_kernel<T, true>), grid, dim3(kRowThreads), 0, st,
                     draft, target, V, npairs, o, grad);
@@ -904,6 +904,8 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
 }
 
 }  // namespace
+
+int device_cus() { return device_cus_cached(); }
 
 hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,
                                const uint8_t* block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,

@@ -17,9 +17,11 @@
 // fragments) for the whole launch; it walks the rows in tiles of 64 (the N
 // side), staging the tile's W1 rows (selected by the forced tokens) in LDS,
 // and adds the bias to the backbone values it streams.  Two looks:
-//  * look 1: per (row, workgroup) the (max, sum exp) of the draft and target
-//    values of its tokens, and the draft value at the row's teacher token;
-//  * rows: the per-row normalisers from those records;
+//  * look 1: per (row, workgroup) the (max, sum exp) of the draft values of
+//    its tokens;
+//  * tnorm: per row the target's normaliser (no bias involved);
+//  * teacher: per row the draft value at the teacher token;
+//  * rows: the per-row draft normalisers from the look-1 records;
 //  * look 2: the bias again, and per (row, workgroup) the share of
 //    sum |P - T|;
 //  * final: per row L1, accept_rate, CE, BCE; then the batch reduction of
@@ -56,7 +58,7 @@ struct SmArgs {
   const int32_t* teacher;
   int32_t rows, gamma, V, r;
   SmRec* rec;       // [rows][G] (look 1)
-  float* dteach;    // [rows]: the draft value at the teacher token (look 1)
+  float* dteach;    // [rows]: the draft value at the teacher token
   SmRec* norm;      // [rows]: per-row normalisers (after look 1)
   float* l1part;    // [rows][G] (look 2)
 };
@@ -64,8 +66,7 @@ struct SmArgs {
 struct SmLds {
   __attribute__((aligned(16))) uint16_t a[kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
   float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];              // per (array, wave, row)
-  SmRec meta[kSmTile];  // per row of the tile: look 1 the teacher token (in md), look 2 the normalisers
-  float dt[kSmTile];    // look 1: the draft value at the row's teacher token, if in this slice
+  SmRec meta[kSmTile];  // per row of the tile: look 2 the normalisers
 };
 
 __device__ __forceinline__ float rows_max(float v) {
@@ -117,12 +118,13 @@ __device__ __forceinline__ int32_t forced_token(const SmArgs& a, int row) {
 // the backbone values and calls epi(pass h, d[16], t[16], token of element 0)
 // for every 16-row pass, element e of the lane's 16 being token
 // v00 + (e / 4) 16 + e % 4 of row row0 + h 16 + lane % 16.
-template <typename T, bool VEC, class Epi>
+template <typename T, bool VEC, bool LT, class Epi>
 __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
                                         int row0, SmLds& L, Epi&& epi) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vb = tok0 + wave * 16 * kSmMS;
   const int V = a.V, r = a.r;
+  const bool dead = __builtin_amdgcn_readfirstlane(vb) >= V;  // wave-uniform
   const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
   const T* bb = static_cast<const T*>(a.backbone);
   const T* tg = static_cast<const T*>(a.target);
@@ -166,7 +168,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
       const int v0 = vb + ms * 16 + 4 * (lane >> 4);
       const int n = row < a.rows ? (V - v0 < 4 ? (V - v0 > 0 ? V - v0 : 0) : 4) : 0;
       qd[h][ms].load(bb + off + (n > 0 ? v0 : 0), n, VEC);
-      qt[h][ms].load(tg + off + (n > 0 ? v0 : 0), n, VEC);
+      if constexpr (LT) qt[h][ms].load(tg + off + (n > 0 ? v0 : 0), n, VEC);
     }
   }
   __syncthreads();
@@ -195,7 +197,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
       for (int i = 0; i < 4; ++i) {
         const bool in = v0 + i < V;
         d[ms * 4 + i] = in ? qd[h][ms].at(i) + acc[ms][i] : neg_inf();
-        t[ms * 4 + i] = in ? qt[h][ms].at(i) : neg_inf();
+        t[ms * 4 + i] = LT && in ? qt[h][ms].at(i) : neg_inf();
       }
     }
     epi(h, d, t, vb + 4 * (lane >> 4));
@@ -221,7 +223,7 @@ __device__ __forceinline__ TileRs<T> tile_rs(const SmArgs& a, int row0) {
 }
 
 // The backbone and target quads of passes h0, h0 + 1 (16 rows each) of a tile.
-template <typename T>
+template <typename T, bool LT>
 __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)[2][kSmMS], const TileRs<T>& rs,
                                           int h0, int vb, int lane, int V) {
 #pragma unroll
@@ -233,14 +235,16 @@ __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)
       const uint32_t off = (n * static_cast<uint32_t>(V) + v0) * sizeof(T);
       if constexpr (sizeof(T) == 2) {
         qd[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.d, off, 0, 0));
-        qt[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.t, off, 0, 0));
+        if constexpr (LT) qt[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.t, off, 0, 0));
       } else {
         const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs.d, off, 0, 0);
-        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rs.t, off, 0, 0);
         qd[hh][ms].u = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
                                    __uint_as_float(x[3]));
-        qt[hh][ms].u = make_float4(__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
-                                   __uint_as_float(y[3]));
+        if constexpr (LT) {
+          const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rs.t, off, 0, 0);
+          qt[hh][ms].u = make_float4(__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
+                                     __uint_as_float(y[3]));
+        }
       }
     }
   }
@@ -252,19 +256,23 @@ __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)
 // next tile's first half before the second half is used, so the workgroup
 // always has loads in flight.  epi as for sm_tile; merge(row0) after each
 // tile's passes (LDS partials complete).
-template <typename T, class Meta, class Epi, class Merge>
+// MASK: tokens past the vocabulary are excluded element by element; without
+// it (V a multiple of 64) a wave's tokens are all in or all out, and a wave
+// past the vocabulary hands its epilogue -inf values.
+template <typename T, bool LT, bool MASK, class Meta, class Epi, class Merge>
 __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
                                             SmLds& L, Meta&& meta, Epi&& epi, Merge&& merge) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vb = tok0 + wave * 16 * kSmMS;
   const int V = a.V, r = a.r;
+  const bool dead = __builtin_amdgcn_readfirstlane(vb) >= V;  // wave-uniform
   const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
   const int pieces = kpad / 8;
   constexpr int kMaxPieces = kSmTile * (kSmMaxR / 8) / kSmThreads;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
   Quad<T> qA[2][kSmMS], tA[2][kSmMS], qB[2][kSmMS], tB[2][kSmMS];
-  load_half<T>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
+  load_half<T, LT>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
   for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
     if (tid < kSmTile) L.meta[tid] = meta(row0 + tid);
     // W1 rows of the tile's forced tokens
@@ -294,7 +302,7 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
       if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a + rt * ld + pc * 8) = stage[j];
     }
     __syncthreads();
-    load_half<T>(qB, tB, tile_rs<T>(a, row0), 2, vb, lane, V);
+    load_half<T, LT>(qB, tB, tile_rs<T>(a, row0), 2, vb, lane, V);
 
     auto pass = [&](int h, const Quad<T> (&qd)[kSmMS], const Quad<T> (&qt)[kSmMS]) {
       f32x4 acc[kSmMS];
@@ -316,18 +324,21 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
         const int v0 = vb + ms * 16 + 4 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool in = v0 + i < V;
+          const bool in = !MASK || v0 + i < V;
           d[ms * 4 + i] = in ? qd[ms].at(i) + acc[ms][i] : neg_inf();
-          t[ms * 4 + i] = in ? qt[ms].at(i) : neg_inf();
+          t[ms * 4 + i] = LT && in ? qt[ms].at(i) : neg_inf();
         }
       }
+      if (!MASK && dead)
+#pragma unroll
+        for (int e = 0; e < 4 * kSmMS; ++e) d[e] = t[e] = neg_inf();
       epi(h, d, t, vb + 4 * (lane >> 4));
     };
     pass(0, qA[0], tA[0]);
     pass(1, qA[1], tA[1]);
     // unconditional (past the last tile the resource is empty and the loads
     // return zeros), so that both paths reach the next waits alike
-    load_half<T>(qA, tA, tile_rs<T>(a, min(row0 + kSmTile, a.rows)), 0, vb, lane, V);
+    load_half<T, LT>(qA, tA, tile_rs<T>(a, min(row0 + kSmTile, a.rows)), 0, vb, lane, V);
     pass(2, qB[0], tB[0]);
     pass(3, qB[1], tB[1]);
     __syncthreads();
@@ -353,9 +364,10 @@ __device__ __forceinline__ void sm_load_w2(bf16x8 (&af)[kSmMS][kSmMaxR / 32], co
   }
 }
 
-// Look 1: per (row, workgroup) record of the draft and target values'
-// (max, sum exp), and the draft value at the row's teacher token.
-template <typename T, bool VEC>
+// Look 1: per (row, workgroup) record of the draft values' (max, sum exp)
+// (the target rows are not needed: their normalisers do not involve the bias,
+// stats_markov_tnorm; nor is the teacher's value, stats_markov_teacher).
+template <typename T, bool VEC, bool MASK>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a) {
   __shared__ SmLds L;
   const int g = blockIdx.x, G = gridDim.x;
@@ -363,70 +375,43 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  auto meta = [&](int row) {
-    const int32_t t = row < a.rows ? clamp_token(a.teacher[row], a.V) : -1;
-    return SmRec{__int_as_float(t), 0.0f, 0.0f, 0.0f};
-  };
-  auto epi = [&](int h, const float* d, const float* t, int v00) {
-    // the teacher token's draft value, from the lane that holds it (to LDS:
-    // a global store here would blur the wait counts of the loads in flight)
-    const int32_t tch = __float_as_int(L.meta[h * 16 + (lane & 15)].md);
+  auto meta = [](int) { return SmRec{}; };
+  auto epi = [&](int h, const float* d, const float*, int) {
+    float md = neg_inf();
 #pragma unroll
-    for (int e = 0; e < 4 * kSmMS; ++e)
-      if (v00 + (e >> 2) * 16 + (e & 3) == tch) L.dt[h * 16 + (lane & 15)] = d[e];
-    float md = neg_inf(), mt = neg_inf();
-#pragma unroll
-    for (int e = 0; e < 4 * kSmMS; ++e) {
-      md = fmaxf(md, d[e]);
-      mt = fmaxf(mt, t[e]);
-    }
+    for (int e = 0; e < 4 * kSmMS; ++e) md = fmaxf(md, d[e]);
     md = rows_max(md);
-    mt = rows_max(mt);
-    float sd = 0.0f, st = 0.0f;
+    float sd = 0.0f;
     if (md > neg_inf())
 #pragma unroll
       for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f((d[e] - md) * kLog2e);
-    if (mt > neg_inf())
-#pragma unroll
-      for (int e = 0; e < 4 * kSmMS; ++e) st += __builtin_amdgcn_exp2f((t[e] - mt) * kLog2e);
     sd = rows_sum(sd);
-    st = rows_sum(st);
     if (lane < 16) {
       const int n = h * 16 + lane;
       L.m[0][wave][n] = md;
       L.s[0][wave][n] = sd;
-      L.m[1][wave][n] = mt;
-      L.s[1][wave][n] = st;
     }
   };
   auto merge = [&](int row0) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       const int n = threadIdx.x;
-      float M[2], S[2];
+      float m = neg_inf();
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float m = neg_inf();
+      for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[0][w][n]);
+      float s = 0.0f;
+      if (m > neg_inf())
 #pragma unroll
-        for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[q][w][n]);
-        float s = 0.0f;
-        if (m > neg_inf())
-#pragma unroll
-          for (int w = 0; w < kSmWaves; ++w)
-            if (L.m[q][w][n] > neg_inf()) s += L.s[q][w][n] * __builtin_amdgcn_exp2f((L.m[q][w][n] - m) * kLog2e);
-        M[q] = m;
-        S[q] = s;
-      }
-      a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{M[0], S[0], M[1], S[1]};
-      const int32_t tch = __float_as_int(L.meta[n].md);
-      if (tch >= tok0 && tch < tok0 + kSmTokens) a.dteach[row0 + n] = L.dt[n];
+        for (int w = 0; w < kSmWaves; ++w)
+          if (L.m[0][w][n] > neg_inf()) s += L.s[0][w][n] * __builtin_amdgcn_exp2f((L.m[0][w][n] - m) * kLog2e);
+      a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{m, s, 0.0f, 0.0f};
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T>(a, af, tok0, L, meta, epi, merge);
+    sm_look_vec<T, false, MASK>(a, af, tok0, L, meta, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
       if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
-      sm_tile<T, VEC>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
+      sm_tile<T, VEC, false>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
       __syncthreads();
       merge(row0);
       __syncthreads();  // the LDS tile is reused by the next tile
@@ -434,32 +419,113 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   }
 }
 
-// Per row: the normalisers from the row's G look-1 records.
+// Per row: the draft value at the teacher token, the backbone's value plus
+// W1[x] . W2[teacher] (bf16 products, exact in fp32, summed in fp32), one
+// wave per row; x is the row's forced previous token (the anchor at the
+// block's first position, else the previous position's teacher token).
+template <typename T>
+__global__ __launch_bounds__(256) void stats_markov_teacher_kernel(SmArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const int k = row % a.gamma;
+  const int x = clamp_token(k == 0 ? a.anchor[row / a.gamma] : a.teacher[row - 1], a.V);
+  const int tch = clamp_token(a.teacher[row], a.V);
+  const uint16_t* w1 = a.w1 + static_cast<size_t>(x) * a.r;
+  const uint16_t* w2 = a.w2 + static_cast<size_t>(tch) * a.r;
+  float s = 0.0f;
+  for (int j = lane; j < a.r; j += 64)
+    s = fmaf(__uint_as_float(static_cast<uint32_t>(w1[j]) << 16), __uint_as_float(static_cast<uint32_t>(w2[j]) << 16), s);
+  s = wave_sum(s);
+  if (lane == 0)
+    a.dteach[row] = load_logit(static_cast<const T*>(a.backbone) + static_cast<size_t>(row) * a.V, tch) + s;
+}
+
+// Per row: the target row's normaliser (max, sum exp), one persistent
+// workgroup of 1024 threads per compute unit looping over rows.
+constexpr int kTnThreads = 1024;
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kTnThreads) void stats_markov_tnorm_kernel(SmArgs a) {
+  constexpr int EPL = VEC ? 16 / static_cast<int>(sizeof(T)) : 1;
+  constexpr int kU = 4;
+  __shared__ float sh[kTnThreads / 64];
+  const T* tg = static_cast<const T*>(a.target);
+  const int V = a.V;
+  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const T* tr = tg + static_cast<size_t>(row) * V;
+    float m = neg_inf(), s = 0.0f;
+    auto add = [&](const float* x) {
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j) mx = fmaxf(mx, x[j]);
+      if (mx > m) {
+        s = m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - mx) * kLog2e) : 0.0f;
+        m = mx;
+      }
+      if (m > neg_inf())
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) s += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+    };
+    auto ld = [&](int e, float* x) {
+      if constexpr (VEC) {
+        const uint4 u = *reinterpret_cast<const uint4*>(tr + e);
+        if constexpr (sizeof(T) == 2) {
+          x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+          x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+        } else {
+          x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+          x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+        }
+      } else {
+        x[0] = load_logit(tr, e);
+      }
+    };
+    const int step = kTnThreads * EPL;
+    int e = threadIdx.x * EPL;
+    for (; e + (kU - 1) * step < V; e += kU * step) {
+      float x[kU][EPL];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) ld(e + u * step, x[u]);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) add(x[u]);
+    }
+    for (; e < V; e += step) {
+      float x[EPL];
+      ld(e, x);
+      add(x);
+    }
+    const float M = block_max<kTnThreads / 64>(m, sh);
+    const float S = block_sum<kTnThreads / 64>(m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f, sh);
+    if (threadIdx.x == 0) {
+      a.norm[row].mt = M;
+      a.norm[row].st = S;
+    }
+  }
+}
+
+// Per row: the draft normaliser from the row's G look-1 records.
 __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_t G) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.rows) return;
   const SmRec* rc = a.rec + static_cast<size_t>(row) * G;
-  float md = neg_inf(), mt = neg_inf();
-  for (int i = lane; i < G; i += 64) {
-    md = fmaxf(md, rc[i].md);
-    mt = fmaxf(mt, rc[i].mt);
-  }
+  float md = neg_inf();
+  for (int i = lane; i < G; i += 64) md = fmaxf(md, rc[i].md);
   md = wave_max(md);
-  mt = wave_max(mt);
-  float sd = 0.0f, st = 0.0f;
+  float sd = 0.0f;
   for (int i = lane; i < G; i += 64) {
     const SmRec q = rc[i];
     if (q.md > neg_inf()) sd += q.sd * __builtin_amdgcn_exp2f((q.md - md) * kLog2e);
-    if (q.mt > neg_inf()) st += q.st * __builtin_amdgcn_exp2f((q.mt - mt) * kLog2e);
   }
   sd = wave_sum(sd);
-  st = wave_sum(st);
-  if (lane == 0) a.norm[row] = SmRec{md, sd, mt, st};
+  if (lane == 0) {  // the target half (mt, st) is stats_markov_tnorm's
+    a.norm[row].md = md;
+    a.norm[row].sd = sd;
+  }
 }
 
 // Look 2: per (row, workgroup) share of sum |P - T|.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool MASK>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a) {
   __shared__ SmLds L;
   const int g = blockIdx.x, G = gridDim.x;
@@ -488,11 +554,11 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T>(a, af, tok0, L, meta, epi, merge);
+    sm_look_vec<T, true, MASK>(a, af, tok0, L, meta, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
       if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
-      sm_tile<T, VEC>(a, af, tok0, row0, L, epi);
+      sm_tile<T, VEC, true>(a, af, tok0, row0, L, epi);
       __syncthreads();
       merge(row0);
       __syncthreads();
@@ -531,15 +597,34 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
                    reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
                    static_cast<uint64_t>(kSmTile) * a.V * sizeof(T) < 0x7fffffffull &&
                    static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull;
-  if (vec)
-    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true>), dim3(G), dim3(kSmThreads), 0, st, a);
+  const bool mask = a.V % 64 != 0;
+  if (vec && !mask)
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true, false>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
+  else if (vec)
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true, true>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
   else
-    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, false>), dim3(G), dim3(kSmThreads), 0, st, a);
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, false, true>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
+  DSPARK_LAUNCH("stats_markov_teacher", stats_markov_teacher_kernel<T>, dim3(rb), dim3(256), 0, st, a);
+  const int epl = 16 / static_cast<int>(sizeof(T));
+  const bool tvec = a.V % epl == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
+  const dim3 tgrid(static_cast<unsigned>(std::min(a.rows, device_cus())));
+  if (tvec)
+    DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, true>), tgrid, dim3(kTnThreads), 0, st, a);
+  else
+    DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, false>), tgrid, dim3(kTnThreads), 0, st, a);
   DSPARK_LAUNCH("stats_markov_rows", stats_markov_rows_kernel, dim3(rb), dim3(256), 0, st, a, G);
-  if (vec)
-    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true>), dim3(G), dim3(kSmThreads), 0, st, a);
+  if (vec && !mask)
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true, false>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
+  else if (vec)
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true, true>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
   else
-    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, false>), dim3(G), dim3(kSmThreads), 0, st, a);
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, false, true>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
   DSPARK_LAUNCH("stats_markov_final", stats_markov_final_kernel, dim3(rb), dim3(256), 0, st, a, G,
                 conf_logits, l1, accept_rate, ce, bce);
   hipError_t e = hipGetLastError();
