@@ -63,10 +63,12 @@ struct SmArgs {
   float* l1part;    // [rows][G] (look 2)
 };
 
+// Two of everything: the aligned path stages tile t + 1 and merges tile
+// t - 1 while tile t runs (index = tile parity); the unaligned path uses 0.
 struct SmLds {
-  __attribute__((aligned(16))) uint16_t a[kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
-  float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];              // per (array, wave, row)
-  SmRec meta[kSmTile];  // per row of the tile: look 2 the normalisers
+  __attribute__((aligned(16))) uint16_t a[2][kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
+  float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];                 // per (parity, wave, row)
+  SmRec meta[2][kSmTile];  // per (parity, row): look 2 the constants of its epilogue
 };
 
 __device__ __forceinline__ float rows_max(float v) {
@@ -153,7 +155,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
     for (int j = 0; j < kRound; ++j) {
       const int idx = tid + (j0 + j) * kSmThreads;
       const int rt = idx / pieces, pc = idx - rt * pieces;
-      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a + rt * ld + pc * 8) = stage[j];
+      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a[0] + rt * ld + pc * 8) = stage[j];
     }
   }
 
@@ -181,7 +183,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
 #pragma unroll
     for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
       if (ks < ksteps) {
-        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a + (h * 16 + (lane & 15)) * ld + ks * 32 +
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a[0] + (h * 16 + (lane & 15)) * ld + ks * 32 +
                                                            (lane >> 4) * 8);
 #pragma unroll
         for (int ms = 0; ms < kSmMS; ++ms)
@@ -200,7 +202,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
         t[ms * 4 + i] = LT && in ? qt[h][ms].at(i) : neg_inf();
       }
     }
-    epi(h, d, t, vb + 4 * (lane >> 4));
+    epi(h, d, t, vb + 4 * (lane >> 4), 0);
   }
 }
 
@@ -250,42 +252,51 @@ __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)
   }
 }
 
-// All row tiles of one look, for 4-aligned rows.  Per tile: the rows'
-// metadata (meta(row) -> LDS) and W1 rows are staged; the second half of
-// the tile's values is requested before the first half is used, and the
-// next tile's first half before the second half is used, so the workgroup
-// always has loads in flight.  epi as for sm_tile; merge(row0) after each
-// tile's passes (LDS partials complete).
+// All row tiles of one look, for 4-aligned rows, with one barrier per tile
+// (LDS buffers indexed by tile parity).  While tile t runs, its second half
+// of values is requested before its first half is used, and tile t + 1's
+// first half before its second half is used; tile t - 1's partials are
+// merged after tile t's barrier.  PIPE: tile t + 1's forced tokens,
+// metadata and W1 rows are also requested during tile t (held in registers
+// across its second half, written to the other buffers after it); without
+// PIPE (for the look that has no registers to spare) each tile is staged at
+// its start.  All global loads are unconditional (past the last row: empty
+// resources or clamped rows), so the compiler's wait counts stay exact.
+// meta_load(row) reads a row's metadata (any row; clamped by the caller),
+// meta_make(rec, row) turns it into the LDS record; epi(h, d, t, v00, parity)
+// as for sm_tile; merge(row0, parity) once a tile's partials are complete.
 // MASK: tokens past the vocabulary are excluded element by element; without
 // it (V a multiple of 64) a wave's tokens are all in or all out, and a wave
-// past the vocabulary hands its epilogue -inf values.
-template <typename T, bool LT, bool MASK, class Meta, class Epi, class Merge>
+// past the vocabulary hands its epilogue -inf values.  RMAX: the rank is
+// the maximum (the k loop and the staging indexes are then compile-time).
+template <typename T, bool LT, bool MASK, bool RMAX, bool PIPE, class MetaLoad, class MetaMake, class Epi,
+          class Merge>
 __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
-                                            SmLds& L, Meta&& meta, Epi&& epi, Merge&& merge) {
+                                            SmLds& L, MetaLoad&& meta_load, MetaMake&& meta_make, Epi&& epi,
+                                            Merge&& merge) {
+  if (a.rows <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vb = tok0 + wave * 16 * kSmMS;
-  const int V = a.V, r = a.r;
+  const int V = a.V, r = RMAX ? kSmMaxR : a.r;
   const bool dead = __builtin_amdgcn_readfirstlane(vb) >= V;  // wave-uniform
   const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
   const int pieces = kpad / 8;
   constexpr int kMaxPieces = kSmTile * (kSmMaxR / 8) / kSmThreads;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
-  Quad<T> qA[2][kSmMS], tA[2][kSmMS], qB[2][kSmMS], tB[2][kSmMS];
-  load_half<T, LT>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
-  for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-    if (tid < kSmTile) L.meta[tid] = meta(row0 + tid);
-    // W1 rows of the tile's forced tokens
-    int32_t xs[kMaxPieces];
+
+  // the forced tokens of the thread's staging pieces of tile row0
+  auto load_xs = [&](int row0, int32_t (&xs)[kMaxPieces]) {
 #pragma unroll
     for (int j = 0; j < kMaxPieces; ++j) {
-      const int idx = tid + j * kSmThreads;
-      const int row = row0 + idx / pieces;
+      const int row = row0 + (tid + j * kSmThreads) / pieces;
       const int rr = row < a.rows ? row : 0;
       const int k = rr % a.gamma;
       xs[j] = *(k == 0 ? a.anchor + rr / a.gamma : a.teacher + (rr - 1));  // one load, no branch
     }
-    uint4 stage[kMaxPieces];
+  };
+  // their W1 pieces (past the last row or the rank: the resource's empty offset)
+  auto load_w1 = [&](int row0, const int32_t (&xs)[kMaxPieces], uint4 (&stage)[kMaxPieces]) {
 #pragma unroll
     for (int j = 0; j < kMaxPieces; ++j) {
       const int idx = tid + j * kSmThreads;
@@ -295,23 +306,57 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
                                : 0xfffffff0u;
       stage[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
     }
+  };
+  auto store_w1 = [&](int buf, const uint4 (&stage)[kMaxPieces]) {
 #pragma unroll
     for (int j = 0; j < kMaxPieces; ++j) {
       const int idx = tid + j * kSmThreads;
       const int rt = idx / pieces, pc = idx - rt * pieces;
-      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a + rt * ld + pc * 8) = stage[j];
+      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a[buf] + rt * ld + pc * 8) = stage[j];
     }
-    __syncthreads();
+  };
+  auto meta_row = [&](int row0) { return min(row0 + (tid & (kSmTile - 1)), a.rows - 1); };
+
+  Quad<T> qA[2][kSmMS], tA[2][kSmMS], qB[2][kSmMS], tB[2][kSmMS];
+  int32_t xs[kMaxPieces];
+  uint4 stage[kMaxPieces];
+  SmRec mrec;
+  if constexpr (PIPE) {  // prologue: tile 0 staged
+    load_xs(0, xs);
+    mrec = meta_load(meta_row(0));
+    load_w1(0, xs, stage);
+    if (tid < kSmTile) L.meta[0][tid] = meta_make(mrec, tid);
+    store_w1(0, stage);
+  }
+  load_half<T, LT>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
+
+  int par = 0;
+  for (int row0 = 0; row0 < a.rows; row0 += kSmTile, par ^= 1) {
+    if constexpr (!PIPE) {  // buffers par were last read in tile t - 2
+      load_xs(row0, xs);
+      mrec = meta_load(meta_row(row0));
+      load_w1(row0, xs, stage);
+      if (tid < kSmTile) L.meta[par][tid] = meta_make(mrec, row0 + tid);
+      store_w1(par, stage);
+    }
+    __syncthreads();  // tile row0 staged in buffers par; tile row0 - 64's partials complete
+    if (row0 > 0) merge(row0 - kSmTile, par ^ 1);
+    const int next = min(row0 + kSmTile, a.rows);  // a.rows: nothing left, loads come back empty
     load_half<T, LT>(qB, tB, tile_rs<T>(a, row0), 2, vb, lane, V);
+    if constexpr (PIPE) {
+      load_xs(next, xs);
+      mrec = meta_load(meta_row(next));
+    }
 
     auto pass = [&](int h, const Quad<T> (&qd)[kSmMS], const Quad<T> (&qt)[kSmMS]) {
+      // the accumulator starts from the backbone values: d = backbone + bias
       f32x4 acc[kSmMS];
 #pragma unroll
-      for (int ms = 0; ms < kSmMS; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ms = 0; ms < kSmMS; ++ms) acc[ms] = f32x4{qd[ms].at(0), qd[ms].at(1), qd[ms].at(2), qd[ms].at(3)};
 #pragma unroll
       for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
         if (ks < ksteps) {
-          const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a + (h * 16 + (lane & 15)) * ld + ks * 32 +
+          const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(L.a[par] + (h * 16 + (lane & 15)) * ld + ks * 32 +
                                                              (lane >> 4) * 8);
 #pragma unroll
           for (int ms = 0; ms < kSmMS; ++ms)
@@ -325,26 +370,28 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool in = !MASK || v0 + i < V;
-          d[ms * 4 + i] = in ? qd[ms].at(i) + acc[ms][i] : neg_inf();
+          d[ms * 4 + i] = in ? acc[ms][i] : neg_inf();
           t[ms * 4 + i] = LT && in ? qt[ms].at(i) : neg_inf();
         }
       }
       if (!MASK && dead)
 #pragma unroll
         for (int e = 0; e < 4 * kSmMS; ++e) d[e] = t[e] = neg_inf();
-      epi(h, d, t, vb + 4 * (lane >> 4));
+      epi(h, d, t, vb + 4 * (lane >> 4), par);
     };
     pass(0, qA[0], tA[0]);
     pass(1, qA[1], tA[1]);
-    // unconditional (past the last tile the resource is empty and the loads
-    // return zeros), so that both paths reach the next waits alike
-    load_half<T, LT>(qA, tA, tile_rs<T>(a, min(row0 + kSmTile, a.rows)), 0, vb, lane, V);
+    if constexpr (PIPE) load_w1(next, xs, stage);
+    load_half<T, LT>(qA, tA, tile_rs<T>(a, next), 0, vb, lane, V);
     pass(2, qB[0], tB[0]);
     pass(3, qB[1], tB[1]);
-    __syncthreads();
-    merge(row0);
-    __syncthreads();  // the LDS tile is reused by the next tile
+    if constexpr (PIPE) {  // buffers par ^ 1 were last read before this tile's barrier
+      if (tid < kSmTile) L.meta[par ^ 1][tid] = meta_make(mrec, next + tid);
+      store_w1(par ^ 1, stage);
+    }
   }
+  __syncthreads();
+  merge(((a.rows - 1) / kSmTile) * kSmTile, par ^ 1);
 }
 
 // W2 fragments of the wave's 16 MS tokens [vb, vb + 16 MS) (A operand).
@@ -367,7 +414,7 @@ __device__ __forceinline__ void sm_load_w2(bf16x8 (&af)[kSmMS][kSmMaxR / 32], co
 // Look 1: per (row, workgroup) record of the draft values' (max, sum exp)
 // (the target rows are not needed: their normalisers do not involve the bias,
 // stats_markov_tnorm; nor is the teacher's value, stats_markov_teacher).
-template <typename T, bool VEC, bool MASK>
+template <typename T, bool VEC, bool MASK, bool RMAX>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a) {
   __shared__ SmLds L;
   const int g = blockIdx.x, G = gridDim.x;
@@ -375,45 +422,48 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  auto meta = [](int) { return SmRec{}; };
-  auto epi = [&](int h, const float* d, const float*, int) {
+  auto meta_load = [](int) { return SmRec{}; };
+  auto meta_make = [](const SmRec&, int) { return SmRec{}; };
+  auto epi = [&](int h, const float* d, const float*, int, int p) {
     float md = neg_inf();
 #pragma unroll
     for (int e = 0; e < 4 * kSmMS; ++e) md = fmaxf(md, d[e]);
     md = rows_max(md);
+    // exp(d - md) = 2^(d log2e - mh) 2^-ml, with mh the fp32 product md log2e
+    // and ml its rounding residual (one FMA per element, the residual once)
+    const float mh = md > neg_inf() ? md * kLog2e : 0.0f;
+    const float ml = md > neg_inf() ? fmaf(md, kLog2e, -mh) : 0.0f;
     float sd = 0.0f;
-    if (md > neg_inf())
 #pragma unroll
-      for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f((d[e] - md) * kLog2e);
-    sd = rows_sum(sd);
+    for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -mh));
+    sd = rows_sum(sd) * __builtin_amdgcn_exp2f(-ml);
     if (lane < 16) {
       const int n = h * 16 + lane;
-      L.m[0][wave][n] = md;
-      L.s[0][wave][n] = sd;
+      L.m[p][wave][n] = md;
+      L.s[p][wave][n] = sd;
     }
   };
-  auto merge = [&](int row0) {
+  auto merge = [&](int row0, int p) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       const int n = threadIdx.x;
       float m = neg_inf();
 #pragma unroll
-      for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[0][w][n]);
+      for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[p][w][n]);
       float s = 0.0f;
       if (m > neg_inf())
 #pragma unroll
         for (int w = 0; w < kSmWaves; ++w)
-          if (L.m[0][w][n] > neg_inf()) s += L.s[0][w][n] * __builtin_amdgcn_exp2f((L.m[0][w][n] - m) * kLog2e);
+          if (L.m[p][w][n] > neg_inf()) s += L.s[p][w][n] * __builtin_amdgcn_exp2f((L.m[p][w][n] - m) * kLog2e);
       a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{m, s, 0.0f, 0.0f};
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T, false, MASK>(a, af, tok0, L, meta, epi, merge);
+    sm_look_vec<T, false, MASK, RMAX, true>(a, af, tok0, L, meta_load, meta_make, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-      if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
-      sm_tile<T, VEC, false>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
+      sm_tile<T, VEC, false>(a, af, tok0, row0, L, epi);
       __syncthreads();
-      merge(row0);
+      merge(row0, 0);
       __syncthreads();  // the LDS tile is reused by the next tile
     }
   }
@@ -525,7 +575,7 @@ __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_
 }
 
 // Look 2: per (row, workgroup) share of sum |P - T|.
-template <typename T, bool VEC, bool MASK>
+template <typename T, bool VEC, bool MASK, bool RMAX>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a) {
   __shared__ SmLds L;
   const int g = blockIdx.x, G = gridDim.x;
@@ -533,34 +583,45 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  auto meta = [&](int row) { return row < a.rows ? a.norm[row] : SmRec{0.0f, 1.0f, 0.0f, 1.0f}; };
-  auto epi = [&](int h, const float* d, const float* t, int) {
-    const SmRec nr = L.meta[h * 16 + (lane & 15)];
-    const float isd = 1.0f / nr.sd, ist = 1.0f / nr.st;
+  // per row: P_v = 2^(d_v log2e - dh) cd and T_v = 2^(t_v log2e - th) ct, with
+  // dh = md log2e in fp32 and cd = 2^-(its rounding residual) / sd (likewise
+  // for the target); the record holds (dh, cd, th, ct / cd), so that
+  // |P_v - T_v| = cd |2^(..d..) - (ct / cd) 2^(..t..)| costs three FMAs
+  auto meta_load = [&](int row) { return a.norm[row]; };
+  auto meta_make = [&](const SmRec& nr, int row) {
+    if (row >= a.rows) return SmRec{0.0f, 0.0f, 0.0f, 0.0f};
+    const float dh = nr.md * kLog2e, th = nr.mt * kLog2e;
+    const float cd = __builtin_amdgcn_exp2f(-fmaf(nr.md, kLog2e, -dh)) / nr.sd;
+    const float ct = __builtin_amdgcn_exp2f(-fmaf(nr.mt, kLog2e, -th)) / nr.st;
+    return SmRec{dh, cd, th, ct / cd};
+  };
+  auto epi = [&](int h, const float* d, const float* t, int, int p) {
+    const SmRec k = L.meta[p][h * 16 + (lane & 15)];
     float l1 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4 * kSmMS; ++e)
-      l1 += fabsf(__builtin_amdgcn_exp2f((d[e] - nr.md) * kLog2e) * isd -
-                  __builtin_amdgcn_exp2f((t[e] - nr.mt) * kLog2e) * ist);
-    l1 = rows_sum(l1);
-    if (lane < 16) L.s[0][wave][h * 16 + lane] = l1;
+      l1 += fabsf(fmaf(-k.st, __builtin_amdgcn_exp2f(fmaf(t[e], kLog2e, -k.mt)),
+                       __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -k.md))));
+    l1 = rows_sum(l1) * k.sd;
+    if (lane < 16) L.s[p][wave][h * 16 + lane] = l1;
   };
-  auto merge = [&](int row0) {
+  auto merge = [&](int row0, int p) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kSmWaves; ++w) s += L.s[0][w][threadIdx.x];
+      for (int w = 0; w < kSmWaves; ++w) s += L.s[p][w][threadIdx.x];
       a.l1part[static_cast<size_t>(row0 + threadIdx.x) * G + g] = s;
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T, true, MASK>(a, af, tok0, L, meta, epi, merge);
+    sm_look_vec<T, true, MASK, RMAX, false>(a, af, tok0, L, meta_load, meta_make, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-      if (threadIdx.x < kSmTile) L.meta[threadIdx.x] = meta(row0 + threadIdx.x);
-      sm_tile<T, VEC, true>(a, af, tok0, row0, L, epi);
+      const int row = row0 + static_cast<int>(threadIdx.x);
+      if (threadIdx.x < kSmTile) L.meta[0][threadIdx.x] = meta_make(meta_load(row < a.rows ? row : 0), row);
+      sm_tile<T, VEC, true>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
       __syncthreads();
-      merge(row0);
+      merge(row0, 0);
       __syncthreads();
     }
   }
@@ -587,6 +648,33 @@ __global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32
   }
 }
 
+// One of the looks, in the instance the shapes allow: aligned rows or not,
+// V a multiple of 64 or not (the token mask), the maximum rank or not.
+template <typename T, int LOOK, bool VEC, bool MASK, bool RMAX>
+hipError_t launch_look_inst(const SmArgs& a, int G, hipStream_t st) {
+  if constexpr (LOOK == 1)
+    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, VEC, MASK, RMAX>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
+  else
+    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, VEC, MASK, RMAX>), dim3(G), dim3(kSmThreads), 0,
+                  st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int LOOK>
+hipError_t launch_look_t(const SmArgs& a, int G, bool vec, bool mask, bool rmax, hipStream_t st) {
+  if (!vec) return launch_look_inst<T, LOOK, false, true, false>(a, G, st);
+  if (mask) return rmax ? launch_look_inst<T, LOOK, true, true, true>(a, G, st)
+                        : launch_look_inst<T, LOOK, true, true, false>(a, G, st);
+  return rmax ? launch_look_inst<T, LOOK, true, false, true>(a, G, st)
+              : launch_look_inst<T, LOOK, true, false, false>(a, G, st);
+}
+
+template <typename T>
+hipError_t launch_look(const SmArgs& a, int G, bool vec, bool mask, bool rmax, int look, hipStream_t st) {
+  return look == 1 ? launch_look_t<T, 1>(a, G, vec, mask, rmax, st) : launch_look_t<T, 2>(a, G, vec, mask, rmax, st);
+}
+
 template <typename T>
 hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, const uint8_t* block_mask,
                            int32_t N, float w_ce, float w_l1, float w_conf, float* l1, float* accept_rate,
@@ -597,16 +685,9 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
                    reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
                    static_cast<uint64_t>(kSmTile) * a.V * sizeof(T) < 0x7fffffffull &&
                    static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull;
-  const bool mask = a.V % 64 != 0;
-  if (vec && !mask)
-    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true, false>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
-  else if (vec)
-    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, true, true>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
-  else
-    DSPARK_LAUNCH("stats_markov_look1", (stats_markov_look1_kernel<T, false, true>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
+  const bool mask = a.V % 64 != 0, rmax = a.r == kSmMaxR;
+  hipError_t e = launch_look<T>(a, G, vec, mask, rmax, 1, st);
+  if (e != hipSuccess) return e;
   DSPARK_LAUNCH("stats_markov_teacher", stats_markov_teacher_kernel<T>, dim3(rb), dim3(256), 0, st, a);
   const int epl = 16 / static_cast<int>(sizeof(T));
   const bool tvec = a.V % epl == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
@@ -616,18 +697,11 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
   else
     DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, false>), tgrid, dim3(kTnThreads), 0, st, a);
   DSPARK_LAUNCH("stats_markov_rows", stats_markov_rows_kernel, dim3(rb), dim3(256), 0, st, a, G);
-  if (vec && !mask)
-    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true, false>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
-  else if (vec)
-    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, true, true>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
-  else
-    DSPARK_LAUNCH("stats_markov_look2", (stats_markov_look2_kernel<T, false, true>), dim3(G), dim3(kSmThreads), 0,
-                  st, a);
+  e = launch_look<T>(a, G, vec, mask, rmax, 2, st);
+  if (e != hipSuccess) return e;
   DSPARK_LAUNCH("stats_markov_final", stats_markov_final_kernel, dim3(rb), dim3(256), 0, st, a, G,
                 conf_logits, l1, accept_rate, ce, bce);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_stats_reduce(l1, accept_rate, ce, bce, block_mask, N, a.gamma, w_ce, w_l1, w_conf, tau, sums,
                              st);
