@@ -44,6 +44,13 @@ constexpr int kSmTokens = kSmWaves * 16 * kSmMS;
 constexpr int kSmTile = 64;      // rows per tile (MFMA N side)
 constexpr int kSmMaxR = DSPARK_MAX_RANK;
 constexpr int kSmPad = 8;
+// The aligned path stages a tile's W1 rows by LDS-DMA buffer loads: each
+// wave instruction fills 64 consecutive 16-byte slots, rows of kpad / 8
+// slots plus one padding slot (up to 33 x 64 slots), kSmDma instructions
+// per wave; slots past the tile land in the buffer's slack (zeros).
+constexpr int kSmDma = (kSmTile * (kSmMaxR / 8 + 1) / 64 + kSmWaves - 1) / kSmWaves;
+constexpr int kSmABuf = kSmDma * kSmWaves * 64 * 8;  // elements per W1 buffer
+static_assert(kSmABuf >= kSmTile * (kSmMaxR + kSmPad), "W1 buffer");
 
 struct SmRec {
   float md, sd, mt, st;  // max and sum exp(x - max) of the draft and target values
@@ -61,12 +68,13 @@ struct SmArgs {
   float* dteach;    // [rows]: the draft value at the teacher token
   SmRec* norm;      // [rows]: per-row normalisers (after look 1)
   float* l1part;    // [rows][G] (look 2)
+  SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, ct / cd)
 };
 
 // Two of everything: the aligned path stages tile t + 1 and merges tile
 // t - 1 while tile t runs (index = tile parity); the unaligned path uses 0.
 struct SmLds {
-  __attribute__((aligned(16))) uint16_t a[2][kSmTile * (kSmMaxR + kSmPad)];  // staged W1 rows
+  __attribute__((aligned(16))) uint16_t a[2][kSmABuf];  // staged W1 rows, kSmMaxR + kSmPad apart
   float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];                 // per (parity, wave, row)
   SmRec meta[2][kSmTile];  // per (parity, row): look 2 the constants of its epilogue
 };
@@ -115,11 +123,22 @@ __device__ __forceinline__ int32_t forced_token(const SmArgs& a, int row) {
   return clamp_token(x, a.V);
 }
 
+// Token (offset in the wave's 64) of MFMA A row m of 16-token block ms; the
+// accumulator element i of lane l holds A row 4 (l >> 4) + i.  Without PERM
+// block ms is tokens 16 ms .. 16 ms + 15; with PERM (the aligned path) the
+// blocks interleave so that a lane's 16 elements are two runs of 8
+// consecutive tokens: 32 (ms / 2) + 8 (m / 4) + 4 (ms % 2) + m % 4.
+template <bool PERM>
+__device__ __forceinline__ int sm_tok(int ms, int m) {
+  return PERM ? 32 * (ms >> 1) + 8 * (m >> 2) + 4 * (ms & 1) + (m & 3) : 16 * ms + m;
+}
+
 // One look over the row tile [row0, row0 + 64) for the workgroup's tokens
 // (any row alignment): stages the W1 rows, forms the bias tile on MFMA, adds
-// the backbone values and calls epi(pass h, d[16], t[16], token of element 0)
-// for every 16-row pass, element e of the lane's 16 being token
-// v00 + (e / 4) 16 + e % 4 of row row0 + h 16 + lane % 16.
+// the backbone values and calls epi(pass h, d[16], t[16], parity 0) for
+// every 16-row pass, element e of the lane's 16 being token
+// vb + sm_tok<false>(e / 4, 4 (lane / 16) + e % 4) of row row0 + h 16 +
+// lane % 16 (the epilogues reduce over tokens and need no token numbers).
 template <typename T, bool VEC, bool LT, class Epi>
 __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
                                         int row0, SmLds& L, Epi&& epi) {
@@ -202,7 +221,7 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
         t[ms * 4 + i] = LT && in ? qt[h][ms].at(i) : neg_inf();
       }
     }
-    epi(h, d, t, vb + 4 * (lane >> 4), 0);
+    epi(h, d, t, 0);
   }
 }
 
@@ -225,128 +244,112 @@ __device__ __forceinline__ TileRs<T> tile_rs(const SmArgs& a, int row0) {
 }
 
 // The backbone and target quads of passes h0, h0 + 1 (16 rows each) of a tile.
+// With the aligned path's token order (sm_tok<true>) a lane's quads ms and
+// ms + 1 (ms even) are 8 consecutive tokens: bf16 rows take one 16-byte load
+// for both, and a row's 16 lanes read 64 contiguous bytes per load.
 template <typename T, bool LT>
 __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)[2][kSmMS], const TileRs<T>& rs,
                                           int h0, int vb, int lane, int V) {
+  auto f4 = [](const u32x4& x) {
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+  };
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const uint32_t n = static_cast<uint32_t>((h0 + hh) * 16 + (lane & 15));
 #pragma unroll
-    for (int ms = 0; ms < kSmMS; ++ms) {
-      const uint32_t v0 = static_cast<uint32_t>(vb + ms * 16 + 4 * (lane >> 4));
+    for (int ms = 0; ms < kSmMS; ms += (sizeof(T) == 2 ? 2 : 1)) {
+      const uint32_t v0 = static_cast<uint32_t>(vb + sm_tok<true>(ms, 4 * (lane >> 4)));
       const uint32_t off = (n * static_cast<uint32_t>(V) + v0) * sizeof(T);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs.d, off, 0, 0);
+      const u32x4 y = LT ? __builtin_amdgcn_raw_buffer_load_b128(rs.t, off, 0, 0) : u32x4{};
       if constexpr (sizeof(T) == 2) {
-        qd[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.d, off, 0, 0));
-        if constexpr (LT) qt[hh][ms].u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.t, off, 0, 0));
-      } else {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs.d, off, 0, 0);
-        qd[hh][ms].u = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                                   __uint_as_float(x[3]));
+        qd[hh][ms].u = make_uint2(x[0], x[1]);
+        qd[hh][ms + 1].u = make_uint2(x[2], x[3]);
         if constexpr (LT) {
-          const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rs.t, off, 0, 0);
-          qt[hh][ms].u = make_float4(__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
-                                     __uint_as_float(y[3]));
+          qt[hh][ms].u = make_uint2(y[0], y[1]);
+          qt[hh][ms + 1].u = make_uint2(y[2], y[3]);
         }
+      } else {
+        qd[hh][ms].u = f4(x);
+        if constexpr (LT) qt[hh][ms].u = f4(y);
       }
     }
   }
 }
 
-// All row tiles of one look, for 4-aligned rows, with one barrier per tile
-// (LDS buffers indexed by tile parity).  While tile t runs, its second half
-// of values is requested before its first half is used, and tile t + 1's
-// first half before its second half is used; tile t - 1's partials are
-// merged after tile t's barrier.  PIPE: tile t + 1's forced tokens,
-// metadata and W1 rows are also requested during tile t (held in registers
-// across its second half, written to the other buffers after it); without
-// PIPE (for the look that has no registers to spare) each tile is staged at
-// its start.  All global loads are unconditional (past the last row: empty
-// resources or clamped rows), so the compiler's wait counts stay exact.
-// meta_load(row) reads a row's metadata (any row; clamped by the caller),
-// meta_make(rec, row) turns it into the LDS record; epi(h, d, t, v00, parity)
-// as for sm_tile; merge(row0, parity) once a tile's partials are complete.
+// All row tiles of one look, for 4-aligned rows, software-pipelined with
+// one barrier per tile (LDS buffers indexed by tile parity).  While tile t
+// runs: its second half of values is requested before its first half is
+// used, and tile t + 1's first half before its second half is used; tile
+// t + 1's forced tokens are read during tile t's first half and its W1 rows
+// (and, with META, its rows' records from meta[]) go by LDS-DMA loads into
+// the other buffers during its second half, holding no registers; tile
+// t - 1's partials are merged after tile t's barrier (which waits for the
+// DMA).  All global loads are unconditional (past the last row: empty
+// resources, zero fills or clamped rows), so the compiler's wait counts stay
+// exact.  epi(h, d, t, parity) as for sm_tile (token order sm_tok<true>);
+// merge(row0, parity) once
+// a tile's partials are complete.
 // MASK: tokens past the vocabulary are excluded element by element; without
 // it (V a multiple of 64) a wave's tokens are all in or all out, and a wave
 // past the vocabulary hands its epilogue -inf values.  RMAX: the rank is
 // the maximum (the k loop and the staging indexes are then compile-time).
-template <typename T, bool LT, bool MASK, bool RMAX, bool PIPE, class MetaLoad, class MetaMake, class Epi,
-          class Merge>
+template <typename T, bool LT, bool MASK, bool RMAX, bool META, class Epi, class Merge>
 __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
-                                            SmLds& L, MetaLoad&& meta_load, MetaMake&& meta_make, Epi&& epi,
-                                            Merge&& merge) {
+                                            SmLds& L, const SmRec* meta, Epi&& epi, Merge&& merge) {
+  typedef __attribute__((address_space(3))) void lds_void;
   if (a.rows <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int vb = tok0 + wave * 16 * kSmMS;
   const int V = a.V, r = RMAX ? kSmMaxR : a.r;
   const bool dead = __builtin_amdgcn_readfirstlane(vb) >= V;  // wave-uniform
   const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
-  const int pieces = kpad / 8;
-  constexpr int kMaxPieces = kSmTile * (kSmMaxR / 8) / kSmThreads;
+  const int slots = kpad / 8 + 1;  // 16-byte slots per staged row
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<SmRec*>(meta), static_cast<short>(0), META ? a.rows * 16 : 0, kBufferWord3);
 
-  // the forced tokens of the thread's staging pieces of tile row0
-  auto load_xs = [&](int row0, int32_t (&xs)[kMaxPieces]) {
+  // the forced tokens of the rows of the thread's DMA slots of tile row0
+  auto load_xs = [&](int row0, int32_t (&xs)[kSmDma]) {
 #pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int row = row0 + (tid + j * kSmThreads) / pieces;
-      const int rr = row < a.rows ? row : 0;
+    for (int j = 0; j < kSmDma; ++j) {
+      const int n = ((j * kSmWaves + wv) * 64 + lane) / slots;
+      const int row = row0 + n;
+      const int rr = n < kSmTile && row < a.rows ? row : 0;
       const int k = rr % a.gamma;
       xs[j] = *(k == 0 ? a.anchor + rr / a.gamma : a.teacher + (rr - 1));  // one load, no branch
     }
   };
-  // their W1 pieces (past the last row or the rank: the resource's empty offset)
-  auto load_w1 = [&](int row0, const int32_t (&xs)[kMaxPieces], uint4 (&stage)[kMaxPieces]) {
+  // tile row0's W1 rows (and records) into buffers buf
+  auto stage = [&](int row0, int buf, const int32_t (&xs)[kSmDma]) {
 #pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int idx = tid + j * kSmThreads;
-      const int rt = idx / pieces, pc = idx - rt * pieces;
-      const uint32_t off = (pc * 8 < r && row0 + rt < a.rows)
-                               ? static_cast<uint32_t>((clamp_token(xs[j], V) * r + pc * 8) * 2)
-                               : 0xfffffff0u;
-      stage[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    for (int j = 0; j < kSmDma; ++j) {
+      const int q = j * kSmWaves + wv;
+      const int sl = q * 64 + lane, n = sl / slots, c = sl - n * slots;
+      const bool ok = n < kSmTile && c < slots - 1 && c * 8 < r && row0 + n < a.rows;
+      const uint32_t off = ok ? static_cast<uint32_t>((clamp_token(xs[j], V) * r + c * 8) * 2) : 0xfffffff0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(L.a[buf] + q * 64 * 8), 16, off, 0, 0, 0);
     }
+    if constexpr (META)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(L.meta[buf]), 16,
+                                               static_cast<uint32_t>(min(row0 + lane, a.rows - 1)) * 16, 0, 0, 0);
   };
-  auto store_w1 = [&](int buf, const uint4 (&stage)[kMaxPieces]) {
-#pragma unroll
-    for (int j = 0; j < kMaxPieces; ++j) {
-      const int idx = tid + j * kSmThreads;
-      const int rt = idx / pieces, pc = idx - rt * pieces;
-      if (rt < kSmTile) *reinterpret_cast<uint4*>(L.a[buf] + rt * ld + pc * 8) = stage[j];
-    }
-  };
-  auto meta_row = [&](int row0) { return min(row0 + (tid & (kSmTile - 1)), a.rows - 1); };
 
   Quad<T> qA[2][kSmMS], tA[2][kSmMS], qB[2][kSmMS], tB[2][kSmMS];
-  int32_t xs[kMaxPieces];
-  uint4 stage[kMaxPieces];
-  SmRec mrec;
-  if constexpr (PIPE) {  // prologue: tile 0 staged
-    load_xs(0, xs);
-    mrec = meta_load(meta_row(0));
-    load_w1(0, xs, stage);
-    if (tid < kSmTile) L.meta[0][tid] = meta_make(mrec, tid);
-    store_w1(0, stage);
-  }
+  int32_t xs[kSmDma];
+  load_xs(0, xs);
+  stage(0, 0, xs);
   load_half<T, LT>(qA, tA, tile_rs<T>(a, 0), 0, vb, lane, V);
 
   int par = 0;
   for (int row0 = 0; row0 < a.rows; row0 += kSmTile, par ^= 1) {
-    if constexpr (!PIPE) {  // buffers par were last read in tile t - 2
-      load_xs(row0, xs);
-      mrec = meta_load(meta_row(row0));
-      load_w1(row0, xs, stage);
-      if (tid < kSmTile) L.meta[par][tid] = meta_make(mrec, row0 + tid);
-      store_w1(par, stage);
-    }
     __syncthreads();  // tile row0 staged in buffers par; tile row0 - 64's partials complete
     if (row0 > 0) merge(row0 - kSmTile, par ^ 1);
     const int next = min(row0 + kSmTile, a.rows);  // a.rows: nothing left, loads come back empty
     load_half<T, LT>(qB, tB, tile_rs<T>(a, row0), 2, vb, lane, V);
-    if constexpr (PIPE) {
-      load_xs(next, xs);
-      mrec = meta_load(meta_row(next));
-    }
+    load_xs(next, xs);
 
     auto pass = [&](int h, const Quad<T> (&qd)[kSmMS], const Quad<T> (&qt)[kSmMS]) {
       // the accumulator starts from the backbone values: d = backbone + bias
@@ -366,7 +369,7 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
       float d[4 * kSmMS], t[4 * kSmMS];
 #pragma unroll
       for (int ms = 0; ms < kSmMS; ++ms) {
-        const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+        const int v0 = vb + sm_tok<true>(ms, 4 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool in = !MASK || v0 + i < V;
@@ -377,30 +380,28 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
       if (!MASK && dead)
 #pragma unroll
         for (int e = 0; e < 4 * kSmMS; ++e) d[e] = t[e] = neg_inf();
-      epi(h, d, t, vb + 4 * (lane >> 4), par);
+      epi(h, d, t, par);
     };
     pass(0, qA[0], tA[0]);
     pass(1, qA[1], tA[1]);
-    if constexpr (PIPE) load_w1(next, xs, stage);
+    stage(next, par ^ 1, xs);  // buffers par ^ 1 were last read before this tile's barrier
     load_half<T, LT>(qA, tA, tile_rs<T>(a, next), 0, vb, lane, V);
     pass(2, qB[0], tB[0]);
     pass(3, qB[1], tB[1]);
-    if constexpr (PIPE) {  // buffers par ^ 1 were last read before this tile's barrier
-      if (tid < kSmTile) L.meta[par ^ 1][tid] = meta_make(mrec, next + tid);
-      store_w1(par ^ 1, stage);
-    }
   }
   __syncthreads();
   merge(((a.rows - 1) / kSmTile) * kSmTile, par ^ 1);
 }
 
-// W2 fragments of the wave's 16 MS tokens [vb, vb + 16 MS) (A operand).
+// W2 fragments of the wave's 16 MS tokens [vb, vb + 16 MS) (A operand), in
+// the token order of the path (sm_tok<PERM>).
+template <bool PERM>
 __device__ __forceinline__ void sm_load_w2(bf16x8 (&af)[kSmMS][kSmMaxR / 32], const uint16_t* w2, int vb, int V,
                                            int r, int lane) {
   const int ksteps = ((r + 31) & ~31) / 32;
 #pragma unroll
   for (int ms = 0; ms < kSmMS; ++ms) {
-    const int v = vb + ms * 16 + (lane & 15);
+    const int v = vb + sm_tok<PERM>(ms, lane & 15);
 #pragma unroll
     for (int ks = 0; ks < kSmMaxR / 32; ++ks) {
       const int k0 = ks * 32 + (lane >> 4) * 8;
@@ -421,10 +422,8 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
-  sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  auto meta_load = [](int) { return SmRec{}; };
-  auto meta_make = [](const SmRec&, int) { return SmRec{}; };
-  auto epi = [&](int h, const float* d, const float*, int, int p) {
+  sm_load_w2<VEC>(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
+  auto epi = [&](int h, const float* d, const float*, int p) {
     float md = neg_inf();
 #pragma unroll
     for (int e = 0; e < 4 * kSmMS; ++e) md = fmaxf(md, d[e]);
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T, false, MASK, RMAX, true>(a, af, tok0, L, meta_load, meta_make, epi, merge);
+    sm_look_vec<T, false, MASK, RMAX, false>(a, af, tok0, L, nullptr, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
       sm_tile<T, VEC, false>(a, af, tok0, row0, L, epi);
@@ -553,7 +552,8 @@ __global__ __launch_bounds__(kTnThreads) void stats_markov_tnorm_kernel(SmArgs a
   }
 }
 
-// Per row: the draft normaliser from the row's G look-1 records.
+// Per row: the draft normaliser from the row's G look-1 records, and look 2's
+// per-row constants (the target normaliser is stats_markov_tnorm's).
 __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_t G) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -569,8 +569,16 @@ __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_
   }
   sd = wave_sum(sd);
   if (lane == 0) {  // the target half (mt, st) is stats_markov_tnorm's
-    a.norm[row].md = md;
-    a.norm[row].sd = sd;
+    SmRec nr = a.norm[row];
+    nr.md = md;
+    nr.sd = sd;
+    a.norm[row] = nr;
+    // look 2's constants: P_v = 2^(d_v log2e - dh) cd with dh = md log2e in
+    // fp32 and cd = 2^-(its rounding residual) / sd; likewise for the target
+    const float dh = nr.md * kLog2e, th = nr.mt * kLog2e;
+    const float cd = __builtin_amdgcn_exp2f(-fmaf(nr.md, kLog2e, -dh)) / nr.sd;
+    const float ct = __builtin_amdgcn_exp2f(-fmaf(nr.mt, kLog2e, -th)) / nr.st;
+    a.k2[row] = SmRec{dh, cd, th, ct / cd};
   }
 }
 
@@ -582,20 +590,10 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
-  sm_load_w2(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  // per row: P_v = 2^(d_v log2e - dh) cd and T_v = 2^(t_v log2e - th) ct, with
-  // dh = md log2e in fp32 and cd = 2^-(its rounding residual) / sd (likewise
-  // for the target); the record holds (dh, cd, th, ct / cd), so that
-  // |P_v - T_v| = cd |2^(..d..) - (ct / cd) 2^(..t..)| costs three FMAs
-  auto meta_load = [&](int row) { return a.norm[row]; };
-  auto meta_make = [&](const SmRec& nr, int row) {
-    if (row >= a.rows) return SmRec{0.0f, 0.0f, 0.0f, 0.0f};
-    const float dh = nr.md * kLog2e, th = nr.mt * kLog2e;
-    const float cd = __builtin_amdgcn_exp2f(-fmaf(nr.md, kLog2e, -dh)) / nr.sd;
-    const float ct = __builtin_amdgcn_exp2f(-fmaf(nr.mt, kLog2e, -th)) / nr.st;
-    return SmRec{dh, cd, th, ct / cd};
-  };
-  auto epi = [&](int h, const float* d, const float* t, int, int p) {
+  sm_load_w2<VEC>(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
+  // per row (stats_markov_rows): P_v = 2^(d_v log2e - dh) cd and
+  // T_v = 2^(t_v log2e - th) ct, and |P_v - T_v| = cd |2^(..d..) - (ct / cd) 2^(..t..)|
+  auto epi = [&](int h, const float* d, const float* t, int p) {
     const SmRec k = L.meta[p][h * 16 + (lane & 15)];
     float l1 = 0.0f;
 #pragma unroll
@@ -614,11 +612,11 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T, true, MASK, RMAX, false>(a, af, tok0, L, meta_load, meta_make, epi, merge);
+    sm_look_vec<T, true, MASK, RMAX, true>(a, af, tok0, L, a.k2, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
       const int row = row0 + static_cast<int>(threadIdx.x);
-      if (threadIdx.x < kSmTile) L.meta[0][threadIdx.x] = meta_make(meta_load(row < a.rows ? row : 0), row);
+      if (threadIdx.x < kSmTile) L.meta[0][threadIdx.x] = a.k2[row < a.rows ? row : 0];
       sm_tile<T, VEC, true>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
       __syncthreads();
       merge(row0, 0);
@@ -684,7 +682,8 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
   const bool vec = a.V % 4 == 0 && reinterpret_cast<uintptr_t>(a.backbone) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
                    static_cast<uint64_t>(kSmTile) * a.V * sizeof(T) < 0x7fffffffull &&
-                   static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull;
+                   static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull &&
+                   static_cast<uint64_t>(a.rows) * sizeof(SmRec) < 0x7fffffffull;
   const bool mask = a.V % 64 != 0, rmax = a.r == kSmMaxR;
   hipError_t e = launch_look<T>(a, G, vec, mask, rmax, 1, st);
   if (e != hipSuccess) return e;
@@ -722,6 +721,8 @@ StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V) {
   off = align_up(off + rows * p.G * sizeof(float), 256);
   p.off_dt = off;
   off = align_up(off + rows * sizeof(float), 256);
+  p.off_k2 = off;
+  off = align_up(off + rows * sizeof(SmRec), 256);
   p.bytes = rows > 0 ? off : 0;
   return p;
 }
@@ -738,7 +739,8 @@ hipError_t launch_stats_markov(const void* backbone, const void* target, int dty
   char* w = static_cast<char*>(ws);
   SmArgs a{backbone, target, anchor, w1, w2, teacher, rows, gamma, V, r,
            reinterpret_cast<SmRec*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
-           reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1)};
+           reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1),
+           reinterpret_cast<SmRec*>(w + pl.off_k2)};
   if (dtype == DSPARK_BF16)
     return launch_sm_typed<uint16_t>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate,
                                      ce, bce, tau, sums, st);
