@@ -16,11 +16,12 @@
 // owns 512 tokens and keeps their W2 rows in registers (the MFMA A
 // fragments) for the whole launch; it walks the rows in tiles of 64 (the N
 // side), staging the tile's W1 rows (selected by the forced tokens) in LDS,
-// and adds the bias to the backbone values it streams.  Two looks:
+// and adds the bias to the backbone values it streams.  Launches, in order:
+//  * teacher: per row the forced previous token and the draft value at the
+//    teacher token;
 //  * look 1: per (row, workgroup) the (max, sum exp) of the draft values of
 //    its tokens;
 //  * tnorm: per row the target's normaliser (no bias involved);
-//  * teacher: per row the draft value at the teacher token;
 //  * rows: the per-row draft normalisers from the look-1 records;
 //  * look 2: the bias again, and per (row, workgroup) the share of
 //    sum |P - T|;
@@ -69,6 +70,7 @@ struct SmArgs {
   SmRec* norm;      // [rows]: per-row normalisers (after look 1)
   float* l1part;    // [rows][G] (look 2)
   SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, ct / cd)
+  int32_t* xf;      // [rows]: each row's forced previous token, clamped (stats_markov_teacher)
 };
 
 // Two of everything: the aligned path stages tile t + 1 and merges tile
@@ -316,10 +318,7 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
 #pragma unroll
     for (int j = 0; j < kSmDma; ++j) {
       const int n = ((j * kSmWaves + wv) * 64 + lane) / slots;
-      const int row = row0 + n;
-      const int rr = n < kSmTile && row < a.rows ? row : 0;
-      const int k = rr % a.gamma;
-      xs[j] = *(k == 0 ? a.anchor + rr / a.gamma : a.teacher + (rr - 1));  // one load, no branch
+      xs[j] = a.xf[min(row0 + min(n, kSmTile - 1), a.rows - 1)];
     }
   };
   // tile row0's W1 rows (and records) into buffers buf
@@ -329,7 +328,7 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
       const int q = j * kSmWaves + wv;
       const int sl = q * 64 + lane, n = sl / slots, c = sl - n * slots;
       const bool ok = n < kSmTile && c < slots - 1 && c * 8 < r && row0 + n < a.rows;
-      const uint32_t off = ok ? static_cast<uint32_t>((clamp_token(xs[j], V) * r + c * 8) * 2) : 0xfffffff0u;
+      const uint32_t off = ok ? static_cast<uint32_t>((xs[j] * r + c * 8) * 2) : 0xfffffff0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(L.a[buf] + q * 64 * 8), 16, off, 0, 0, 0);
     }
     if constexpr (META)
@@ -470,15 +469,15 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
 
 // Per row: the draft value at the teacher token, the backbone's value plus
 // W1[x] . W2[teacher] (bf16 products, exact in fp32, summed in fp32), one
-// wave per row; x is the row's forced previous token (the anchor at the
-// block's first position, else the previous position's teacher token).
+// wave per row, and x itself for the looks; x is the row's forced previous
+// token (the anchor at the block's first position, else the previous
+// position's teacher token).
 template <typename T>
 __global__ __launch_bounds__(256) void stats_markov_teacher_kernel(SmArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.rows) return;
-  const int k = row % a.gamma;
-  const int x = clamp_token(k == 0 ? a.anchor[row / a.gamma] : a.teacher[row - 1], a.V);
+  const int x = forced_token(a, row);
   const int tch = clamp_token(a.teacher[row], a.V);
   const uint16_t* w1 = a.w1 + static_cast<size_t>(x) * a.r;
   const uint16_t* w2 = a.w2 + static_cast<size_t>(tch) * a.r;
@@ -486,8 +485,10 @@ __global__ __launch_bounds__(256) void stats_markov_teacher_kernel(SmArgs a) {
   for (int j = lane; j < a.r; j += 64)
     s = fmaf(__uint_as_float(static_cast<uint32_t>(w1[j]) << 16), __uint_as_float(static_cast<uint32_t>(w2[j]) << 16), s);
   s = wave_sum(s);
-  if (lane == 0)
+  if (lane == 0) {
     a.dteach[row] = load_logit(static_cast<const T*>(a.backbone) + static_cast<size_t>(row) * a.V, tch) + s;
+    a.xf[row] = x;
+  }
 }
 
 // Per row: the target row's normaliser (max, sum exp), one persistent
@@ -685,9 +686,9 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
                    static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull &&
                    static_cast<uint64_t>(a.rows) * sizeof(SmRec) < 0x7fffffffull;
   const bool mask = a.V % 64 != 0, rmax = a.r == kSmMaxR;
+  DSPARK_LAUNCH("stats_markov_teacher", stats_markov_teacher_kernel<T>, dim3(rb), dim3(256), 0, st, a);
   hipError_t e = launch_look<T>(a, G, vec, mask, rmax, 1, st);
   if (e != hipSuccess) return e;
-  DSPARK_LAUNCH("stats_markov_teacher", stats_markov_teacher_kernel<T>, dim3(rb), dim3(256), 0, st, a);
   const int epl = 16 / static_cast<int>(sizeof(T));
   const bool tvec = a.V % epl == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
   const dim3 tgrid(static_cast<unsigned>(std::min(a.rows, device_cus())));
@@ -723,6 +724,8 @@ StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V) {
   off = align_up(off + rows * sizeof(float), 256);
   p.off_k2 = off;
   off = align_up(off + rows * sizeof(SmRec), 256);
+  p.off_xf = off;
+  off = align_up(off + rows * sizeof(int32_t), 256);
   p.bytes = rows > 0 ? off : 0;
   return p;
 }
@@ -740,7 +743,7 @@ hipError_t launch_stats_markov(const void* backbone, const void* target, int dty
   SmArgs a{backbone, target, anchor, w1, w2, teacher, rows, gamma, V, r,
            reinterpret_cast<SmRec*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
            reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1),
-           reinterpret_cast<SmRec*>(w + pl.off_k2)};
+           reinterpret_cast<SmRec*>(w + pl.off_k2), reinterpret_cast<int32_t*>(w + pl.off_xf)};
   if (dtype == DSPARK_BF16)
     return launch_sm_typed<uint16_t>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate,
                                      ce, bce, tau, sums, st);
