@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified rows/sec (B×(γ+1)×V logits) at V=129280,B=64,γ=5; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 
 
 def parse():
@@ -129,17 +130,32 @@ PROFILES = {
               "Training statistics and their gradient (dspark_accept_stats + "
               "dspark_accept_stats_backward), 2048 blocks x gamma 7, V=129280, bf16",
               " --workload train"),
+    "markov_stats": (os.path.join(ROOT, "profiles", "stats_markov_N2048_g7_V129280_r256.md"),
+                     "Statistics of the teacher-forced Markov draft (dspark_accept_stats_markov), "
+                     "2048 blocks x gamma 7, V=129280, rank 256, bf16",
+                     " --workload markov_stats"),
 }
 CSRC = os.path.join(ROOT, "dspark_draft_sampling_amd", "csrc")
 
 
-def source_digest():
-    """sha256 over the kernel sources (file names and contents, sorted)."""
+# the sources a workload's kernels are built from (the digest of a profile
+# summary covers these; None: every kernel source)
+DIGEST_SOURCES = {
+    "decode": ("common.hpp", "internal.hpp", "markov.hip", "stats.hip", "truncate.hpp", "verify.hip"),
+    "train": ("common.hpp", "internal.hpp", "stats.hip"),
+    "markov_stats": ("common.hpp", "internal.hpp", "stats.hip", "stats_markov.hip"),
+}
+
+
+def source_digest(workload="decode"):
+    """sha256 over the kernel sources of `workload` (file names and
+    contents, sorted)."""
     import hashlib
 
+    want = DIGEST_SOURCES.get(workload)
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp", ".h")):
+        if f.endswith((".hip", ".hpp", ".h")) and (want is None or f in want):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(fh.read())
@@ -190,7 +206,7 @@ def summarize_profile(base, workload="decode"):
     true_kib = 256 * 1024
     sf, sw = true_kib / cf, true_kib / cw
     cmd = "python3 bench.py" + wl
-    steps = " --steps 10 --warmup 2" if workload == "train" else " --steps 50 --warmup 5"
+    steps = " --steps 50 --warmup 5" if workload == "decode" else " --steps 10 --warmup 2"
     lines = [
         f"# {title}",
         "",
@@ -225,7 +241,8 @@ def summarize_profile(base, workload="decode"):
         "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
         "|---|---|---|---|---|",
     ]
-    rec = dict(source_sha256=source_digest(), fetch_scale=sf, write_scale=sw, kernels={})
+    rec = dict(source_sha256=source_digest(workload), sources=list(DIGEST_SOURCES.get(workload) or []),
+               fetch_scale=sf, write_scale=sw, kernels={})
     for k in sorted(fetch):
         if not k.startswith(ours):
             continue
@@ -285,10 +302,21 @@ def _roofline(kernels, headline):
                 traffic=counter_traffic(dom) if headline else None)
 
 
+def _roofline_mfma(kernels):
+    """The dominant kernel against the dense bf16 MFMA peak when it carries a
+    contraction (the teacher-forced looks), else against HBM."""
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+    if "mfma_tflops" not in kernels[dom]:
+        return _roofline(kernels, False)
+    ach = kernels[dom]["mfma_tflops"]
+    return dict(bound="mfma", kernel=dom, achieved=ach, peak=MFMA_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / MFMA_BF16_TFLOPS, 4), traffic=None)
+
+
 def main():
     args = parse()
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, "train" if args.workload == "train" else "decode")
+        summarize_profile(args.summarize_profile, args.workload if args.workload in PROFILES else "decode")
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -533,7 +561,7 @@ def run_markov_stats(args, torch, ds):
                 vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload="acceptance statistics of the teacher-forced Markov draft", N=N,
                             gamma=g, V=V, r=r, logits="bf16", rotated_batches=len(sets)),
-                roofline=_roofline(kernels, False), cpu_baseline=None,
+                roofline=_roofline_mfma(kernels), cpu_baseline=None,
                 step=dict(kernels=kernels, bias_gflop_per_look=round(flops / 1e9, 1)))
 
 
