@@ -58,6 +58,17 @@ def test_small(dtype, r):
     check(inp)
 
 
+@pytest.mark.parametrize("dtype,r,V", [("bf16", 256, 1000), ("f32", 256, 1024), ("f32", 256, 1000),
+                                       ("bf16", 96, 1536)])
+def test_aligned_shapes_several_tiles(dtype, r, V):
+    # 147 rows: two full 64-row tiles and a ragged third; rank 256 takes the
+    # compile-time rank path, V = 1000 the per-element token mask, rank 96 a
+    # padded k range
+    inp = stats_markov_inputs(dict(seed=V + r, N=21, gamma=7, V=V, dtype=dtype, draft_std=2.0,
+                                   noise_std=0.8), r=r, w_std=0.05, mask_every=4)
+    check(inp)
+
+
 @pytest.mark.parametrize("V,gamma", [(999, 3), (1000, 1), (513, 4), (40, 7)])
 def test_ragged(V, gamma):
     inp = stats_markov_inputs(dict(seed=V, N=9, gamma=gamma, V=V, dtype="bf16", draft_std=2.0,
