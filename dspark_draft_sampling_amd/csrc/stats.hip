@@ -11,7 +11,10 @@
 // stats_rows: one workgroup per row pair.  Pass 1 streams both rows once with
 // 16-byte loads and keeps an online (max, sum exp) per thread; pass 2 streams
 // them again (the pair was just read, so it is served from the caches) for
-// the L1 term.  stats_reduce: one workgroup computes tau and the sums in fp64
+// the L1 term.  The L1 pass forms the overlap sum_v min(P_v, T_v) instead of
+// sum |P_v - T_v|: both rows sum to 1, so L1 = 2 (1 - overlap) exactly, and
+// min(P_v, T_v) = exp(min(d_v - lse_d, t_v - lse_t)) takes one exponential
+// per element pair where |P_v - T_v| takes two.  stats_reduce: one workgroup computes tau and the sums in fp64
 // in a fixed order, so the sums are deterministic.
 #include <algorithm>
 #include <atomic>
@@ -122,9 +125,11 @@ __global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
   const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
   const float Mt = block_max<kWaves>(mt, shv);
   const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
-  const float isd = 1.0f / Sd, ist = 1.0f / St;
+  // log2(Sd / St): min(P_v, T_v) = 2^min((d_v - Md) log2e, (t_v - Mt) log2e + lam) / Sd
+  const float lam = __log2f(Sd) - __log2f(St);
 
-  // pass 2: L1 = sum |P - T|
+  // pass 2: the overlap sum_v min(P_v, T_v); L1 = sum |P - T| = 2 (1 - overlap)
+  // (both rows sum to 1), one exponential per element pair
   float acc = 0.0f;
   e = threadIdx.x * EPL;
   for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
@@ -138,8 +143,7 @@ __global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        acc += fabsf(__builtin_amdgcn_exp2f((xd[u][j] - Md) * kLog2e) * isd -
-                     __builtin_amdgcn_exp2f((xt[u][j] - Mt) * kLog2e) * ist);
+        acc += __builtin_amdgcn_exp2f(fminf((xd[u][j] - Md) * kLog2e, fmaf(xt[u][j] - Mt, kLog2e, lam)));
   }
   for (; e < V; e += step) {
     float xd[EPL], xt[EPL];
@@ -147,13 +151,13 @@ __global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
     L::load(tr + e, xt);
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      acc += fabsf(__builtin_amdgcn_exp2f((xd[j] - Md) * kLog2e) * isd -
-                   __builtin_amdgcn_exp2f((xt[j] - Mt) * kLog2e) * ist);
+      acc += __builtin_amdgcn_exp2f(fminf((xd[j] - Md) * kLog2e, fmaf(xt[j] - Mt, kLog2e, lam)));
   }
-  const float L1 = block_sum<kWaves>(acc, shv);
+  const float ov = block_sum<kWaves>(acc, shv) / Sd;
 
   if (threadIdx.x == 0) {
-    const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+    const float L1 = fmaxf(0.0f, 2.0f * (1.0f - ov));
+    const float a = fminf(1.0f, fmaxf(0.0f, ov));
     const int32_t tch = clamp_token(teacher[row], V);
     const float lse_d = Md + logf(Sd);
     const float c = conf_logits[row];
@@ -171,8 +175,9 @@ __global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
 //   stats_part1  per item: (max, sum) of both rows, sums with an integer
 //                base-2 shift (s = sum 2^(x log2e - floor(m log2e)))
 //   stats_part2  per item: the pair's normalisers from all its part1
-//                records, then the item's share of sum |P - T| (a second
-//                read of the pair), with a ticket per pair: the pair's last
+//                records, then the item's share of the overlap sum_v
+//                min(P_v, T_v) (a second read of the pair; L1 = 2 (1 -
+//                overlap)), with a ticket per pair: the pair's last
 //                item writes L1, accept_rate, CE and BCE, and the wave
 //                finishing the last pair writes tau and the sums
 // Both item kernels keep the next item's loads in flight while reducing the
@@ -384,7 +389,7 @@ struct StatsOut {
 };
 
 // Per item: the pair's normalisers from all its part1 records, then the
-// item's share of sum |P - T|, with a ticket on the pair: the pair's last
+// item's share of the overlap (times Sd), with a ticket on the pair: the pair's last
 // item writes L1, accept_rate, CE and BCE, and the wave finishing the last
 // pair writes tau and the sums.
 template <typename T>
@@ -408,14 +413,16 @@ __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
     float M2d, Sd, M2t, St;
     pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
     seg_mask<T>(V, seg * SEG, lane, ud, ut);
-    const float isd = 1.0f / Sd, ist = 1.0f / St;
+    // the item's share of the overlap sum_v min(P_v, T_v), times Sd:
+    // min(P_v, T_v) = 2^min(d_v log2e - M2d, t_v log2e - M2t + lam) / Sd
+    const float lam = __log2f(Sd) - __log2f(St);
     float acc = 0.0f;
 #pragma unroll
     for (int it = 0; it < kSegIters; ++it)
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        acc += fabsf(__builtin_amdgcn_exp2f(fmaf(elem16(ud[it], j, T{}), kLog2e, -M2d)) * isd -
-                     __builtin_amdgcn_exp2f(fmaf(elem16(ut[it], j, T{}), kLog2e, -M2t)) * ist);
+        acc += __builtin_amdgcn_exp2f(fminf(fmaf(elem16(ud[it], j, T{}), kLog2e, -M2d),
+                                            fmaf(elem16(ut[it], j, T{}), kLog2e, -M2t) + lam));
     acc = wave_sum(acc);
     uint32_t ticket = 0;
     if (lane == 0) {
@@ -424,13 +431,15 @@ __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
     }
     ticket = __builtin_amdgcn_readfirstlane(ticket);
     if (ticket != static_cast<uint32_t>(P - 1)) continue;
-    // the pair's last item: L1 from the item shares (fixed order), outputs
-    float L1 = 0.0f;
-    for (int i = lane; i < P; i += 64) L1 += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
-    L1 = wave_sum(L1);
+    // the pair's last item: the overlap from the item shares (fixed order);
+    // L1 = sum |P - T| = 2 (1 - overlap), both rows summing to 1
+    float ov = 0.0f;
+    for (int i = lane; i < P; i += 64) ov += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
+    ov = wave_sum(ov) / Sd;
     uint32_t last = 0;
     if (lane == 0) {
-      const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+      const float L1 = fmaxf(0.0f, 2.0f * (1.0f - ov));
+      const float a = fminf(1.0f, fmaxf(0.0f, ov));
       const int32_t tch = clamp_token(o.teacher[pair], V);
       const float c = o.conf_logits[pair];
       const float lse_d = M2d * kLn2 + logf(Sd);

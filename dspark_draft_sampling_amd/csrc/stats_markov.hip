@@ -23,8 +23,8 @@
 //    its tokens;
 //  * tnorm: per row the target's normaliser (no bias involved);
 //  * rows: the per-row draft normalisers from the look-1 records;
-//  * look 2: the bias again, and per (row, workgroup) the share of
-//    sum |P - T|;
+//  * look 2: the bias again, and per (row, workgroup) the share of the
+//    overlap sum_v min(P_v, T_v) (L1 = 2 (1 - overlap));
 //  * final: per row L1, accept_rate, CE, BCE; then the batch reduction of
 //    the plain statistics.
 #include <algorithm>
@@ -69,7 +69,7 @@ struct SmArgs {
   float* dteach;    // [rows]: the draft value at the teacher token
   SmRec* norm;      // [rows]: per-row normalisers (after look 1)
   float* l1part;    // [rows][G] (look 2)
-  SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, ct / cd)
+  SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, lam)
   int32_t* xf;      // [rows]: each row's forced previous token, clamped (stats_markov_teacher)
 };
 
@@ -575,15 +575,18 @@ __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_
     nr.sd = sd;
     a.norm[row] = nr;
     // look 2's constants: P_v = 2^(d_v log2e - dh) cd with dh = md log2e in
-    // fp32 and cd = 2^-(its rounding residual) / sd; likewise for the target
+    // fp32 and cd = 2^-rd / sd (rd: the product's rounding residual);
+    // likewise T_v with (th, ct); lam = log2(ct / cd), so that
+    // min(P_v, T_v) = cd 2^min(d_v log2e - dh, t_v log2e - th + lam)
     const float dh = nr.md * kLog2e, th = nr.mt * kLog2e;
-    const float cd = __builtin_amdgcn_exp2f(-fmaf(nr.md, kLog2e, -dh)) / nr.sd;
-    const float ct = __builtin_amdgcn_exp2f(-fmaf(nr.mt, kLog2e, -th)) / nr.st;
-    a.k2[row] = SmRec{dh, cd, th, ct / cd};
+    const float rd = fmaf(nr.md, kLog2e, -dh), rt = fmaf(nr.mt, kLog2e, -th);
+    const float cd = __builtin_amdgcn_exp2f(-rd) / nr.sd;
+    const float lam = (rd - rt) + (__log2f(nr.sd) - __log2f(nr.st));
+    a.k2[row] = SmRec{dh, cd, th, lam};
   }
 }
 
-// Look 2: per (row, workgroup) share of sum |P - T|.
+// Look 2: per (row, workgroup) share of the overlap sum_v min(P_v, T_v).
 template <typename T, bool VEC, bool MASK, bool RMAX>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a) {
   __shared__ SmLds L;
@@ -592,15 +595,16 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2<VEC>(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  // per row (stats_markov_rows): P_v = 2^(d_v log2e - dh) cd and
-  // T_v = 2^(t_v log2e - th) ct, and |P_v - T_v| = cd |2^(..d..) - (ct / cd) 2^(..t..)|
+  // the shares of the overlap sum_v min(P_v, T_v) (L1 = 2 (1 - overlap), both
+  // rows summing to 1): with the row's (dh, cd, th, lam) from
+  // stats_markov_rows, min(P_v, T_v) = cd 2^min(d_v log2e - dh, t_v log2e - th + lam),
+  // one exponential per element pair
   auto epi = [&](int h, const float* d, const float* t, int p) {
     const SmRec k = L.meta[p][h * 16 + (lane & 15)];
     float l1 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4 * kSmMS; ++e)
-      l1 += fabsf(fmaf(-k.st, __builtin_amdgcn_exp2f(fmaf(t[e], kLog2e, -k.mt)),
-                       __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -k.md))));
+      l1 += __builtin_amdgcn_exp2f(fminf(fmaf(d[e], kLog2e, -k.md), fmaf(t[e], kLog2e, -k.mt) + k.st));
     l1 = rows_sum(l1) * k.sd;
     if (lane < 16) L.s[p][wave][h * 16 + lane] = l1;
   };
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   }
 }
 
-// Per row: L1 from its G shares, then accept_rate, CE and BCE.
+// Per row: the overlap from its G shares, then L1, accept_rate, CE and BCE.
 __global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32_t G, const float* conf_logits,
                                                                  float* l1, float* accept_rate, float* ce,
                                                                  float* bce) {
@@ -636,11 +640,11 @@ __global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32
   float s = 0.0f;
   for (int i = lane; i < G; i += 64) s += a.l1part[static_cast<size_t>(row) * G + i];
   s = wave_sum(s);
-  if (lane == 0) {
+  if (lane == 0) {  // s: the overlap sum_v min(P_v, T_v)
     const SmRec nr = a.norm[row];
-    const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * s));
+    const float av = fminf(1.0f, fmaxf(0.0f, s));
     const float c = conf_logits[row];
-    l1[row] = s;
+    l1[row] = fmaxf(0.0f, 2.0f * (1.0f - s));
     accept_rate[row] = av;
     ce[row] = nr.md + logf(nr.sd) - a.dteach[row];
     bce[row] = fmaxf(c, 0.0f) - c * av + log1pf(expf(-fabsf(c)));

@@ -243,6 +243,33 @@ def test_stats_paths(N, gamma, V, dtype):
     assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
 
 
+@pytest.mark.parametrize("N,gamma,V,dtype", [(6, 5, 4096, "bf16"), (300, 7, 512, "bf16"),
+                                             (4, 3, 2000, "f32")])
+def test_stats_identical_near_and_disjoint_rows(N, gamma, V, dtype):
+    """Both stats paths on rows whose L1 is 0 (identical), tiny (the target
+    perturbed by 1e-3 to 3e-2) or 2 (disjoint supports): the kernels form L1
+    as 2 (1 - sum min(P, T)), so these check its rounding where L1 is small,
+    against the oracle's direct sum |P - T| (binary64)."""
+    rng = np.random.default_rng(N * V)
+    d = rng.normal(0, 3.0, (N, gamma, V)).astype(np.float32)
+    scale = np.array([0.0, 1e-3, 1e-2, 3e-2])[np.arange(N * gamma) % 4].reshape(N, gamma, 1)
+    t = (d + scale * rng.normal(0, 1.0, d.shape)).astype(np.float32)
+    t[0, 0] = d[0, 0]
+    t[-1, -1] = -np.inf
+    t[-1, -1, ::2] = rng.normal(0, 3.0, V - V // 2)
+    d[-1, -1, ::2] = -np.inf  # disjoint supports
+    teacher = rng.integers(1, V, (N, gamma))
+    teacher[-1, -1] = 1  # a token the disjoint row's draft keeps
+    si = stats_case(d, t, teacher=teacher, conf_logits=rng.normal(0, 1, (N, gamma)), dtype=dtype)
+    ref = O.accept_stats(si)
+    got = G.stats(si)
+    for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
+        assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
+    assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
+    assert got["l1"][0, 0] <= 1e-6 and got["accept_rate"][0, 0] >= 1 - 1e-6
+    assert got["l1"][-1, -1] == 2.0 and got["accept_rate"][-1, -1] == 0.0
+
+
 @pytest.mark.parametrize("config", ["decode", "truncated"])
 def test_markov_plans_agree(config, decode_full, truncated_full):
     """The one-launch plans (W2 resident, steps handed off through polled
