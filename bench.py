@@ -211,14 +211,15 @@ def summarize_profile(base, workload="decode"):
         f"# {title}",
         "",
         "Commands, from the repository root after `cd /tmp && export TMPDIR=/tmp` (paths "
-        f"absolute on the run; `python3 bench.py{wl} --summarize-profile gpurun_out` wrote this file):",
+        f"absolute on the run; $OUT is the output directory; `python3 bench.py{wl} --summarize-profile $OUT` "
+        "wrote this file):",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats -T -f csv -d gpurun_out/prof_kt -o kt -- {cmd}{steps} --no-cpu",
-        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
-        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d gpurun_out/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
-        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d gpurun_out/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
-        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d gpurun_out/prof_copy_WRITE_SIZE -o p -- {cmd} --copy-calibration 256",
+        f"rocprofv3 --kernel-trace --stats -T -f csv -d $OUT/prof_kt -o kt -- {cmd}{steps} --no-cpu",
+        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
+        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
+        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
+        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_copy_WRITE_SIZE -o p -- {cmd} --copy-calibration 256",
         "```",
         "",
         "## Kernel time (`--kernel-trace --stats`)",
