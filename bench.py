@@ -323,8 +323,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(one GPU's share of a sharded batch is the same kernels at a smaller shape)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
