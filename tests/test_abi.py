@@ -182,3 +182,14 @@ def test_markov_plan_switch(L):
         assert L.dspark_markov_plan(0) == 0
     finally:
         L.dspark_markov_plan(prev)
+
+
+def test_binding_constants_match_header():
+    """The binding's limits, dtype and operation codes are the header's."""
+    text = open(HEADER).read()
+    defines = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(DSPARK_MAX_\w+)\s+(\d+)", text)}
+    assert defines["DSPARK_MAX_GAMMA"] == ds.DSPARK_MAX_GAMMA
+    assert defines["DSPARK_MAX_RANK"] == ds.DSPARK_MAX_RANK
+    enums = dict(re.findall(r"\b(DSPARK_(?:BF16|F32|OP_\w+))\s*=\s*(\d+)", text))
+    for name, value in enums.items():
+        assert getattr(ds, name) == int(value), name

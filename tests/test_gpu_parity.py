@@ -20,6 +20,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
+import dspark_draft_sampling_amd as ds  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import _gpu as G  # noqa: E402
 from tests._cases import decode_case, stats_case  # noqa: E402
@@ -171,7 +172,6 @@ def test_flag_rate_many_draws():
 
 # ---------------------------------------------------------- edge cases ------
 def test_empty_batch():
-    import dspark_draft_sampling_amd as ds
 
     inp = decode_inputs("tiny", B=0, with_embed=True)
     out = G.verify(inp, np.zeros((0, inp["gamma"]), np.int32))
@@ -193,6 +193,28 @@ def test_ragged_shapes(V, dtype, B):
     vref = O.verify(inp, ref["draft_tokens"], **G.q_of(ref))
     vgot = G.verify(inp, ref["draft_tokens"], G.q_of(ref))
     assert check_verify(vgot, vref) <= 1
+
+
+def test_max_gamma_and_rank():
+    """The largest draft width (gamma = DSPARK_MAX_GAMMA) with the largest
+    rank, mixed greedy / sampled requests: Markov, verify and the statistics
+    of the same rows."""
+    cfg = dict(seed=91, B=9, gamma=ds.DSPARK_MAX_GAMMA, V=2048, r=ds.DSPARK_MAX_RANK, d=64, dtype="bf16",
+               draft_std=2.0, noise_std=0.5, w_std=0.05, mode="mixed")
+    inp = decode_inputs(cfg)
+    ref = O.markov_sample(inp)
+    got = G.markov(inp)
+    check_markov(inp, got, ref)
+    vref = O.verify(inp, ref["draft_tokens"], **G.q_of(ref))
+    vgot = G.verify(inp, ref["draft_tokens"], G.q_of(ref))
+    assert check_verify(vgot, vref) <= 1
+    si = stats_inputs(dict(seed=92, N=9, gamma=ds.DSPARK_MAX_GAMMA, V=2048, dtype="bf16", draft_std=2.0,
+                           noise_std=0.5), mask_every=3)
+    sref = O.accept_stats(si)
+    sgot = G.stats(si)
+    for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
+        assert np.allclose(sgot[key], sref[key], rtol=RTOL, atol=1e-6), key
+    assert np.allclose(sgot["sums"], sref["sums"], rtol=RTOL, atol=1e-6)
 
 
 def test_n_draft_and_bad_rows():
@@ -277,7 +299,6 @@ def test_markov_plans_agree(config, decode_full, truncated_full):
     full size: tokens, flags, z and thresholds bit for bit; the
     log-normalisers up to the order of their fp32 partial sums (the plans
     combine chunk partials over different workgroup shapes)."""
-    import dspark_draft_sampling_amd as ds
 
     inp = decode_full if config == "decode" else truncated_full
     prev = ds.markov_plan(ds.MARKOV_AUTO)
@@ -306,7 +327,6 @@ def test_markov_concurrent_streams(decode_full):
     library chains its fused launches on the device, so neither grid waits
     on compute units the other holds; both end with a lone call's results and
     no wait gives up."""
-    import dspark_draft_sampling_amd as ds
 
     inp = decode_full
     ref = G.markov(inp)

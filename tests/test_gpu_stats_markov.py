@@ -69,7 +69,7 @@ def test_aligned_shapes_several_tiles(dtype, r, V):
     check(inp)
 
 
-@pytest.mark.parametrize("V,gamma", [(999, 3), (1000, 1), (513, 4), (40, 7)])
+@pytest.mark.parametrize("V,gamma", [(999, 3), (1000, 1), (513, 4), (40, 7), (1024, ds.DSPARK_MAX_GAMMA)])
 def test_ragged(V, gamma):
     inp = stats_markov_inputs(dict(seed=V, N=9, gamma=gamma, V=V, dtype="bf16", draft_std=2.0,
                                    noise_std=0.8), r=48, w_std=0.1)
