@@ -21,7 +21,7 @@
 //    teacher token;
 //  * look 1: per (row, workgroup) the (max, sum exp) of the draft values of
 //    its tokens;
-//  * tnorm: per row the target's normaliser (no bias involved);
+//  * tnorm: the target's normaliser (no bias involved), per half row;
 //  * rows: the per-row draft normalisers from the look-1 records;
 //  * look 2: the bias again, and per (row, workgroup) the share of the
 //    overlap sum_v min(P_v, T_v) (L1 = 2 (1 - overlap));
@@ -71,6 +71,7 @@ struct SmArgs {
   float* l1part;    // [rows][G] (look 2)
   SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, lam)
   int32_t* xf;      // [rows]: each row's forced previous token, clamped (stats_markov_teacher)
+  SmRec* tpart;     // [rows]: the target's (max, sum exp) of each half row (stats_markov_tnorm)
 };
 
 // Two of everything: the aligned path stages tile t + 1 and merges tile
@@ -491,17 +492,25 @@ __global__ __launch_bounds__(256) void stats_markov_teacher_kernel(SmArgs a) {
   }
 }
 
-// Per row: the target row's normaliser (max, sum exp), one persistent
-// workgroup of 1024 threads per compute unit looping over rows.
-constexpr int kTnThreads = 1024;
+// The target rows' normalisers, one wave per half row (no barriers, so a
+// wave streams its half rows back to back): unit u is half u % 2 of row
+// u / 2, and the wave writes its (max, sum exp) into tpart[row] (half 0 in
+// (md, sd), half 1 in (mt, st)); stats_markov_rows combines the halves.
+constexpr int kTnThreads = 256;
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kTnThreads) void stats_markov_tnorm_kernel(SmArgs a) {
   constexpr int EPL = VEC ? 16 / static_cast<int>(sizeof(T)) : 1;
-  constexpr int kU = 4;
-  __shared__ float sh[kTnThreads / 64];
+  constexpr int kU = 8;
   const T* tg = static_cast<const T*>(a.target);
   const int V = a.V;
-  for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * (kTnThreads / 64);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kTnThreads / 64) +
+                                               static_cast<int>(threadIdx.x >> 6));
+  const int Vh = (V / 2 + EPL - 1) / EPL * EPL;  // half 0's length, a multiple of EPL
+  for (int u = w; u < 2 * a.rows; u += nwaves) {
+    const int row = u >> 1, hf = u & 1;
+    const int lo = hf ? Vh : 0, hi = hf ? V : min(Vh, V);
     const T* tr = tg + static_cast<size_t>(row) * V;
     float m = neg_inf(), s = 0.0f;
     auto add = [&](const float* x) {
@@ -518,43 +527,45 @@ __global__ __launch_bounds__(kTnThreads) void stats_markov_tnorm_kernel(SmArgs a
     };
     auto ld = [&](int e, float* x) {
       if constexpr (VEC) {
-        const uint4 u = *reinterpret_cast<const uint4*>(tr + e);
+        const uint4 q = *reinterpret_cast<const uint4*>(tr + e);
         if constexpr (sizeof(T) == 2) {
-          x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
-          x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+          x[0] = bf_lo(q.x); x[1] = bf_hi(q.x); x[2] = bf_lo(q.y); x[3] = bf_hi(q.y);
+          x[4] = bf_lo(q.z); x[5] = bf_hi(q.z); x[6] = bf_lo(q.w); x[7] = bf_hi(q.w);
         } else {
-          x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
-          x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+          x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+          x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
         }
       } else {
         x[0] = load_logit(tr, e);
       }
     };
-    const int step = kTnThreads * EPL;
-    int e = threadIdx.x * EPL;
-    for (; e + (kU - 1) * step < V; e += kU * step) {
+    constexpr int step = 64 * EPL;
+    int e = lo + lane * EPL;
+    for (; e + (kU - 1) * step < hi; e += kU * step) {
       float x[kU][EPL];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) ld(e + u * step, x[u]);
+      for (int k = 0; k < kU; ++k) ld(e + k * step, x[k]);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) add(x[u]);
+      for (int k = 0; k < kU; ++k) add(x[k]);
     }
-    for (; e < V; e += step) {
+    for (; e < hi; e += step) {
       float x[EPL];
       ld(e, x);
       add(x);
     }
-    const float M = block_max<kTnThreads / 64>(m, sh);
-    const float S = block_sum<kTnThreads / 64>(m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f, sh);
-    if (threadIdx.x == 0) {
-      a.norm[row].mt = M;
-      a.norm[row].st = S;
+    const float M = wave_max(m);
+    const float S = wave_sum(m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f);
+    if (lane == 0) {
+      float* dst = hf ? &a.tpart[row].mt : &a.tpart[row].md;
+      dst[0] = M;
+      dst[1] = S;
     }
   }
 }
 
-// Per row: the draft normaliser from the row's G look-1 records, and look 2's
-// per-row constants (the target normaliser is stats_markov_tnorm's).
+// Per row: the draft normaliser from the row's G look-1 records, the target
+// normaliser from stats_markov_tnorm's two halves, and look 2's per-row
+// constants.
 __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_t G) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -569,10 +580,13 @@ __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_
     if (q.md > neg_inf()) sd += q.sd * __builtin_amdgcn_exp2f((q.md - md) * kLog2e);
   }
   sd = wave_sum(sd);
-  if (lane == 0) {  // the target half (mt, st) is stats_markov_tnorm's
-    SmRec nr = a.norm[row];
-    nr.md = md;
-    nr.sd = sd;
+  if (lane == 0) {
+    // the target normaliser from the two half-row records of stats_markov_tnorm
+    const SmRec tp = a.tpart[row];
+    const float mt = fmaxf(tp.md, tp.mt);
+    const float st = (tp.md > neg_inf() ? tp.sd * __builtin_amdgcn_exp2f((tp.md - mt) * kLog2e) : 0.0f) +
+                     (tp.mt > neg_inf() ? tp.st * __builtin_amdgcn_exp2f((tp.mt - mt) * kLog2e) : 0.0f);
+    const SmRec nr{md, sd, mt, st};
     a.norm[row] = nr;
     // look 2's constants: P_v = 2^(d_v log2e - dh) cd with dh = md log2e in
     // fp32 and cd = 2^-rd / sd (rd: the product's rounding residual);
@@ -695,7 +709,7 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
   if (e != hipSuccess) return e;
   const int epl = 16 / static_cast<int>(sizeof(T));
   const bool tvec = a.V % epl == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
-  const dim3 tgrid(static_cast<unsigned>(std::min(a.rows, device_cus())));
+  const dim3 tgrid(static_cast<unsigned>(std::max(1, std::min((2 * a.rows + 3) / 4, 4 * device_cus()))));
   if (tvec)
     DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, true>), tgrid, dim3(kTnThreads), 0, st, a);
   else
@@ -730,6 +744,8 @@ StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V) {
   off = align_up(off + rows * sizeof(SmRec), 256);
   p.off_xf = off;
   off = align_up(off + rows * sizeof(int32_t), 256);
+  p.off_tp = off;
+  off = align_up(off + rows * sizeof(SmRec), 256);
   p.bytes = rows > 0 ? off : 0;
   return p;
 }
@@ -747,7 +763,8 @@ hipError_t launch_stats_markov(const void* backbone, const void* target, int dty
   SmArgs a{backbone, target, anchor, w1, w2, teacher, rows, gamma, V, r,
            reinterpret_cast<SmRec*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
            reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1),
-           reinterpret_cast<SmRec*>(w + pl.off_k2), reinterpret_cast<int32_t*>(w + pl.off_xf)};
+           reinterpret_cast<SmRec*>(w + pl.off_k2), reinterpret_cast<int32_t*>(w + pl.off_xf),
+           reinterpret_cast<SmRec*>(w + pl.off_tp)};
   if (dtype == DSPARK_BF16)
     return launch_sm_typed<uint16_t>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate,
                                      ce, bce, tau, sums, st);
