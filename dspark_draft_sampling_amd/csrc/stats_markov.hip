@@ -148,7 +148,6 @@ __device__ __forceinline__ void sm_tile(const SmArgs& a, const bf16x8 (&af)[kSmM
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vb = tok0 + wave * 16 * kSmMS;
   const int V = a.V, r = a.r;
-  const bool dead = __builtin_amdgcn_readfirstlane(vb) >= V;  // wave-uniform
   const int kpad = (r + 31) & ~31, ld = kpad + kSmPad, ksteps = kpad / 32;
   const T* bb = static_cast<const T*>(a.backbone);
   const T* tg = static_cast<const T*>(a.target);

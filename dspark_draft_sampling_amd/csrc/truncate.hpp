@@ -827,7 +827,7 @@ __device__ __forceinline__ void hist_pass_b(const Row& row, int V, const HistMap
 template <int NT, bool CW, class Row>
 __device__ __forceinline__ bool hist_cut(const Row& row, int V, const float* cm, int C, float M, float total,
                          float wa, float wb, float top_p, HistLds<NT>& H) {
-  constexpr int NW = NT / 64, CU = 8, PB = kHistBins / NT;
+  constexpr int CU = 8, PB = kHistBins / NT;
   static_assert(kHistBins % NT == 0, "bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (C > kMaxChunksBound || !(total > 0.0f) || !(total < pos_inf())) return false;
