@@ -28,13 +28,14 @@ DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_ESHAPE, DSPARK_EWORKSPACE, DSPAR
 DSPARK_BF16, DSPARK_F32 = 1, 2
 DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS, DSPARK_OP_STATS_BACKWARD = 1, 2, 3, 4
 DSPARK_OP_STATS_MARKOV = 5
-DSPARK_MAX_GAMMA, DSPARK_MAX_RANK = 16, 256  # as include/dspark.h
+DSPARK_MAX_GAMMA, DSPARK_MAX_RANK, DSPARK_MAX_VERIFY_BATCH = 16, 256, 65535  # as include/dspark.h
 FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
 
 __all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
            "dspark_accept_stats", "dspark_accept_stats_backward", "dspark_accept_stats_markov",
            "dspark_select_width", "dspark_workspace_size", "profile_enable",
-           "profile_summary", "DSPARK_MAX_GAMMA", "DSPARK_MAX_RANK"]
+           "profile_summary", "DSPARK_MAX_GAMMA", "DSPARK_MAX_RANK",
+           "DSPARK_MAX_VERIFY_BATCH"]
 
 
 class DSparkError(RuntimeError):

@@ -113,6 +113,7 @@ dspark_status dspark_verify(const void* target_logits, int logits_dtype,
   if (B < 0) return DSPARK_EINVAL;
   dspark_status s = check_common(logits_dtype, gamma, V);
   if (s != DSPARK_OK) return s;
+  if (B > DSPARK_MAX_VERIFY_BATCH) return DSPARK_ESHAPE;
   if (B == 0) return DSPARK_OK;
   if (!target_logits || !draft_tokens || !policy_ok(policy) || !accept_len || !out_tokens ||
       !flags)

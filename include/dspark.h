@@ -155,6 +155,7 @@ enum {
 #define DSPARK_MAX_RANK 256      /* r must also be a multiple of 16 */
 #define DSPARK_MAX_HIDDEN 65536  /* d                                */
 #define DSPARK_MAX_VOCAB (1 << 30)
+#define DSPARK_MAX_VERIFY_BATCH 65535  /* B of dspark_verify (one grid row each) */
 
 /* ---- per-request sampling policy: all DEVICE arrays of length B ----------- */
 typedef struct dspark_policy {
@@ -311,7 +312,8 @@ dspark_status dspark_markov_sample(
  *   accept_len     [B] int32: accepted proposals n in [0, n_d]
  *   out_tokens     [B, gamma+1] int32: the n+1 emitted tokens, then -1
  *   flags          [B, gamma+1] uint8: bits per target row
- * Errors: as dspark_markov_sample (gamma range, V range).
+ * Errors: as dspark_markov_sample (gamma range, V range), and ESHAPE for
+ * B > DSPARK_MAX_VERIFY_BATCH.
  * ------------------------------------------------------------------------- */
 dspark_status dspark_verify(
     const void* target_logits, int logits_dtype, const int32_t* draft_tokens,

@@ -120,6 +120,7 @@ def test_verify_validation(L):
     assert verify(L, dtype=7) == ds.DSPARK_EDTYPE
     assert verify(L, gamma=17) == ds.DSPARK_ESHAPE
     assert verify(L, V=(1 << 30) + 1) == ds.DSPARK_ESHAPE
+    assert verify(L, B=65536) == ds.DSPARK_ESHAPE  # the decide grid's row limit
     assert verify(L, target=None) == ds.DSPARK_EINVAL
     assert verify(L, out=None) == ds.DSPARK_EINVAL
     assert verify(L, pol=ds.dspark_policy(4096, None, 4096, 4096, 4096, 4096)) == ds.DSPARK_EINVAL
@@ -190,6 +191,7 @@ def test_binding_constants_match_header():
     defines = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(DSPARK_MAX_\w+)\s+(\d+)", text)}
     assert defines["DSPARK_MAX_GAMMA"] == ds.DSPARK_MAX_GAMMA
     assert defines["DSPARK_MAX_RANK"] == ds.DSPARK_MAX_RANK
+    assert defines["DSPARK_MAX_VERIFY_BATCH"] == ds.DSPARK_MAX_VERIFY_BATCH
     enums = dict(re.findall(r"\b(DSPARK_(?:BF16|F32|OP_\w+))\s*=\s*(\d+)", text))
     for name, value in enums.items():
         assert getattr(ds, name) == int(value), name
