@@ -122,8 +122,14 @@ _ws = {}
 
 
 def _workspace(op, device, nbytes):
-    """A cached per-(device, op) scratch buffer of at least nbytes."""
-    key = (device, op)
+    """A cached scratch buffer of at least nbytes per (device, stream, op).
+
+    Calls on one stream are ordered, so they can share a buffer; calls on
+    different streams may overlap, so each stream gets its own.  The buffer is
+    allocated while its stream is current, so when a larger one replaces it,
+    torch's allocator reuses the old memory only after that stream's pending
+    work."""
+    key = (device, torch.cuda.current_stream(device).cuda_stream, op)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
