@@ -325,8 +325,9 @@ def test_markov_plans_agree(config, decode_full, truncated_full):
 def test_markov_concurrent_streams(decode_full):
     """Two one-launch Markov calls enqueued at once on two streams: the
     library chains its fused launches on the device, so neither grid waits
-    on compute units the other holds; both end with a lone call's results and
-    no wait gives up."""
+    on compute units the other holds, and the binding gives each stream its
+    own workspace, so neither call's reset touches the other's chunk records;
+    both end with a lone call's results and no wait gives up."""
 
     inp = decode_full
     ref = G.markov(inp)
