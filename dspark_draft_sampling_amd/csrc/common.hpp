@@ -15,7 +15,8 @@
 
 namespace dspark {
 
-constexpr int kChunk = DSPARK_CHUNK;  // tokens per chunk of two-level Gumbel-max
+constexpr int kChunk = DSPARK_CHUNK;  // tokens per level-1 chunk of the sampler
+constexpr int kSub = DSPARK_SUB;      // tokens per level-2 sub-chunk of the sampler
 constexpr float kNearEps = 1e-6f;     // margin of the NEAR_THRESHOLD diagnostic
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -347,6 +348,73 @@ __device__ __forceinline__ Top2 block_top2(Top2 a, float* shv, int32_t* shi, flo
   Top2 r{shv[0], shi[0], shv2[0]};
 #pragma unroll
   for (int i = 1; i < NW; ++i) r = top2_merge(r, Top2{shv[i], shi[i], shv2[i]});
+  return r;
+}
+
+// Reductions over each group of four consecutive lanes (DPP quad_perm); the
+// result is the same on the four lanes.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  return fmaxf(v, dpp_f<kDppXor2>(v));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  return v + dpp_f<kDppXor2>(v);
+}
+
+// Levels 2 and 3 of the library's three-level Gumbel-max draw, inside the
+// chosen 256-token chunk c, by one whole wave.  Lane l holds the log-weights
+// lw[e] of tokens 256 c + 4 l + e (-inf: excluded or past the row), so lanes
+// 4 j .. 4 j + 3 hold sub-chunk j of the chunk.
+//  * level 2: sub-chunk j* = argmax_j (ln W_j + g_j), W_j its total weight,
+//    g_j the sub-chunk noise of global sub-chunk index 16 c + j;
+//  * level 3: token v* = argmax_{v in j*} (lw_v + g_v), token noise of v.
+// Ties go to the lowest index.  Returns the token (-1 if the chunk has no
+// weight), its log-weight, and whether a level's top-2 gap is within the
+// NEAR margin.  Every lane gets the same result.
+struct InChunk {
+  int32_t tok;
+  float lw;
+  bool near;
+};
+__device__ __forceinline__ InChunk draw_in_chunk(const float (&lw)[4], int c, uint64_t seed, int32_t pos,
+                                                 uint32_t req, uint32_t tag_sub, uint32_t tag_tok) {
+  const int lane = threadIdx.x & 63;
+  float m = fmaxf(fmaxf(lw[0], lw[1]), fmaxf(lw[2], lw[3]));
+  m = quad_max(m);
+  float s = 0.0f;
+  if (m > neg_inf()) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (lw[e] > neg_inf()) s += __builtin_amdgcn_exp2f((lw[e] - m) * kLog2e);
+  }
+  s = quad_sum(s);
+  const uint32_t j = static_cast<uint32_t>(c) * (kChunk / kSub) + static_cast<uint32_t>(lane >> 2);
+  const float g2 = gumbel(seed, j, pos, req, tag_sub);
+  Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
+  if ((lane & 3) == 0 && m > neg_inf()) t2 = Top2{m + logf(s) + g2, static_cast<int32_t>(j), neg_inf()};
+  t2 = wave_top2(t2);
+  InChunk r{-1, neg_inf(), false};
+  if (t2.i1 == INT32_MAX) return r;
+  r.near = t2.v2 > neg_inf() && near_gap(t2.v1, t2.v2);
+  // tokens 4 l .. 4 l + 3 of the chunk share Philox counter (64 c + l, pos, req, tag)
+  uint32_t c0 = static_cast<uint32_t>(c) * (kChunk / 4) + static_cast<uint32_t>(lane), c1 = static_cast<uint32_t>(pos),
+           c2 = req, c3 = tag_tok;
+  philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  const uint32_t w[4] = {c0, c1, c2, c3};
+  Top2 t3{neg_inf(), INT32_MAX, neg_inf()};
+  if (static_cast<uint32_t>(lane >> 2) == static_cast<uint32_t>(t2.i1) - static_cast<uint32_t>(c) * (kChunk / kSub)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (lw[e] > neg_inf()) t3 = top2_merge(t3, Top2{lw[e] + gumbel_of(w[e]), c * kChunk + 4 * lane + e, neg_inf()});
+  }
+  t3 = wave_top2(t3);
+  if (t3.i1 == INT32_MAX) return r;
+  r.tok = t3.i1;
+  if (t3.v2 > neg_inf() && near_gap(t3.v1, t3.v2)) r.near = true;
+  const int e = r.tok & 3;
+  const float mine = e == 0 ? lw[0] : e == 1 ? lw[1] : e == 2 ? lw[2] : lw[3];
+  r.lw = __shfl(mine, (r.tok - c * kChunk) >> 2, 64);
   return r;
 }
 

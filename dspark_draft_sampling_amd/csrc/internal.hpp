@@ -28,7 +28,7 @@ struct RowTrunc {
   float s_kept;
 };
 
-// Per (request, slice) best chunk of a two-level Gumbel-max draw.
+// Per (request, slice) best chunk (level 1) of a three-level Gumbel-max draw.
 struct Pick {
   float v1;     // best score
   int32_t i1;   // its chunk

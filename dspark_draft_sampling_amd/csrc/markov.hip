@@ -16,10 +16,10 @@
 //    16-byte stores.  The epilogue reduces each request's 256-token chunk to
 //    (max z, lowest argmax, sum exp(z - max), ln mass + chunk Gumbel).
 //  * finalize, per request: combines the chunk partials into the
-//    log-normaliser, picks the chunk by Gumbel-max over the chunk log-masses
-//    and the token inside it by Gumbel-max over its 256 z values (two-level
-//    Gumbel-max: exact, no prefix sum over the vocabulary), and applies
-//    top-k / top-p when the request truncates.
+//    log-normaliser, picks the chunk by Gumbel-max over the chunk log-masses,
+//    then a 16-token sub-chunk inside it and the token inside that (the
+//    library's three-level Gumbel-max: exact, no prefix sum over the
+//    vocabulary), and applies top-k / top-p when the request truncates.
 // The confidence head needs only x_{k-1}, so one kernel evaluates it for every
 // row after the last step.
 //
@@ -430,7 +430,7 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       am = better(am, ArgMax{L.red_m[w0 + w][n], L.red_i[w0 + w][n]});
       bad |= L.red_f[w0 + w][n];
     }
-    // chunk level of the two-level Gumbel-max draw: ln(mass) + chunk noise
+    // level 1 of the three-level Gumbel-max draw: ln(chunk mass) + chunk noise
     float score = neg_inf();
     const float Tb = a.pol.temperature[b];
     if (a.pol.mode[b] != 0 && !bad_temperature(Tb) && m > neg_inf() && m < pos_inf() && s > 0.0f)
@@ -487,7 +487,7 @@ struct QzRow {
   }
 };
 
-// Level-1 scores of the two-level draw restricted to the kept set
+// Level-1 scores of the three-level draw restricted to the kept set
 // (z >= thr): for each listed chunk (list[j], or j itself without a list)
 // holding kept tokens, log of its kept mass plus the chunk's Gumbel.  Wave w
 // takes entries w, w + NW, ...; four chunks' loads are issued together.
@@ -813,27 +813,18 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
       } else {
         qr.load4(v0, z);
       }
-      // tokens v0..v0+3 share Philox counter (v0 / 4, pos, req, tag)
-      uint32_t c0 = static_cast<uint32_t>(v0) >> 2, c1 = static_cast<uint32_t>(pos), c2 = req,
-               c3 = DSPARK_TAG_DRAFT_TOKEN;
-      philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(a.seed),
-                    static_cast<uint32_t>(a.seed >> 32));
-      const uint32_t wv[4] = {c0, c1, c2, c3};
-      Top2 t{neg_inf(), INT32_MAX, neg_inf()};
+      // levels 2 and 3 of the draw over the chunk's kept tokens
+      float lw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (z[e] > neg_inf() && z[e] >= thr)
-          t = top2_merge(t, Top2{z[e] + gumbel_of(wv[e]), v0 + e, neg_inf()});
-      t = wave_top2(t);
-      if (t.i1 == INT32_MAX) {
+      for (int e = 0; e < 4; ++e) lw[e] = (z[e] > neg_inf() && z[e] >= thr) ? z[e] : neg_inf();
+      const InChunk dr =
+          draw_in_chunk(lw, Bst.i1, a.seed, pos, req, DSPARK_TAG_DRAFT_SUB, DSPARK_TAG_DRAFT_TOKEN);
+      if (dr.tok < 0) {
         fl |= DSPARK_FLAG_EMPTY_ROW;
       } else {
-        x = t.i1;
-        if (t.v2 > neg_inf() && near_gap(t.v1, t.v2)) near = 1;
-        // the winner's z, from the lane that loaded it
-        const int owner = (x - Bst.i1 * kChunk) >> 2;
-        const float zo = (x & 3) == 0 ? z[0] : (x & 3) == 1 ? z[1] : (x & 3) == 2 ? z[2] : z[3];
-        zx = __shfl(zo, owner, 64);
+        x = dr.tok;
+        zx = dr.lw;
+        if (dr.near) near = 1;
       }
     }
     if (near) fl |= DSPARK_FLAG_NEAR_THRESHOLD;

@@ -17,9 +17,10 @@
 //     combines the segment partials of its rows and replays the accept scan
 //     (one thread per proposal, first reject by ballot), so all of them agree
 //     on the row to sample from.  Each then scores its slice of 256-token
-//     chunks for the two-level Gumbel-max draw; the last workgroup to finish
-//     (atomic ticket, armed by launch 1) picks the chunk and the token inside
-//     it and writes the outputs.
+//     chunks (level 1 of the library's three-level Gumbel-max draw); the last
+//     workgroup to finish (atomic ticket, armed by launch 1) picks the chunk,
+//     then the 16-token sub-chunk and the token inside it (levels 2 and 3),
+//     and writes the outputs.
 //
 // Sums use an integer base-2 shift: s = sum 2^(l cT - M2), cT = log2(e) / T,
 // M2 = floor(max(l) cT).  Partials with different shifts combine by exact
@@ -495,6 +496,8 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   __shared__ int32_t shi[kWaves];
   __shared__ int sh_last;
   __shared__ Top2 sh_best;
+  __shared__ int32_t sh_tok;
+  __shared__ uint32_t sh_near;
 
   const int G1 = gamma + 1;
   const int b = blockIdx.y, s2 = blockIdx.x;
@@ -728,27 +731,34 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   if (best.i1 != INT32_MAX && best.v2 > neg_inf() && near_gap(best.v1, best.v2))
     row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
 
-  Top2 tok{neg_inf(), INT32_MAX, neg_inf()};
-  if (best.i1 != INT32_MAX) {
-    const int v = best.i1 * kChunk + tid;
-    if (v < V) {
-      const float l = load_logit(trow, v);
-      float lw = neg_inf();
-      if (kind == 1) {
-        const float w = draw_weight(1, l, q_z[qoff + v], cT, M2, inv_s, lse_q, thr_q, thr_p);
-        lw = w > 0.0f ? logf(w) : neg_inf();
-      } else if (l > neg_inf() && l >= thr_p) {
-        lw = (l - rm[d.srow]) / Tb;
+  // levels 2 and 3 inside the chosen chunk, by wave 0 (lane l: tokens 4l..4l+3)
+  if (wave == 0) {
+    InChunk dr{-1, neg_inf(), false};
+    if (best.i1 != INT32_MAX) {
+      const int v0 = best.i1 * kChunk + 4 * lane;
+      float l[4], zq[4], lw[4];
+      load4<T, VEC4>(trow, v0, V, l);
+      if (kind == 1) load4<float, VEC4>(q_z + qoff, v0, V, zq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lw[e] = neg_inf();
+        if (kind == 1) {
+          const float w = draw_weight(1, l[e], zq[e], cT, M2, inv_s, lse_q, thr_q, thr_p);
+          lw[e] = w > 0.0f ? logf(w) : neg_inf();
+        } else if (l[e] > neg_inf() && l[e] >= thr_p) {
+          lw[e] = (l[e] - rm[d.srow]) / Tb;
+        }
       }
-      if (lw > neg_inf())
-        tok = Top2{lw + gumbel(seed, static_cast<uint32_t>(v), pos, req, DSPARK_TAG_TARGET_TOKEN),
-                   v, neg_inf()};
+      dr = draw_in_chunk(lw, best.i1, seed, pos, req, DSPARK_TAG_TARGET_SUB, DSPARK_TAG_TARGET_TOKEN);
+    }
+    if (lane == 0) {
+      sh_tok = dr.tok;
+      sh_near = dr.near ? 1u : 0u;
     }
   }
-  tok = block_top2<kWaves>(tok, shv, shi, shv2);
-  if (tok.i1 != INT32_MAX && tok.v2 > neg_inf() && near_gap(tok.v1, tok.v2))
-    row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
-  write_outputs(tok.i1 == INT32_MAX ? 0 : tok.i1, row_flags, d.srow);
+  __syncthreads();
+  if (sh_near) row_flags |= DSPARK_FLAG_NEAR_THRESHOLD;
+  write_outputs(sh_tok < 0 ? 0 : sh_tok, row_flags, d.srow);
 }
 
 template <typename T>

@@ -60,23 +60,31 @@
  *  "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) with
  *      key     = (seed & 0xffffffff, seed >> 32)
  *      counter = (i >> 2, (uint32_t)position, request_id, tag)
- *  taking 32-bit output word (i & 3), where i is the token index (or chunk
- *  index) being scored and `position` is the absolute position of the token
- *  being decided (anchor position + k for proposal / emitted token k).  Tags:
+ *  taking 32-bit output word (i & 3), where i is the token index (or chunk or
+ *  sub-chunk index) being scored and `position` is the absolute position of
+ *  the token being decided (anchor position + k for proposal / emitted token
+ *  k).  Tags:
  *      0 DSPARK_TAG_DRAFT_TOKEN   token-level draft noise
  *      1 DSPARK_TAG_ACCEPT        accept-test uniform (i = 0)
  *      2 DSPARK_TAG_TARGET_TOKEN  token-level residual / bonus noise
  *      3 DSPARK_TAG_DRAFT_CHUNK   chunk-level draft noise
  *      4 DSPARK_TAG_TARGET_CHUNK  chunk-level residual / bonus noise
+ *      5 DSPARK_TAG_DRAFT_SUB     sub-chunk-level draft noise
+ *      6 DSPARK_TAG_TARGET_SUB    sub-chunk-level residual / bonus noise
  *  Uniforms: Gumbel u = ((w >> 9) + 0.5) * 2^-23 in (0,1); accept
  *  u' = (w >> 8) * 2^-24 in [0,1).  Gumbel noise g = -ln(-ln u).
  *
- *  Sampling from weights w_v >= 0 is two-level Gumbel-max over chunks of
- *  DSPARK_CHUNK = 256 consecutive tokens: pick chunk
- *  c* = argmax_c (ln W_c + g_c) with W_c the chunk's total weight (chunk tag),
- *  then token v* = argmax_{v in c*} (ln w_v + g_v) (token tag); ties go to the
- *  lowest index.  P(v*) = (W_c / sum W) (w_v / W_c) = w_v / sum w exactly, and
- *  no prefix sum over the vocabulary is needed.
+ *  Sampling from weights w_v >= 0 is a three-level Gumbel-max descent over a
+ *  fixed partition of the vocabulary ([FT] "Probabilistic" requires only that
+ *  the emitted tokens follow the target distribution exactly):
+ *    1. chunk c* = argmax_c (ln W_c + g_c) over chunks of DSPARK_CHUNK = 256
+ *       consecutive tokens, W_c the chunk's total weight (chunk tag, i = c);
+ *    2. sub-chunk j* = argmax_j (ln W_j + g_j) over the DSPARK_SUB = 16-token
+ *       sub-chunks of c* (sub-chunk tag, i = the global index v / 16);
+ *    3. token v* = argmax_{v in j*} (ln w_v + g_v) (token tag, i = v).
+ *  Ties go to the lowest index.  P(v*) = (W_c/W)(W_j/W_c)(w_v/W_j) = w_v/W
+ *  exactly, no prefix sum over the vocabulary is needed, and every level can
+ *  be evaluated where its data already is.
  *
  * Sampling policy ([FT] "Probabilistic": p and q are both formed after the
  * request's temperature, top-k and top-p)
@@ -144,11 +152,14 @@ enum {
   DSPARK_TAG_ACCEPT = 1,
   DSPARK_TAG_TARGET_TOKEN = 2,
   DSPARK_TAG_DRAFT_CHUNK = 3,
-  DSPARK_TAG_TARGET_CHUNK = 4
+  DSPARK_TAG_TARGET_CHUNK = 4,
+  DSPARK_TAG_DRAFT_SUB = 5,
+  DSPARK_TAG_TARGET_SUB = 6
 };
 
-/* Tokens per chunk of the two-level Gumbel-max sampler. */
+/* Tokens per level-1 chunk and per level-2 sub-chunk of the sampler. */
 #define DSPARK_CHUNK 256
+#define DSPARK_SUB 16
 
 /* ---- supported ranges (DSPARK_ESHAPE outside them) ------------------------ */
 #define DSPARK_MAX_GAMMA 16
@@ -236,7 +247,7 @@ int dspark_markov_plan(int plan);
  * For k = 1..gamma, in order (x_0 = anchor[b]):
  *   y_k   = backbone_logits[b, k-1, :] + markov_w1[x_{k-1}, :] . markov_w2^T
  *           (bias_v = sum_i markov_w1[x_{k-1}, i] * markov_w2[v, i])
- *   q_k   = policy(y_k); x_k ~ q_k (two-level Gumbel-max, draft tags) for a
+ *   q_k   = policy(y_k); x_k ~ q_k (three-level Gumbel-max, draft tags) for a
  *           sampled row, x_k = argmax y_k for a greedy row
  *   c_k   = sigmoid(sum_i conf_w[i] h[b,k-1,i]
  *                   + sum_i conf_w[d+i] embed[x_{k-1}, i])

@@ -40,7 +40,8 @@
 namespace {
 
 constexpr double kEps = 1e-6;
-constexpr int kChunk = 256;  // tokens per chunk of the two-level sampler
+constexpr int kChunk = 256;  // tokens per level-1 chunk of the sampler
+constexpr int kSub = 16;     // tokens per level-2 sub-chunk of the sampler
 constexpr double kNegInf = -std::numeric_limits<double>::infinity();
 
 // flag bits (restated; same meaning as the library's per-row flags)
@@ -49,7 +50,8 @@ constexpr uint8_t F_NEAR = 1, F_NONFINITE = 2, F_RESID_ZERO = 4, F_EMPTY = 8,
 
 // Philox stream tags (restated)
 constexpr uint32_t TAG_DRAFT_TOKEN = 0, TAG_ACCEPT = 1, TAG_TARGET_TOKEN = 2,
-                   TAG_DRAFT_CHUNK = 3, TAG_TARGET_CHUNK = 4;
+                   TAG_DRAFT_CHUNK = 3, TAG_TARGET_CHUNK = 4, TAG_DRAFT_SUB = 5,
+                   TAG_TARGET_SUB = 6;
 
 // ---------------------------------------------------------------------------
 // Element conversion.  bf16 is the upper half of a binary32.
@@ -141,57 +143,84 @@ bool near_gap(double best, double second) {
 }
 
 // ---------------------------------------------------------------------------
-// Two-level Gumbel-max sample from log-weights lw (-inf = excluded).
-// Level 1 picks a chunk of kChunk consecutive tokens by Gumbel-max over the
-// chunk log-masses; level 2 picks a token inside it by Gumbel-max over the
-// token log-weights.  Ties go to the lowest index.  Returns -1 if every weight
-// is zero.  `near` is set if either level's top-2 gap is within the margin.
-int32_t sample_two_level(const double* lw, int32_t V, uint64_t seed,
-                         uint32_t request, int32_t position,
-                         uint32_t tag_chunk, uint32_t tag_token, bool* near) {
-  const int32_t C = (V + kChunk - 1) / kChunk;
-  // level 1
-  int32_t best_c = -1;
+// Three-level Gumbel-max sample from log-weights lw (-inf = excluded).
+// The pages fix only that emitted tokens follow the target distribution
+// exactly ([FT] "Exact decoding semantics", "Probabilistic"); the draw itself
+// is this library's reading: a Gumbel-max descent over a fixed partition of
+// the vocabulary.
+//   level 1: chunks of kChunk consecutive tokens, chunk c scored by
+//            ln(mass of c) + g(c, chunk tag);
+//   level 2: inside the chosen chunk, sub-chunks of kSub consecutive tokens,
+//            sub-chunk j (global index j = v / kSub) scored by
+//            ln(mass of j) + g(j, sub-chunk tag);
+//   level 3: inside the chosen sub-chunk, token v scored by lw_v + g(v, token
+//            tag).
+// Each level's winner is a draw from that level's masses renormalised over
+// the chosen parent, with independent noise, so
+// P(v) = (W_c / W)(W_j / W_c)(w_v / W_j) = w_v / W exactly.  Ties go to the
+// lowest index.  Returns -1 if every weight is zero.  `near` is set if any
+// level's top-2 gap is within the margin.
+namespace {
+struct Best2 {
+  int32_t arg = -1;
   double s1 = kNegInf, s2 = kNegInf;
-  for (int32_t c = 0; c < C; ++c) {
-    const int32_t lo = c * kChunk, hi = std::min(V, lo + kChunk);
-    double mx = kNegInf;
-    for (int32_t v = lo; v < hi; ++v) mx = std::max(mx, lw[v]);
-    if (mx == kNegInf) continue;
-    double s = 0.0;
-    for (int32_t v = lo; v < hi; ++v)
-      if (lw[v] != kNegInf) s += std::exp(lw[v] - mx);
-    const double score =
-        mx + std::log(s) + gumbel(seed, static_cast<uint32_t>(c), position, request, tag_chunk);
+  void offer(double score, int32_t idx) {
     if (score > s1) {
       s2 = s1;
       s1 = score;
-      best_c = c;
+      arg = idx;
     } else if (score > s2) {
       s2 = score;
     }
   }
-  if (best_c < 0) return -1;
-  bool nr = (s2 != kNegInf) && near_gap(s1, s2);
-  // level 2
-  const int32_t lo = best_c * kChunk, hi = std::min(V, lo + kChunk);
-  int32_t best_v = -1;
-  double t1 = kNegInf, t2 = kNegInf;
-  for (int32_t v = lo; v < hi; ++v) {
-    if (lw[v] == kNegInf) continue;
-    const double score =
-        lw[v] + gumbel(seed, static_cast<uint32_t>(v), position, request, tag_token);
-    if (score > t1) {
-      t2 = t1;
-      t1 = score;
-      best_v = v;
-    } else if (score > t2) {
-      t2 = score;
-    }
+  bool near() const { return arg >= 0 && s2 != kNegInf && near_gap(s1, s2); }
+};
+
+// ln(sum of exp(lw_v)) over v in [lo, hi), -inf if every lw_v is -inf
+double log_mass(const double* lw, int32_t lo, int32_t hi) {
+  double mx = kNegInf;
+  for (int32_t v = lo; v < hi; ++v) mx = std::max(mx, lw[v]);
+  if (mx == kNegInf) return kNegInf;
+  double s = 0.0;
+  for (int32_t v = lo; v < hi; ++v)
+    if (lw[v] != kNegInf) s += std::exp(lw[v] - mx);
+  return mx + std::log(s);
+}
+}  // namespace
+
+int32_t sample_three_level(const double* lw, int32_t V, uint64_t seed,
+                           uint32_t request, int32_t position,
+                           uint32_t tag_chunk, uint32_t tag_sub,
+                           uint32_t tag_token, bool* near) {
+  // level 1: chunks
+  Best2 l1;
+  const int32_t C = (V + kChunk - 1) / kChunk;
+  for (int32_t c = 0; c < C; ++c) {
+    const double lm = log_mass(lw, c * kChunk, std::min(V, (c + 1) * kChunk));
+    if (lm == kNegInf) continue;
+    l1.offer(lm + gumbel(seed, static_cast<uint32_t>(c), position, request, tag_chunk), c);
   }
-  if (t2 != kNegInf && near_gap(t1, t2)) nr = true;
-  *near = nr;
-  return best_v;
+  if (l1.arg < 0) {
+    *near = false;
+    return -1;
+  }
+  // level 2: sub-chunks of the chosen chunk
+  Best2 l2;
+  const int32_t c_lo = l1.arg * kChunk, c_hi = std::min(V, c_lo + kChunk);
+  for (int32_t j = c_lo / kSub; j * kSub < c_hi; ++j) {
+    const double lm = log_mass(lw, j * kSub, std::min(c_hi, (j + 1) * kSub));
+    if (lm == kNegInf) continue;
+    l2.offer(lm + gumbel(seed, static_cast<uint32_t>(j), position, request, tag_sub), j);
+  }
+  // level 3: tokens of the chosen sub-chunk
+  Best2 l3;
+  const int32_t j_lo = l2.arg * kSub, j_hi = std::min(c_hi, j_lo + kSub);
+  for (int32_t v = j_lo; v < j_hi; ++v) {
+    if (lw[v] == kNegInf) continue;
+    l3.offer(lw[v] + gumbel(seed, static_cast<uint32_t>(v), position, request, tag_token), v);
+  }
+  *near = l1.near() || l2.near() || l3.near();
+  return l3.arg;
 }
 
 // ---------------------------------------------------------------------------
@@ -378,14 +407,14 @@ double oracle_accept_uniform(uint64_t seed, int32_t position, uint32_t request) 
   return accept_uniform(seed, position, request);
 }
 
-// Two-level Gumbel-max over log-weights (for distribution tests).
-int32_t oracle_sample_two_level(const double* lw, int32_t V, uint64_t seed,
-                                uint32_t request, int32_t position,
-                                uint32_t tag_chunk, uint32_t tag_token,
-                                int32_t* near) {
+// Three-level Gumbel-max over log-weights (for distribution tests).
+int32_t oracle_sample_three_level(const double* lw, int32_t V, uint64_t seed,
+                                  uint32_t request, int32_t position,
+                                  uint32_t tag_chunk, uint32_t tag_sub,
+                                  uint32_t tag_token, int32_t* near) {
   bool nr = false;
-  const int32_t v = sample_two_level(lw, V, seed, request, position, tag_chunk,
-                                     tag_token, &nr);
+  const int32_t v = sample_three_level(lw, V, seed, request, position, tag_chunk,
+                                       tag_sub, tag_token, &nr);
   if (near) *near = nr ? 1 : 0;
   return v;
 }
@@ -416,7 +445,7 @@ int32_t oracle_policy_row(const double* l, int32_t V, double T, int32_t top_k,
 // x_0 = anchor:
 //   y_k = backbone[b,k-1,:] + A[x_{k-1},:] . Bt^T      (A = markov_w1 [V,r],
 //                                                       Bt = markov_w2 [V,r])
-//   q_k = policy(y_k);  x_k ~ q_k (two-level Gumbel-max, draft tags,
+//   q_k = policy(y_k);  x_k ~ q_k (three-level Gumbel-max, draft tags,
 //                       position = anchor position + k)  or argmax if greedy
 //   c_k = sigmoid(w[:d] . h[b,k-1,:] + w[d:] . E[x_{k-1},:])   (no bias term,
 //         order [h ; embed] as the confidence-head formula writes it)
@@ -489,8 +518,8 @@ int32_t oracle_markov_sample(
         for (int32_t v = 0; v < V; ++v)
           if (rp.kept[v]) lw[v] = rp.z[v];
         bool nr = false;
-        x = sample_two_level(lw.data(), V, seed, request_id[b], position[b] + k,
-                             TAG_DRAFT_CHUNK, TAG_DRAFT_TOKEN, &nr);
+        x = sample_three_level(lw.data(), V, seed, request_id[b], position[b] + k,
+                               TAG_DRAFT_CHUNK, TAG_DRAFT_SUB, TAG_DRAFT_TOKEN, &nr);
         if (nr) fl |= F_NEAR;
         if (x < 0) {
           x = 0;
@@ -628,8 +657,8 @@ int32_t oracle_verify(const void* target, int32_t dtype,
         fl[j - 1] |= F_RESID_ZERO;
         for (int32_t v = 0; v < V; ++v) lw[v] = rp.kept[v] ? rp.z[v] : kNegInf;
       }
-      emitted = sample_two_level(lw.data(), V, seed, request_id[b], pos0 + j,
-                                 TAG_TARGET_CHUNK, TAG_TARGET_TOKEN, &nr);
+      emitted = sample_three_level(lw.data(), V, seed, request_id[b], pos0 + j,
+                                   TAG_TARGET_CHUNK, TAG_TARGET_SUB, TAG_TARGET_TOKEN, &nr);
       if (nr) fl[j - 1] |= F_NEAR;
       if (emitted < 0) emitted = 0;
       for (int32_t k = 1; k < j; ++k) out[k - 1] = x[k];
@@ -644,9 +673,9 @@ int32_t oracle_verify(const void* target, int32_t dtype,
       for (int32_t v = 0; v < V; ++v)
         if (rp.kept[v]) lw[v] = rp.z[v];
       bool nr = false;
-      emitted = sample_two_level(lw.data(), V, seed, request_id[b],
-                                 pos0 + nd + 1, TAG_TARGET_CHUNK,
-                                 TAG_TARGET_TOKEN, &nr);
+      emitted = sample_three_level(lw.data(), V, seed, request_id[b],
+                                   pos0 + nd + 1, TAG_TARGET_CHUNK,
+                                   TAG_TARGET_SUB, TAG_TARGET_TOKEN, &nr);
       if (nr) fl[nd] |= F_NEAR;
       if (emitted < 0) emitted = 0;
       for (int32_t k = 1; k <= nd; ++k) out[k - 1] = x[k];

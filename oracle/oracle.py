@@ -24,7 +24,9 @@ _lib = None
 DTYPES = {"bf16": 1, "f32": 2}
 
 F_NEAR, F_NONFINITE, F_RESID_ZERO, F_EMPTY, F_BAD_POLICY = 1, 2, 4, 8, 16
-TAG_DRAFT_TOKEN, TAG_ACCEPT, TAG_TARGET_TOKEN, TAG_DRAFT_CHUNK, TAG_TARGET_CHUNK = 0, 1, 2, 3, 4
+(TAG_DRAFT_TOKEN, TAG_ACCEPT, TAG_TARGET_TOKEN, TAG_DRAFT_CHUNK, TAG_TARGET_CHUNK, TAG_DRAFT_SUB,
+ TAG_TARGET_SUB) = 0, 1, 2, 3, 4, 5, 6
+CHUNK, SUB = 256, 16  # tokens per level-1 chunk and per level-2 sub-chunk of the sampler
 
 
 def lib():
@@ -51,8 +53,8 @@ def _declare(L):
     L.oracle_gumbel.restype = f64
     L.oracle_accept_uniform.argtypes = [u64, i32, u32]
     L.oracle_accept_uniform.restype = f64
-    L.oracle_sample_two_level.argtypes = [P, i32, u64, u32, i32, u32, u32, P]
-    L.oracle_sample_two_level.restype = i32
+    L.oracle_sample_three_level.argtypes = [P, i32, u64, u32, i32, u32, u32, u32, P]
+    L.oracle_sample_three_level.restype = i32
     L.oracle_policy_row.argtypes = [P, i32, f64, i32, f64, i32, P, P, P, P, P]
     L.oracle_policy_row.restype = i32
     L.oracle_markov_sample.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -107,13 +109,14 @@ def accept_uniform(seed, position, request):
     return float(lib().oracle_accept_uniform(seed, position, request))
 
 
-def sample_two_level(lw, seed, request, position, tag_chunk=TAG_DRAFT_CHUNK,
-                     tag_token=TAG_DRAFT_TOKEN):
-    """Two-level Gumbel-max draw from log-weights lw (-inf = excluded)."""
+def sample_three_level(lw, seed, request, position, tag_chunk=TAG_DRAFT_CHUNK,
+                       tag_sub=TAG_DRAFT_SUB, tag_token=TAG_DRAFT_TOKEN):
+    """Three-level Gumbel-max draw (chunk, sub-chunk, token) from log-weights lw
+    (-inf = excluded).  Returns (token or -1, near flag)."""
     a = _c(lw, np.float64)
     near = C.c_int32(0)
-    v = lib().oracle_sample_two_level(_p(a), a.size, seed, request, position,
-                                      tag_chunk, tag_token, C.byref(near))
+    v = lib().oracle_sample_three_level(_p(a), a.size, seed, request, position,
+                                        tag_chunk, tag_sub, tag_token, C.byref(near))
     return int(v), bool(near.value)
 
 
