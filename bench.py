@@ -57,8 +57,11 @@ def parse():
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
     ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative"], default="auto",
-                    help="Markov launch plan: one cooperative launch when it fits (auto) or "
-                         "two launches per step")
+                    help="Markov launch plan: one launch for all steps when its grid fits "
+                         "(auto), the same through cooperative launch, or two launches per step")
+    ap.add_argument("--truncation-arrays", action="store_true",
+                    help="pass the top-k / top-p arrays even when no request truncates (the "
+                         "library then takes its truncating kernels)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="instead of the benchmark, write the rocprofv3 summary of the "
                          "profiling run under DIR to profiles/")
@@ -84,7 +87,7 @@ def copy_calibration(mib):
 def kernel_bytes(name, B, g, V, r, d, S, R):
     """Algorithmic (compulsory) HBM bytes of one launch of each kernel."""
     C = (V + 255) // 256
-    if name == "markov_fused":     # one launch for all gamma steps: backbone, q, W2 once, A rows
+    if name in ("markov_fused", "markov_fast"):  # one launch for all gamma steps: backbone, q, W2 once, A rows
         return 2 * B * g * V + 4 * S * g * V + 2 * r * V + 2 * B * g * r
     if name == "markov_step":      # backbone row + q row written + W2 (once per call) + A rows
         return 2 * B * V + 4 * S * V + (2 * r * V) / g + 2 * B * r
@@ -385,10 +388,14 @@ def run_decode(args, torch, ds):
                          embed=bf(inp["embed"])))
     anchor = torch.from_numpy(inp["anchor"]).to(dev)
     conf_w = torch.from_numpy(inp["conf_w"]).to(dev)
+    # truncation arrays only when some request truncates: the library then
+    # skips every truncation pass (untruncated Markov kernel, no verify_select)
+    trunc = args.truncation_arrays or bool(np.any((inp["top_k"] > 0) & (inp["top_k"] < V))
+                                           or np.any(inp["top_p"] < 1))
     pol = ds.Policy(mode=torch.from_numpy(inp["mode"]).to(dev),
                     temperature=torch.from_numpy(inp["temperature"]).to(dev),
-                    top_k=torch.from_numpy(inp["top_k"]).to(dev),
-                    top_p=torch.from_numpy(inp["top_p"]).to(dev),
+                    top_k=torch.from_numpy(inp["top_k"]).to(dev) if trunc else None,
+                    top_p=torch.from_numpy(inp["top_p"]).to(dev) if trunc else None,
                     request_id=torch.from_numpy(inp["request_id"].view(np.int32)).to(dev),
                     position=torch.from_numpy(inp["position"]).to(dev))
     # the accept stats read the same rows: draft logits and the first gamma target rows

@@ -15,9 +15,11 @@ fallback: without the built library every call raises.
 
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
 from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
@@ -87,8 +89,17 @@ def lib():
         L.dspark_markov_plan.restype = C.c_int
         L.dspark_profile_summary.argtypes = [C.c_char_p, sz]
         L.dspark_profile_summary.restype = C.c_int
+        L.dspark_release.argtypes = []
+        L.dspark_release.restype = C.c_int
         _lib = L
+        # the library's HIP objects go before the runtime's own teardown
+        atexit.register(_release_at_exit)
     return _lib
+
+
+def _release_at_exit():
+    if _lib is not None:
+        _lib.dspark_release()
 
 
 def _check(rc):
@@ -100,14 +111,28 @@ def _p(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
-def _dev_tensor(t, dtype, name):
+def _dev_tensor(t, dtype, name, shape=None, device=None):
+    """Check that t is a contiguous GPU tensor of this dtype (and shape and
+    device, when given): the library reads and writes exactly that extent."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise DSparkError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise DSparkError(f"{name} must have dtype {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise DSparkError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise DSparkError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise DSparkError(f"{name} must be on {device}, got {t.device}")
     return t
+
+
+def _check_out(out, spec, device, what):
+    """Check every caller-supplied output tensor against (name, dtype, shape)."""
+    for name, dtype, shape in spec:
+        if name not in out or out[name] is None:
+            raise DSparkError(f"{what}: out is missing {name}")
+        _dev_tensor(out[name], dtype, f"out[{name!r}]", shape, device)
 
 
 def _logits_dtype(t, name):
@@ -143,24 +168,32 @@ def dspark_workspace_size(op, B, gamma, V, r=0, d=0):
 
 @dataclass
 class Policy:
-    """Per-request sampling policy as device tensors of length B."""
+    """Per-request sampling policy as device tensors of length B.
 
-    mode: torch.Tensor          # uint8: 0 greedy, 1 sampled
-    temperature: torch.Tensor   # float32
-    top_k: torch.Tensor         # int32 (0 = off)
-    top_p: torch.Tensor         # float32 (>= 1 = off)
-    request_id: torch.Tensor    # int32 holding the uint32 request ids
-    position: torch.Tensor      # int32: absolute position of the anchor
+    top_k and top_p are both given or both None; None means that no request of
+    the call truncates (the library then skips every truncation pass and the
+    Markov sampler takes its untruncated one-launch kernel)."""
 
-    def c(self):
-        _dev_tensor(self.mode, torch.uint8, "mode")
-        _dev_tensor(self.temperature, torch.float32, "temperature")
-        _dev_tensor(self.top_k, torch.int32, "top_k")
-        _dev_tensor(self.top_p, torch.float32, "top_p")
-        _dev_tensor(self.request_id, torch.int32, "request_id")
-        _dev_tensor(self.position, torch.int32, "position")
+    mode: torch.Tensor                    # uint8: 0 greedy, 1 sampled
+    temperature: torch.Tensor             # float32
+    top_k: Optional[torch.Tensor]         # int32 (0 = off), or None
+    top_p: Optional[torch.Tensor]         # float32 (>= 1 = off), or None
+    request_id: torch.Tensor              # int32 holding the uint32 request ids
+    position: torch.Tensor                # int32: absolute position of the anchor
+
+    def c(self, B, device):
+        _dev_tensor(self.mode, torch.uint8, "mode", (B,), device)
+        _dev_tensor(self.temperature, torch.float32, "temperature", (B,), device)
+        if (self.top_k is None) != (self.top_p is None):
+            raise DSparkError("policy: top_k and top_p must both be given or both be None")
+        if self.top_k is not None:
+            _dev_tensor(self.top_k, torch.int32, "top_k", (B,), device)
+            _dev_tensor(self.top_p, torch.float32, "top_p", (B,), device)
+        _dev_tensor(self.request_id, torch.int32, "request_id", (B,), device)
+        _dev_tensor(self.position, torch.int32, "position", (B,), device)
         return dspark_policy(self.mode.data_ptr(), self.temperature.data_ptr(),
-                             self.top_k.data_ptr(), self.top_p.data_ptr(),
+                             None if self.top_k is None else self.top_k.data_ptr(),
+                             None if self.top_p is None else self.top_p.data_ptr(),
                              self.request_id.data_ptr(), self.position.data_ptr())
 
 
@@ -175,32 +208,35 @@ def dspark_markov_sample(backbone, anchor, markov_w1, markov_w2, hidden, embed, 
     confidence [B,g] f32, flags [B,g] uint8."""
     dt = _logits_dtype(backbone, "backbone")
     _dev_tensor(backbone, backbone.dtype, "backbone")
+    if backbone.dim() != 3:
+        raise DSparkError("markov_sample: backbone must be [B, gamma, V]")
     B, g, V = backbone.shape
-    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1")
-    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2")
-    _dev_tensor(hidden, torch.bfloat16, "hidden")
-    _dev_tensor(embed, torch.bfloat16, "embed")
-    _dev_tensor(conf_w, torch.float32, "conf_w")
-    _dev_tensor(anchor, torch.int32, "anchor")
+    dev = backbone.device
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1", device=dev)
+    if markov_w1.dim() != 2 or hidden.dim() != 3:
+        raise DSparkError("markov_sample: markov_w1 must be [V, r] and hidden [B, gamma, d]")
     r = markov_w1.shape[1]
     d = hidden.shape[2]
-    if markov_w1.shape != (V, r) or markov_w2.shape != (V, r) or hidden.shape != (B, g, d) \
-            or embed.shape != (V, d) or conf_w.shape != (2 * d,) or anchor.shape != (B,):
-        raise DSparkError("markov_sample: inconsistent shapes")
-    dev = backbone.device
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1", (V, r), dev)
+    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2", (V, r), dev)
+    _dev_tensor(hidden, torch.bfloat16, "hidden", (B, g, d), dev)
+    _dev_tensor(embed, torch.bfloat16, "embed", (V, d), dev)
+    _dev_tensor(conf_w, torch.float32, "conf_w", (2 * d,), dev)
+    _dev_tensor(anchor, torch.int32, "anchor", (B,), dev)
+    pol = policy.c(B, dev)
+    spec = [("draft_tokens", torch.int32, (B, g)), ("q_logits", torch.float32, (B, g, V)),
+            ("q_lse", torch.float32, (B, g)), ("q_thr", torch.float32, (B, g)),
+            ("q_tok", torch.float32, (B, g)), ("confidence", torch.float32, (B, g)),
+            ("flags", torch.uint8, (B, g))]
     if out is None:
-        out = dict(draft_tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
-                   q_logits=torch.empty((B, g, V), dtype=torch.float32, device=dev),
-                   q_lse=torch.empty((B, g), dtype=torch.float32, device=dev),
-                   q_thr=torch.empty((B, g), dtype=torch.float32, device=dev),
-                   q_tok=torch.empty((B, g), dtype=torch.float32, device=dev),
-                   confidence=torch.empty((B, g), dtype=torch.float32, device=dev),
-                   flags=torch.empty((B, g), dtype=torch.uint8, device=dev))
+        out = {name: torch.empty(shape, dtype=dtype, device=dev) for name, dtype, shape in spec}
+    else:
+        _check_out(out, spec, dev, "markov_sample")
     nb = dspark_workspace_size(DSPARK_OP_MARKOV, B, g, V, r, d)
     ws = _workspace(DSPARK_OP_MARKOV, dev, nb)
     rc = lib().dspark_markov_sample(
         _p(backbone), dt, _p(anchor), _p(markov_w1), _p(markov_w2), _p(hidden), _p(embed),
-        _p(conf_w), policy.c(), int(seed), B, g, V, r, d, _p(out["draft_tokens"]),
+        _p(conf_w), pol, int(seed), B, g, V, r, d, _p(out["draft_tokens"]),
         _p(out["q_logits"]), _p(out["q_lse"]), _p(out["q_thr"]), _p(out["q_tok"]),
         _p(out["confidence"]), _p(out["flags"]), _p(ws), ws.numel(), _stream(dev))
     _check(rc)
@@ -213,31 +249,51 @@ def dspark_verify(target, draft_tokens, policy: Policy, q_logits=None, q_lse=Non
     int32, flags [B,g+1] uint8 (device tensors)."""
     dt = _logits_dtype(target, "target")
     _dev_tensor(target, target.dtype, "target")
+    if target.dim() != 3:
+        raise DSparkError("verify: target must be [B, gamma + 1, V]")
     B, g1, V = target.shape
     g = g1 - 1
-    _dev_tensor(draft_tokens, torch.int32, "draft_tokens")
-    if draft_tokens.shape != (B, g):
-        raise DSparkError("verify: draft_tokens must be [B, gamma]")
+    dev = target.device
+    _dev_tensor(draft_tokens, torch.int32, "draft_tokens", (B, g), dev)
     for name, t, shape in [("q_logits", q_logits, (B, g, V)), ("q_lse", q_lse, (B, g)),
                            ("q_thr", q_thr, (B, g)), ("q_tok", q_tok, (B, g))]:
         if t is not None:
-            _dev_tensor(t, torch.float32, name)
-            if tuple(t.shape) != shape:
-                raise DSparkError(f"verify: {name} must be {shape}")
+            _dev_tensor(t, torch.float32, name, shape, dev)
     if n_draft is not None:
-        _dev_tensor(n_draft, torch.int32, "n_draft")
-    dev = target.device
+        _dev_tensor(n_draft, torch.int32, "n_draft", (B,), dev)
+    pol = policy.c(B, dev)
+    spec = [("accept_len", torch.int32, (B,)), ("out_tokens", torch.int32, (B, g1)),
+            ("flags", torch.uint8, (B, g1))]
     if out is None:
-        out = dict(accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((B, g1), dtype=torch.int32, device=dev),
-                   flags=torch.empty((B, g1), dtype=torch.uint8, device=dev))
+        out = {name: torch.empty(shape, dtype=dtype, device=dev) for name, dtype, shape in spec}
+    else:
+        _check_out(out, spec, dev, "verify")
     nb = dspark_workspace_size(DSPARK_OP_VERIFY, B, g, V)
     ws = _workspace(DSPARK_OP_VERIFY, dev, nb)
     rc = lib().dspark_verify(_p(target), dt, _p(draft_tokens), _p(q_logits), _p(q_lse),
-                             _p(q_thr), _p(q_tok), _p(n_draft), policy.c(), int(seed), B, g, V,
+                             _p(q_thr), _p(q_tok), _p(n_draft), pol, int(seed), B, g, V,
                              _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["flags"]),
                              _p(ws), ws.numel(), _stream(dev))
     _check(rc)
+    return out
+
+
+_STATS_OUT = ["l1", "accept_rate", "ce", "bce"]
+
+
+def _stats_args(what, target, draft, teacher, conf_logits, block_mask, out, dev):
+    """Checks shared by the statistics calls; returns the output dict."""
+    N, g, V = draft.shape
+    _dev_tensor(target, draft.dtype, "target", (N, g, V), dev)
+    _dev_tensor(teacher, torch.int32, "teacher", (N, g), dev)
+    _dev_tensor(conf_logits, torch.float32, "conf_logits", (N, g), dev)
+    if block_mask is not None:
+        _dev_tensor(block_mask, torch.uint8, "block_mask", (N,), dev)
+    spec = [(name, torch.float32, (N, g)) for name in _STATS_OUT]
+    spec += [("tau", torch.float32, (N,)), ("sums", torch.float32, (12,))]
+    if out is None:
+        return {name: torch.empty(shape, dtype=dtype, device=dev) for name, dtype, shape in spec}
+    _check_out(out, spec, dev, what)
     return out
 
 
@@ -247,20 +303,11 @@ def dspark_accept_stats(draft, target, teacher, conf_logits, block_mask=None, w_
     tau [N], sums [12] (float32 device tensors)."""
     dt = _logits_dtype(draft, "draft")
     _dev_tensor(draft, draft.dtype, "draft")
-    _dev_tensor(target, draft.dtype, "target")
+    if draft.dim() != 3:
+        raise DSparkError("accept_stats: draft must be [N, gamma, V]")
     N, g, V = draft.shape
-    if target.shape != draft.shape:
-        raise DSparkError("accept_stats: draft and target shapes differ")
-    _dev_tensor(teacher, torch.int32, "teacher")
-    _dev_tensor(conf_logits, torch.float32, "conf_logits")
-    if block_mask is not None:
-        _dev_tensor(block_mask, torch.uint8, "block_mask")
     dev = draft.device
-    if out is None:
-        f = dict(dtype=torch.float32, device=dev)
-        out = dict(l1=torch.empty((N, g), **f), accept_rate=torch.empty((N, g), **f),
-                   ce=torch.empty((N, g), **f), bce=torch.empty((N, g), **f),
-                   tau=torch.empty((N,), **f), sums=torch.empty((12,), **f))
+    out = _stats_args("accept_stats", target, draft, teacher, conf_logits, block_mask, out, dev)
     nb = dspark_workspace_size(DSPARK_OP_STATS, N, g, V)
     ws = _workspace(DSPARK_OP_STATS, dev, nb) if nb > 0 else None
     rc = lib().dspark_accept_stats(_p(draft), _p(target), dt, _p(teacher), _p(conf_logits),
@@ -280,26 +327,19 @@ def dspark_accept_stats_markov(backbone, target, anchor, markov_w1, markov_w2, t
     dspark_accept_stats."""
     dt = _logits_dtype(backbone, "backbone")
     _dev_tensor(backbone, backbone.dtype, "backbone")
-    _dev_tensor(target, backbone.dtype, "target")
+    if backbone.dim() != 3:
+        raise DSparkError("accept_stats_markov: backbone must be [N, gamma, V]")
     N, g, V = backbone.shape
-    if target.shape != backbone.shape:
-        raise DSparkError("accept_stats_markov: backbone and target shapes differ")
-    _dev_tensor(anchor, torch.int32, "anchor")
-    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1")
-    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2")
-    r = markov_w1.shape[1]
-    if markov_w1.shape != (V, r) or markov_w2.shape != (V, r):
-        raise DSparkError("accept_stats_markov: markov_w1 and markov_w2 must be [V, r]")
-    _dev_tensor(teacher, torch.int32, "teacher")
-    _dev_tensor(conf_logits, torch.float32, "conf_logits")
-    if block_mask is not None:
-        _dev_tensor(block_mask, torch.uint8, "block_mask")
     dev = backbone.device
-    if out is None:
-        f = dict(dtype=torch.float32, device=dev)
-        out = dict(l1=torch.empty((N, g), **f), accept_rate=torch.empty((N, g), **f),
-                   ce=torch.empty((N, g), **f), bce=torch.empty((N, g), **f),
-                   tau=torch.empty((N,), **f), sums=torch.empty((12,), **f))
+    _dev_tensor(anchor, torch.int32, "anchor", (N,), dev)
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1", device=dev)
+    if markov_w1.dim() != 2:
+        raise DSparkError("accept_stats_markov: markov_w1 must be [V, r]")
+    r = markov_w1.shape[1]
+    _dev_tensor(markov_w1, torch.bfloat16, "markov_w1", (V, r), dev)
+    _dev_tensor(markov_w2, torch.bfloat16, "markov_w2", (V, r), dev)
+    out = _stats_args("accept_stats_markov", target, backbone, teacher, conf_logits, block_mask, out,
+                      dev)
     nb = dspark_workspace_size(DSPARK_OP_STATS_MARKOV, N, g, V, r)
     ws = _workspace(DSPARK_OP_STATS_MARKOV, dev, nb) if nb > 0 else None
     rc = lib().dspark_accept_stats_markov(_p(backbone), _p(target), dt, _p(anchor), _p(markov_w1),
@@ -320,22 +360,24 @@ def dspark_accept_stats_backward(draft, target, teacher, conf_logits, block_mask
     tensors).  grad_scale: a one-element float32 device tensor or None (1)."""
     dt = _logits_dtype(draft, "draft")
     _dev_tensor(draft, draft.dtype, "draft")
-    _dev_tensor(target, draft.dtype, "target")
+    if draft.dim() != 3:
+        raise DSparkError("accept_stats_backward: draft must be [N, gamma, V]")
     N, g, V = draft.shape
-    if target.shape != draft.shape:
-        raise DSparkError("accept_stats_backward: draft and target shapes differ")
-    _dev_tensor(teacher, torch.int32, "teacher")
-    _dev_tensor(conf_logits, torch.float32, "conf_logits")
+    dev = draft.device
+    _dev_tensor(target, draft.dtype, "target", (N, g, V), dev)
+    _dev_tensor(teacher, torch.int32, "teacher", (N, g), dev)
+    _dev_tensor(conf_logits, torch.float32, "conf_logits", (N, g), dev)
     if block_mask is not None:
-        _dev_tensor(block_mask, torch.uint8, "block_mask")
+        _dev_tensor(block_mask, torch.uint8, "block_mask", (N,), dev)
     if grad_scale is not None:
-        _dev_tensor(grad_scale, torch.float32, "grad_scale")
+        _dev_tensor(grad_scale, torch.float32, "grad_scale", device=dev)
         if grad_scale.numel() != 1:
             raise DSparkError("accept_stats_backward: grad_scale must hold one value")
-    dev = draft.device
+    spec = [("grad_draft", draft.dtype, (N, g, V)), ("grad_conf", torch.float32, (N, g))]
     if out is None:
-        out = dict(grad_draft=torch.empty((N, g, V), dtype=draft.dtype, device=dev),
-                   grad_conf=torch.empty((N, g), dtype=torch.float32, device=dev))
+        out = {name: torch.empty(shape, dtype=dtype, device=dev) for name, dtype, shape in spec}
+    else:
+        _check_out(out, spec, dev, "accept_stats_backward")
     nb = dspark_workspace_size(DSPARK_OP_STATS_BACKWARD, N, g, V)
     ws = _workspace(DSPARK_OP_STATS_BACKWARD, dev, nb) if nb > 0 else None
     rc = lib().dspark_accept_stats_backward(_p(draft), _p(target), dt, _p(teacher), _p(conf_logits),
@@ -352,17 +394,19 @@ def dspark_select_width(confidence, cost, want_expected=True, out=None):
     expected float32 [B] (or None) as device tensors.  cost is the device
     float32 table {D, V(0), ..., V(gamma)}."""
     _dev_tensor(confidence, torch.float32, "confidence")
-    _dev_tensor(cost, torch.float32, "cost")
     if confidence.dim() != 2:
         raise DSparkError("select_width: confidence must be [B, gamma]")
     B, g = confidence.shape
-    if cost.shape != (g + 2,):
-        raise DSparkError("select_width: cost must hold gamma + 2 values")
     dev = confidence.device
+    _dev_tensor(cost, torch.float32, "cost", (g + 2,), dev)
     if out is None:
         out = dict(n_draft=torch.empty((B,), dtype=torch.int32, device=dev),
                    expected=torch.empty((B,), dtype=torch.float32, device=dev)
                    if want_expected else None)
+    else:
+        _check_out(out, [("n_draft", torch.int32, (B,))], dev, "select_width")
+        if out.get("expected") is not None:
+            _dev_tensor(out["expected"], torch.float32, "out['expected']", (B,), dev)
     rc = lib().dspark_select_width(_p(confidence), _p(cost), B, g, _p(out["n_draft"]),
                                    _p(out["expected"]), _stream(dev))
     _check(rc)

@@ -21,8 +21,9 @@ dspark_status check_common(int dtype, int32_t gamma, int32_t V) {
   return DSPARK_OK;
 }
 
+// top_k and top_p are either both given or both NULL (no request truncates).
 bool policy_ok(const dspark_policy& p) {
-  return p.mode && p.temperature && p.top_k && p.top_p && p.request_id && p.position;
+  return p.mode && p.temperature && p.request_id && p.position && (!p.top_k == !p.top_p);
 }
 
 size_t verify_bytes(int dtype, int32_t B, int32_t gamma, int32_t V) {

@@ -206,6 +206,12 @@ __device__ __forceinline__ uint32_t rows_or(uint32_t v) {
   return rows_combine(v, [](uint32_t p, uint32_t q) { return p | q; });
 }
 
+__device__ __forceinline__ float rows_max(float v) {
+  return __uint_as_float(rows_combine(__float_as_uint(v), [](uint32_t p, uint32_t q) {
+    return __float_as_uint(fmaxf(__uint_as_float(p), __uint_as_float(q)));
+  }));
+}
+
 // Top-2 scores with the argmax: (best, index, second best).
 struct Top2 {
   float v1;
@@ -238,6 +244,26 @@ __device__ __forceinline__ Top2 wave_top2(Top2 a) {
 #pragma unroll
   for (int l = 16; l < 64; l += 16) r = top2_merge(r, Top2{lane_f(a.v1, l), lane_i(a.i1, l), lane_f(a.v2, l)});
   return r;
+}
+
+// Top2 over each group of four consecutive lanes (DPP quad_perm).
+__device__ __forceinline__ Top2 quad_top2(Top2 a) {
+  a = dpp_step<kDppXor1>(a);
+  return dpp_step<kDppXor2>(a);
+}
+
+// Top2 over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ Top2 rows_top2(Top2 a) {
+  const auto v1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.v1), __float_as_uint(a.v1), false, false);
+  const auto i1 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(a.i1), static_cast<uint32_t>(a.i1), false, false);
+  const auto v2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.v2), __float_as_uint(a.v2), false, false);
+  a = top2_merge(Top2{__uint_as_float(v1[0]), static_cast<int32_t>(i1[0]), __uint_as_float(v2[0])},
+                 Top2{__uint_as_float(v1[1]), static_cast<int32_t>(i1[1]), __uint_as_float(v2[1])});
+  const auto w1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.v1), __float_as_uint(a.v1), false, false);
+  const auto j1 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(a.i1), static_cast<uint32_t>(a.i1), false, false);
+  const auto w2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.v2), __float_as_uint(a.v2), false, false);
+  return top2_merge(Top2{__uint_as_float(w1[0]), static_cast<int32_t>(j1[0]), __uint_as_float(w2[0])},
+                    Top2{__uint_as_float(w1[1]), static_cast<int32_t>(j1[1]), __uint_as_float(w2[1])});
 }
 
 // Cross-workgroup hand-off without whole-cache maintenance: values are written
@@ -273,12 +299,12 @@ __device__ __forceinline__ uint32_t publish(uint32_t* ticket) {
 // relative to the larger maximum.  exp here is exp(x) via exp2.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   if (m2 > m) {
-    s = s * exp2f((m - m2) * kLog2e) + s2;
+    s = s * __builtin_amdgcn_exp2f((m - m2) * kLog2e) + s2;
     m = m2;
   } else if (m2 == m) {
     s += s2;
   } else if (m2 > neg_inf()) {
-    s += s2 * exp2f((m2 - m) * kLog2e);
+    s += s2 * __builtin_amdgcn_exp2f((m2 - m) * kLog2e);
   }
 }
 
@@ -380,19 +406,26 @@ struct InChunk {
 __device__ __forceinline__ InChunk draw_in_chunk(const float (&lw)[4], int c, uint64_t seed, int32_t pos,
                                                  uint32_t req, uint32_t tag_sub, uint32_t tag_tok) {
   const int lane = threadIdx.x & 63;
+  // sub-chunk masses relative to the maximum m64 of the sub-chunk's 64-token
+  // group (lanes 16 w .. 16 w + 15), exactly as the one-launch Markov kernel
+  // forms them from the values it holds: per lane the sum of
+  // 2^(lw log2e - m64 log2e) over its four tokens, then over the four lanes
+  // of the sub-chunk as (l0 + l1) + (l2 + l3)
   float m = fmaxf(fmaxf(lw[0], lw[1]), fmaxf(lw[2], lw[3]));
-  m = quad_max(m);
+  m = fmaxf(m, dpp_f<kDppXor1>(m));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp_f<kDppMirror>(m));
   float s = 0.0f;
-  if (m > neg_inf()) {
+  const float mb = (m > neg_inf() && m < pos_inf()) ? m * kLog2e : 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (lw[e] > neg_inf()) s += __builtin_amdgcn_exp2f((lw[e] - m) * kLog2e);
-  }
+  for (int e = 0; e < 4; ++e) s += __builtin_amdgcn_exp2f(fmaf(lw[e], kLog2e, -mb));
   s = quad_sum(s);
   const uint32_t j = static_cast<uint32_t>(c) * (kChunk / kSub) + static_cast<uint32_t>(lane >> 2);
   const float g2 = gumbel(seed, j, pos, req, tag_sub);
   Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
-  if ((lane & 3) == 0 && m > neg_inf()) t2 = Top2{m + logf(s) + g2, static_cast<int32_t>(j), neg_inf()};
+  if ((lane & 3) == 0 && m > neg_inf() && m < pos_inf() && s > 0.0f)
+    t2 = Top2{m + logf(s) + g2, static_cast<int32_t>(j), neg_inf()};
   t2 = wave_top2(t2);
   InChunk r{-1, neg_inf(), false};
   if (t2.i1 == INT32_MAX) return r;

@@ -89,7 +89,8 @@ VerifyPlan plan_verify(int logits_dtype, int32_t B, int32_t gamma, int32_t V, bo
 
 struct MarkovPlan {
   int C;  // chunks per row
-  size_t off_part, off_sync, bytes;
+  int G;  // workgroups (512-token slices) of the one-launch plans
+  size_t off_part, off_xk, off_sync, bytes;
 };
 MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d);
 
@@ -155,6 +156,8 @@ hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
 
 // Launch plan of the Markov sampler (DSPARK_MARKOV_AUTO / _PER_STEP).
 int markov_plan_mode();
+// Destroys the one-launch chain's per-device events (markov.hip).
+void release_markov_chain();
 
 hipError_t launch_stats(const void* draft, const void* target, int dtype, const int32_t* teacher,
                         const float* conf_logits, const uint8_t* block_mask, int32_t N,

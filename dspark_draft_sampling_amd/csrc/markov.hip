@@ -59,12 +59,13 @@ constexpr int kFusedTokens = kFusedThreads / 64 * 16 * kFusedMS;
 constexpr int kMaxR = DSPARK_MAX_RANK;
 constexpr int kPad = 8;             // bf16 padding per staged W1 row (bank spread)
 constexpr int kFinThreads = 256;    // per-step finalize kernel
-constexpr uint32_t kSpinLimit = 1u << 22;  // polls (~1 us each) of one wait before giving up
-
-// The one-launch plan's synchronisation area: the timeout word, alone on its
-// 256-byte line.
-constexpr int kSyncTimeout = 0;
-constexpr int kSyncWords = 64;
+// Every wait of the one-launch plans for another workgroup's data gives up
+// after this many ticks of the 100 MHz real-time counter (20 ms; a whole call
+// takes well under 1 ms when its grid is resident).
+constexpr uint64_t kWaitTicks = 2000000;
+// Second-word patterns of the tagged two-word values (x_k, the timeout mark).
+constexpr uint32_t kTokenCheck = 0x5A5A5A5Au;
+constexpr uint32_t kTimeoutMark = 0x7113007Du;
 
 // Everything one Markov call reads and writes.
 struct MarkovArgs {
@@ -85,8 +86,16 @@ struct MarkovArgs {
   float* q_tok;
   float* confidence;
   uint8_t* flags;
-  ChunkPart* part;
-  uint32_t* sync;  // fused plan: timeout word (kSyncWords)
+  ChunkPart* part;  // per-step plan: chunk records [gamma][B][C]
+  // one-launch plans: everything that crosses workgroups is a 64-bit word
+  // (epoch << 32 | payload), so a reader accepts a word only from this call
+  // and never depends on more than 64-bit single-copy atomicity
+  uint32_t epoch;   // this call's tag (never 0)
+  int32_t G;        // workgroups of the one-launch plans (512-token slices)
+  uint64_t* tpart;  // truncating plan: chunk records [gamma][B][C][4]
+  uint64_t* frec;   // untruncated plan: workgroup records [gamma][B][7][G] (word-major)
+  uint64_t* xk;     // x_k hand-off [gamma][B][2]
+  uint64_t* sync;   // timeout mark [2]
 };
 
 // Four consecutive logits starting at a multiple of 4, kept packed (bf16:
@@ -134,40 +143,6 @@ __device__ __forceinline__ void store4_coherent(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
-// Device-scope 16-byte load (bypassing stale cached copies); the wait for its
-// data is part of the instruction sequence.
-__device__ __forceinline__ f32x4 load4_coherent(const void* p) {
-  f32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
-               : "=v"(v)
-               : "v"(p)
-               : "memory");
-  return v;
-}
-
-template <bool COH>
-__device__ __forceinline__ ChunkPart load_part(const ChunkPart* p) {
-  if constexpr (COH) {
-    const f32x4 v = load4_coherent(p);
-    return ChunkPart{v[0], v[1], v[2], __float_as_uint(v[3])};
-  } else {
-    return *p;
-  }
-}
-template <bool COH>
-__device__ __forceinline__ void store_part(ChunkPart* p, ChunkPart v) {
-  if constexpr (COH) {
-    store4_coherent(reinterpret_cast<float*>(p), f32x4{v.m, v.s, v.score, __uint_as_float(v.arg_nf)});
-  } else {
-    *p = v;
-  }
-}
-template <bool COH>
-__device__ __forceinline__ void store_flag(uint8_t* p, uint8_t v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-
 // The thread index, opaque to the optimiser: the phases of the one-launch plan
 // recompute their lane-derived addresses instead of keeping them live (in
 // registers) across the whole step loop.
@@ -175,6 +150,108 @@ __device__ __forceinline__ int opaque_tid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
   return t;
+}
+
+// ---------------------------------------------------------------------------
+// Tagged hand-off of the one-launch plans.  A 64-bit word carries the call's
+// epoch in its upper half; it is stored and loaded as one agent-scope atomic
+// (single-copy atomic at 64 bits, write-through to the device-coherent level),
+// so a reader that sees the epoch sees the payload stored with it, and a word
+// left by an earlier call (another epoch) is never taken for this call's.
+
+__device__ __forceinline__ void st_tagged(uint64_t* p, uint32_t epoch, uint32_t v) {
+  __hip_atomic_store(p, (static_cast<uint64_t>(epoch) << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(uint64_t w, uint32_t epoch) { return static_cast<uint32_t>(w >> 32) == epoch; }
+__device__ __forceinline__ uint32_t payload(uint64_t w) { return static_cast<uint32_t>(w); }
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// The call's timeout mark: set by any wait that gave up; read by the waits
+// (to give up at once) and by the confidence kernel (to flag every row).
+__device__ __forceinline__ void mark_timeout(const MarkovArgs& a) {
+  st_tagged(a.sync, a.epoch, kTimeoutMark);
+  st_tagged(a.sync + 1, a.epoch, ~kTimeoutMark);
+}
+__device__ __forceinline__ bool timed_out(const MarkovArgs& a) {
+  const uint64_t w0 = ld_tagged(a.sync), w1 = ld_tagged(a.sync + 1);
+  return tag_is(w0, a.epoch) && tag_is(w1, a.epoch) && payload(w0) == kTimeoutMark &&
+         payload(w1) == ~kTimeoutMark;
+}
+// True (after marking the timeout) once a wait begun at t0 should give up.
+__device__ __forceinline__ bool give_up(const MarkovArgs& a, uint64_t t0) {
+  if (now_ticks() - t0 > kWaitTicks || timed_out(a)) {
+    mark_timeout(a);
+    return true;
+  }
+  return false;
+}
+
+// x_k of request b (step k) as two tagged words: the token and the token
+// xor a fixed pattern.
+__device__ __forceinline__ void put_token(const MarkovArgs& a, int k, int b, int32_t x) {
+  uint64_t* p = a.xk + (static_cast<size_t>(k - 1) * a.B + b) * 2;
+  st_tagged(p, a.epoch, static_cast<uint32_t>(x));
+  st_tagged(p + 1, a.epoch, static_cast<uint32_t>(x) ^ kTokenCheck);
+}
+// Waits for x_k of request b; -1 if the wait gave up.
+__device__ __forceinline__ int32_t wait_token(const MarkovArgs& a, int k, int b) {
+  const uint64_t* p = a.xk + (static_cast<size_t>(k - 1) * a.B + b) * 2;
+  const uint64_t t0 = now_ticks();
+  for (uint32_t it = 1;; ++it) {
+    const uint64_t w0 = ld_tagged(p), w1 = ld_tagged(p + 1);
+    if (tag_is(w0, a.epoch) && tag_is(w1, a.epoch) && (payload(w0) ^ kTokenCheck) == payload(w1))
+      return static_cast<int32_t>(payload(w0));
+    if ((it & 31) == 0 && give_up(a, t0)) return -1;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Waits for the tagged chunk record idx of the truncating one-launch plan; a
+// placeholder (no mass, no maximum) if the wait gave up.
+__device__ __forceinline__ ChunkPart wait_part(const MarkovArgs& a, size_t idx) {
+  const uint64_t* t = a.tpart + idx * 4;
+  const uint64_t t0 = now_ticks();
+  for (uint32_t it = 1;; ++it) {
+    const uint64_t w0 = ld_tagged(t), w1 = ld_tagged(t + 1), w2 = ld_tagged(t + 2), w3 = ld_tagged(t + 3);
+    if (tag_is(w0, a.epoch) && tag_is(w1, a.epoch) && tag_is(w2, a.epoch) && tag_is(w3, a.epoch))
+      return ChunkPart{__uint_as_float(payload(w0)), __uint_as_float(payload(w1)), __uint_as_float(payload(w2)),
+                       payload(w3)};
+    if ((it & 31) == 0 && give_up(a, t0)) return ChunkPart{neg_inf(), 0.0f, neg_inf(), 0x7fffffffu};
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Partials of one request over a wave's 16 MS tokens, from the lane's 4 MS
+// values z[4 ms + i] (token vb + 16 ms + 4 (lane >> 4) + i; the lanes l,
+// l ^ 16, l ^ 32, l ^ 48 hold the request) and the wave's maximum m over
+// them: sj[ms] = the sum of 2^(z log2e - m log2e) over 16-token sub-chunk ms
+// (per lane over its four tokens in order, then (l0 + l1) + (l2 + l3) over
+// the lanes), and s = the sum of the sj in a fixed order.  Every lane of the
+// wave must call it; the results are equal on the four lanes of a request.
+// The level-2 mass of sub-chunk ms relative to m is sj[ms] (the three-level
+// draw inside a chunk forms the same sums from the same values).
+template <int MS>
+__device__ __forceinline__ void sub_partials(const float (&z)[4 * MS], float m, float (&sj)[MS], float& s) {
+  // branch-free: with no finite maximum every z is -inf (or the row is
+  // flagged), so a zero shift gives the empty sums 0
+  const float mb = (m > neg_inf() && m < pos_inf()) ? m * kLog2e : 0.0f;
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t += __builtin_amdgcn_exp2f(fmaf(z[4 * ms + i], kLog2e, -mb));
+    sj[ms] = rows_sum(t);
+  }
+  if constexpr (MS == 4) {
+    s = (sj[0] + sj[1]) + (sj[2] + sj[3]);
+  } else {
+    s = 0.0f;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) s += sj[ms];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -263,16 +340,8 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       if (k == 1) {
         xv = a.anchor[b];
       } else if constexpr (COH) {
-        // one-launch plan: x_{k-1} is -1 until its finalize stores it
-        const int32_t* xp = a.draft_tokens + static_cast<size_t>(b) * gamma + (k - 2);
-        uint32_t polls = 0;
-        while ((xv = load_coherent(xp)) < 0) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++polls > kSpinLimit) {
-            __hip_atomic_store(a.sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
+        // one-launch plan: x_{k-1} from its finalize's tagged hand-off
+        xv = wait_token(a, k - 1, b);
       } else {
         xv = a.draft_tokens[static_cast<size_t>(b) * gamma + (k - 2)];
       }
@@ -390,14 +459,11 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       m = am.v;
       arg = am.i;
     }
-    // sum of 2^(z log2e - m log2e) relative to the 4 lanes' maximum
-    float s = 0.0f;
-    if (m > neg_inf() && m < pos_inf()) {
-      const float mb = m * kLog2e;
-#pragma unroll
-      for (int e = 0; e < 4 * MS; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[e], kLog2e, -mb));
-    }
-    s = rows_sum(s);
+    // sum of 2^((z - m) log2e) over the wave's tokens, through the
+    // 16-token sub-chunk sums (the same arithmetic as the untruncated
+    // one-launch kernel)
+    float sj[MS], s;
+    sub_partials<MS>(z, m, sj, s);
     if (lane < 16) {
       L.red_m[wave][n] = m;
       L.red_s[wave][n] = s;
@@ -411,10 +477,11 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
   constexpr int kChunksPerWG = NW / WPC;
   constexpr int kRecPerThread = (kChunksPerWG * kTile + NT - 1) / NT;
   ChunkPart rec[kRecPerThread];
-  ChunkPart* dst[kRecPerThread];
+  size_t dst[kRecPerThread];  // record index, or kNoRec
+  constexpr size_t kNoRec = ~static_cast<size_t>(0);
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j) {
-    dst[j] = nullptr;
+    dst[j] = kNoRec;
     const int idx = tid + j * NT;
     const int h = idx / kTile, n = idx - h * kTile;
     const int c = tok0 / kChunk + h;
@@ -437,7 +504,7 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
       score = m + logf(s) + gumbel(a.seed, static_cast<uint32_t>(c), a.pol.position[b] + k,
                                    a.pol.request_id[b], DSPARK_TAG_DRAFT_CHUNK);
     rec[j] = ChunkPart{m, s, score, (static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u)};
-    dst[j] = a.part + (static_cast<size_t>(k - 1) * B + b) * a.C + c;
+    dst[j] = (static_cast<size_t>(k - 1) * B + b) * a.C + c;
   }
   if constexpr (COH) {
     // a record, once visible, vouches for every z of the step this
@@ -447,7 +514,18 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
   }
 #pragma unroll
   for (int j = 0; j < kRecPerThread; ++j)
-    if (dst[j]) store_part<COH>(dst[j], rec[j]);
+    if (dst[j] != kNoRec) {
+      const size_t idx = dst[j];
+      if constexpr (COH) {
+        uint64_t* t = a.tpart + idx * 4;
+        st_tagged(t, a.epoch, __float_as_uint(rec[j].m));
+        st_tagged(t + 1, a.epoch, __float_as_uint(rec[j].s));
+        st_tagged(t + 2, a.epoch, __float_as_uint(rec[j].score));
+        st_tagged(t + 3, a.epoch, rec[j].arg_nf);
+      } else {
+        a.part[idx] = rec[j];
+      }
+    }
   __syncthreads();  // the LDS tile is reused by the next call
 }
 
@@ -710,8 +788,8 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   ArgMax am{neg_inf(), INT32_MAX};
   Top2 best{neg_inf(), INT32_MAX, neg_inf()};
   uint32_t bad = 0;
-  const float tp = a.pol.top_p[b];
-  const int tk_raw = a.pol.top_k[b];
+  const float tp = top_p_of(a.pol.top_p, b);
+  const int tk_raw = top_k_of(a.pol.top_k, b);
   const bool want_cm = sampled && truncated(tk_raw, tp, V) && C <= kMaxChunksBound;
   // a sampled row without truncation draws inside its best-scoring chunk:
   // each wave fetches its own best chunk while the waves' results merge, and
@@ -721,20 +799,9 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
   Top2 wbest;
   float zpre[4];
   for (int c = tid; c < C; c += NT) {
-    ChunkPart p = load_part<COH>(pb + c);
-    if constexpr (COH) {
-      // the fused plan's records start as s = -1 (a stored s is >= 0 or NaN)
-      uint32_t polls = 0;
-      while (p.s < 0.0f) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++polls > kSpinLimit) {
-          __hip_atomic_store(a.sync + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          p = ChunkPart{neg_inf(), 0.0f, neg_inf(), 0x7fffffffu};
-          break;
-        }
-        p = load_part<COH>(pb + c);
-      }
-    }
+    ChunkPart p;
+    if constexpr (COH) p = wait_part(a, (static_cast<size_t>(k - 1) * a.B + b) * C + c);
+    else p = pb[c];
     if (want_cm) F.cm[c] = p.m;
     const int32_t arg = static_cast<int32_t>(p.arg_nf & 0x7fffffffu);
     bad |= p.arg_nf >> 31;
@@ -831,8 +898,8 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
     // the drawing wave writes the row's outputs, x_k first: the next step's
     // workgroups wait for it
     if (lane == 0) {
-      if constexpr (COH) store_coherent(a.draft_tokens + row, x);
-      else a.draft_tokens[row] = x;
+      if constexpr (COH) put_token(a, k, b, x);
+      a.draft_tokens[row] = x;
       if (!sampled) {
         a.q_lse[row] = 0.0f;
         a.q_thr[row] = 0.0f;
@@ -849,10 +916,480 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
         a.q_tok[row] = (zx > neg_inf() && S > 0.0f) ? expf(zx - M) / S : 0.0f;
       }
       if (a.pol.mode[b] != 0 && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
-      store_flag<COH>(a.flags + row, static_cast<uint8_t>(fl));
+      a.flags[row] = static_cast<uint8_t>(fl);
     }
   }
   __syncthreads();  // F is reused by the next request
+}
+
+// ---------------------------------------------------------------------------
+// Untruncated one-launch plan (no request of the call truncates).
+//
+// Workgroup g owns the 512 tokens [512 g, 512 g + 512) (chunks 2g, 2g + 1)
+// and keeps their W2 rows in registers, as in the truncating plan.  Nothing
+// is read back across workgroups except small tagged records:
+//  * in the stream phase each wave keeps, per request, the best two level-2
+//    scores of its four 16-token sub-chunks and stashes the best one's 16 z
+//    values in LDS;
+//  * the workgroup then takes, per request, level 1 over its two chunks, level
+//    2 over the chosen chunk's sub-chunks and level 3 over the chosen
+//    sub-chunk's tokens: the token the draw would pick if the chunk choice
+//    fell on this workgroup's best chunk;
+//  * wave 0 stores one record per request (the slice's maximum and sum, its
+//    argmax, its best and second chunk scores, the candidate and its z), and
+//    one wave of workgroup b mod G finalizes request b: the record with the
+//    best chunk score holds x_k.
+// The q stores of a step are plain stores that drain while the hand-off runs:
+// no record depends on them.  Wave 0 does all the waiting (x_{k-1}, records),
+// so its loads never queue behind the other waves' stores.
+
+constexpr int kZ0Ld = 68;  // floats per row of wave 0's z tile (64 + 4: bank spread)
+constexpr int kW1Slots = (kMaxR + kPad) / 8;  // 16-byte slots per staged W1 row (the last: padding)
+
+struct FastLds {
+  __attribute__((aligned(16))) uint16_t a[kTile * (kMaxR + kPad)];  // staged W1 rows (kW1Slots slots each)
+  // per (wave, request): partials of the wave's 64 tokens
+  float red_m[kFusedThreads / 64][kTile], red_s[kFusedThreads / 64][kTile];
+  uint32_t red_i[kFusedThreads / 64][kTile];  // lowest argmax (bits 0..30); bit 31: NaN / +inf seen
+  float sub_v1[kFusedThreads / 64][kTile], sub_v2[kFusedThreads / 64][kTile];  // best two level-2 scores
+  int32_t sub_i1[kFusedThreads / 64][kTile];  // global sub-chunk index of the best
+  __attribute__((aligned(16))) float stash[kFusedThreads / 64][kTile][kSub];   // its z values
+  int32_t xs[kTile];
+  uint32_t rec[kTile][8];  // the workgroup's record per request
+  // Gumbel noise of the step (it does not depend on x_{k-1}): level 2 per
+  // (wave, request, sub-chunk of the wave), level 1 per (request, chunk)
+  __attribute__((aligned(16))) float g2[kFusedThreads / 64][kTile][4];
+  float g1[kTile][2];
+  // the tile's policy: 1 / T for sampled requests (0 for greedy, -1 absent),
+  // request ids and the step's positions
+  float invT[kTile];
+  uint32_t req[kTile];
+  int32_t pos[kTile];
+  // wave 0's z tiles (stored to q by waves 4..7 one step later, so that no
+  // barrier waits for those stores): by step parity, rows of 64 tokens, padded
+  __attribute__((aligned(16))) float z0[2][kTile][kZ0Ld];
+  float z0_invT[2][kTile];  // the tile's policy of that step (> 0: sampled)
+};
+
+// Waves 4..7: wave 0's z tile of step k (tile b0, workgroup tokens from tok0)
+// to q, for the sampled requests; 16 lanes per 64-token row.
+template <bool VEC>
+__device__ __forceinline__ void store_z0(const MarkovArgs& a, const FastLds& L, int tok0, int b0, int k) {
+  const int t = static_cast<int>(threadIdx.x) - 4 * kTile;
+  const int par = k & 1;
+#pragma unroll
+  for (int i = 0; i < kTile * 16 / (4 * kTile); ++i) {
+    const int f = t + i * 4 * kTile;
+    const int n = f >> 4, col = (f & 15) * 4;
+    if (!(L.z0_invT[par][n] > 0.0f)) continue;  // absent or greedy request
+    const int v0 = tok0 + col;
+    const f32x4 zz = *reinterpret_cast<const f32x4*>(&L.z0[par][n][col]);
+    float* dst = a.q_z + (static_cast<size_t>(b0 + n) * a.gamma + (k - 1)) * a.V + v0;
+    if (VEC && v0 + 3 < a.V) {
+      *reinterpret_cast<f32x4*>(dst) = zz;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v0 + e < a.V) dst[e] = zz[e];
+    }
+  }
+}
+
+// Step k of the requests [b0, b0 + 64) over workgroup g's tokens.  EDGE: the
+// tile holds absent requests or the workgroup tokens past the vocabulary
+// (element-wise checks); otherwise every value is in range.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void fast_tile(const MarkovArgs& a, const bf16x8 (&af)[kFusedMS][kMaxR / 32], int g,
+                                          int b0, int k, FastLds& L) {
+  constexpr int MS = kFusedMS, NH = 4, NSP = 1, TPW = 16 * MS;
+  const T* __restrict__ backbone = static_cast<const T*>(a.backbone);
+  const int B = a.B, gamma = a.gamma, V = a.V, r = a.r;
+  const int tid = opaque_tid(), lane = tid & 63, wave = wave_id();
+  const int tok0 = g * kFusedTokens;
+  const int vb = tok0 + wave * TPW;
+  const int kpad = (r + 31) & ~31;
+  constexpr int ld = kMaxR + kPad;  // fixed row stride of the DMA-staged W1 rows
+  const int ksteps = kpad / 32;
+
+  typedef __attribute__((address_space(3))) void lds_void;
+  // the backbone values do not depend on x_{k-1}: waves 1..7 request them
+  // first (behind their previous q stores); wave 0, which does the waiting,
+  // requests its own after x_{k-1} arrived, so that no poll queues behind them
+  QuadRaw<T> bbv[NH][NSP][MS];
+  if (wave != 0) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      load_backbone<T, VEC, MS, NSP>(bbv[h], backbone, B, gamma, V, k, b0, h * NSP, vb, lane);
+  }
+
+  // the step's level-2 noise (thread (w, n): sub-chunks 4w .. 4w+3 of the
+  // workgroup for request n, one Philox block) and level-1 noise (wave 1:
+  // chunks 2g, 2g+1), while wave 0 waits for x_{k-1}
+  {
+    const int n = lane;
+    const int b = b0 + n;
+    uint32_t req = 0;
+    int32_t pos = 0;
+    if (b < B) {
+      req = a.pol.request_id[b];
+      pos = a.pol.position[b] + k;
+    }
+    if (wave == 2) {
+      float it = -1.0f;
+      if (b < B) {
+        const float Tb = a.pol.temperature[b];
+        it = (a.pol.mode[b] != 0 && !bad_temperature(Tb)) ? 1.0f / Tb : 0.0f;
+      }
+      L.invT[n] = it;
+      L.req[n] = req;
+      L.pos[n] = pos;
+    }
+    uint32_t c0 = (static_cast<uint32_t>(tok0) >> 6) + static_cast<uint32_t>(wave), c1 = static_cast<uint32_t>(pos),
+             c2 = req, c3 = DSPARK_TAG_DRAFT_SUB;
+    philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+    *reinterpret_cast<f32x4*>(&L.g2[wave][n][0]) = f32x4{gumbel_of(c0), gumbel_of(c1), gumbel_of(c2), gumbel_of(c3)};
+    if (wave == 1) {
+      uint32_t d0 = static_cast<uint32_t>(2 * g) >> 2, d1 = static_cast<uint32_t>(pos), d2 = req,
+               d3 = DSPARK_TAG_DRAFT_CHUNK;
+      philox4x32_10(d0, d1, d2, d3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+      const uint32_t cw[4] = {d0, d1, d2, d3};
+      L.g1[n][0] = gumbel_of(cw[(2 * g) & 3]);
+      L.g1[n][1] = gumbel_of(cw[(2 * g + 1) & 3]);
+    }
+  }
+  if (wave == 0) {
+    int32_t xv = -1;
+    const int b = b0 + lane;
+    if (b < B) {
+      xv = k == 1 ? a.anchor[b] : wait_token(a, k - 1, b);
+      xv = clamp_token(xv, V);
+    }
+    L.xs[lane] = xv;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      load_backbone<T, VEC, MS, NSP>(bbv[h], backbone, B, gamma, V, k, b0, h * NSP, vb, lane);
+    // the tile's W1 rows (MFMA B operand) by LDS DMA: instruction q fills the
+    // 16-byte slots 64 q .. 64 q + 63 (row n = slot / kW1Slots); padding
+    // slots, pieces past the rank and absent rows read past the buffer (0)
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
+#pragma unroll
+    for (int q = 0; q < kTile * kW1Slots / 64; ++q) {
+      const int sl = q * 64 + lane, n = sl / kW1Slots, c = sl - n * kW1Slots;
+      const int32_t x = L.xs[n];
+      const bool ok = c < kW1Slots - 1 && c * 8 < r && x >= 0;
+      const uint32_t off = ok ? static_cast<uint32_t>((x * r + c * 8) * 2) : 0xfffffff0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(L.a + q * 64 * 8), 16, off, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the DMA (and the backbone loads) landed
+  }
+  if (wave == 2) L.z0_invT[k & 1][lane] = L.invT[lane];
+  __syncthreads();
+  // waves 4..7: wave 0's z tile of the previous step (a one-tile batch; a
+  // batch of several tiles stores each tile's right after its draw)
+  if (tid >= 4 * kTile && B <= kTile && k > 1) store_z0<VEC>(a, L, tok0, b0, k - 1);
+
+  const uint32_t jbase = static_cast<uint32_t>(vb) >> 4;  // global index of the wave's first sub-chunk
+  const int q = lane >> 4;                                // this lane's sub-chunk for level 2
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    f32x4 acc[MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kMaxR / 32; ++ks) {
+      if (ks < ksteps) {
+        const bf16x8 bfr = load_frag(L.a + (h * 16 + (lane & 15)) * ld + ks * 32 + (lane >> 4) * 8);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+          acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms], 0, 0, 0);
+      }
+    }
+    // epilogue: lane holds tokens vb + ms*16 + 4*(lane>>4) + i of request n
+    const int n = h * 16 + (lane & 15);
+    const int b = b0 + n;
+    const float pit = L.invT[n];  // 1 / T (sampled), 0 (greedy), -1 (absent)
+    const bool bvalid = pit >= 0.0f;
+    const bool sampled = pit > 0.0f;
+    const float invT = sampled ? pit : 1.0f;
+    const size_t rowoff = (static_cast<size_t>(bvalid ? b : 0) * gamma + (k - 1)) * V;
+    float z[4 * MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+      const QuadRaw<T>& bb = bbv[h][0][ms];
+      const bool full = bvalid && v0 + 3 < V;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = (acc[ms][i] + bb.at(i)) * invT;
+        if constexpr (EDGE) z[ms * 4 + i] = (bvalid && v0 + i < V) ? y : neg_inf();
+        else z[ms * 4 + i] = y;
+      }
+      if (wave == 0) {
+        // wave 0 keeps its memory queue free for the hand-off: its z go to
+        // LDS and waves 4..7 store them
+        *reinterpret_cast<f32x4*>(&L.z0[k & 1][n][ms * 16 + 4 * (lane >> 4)]) =
+            f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+      } else if (VEC && !EDGE) {
+        if (sampled)
+          *reinterpret_cast<f32x4*>(a.q_z + rowoff + v0) = f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+      } else if (sampled) {
+        float* dst = a.q_z + rowoff + v0;
+        if (VEC && full) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v0 + i < V) dst[i] = z[ms * 4 + i];
+        }
+      }
+    }
+    // the wave's maximum over its 64 tokens
+    float lm = z[0];
+#pragma unroll
+    for (int e = 1; e < 4 * MS; ++e) lm = fmaxf(lm, z[e]);
+    const float m = rows_max(lm);
+    // lowest argmax, only when the pass holds a greedy request
+    int32_t arg = INT32_MAX;
+    if (__builtin_amdgcn_ballot_w64(bvalid && !sampled)) {
+#pragma unroll
+      for (int e = 4 * MS - 1; e >= 0; --e)
+        if (z[e] == m && m > neg_inf()) arg = vb + (e >> 2) * 16 + 4 * (lane >> 4) + (e & 3);
+      arg = static_cast<int32_t>(rows_combine(static_cast<uint32_t>(arg), [](uint32_t p, uint32_t q) {
+        return p < q ? p : q;
+      }));
+    }
+    // sub-chunk sums relative to m (the level-2 masses) and the wave's sum;
+    // a NaN, or +inf, in the row shows as a NaN sum or an infinite maximum
+    float sj[MS], s;
+    sub_partials<MS>(z, m, sj, s);
+    const bool bad = s != s || m == pos_inf();
+    // level 2 inside the wave: lane row q scores sub-chunk jbase + q
+    const float sq = q == 0 ? sj[0] : q == 1 ? sj[1] : q == 2 ? sj[2] : sj[3];
+    Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
+    if (sampled && m > neg_inf() && !bad && sq > 0.0f)
+      t2 = Top2{m + logf(sq) + L.g2[wave][n][q], static_cast<int32_t>(jbase + q), neg_inf()};
+    t2 = rows_top2(t2);
+    if (t2.i1 != INT32_MAX) {
+      const int m1 = t2.i1 - static_cast<int32_t>(jbase);
+      const f32x4 zz = m1 == 0   ? f32x4{z[0], z[1], z[2], z[3]}
+                       : m1 == 1 ? f32x4{z[4], z[5], z[6], z[7]}
+                       : m1 == 2 ? f32x4{z[8], z[9], z[10], z[11]}
+                                 : f32x4{z[12], z[13], z[14], z[15]};
+      *reinterpret_cast<f32x4*>(&L.stash[wave][n][4 * q]) = zz;
+    }
+    if (q == 0) {
+      L.red_m[wave][n] = m;
+      L.red_s[wave][n] = s;
+      L.red_i[wave][n] = (static_cast<uint32_t>(arg) & 0x7fffffffu) | (bad ? 0x80000000u : 0u);
+      L.sub_v1[wave][n] = t2.v1;
+      L.sub_i1[wave][n] = t2.i1;
+      L.sub_v2[wave][n] = t2.v2;
+    }
+  }
+  __syncthreads();  // every wave's partials, stash and wave 0's z tile are in LDS
+  if (tid >= 4 * kTile && B > kTile) store_z0<VEC>(a, L, tok0, b0, k);
+
+  // the workgroup's candidate per request: 4 threads per request (waves 0-3,
+  // one per SIMD)
+  if (tid < 4 * kTile) {
+    const int n = tid >> 2, p = tid & 3;
+    const int b = b0 + n;
+    const bool bvalid = b < B;
+    float wm[8], wsum[8];
+    uint32_t wi[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      wm[w] = L.red_m[w][n];
+      wsum[w] = L.red_s[w][n];
+      wi[w] = L.red_i[w][n];
+    }
+    ArgMax am{wm[0], static_cast<int32_t>(wi[0] & 0x7fffffffu)};
+    uint32_t bad = wi[0] >> 31;
+#pragma unroll
+    for (int w = 1; w < 8; ++w) {
+      am = better(am, ArgMax{wm[w], static_cast<int32_t>(wi[w] & 0x7fffffffu)});
+      bad |= wi[w] >> 31;
+    }
+    const bool sampled = L.invT[n] > 0.0f;
+    const uint32_t req = L.req[n];
+    const int32_t pos = L.pos[n];
+    // level 1 over the workgroup's chunks 2g, 2g + 1 (their partials merged
+    // wave by wave, as the chunk records of the truncating kernel); the
+    // workgroup's partials are the two chunks' merged
+    float sc[2], cmv[2], csv[2];
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc) {
+      const int c = 2 * g + hc;
+      float cm = wm[4 * hc], cs = wsum[4 * hc];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) lse_merge(cm, cs, wm[4 * hc + w], wsum[4 * hc + w]);
+      cmv[hc] = cm;
+      csv[hc] = cs;
+      sc[hc] = (sampled && c < a.C && cm > neg_inf() && cm < pos_inf() && cs > 0.0f)
+                   ? cm + logf(cs) + L.g1[n][hc]
+                   : neg_inf();
+    }
+    float m = cmv[0], s = csv[0];
+    lse_merge(m, s, cmv[1], csv[1]);
+    const int hb = sc[1] > sc[0] ? 1 : 0;
+    // level 2 over the chosen chunk's sub-chunks (its waves' best two)
+    Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      t2 = top2_merge(t2, Top2{L.sub_v1[4 * hb + w][n], L.sub_i1[4 * hb + w][n], L.sub_v2[4 * hb + w][n]});
+    // level 3 over the chosen sub-chunk's tokens: thread p takes 4p .. 4p+3
+    const bool draw = sampled && sc[hb] > neg_inf() && t2.i1 != INT32_MAX;
+    Top2 t3{neg_inf(), INT32_MAX, neg_inf()};
+    f32x4 zz = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+    if (draw) {
+      const int wj = (t2.i1 - (tok0 >> 4)) >> 2;  // wave holding the sub-chunk
+      zz = *reinterpret_cast<const f32x4*>(&L.stash[wj][n][4 * p]);
+      uint32_t d0 = static_cast<uint32_t>(t2.i1) * 4u + static_cast<uint32_t>(p), d1 = static_cast<uint32_t>(pos),
+               d2 = req, d3 = DSPARK_TAG_DRAFT_TOKEN;
+      philox4x32_10(d0, d1, d2, d3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+      const uint32_t tw[4] = {d0, d1, d2, d3};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (zz[e] > neg_inf())
+          t3 = top2_merge(t3, Top2{zz[e] + gumbel_of(tw[e]), t2.i1 * kSub + 4 * p + e, neg_inf()});
+    }
+    t3 = quad_top2(t3);
+    float zmine = neg_inf();
+    if (draw && t3.i1 != INT32_MAX && ((t3.i1 - t2.i1 * kSub) >> 2) == p) {
+      const int e = t3.i1 & 3;
+      zmine = e == 0 ? zz[0] : e == 1 ? zz[1] : e == 2 ? zz[2] : zz[3];
+    }
+    const float zc = quad_max(zmine);
+    const bool near23 = (t2.v2 > neg_inf() && near_gap(t2.v1, t2.v2)) ||
+                        (t3.i1 != INT32_MAX && t3.v2 > neg_inf() && near_gap(t3.v1, t3.v2));
+    if (p == 0) {
+      L.rec[n][0] = __float_as_uint(m);
+      L.rec[n][1] = __float_as_uint(s);
+      L.rec[n][2] = __float_as_uint(sc[hb]);
+      L.rec[n][3] = __float_as_uint(sc[1 - hb]);
+      L.rec[n][4] = (static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u);
+      L.rec[n][5] = (draw && t3.i1 != INT32_MAX)
+                        ? (0x80000000u | (near23 ? 0x40000000u : 0u) | static_cast<uint32_t>(t3.i1))
+                        : 0u;
+      L.rec[n][6] = __float_as_uint(zc);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int b = b0 + lane;
+    if (b < B) {
+      // word i of every workgroup's record sits side by side: the finalize
+      // reads each word of 64 records with one contiguous 512-byte load
+      uint64_t* R = a.frec + (static_cast<size_t>(k - 1) * B + b) * 7 * a.G + g;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) st_tagged(R + static_cast<size_t>(i) * a.G, a.epoch, L.rec[lane][i]);
+    }
+  }
+}
+
+// Finalize step k of request b from the G workgroup records, by one wave.
+constexpr int kFastMaxG = 256;
+__device__ __forceinline__ void fast_finalize(const MarkovArgs& a, int b, int k) {
+  constexpr int kPer = kFastMaxG / 64;  // records per lane
+  const int lane = threadIdx.x & 63;
+  const int G = a.G;
+  const uint64_t* R = a.frec + (static_cast<size_t>(k - 1) * a.B + b) * 7 * G;
+  // the request's policy, read before the wait
+  const float Tb = a.pol.temperature[b];
+  const bool req_sampled = a.pol.mode[b] != 0;
+  // every poll issues the loads of all of the lane's records at once (absent
+  // records read record 0 and are ignored); a record once whole stays whole
+  const uint64_t* rp[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) rp[t] = R + (lane + 64 * t < G ? lane + 64 * t : 0);
+  uint64_t w[kPer][7];
+  uint32_t have = 0;  // bit t: record lane + 64 t read whole (or absent)
+  const uint64_t t0 = now_ticks();
+  for (uint32_t it = 1;; ++it) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+#pragma unroll
+      for (int i = 0; i < 7; ++i) w[t][i] = ld_tagged(rp[t] + static_cast<size_t>(i) * G);
+    have = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      bool ok = lane + 64 * t >= G;
+      if (!ok) {
+        ok = true;
+#pragma unroll
+        for (int i = 0; i < 7; ++i) ok = ok && tag_is(w[t][i], a.epoch);
+      }
+      if (ok) have |= 1u << t;
+    }
+    if (have == (1u << kPer) - 1) break;
+    if ((it & 31) == 0 && give_up(a, t0)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float m = neg_inf(), s = 0.0f;
+  ArgMax am{neg_inf(), INT32_MAX};
+  Top2 best{neg_inf(), INT32_MAX, neg_inf()};
+  uint32_t bad = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    if (lane + 64 * t >= G || !(have & (1u << t))) continue;
+    const float rm = __uint_as_float(payload(w[t][0])), rs = __uint_as_float(payload(w[t][1]));
+    const float s1 = __uint_as_float(payload(w[t][2])), s2 = __uint_as_float(payload(w[t][3]));
+    const uint32_t ai = payload(w[t][4]), cand = payload(w[t][5]);
+    lse_merge(m, s, rm, rs);
+    am = better(am, ArgMax{rm, static_cast<int32_t>(ai & 0x7fffffffu)});
+    bad |= ai >> 31;
+    if ((cand >> 31) && s1 > neg_inf())
+      best = top2_merge(best, Top2{s1, static_cast<int32_t>(cand & 0x3fffffffu), s2});
+  }
+  const float M = wave_max(m);
+  const float S = wave_sum((m > neg_inf() && M < pos_inf()) ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f);
+  const ArgMax A = wave_argmax(am);
+  const Top2 Bst = wave_top2(best);
+  const uint32_t anybad = wave_or(bad);
+  // the winning record's candidate z and its level-2 / level-3 margin bit
+  float zw = neg_inf();
+  uint32_t nw = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    if (lane + 64 * t >= G || !(have & (1u << t))) continue;
+    const uint32_t cand = payload(w[t][5]);
+    if ((cand >> 31) && static_cast<int32_t>(cand & 0x3fffffffu) == Bst.i1) {
+      zw = __uint_as_float(payload(w[t][6]));
+      nw = (cand >> 30) & 1u;
+    }
+  }
+  zw = wave_max(zw);
+  nw = wave_or(nw);
+  if (lane == 0) {
+    const size_t row = static_cast<size_t>(b) * a.gamma + (k - 1);
+    const bool sampled = req_sampled && !bad_temperature(Tb);
+    uint32_t fl = anybad ? DSPARK_FLAG_NONFINITE : 0u;
+    int32_t x = 0;
+    if (!sampled) {
+      if (A.i == INT32_MAX) fl |= DSPARK_FLAG_EMPTY_ROW;
+      else x = A.i;
+    } else if (Bst.i1 == INT32_MAX) {
+      fl |= DSPARK_FLAG_EMPTY_ROW;
+    } else {
+      x = Bst.i1;
+      if ((Bst.v2 > neg_inf() && near_gap(Bst.v1, Bst.v2)) || nw) fl |= DSPARK_FLAG_NEAR_THRESHOLD;
+    }
+    // x_k first: the next step's workgroups wait for it
+    put_token(a, k, b, x);
+    a.draft_tokens[row] = x;
+    if (!sampled) {
+      a.q_lse[row] = 0.0f;
+      a.q_thr[row] = 0.0f;
+      a.q_tok[row] = 1.0f;
+    } else {
+      a.q_lse[row] = M + logf(S);
+      a.q_thr[row] = neg_inf();
+      a.q_tok[row] = (zw > neg_inf() && S > 0.0f) ? expf(zw - M) / S : 0.0f;
+    }
+    if (req_sampled && !sampled) fl |= DSPARK_FLAG_BAD_POLICY;
+    a.flags[row] = static_cast<uint8_t>(fl);
+  }
 }
 
 // Confidence head of every draft row (b, k): c = sigmoid(w . [h_k ;
@@ -911,7 +1448,11 @@ __global__ __launch_bounds__(kConfThreads) void markov_confidence_kernel(MarkovA
       dot += cw[i] * load_logit(h, i) + cw[d + i] * load_logit(e, i);
   }
   dot = block_sum<kConfThreads / 64>(dot, sh);
-  if (t == 0) a.confidence[row] = 1.0f / (1.0f + expf(-dot));
+  if (t == 0) {
+    a.confidence[row] = 1.0f / (1.0f + expf(-dot));
+    // a one-launch call whose waits gave up: every row is unspecified
+    if (a.epoch && timed_out(a)) a.flags[row] = static_cast<uint8_t>(a.flags[row] | DSPARK_FLAG_SYNC_TIMEOUT);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -933,30 +1474,16 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(MarkovArgs
   finalize_request<kFinThreads, VEC, false>(a, blockIdx.x, k, F);
 }
 
-// One-launch plan.  Every workgroup streams its vocabulary slice for every
-// request and step; workgroup g also finalizes requests g, g + G, ...  The
-// steps meet through the data itself, without a grid-wide barrier:
-//  * each step's chunk records have their own slice of the workspace, reset
-//    to s = -1 before the launch; a workgroup stores its records of step k
-//    only after all of its waves' stores of step k completed, so a record
-//    that is visible vouches for the z values behind it, and a finalizer
-//    polls its request's records until none is -1;
-//  * x_k reaches the next step's stream phase through draft_tokens (-1
-//    until its finalizer stores it).
-// A poll limit bounds every wait; on expiry the timeout word is set and the
-// launch runs on to its end (its rows are then flagged).
-
-// Clears the timeout word, marks every draft token as not yet drawn and every
-// chunk record (nrec of them) as not yet stored.
-__global__ void markov_sync_reset_kernel(uint32_t* sync, int32_t* draft_tokens, size_t n, ChunkPart* part,
-                                         size_t nrec) {
-  const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const size_t step = static_cast<size_t>(gridDim.x) * blockDim.x;
-  for (size_t i = i0; i < kSyncWords; i += step) sync[i] = 0u;
-  for (size_t i = i0; i < n; i += step) draft_tokens[i] = -1;
-  for (size_t i = i0; i < nrec; i += step) part[i] = ChunkPart{neg_inf(), -1.0f, neg_inf(), 0x7fffffffu};
-}
-
+// Truncating one-launch plan.  Every workgroup streams its vocabulary slice
+// for every request and step; workgroup g also finalizes requests g, g + G,
+// ...  The steps meet through tagged data, without a grid-wide barrier:
+//  * a workgroup stores its chunk records of step k only after all of its
+//    waves' z stores of step k completed, so a record that carries this
+//    call's epoch vouches for the z values behind it (a truncated row's
+//    finalize reads its whole z row);
+//  * x_k reaches the next step's stream phase through the tagged hand-off.
+// Every wait gives up after kWaitTicks; the call's rows are then flagged by
+// the confidence kernel.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs a) {
   __shared__ StreamLds<kFusedThreads> SL;
@@ -971,27 +1498,40 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs 
       stream_tile<T, VEC, kFusedThreads, kFusedMS, 4, true>(a, af, tok0, b0, k, SL);
     for (int b = g; b < a.B; b += G) finalize_request<kFusedThreads, VEC, true>(a, b, k, FL);
   }
-  // after a timed-out wait, mark the rows this workgroup finalized
-  if (threadIdx.x == 0 &&
-      __hip_atomic_load(a.sync + kSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-    for (int b = g; b < a.B; b += G)
-      for (int k = 0; k < a.gamma; ++k) {
-        uint8_t* f = a.flags + static_cast<size_t>(b) * a.gamma + k;
-        *f = static_cast<uint8_t>(*f | DSPARK_FLAG_SYNC_TIMEOUT);
-      }
-  }
 }
 
-// Resident workgroups per compute unit of a fused instantiation, the
-// device's compute units and whether it offers cooperative launch, cached per
-// device: a property of the device and the code object only.
+// Untruncated one-launch plan (see fast_tile / fast_finalize).
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kFusedThreads) void markov_fast_kernel(MarkovArgs a) {
+  __shared__ FastLds L;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  bf16x8 af[kFusedMS][kMaxR / 32];  // resident for the whole call
+  load_w2<kFusedMS>(af, a.w2, g * kFusedTokens + wave * 16 * kFusedMS, a.V, a.r, lane);
+  const bool edge_wg = (g + 1) * kFusedTokens > a.V;  // the slice runs past the vocabulary
+  for (int k = 1; k <= a.gamma; ++k) {
+    for (int b0 = 0; b0 < a.B; b0 += kTile) {
+      if (edge_wg || b0 + kTile > a.B) fast_tile<T, VEC, true>(a, af, g, b0, k, L);
+      else fast_tile<T, VEC, false>(a, af, g, b0, k, L);
+    }
+    if (wave == 0)
+      for (int b = g; b < a.B; b += G) fast_finalize(a, b, k);
+  }
+  // a one-tile batch's last wave-0 z tile (the barrier after the last draw
+  // ordered its LDS writes)
+  if (threadIdx.x >= 4 * kTile && a.B <= kTile) store_z0<VEC>(a, L, g * kFusedTokens, 0, a.gamma);
+}
+
+// Resident workgroups per compute unit of a one-launch kernel, the device's
+// compute units and whether it offers cooperative launch, cached per device
+// and kernel: a property of the device and the code object only.
 struct FusedFit {
   int blocks_per_cu;
   int cus;
   bool coop;
 };
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool FAST>
 FusedFit fused_fit() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];  // (coop << 30 | blocks << 16 | cus) + 1; 0 = unknown
@@ -1004,9 +1544,9 @@ FusedFit fused_fit() {
   int coop = 0, cus = 0, nb = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, markov_fused_kernel<T, VEC>, kFusedThreads,
-                                                   0) != hipSuccess)
-    nb = 0;
+  const void* fn = FAST ? reinterpret_cast<const void*>(markov_fast_kernel<T, VEC>)
+                        : reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kFusedThreads, 0) != hipSuccess) nb = 0;
   FusedFit f{nb, cus, coop != 0};
   if (f.blocks_per_cu < 0 || f.blocks_per_cu > 0x3fff || cus < 0 || cus > 0xffff) f = FusedFit{0, 0, false};
   if (dev < kMaxDev)
@@ -1024,12 +1564,14 @@ int stream_cus(hipStream_t st, int cus) {
   return n > 0 && n < cus ? n : cus;
 }
 
-// An ordinary launch of the fused grid relies on all of it being resident at
-// once, which an occupancy-sized grid is unless another such grid holds part
-// of the device: fused launches on one device are therefore chained, each
-// waiting for the previous one's completion event when that one went to
-// another stream (one stream orders its own launches), not inside a stream
-// capture (where the caller orders the work).
+// An ordinary launch of a one-launch grid relies on all of it being resident
+// at once, which an occupancy-sized grid is unless another such grid holds
+// part of the device: one-launch grids of this library on one device are
+// therefore chained, each waiting for the previous one's completion event when
+// that one went to another stream (one stream orders its own launches), not
+// inside a stream capture (where the caller orders the work).  The events are
+// the library's only HIP objects besides the profiler's; dspark_release
+// destroys them.
 struct FusedChain {
   std::mutex mu;
   hipEvent_t ev[64] = {};
@@ -1037,65 +1579,71 @@ struct FusedChain {
 };
 FusedChain g_chain;
 
-// fused: 0 per-step kernels, 1 one ordinary launch, 2 one cooperative launch
-template <typename T, bool VEC>
-hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
-  if (fused) {
-    const size_t ntok = static_cast<size_t>(a.B) * a.gamma;
-    const size_t nrec = ntok * static_cast<size_t>(a.C);
-    const size_t most = std::max({ntok, nrec, static_cast<size_t>(kSyncWords)});
-    DSPARK_LAUNCH("markov_sync_reset", markov_sync_reset_kernel,
-                  dim3(static_cast<unsigned>(std::min<size_t>(1024, (most + 255) / 256))), dim3(256), 0, st,
-                  a.sync, a.draft_tokens, ntok, a.part, nrec);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
-    MarkovArgs arg = a;
-    if (fused == 2) {
-      void* params[] = {&arg};
-      ProfScope ps("markov_fused");
-      if (ps.active()) (void)hipEventRecord(ps.start(), st);
-      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>),
-                                     dim3(G), dim3(kFusedThreads), params, 0, st);
-      if (ps.active()) (void)hipEventRecord(ps.stop(), st);
+// The epoch of a one-launch call: a process-wide counter, never 0.
+std::atomic<uint32_t> g_epoch{0};
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
+// One ordinary (or cooperative) launch of a one-launch kernel, chained.
+hipError_t launch_one(const void* fn, const char* name, const MarkovArgs& a, bool coop, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.G)), block(kFusedThreads);
+  MarkovArgs arg = a;
+  void* params[] = {&arg};
+  if (coop) {
+    ProfScope ps(name);
+    if (ps.active()) (void)hipEventRecord(ps.start(), st);
+    hipError_t e = hipLaunchCooperativeKernel(fn, grid, block, params, 0, st);
+    if (ps.active()) (void)hipEventRecord(ps.stop(), st);
+    return e;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+  const bool chain = cs == hipStreamCaptureStatusNone && dev >= 0 && dev < 64;
+  std::unique_lock<std::mutex> lk(g_chain.mu, std::defer_lock);
+  if (chain) {
+    lk.lock();
+    hipEvent_t& ev = g_chain.ev[dev];
+    if (!ev) {
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
       if (e != hipSuccess) return e;
-    } else {
-      int dev = 0;
-      e = hipGetDevice(&dev);
+    } else if (g_chain.last[dev] != st) {
+      e = hipStreamWaitEvent(st, ev, 0);
       if (e != hipSuccess) return e;
-      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-      if (hipStreamIsCapturing(st, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
-      const bool chain = cs == hipStreamCaptureStatusNone && dev >= 0 && dev < 64;
-      std::unique_lock<std::mutex> lk(g_chain.mu, std::defer_lock);
-      if (chain) {
-        lk.lock();
-        hipEvent_t& ev = g_chain.ev[dev];
-        if (!ev) {
-          e = hipEventCreate(&ev);
-          if (e != hipSuccess) return e;
-        } else if (g_chain.last[dev] != st) {
-          e = hipStreamWaitEvent(st, ev, 0);
-          if (e != hipSuccess) return e;
-        }
-      }
-      // the chain's event rides on the kernel's own dispatch (no marker
-      // packet between it and the next kernel of the stream)
-      ProfScope ps("markov_fused");
-      if (ps.active()) {
-        hipExtLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, ps.start(),
-                              ps.stop(), 0, arg);
-        if (chain) (void)hipEventRecord(g_chain.ev[dev], st);
-      } else if (chain) {
-        hipExtLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, nullptr,
-                              g_chain.ev[dev], 0, arg);
-      } else {
-        hipLaunchKernelGGL((markov_fused_kernel<T, VEC>), dim3(G), dim3(kFusedThreads), 0, st, arg);
-      }
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      if (chain) g_chain.last[dev] = st;
     }
+  }
+  // the chain's event rides on the kernel's own dispatch (no marker packet
+  // between it and the next kernel of the stream)
+  ProfScope ps(name);
+  if (ps.active()) {
+    e = hipExtLaunchKernel(fn, grid, block, params, 0, st, ps.start(), ps.stop(), 0);
+    if (e == hipSuccess && chain) e = hipEventRecord(g_chain.ev[dev], st);
+  } else if (chain) {
+    e = hipExtLaunchKernel(fn, grid, block, params, 0, st, nullptr, g_chain.ev[dev], 0);
   } else {
+    e = hipLaunchKernel(fn, grid, block, params, 0, st);
+  }
+  if (e != hipSuccess) return e;
+  if (chain) g_chain.last[dev] = st;
+  return hipSuccess;
+}
+
+// plan: 0 per-step kernels, 1 one ordinary launch, 2 one cooperative launch
+template <typename T, bool VEC>
+hipError_t launch_plan(MarkovArgs a, int plan, bool fast, hipStream_t st) {
+  if (plan) {
+    a.epoch = next_epoch();
+    const void* fn = fast ? reinterpret_cast<const void*>(markov_fast_kernel<T, VEC>)
+                          : reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>);
+    hipError_t e = launch_one(fn, fast ? "markov_fast" : "markov_fused", a, plan == 2, st);
+    if (e != hipSuccess) return e;
+  } else {
+    a.epoch = 0;
     const dim3 g_step(a.C, (a.B + kTile - 1) / kTile);
     for (int k = 1; k <= a.gamma; ++k) {
       DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, VEC>), g_step, dim3(kStepThreads), 0, st,
@@ -1115,30 +1663,56 @@ hipError_t launch_plan(const MarkovArgs& a, int fused, hipStream_t st) {
 
 template <typename T, bool VEC>
 hipError_t launch_typed(const MarkovArgs& a, int plan_mode, hipStream_t st) {
-  // fused when its grid (one workgroup per 512 tokens) is resident at once
-  const int G = (a.V + kFusedTokens - 1) / kFusedTokens;
-  int fused = 0;
-  if (plan_mode == DSPARK_MARKOV_AUTO) {
-    const FusedFit f = fused_fit<T, VEC>();
-    if (f.blocks_per_cu > 0 && G <= f.blocks_per_cu * stream_cus(st, f.cus)) fused = 1;
+  // the untruncated kernel when the call passes no truncation arrays; a
+  // one-launch plan when its grid (one workgroup per 512 tokens) is resident
+  // at once
+  const bool fast = !a.pol.top_k && !a.pol.top_p;
+  const FusedFit f = fast ? fused_fit<T, VEC, true>() : fused_fit<T, VEC, false>();
+  int plan = 0;
+  if (fast && a.G > kFastMaxG) {
+    // the untruncated finalize reads at most kFastMaxG records per request
+  } else if (plan_mode == DSPARK_MARKOV_AUTO) {
+    if (f.blocks_per_cu > 0 && a.G <= f.blocks_per_cu * stream_cus(st, f.cus)) plan = 1;
   } else if (plan_mode == DSPARK_MARKOV_COOPERATIVE) {
-    const FusedFit f = fused_fit<T, VEC>();
-    if (f.coop && f.blocks_per_cu > 0 && G <= f.blocks_per_cu * f.cus) fused = 2;
+    if (f.coop && f.blocks_per_cu > 0 && a.G <= f.blocks_per_cu * f.cus) plan = 2;
   }
-  return launch_plan<T, VEC>(a, fused, st);
+  return launch_plan<T, VEC>(a, plan, fast, st);
 }
 
 }  // namespace
+
+void release_markov_chain() {
+  std::lock_guard<std::mutex> lk(g_chain.mu);
+  for (int dev = 0; dev < 64; ++dev) {
+    if (!g_chain.ev[dev]) continue;
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(dev) == hipSuccess) {
+      (void)hipEventSynchronize(g_chain.ev[dev]);
+      (void)hipEventDestroy(g_chain.ev[dev]);
+      (void)hipSetDevice(cur);
+    }
+    g_chain.ev[dev] = nullptr;
+    g_chain.last[dev] = nullptr;
+  }
+}
 
 MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d) {
   (void)r;
   (void)d;
   MarkovPlan p{};
   p.C = (V + kChunk - 1) / kChunk;
-  p.off_part = 0;  // one slice of B x C records per step
-  size_t off = align_up(static_cast<size_t>(gamma) * B * p.C * sizeof(ChunkPart), 256);
+  p.G = (V + kFusedTokens - 1) / kFusedTokens;
+  // one record area, used by whichever plan runs: per-step chunk records
+  // (16 B), tagged chunk records (32 B) or tagged workgroup records (64 B)
+  const size_t rows = static_cast<size_t>(gamma) * B;
+  const size_t rec = std::max({rows * p.C * sizeof(ChunkPart), rows * p.C * 4 * sizeof(uint64_t),
+                               rows * p.G * 7 * sizeof(uint64_t)});
+  p.off_part = 0;
+  size_t off = align_up(rec, 256);
+  p.off_xk = off;
+  off += align_up(rows * 2 * sizeof(uint64_t), 256);
   p.off_sync = off;
-  off += align_up(kSyncWords * sizeof(uint32_t), 256);
+  off += 256;
   p.bytes = off;
   return p;
 }
@@ -1179,7 +1753,11 @@ hipError_t launch_markov(const void* backbone, int dtype, const int32_t* anchor,
   a.confidence = confidence;
   a.flags = flags;
   a.part = reinterpret_cast<ChunkPart*>(w + plan.off_part);
-  a.sync = reinterpret_cast<uint32_t*>(w + plan.off_sync);
+  a.tpart = reinterpret_cast<uint64_t*>(w + plan.off_part);
+  a.frec = reinterpret_cast<uint64_t*>(w + plan.off_part);
+  a.xk = reinterpret_cast<uint64_t*>(w + plan.off_xk);
+  a.sync = reinterpret_cast<uint64_t*>(w + plan.off_sync);
+  a.G = plan.G;
   const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(backbone) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(q_z) % 16 == 0);
   if (dtype == DSPARK_BF16)

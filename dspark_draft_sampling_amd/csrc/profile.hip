@@ -70,6 +70,21 @@ int dspark_profile_enable(int on) {
   return 0;
 }
 
+int dspark_release(void) {
+  std::vector<dspark::Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(dspark::g_mu);
+    recs.swap(dspark::g_recs);
+  }
+  for (const auto& r : recs) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  dspark::release_markov_chain();
+  return 0;
+}
+
 int dspark_profile_summary(char* buf, size_t n) {
   std::vector<dspark::Rec> recs;
   {

@@ -210,6 +210,11 @@ __device__ __forceinline__ SelResult select_threshold(const Row& row, int V, int
   return SelResult{key_value(key), s_kept};
 }
 
+// Truncation settings of request b; the two arrays are both NULL when no
+// request of the call truncates.
+__device__ __forceinline__ int top_k_of(const int32_t* top_k, int b) { return top_k ? top_k[b] : 0; }
+__device__ __forceinline__ float top_p_of(const float* top_p, int b) { return top_p ? top_p[b] : 1.0f; }
+
 __device__ __forceinline__ bool truncated(int top_k, float top_p, int V) {
   return (top_k > 0 && top_k < V) || top_p < 1.0f;
 }

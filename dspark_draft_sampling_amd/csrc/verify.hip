@@ -205,7 +205,7 @@ __device__ __forceinline__ void rows_reduce(typename RowLoad<T, VEC>::Raw* u, in
       sum = wave_sum(sum);
     }
     if (m == pos_inf() || !(sum < pos_inf())) fl |= DSPARK_FLAG_NONFINITE;
-    if (truncated(top_k[b], top_p[b], V)) {
+    if (truncated(top_k_of(top_k, b), top_p_of(top_p, b), V)) {
       const int C = (V + kChunk - 1) / kChunk;
       rows_chunk_max<T, VEC>(u, lo, V, C, lane, cmax + static_cast<size_t>(row) * C);
     }
@@ -321,8 +321,8 @@ __device__ __forceinline__ int slow_first_row(int w, int B, int G1, int V, const
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto cls = [&](int b) {
     if (mode[b] == 0 || bad_temperature(temperature[b])) return 2;
-    const int tk = top_k[b];
-    if (!truncated(tk, top_p[b], V)) return 2;
+    const int tk = top_k_of(top_k, b);
+    if (!truncated(tk, top_p_of(top_p, b), V)) return 2;
     return (tk > 0 && tk < V) ? 1 : 0;
   };
   const int per = (B + NT - 1) / NT, lo = min(B, tid * per), hi = min(B, lo + per);
@@ -385,8 +385,8 @@ __global__ __launch_bounds__(kSelThreads) void verify_select_kernel(
   const int b = row / G1, k = row - b * G1;
   const float Tb = temperature[b];
   const bool sampled = mode[b] != 0 && !bad_temperature(Tb);
-  const int tk_raw = top_k[b];
-  const float tp = top_p[b];
+  const int tk_raw = top_k_of(top_k, b);
+  const float tp = top_p_of(top_p, b);
   if (!sampled || !truncated(tk_raw, tp, V) || k > n_draft_of(n_draft, b, gamma)) return;
   const int tk = (tk_raw > 0 && tk_raw < V) ? tk_raw : 0;
   // row maximum, its base-2 shift and the total weight, from the row pass
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
   const int C = (V + kChunk - 1) / kChunk;
   const uint32_t req = request_id[b];
   const int32_t pos0 = position[b];
-  const bool trunc_row = sampled && truncated(top_k[b], top_p[b], V);
+  const bool trunc_row = sampled && truncated(top_k_of(top_k, b), top_p_of(top_p, b), V);
 
   // proposal-side values of the accept scan, fetched up front (thread k-1
   // owns proposal k)
@@ -785,11 +785,15 @@ hipError_t launch_typed(const T* target, const int32_t* draft, const float* q_z,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   RowTrunc* trunc = reinterpret_cast<RowTrunc*>(w + pl.off_trunc);
-  DSPARK_LAUNCH("verify_select", (verify_select_kernel<T>), dim3(B * (gamma + 1)),
-                dim3(kSelThreads), 0, st, target, V, gamma, pl.S, pl.vec, pol.mode,
-                pol.temperature, pol.top_k, pol.top_p, n_draft, part, cmax, trunc);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // truncation thresholds, unless the caller passed no truncation arrays (no
+  // request truncates)
+  if (pol.top_k || pol.top_p) {
+    DSPARK_LAUNCH("verify_select", (verify_select_kernel<T>), dim3(B * (gamma + 1)),
+                  dim3(kSelThreads), 0, st, target, V, gamma, pl.S, pl.vec, pol.mode,
+                  pol.temperature, pol.top_k, pol.top_p, n_draft, part, cmax, trunc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool vec4 = V % 4 == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(q_z) % 16 == 0;
   if (vec4)

@@ -208,6 +208,15 @@ int dspark_version(void);
 int dspark_profile_enable(int on);
 int dspark_profile_summary(char* buf, size_t n);
 
+/* Waits for and destroys every HIP object the library holds: the profiler's
+ * pending events and the per-device completion events that order the
+ * one-launch Markov grids (created on first use; see dspark_markov_plan).
+ * Call it before the HIP runtime is torn down (for example from an exit
+ * handler that runs before the process's static destructors); later calls
+ * create what they need again.  Not concurrent-safe with calls in flight on
+ * other threads.  Returns 0. */
+int dspark_release(void);
+
 /* Launch plan of dspark_markov_sample (process-wide, like the profiler
  * switch; read when a call is enqueued).
  *   DSPARK_MARKOV_AUTO (default): one launch for all gamma steps whenever its

@@ -124,6 +124,11 @@ def test_verify_validation(L):
     assert verify(L, target=None) == ds.DSPARK_EINVAL
     assert verify(L, out=None) == ds.DSPARK_EINVAL
     assert verify(L, pol=ds.dspark_policy(4096, None, 4096, 4096, 4096, 4096)) == ds.DSPARK_EINVAL
+    # top_k and top_p: both given or both NULL (no request truncates)
+    assert verify(L, pol=ds.dspark_policy(4096, 4096, None, 4096, 4096, 4096)) == ds.DSPARK_EINVAL
+    assert verify(L, pol=ds.dspark_policy(4096, 4096, 4096, None, 4096, 4096)) == ds.DSPARK_EINVAL
+    assert verify(L, pol=ds.dspark_policy(4096, 4096, None, None, 4096, 4096),
+                  ws=None) == ds.DSPARK_EWORKSPACE  # the policy itself passes
     assert verify(L, ws=None) == ds.DSPARK_EWORKSPACE
     assert verify(L, wsb=16) == ds.DSPARK_EWORKSPACE
     assert verify(L, B=0, target=None, out=None, ws=None) == ds.DSPARK_OK  # empty batch: no-op

@@ -294,16 +294,18 @@ def test_stats_identical_near_and_disjoint_rows(N, gamma, V, dtype):
 
 @pytest.mark.parametrize("config", ["decode", "truncated"])
 def test_markov_plans_agree(config, decode_full, truncated_full):
-    """The one-launch plans (W2 resident, steps handed off through polled
-    records; ordinary and cooperative launch) and the per-step plan agree at
-    full size: tokens, flags, z and thresholds bit for bit; the
+    """The launch plans agree at full size: the untruncated one-launch kernel
+    (no truncation arrays; ordinary and cooperative launch), the truncating
+    one-launch kernel (arrays passed, all off for the decode batch) and the
+    per-step kernels.  Tokens, flags, z and thresholds bit for bit; the
     log-normalisers up to the order of their fp32 partial sums (the plans
-    combine chunk partials over different workgroup shapes)."""
+    combine partials over different workgroup shapes)."""
 
     inp = decode_full if config == "decode" else truncated_full
     prev = ds.markov_plan(ds.MARKOV_AUTO)
     try:
         fused = G.markov(inp)
+        fused_arrays = G.markov(inp, arrays=True)
         ds.markov_plan(ds.MARKOV_COOPERATIVE)
         coop = G.markov(inp)
         ds.markov_plan(ds.MARKOV_PER_STEP)
@@ -313,21 +315,42 @@ def test_markov_plans_agree(config, decode_full, truncated_full):
     samp = inp["mode"] != 0
     for k in ("draft_tokens", "q_thr", "confidence", "flags", "q_lse", "q_tok"):
         assert np.array_equal(fused[k], coop[k]), k  # the same kernel
-    for k in ("draft_tokens", "q_thr", "confidence", "flags"):
-        assert np.array_equal(fused[k], step[k]), k
-    for k in ("q_lse", "q_tok"):
-        assert np.allclose(fused[k], step[k], rtol=1e-6, atol=0), k
-    assert np.array_equal(fused["q_logits"][samp], step["q_logits"][samp])
+    for other in (step, fused_arrays):
+        for k in ("draft_tokens", "q_thr", "confidence", "flags"):
+            assert np.array_equal(fused[k], other[k]), k
+        for k in ("q_lse", "q_tok"):
+            assert np.allclose(fused[k], other[k], rtol=1e-6, atol=0), k
+        assert np.array_equal(fused["q_logits"][samp], other["q_logits"][samp])
     assert np.array_equal(fused["q_logits"][samp], coop["q_logits"][samp])
-    assert not np.any(fused["flags"] & (1 << 5))  # no wait gave up
+    for o in (fused, fused_arrays, coop, step):
+        assert not np.any(o["flags"] & (1 << 5))  # no wait gave up
+
+
+def test_markov_stale_workspace(decode_full):
+    """A one-launch call accepts only words tagged with its own epoch: a
+    workspace left by earlier calls of the other one-launch kernel and of the
+    per-step kernels (same buffer, other layouts) changes nothing."""
+    inp = decode_full
+    prev = ds.markov_plan(ds.MARKOV_AUTO)
+    try:
+        ref = G.markov(inp)
+        G.markov(inp, arrays=True)  # truncating kernel: chunk records in the same area
+        ds.markov_plan(ds.MARKOV_PER_STEP)
+        G.markov(inp)  # untagged chunk records in the same area
+        ds.markov_plan(ds.MARKOV_AUTO)
+        again = G.markov(inp)
+    finally:
+        ds.markov_plan(prev)
+    for k in ref:
+        assert np.array_equal(ref[k], again[k]), k
 
 
 def test_markov_concurrent_streams(decode_full):
     """Two one-launch Markov calls enqueued at once on two streams: the
-    library chains its fused launches on the device, so neither grid waits
+    library chains its one-launch grids on the device, so neither grid waits
     on compute units the other holds, and the binding gives each stream its
-    own workspace, so neither call's reset touches the other's chunk records;
-    both end with a lone call's results and no wait gives up."""
+    own workspace; both end with a lone call's results and no wait gives
+    up."""
 
     inp = decode_full
     ref = G.markov(inp)
