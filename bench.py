@@ -107,10 +107,8 @@ def kernel_bytes(name, B, g, V, r, d, S, R):
         return 0
     if name in ("stats_pairs", "stats_reduce"):
         return 16 * B * g
-    if name == "stats_markov_look1":  # backbone rows, W2 once per token slice
-        return 2 * B * g * V + 2 * r * V
-    if name == "stats_markov_tnorm":  # target rows
-        return 2 * B * g * V
+    if name == "stats_markov_look1":  # backbone and target rows, W2 once per token slice
+        return 2 * 2 * B * g * V + 2 * r * V
     if name == "stats_markov_look2":  # second look: not compulsory
         return 0
     if name == "stats_grad_rows":  # row pair read once, gradient row written once (bf16)

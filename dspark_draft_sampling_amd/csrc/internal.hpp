@@ -113,7 +113,7 @@ hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const 
 // Statistics of the teacher-forced Markov draft (stats_markov.hip).
 struct StatsMarkovPlan {
   int G;  // token slices (workgroups of the look kernels)
-  size_t off_rec, off_norm, off_l1, off_dt, off_k2, off_xf, off_tp, bytes;
+  size_t off_rec, off_norm, off_l1, off_dt, off_k1, off_k2, off_xf, bytes;
 };
 StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V);
 hipError_t launch_stats_markov(const void* backbone, const void* target, int dtype, const int32_t* anchor,
@@ -127,7 +127,7 @@ hipError_t launch_stats_markov(const void* backbone, const void* target, int dty
 struct StatsGradPlan {
   int sliced;  // 1: (row pair, segment) item kernels; 0: one workgroup per row pair
   int P;       // segments per row pair
-  size_t off_part, off_l1, off_s, off_rows, off_cnt, bytes;
+  size_t off_part, off_l1, off_rows, off_cnt, bytes;
 };
 StatsGradPlan plan_stats_backward(int32_t N, int32_t gamma, int32_t V);
 hipError_t launch_stats_backward(const void* draft, const void* target, int dtype, const int32_t* teacher,

@@ -1194,8 +1194,6 @@ __device__ __forceinline__ void fast_tile(const MarkovArgs& a, const bf16x8 (&af
   // one per SIMD)
   if (tid < 4 * kTile) {
     const int n = tid >> 2, p = tid & 3;
-    const int b = b0 + n;
-    const bool bvalid = b < B;
     float wm[8], wsum[8];
     uint32_t wi[8];
 #pragma unroll

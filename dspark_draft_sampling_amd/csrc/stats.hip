@@ -8,19 +8,31 @@
 // prod_{j<=k} a_j; the position-weighted loss numerator (weights exp(-k/gamma))
 // and [sum, count] report pairs are returned unnormalised.
 //
-// stats_rows: one workgroup per row pair.  Pass 1 streams both rows once with
-// 16-byte loads and keeps an online (max, sum exp) per thread; pass 2 streams
-// them again (the pair was just read, so it is served from the caches) for
-// the L1 term.  The L1 pass forms the overlap sum_v min(P_v, T_v) instead of
-// sum |P_v - T_v|: both rows sum to 1, so L1 = 2 (1 - overlap) exactly, and
-// min(P_v, T_v) = exp(min(d_v - lse_d, t_v - lse_t)) takes one exponential
-// per element pair where |P_v - T_v| takes two.  stats_reduce: one workgroup computes tau and the sums in fp64
-// in a fixed order, so the sums are deterministic.
+// Every row pair is cut into segments of kSegIters x 64 16-byte groups per
+// row (2048 bf16 or 1024 fp32 tokens), one wave each.  Look 1 forms each
+// segment's normaliser part (l1norm.hpp: the maxima, and the sums under one
+// power-of-two shift shared by both rows where the maxima allow it); a pair's
+// parts merge exactly into its constants.  Look 2 reads the pair again and
+// sums, for pairs whose L1 is at least kFarL1 by look 1's bound, the overlap
+// sum min(P_v, T_v) (one exponential per element pair), and for the others
+// |P_v - T_v| in the form that keeps relative accuracy when the rows nearly
+// agree.
+//   row path (>= 2048 pairs, or rows not 16-byte aligned): one persistent
+//     workgroup of 16 waves per compute unit takes a pair at a time, its
+//     waves striding over the pair's segments; the parts merge through LDS.
+//   sliced path (small batches): items (pair, segment) spread over the GPU;
+//     stats_part1 writes each item's part; stats_part2 merges the pair's
+//     parts in registers (one wave per item), sums the item's share of L1
+//     and takes a ticket on the pair: the pair's last item writes the
+//     outputs, and the wave finishing the last pair writes tau and the sums.
+// stats_reduce (row path): one workgroup computes tau and the sums in fp64 in
+// a fixed order, so the sums are deterministic.
 #include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "l1norm.hpp"
 
 namespace dspark {
 namespace {
@@ -30,163 +42,12 @@ constexpr int kWaves = kThreads / 64;
 // Row path: one workgroup of kRowThreads per compute unit, each looping over
 // row pairs, so that the pairs being read at once (one per CU, 0.5 MB each at
 // V = 129280 in bf16) stay within the 256 MB Infinity Cache and the later
-// looks at a pair are served from it rather than from HBM.
-constexpr int kRowThreads = 1024;
+// looks at a pair can be served from it rather than from HBM.
+constexpr int kRowThreads = 512;
 constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kUnroll = 4;
 constexpr int kItemMaxWGs = 2048;      // grid of the sliced item kernels
 constexpr int kSlicedMaxPairs = 2048;  // row pairs below which the sliced path is used
-
-template <typename T, bool VEC>
-struct Vec8;
-
-template <>
-struct Vec8<uint16_t, true> {
-  static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* o) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    o[0] = bf_lo(u.x);
-    o[1] = bf_hi(u.x);
-    o[2] = bf_lo(u.y);
-    o[3] = bf_hi(u.y);
-    o[4] = bf_lo(u.z);
-    o[5] = bf_hi(u.z);
-    o[6] = bf_lo(u.w);
-    o[7] = bf_hi(u.w);
-  }
-};
-template <>
-struct Vec8<float, true> {
-  static constexpr int N = 4;
-  __device__ static void load(const float* p, float* o) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    o[0] = u.x;
-    o[1] = u.y;
-    o[2] = u.z;
-    o[3] = u.w;
-  }
-};
-template <typename T>
-struct Vec8<T, false> {
-  static constexpr int N = 1;
-  __device__ static void load(const T* p, float* o) { o[0] = load_logit(p, 0); }
-};
-
-__device__ __forceinline__ void online(float& m, float& s, const float* x, int n) {
-  float mx = x[0];
-  for (int j = 1; j < n; ++j) mx = fmaxf(mx, x[j]);
-  if (mx > m) {
-    s = (m > neg_inf()) ? s * __builtin_amdgcn_exp2f((m - mx) * kLog2e) : 0.0f;
-    m = mx;
-  }
-  if (m > neg_inf())
-    for (int j = 0; j < n; ++j) s += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
-}
-
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
-    const T* __restrict__ draft, const T* __restrict__ target, const int32_t* __restrict__ teacher,
-    const float* __restrict__ conf_logits, int32_t V, int32_t npairs, float* __restrict__ l1,
-    float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
-  using L = Vec8<T, VEC>;
-  constexpr int EPL = L::N;
-  constexpr int kThreads = kRowThreads, kWaves = kRowWaves;
-  __shared__ float shv[kWaves];
-  for (int rr = blockIdx.x; rr < npairs; rr += gridDim.x) {
-  const size_t row = static_cast<size_t>(rr);
-  const T* dr = draft + row * V;
-  const T* tr = target + row * V;
-  const int step = kThreads * EPL;
-
-  // pass 1: online normalisers of both rows
-  float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
-  int e = threadIdx.x * EPL;
-  for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
-    float xd[kUnroll][EPL], xt[kUnroll][EPL];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      L::load(dr + e + u * step, xd[u]);
-      L::load(tr + e + u * step, xt[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      online(md, sd, xd[u], EPL);
-      online(mt, st, xt[u], EPL);
-    }
-  }
-  for (; e < V; e += step) {
-    float xd[EPL], xt[EPL];
-    L::load(dr + e, xd);
-    L::load(tr + e, xt);
-    online(md, sd, xd, EPL);
-    online(mt, st, xt, EPL);
-  }
-  const float Md = block_max<kWaves>(md, shv);
-  const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
-  const float Mt = block_max<kWaves>(mt, shv);
-  const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
-  // log2(Sd / St): min(P_v, T_v) = 2^min((d_v - Md) log2e, (t_v - Mt) log2e + lam) / Sd
-  const float lam = __log2f(Sd) - __log2f(St);
-
-  // pass 2: the overlap sum_v min(P_v, T_v); L1 = sum |P - T| = 2 (1 - overlap)
-  // (both rows sum to 1), one exponential per element pair
-  float acc = 0.0f;
-  e = threadIdx.x * EPL;
-  for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
-    float xd[kUnroll][EPL], xt[kUnroll][EPL];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      L::load(dr + e + u * step, xd[u]);
-      L::load(tr + e + u * step, xt[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        acc += __builtin_amdgcn_exp2f(fminf((xd[u][j] - Md) * kLog2e, fmaf(xt[u][j] - Mt, kLog2e, lam)));
-  }
-  for (; e < V; e += step) {
-    float xd[EPL], xt[EPL];
-    L::load(dr + e, xd);
-    L::load(tr + e, xt);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      acc += __builtin_amdgcn_exp2f(fminf((xd[j] - Md) * kLog2e, fmaf(xt[j] - Mt, kLog2e, lam)));
-  }
-  const float ov = block_sum<kWaves>(acc, shv) / Sd;
-
-  if (threadIdx.x == 0) {
-    const float L1 = fmaxf(0.0f, 2.0f * (1.0f - ov));
-    const float a = fminf(1.0f, fmaxf(0.0f, ov));
-    const int32_t tch = clamp_token(teacher[row], V);
-    const float lse_d = Md + logf(Sd);
-    const float c = conf_logits[row];
-    l1[row] = L1;
-    accept_rate[row] = a;
-    ce[row] = lse_d - load_logit(dr, tch);
-    bce[row] = fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
-  }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Sliced path for small batches: (row pair, 2048-token segment) items, one
-// wave each, so that a few hundred row pairs still fill the GPU.
-//   stats_part1  per item: (max, sum) of both rows, sums with an integer
-//                base-2 shift (s = sum 2^(x log2e - floor(m log2e)))
-//   stats_part2  per item: the pair's normalisers from all its part1
-//                records, then the item's share of the overlap sum_v
-//                min(P_v, T_v) (a second read of the pair; L1 = 2 (1 -
-//                overlap)), with a ticket per pair: the pair's last
-//                item writes L1, accept_rate, CE and BCE, and the wave
-//                finishing the last pair writes tau and the sums
-// Both item kernels keep the next item's loads in flight while reducing the
-// current one (two register buffers, unconditional clamped loads).
-constexpr int kSegIters = 4;  // 16-byte loads per lane per row per segment
-
-struct StatPart {
-  float md, sd, mt, st;
-};
+constexpr int kSegIters = 4;           // 16-byte groups per lane per row per segment
 
 template <typename T>
 constexpr int stat_seg() {
@@ -201,113 +62,270 @@ __device__ __forceinline__ float elem16(const uint4& u, int j, float) {
   return __uint_as_float(j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w);
 }
 
-template <typename T>
-__device__ __forceinline__ void seg_load(const T* __restrict__ draft, const T* __restrict__ target,
-                                         int32_t V, int32_t P, int item, int lane, uint4* ud,
-                                         uint4* ut) {
+// Segment [lo, lo + stat_seg) of a row pair into registers, lane l holding
+// the 16-byte groups it * 64 + l.  VEC (16-byte aligned rows, V a multiple of
+// the group): one load per group, clamped into the row (seg_mask marks the
+// groups past the row -inf before use); otherwise element loads, -inf past
+// the row.
+template <typename T, bool VEC>
+__device__ __forceinline__ void seg_load(const T* __restrict__ dr, const T* __restrict__ tr, int32_t V, int lo,
+                                         int lane, uint4* ud, uint4* ut) {
   constexpr int EPL = 16 / sizeof(T);
-  constexpr int SEG = stat_seg<T>();
-  const int pair = item / P, seg = item - pair * P;
-  const size_t off = static_cast<size_t>(pair) * V;
-  const int lo = seg * SEG;
 #pragma unroll
   for (int it = 0; it < kSegIters; ++it) {
-    const int e = min(lo + (it * 64 + lane) * EPL, V - EPL);
-    ud[it] = *reinterpret_cast<const uint4*>(draft + off + e);
-    ut[it] = *reinterpret_cast<const uint4*>(target + off + e);
+    const int e0 = lo + (it * 64 + lane) * EPL;
+    if constexpr (VEC) {
+      const int e = min(e0, V - EPL);
+      ud[it] = *reinterpret_cast<const uint4*>(dr + e);
+      ut[it] = *reinterpret_cast<const uint4*>(tr + e);
+    } else if constexpr (sizeof(T) == 2) {
+      uint32_t wd[4], wt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + 2 * q;
+        const uint32_t d0 = e < V ? dr[e] : 0xFF80u, d1 = e + 1 < V ? dr[e + 1] : 0xFF80u;
+        const uint32_t t0 = e < V ? tr[e] : 0xFF80u, t1 = e + 1 < V ? tr[e + 1] : 0xFF80u;
+        wd[q] = d0 | (d1 << 16);
+        wt[q] = t0 | (t1 << 16);
+      }
+      ud[it] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      ut[it] = make_uint4(wt[0], wt[1], wt[2], wt[3]);
+    } else {
+      uint32_t wd[4], wt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + q;
+        wd[q] = e < V ? __float_as_uint(dr[e]) : 0xFF800000u;
+        wt[q] = e < V ? __float_as_uint(tr[e]) : 0xFF800000u;
+      }
+      ud[it] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      ut[it] = make_uint4(wt[0], wt[1], wt[2], wt[3]);
+    }
   }
 }
 
-// mask the clamped loads of a partial segment with -inf
-template <typename T>
+// VEC: mark the clamped groups of a partial segment -inf (the element loads
+// of the other path already did).
+template <typename T, bool VEC>
 __device__ __forceinline__ void seg_mask(int32_t V, int lo, int lane, uint4* ud, uint4* ut) {
   constexpr int EPL = 16 / sizeof(T);
   constexpr uint32_t kNeg = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
-  if (V - lo < stat_seg<T>()) {
+  if constexpr (VEC) {
+    if (V - lo < stat_seg<T>()) {
 #pragma unroll
-    for (int it = 0; it < kSegIters; ++it)
-      if (lo + (it * 64 + lane) * EPL >= V) ud[it] = ut[it] = make_uint4(kNeg, kNeg, kNeg, kNeg);
+      for (int it = 0; it < kSegIters; ++it)
+        if (lo + (it * 64 + lane) * EPL >= V) ud[it] = ut[it] = make_uint4(kNeg, kNeg, kNeg, kNeg);
+    }
   }
 }
 
+// The pair's reference offset (l1norm.hpp) in two steps, so that the loads
+// can travel with a segment's: pair_r5 loads t_v - d_v of token `lane` (lanes
+// 0..4), pair_k5 combines them (wave-uniform).
 template <typename T>
-__device__ __forceinline__ void seg_stats(const uint4* u, float& m, float& s) {
+__device__ __forceinline__ float pair_r5(const T* __restrict__ dr, const T* __restrict__ tr, int32_t V, int lane) {
+  return (lane < 5 && lane < V) ? load_logit(tr, lane) - load_logit(dr, lane) : pos_inf();
+}
+__device__ __forceinline__ float pair_k5(float r) {
+  return ref_offset(lane_f(r, 0), lane_f(r, 1), lane_f(r, 2), lane_f(r, 3), lane_f(r, 4));
+}
+
+// Look 1 of a segment: its normaliser part (wave-uniform), the target values
+// moved by the pair's reference offset K.
+template <typename T>
+__device__ __forceinline__ NormPart seg_part(const uint4* ud, const uint4* ut, float K) {
   constexpr int EPL = 16 / sizeof(T);
-  m = neg_inf();
+  float md = neg_inf(), mt = neg_inf();
 #pragma unroll
   for (int it = 0; it < kSegIters; ++it)
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) m = fmaxf(m, elem16(u[it], j, T{}));
-  m = wave_max(m);
-  s = 0.0f;
-  if (m > neg_inf()) {
-    const float M2 = floorf(m * kLog2e);
+    for (int j = 0; j < EPL; ++j) {
+      md = fmaxf(md, elem16(ud[it], j, T{}));
+      mt = fmaxf(mt, elem16(ut[it], j, T{}) - K);
+    }
+  md = wave_max(md);
+  mt = wave_max(mt);
+  float a2d, a2t;
+  np_shifts(md, mt, a2d, a2t);
+  float sd = 0.0f, x = 0.0f, ad = 0.0f;
+  if (np_common(md, mt)) {
 #pragma unroll
     for (int it = 0; it < kSegIters; ++it)
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) s += __builtin_amdgcn_exp2f(fmaf(elem16(u[it], j, T{}), kLog2e, -M2));
-    s = wave_sum(s);
+      for (int j = 0; j < EPL; ++j)
+        np_elem<true>(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}) - K, a2d, a2t, sd, x, ad);
+    ad = wave_sum(ad);
+  } else {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        np_elem<false>(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}) - K, a2d, a2t, sd, x, ad);
+  }
+  return NormPart{md, mt, wave_sum(sd), wave_sum(x), ad};
+}
+
+// Look 2 of a segment: the lane's share of min(P_v, T_v) Sd (far pairs) or
+// of |P_v - T_v| St (near pairs); k.far is uniform.
+template <typename T>
+__device__ __forceinline__ void seg_l1(const uint4* ud, const uint4* ut, const PairK& k, float& acc) {
+  constexpr int EPL = 16 / sizeof(T);
+  if (k.far) {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        acc += l1_far(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}) - k.K, k.a2d, k.a2t, k.lam2);
+  } else {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        acc += l1_near(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}) - k.K, k.a2d, k.kappa);
   }
 }
+
+// The segments first, first + stride, ... of a pair, each handed to
+// f(ud, ut, its first token) after seg_mask, the next one's loads in flight meanwhile.
+template <typename T, bool VEC, class F>
+__device__ __forceinline__ void seg_scan(const T* __restrict__ dr, const T* __restrict__ tr, int32_t V, int P,
+                                         int first, int stride, int lane, F&& f) {
+  constexpr int SEG = stat_seg<T>();
+  if (first >= P) return;
+  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  seg_load<T, VEC>(dr, tr, V, first * SEG, lane, ad, at);
+  for (int s = first;;) {
+    const int n1 = s + stride;
+    if (n1 < P) seg_load<T, VEC>(dr, tr, V, n1 * SEG, lane, bd, bt);
+    seg_mask<T, VEC>(V, s * SEG, lane, ad, at);
+    f(ad, at, s * SEG);
+    if (n1 >= P) break;
+    const int n2 = n1 + stride;
+    if (n2 < P) seg_load<T, VEC>(dr, tr, V, n2 * SEG, lane, ad, at);
+    seg_mask<T, VEC>(V, n1 * SEG, lane, bd, bt);
+    f(bd, bt, n1 * SEG);
+    if (n2 >= P) break;
+    s = n2;
+  }
+}
+
+// A pair's parts rec[0, P) merged by one wave (on every lane).
+__device__ __forceinline__ NormPart pair_merge(const NormPart* __restrict__ rec, int P, int lane) {
+  NormPart p = np_empty();
+  for (int i = lane; i < P; i += 64) p = np_merge(p, rec[i]);
+  return np_wave_merge(p);
+}
+
+__device__ __forceinline__ float bce_of(float c, float a) {
+  return fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c)));
+}
+
+// Row path: one persistent workgroup per compute unit, the two looks of each
+// of its row pairs in turn.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void stats_rows_kernel(
+    const T* __restrict__ draft, const T* __restrict__ target, const int32_t* __restrict__ teacher,
+    const float* __restrict__ conf_logits, int32_t V, int32_t npairs, float* __restrict__ l1,
+    float* __restrict__ accept_rate, float* __restrict__ ce, float* __restrict__ bce) {
+  constexpr int SEG = stat_seg<T>();
+  __shared__ NormPart shp[kRowWaves];
+  __shared__ float sha[kRowWaves];
+  __shared__ PairK shk;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int P = (V + SEG - 1) / SEG;
+  for (int rr = blockIdx.x; rr < npairs; rr += gridDim.x) {
+    const size_t row = static_cast<size_t>(rr);
+    const T* dr = draft + row * V;
+    const T* tr = target + row * V;
+    const float r5 = pair_r5(dr, tr, V, lane);  // issued ahead of the first segment's loads
+    NormPart acc = np_empty();
+    float K = 0.0f;
+    bool kset = false;
+    seg_scan<T, VEC>(dr, tr, V, P, wave, kRowWaves, lane, [&](const uint4* ud, const uint4* ut, int) {
+      if (!kset) {  // once the first segment's loads are in flight
+        K = pair_k5(r5);
+        kset = true;
+      }
+      acc = np_merge(acc, seg_part<T>(ud, ut, K));
+    });
+    if (lane == 0) shp[wave] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      const NormPart m = np_wave_merge(lane < kRowWaves ? shp[lane] : np_empty());
+      K = pair_k5(r5);  // wave 0 may have had no segment
+      if (lane == 0) {
+        shk = pair_k(m);
+        shk.K = K;
+      }
+    }
+    __syncthreads();
+    const PairK k = shk;
+    float a = 0.0f;
+    seg_scan<T, VEC>(dr, tr, V, P, wave, kRowWaves, lane,
+                     [&](const uint4* ud, const uint4* ut, int) { seg_l1<T>(ud, ut, k, a); });
+    a = wave_sum(a);
+    if (lane == 0) sha[wave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float A = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) A += sha[w];
+      const float L1 = l1_final(k, A);
+      const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+      l1[row] = L1;
+      accept_rate[row] = av;
+      ce[row] = k.lse_d - load_logit(dr, clamp_token(teacher[row], V));
+      bce[row] = bce_of(conf_logits[row], av);
+    }
+    __syncthreads();  // shp, sha and shk are reused by the next pair
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sliced path for small batches: (row pair, segment) items, one wave each, so
+// that a few hundred row pairs still fill the GPU.  Both item kernels keep
+// the next item's loads in flight while reducing the current one (two
+// register buffers, unconditional clamped loads).
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_part1_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
-    int32_t items, StatPart* __restrict__ part, uint32_t* __restrict__ counters,
+    int32_t items, NormPart* __restrict__ part, uint32_t* __restrict__ counters,
     int32_t ncounters) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
-  // the ticket counters of stats_part2 start at zero
+  // the ticket counters of the second look start at zero
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < ncounters; i += kThreads) counters[i * kTicketStride] = 0u;
   const int nwaves = gridDim.x * kWaves;
-  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
-                                            (threadIdx.x >> 6));
+  int item = uniform_i(static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6));
   if (item >= items) return;
   uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
-  auto reduce = [&](uint4* ud, uint4* ut, int it_) {
+  float ra, rb;  // pair_r5 of the buffered items, loaded ahead of their segments
+  auto load = [&](int it_, uint4* ud, uint4* ut, float& r5) {
+    const int pair = it_ / P, seg = it_ - pair * P;
+    const size_t off = static_cast<size_t>(pair) * V;
+    r5 = pair_r5(draft + off, target + off, V, lane);
+    seg_load<T, true>(draft + off, target + off, V, seg * SEG, lane, ud, ut);
+  };
+  auto reduce = [&](uint4* ud, uint4* ut, float r5, int it_) {
     const int seg = it_ - (it_ / P) * P;
-    seg_mask<T>(V, seg * SEG, lane, ud, ut);
-    StatPart r;
-    seg_stats<T>(ud, r.md, r.sd);
-    seg_stats<T>(ut, r.mt, r.st);
+    seg_mask<T, true>(V, seg * SEG, lane, ud, ut);
+    const NormPart r = seg_part<T>(ud, ut, pair_k5(r5));
     if (lane == 0) part[it_] = r;
   };
-  seg_load<T>(draft, target, V, P, item, lane, ad, at);
+  load(item, ad, at, ra);
   while (true) {
-    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
-    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
-    reduce(ad, at, item);
+    const int n1 = uniform_i(item + nwaves);
+    load(n1 < items ? n1 : item, bd, bt, rb);
+    reduce(ad, at, ra, item);
     if (n1 >= items) break;
-    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
-    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
-    reduce(bd, bt, n1);
+    const int n2 = uniform_i(n1 + nwaves);
+    load(n2 < items ? n2 : n1, ad, at, ra);
+    reduce(bd, bt, rb, n1);
     if (n2 >= items) break;
     item = n2;
   }
-}
-
-// combine a pair's part1 records: the base-2 shift M2 of the pair and the sum
-// relative to it, for the draft (d) and target (t) rows
-__device__ __forceinline__ void pair_norm(const StatPart* __restrict__ rec, int P, int lane,
-                                          float& M2d, float& Sd, float& M2t, float& St) {
-  float md = neg_inf(), mt = neg_inf();
-  for (int i = lane; i < P; i += 64) {
-    md = fmaxf(md, rec[i].md);
-    mt = fmaxf(mt, rec[i].mt);
-  }
-  md = wave_max(md);
-  mt = wave_max(mt);
-  M2d = md > neg_inf() ? floorf(md * kLog2e) : 0.0f;
-  M2t = mt > neg_inf() ? floorf(mt * kLog2e) : 0.0f;
-  float sd = 0.0f, st = 0.0f;
-  for (int i = lane; i < P; i += 64) {
-    const StatPart r = rec[i];
-    if (r.md > neg_inf()) sd += r.sd * __builtin_amdgcn_exp2f(floorf(r.md * kLog2e) - M2d);
-    if (r.mt > neg_inf()) st += r.st * __builtin_amdgcn_exp2f(floorf(r.mt * kLog2e) - M2t);
-  }
-  Sd = wave_sum(sd);
-  St = wave_sum(st);
 }
 
 // Per-block tau and the loss / report sums by one wave, in fp64 and a fixed
@@ -388,71 +406,58 @@ struct StatsOut {
   uint32_t* counters;  // per pair: segments done; then pairs done (kTicketStride apart)
 };
 
-// Per item: the pair's normalisers from all its part1 records, then the
-// item's share of the overlap (times Sd), with a ticket on the pair: the pair's last
-// item writes L1, accept_rate, CE and BCE, and the wave finishing the last
-// pair writes tau and the sums.
+// Per item: the pair's constants from all its part1 records, then the item's
+// share of the pair's L1 sum (seg_l1), with a ticket on the pair: the pair's
+// last item writes L1, accept_rate, CE and BCE, and the wave finishing the
+// last pair writes tau and the sums.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
-    int32_t items, const StatPart* __restrict__ part, float* __restrict__ l1part, StatsOut o) {
-  constexpr int EPL = 16 / sizeof(T);
+    int32_t items, const NormPart* __restrict__ part, float* __restrict__ l1part, StatsOut o) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
   const int npairs = items / P;
-  // one item at a time per wave (its ticket waits for its own stores, so no
-  // later item's loads may be in flight); the other waves of the CU cover
-  // the latency
   for (int item = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6); item < items;
        item += nwaves) {
-    const int it_ = __builtin_amdgcn_readfirstlane(item);
+    const int it_ = uniform_i(item);
     const int pair = it_ / P, seg = it_ - pair * P;
+    const size_t off = static_cast<size_t>(pair) * V;
     uint4 ud[kSegIters], ut[kSegIters];
-    seg_load<T>(draft, target, V, P, it_, lane, ud, ut);
-    float M2d, Sd, M2t, St;
-    pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
-    seg_mask<T>(V, seg * SEG, lane, ud, ut);
-    // the item's share of the overlap sum_v min(P_v, T_v), times Sd:
-    // min(P_v, T_v) = 2^min(d_v log2e - M2d, t_v log2e - M2t + lam) / Sd
-    const float lam = __log2f(Sd) - __log2f(St);
-    float acc = 0.0f;
-#pragma unroll
-    for (int it = 0; it < kSegIters; ++it)
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        acc += __builtin_amdgcn_exp2f(fminf(fmaf(elem16(ud[it], j, T{}), kLog2e, -M2d),
-                                            fmaf(elem16(ut[it], j, T{}), kLog2e, -M2t) + lam));
-    acc = wave_sum(acc);
+    const float r5 = pair_r5(draft + off, target + off, V, lane);
+    seg_load<T, true>(draft + off, target + off, V, seg * SEG, lane, ud, ut);
+    PairK k = pair_k(pair_merge(part + static_cast<size_t>(pair) * P, P, lane));
+    k.K = pair_k5(r5);
+    seg_mask<T, true>(V, seg * SEG, lane, ud, ut);
+    float a = 0.0f;
+    seg_l1<T>(ud, ut, k, a);
+    a = wave_sum(a);
     uint32_t ticket = 0;
     if (lane == 0) {
-      store_coherent(l1part + it_, acc);
+      store_coherent(l1part + it_, a);
       ticket = publish(o.counters + static_cast<size_t>(pair) * kTicketStride);
     }
-    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    ticket = uniform_i(static_cast<int>(ticket));
     if (ticket != static_cast<uint32_t>(P - 1)) continue;
-    // the pair's last item: the overlap from the item shares (fixed order);
-    // L1 = sum |P - T| = 2 (1 - overlap), both rows summing to 1
-    float ov = 0.0f;
-    for (int i = lane; i < P; i += 64) ov += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
-    ov = wave_sum(ov) / Sd;
+    // the pair's last item: its L1 from the item shares (fixed order)
+    float A = 0.0f;
+    for (int i = lane; i < P; i += 64) A += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
+    A = wave_sum(A);
     uint32_t last = 0;
     if (lane == 0) {
-      const float L1 = fmaxf(0.0f, 2.0f * (1.0f - ov));
-      const float a = fminf(1.0f, fmaxf(0.0f, ov));
+      const float L1 = l1_final(k, A);
+      const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
       const int32_t tch = clamp_token(o.teacher[pair], V);
-      const float c = o.conf_logits[pair];
-      const float lse_d = M2d * kLn2 + logf(Sd);
       store_coherent(o.l1 + pair, L1);
-      store_coherent(o.accept_rate + pair, a);
-      store_coherent(o.ce + pair, lse_d - load_logit(draft + static_cast<size_t>(pair) * V, tch));
-      store_coherent(o.bce + pair, fmaxf(c, 0.0f) - c * a + log1pf(expf(-fabsf(c))));
+      store_coherent(o.accept_rate + pair, av);
+      store_coherent(o.ce + pair, k.lse_d - load_logit(draft + off, tch));
+      store_coherent(o.bce + pair, bce_of(o.conf_logits[pair], av));
       last = publish(o.counters + static_cast<size_t>(npairs) * kTicketStride) ==
                      static_cast<uint32_t>(npairs - 1)
                  ? 1u
                  : 0u;
     }
-    if (__builtin_amdgcn_readfirstlane(last))
+    if (uniform_i(static_cast<int>(last)))
       wave_batch_reduce(o.l1, o.accept_rate, o.ce, o.bce, o.block_mask, o.N, o.gamma, o.w_ce,
                         o.w_l1, o.w_conf, o.tau, o.sums);
   }
@@ -533,27 +538,28 @@ __global__ __launch_bounds__(kThreads) void stats_reduce_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Backward: the gradient of scale x the loss numerator (definition in
-// include/dspark.h).  Per row pair, three looks: the normalisers; then
-// L1 = sum |P - T| and S = sum_u sign(P_u - T_u) P_u; then the gradient row
-//   g_v = a_ce (P_v - [v == teacher]) + a_l1 P_v (s_v - S),
-// a_ce = scale m_b w_k w_ce, a_l1 = scale m_b w_k w_l1 (the only write).  The
-// sliced path runs the looks as item kernels (the first is stats_part1); the
-// row path keeps one workgroup per pair for all three, its second and third
-// looks served by the caches.
-
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// A pair's coefficients: P_v = 2^(x log2e - shd) isd, and
-// log2 P_v - log2 T_v = (x - y) log2e - lr (lr: the pair's log2 ratio of the
-// two normalisers), so the sign of P_v - T_v needs no second exponential.
+// ---------------------------------------------------------------------------
+// Backward: the gradient of scale x the loss numerator (definition in
+// include/dspark.h).  Per row pair, three looks: the normalisers (look 1 of
+// the forward); then L1 = sum |P - T| and S = sum_u sign(P_u - T_u) P_u; then
+// the gradient row
+//   g_v = a_ce (P_v - [v == teacher]) + a_l1 P_v (s_v - S),
+// a_ce = scale m_b w_k w_ce, a_l1 = scale m_b w_k w_l1 (the only write).  For
+// near pairs (l1norm.hpp) the sign s_v is that of D_v kappa - (T_v - D_v),
+// exact wherever that term is, so that nearly equal rows get the oracle's
+// signs; for far pairs that of log2 P_v - log2 T_v.  The sliced
+// path runs the looks as item kernels (the first is stats_part1); the row
+// path keeps one workgroup per pair for all three, its later looks served by
+// the caches.
+
 struct GradRow {
-  float shd, isd, lr;
+  PairK k;
   float S, a_ce, a_l1;
   int32_t teacher;
 };
@@ -570,83 +576,110 @@ struct GradArgs {
   uint32_t* counters;
 };
 
-// the pair's coefficients from its normalisers, L1 and S; writes the
+// the pair's coefficients from its constants, L1 and S; writes the
 // confidence-logit gradient scale m_b w_k w_conf (sigmoid(c) - a)
-__device__ __forceinline__ GradRow grad_row(const GradArgs& g, int pair, float shd, float Sd, float sht,
-                                            float St, float L1, float S, int32_t V) {
-  const int k = pair % g.gamma + 1, b = pair / g.gamma;
+__device__ __forceinline__ GradRow grad_row(const GradArgs& g, int pair, const PairK& k, float L1, float S,
+                                            int32_t V) {
+  const int kk = pair % g.gamma + 1, b = pair / g.gamma;
   const bool m = g.block_mask ? g.block_mask[b] != 0 : true;
   const float sc = g.scale ? *g.scale : 1.0f;
-  const float alpha = m ? sc * expf(-static_cast<float>(k) / static_cast<float>(g.gamma)) : 0.0f;
+  const float alpha = m ? sc * expf(-static_cast<float>(kk) / static_cast<float>(g.gamma)) : 0.0f;
   const float a = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
   const float c = g.conf_logits[pair];
   g.grad_conf[pair] = alpha * g.w_conf * (1.0f / (1.0f + expf(-c)) - a);
-  // log2 P_v - log2 T_v = (x - y) log2e - [(shd + log2 Sd) - (sht + log2 St)]
-  const float lr = (shd + __log2f(Sd)) - (sht + __log2f(St));
-  return GradRow{shd, 1.0f / Sd, lr, S, alpha * g.w_ce, alpha * g.w_l1, clamp_token(g.teacher[pair], V)};
+  return GradRow{k, S, alpha * g.w_ce, alpha * g.w_l1, clamp_token(g.teacher[pair], V)};
 }
 
-__device__ __forceinline__ void l1_and_s(float x, float y, float shd, float isd, float sht, float ist,
-                                         float& l1, float& s) {
-  const float P = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -shd)) * isd;
-  const float T = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -sht)) * ist;
-  l1 += fabsf(P - T);
-  s += P > T ? P : (P < T ? -P : 0.0f);
+// Look 2 of a segment for the gradient: the lane's share of the L1 sum (as
+// seg_l1) and of sum_v sign(P_v - T_v) D_v; k.far is uniform.
+template <typename T>
+__device__ __forceinline__ void seg_l1s(const uint4* ud, const uint4* ut, const PairK& k, float& acc, float& s) {
+  constexpr int EPL = 16 / sizeof(T);
+  if (k.far) {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const float u = fmaf(elem16(ud[it], j, T{}), kLog2e, -k.a2d);
+        const float w = fmaf(elem16(ut[it], j, T{}) - k.K, kLog2e, -k.a2t) + k.lam2;
+        const float D = __builtin_amdgcn_exp2f(u);
+        acc += __builtin_amdgcn_exp2f(fminf(u, w));
+        s += u > w ? D : (u < w ? -D : 0.0f);
+      }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const float d = elem16(ud[it], j, T{}), t = elem16(ut[it], j, T{}) - k.K;
+        const float D = __builtin_amdgcn_exp2f(fmaf(d, kLog2e, -k.a2d));
+        const float Tv = __builtin_amdgcn_exp2f(fmaf(t, kLog2e, -k.a2t));
+        const float e = fmaf(D, k.kappa, -np_diff(d, t, D, Tv));
+        acc += fabsf(e);
+        s += e > 0.0f ? D : (e < 0.0f ? -D : 0.0f);
+      }
+  }
 }
 
-__device__ __forceinline__ float grad_elem(const GradRow& r, float x, float y, int v) {
-  const float P = __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r.shd)) * r.isd;
-  const float dl = fmaf(x - y, kLog2e, -r.lr);  // NaN (both -inf: P = 0) gives sign 0
-  const float sg = dl > 0.0f ? 1.0f : (dl < 0.0f ? -1.0f : 0.0f);
+__device__ __forceinline__ float grad_elem(const GradRow& r, float x, float y0, int v) {
+  const float y = y0 - r.k.K;
+  const float u = fmaf(x, kLog2e, -r.k.a2d);
+  const float D = __builtin_amdgcn_exp2f(u);
+  float e;
+  if (r.k.far) {
+    e = u - (fmaf(y, kLog2e, -r.k.a2t) + r.k.lam2);
+  } else {
+    const float Tv = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -r.k.a2t));
+    e = fmaf(D, r.k.kappa, -np_diff(x, y, D, Tv));
+  }
+  const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
+  const float P = D * r.k.isd;
   return r.a_ce * (P - (v == r.teacher ? 1.0f : 0.0f)) + r.a_l1 * P * (sg - r.S);
 }
 
-// Sliced second look: per item the pair's normalisers (its part1 records)
-// and the item's shares of L1 and S; the pair's last item (ticket) sums the
+// Sliced second look: per item the pair's constants (its part1 records) and
+// the item's shares of L1 and S; the pair's last item (ticket) sums the
 // shares in a fixed order and stores the pair's GradRow.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_grad_part2_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P, int32_t items,
-    const StatPart* __restrict__ part, float* __restrict__ l1part, float* __restrict__ spart,
-    GradArgs o) {
-  constexpr int EPL = 16 / sizeof(T);
+    const NormPart* __restrict__ part, float* __restrict__ l1part, GradArgs o) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
   for (int item = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6); item < items;
        item += nwaves) {
-    const int it_ = __builtin_amdgcn_readfirstlane(item);
+    const int it_ = uniform_i(item);
     const int pair = it_ / P, seg = it_ - pair * P;
+    const size_t off = static_cast<size_t>(pair) * V;
     uint4 ud[kSegIters], ut[kSegIters];
-    seg_load<T>(draft, target, V, P, it_, lane, ud, ut);
-    float M2d, Sd, M2t, St;
-    pair_norm(part + static_cast<size_t>(pair) * P, P, lane, M2d, Sd, M2t, St);
-    seg_mask<T>(V, seg * SEG, lane, ud, ut);
-    const float isd = 1.0f / Sd, ist = 1.0f / St;
-    float l1 = 0.0f, sv = 0.0f;
-#pragma unroll
-    for (int it = 0; it < kSegIters; ++it)
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        l1_and_s(elem16(ud[it], j, T{}), elem16(ut[it], j, T{}), M2d, isd, M2t, ist, l1, sv);
-    l1 = wave_sum(l1);
-    sv = wave_sum(sv);
+    const float r5 = pair_r5(draft + off, target + off, V, lane);
+    seg_load<T, true>(draft + off, target + off, V, seg * SEG, lane, ud, ut);
+    PairK k = pair_k(pair_merge(part + static_cast<size_t>(pair) * P, P, lane));
+    k.K = pair_k5(r5);
+    seg_mask<T, true>(V, seg * SEG, lane, ud, ut);
+    float a = 0.0f, s = 0.0f;
+    seg_l1s<T>(ud, ut, k, a, s);
+    a = wave_sum(a);
+    s = wave_sum(s);
     uint32_t ticket = 0;
     if (lane == 0) {
-      store_coherent(l1part + it_, l1);
-      store_coherent(spart + it_, sv);
+      float* q = l1part + 2 * static_cast<size_t>(it_);
+      store_coherent(q, a);
+      store_coherent(q + 1, s);
       ticket = publish(o.counters + static_cast<size_t>(pair) * kTicketStride);
     }
-    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    ticket = uniform_i(static_cast<int>(ticket));
     if (ticket != static_cast<uint32_t>(P - 1)) continue;
-    float L1 = 0.0f, S = 0.0f;
+    float A = 0.0f, S = 0.0f;
     for (int i = lane; i < P; i += 64) {
-      L1 += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
-      S += load_coherent(spart + static_cast<size_t>(pair) * P + i);
+      const float* q = l1part + 2 * (static_cast<size_t>(pair) * P + i);
+      A += load_coherent(q);
+      S += load_coherent(q + 1);
     }
-    L1 = wave_sum(L1);
+    A = wave_sum(A);
     S = wave_sum(S);
-    if (lane == 0) o.rows[pair] = grad_row(o, pair, M2d, Sd, M2t, St, L1, S, V);
+    if (lane == 0) o.rows[pair] = grad_row(o, pair, k, l1_final(k, A), S * k.isd, V);
   }
 }
 
@@ -665,41 +698,61 @@ __device__ __forceinline__ void store16<float>(float* p, const float* g) {
   *reinterpret_cast<float4*>(p) = make_float4(g[0], g[1], g[2], g[3]);
 }
 
+
+// The gradient of one segment (lane l: groups it * 64 + l) into row gr.
+template <typename T, bool VEC>
+__device__ __forceinline__ void seg_grad_store(const GradRow& r, const uint4* ud, const uint4* ut, int32_t V, int lo,
+                                               int lane, T* __restrict__ gr) {
+  constexpr int EPL = 16 / sizeof(T);
+#pragma unroll
+  for (int it = 0; it < kSegIters; ++it) {
+    const int e = lo + (it * 64 + lane) * EPL;
+    if (e >= V) continue;  // VEC: a clamped load past the row
+    float g[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, elem16(ud[it], j, T{}), elem16(ut[it], j, T{}), e + j);
+    if constexpr (VEC) {
+      store16<T>(gr + e, g);
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (e + j < V) {
+          if constexpr (sizeof(T) == 2) gr[e + j] = bf16_rne(g[j]);
+          else gr[e + j] = g[j];
+        }
+    }
+  }
+}
+
 // Sliced third look: per item the gradient of its segment (the next item's
 // loads in flight while the current one is computed and stored).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_grad_write_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P, int32_t items,
     const GradRow* __restrict__ rows, T* __restrict__ grad) {
-  constexpr int EPL = 16 / sizeof(T);
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * kWaves;
-  int item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6));
+  int item = uniform_i(static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6));
   if (item >= items) return;
   uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  auto load = [&](int it_, uint4* ud, uint4* ut) {
+    const int pair = it_ / P, seg = it_ - pair * P;
+    const size_t off = static_cast<size_t>(pair) * V;
+    seg_load<T, true>(draft + off, target + off, V, seg * SEG, lane, ud, ut);
+  };
   auto write = [&](const uint4* ud, const uint4* ut, int it_) {
     const int pair = it_ / P, seg = it_ - pair * P;
-    const GradRow r = rows[pair];
-    const size_t off = static_cast<size_t>(pair) * V;
-#pragma unroll
-    for (int it = 0; it < kSegIters; ++it) {
-      const int e = seg * SEG + (it * 64 + lane) * EPL;
-      if (e >= V) continue;  // a clamped load past the row
-      float g[EPL];
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, elem16(ud[it], j, T{}), elem16(ut[it], j, T{}), e + j);
-      store16<T>(grad + off + e, g);
-    }
+    seg_grad_store<T, true>(rows[pair], ud, ut, V, seg * SEG, lane, grad + static_cast<size_t>(pair) * V);
   };
-  seg_load<T>(draft, target, V, P, item, lane, ad, at);
+  load(item, ad, at);
   while (true) {
-    const int n1 = __builtin_amdgcn_readfirstlane(item + nwaves);
-    seg_load<T>(draft, target, V, P, n1 < items ? n1 : item, lane, bd, bt);
+    const int n1 = uniform_i(item + nwaves);
+    load(n1 < items ? n1 : item, bd, bt);
     write(ad, at, item);
     if (n1 >= items) break;
-    const int n2 = __builtin_amdgcn_readfirstlane(n1 + nwaves);
-    seg_load<T>(draft, target, V, P, n2 < items ? n2 : n1, lane, ad, at);
+    const int n2 = uniform_i(n1 + nwaves);
+    load(n2 < items ? n2 : n1, ad, at);
     write(bd, bt, n1);
     if (n2 >= items) break;
     item = n2;
@@ -713,108 +766,65 @@ __global__ __launch_bounds__(kRowThreads) void stats_grad_rows_kernel(const T* _
                                                                       const T* __restrict__ target,
                                                                       int32_t V, int32_t npairs, GradArgs o,
                                                                       T* __restrict__ grad) {
-  using L = Vec8<T, VEC>;
-  constexpr int EPL = L::N;
-  constexpr int kWaves = kRowWaves;
-  __shared__ float shv[kWaves];
+  constexpr int SEG = stat_seg<T>();
+  __shared__ NormPart shp[kRowWaves];
+  __shared__ float sha[kRowWaves], shs[kRowWaves];
   __shared__ GradRow shr;
-  const int step = kRowThreads * EPL;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int P = (V + SEG - 1) / SEG;
   for (int rr = blockIdx.x; rr < npairs; rr += gridDim.x) {
     const size_t row = static_cast<size_t>(rr);
     const T* dr = draft + row * V;
     const T* tr = target + row * V;
-    T* gr = grad + row * V;
-
-    float md = neg_inf(), sd = 0.0f, mt = neg_inf(), st = 0.0f;
-    int e = threadIdx.x * EPL;
-    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
-      float xd[kUnroll][EPL], xt[kUnroll][EPL];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        L::load(dr + e + u * step, xd[u]);
-        L::load(tr + e + u * step, xt[u]);
+    const float r5 = pair_r5(dr, tr, V, lane);  // issued ahead of the first segment's loads
+    NormPart acc = np_empty();
+    float K = 0.0f;
+    bool kset = false;
+    seg_scan<T, VEC>(dr, tr, V, P, wave, kRowWaves, lane, [&](const uint4* ud, const uint4* ut, int) {
+      if (!kset) {  // once the first segment's loads are in flight
+        K = pair_k5(r5);
+        kset = true;
       }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        online(md, sd, xd[u], EPL);
-        online(mt, st, xt[u], EPL);
+      acc = np_merge(acc, seg_part<T>(ud, ut, K));
+    });
+    if (lane == 0) shp[wave] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      const NormPart m = np_wave_merge(lane < kRowWaves ? shp[lane] : np_empty());
+      K = pair_k5(r5);  // wave 0 may have had no segment
+      if (lane == 0) {
+        shr.k = pair_k(m);
+        shr.k.K = K;
       }
     }
-    for (; e < V; e += step) {
-      float xd[EPL], xt[EPL];
-      L::load(dr + e, xd);
-      L::load(tr + e, xt);
-      online(md, sd, xd, EPL);
-      online(mt, st, xt, EPL);
+    __syncthreads();
+    const PairK k = shr.k;
+    float a = 0.0f, s = 0.0f;
+    seg_scan<T, VEC>(dr, tr, V, P, wave, kRowWaves, lane,
+                     [&](const uint4* ud, const uint4* ut, int) { seg_l1s<T>(ud, ut, k, a, s); });
+    a = wave_sum(a);
+    s = wave_sum(s);
+    if (lane == 0) {
+      sha[wave] = a;
+      shs[wave] = s;
     }
-    const float Md = block_max<kWaves>(md, shv);
-    const float Sd = block_sum<kWaves>(md > neg_inf() ? sd * __builtin_amdgcn_exp2f((md - Md) * kLog2e) : 0.0f, shv);
-    const float Mt = block_max<kWaves>(mt, shv);
-    const float St = block_sum<kWaves>(mt > neg_inf() ? st * __builtin_amdgcn_exp2f((mt - Mt) * kLog2e) : 0.0f, shv);
-    const float shd = Md > neg_inf() ? Md * kLog2e : 0.0f, sht = Mt > neg_inf() ? Mt * kLog2e : 0.0f;
-    const float isd = 1.0f / Sd, ist = 1.0f / St;
-
-    float l1 = 0.0f, sv = 0.0f;
-    e = threadIdx.x * EPL;
-    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
-      float xd[kUnroll][EPL], xt[kUnroll][EPL];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float A = 0.0f, S = 0.0f;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        L::load(dr + e + u * step, xd[u]);
-        L::load(tr + e + u * step, xt[u]);
+      for (int w = 0; w < kRowWaves; ++w) {
+        A += sha[w];
+        S += shs[w];
       }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) l1_and_s(xd[u][j], xt[u][j], shd, isd, sht, ist, l1, sv);
+      shr = grad_row(o, static_cast<int>(row), k, l1_final(k, A), S * k.isd, V);
     }
-    for (; e < V; e += step) {
-      float xd[EPL], xt[EPL];
-      L::load(dr + e, xd);
-      L::load(tr + e, xt);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) l1_and_s(xd[j], xt[j], shd, isd, sht, ist, l1, sv);
-    }
-    const float L1 = block_sum<kWaves>(l1, shv);
-    const float S = block_sum<kWaves>(sv, shv);
-    if (threadIdx.x == 0) shr = grad_row(o, static_cast<int>(row), shd, Sd, sht, St, L1, S, V);
     __syncthreads();
     const GradRow r = shr;
-
-    e = threadIdx.x * EPL;
-    for (; e + (kUnroll - 1) * step < V; e += kUnroll * step) {
-      float xd[kUnroll][EPL], xt[kUnroll][EPL];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        L::load(dr + e + u * step, xd[u]);
-        L::load(tr + e + u * step, xt[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float g[EPL];
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[u][j], xt[u][j], e + u * step + j);
-        if constexpr (VEC) {
-          store16<T>(gr + e + u * step, g);
-        } else {
-          if constexpr (sizeof(T) == 2) gr[e + u * step] = bf16_rne(g[0]);
-          else gr[e + u * step] = g[0];
-        }
-      }
-    }
-    for (; e < V; e += step) {
-      float xd[EPL], xt[EPL], g[EPL];
-      L::load(dr + e, xd);
-      L::load(tr + e, xt);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) g[j] = grad_elem(r, xd[j], xt[j], e + j);
-      if constexpr (VEC) {
-        store16<T>(gr + e, g);
-      } else {
-        if constexpr (sizeof(T) == 2) gr[e] = bf16_rne(g[0]);
-        else gr[e] = g[0];
-      }
-    }
+    T* gr = grad + row * V;
+    seg_scan<T, VEC>(dr, tr, V, P, wave, kRowWaves, lane, [&](const uint4* ud, const uint4* ut, int lo) {
+      seg_grad_store<T, VEC>(r, ud, ut, V, lo, lane, gr);
+    });
+    __syncthreads();  // shp, sha, shs and shr are reused by the next pair
   }
 }
 
@@ -841,13 +851,13 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                         int32_t gamma, int32_t V, float w_ce, float w_l1, float w_conf, float* l1,
                         float* accept_rate, float* ce, float* bce, float* tau, float* sums,
                         void* ws, const StatsPlan& pl, hipStream_t st) {
-  const int epl = sizeof(T) == 2 ? 8 : 4;
+  const int epl = 16 / static_cast<int>(sizeof(T));
   const bool vec = (V % epl == 0) && reinterpret_cast<uintptr_t>(draft) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(target) % 16 == 0;
   const int npairs = N * gamma;
   if (npairs > 0 && vec && pl.sliced) {
     char* w = static_cast<char*>(ws);
-    StatPart* part = reinterpret_cast<StatPart*>(w + pl.off_part);
+    NormPart* part = reinterpret_cast<NormPart*>(w + pl.off_part);
     float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
     const int items = npairs * pl.P;
@@ -887,9 +897,8 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
   if (npairs == 0) return hipSuccess;
   if (vec && pl.sliced) {
     char* w = static_cast<char*>(ws);
-    StatPart* part = reinterpret_cast<StatPart*>(w + pl.off_part);
+    NormPart* part = reinterpret_cast<NormPart*>(w + pl.off_part);
     float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
-    float* spart = reinterpret_cast<float*>(w + pl.off_s);
     o.rows = reinterpret_cast<GradRow*>(w + pl.off_rows);
     o.counters = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
     const int items = npairs * pl.P;
@@ -897,7 +906,7 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
     DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
                   target, V, pl.P, items, part, o.counters, npairs);
     DSPARK_LAUNCH("stats_grad_part2", (stats_grad_part2_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
-                  draft, target, V, pl.P, items, part, l1part, spart, o);
+                  draft, target, V, pl.P, items, part, l1part, o);
     DSPARK_LAUNCH("stats_grad_write", (stats_grad_write_kernel<T>), dim3(wgs), dim3(kThreads), 0, st,
                   draft, target, V, pl.P, items, o.rows, grad);
   } else {
@@ -935,11 +944,9 @@ StatsGradPlan plan_stats_backward(int32_t N, int32_t gamma, int32_t V) {
   if (p.sliced) {
     const size_t items = static_cast<size_t>(npairs) * Pmax;
     p.off_part = off;
-    off = align_up(off + items * sizeof(StatPart), 256);
-    p.off_l1 = off;
-    off = align_up(off + items * sizeof(float), 256);
-    p.off_s = off;
-    off = align_up(off + items * sizeof(float), 256);
+    off = align_up(off + items * sizeof(NormPart), 256);
+    p.off_l1 = off;  // per item: shares of the L1 sum and of S Sd
+    off = align_up(off + 2 * items * sizeof(float), 256);
     p.off_rows = off;
     off = align_up(off + static_cast<size_t>(npairs) * sizeof(GradRow), 256);
     p.off_cnt = off;
@@ -979,8 +986,8 @@ StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
   if (p.sliced) {
     const size_t items = static_cast<size_t>(npairs) * Pmax;
     p.off_part = off;
-    off = align_up(off + items * sizeof(StatPart), 256);
-    p.off_l1 = off;
+    off = align_up(off + items * sizeof(NormPart), 256);
+    p.off_l1 = off;  // per item: share of the L1 sum
     off = align_up(off + items * sizeof(float), 256);
     p.off_cnt = off;
     off = align_up(off + (static_cast<size_t>(npairs) + 1) * kTicketStride * sizeof(uint32_t), 256);

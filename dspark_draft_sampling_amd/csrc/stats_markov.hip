@@ -17,20 +17,24 @@
 // fragments) for the whole launch; it walks the rows in tiles of 64 (the N
 // side), staging the tile's W1 rows (selected by the forced tokens) in LDS,
 // and adds the bias to the backbone values it streams.  Launches, in order:
-//  * teacher: per row the forced previous token and the draft value at the
-//    teacher token;
-//  * look 1: per (row, workgroup) the (max, sum exp) of the draft values of
-//    its tokens;
-//  * tnorm: the target's normaliser (no bias involved), per half row;
-//  * rows: the per-row draft normalisers from the look-1 records;
-//  * look 2: the bias again, and per (row, workgroup) the share of the
-//    overlap sum_v min(P_v, T_v) (L1 = 2 (1 - overlap));
+//  * teacher: per row the forced previous token, the draft value at the
+//    teacher token and the row's reference offset (l1norm.hpp) from its
+//    first five tokens;
+//  * look 1: per (row, workgroup) the normaliser part of the draft and target
+//    values of its tokens (l1norm.hpp: the maxima, and the sums under one
+//    power-of-two shift shared by both rows where the maxima allow it);
+//  * rows: per row the merged part and look 2's constants;
+//  * look 2: the bias again, and per (row, workgroup) the share of the row's
+//    L1 sum: min(P_v, T_v) for rows whose L1 is at least kFarL1 by look 1's
+//    bound, |P_v - T_v| in the form that keeps relative accuracy where the
+//    rows nearly agree for the others;
 //  * final: per row L1, accept_rate, CE, BCE; then the batch reduction of
 //    the plain statistics.
 #include <algorithm>
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "l1norm.hpp"
 
 namespace dspark {
 namespace {
@@ -53,8 +57,18 @@ constexpr int kSmDma = (kSmTile * (kSmMaxR / 8 + 1) / 64 + kSmWaves - 1) / kSmWa
 constexpr int kSmABuf = kSmDma * kSmWaves * 64 * 8;  // elements per W1 buffer
 static_assert(kSmABuf >= kSmTile * (kSmMaxR + kSmPad), "W1 buffer");
 
-struct SmRec {
-  float md, sd, mt, st;  // max and sum exp(x - max) of the draft and target values
+// The looks' per-row constants, 16 bytes (one LDS-DMA slot per row):
+//   look 1: x = K (the reference offset)
+//   look 2, near rows: x = the common shift, y = K, z = kappa, far = 0
+//   look 2, far rows: x = a2d, y = a2t + K log2e, z = lam2, far = 1
+// and the final kernel's.
+struct SmMeta {
+  float x, y, z;
+  uint32_t far;
+};
+struct SmFin {
+  float inv_st, isd, lse_d;
+  uint32_t flags;  // empty | far << 2
 };
 
 struct SmArgs {
@@ -65,21 +79,22 @@ struct SmArgs {
   const uint16_t* w2;
   const int32_t* teacher;
   int32_t rows, gamma, V, r;
-  SmRec* rec;       // [rows][G] (look 1)
+  NormPart* rec;    // [rows][G] (look 1)
   float* dteach;    // [rows]: the draft value at the teacher token
-  SmRec* norm;      // [rows]: per-row normalisers (after look 1)
-  float* l1part;    // [rows][G] (look 2)
-  SmRec* k2;        // [rows]: look 2's per-row constants (dh, cd, th, lam)
+  SmFin* norm;      // [rows]: the final kernel's constants (after look 1)
+  float* l1part;    // [rows][G][2] (look 2)
+  SmMeta* k1;       // [rows]: look 1's per-row constants
+  SmMeta* k2;       // [rows]: look 2's per-row constants
   int32_t* xf;      // [rows]: each row's forced previous token, clamped (stats_markov_teacher)
-  SmRec* tpart;     // [rows]: the target's (max, sum exp) of each half row (stats_markov_tnorm)
 };
 
 // Two of everything: the aligned path stages tile t + 1 and merges tile
 // t - 1 while tile t runs (index = tile parity); the unaligned path uses 0.
 struct SmLds {
   __attribute__((aligned(16))) uint16_t a[2][kSmABuf];  // staged W1 rows, kSmMaxR + kSmPad apart
-  float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];                 // per (parity, wave, row)
-  SmRec meta[2][kSmTile];  // per (parity, row): look 2 the constants of its epilogue
+  float m[2][kSmWaves][kSmTile], s[2][kSmWaves][kSmTile];  // per (parity, wave, row)
+  float u[2][kSmWaves][kSmTile], w[2][kSmWaves][kSmTile], ad[2][kSmWaves][kSmTile];
+  SmMeta meta[2][kSmTile];  // per (parity, row): the constants of the look's epilogue
 };
 
 __device__ __forceinline__ float rows_max(float v) {
@@ -298,7 +313,7 @@ __device__ __forceinline__ void load_half(Quad<T> (&qd)[2][kSmMS], Quad<T> (&qt)
 // the maximum (the k loop and the staging indexes are then compile-time).
 template <typename T, bool LT, bool MASK, bool RMAX, bool META, class Epi, class Merge>
 __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[kSmMS][kSmMaxR / 32], int tok0,
-                                            SmLds& L, const SmRec* meta, Epi&& epi, Merge&& merge) {
+                                            SmLds& L, const SmMeta* meta, Epi&& epi, Merge&& merge) {
   typedef __attribute__((address_space(3))) void lds_void;
   if (a.rows <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -311,7 +326,7 @@ __device__ __forceinline__ void sm_look_vec(const SmArgs& a, const bf16x8 (&af)[
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w1), static_cast<short>(0), V * r * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<SmRec*>(meta), static_cast<short>(0), META ? a.rows * 16 : 0, kBufferWord3);
+      const_cast<SmMeta*>(meta), static_cast<short>(0), META ? a.rows * 16 : 0, kBufferWord3);
 
   // the forced tokens of the rows of the thread's DMA slots of tile row0
   auto load_xs = [&](int row0, int32_t (&xs)[kSmDma]) {
@@ -411,9 +426,8 @@ __device__ __forceinline__ void sm_load_w2(bf16x8 (&af)[kSmMS][kSmMaxR / 32], co
   }
 }
 
-// Look 1: per (row, workgroup) record of the draft values' (max, sum exp)
-// (the target rows are not needed: their normalisers do not involve the bias,
-// stats_markov_tnorm; nor is the teacher's value, stats_markov_teacher).
+// Look 1: per (row, workgroup) the normaliser part of the draft and target
+// values of its tokens (the teacher's draft value is stats_markov_teacher's).
 template <typename T, bool VEC, bool MASK, bool RMAX>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a) {
   __shared__ SmLds L;
@@ -422,44 +436,63 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2<VEC>(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  auto epi = [&](int h, const float* d, const float*, int p) {
-    float md = neg_inf();
+  // per (wave, row): the part of the lane group's 64 tokens; the shift mode
+  // is per row, so per lane here
+  auto epi = [&](int h, const float* d, const float* t0, int p) {
+    const float K = L.meta[p][h * 16 + (lane & 15)].x;
+    float t[4 * kSmMS];
 #pragma unroll
-    for (int e = 0; e < 4 * kSmMS; ++e) md = fmaxf(md, d[e]);
+    for (int e = 0; e < 4 * kSmMS; ++e) t[e] = t0[e] - K;
+    float md = neg_inf(), mt = neg_inf();
+#pragma unroll
+    for (int e = 0; e < 4 * kSmMS; ++e) {
+      md = fmaxf(md, d[e]);
+      mt = fmaxf(mt, t[e]);
+    }
     md = rows_max(md);
-    // exp(d - md) = 2^(d log2e - mh) 2^-ml, with mh the fp32 product md log2e
-    // and ml its rounding residual (one FMA per element, the residual once)
-    const float mh = md > neg_inf() ? md * kLog2e : 0.0f;
-    const float ml = md > neg_inf() ? fmaf(md, kLog2e, -mh) : 0.0f;
-    float sd = 0.0f;
+    mt = rows_max(mt);
+    const bool common = np_common(md, mt);
+    float a2d, a2t;
+    np_shifts(md, mt, a2d, a2t);
+    float sd = 0.0f, x = 0.0f, ad = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4 * kSmMS; ++e) sd += __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -mh));
-    sd = rows_sum(sd) * __builtin_amdgcn_exp2f(-ml);
+    for (int e = 0; e < 4 * kSmMS; ++e) {
+      const float D = __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -a2d));
+      const float Tv = __builtin_amdgcn_exp2f(fmaf(t[e], kLog2e, -a2t));
+      const float df = np_diff(d[e], t[e], D, Tv);
+      sd += D;
+      x += common ? df : Tv;
+      ad += fabsf(df);
+    }
+    sd = rows_sum(sd);
+    x = rows_sum(x);
+    ad = rows_sum(ad);
     if (lane < 16) {
       const int n = h * 16 + lane;
       L.m[p][wave][n] = md;
-      L.s[p][wave][n] = sd;
+      L.s[p][wave][n] = mt;
+      L.u[p][wave][n] = sd;
+      L.w[p][wave][n] = x;
+      L.ad[p][wave][n] = ad;
     }
   };
   auto merge = [&](int row0, int p) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
       const int n = threadIdx.x;
-      float m = neg_inf();
+      NormPart q = np_empty();
 #pragma unroll
-      for (int w = 0; w < kSmWaves; ++w) m = fmaxf(m, L.m[p][w][n]);
-      float s = 0.0f;
-      if (m > neg_inf())
-#pragma unroll
-        for (int w = 0; w < kSmWaves; ++w)
-          if (L.m[p][w][n] > neg_inf()) s += L.s[p][w][n] * __builtin_amdgcn_exp2f((L.m[p][w][n] - m) * kLog2e);
-      a.rec[static_cast<size_t>(row0 + n) * G + g] = SmRec{m, s, 0.0f, 0.0f};
+      for (int w = 0; w < kSmWaves; ++w)
+        q = np_merge(q, NormPart{L.m[p][w][n], L.s[p][w][n], L.u[p][w][n], L.w[p][w][n], L.ad[p][w][n]});
+      a.rec[static_cast<size_t>(row0 + n) * G + g] = q;
     }
   };
   if constexpr (VEC) {
-    sm_look_vec<T, false, MASK, RMAX, false>(a, af, tok0, L, nullptr, epi, merge);
+    sm_look_vec<T, true, MASK, RMAX, true>(a, af, tok0, L, a.k1, epi, merge);
   } else {
     for (int row0 = 0; row0 < a.rows; row0 += kSmTile) {
-      sm_tile<T, VEC, false>(a, af, tok0, row0, L, epi);
+      const int row = row0 + static_cast<int>(threadIdx.x);
+      if (threadIdx.x < kSmTile) L.meta[0][threadIdx.x] = a.k1[row < a.rows ? row : 0];
+      sm_tile<T, VEC, true>(a, af, tok0, row0, L, epi);  // its staging barrier publishes meta
       __syncthreads();
       merge(row0, 0);
       __syncthreads();  // the LDS tile is reused by the next tile
@@ -485,121 +518,47 @@ __global__ __launch_bounds__(256) void stats_markov_teacher_kernel(SmArgs a) {
   for (int j = lane; j < a.r; j += 64)
     s = fmaf(__uint_as_float(static_cast<uint32_t>(w1[j]) << 16), __uint_as_float(static_cast<uint32_t>(w2[j]) << 16), s);
   s = wave_sum(s);
+  // the reference offset: t_v - d_v of tokens 0..4 (bias summed as above)
+  const T* bb = static_cast<const T*>(a.backbone) + static_cast<size_t>(row) * a.V;
+  const T* tg = static_cast<const T*>(a.target) + static_cast<size_t>(row) * a.V;
+  float r[5];
+#pragma unroll
+  for (int v = 0; v < 5; ++v) {
+    const int vv = v < a.V ? v : 0;
+    const uint16_t* w2v = a.w2 + static_cast<size_t>(vv) * a.r;
+    float b = 0.0f;
+    for (int j = lane; j < a.r; j += 64)
+      b = fmaf(__uint_as_float(static_cast<uint32_t>(w1[j]) << 16), __uint_as_float(static_cast<uint32_t>(w2v[j]) << 16), b);
+    b = wave_sum(b);
+    r[v] = v < a.V ? load_logit(tg, vv) - (load_logit(bb, vv) + b) : pos_inf();
+  }
   if (lane == 0) {
-    a.dteach[row] = load_logit(static_cast<const T*>(a.backbone) + static_cast<size_t>(row) * a.V, tch) + s;
+    a.dteach[row] = load_logit(bb, tch) + s;
     a.xf[row] = x;
+    a.k1[row] = SmMeta{ref_offset(r[0], r[1], r[2], r[3], r[4]), 0.0f, 0.0f, 0u};
   }
 }
 
-// The target rows' normalisers, one wave per half row (no barriers, so a
-// wave streams its half rows back to back): unit u is half u % 2 of row
-// u / 2, and the wave writes its (max, sum exp) into tpart[row] (half 0 in
-// (md, sd), half 1 in (mt, st)); stats_markov_rows combines the halves.
-constexpr int kTnThreads = 256;
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kTnThreads) void stats_markov_tnorm_kernel(SmArgs a) {
-  constexpr int EPL = VEC ? 16 / static_cast<int>(sizeof(T)) : 1;
-  constexpr int kU = 8;
-  const T* tg = static_cast<const T*>(a.target);
-  const int V = a.V;
-  const int lane = threadIdx.x & 63;
-  const int nwaves = gridDim.x * (kTnThreads / 64);
-  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kTnThreads / 64) +
-                                               static_cast<int>(threadIdx.x >> 6));
-  const int Vh = (V / 2 + EPL - 1) / EPL * EPL;  // half 0's length, a multiple of EPL
-  for (int u = w; u < 2 * a.rows; u += nwaves) {
-    const int row = u >> 1, hf = u & 1;
-    const int lo = hf ? Vh : 0, hi = hf ? V : min(Vh, V);
-    const T* tr = tg + static_cast<size_t>(row) * V;
-    float m = neg_inf(), s = 0.0f;
-    auto add = [&](const float* x) {
-      float mx = x[0];
-#pragma unroll
-      for (int j = 1; j < EPL; ++j) mx = fmaxf(mx, x[j]);
-      if (mx > m) {
-        s = m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - mx) * kLog2e) : 0.0f;
-        m = mx;
-      }
-      if (m > neg_inf())
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) s += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
-    };
-    auto ld = [&](int e, float* x) {
-      if constexpr (VEC) {
-        const uint4 q = *reinterpret_cast<const uint4*>(tr + e);
-        if constexpr (sizeof(T) == 2) {
-          x[0] = bf_lo(q.x); x[1] = bf_hi(q.x); x[2] = bf_lo(q.y); x[3] = bf_hi(q.y);
-          x[4] = bf_lo(q.z); x[5] = bf_hi(q.z); x[6] = bf_lo(q.w); x[7] = bf_hi(q.w);
-        } else {
-          x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
-          x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
-        }
-      } else {
-        x[0] = load_logit(tr, e);
-      }
-    };
-    constexpr int step = 64 * EPL;
-    int e = lo + lane * EPL;
-    for (; e + (kU - 1) * step < hi; e += kU * step) {
-      float x[kU][EPL];
-#pragma unroll
-      for (int k = 0; k < kU; ++k) ld(e + k * step, x[k]);
-#pragma unroll
-      for (int k = 0; k < kU; ++k) add(x[k]);
-    }
-    for (; e < hi; e += step) {
-      float x[EPL];
-      ld(e, x);
-      add(x);
-    }
-    const float M = wave_max(m);
-    const float S = wave_sum(m > neg_inf() ? s * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f);
-    if (lane == 0) {
-      float* dst = hf ? &a.tpart[row].mt : &a.tpart[row].md;
-      dst[0] = M;
-      dst[1] = S;
-    }
-  }
-}
-
-// Per row: the draft normaliser from the row's G look-1 records, the target
-// normaliser from stats_markov_tnorm's two halves, and look 2's per-row
-// constants.
+// Per row: the merged part of the row's G look-1 records, look 2's constants
+// and the final kernel's (one wave per row, fixed merge order).
 __global__ __launch_bounds__(256) void stats_markov_rows_kernel(SmArgs a, int32_t G) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.rows) return;
-  const SmRec* rc = a.rec + static_cast<size_t>(row) * G;
-  float md = neg_inf();
-  for (int i = lane; i < G; i += 64) md = fmaxf(md, rc[i].md);
-  md = wave_max(md);
-  float sd = 0.0f;
-  for (int i = lane; i < G; i += 64) {
-    const SmRec q = rc[i];
-    if (q.md > neg_inf()) sd += q.sd * __builtin_amdgcn_exp2f((q.md - md) * kLog2e);
-  }
-  sd = wave_sum(sd);
+  const NormPart* rc = a.rec + static_cast<size_t>(row) * G;
+  NormPart q = np_empty();
+  for (int i = lane; i < G; i += 64) q = np_merge(q, rc[i]);
+  const PairK k = pair_k(np_wave_merge(q));
   if (lane == 0) {
-    // the target normaliser from the two half-row records of stats_markov_tnorm
-    const SmRec tp = a.tpart[row];
-    const float mt = fmaxf(tp.md, tp.mt);
-    const float st = (tp.md > neg_inf() ? tp.sd * __builtin_amdgcn_exp2f((tp.md - mt) * kLog2e) : 0.0f) +
-                     (tp.mt > neg_inf() ? tp.st * __builtin_amdgcn_exp2f((tp.mt - mt) * kLog2e) : 0.0f);
-    const SmRec nr{md, sd, mt, st};
-    a.norm[row] = nr;
-    // look 2's constants: P_v = 2^(d_v log2e - dh) cd with dh = md log2e in
-    // fp32 and cd = 2^-rd / sd (rd: the product's rounding residual);
-    // likewise T_v with (th, ct); lam = log2(ct / cd), so that
-    // min(P_v, T_v) = cd 2^min(d_v log2e - dh, t_v log2e - th + lam)
-    const float dh = nr.md * kLog2e, th = nr.mt * kLog2e;
-    const float rd = fmaf(nr.md, kLog2e, -dh), rt = fmaf(nr.mt, kLog2e, -th);
-    const float cd = __builtin_amdgcn_exp2f(-rd) / nr.sd;
-    const float lam = (rd - rt) + (__log2f(nr.sd) - __log2f(nr.st));
-    a.k2[row] = SmRec{dh, cd, th, lam};
+    const float K = a.k1[row].x;
+    a.k2[row] = k.far ? SmMeta{k.a2d, fmaf(K, kLog2e, k.a2t), k.lam2, 1u} : SmMeta{k.a2d, K, k.kappa, 0u};
+    a.norm[row] = SmFin{k.inv_st, k.isd, k.lse_d, k.empty | (k.far << 2)};
   }
 }
 
-// Look 2: per (row, workgroup) share of the overlap sum_v min(P_v, T_v).
+// Look 2: per (row, workgroup) the share of the row's L1 sum (min(P_v, T_v) Sd
+// for far rows, |P_v - T_v| St for near rows; the form is per row, so per
+// lane here).
 template <typename T, bool VEC, bool MASK, bool RMAX>
 __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a) {
   __shared__ SmLds L;
@@ -608,25 +567,25 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   const int tok0 = g * kSmTokens;
   bf16x8 af[kSmMS][kSmMaxR / 32];
   sm_load_w2<VEC>(af, a.w2, tok0 + wave * 16 * kSmMS, a.V, a.r, lane);
-  // the shares of the overlap sum_v min(P_v, T_v) (L1 = 2 (1 - overlap), both
-  // rows summing to 1): with the row's (dh, cd, th, lam) from
-  // stats_markov_rows, min(P_v, T_v) = cd 2^min(d_v log2e - dh, t_v log2e - th + lam),
-  // one exponential per element pair
   auto epi = [&](int h, const float* d, const float* t, int p) {
-    const SmRec k = L.meta[p][h * 16 + (lane & 15)];
-    float l1 = 0.0f;
+    const SmMeta k = L.meta[p][h * 16 + (lane & 15)];
+    float acc = 0.0f;
+    if (k.far) {
 #pragma unroll
-    for (int e = 0; e < 4 * kSmMS; ++e)
-      l1 += __builtin_amdgcn_exp2f(fminf(fmaf(d[e], kLog2e, -k.md), fmaf(t[e], kLog2e, -k.mt) + k.st));
-    l1 = rows_sum(l1) * k.sd;
-    if (lane < 16) L.s[p][wave][h * 16 + lane] = l1;
+      for (int e = 0; e < 4 * kSmMS; ++e) acc += l1_far(d[e], t[e], k.x, k.y, k.z);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4 * kSmMS; ++e) acc += l1_near(d[e], t[e] - k.y, k.x, k.z);
+    }
+    acc = rows_sum(acc);
+    if (lane < 16) L.m[p][wave][h * 16 + lane] = acc;
   };
   auto merge = [&](int row0, int p) {
     if (threadIdx.x < kSmTile && row0 + static_cast<int>(threadIdx.x) < a.rows) {
-      float s = 0.0f;
+      float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kSmWaves; ++w) s += L.s[p][w][threadIdx.x];
-      a.l1part[static_cast<size_t>(row0 + threadIdx.x) * G + g] = s;
+      for (int w = 0; w < kSmWaves; ++w) acc += L.m[p][w][threadIdx.x];
+      a.l1part[static_cast<size_t>(row0 + threadIdx.x) * G + g] = acc;
     }
   };
   if constexpr (VEC) {
@@ -643,7 +602,7 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look2_kernel(SmArgs a
   }
 }
 
-// Per row: the overlap from its G shares, then L1, accept_rate, CE and BCE.
+// Per row: L1 from its G shares, then accept_rate, CE and BCE.
 __global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32_t G, const float* conf_logits,
                                                                  float* l1, float* accept_rate, float* ce,
                                                                  float* bce) {
@@ -653,13 +612,14 @@ __global__ __launch_bounds__(256) void stats_markov_final_kernel(SmArgs a, int32
   float s = 0.0f;
   for (int i = lane; i < G; i += 64) s += a.l1part[static_cast<size_t>(row) * G + i];
   s = wave_sum(s);
-  if (lane == 0) {  // s: the overlap sum_v min(P_v, T_v)
-    const SmRec nr = a.norm[row];
-    const float av = fminf(1.0f, fmaxf(0.0f, s));
+  if (lane == 0) {
+    const SmFin f = a.norm[row];
+    const float L1 = l1_final(f.flags & 3u, f.flags >> 2, f.inv_st, f.isd, s);
+    const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
     const float c = conf_logits[row];
-    l1[row] = fmaxf(0.0f, 2.0f * (1.0f - s));
+    l1[row] = L1;
     accept_rate[row] = av;
-    ce[row] = nr.md + logf(nr.sd) - a.dteach[row];
+    ce[row] = f.lse_d - a.dteach[row];
     bce[row] = fmaxf(c, 0.0f) - c * av + log1pf(expf(-fabsf(c)));
   }
 }
@@ -701,18 +661,11 @@ hipError_t launch_sm_typed(const SmArgs& a, int G, const float* conf_logits, con
                    reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
                    static_cast<uint64_t>(kSmTile) * a.V * sizeof(T) < 0x7fffffffull &&
                    static_cast<uint64_t>(a.V) * a.r * 2 < 0x7fffffffull &&
-                   static_cast<uint64_t>(a.rows) * sizeof(SmRec) < 0x7fffffffull;
+                   static_cast<uint64_t>(a.rows) * sizeof(SmMeta) < 0x7fffffffull;
   const bool mask = a.V % 64 != 0, rmax = a.r == kSmMaxR;
   DSPARK_LAUNCH("stats_markov_teacher", stats_markov_teacher_kernel<T>, dim3(rb), dim3(256), 0, st, a);
   hipError_t e = launch_look<T>(a, G, vec, mask, rmax, 1, st);
   if (e != hipSuccess) return e;
-  const int epl = 16 / static_cast<int>(sizeof(T));
-  const bool tvec = a.V % epl == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0;
-  const dim3 tgrid(static_cast<unsigned>(std::max(1, std::min((2 * a.rows + 3) / 4, 4 * device_cus()))));
-  if (tvec)
-    DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, true>), tgrid, dim3(kTnThreads), 0, st, a);
-  else
-    DSPARK_LAUNCH("stats_markov_tnorm", (stats_markov_tnorm_kernel<T, false>), tgrid, dim3(kTnThreads), 0, st, a);
   DSPARK_LAUNCH("stats_markov_rows", stats_markov_rows_kernel, dim3(rb), dim3(256), 0, st, a, G);
   e = launch_look<T>(a, G, vec, mask, rmax, 2, st);
   if (e != hipSuccess) return e;
@@ -732,19 +685,19 @@ StatsMarkovPlan plan_stats_markov(int32_t N, int32_t gamma, int32_t V) {
   p.G = (V + kSmTokens - 1) / kSmTokens;
   size_t off = 0;
   p.off_rec = off;
-  off = align_up(off + rows * p.G * sizeof(SmRec), 256);
+  off = align_up(off + rows * p.G * sizeof(NormPart), 256);
   p.off_norm = off;
-  off = align_up(off + rows * sizeof(SmRec), 256);
+  off = align_up(off + rows * sizeof(SmFin), 256);
   p.off_l1 = off;
   off = align_up(off + rows * p.G * sizeof(float), 256);
   p.off_dt = off;
   off = align_up(off + rows * sizeof(float), 256);
+  p.off_k1 = off;
+  off = align_up(off + rows * sizeof(SmMeta), 256);
   p.off_k2 = off;
-  off = align_up(off + rows * sizeof(SmRec), 256);
+  off = align_up(off + rows * sizeof(SmMeta), 256);
   p.off_xf = off;
   off = align_up(off + rows * sizeof(int32_t), 256);
-  p.off_tp = off;
-  off = align_up(off + rows * sizeof(SmRec), 256);
   p.bytes = rows > 0 ? off : 0;
   return p;
 }
@@ -760,10 +713,10 @@ hipError_t launch_stats_markov(const void* backbone, const void* target, int dty
     return launch_stats_reduce(l1, accept_rate, ce, bce, block_mask, N, gamma, w_ce, w_l1, w_conf, tau, sums, st);
   char* w = static_cast<char*>(ws);
   SmArgs a{backbone, target, anchor, w1, w2, teacher, rows, gamma, V, r,
-           reinterpret_cast<SmRec*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
-           reinterpret_cast<SmRec*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1),
-           reinterpret_cast<SmRec*>(w + pl.off_k2), reinterpret_cast<int32_t*>(w + pl.off_xf),
-           reinterpret_cast<SmRec*>(w + pl.off_tp)};
+           reinterpret_cast<NormPart*>(w + pl.off_rec), reinterpret_cast<float*>(w + pl.off_dt),
+           reinterpret_cast<SmFin*>(w + pl.off_norm), reinterpret_cast<float*>(w + pl.off_l1),
+           reinterpret_cast<SmMeta*>(w + pl.off_k1), reinterpret_cast<SmMeta*>(w + pl.off_k2),
+           reinterpret_cast<int32_t*>(w + pl.off_xf)};
   if (dtype == DSPARK_BF16)
     return launch_sm_typed<uint16_t>(a, pl.G, conf_logits, block_mask, N, w_ce, w_l1, w_conf, l1, accept_rate,
                                      ce, bce, tau, sums, st);

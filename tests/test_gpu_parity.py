@@ -24,7 +24,7 @@ import dspark_draft_sampling_amd as ds  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import _gpu as G  # noqa: E402
 from tests._cases import decode_case, stats_case  # noqa: E402
-from workloads import decode_inputs, stats_inputs  # noqa: E402
+from workloads import STATS_CONFIG, bf16_to_f32, decode_inputs, stats_inputs, to_bf16  # noqa: E402
 
 RTOL = 1e-4
 DATA_FLAGS = O.F_NONFINITE | O.F_EMPTY
@@ -151,6 +151,116 @@ def test_stats_full_vocab():
     for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
         assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
     assert np.allclose(got["sums"], ref["sums"], rtol=RTOL, atol=1e-6)
+
+
+def test_stats_full_config_row_path():
+    """The training statistics at their full shape (2048 blocks x gamma 7,
+    V=129280, bf16, every 4th block masked: 14336 row pairs, the row path).
+    Blocks 0, 1, 1023 and 2047 element by element against the oracle; tau
+    and the sums against the call's own per-position outputs (fp64)."""
+    cfg = dict(STATS_CONFIG)
+    si = stats_inputs(cfg, mask_every=4)
+    got = G.stats(si)
+    del si
+    blocks = [0, 1, 1023, 2047]
+    sub = stats_inputs(cfg, blocks=blocks, mask_every=4)
+    ref = O.accept_stats(sub)
+    for key in ["l1", "accept_rate", "ce", "bce", "tau"]:
+        assert np.allclose(got[key][blocks], ref[key], rtol=RTOL, atol=1e-6), key
+    a = got["accept_rate"].astype(np.float64)
+    tau = 1.0 + np.cumprod(a, axis=1).sum(1)
+    assert np.allclose(got["tau"], tau, rtol=1e-6, atol=0)
+    m = (np.arange(cfg["N"]) % 4 != 3)
+    g = cfg["gamma"]
+    w = np.exp(-np.arange(1, g + 1) / g)
+    num = (m[:, None] * w[None, :] * (0.1 * got["ce"] + 0.9 * got["l1"] + 1.0 * got["bce"])).sum()
+    n = g * m.sum()
+    want = [num, n, (got["l1"] * m[:, None]).sum(), n, (a * m[:, None]).sum(), n,
+            (tau * m).sum(), m.sum(), (got["ce"] * m[:, None]).sum(), n, (got["bce"] * m[:, None]).sum(), n]
+    assert np.allclose(got["sums"], want, rtol=1e-5, atol=0)
+
+
+def _near_rows(N, gamma, V, seed):
+    """Row pairs at bf16 whose L1 spans 0 to 2: per position, in turn, equal
+    rows; 300 logits moved by one bf16 step; every logit moved by
+    bf16(N(0, 0.004^2)) noise (most round back, L1 about 4e-5); the row's
+    maximum and 50 others moved by one step; disjoint supports; the target
+    N(0, 1) away; the target offset by 100 (separate shifts); an empty
+    target row; the target offset by +10.5 and by -9.75 exactly (logits on
+    a 1/8 grid), with 300 logits moved by 1/8.  L1 is offset-invariant."""
+    rng = np.random.default_rng(seed)
+    d = rng.normal(0, 3.0, (N, gamma, V)).astype(np.float32)
+    d = bf16_to_f32(to_bf16(d))
+    t = d.copy()
+    for i in range(N * gamma):
+        b, k = divmod(i, gamma)
+        x = d[b, k]
+        kind = i % 10
+        if kind == 1:
+            idx = rng.choice(V, 300, replace=False)
+            t[b, k, idx] = bf16_to_f32(to_bf16(x[idx] * np.float32(1 + 2.0 ** -7)))
+        elif kind == 2:
+            t[b, k] = bf16_to_f32(to_bf16(x + rng.normal(0, 0.004, V).astype(np.float32)))
+        elif kind == 3:
+            idx = np.concatenate([[np.argmax(x)], rng.choice(V, 50, replace=False)])
+            t[b, k, idx] = bf16_to_f32(to_bf16(x[idx] * np.float32(1 + 2.0 ** -7)))
+        elif kind == 4:
+            t[b, k, 1::2] = -np.inf
+            d[b, k, ::2] = -np.inf
+        elif kind == 5:
+            t[b, k] = x + rng.normal(0, 1.0, V).astype(np.float32)
+        elif kind == 6:
+            t[b, k] = x + np.float32(100.0)
+        elif kind == 7:
+            t[b, k] = -np.inf
+        elif kind in (8, 9):
+            g = np.clip(np.round(x * 8.0) / 8.0, -15.0, 15.0).astype(np.float32)
+            d[b, k] = g
+            t[b, k] = g + np.float32(10.5 if kind == 8 else -9.75)
+            idx = rng.choice(V, 300, replace=False)
+            t[b, k, idx] += np.float32(0.125) * rng.choice(np.array([-1.0, 1.0], np.float32), 300)
+    teacher = rng.integers(0, V, (N, gamma))
+    teacher[:, :] = np.argmax(np.where(np.isfinite(d), d, -1e30), axis=2)
+    return stats_case(d, t, teacher=teacher, conf_logits=rng.normal(0, 1, (N, gamma)), dtype="bf16")
+
+
+def _misaligned(x):
+    """x (a device tensor) in storage that starts 2 bytes off a 16-byte boundary."""
+    buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=x.device)
+    y = buf[1:1 + x.numel()].view(x.shape)
+    y.copy_(x)
+    assert y.is_contiguous() and y.data_ptr() % 16 != 0
+    return y
+
+
+@pytest.mark.parametrize("path", ["sliced", "row"])
+def test_stats_near_rows_full_vocab(path):
+    """L1 at V=129280 from 0 (equal rows) through 4e-5 (bf16 noise) to 2
+    (disjoint), relative to L1 itself (1e-4), on the sliced path (28 pairs,
+    aligned rows) and on the row path (the same rows 2 bytes off 16-byte
+    alignment)."""
+    si = _near_rows(4, 7, 129280, 2024)
+    ref = O.accept_stats(si)
+    if path == "sliced":
+        got = G.stats(si)
+    else:
+        out = ds.dspark_accept_stats(_misaligned(G.logits(si["draft"], "bf16")),
+                                     _misaligned(G.logits(si["target"], "bf16")),
+                                     G.i32(si["teacher"]), G.f32(si["conf_logits"]))
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+    l1r, l1g = ref["l1"], got["l1"].astype(np.float64)
+    bad = np.abs(l1g - l1r) > RTOL * l1r + 1e-9
+    assert not bad.any(), (np.argwhere(bad), l1g[bad], l1r[bad])
+    assert np.all(l1g.reshape(-1)[0::10] == 0.0)  # equal rows
+    assert np.all(l1g.reshape(-1)[4::10] == 2.0)  # disjoint supports
+    assert np.all(l1g.reshape(-1)[7::10] == 1.0)  # empty target row
+    assert 1e-5 < l1r.reshape(-1)[2::10].max() < 1e-3
+    assert np.all(l1r.reshape(-1)[8::10] < 1e-2) and np.all(l1r.reshape(-1)[9::10] < 1e-2)
+    for key in ["accept_rate", "bce", "tau"]:
+        assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
+    ce_ok = np.isfinite(ref["ce"])
+    assert np.allclose(got["ce"][ce_ok], ref["ce"][ce_ok], rtol=RTOL, atol=1e-6)
 
 
 # ---------------------------------------------------------- flag rate -------

@@ -26,7 +26,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import dspark_draft_sampling_amd as ds  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import _gpu as G  # noqa: E402
-from workloads import STATS_CONFIG, stats_markov_inputs  # noqa: E402
+from workloads import STATS_CONFIG, bf16_to_f32, stats_markov_inputs, to_bf16  # noqa: E402
 
 RTOL = 1e-4
 KEYS = ["l1", "accept_rate", "ce", "bce"]
@@ -84,6 +84,39 @@ def test_zero_factors_match_plain_statistics():
     plain = G.stats(dict(inp, draft=inp["backbone"]))
     for key in KEYS + ["tau", "sums"]:
         assert np.allclose(got[key], plain[key], rtol=1e-5, atol=1e-6), key
+
+
+def test_near_rows_full_vocab():
+    """L1 relative to itself (1e-4) at V=129280 for row pairs from equal to
+    disjoint (the rows of the plain statistics' test), the Markov bias zero
+    (W1 = 0) so that the draft rows are the backbone's bf16 values; and with
+    a small bias (W1, W2 ~ N(0, 0.02^2), rank 16) against the oracle's own
+    Markov rows, where each draft logit backbone + bias is itself rounded to
+    fp32 once (|delta| <= 2^-24 |d|), which may move L1 by up to
+    2^-23 sum_v P_v |d_v| on top of the 1e-4 relative bar."""
+    from tests.test_gpu_parity import _near_rows
+    si = _near_rows(2, 7, 129280, 77)
+    rng = np.random.default_rng(3)
+    V, r = si["V"], 16
+    w = lambda: np.asarray(to_bf16(rng.normal(0, 0.02, (V, r)).astype(np.float32)))
+    for w1 in (np.zeros((V, r), np.uint16), w()):
+        inp = dict(backbone=si["draft"], target=si["target"], anchor=np.arange(si["N"], dtype=np.int32),
+                   w1=w1, w2=w(), r=r, teacher=si["teacher"], conf_logits=si["conf_logits"],
+                   block_mask=None, N=si["N"], gamma=si["gamma"], V=V, dtype="bf16")
+        got = run(inp)
+        ref = O.accept_stats_markov(inp)
+        l1r, l1g = ref["l1"], got["l1"].astype(np.float64)
+        bound = RTOL * l1r + 1e-9
+        if w1.any():
+            bb = bf16_to_f32(si["draft"]).astype(np.float64)
+            fin = np.isfinite(bb)
+            e = np.where(fin, np.exp(bb - np.max(np.where(fin, bb, -np.inf), -1, keepdims=True)), 0.0)
+            P = e / e.sum(-1, keepdims=True)
+            bound = bound + 2.0 ** -23 * (P * np.where(fin, np.abs(bb), 0.0)).sum(-1)
+        bad = np.abs(l1g - l1r) > bound
+        assert not bad.any(), (bool(w1.any()), np.argwhere(bad), l1g[bad], l1r[bad])
+        for key in ["accept_rate", "bce", "tau"]:
+            assert np.allclose(got[key], ref[key], rtol=RTOL, atol=1e-6), key
 
 
 def test_full_config_sampled():
