@@ -30,10 +30,12 @@ DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_ESHAPE, DSPARK_EWORKSPACE, DSPAR
 DSPARK_BF16, DSPARK_F32 = 1, 2
 DSPARK_OP_MARKOV, DSPARK_OP_VERIFY, DSPARK_OP_STATS, DSPARK_OP_STATS_BACKWARD = 1, 2, 3, 4
 DSPARK_OP_STATS_MARKOV = 5
+DSPARK_NOALLOC_SCRATCH_BYTES = 32 << 20  # per-GPU scratch of dspark_verify_noalloc
 DSPARK_MAX_GAMMA, DSPARK_MAX_RANK, DSPARK_MAX_VERIFY_BATCH = 16, 256, 65535  # as include/dspark.h
 FLAG_NEAR, FLAG_NONFINITE, FLAG_RESIDUAL_ZERO, FLAG_EMPTY_ROW, FLAG_BAD_POLICY = 1, 2, 4, 8, 16
 
 __all__ = ["DSparkError", "Policy", "lib", "dspark_markov_sample", "dspark_verify",
+           "dspark_verify_noalloc",
            "dspark_accept_stats", "dspark_accept_stats_backward", "dspark_accept_stats_markov",
            "dspark_select_width", "dspark_workspace_size", "profile_enable",
            "profile_summary", "DSPARK_MAX_GAMMA", "DSPARK_MAX_RANK",
@@ -72,6 +74,8 @@ def lib():
         L.dspark_verify.argtypes = [P, C.c_int, P, P, P, P, P, P, dspark_policy, u64, i32, i32,
                                     i32, P, P, P, P, sz, P]
         L.dspark_verify.restype = C.c_int
+        L.dspark_verify_noalloc.argtypes = L.dspark_verify.argtypes[:16] + [P]
+        L.dspark_verify_noalloc.restype = C.c_int
         L.dspark_accept_stats.argtypes = [P, P, C.c_int, P, P, P, i32, i32, i32, f32, f32, f32,
                                           P, P, P, P, P, P, P, sz, P]
         L.dspark_accept_stats.restype = C.c_int
@@ -277,6 +281,36 @@ def dspark_verify(target, draft_tokens, policy: Policy, q_logits=None, q_lse=Non
     _check(rc)
     return out
 
+
+
+def dspark_verify_noalloc(target, draft_tokens, policy: Policy, out, q_logits=None, q_lse=None,
+                          q_thr=None, q_tok=None, n_draft=None, seed=0):
+    """dspark_verify on the library's own per-GPU scratch: no workspace and no
+    allocation (the caller passes out: accept_len [B] int32, out_tokens
+    [B,g+1] int32, flags [B,g+1] uint8).  Calls that overlap on one GPU race."""
+    dt = _logits_dtype(target, "target")
+    _dev_tensor(target, target.dtype, "target")
+    if target.dim() != 3:
+        raise DSparkError("verify: target must be [B, gamma + 1, V]")
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    _dev_tensor(draft_tokens, torch.int32, "draft_tokens", (B, g), dev)
+    for name, t, shape in [("q_logits", q_logits, (B, g, V)), ("q_lse", q_lse, (B, g)),
+                           ("q_thr", q_thr, (B, g)), ("q_tok", q_tok, (B, g))]:
+        if t is not None:
+            _dev_tensor(t, torch.float32, name, shape, dev)
+    if n_draft is not None:
+        _dev_tensor(n_draft, torch.int32, "n_draft", (B,), dev)
+    pol = policy.c(B, dev)
+    _check_out(out, [("accept_len", torch.int32, (B,)), ("out_tokens", torch.int32, (B, g1)),
+                     ("flags", torch.uint8, (B, g1))], dev, "verify_noalloc")
+    rc = lib().dspark_verify_noalloc(_p(target), dt, _p(draft_tokens), _p(q_logits), _p(q_lse),
+                                     _p(q_thr), _p(q_tok), _p(n_draft), pol, int(seed), B, g, V,
+                                     _p(out["accept_len"]), _p(out["out_tokens"]), _p(out["flags"]),
+                                     _stream(dev))
+    _check(rc)
+    return out
 
 _STATS_OUT = ["l1", "accept_rate", "ce", "bce"]
 

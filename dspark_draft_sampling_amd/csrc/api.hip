@@ -3,6 +3,8 @@
 // per-operation launchers.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dspark.h"
 #include "internal.hpp"
 
@@ -24,6 +26,46 @@ dspark_status check_common(int dtype, int32_t gamma, int32_t V) {
 // top_k and top_p are either both given or both NULL (no request truncates).
 bool policy_ok(const dspark_policy& p) {
   return p.mode && p.temperature && p.request_id && p.position && (!p.top_k == !p.top_p);
+}
+
+// Scratch of dspark_verify_noalloc: one copy on every GPU the library runs
+// on, held until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the device's first call).
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Host-side checks of dspark_verify (everything but the workspace).
+dspark_status verify_args(const void* target_logits, int logits_dtype, const int32_t* draft_tokens,
+                          const dspark_policy& policy, int32_t B, int32_t gamma, int32_t V,
+                          const int32_t* accept_len, const int32_t* out_tokens, const uint8_t* flags) {
+  if (B < 0) return DSPARK_EINVAL;
+  dspark_status s = check_common(logits_dtype, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if (B > DSPARK_MAX_VERIFY_BATCH) return DSPARK_ESHAPE;
+  if (B == 0) return DSPARK_OK;
+  if (!target_logits || !draft_tokens || !policy_ok(policy) || !accept_len || !out_tokens || !flags)
+    return DSPARK_EINVAL;
+  return DSPARK_OK;
 }
 
 size_t verify_bytes(int dtype, int32_t B, int32_t gamma, int32_t V) {
@@ -111,14 +153,9 @@ dspark_status dspark_verify(const void* target_logits, int logits_dtype,
                             dspark_policy policy, uint64_t seed, int32_t B, int32_t gamma,
                             int32_t V, int32_t* accept_len, int32_t* out_tokens, uint8_t* flags,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0) return DSPARK_EINVAL;
-  dspark_status s = check_common(logits_dtype, gamma, V);
-  if (s != DSPARK_OK) return s;
-  if (B > DSPARK_MAX_VERIFY_BATCH) return DSPARK_ESHAPE;
-  if (B == 0) return DSPARK_OK;
-  if (!target_logits || !draft_tokens || !policy_ok(policy) || !accept_len || !out_tokens ||
-      !flags)
-    return DSPARK_EINVAL;
+  const dspark_status s = verify_args(target_logits, logits_dtype, draft_tokens, policy, B, gamma, V,
+                                      accept_len, out_tokens, flags);
+  if (s != DSPARK_OK || B == 0) return s;
   const VerifyPlan plan =
       dspark::plan_verify(logits_dtype, B, gamma, V, aligned16(target_logits));
   if (!workspace || workspace_bytes < plan.bytes) return DSPARK_EWORKSPACE;
@@ -126,6 +163,26 @@ dspark_status dspark_verify(const void* target_logits, int logits_dtype,
       target_logits, logits_dtype, draft_tokens, q_logits, q_lse, q_thr, q_tok, n_draft, policy,
       seed, B, gamma, V, accept_len, out_tokens, flags, workspace, plan,
       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
+}
+
+dspark_status dspark_verify_noalloc(const void* target_logits, int logits_dtype,
+                                    const int32_t* draft_tokens, const float* q_logits,
+                                    const float* q_lse, const float* q_thr, const float* q_tok,
+                                    const int32_t* n_draft, dspark_policy policy, uint64_t seed,
+                                    int32_t B, int32_t gamma, int32_t V, int32_t* accept_len,
+                                    int32_t* out_tokens, uint8_t* flags, void* stream) {
+  const dspark_status s = verify_args(target_logits, logits_dtype, draft_tokens, policy, B, gamma, V,
+                                      accept_len, out_tokens, flags);
+  if (s != DSPARK_OK || B == 0) return s;
+  const VerifyPlan plan =
+      dspark::plan_verify(logits_dtype, B, gamma, V, aligned16(target_logits));
+  if (plan.bytes > DSPARK_NOALLOC_SCRATCH_BYTES) return DSPARK_EWORKSPACE;
+  void* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return DSPARK_EDEVICE;
+  const hipError_t e = dspark::launch_verify(
+      target_logits, logits_dtype, draft_tokens, q_logits, q_lse, q_thr, q_tok, n_draft, policy,
+      seed, B, gamma, V, accept_len, out_tokens, flags, ws, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSPARK_OK : DSPARK_EDEVICE;
 }
 

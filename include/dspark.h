@@ -344,6 +344,31 @@ dspark_status dspark_verify(
     size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dspark_verify_noalloc
+ *
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): dspark_verify with the same arguments, semantics, outputs and
+ * errors, minus workspace and workspace_bytes.  Its scratch is a
+ * DSPARK_NOALLOC_SCRATCH_BYTES array of device memory owned by the library,
+ * one copy per GPU, held until the process ends; the call itself allocates
+ * nothing.  Every call on a GPU shares that GPU's copy: calls that overlap on
+ * one GPU (other streams, other threads) race, so order them.  The scratch
+ * keeps the last call's contents; the call clears what must start at zero.
+ * Errors: as dspark_verify, and EWORKSPACE when the call needs more than
+ * DSPARK_NOALLOC_SCRATCH_BYTES (dspark_workspace_size(DSPARK_OP_VERIFY, ...)
+ * bounds the need: 1.5 MiB at B = 64, gamma = 5, V = 129280).
+ * ------------------------------------------------------------------------- */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+dspark_status dspark_verify_noalloc(
+    const void* target_logits, int logits_dtype, const int32_t* draft_tokens,
+    const float* q_logits, const float* q_lse, const float* q_thr,
+    const float* q_tok, const int32_t* n_draft, dspark_policy policy,
+    uint64_t seed, int32_t B, int32_t gamma, int32_t V, int32_t* accept_len,
+    int32_t* out_tokens, uint8_t* flags, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dspark_accept_stats
  *
  * [MB] "Training objective", "Acceptance and confidence", "Loss return
