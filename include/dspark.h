@@ -37,9 +37,18 @@
  *    caller's `workspace` (size from dspark_workspace_size), which must stay
  *    untouched until the work queued on `stream` has finished.
  *  * Every call only enqueues work on `stream` (a hipStream_t; NULL = the
- *    default stream) and returns; it never synchronises.  The library keeps no
- *    global state, so calls on different streams with disjoint workspaces may
- *    run concurrently.  Two calls that share a workspace must be ordered.
+ *    default stream) and returns; it never synchronises.  Calls on different
+ *    streams with disjoint workspaces may run concurrently; two calls that
+ *    share a workspace must be ordered.  Process-wide state is limited to:
+ *    the profiler switch and its pending events, the Markov launch-plan
+ *    switch, per device one completion event that chains the library's
+ *    one-launch Markov grids and a counter that tags their hand-off words
+ *    (dspark_markov_plan), and dspark_verify_noalloc's per-GPU scratch.
+ *    Several processes on one GPU share nothing but the device: each has its
+ *    own chain and counter, so one-launch Markov grids of two processes are
+ *    not ordered against each other; if the other process's kernels keep
+ *    compute units busy, a grid's bounded waits give up and flag
+ *    DSPARK_FLAG_SYNC_TIMEOUT (no hang).
  *  * Arguments are validated on the host BEFORE anything is enqueued; on any
  *    error nothing is launched and the outputs are left untouched.  Device
  *    memory contents are never read on the host, so value problems found on
@@ -174,6 +183,10 @@ typedef struct dspark_policy {
   const float* temperature;    /* T > 0 for sampled rows (ignored if greedy) */
   const int32_t* top_k;        /* 0 or >= V: off                             */
   const float* top_p;          /* >= 1: off                                  */
+  /* top_k and top_p are both given or both NULL; NULL means that no request
+   * of the call truncates (the calls then skip every truncation pass, and
+   * dspark_markov_sample takes its untruncated one-launch kernel).  One NULL
+   * without the other is EINVAL.                                             */
   const uint32_t* request_id;  /* Philox counter word 2                      */
   const int32_t* position;     /* absolute position of the anchor x_0        */
 } dspark_policy;
@@ -199,8 +212,8 @@ const char* dspark_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch.  Host-only. */
 int dspark_version(void);
 
-/* Diagnostics: per-kernel timing with HIP events (off by default; the only
- * process-wide state of the library).  While enabled, every kernel the library
+/* Diagnostics: per-kernel timing with HIP events (off by default; a
+ * process-wide switch).  While enabled, every kernel the library
  * launches is bracketed by two events recorded on its stream.
  * dspark_profile_summary waits for the recorded events, writes one line
  * "<kernel> <launches> <total_ms>" per kernel name into buf (NUL-terminated,
@@ -224,7 +237,9 @@ int dspark_release(void);
  *     units the stream may use, resident at once; each workgroup then keeps
  *     its slice of markov_w2 in registers for the whole call, and the steps
  *     hand their results to one another through the workspace (polled, no
- *     device-wide barrier).  It is an ordinary launch: the library
+ *     device-wide barrier; every hand-off word carries a per-call tag, so
+ *     the workspace needs no clearing and a stale word is never read as
+ *     this call's).  It is an ordinary launch: the library
  *     chains its own such launches on a device (each waits for the previous
  *     one's completion event, whatever the stream; not inside a stream
  *     capture), and residency otherwise relies on no other kernel holding
