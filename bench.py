@@ -135,16 +135,34 @@ PROFILES = {
                      "Statistics of the teacher-forced Markov draft (dspark_accept_stats_markov), "
                      "2048 blocks x gamma 7, V=129280, rank 256, bf16",
                      " --workload markov_stats"),
+    "truncated": (os.path.join(ROOT, "profiles", "truncated_step_B256_g5_V129280.md"),
+                  "Truncated decode step (Markov sample + verify + accept stats), B=256, gamma=5, "
+                  "V=129280, bf16, per-request temperature, top-k, top-p, mixed greedy/sampled",
+                  " --workload truncated"),
+    "wide_greedy": (os.path.join(ROOT, "profiles", "wide_greedy_step_B64_g7_V129280.md"),
+                    "Wide greedy decode step (Markov sample + verify + accept stats), 64 requests x "
+                    "8 target rows (gamma=7), V=129280, bf16, greedy",
+                    " --workload wide_greedy"),
 }
+# the SQ counter passes of a profile (each within one pass's limits: at most
+# 8 SQ and 2 GRBM counters)
+SQ_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+             ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_WAVE_CYCLES"))
+DEVICE_CUS = 256
 CSRC = os.path.join(ROOT, "dspark_draft_sampling_amd", "csrc")
 
 
 # the sources a workload's kernels are built from (the digest of a profile
 # summary covers these; None: every kernel source)
 DIGEST_SOURCES = {
-    "decode": ("common.hpp", "internal.hpp", "markov.hip", "stats.hip", "truncate.hpp", "verify.hip"),
-    "train": ("common.hpp", "internal.hpp", "stats.hip"),
-    "markov_stats": ("common.hpp", "internal.hpp", "stats.hip", "stats_markov.hip"),
+    "decode": ("common.hpp", "internal.hpp", "l1norm.hpp", "markov.hip", "stats.hip", "truncate.hpp",
+               "verify.hip"),
+    "train": ("common.hpp", "internal.hpp", "l1norm.hpp", "stats.hip"),
+    "markov_stats": ("common.hpp", "internal.hpp", "l1norm.hpp", "stats.hip", "stats_markov.hip"),
+    "truncated": ("common.hpp", "internal.hpp", "l1norm.hpp", "markov.hip", "stats.hip", "truncate.hpp",
+                  "verify.hip"),
+    "wide_greedy": ("common.hpp", "internal.hpp", "l1norm.hpp", "markov.hip", "stats.hip", "truncate.hpp",
+                    "verify.hip"),
 }
 
 
@@ -163,17 +181,20 @@ def source_digest(workload="decode"):
     return h.hexdigest()
 
 
-def counter_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (copy-calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary was
-    taken on other kernel sources."""
+def counter_traffic(kernel, workload="decode"):
+    """L2-miss bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated: reads served by
+    the Infinity Cache are counted too) per launch of `kernel` from the
+    workload's committed counter summary, or None when that summary was taken
+    on other kernel sources."""
+    if workload not in PROFILES:
+        return None
     try:
-        text = open(PROFILE).read()
+        text = open(PROFILES[workload][0]).read()
         blob = text.split("```json", 1)[1].split("```", 1)[0]
         rec = json.loads(blob)
     except (OSError, IndexError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest():
+    if rec.get("source_sha256") != source_digest(workload):
         return None
     k = rec.get("kernels", {}).get(kernel)
     if not k:
@@ -207,7 +228,7 @@ def summarize_profile(base, workload="decode"):
     true_kib = 256 * 1024
     sf, sw = true_kib / cf, true_kib / cw
     cmd = "python3 bench.py" + wl
-    steps = " --steps 50 --warmup 5" if workload == "decode" else " --steps 10 --warmup 2"
+    steps = " --steps 50 --warmup 5" if workload in ("decode", "truncated", "wide_greedy") else " --steps 10 --warmup 2"
     lines = [
         f"# {title}",
         "",
@@ -221,6 +242,8 @@ def summarize_profile(base, workload="decode"):
         f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
         f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
         f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_copy_WRITE_SIZE -o p -- {cmd} --copy-calibration 256",
+        *[f"rocprofv3 --pmc {' '.join(ps)} -T -f csv -d $OUT/prof_SQ{i} -o p -- {cmd} --steps 2 --warmup 1 --no-cpu"
+          for i, ps in enumerate(SQ_PASSES)],
         "```",
         "",
         "## Kernel time (`--kernel-trace --stats`)",
@@ -253,12 +276,50 @@ def summarize_profile(base, workload="decode"):
         avg = next((float(r["AverageNs"]) / 1e3 for r in stats if r["Name"] == k), None)
         rec["kernels"][name] = dict(read_bytes=round(rd), write_bytes=round(wr), avg_us=avg)
         lines.append(f"| {k} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+    lines += sq_section(base, ours, stats)
     lines += ["", "Machine-readable copy (bench.py fills `roofline.traffic` from it while the "
               "kernel sources still hash to `source_sha256`):", "", "```json",
               json.dumps(rec, indent=1), "```"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def sq_section(base, ours, stats):
+    """MFMA and VALU activity per kernel from the SQ counter passes (if run):
+    per-dispatch averages and the usual ratios,
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs),
+      VALU busy = SQ_ACTIVE_INST_VALU x 4 / (CUs x 4 SIMDs) / GRBM_GUI_ACTIVE,
+      MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / kernel time."""
+    import collections
+    import csv
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for i in range(len(SQ_PASSES)):
+        path = f"{base}/prof_SQ{i}/p_counter_collection.csv"
+        if not os.path.exists(path):
+            return []
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                vals[row["Kernel_Name"]][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    out = ["", "## MFMA and VALU activity per dispatch (`--pmc`, two SQ passes)", "",
+           f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {DEVICE_CUS} CUs x 4 SIMDs); "
+           f"VALU busy = SQ_ACTIVE_INST_VALU x 4 / ({DEVICE_CUS} x 4) / GRBM_GUI_ACTIVE; MFMA TFLOP/s = "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / the kernel's average time (kernel trace above).", "",
+           "| kernel | GRBM_GUI_ACTIVE | MFMA busy % | VALU busy % | VALU insts | MFMA insts | MFMA TFLOP/s |",
+           "|---|---|---|---|---|---|---|"]
+    for k in sorted(vals):
+        if not k.startswith(ours):
+            continue
+        a = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        gui = a.get("GRBM_GUI_ACTIVE", 0.0)
+        mb = 100.0 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * DEVICE_CUS * 4) if gui else 0.0
+        vb = 100.0 * a.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (DEVICE_CUS * 4) / gui if gui else 0.0
+        avg = next((float(r["AverageNs"]) for r in stats if r["Name"] == k), None)
+        tf = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / (avg * 1e-9) / 1e12 if avg else 0.0
+        out.append(f"| {k} | {gui:.0f} | {mb:.2f} | {vb:.1f} | {a.get('SQ_INSTS_VALU', 0):.3g} | "
+                   f"{a.get('SQ_INSTS_MFMA', 0):.3g} | {tf:.1f} |")
+    return out
 
 
 def _timed(step, args, torch):
@@ -275,6 +336,21 @@ def _timed(step, args, torch):
     ev1.record()
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1), time.perf_counter() - t_wall
+
+
+def _step_percentiles(step, args, torch):
+    """p10 / p50 / p90 of single-step durations (HIP events around each step,
+    a separate pass after the timed one)."""
+    n = max(20, min(args.steps, 200))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record()
+    for i in range(n):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
+    return dict(steps=n, p10_us=round(float(np.percentile(us, 10)), 2),
+                p50_us=round(float(np.percentile(us, 50)), 2), p90_us=round(float(np.percentile(us, 90)), 2))
 
 
 def _kernels(step, args, torch, ds, bytes_of):
@@ -296,12 +372,12 @@ def _kernels(step, args, torch, ds, bytes_of):
     return kernels
 
 
-def _roofline(kernels, headline):
+def _roofline(kernels, workload):
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
     ach = kernels[dom]["gbs"]
     return dict(bound="hbm", kernel=dom, achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(ach / HBM_PEAK_GBS, 4),
-                traffic=counter_traffic(dom) if headline else None)
+                traffic=counter_traffic(dom, workload) if workload else None)
 
 
 def _roofline_mfma(kernels):
@@ -309,7 +385,7 @@ def _roofline_mfma(kernels):
     contraction (the teacher-forced looks), else against HBM."""
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
     if "mfma_tflops" not in kernels[dom]:
-        return _roofline(kernels, False)
+        return _roofline(kernels, None)
     ach = kernels[dom]["mfma_tflops"]
     return dict(bound="mfma", kernel=dom, achieved=ach, peak=MFMA_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / MFMA_BF16_TFLOPS, 4), traffic=None)
@@ -438,8 +514,16 @@ def run_decode(args, torch, ds):
     S = int((inp["mode"] != 0).sum())
     R = int((vf_out["accept_len"] < g).sum().item())
     kernels = _kernels(step, args, torch, ds, lambda n: kernel_bytes(n, B, g, V, r, d, S, R))
-    roofline = _roofline(kernels, headline)
+    roofline = _roofline(kernels, args.workload)
     step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
+    pct = _step_percentiles(step, args, torch)
+    # decode-path rates from the per-kernel event times: verify alone, and
+    # Markov + verify (the statistics are the training side of the path)
+    t_of = lambda pre: sum(k["avg_us"] * k["launches_per_step"] for n, k in kernels.items()
+                           if n.startswith(pre))
+    t_verify, t_markov, t_stats = t_of("verify"), t_of("markov"), t_of("stats")
+    acc = vf_out["accept_len"].double().cpu().numpy()
+    reached = acc + (acc < g)  # proposals whose accept test ran
 
     cpu = None
     if not args.no_cpu:
@@ -455,9 +539,16 @@ def run_decode(args, torch, ds):
                             temperature=1.0 if headline else "per request", truncation=truncation,
                             mode=modes, rotated_batches=len(sets), markov_plan=args.markov_plan),
                 roofline=roofline, cpu_baseline=cpu,
+                verified_rows_s=round(B * (g + 1) / (t_verify * 1e-6), 1),
+                step_rows_s=round(B * (g + 1) / ((t_markov + t_verify) * 1e-6), 1),
+                step_us=dict(**pct, markov_us=round(t_markov, 2), verify_us=round(t_verify, 2),
+                             stats_us=round(t_stats, 2), width_us=round(t_of("select_width"), 2)),
+                acceptance=dict(mean_accept_len=round(float(acc.mean()), 4),
+                                accepted_per_proposal=round(float(acc.mean()) / g, 4),
+                                per_position_accept_rate=round(float(acc.sum() / max(reached.sum(), 1)), 4),
+                                tokens_per_step=round(float(acc.mean()) + 1.0, 4)),
                 step=dict(alg_bytes=int(step_bytes),
                           alg_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                          accept_rate=round(float(vf_out["accept_len"].float().mean().item()) / g, 4),
                           **(dict(mean_width=round(float(wd_out["n_draft"].float().mean().item()), 3),
                                   cost_us=ADAPTIVE_COST_US) if adaptive else {}),
                           kernels=kernels))
@@ -521,7 +612,7 @@ def run_stats(args, torch, ds):
                 config=dict(workload="training acceptance statistics" +
                             (" and their gradient" if train else ""), N=N, gamma=g, V=V,
                             logits="bf16", rotated_batches=len(sets)),
-                roofline=_roofline(kernels, False), cpu_baseline=cpu,
+                roofline=_roofline(kernels, args.workload), cpu_baseline=cpu,
                 step=dict(kernels=kernels))
 
 
@@ -572,8 +663,39 @@ def run_markov_stats(args, torch, ds):
                 step=dict(kernels=kernels, bias_gflop_per_look=round(flops / 1e9, 1)))
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def _oracle_step(O, sub):
+    """One pass of the whole path through the oracle on a request subset."""
+    g = sub["gamma"]
+    mk = O.markov_sample(sub)
+    q = dict(q_z=mk["q_z"].astype(np.float32), q_lse=mk["q_lse"].astype(np.float32),
+             q_thr=mk["q_thr"].astype(np.float32), q_tok=mk["q_tok"].astype(np.float32))
+    O.verify(sub, mk["draft_tokens"], **q)
+    n = sub["B"]
+    O.accept_stats(dict(draft=sub["backbone"], target=np.ascontiguousarray(sub["target"][:, :g]),
+                        teacher=np.zeros((n, g), np.int32), conf_logits=np.zeros((n, g), np.float32),
+                        block_mask=None, N=n, gamma=g, V=sub["V"], dtype=sub["dtype"]))
+
+
 def cpu_baseline(inp, nreq, cfg_name="decode"):
-    """The oracle on the first nreq requests of the batch, single-threaded."""
+    """The oracle (single-threaded C++) on the first nreq requests of the
+    batch: once on one core, then with the requests split over one thread per
+    host core (up to 16, the machine's CPU share); the oracle's calls release the
+    GIL, so the threads run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import oracle as O
     from workloads import decode_inputs
 
@@ -582,18 +704,25 @@ def cpu_baseline(inp, nreq, cfg_name="decode"):
     sub["embed"] = inp["embed"]
     g = sub["gamma"]
     t = time.perf_counter()
-    mk = O.markov_sample(sub)
-    q = dict(q_z=mk["q_z"].astype(np.float32), q_lse=mk["q_lse"].astype(np.float32),
-             q_thr=mk["q_thr"].astype(np.float32), q_tok=mk["q_tok"].astype(np.float32))
-    O.verify(sub, mk["draft_tokens"], **q)
-    st = dict(draft=sub["backbone"], target=np.ascontiguousarray(sub["target"][:, :g]),
-              teacher=np.zeros((nreq, g), np.int32), conf_logits=np.zeros((nreq, g), np.float32),
-              block_mask=None, N=nreq, gamma=g, V=sub["V"], dtype=sub["dtype"])
-    O.accept_stats(st)
+    _oracle_step(O, sub)
     sec = time.perf_counter() - t
+    nth = max(1, min(16, os.cpu_count() or 1, nreq))
+    parts = [reqs[i::nth] for i in range(nth)]
+    subs = []
+    for pr in parts:
+        sp = decode_inputs(cfg_name, requests=pr, with_embed=False)
+        sp["embed"] = inp["embed"]
+        subs.append(sp)
+    t = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nth) as ex:
+        list(ex.map(lambda sp: _oracle_step(O, sp), subs))
+    sec_t = time.perf_counter() - t
     return dict(value=round(nreq * (g + 1) / sec, 2), unit="rows/s", cores=1, kind="oracle",
                 sample=f"{nreq} of the {inp['B']} requests (Markov sample + verify + accept "
-                       f"stats), {sec:.1f}s single-threaded")
+                       f"stats), {sec:.1f}s single-threaded",
+                cpu_model=cpu_model(),
+                threaded=dict(value=round(nreq * (g + 1) / sec_t, 2), unit="rows/s", cores=nth,
+                              sample=f"the same {nreq} requests over {nth} threads, {sec_t:.1f}s"))
 
 
 if __name__ == "__main__":
