@@ -149,6 +149,7 @@ PROFILES = {
 SQ_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
              ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_WAVE_CYCLES"))
 DEVICE_CUS = 256
+DEVICE_XCDS = 8  # GRBM_GUI_ACTIVE is summed over the XCDs
 CSRC = os.path.join(ROOT, "dspark_draft_sampling_amd", "csrc")
 
 
@@ -287,10 +288,12 @@ def summarize_profile(base, workload="decode"):
 
 def sq_section(base, ours, stats):
     """MFMA and VALU activity per kernel from the SQ counter passes (if run):
-    per-dispatch averages and the usual ratios,
-      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs),
-      VALU busy = SQ_ACTIVE_INST_VALU x 4 / (CUs x 4 SIMDs) / GRBM_GUI_ACTIVE,
-      MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / kernel time."""
+    per-dispatch averages and the usual ratios, with c = GRBM_GUI_ACTIVE /
+    XCDs the kernel's active cycles (the counter is summed over the XCDs),
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (c x CUs x 4 SIMDs),
+      VALU busy = SQ_ACTIVE_INST_VALU x 4 / (CUs x 4 SIMDs) / c,
+      MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / kernel time
+    (the last cross-checks the first: one MFMA MOP is 512 flops)."""
     import collections
     import csv
 
@@ -303,9 +306,11 @@ def sq_section(base, ours, stats):
             for row in csv.DictReader(fh):
                 vals[row["Kernel_Name"]][row["Counter_Name"]].append(float(row["Counter_Value"]))
     out = ["", "## MFMA and VALU activity per dispatch (`--pmc`, two SQ passes)", "",
-           f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {DEVICE_CUS} CUs x 4 SIMDs); "
-           f"VALU busy = SQ_ACTIVE_INST_VALU x 4 / ({DEVICE_CUS} x 4) / GRBM_GUI_ACTIVE; MFMA TFLOP/s = "
-           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / the kernel's average time (kernel trace above).", "",
+           f"With c = GRBM_GUI_ACTIVE / {DEVICE_XCDS} (the counter is summed over the {DEVICE_XCDS} XCDs): "
+           f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (c x {DEVICE_CUS} CUs x 4 SIMDs); "
+           f"VALU busy = SQ_ACTIVE_INST_VALU x 4 / ({DEVICE_CUS} x 4) / c; MFMA TFLOP/s = "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / the kernel's average time (kernel trace above), which "
+           "cross-checks MFMA busy against the 2.5 PFLOP/s dense bf16 peak.", "",
            "| kernel | GRBM_GUI_ACTIVE | MFMA busy % | VALU busy % | VALU insts | MFMA insts | MFMA TFLOP/s |",
            "|---|---|---|---|---|---|---|"]
     for k in sorted(vals):
@@ -313,8 +318,9 @@ def sq_section(base, ours, stats):
             continue
         a = {c: sum(v) / len(v) for c, v in vals[k].items()}
         gui = a.get("GRBM_GUI_ACTIVE", 0.0)
-        mb = 100.0 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * DEVICE_CUS * 4) if gui else 0.0
-        vb = 100.0 * a.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (DEVICE_CUS * 4) / gui if gui else 0.0
+        cyc = gui / DEVICE_XCDS
+        mb = 100.0 * a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * DEVICE_CUS * 4) if gui else 0.0
+        vb = 100.0 * a.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (DEVICE_CUS * 4) / cyc if gui else 0.0
         avg = next((float(r["AverageNs"]) for r in stats if r["Name"] == k), None)
         tf = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / (avg * 1e-9) / 1e12 if avg else 0.0
         out.append(f"| {k} | {gui:.0f} | {mb:.2f} | {vb:.1f} | {a.get('SQ_INSTS_VALU', 0):.3g} | "

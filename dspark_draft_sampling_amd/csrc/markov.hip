@@ -28,12 +28,15 @@
 //    Workgroup g owns the 512 tokens [512 g, 512 g + 512) and keeps their W2
 //    rows in registers (the MFMA A fragments) for the whole call, so the
 //    rank-r factor is read from HBM once per call rather than once per step.
-//    A finalize starts when its request's chunk records of the step are all
+//    A finalize starts when its request's records of the step are all
 //    stored (polled, no grid barrier) and hands x_k to the next stream phase
-//    through draft_tokens (both cleared before the launch).  Everything that
-//    crosses workgroups inside the launch (chunk records, z rows read by the
-//    draw, x_k) is stored and loaded at device scope (sc1), so no L2
-//    writeback or invalidate is needed.
+//    through tagged words in the workspace: every word that crosses
+//    workgroups carries the call's epoch, so nothing is cleared before the
+//    launch.  Everything that crosses workgroups inside the launch (records,
+//    z rows read by the draw, x_k) is stored and loaded at device scope
+//    (sc1), so no L2 writeback or invalidate is needed.  Without truncation
+//    arrays the untruncated kernel (markov_fast) draws a candidate in every
+//    workgroup and the finalize only compares records.
 //  * per step: 2 gamma launches (stream kernel over all chunks, finalize
 //    kernel over all requests), used when the fused grid cannot be resident
 //    at once (V above 512 tokens per compute unit).
