@@ -282,7 +282,6 @@ def dspark_verify(target, draft_tokens, policy: Policy, q_logits=None, q_lse=Non
     return out
 
 
-
 def dspark_verify_noalloc(target, draft_tokens, policy: Policy, out, q_logits=None, q_lse=None,
                           q_thr=None, q_tok=None, n_draft=None, seed=0):
     """dspark_verify on the library's own per-GPU scratch: no workspace and no
@@ -311,6 +310,7 @@ def dspark_verify_noalloc(target, draft_tokens, policy: Policy, out, q_logits=No
                                      _stream(dev))
     _check(rc)
     return out
+
 
 _STATS_OUT = ["l1", "accept_rate", "ce", "bce"]
 
