@@ -97,7 +97,7 @@ MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d
 struct StatsPlan {
   int sliced;  // 1: (row pair, segment) item kernels; 0: one workgroup per row pair
   int P;       // segments per row pair
-  size_t off_part, off_l1, off_cnt, bytes;
+  size_t off_part, off_l1, off_pk, off_cnt, bytes;
 };
 StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 

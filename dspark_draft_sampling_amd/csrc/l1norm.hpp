@@ -111,7 +111,8 @@ __device__ __forceinline__ float expm1_series(float r) { return r * fmaf(r, fmaf
 // T - D of one element pair under a common shift; d = t = -inf gives 0.
 __device__ __forceinline__ float np_diff(float d, float t, float D, float T) {
   const float r = t - d;
-  return fabsf(r) < kSeriesBand ? D * expm1_series(r) : T - D;
+  const float near = D * expm1_series(r), far = T - D;
+  return fabsf(r) < kSeriesBand ? near : far;
 }
 
 // Accumulate one element pair into a part's sums under shifts (a2d, a2t);

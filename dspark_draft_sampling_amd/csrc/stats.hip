@@ -18,13 +18,15 @@
 // |P_v - T_v| in the form that keeps relative accuracy when the rows nearly
 // agree.
 //   row path (>= 2048 pairs, or rows not 16-byte aligned): one persistent
-//     workgroup of 16 waves per compute unit takes a pair at a time, its
+//     workgroup of 8 waves per compute unit takes a pair at a time, its
 //     waves striding over the pair's segments; the parts merge through LDS.
-//   sliced path (small batches): items (pair, segment) spread over the GPU;
-//     stats_part1 writes each item's part; stats_part2 merges the pair's
-//     parts in registers (one wave per item), sums the item's share of L1
-//     and takes a ticket on the pair: the pair's last item writes the
-//     outputs, and the wave finishing the last pair writes tau and the sums.
+//   sliced path (small batches): items (pair, segment) spread over a grid
+//     that is resident at once; stats_part1 writes each item's part;
+//     stats_part2 gives each wave a contiguous run of items, merges a pair's
+//     parts once per run, stores each item's share of L1, and at the end of
+//     the run adds its item count to each pair's ticket: the wave completing
+//     a pair writes the pair's outputs, the one completing the last pair tau
+//     and the sums.
 // stats_reduce (row path): one workgroup computes tau and the sums in fp64 in
 // a fixed order, so the sums are deterministic.
 #include <algorithm>
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void stats_part1_kernel(
     int32_t ncounters) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
-  // the ticket counters of the second look start at zero
+  // the ticket counters of the later kernels start at zero
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < ncounters; i += kThreads) counters[i * kTicketStride] = 0u;
   const int nwaves = gridDim.x * kWaves;
@@ -328,40 +330,67 @@ __global__ __launch_bounds__(kThreads) void stats_part1_kernel(
   }
 }
 
+struct StatsOut {
+  const int32_t* teacher;
+  const float* conf_logits;
+  const uint8_t* block_mask;
+  int32_t N, gamma;
+  float w_ce, w_l1, w_conf;
+  float* l1;
+  float* accept_rate;
+  float* ce;
+  float* bce;
+  float* tau;
+  float* sums;
+  uint32_t* counters;  // per pair: items done; then pairs done (kTicketStride apart)
+};
+
 // Per-block tau and the loss / report sums by one wave, in fp64 and a fixed
 // order (lane l owns blocks l, l + 64, ...; then a fixed butterfly), so the
 // sums are deterministic.  The per-position values were stored by other
-// waves of the same launch (device-scope loads).
+// waves of the same launch (device-scope loads, four positions' at a time in
+// flight).
 __device__ void wave_batch_reduce(const float* __restrict__ l1, const float* __restrict__ accept_rate,
                                   const float* __restrict__ ce, const float* __restrict__ bce,
                                   const uint8_t* __restrict__ block_mask, int32_t N,
                                   int32_t gamma, float w_ce, float w_l1, float w_conf,
                                   float* __restrict__ tau, float* __restrict__ sums) {
   constexpr int Q = 8;  // num, tokens, l1, accept, tau, blocks, ce, bce
+  constexpr int kG = 4;  // positions per group of loads
   const int lane = threadIdx.x & 63;
-  // w_k = exp(-k / gamma) = r^k (k 1-based), r to fp32 accuracy
-  const double r = static_cast<double>(expf(-1.0f / static_cast<float>(gamma)));
+  // w_k = exp(-k / gamma) (k 1-based) as powers of exp(-1 / gamma), in fp64
+  const double r = exp(-1.0 / gamma);
   double acc[Q] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int b = lane; b < N; b += 64) {
     const size_t base = static_cast<size_t>(b) * gamma;
     const bool m = block_mask ? block_mask[b] != 0 : true;
     double cum = 1.0, t = 1.0, wk = 1.0;
-    for (int k = 0; k < gamma; ++k) {
-      const float a = load_coherent(accept_rate + base + k);
-      const float c = load_coherent(ce + base + k);
-      const float l = load_coherent(l1 + base + k);
-      const float x = load_coherent(bce + base + k);
-      cum *= a;
-      t += cum;
-      wk *= r;
-      if (m) {
-        acc[0] += wk * (w_ce * static_cast<double>(c) + w_l1 * static_cast<double>(l) +
-                        w_conf * static_cast<double>(x));
-        acc[1] += 1.0;
-        acc[2] += l;
-        acc[3] += a;
-        acc[6] += c;
-        acc[7] += x;
+    for (int k0 = 0; k0 < gamma; k0 += kG) {
+      float a[kG], c[kG], l[kG], x[kG];
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        const size_t i = base + static_cast<size_t>(min(k0 + j, gamma - 1));
+        a[j] = load_coherent(accept_rate + i);
+        c[j] = load_coherent(ce + i);
+        l[j] = load_coherent(l1 + i);
+        x[j] = load_coherent(bce + i);
+      }
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        if (k0 + j < gamma) {
+          cum *= a[j];
+          t += cum;
+          wk *= r;
+          if (m) {
+            acc[0] += wk * (w_ce * static_cast<double>(c[j]) + w_l1 * static_cast<double>(l[j]) +
+                            w_conf * static_cast<double>(x[j]));
+            acc[1] += 1.0;
+            acc[2] += l[j];
+            acc[3] += a[j];
+            acc[6] += c[j];
+            acc[7] += x[j];
+          }
+        }
       }
     }
     tau[b] = static_cast<float>(t);
@@ -391,75 +420,129 @@ __device__ void wave_batch_reduce(const float* __restrict__ l1, const float* __r
   }
 }
 
-struct StatsOut {
-  const int32_t* teacher;
-  const float* conf_logits;
-  const uint8_t* block_mask;
-  int32_t N, gamma;
-  float w_ce, w_l1, w_conf;
-  float* l1;
-  float* accept_rate;
-  float* ce;
-  float* bce;
-  float* tau;
-  float* sums;
-  uint32_t* counters;  // per pair: segments done; then pairs done (kTicketStride apart)
-};
+// Look 2 of the sliced path, and its outputs.  Each wave takes a contiguous
+// run of items (so mostly one or two pairs), forms a pair's constants once
+// per run from its part1 records, and stores each item's share of the L1
+// sum; a pair's first item also stores the pair's constants.  Inside the run
+// nothing waits on another wave, so the next item's loads stay in flight the
+// whole time.  At the end of its run the wave adds the number of items it did
+// to each pair's ticket; the wave that completes a pair writes the pair's
+// outputs (stats_finish_pair), and the wave that completes the last pair
+// writes tau and the sums.
+template <typename T>
+__device__ void stats_finish_pair(const T* __restrict__ draft, int32_t V, int32_t P, int32_t npairs, int pair,
+                                  const float* __restrict__ l1part, const PairK* __restrict__ pk,
+                                  const StatsOut& o) {
+  const int lane = threadIdx.x & 63;
+  // the pair's constants (10 words, one a lane) and the item shares were
+  // stored by other waves of this launch: device-scope loads
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(pk + pair);
+  const uint32_t kv = lane < static_cast<int>(sizeof(PairK) / 4) ? load_coherent(kw + lane) : 0u;
+  const int32_t tch = clamp_token(o.teacher[pair], V);
+  const float cl = o.conf_logits[pair];
+  const float xt = load_logit(draft + static_cast<size_t>(pair) * V, tch);
+  float A = 0.0f;
+  for (int i = lane; i < P; i += 64) A += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
+  A = wave_sum(A);
+  PairK k;
+  uint32_t* kd = reinterpret_cast<uint32_t*>(&k);
+#pragma unroll
+  for (int w = 0; w < static_cast<int>(sizeof(PairK) / 4); ++w) kd[w] = __builtin_amdgcn_readlane(kv, w);
+  uint32_t last = 0;
+  if (lane == 0) {
+    const float L1 = l1_final(k, A);
+    const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
+    store_coherent(o.l1 + pair, L1);
+    store_coherent(o.accept_rate + pair, av);
+    store_coherent(o.ce + pair, k.lse_d - xt);
+    store_coherent(o.bce + pair, bce_of(cl, av));
+    last = publish(o.counters + static_cast<size_t>(npairs) * kTicketStride) ==
+                   static_cast<uint32_t>(npairs - 1)
+               ? 1u
+               : 0u;
+  }
+  if (uniform_i(static_cast<int>(last)))
+    wave_batch_reduce(o.l1, o.accept_rate, o.ce, o.bce, o.block_mask, o.N, o.gamma, o.w_ce,
+                      o.w_l1, o.w_conf, o.tau, o.sums);
+}
 
-// Per item: the pair's constants from all its part1 records, then the item's
-// share of the pair's L1 sum (seg_l1), with a ticket on the pair: the pair's
-// last item writes L1, accept_rate, CE and BCE, and the wave finishing the
-// last pair writes tau and the sums.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void stats_part2_kernel(
     const T* __restrict__ draft, const T* __restrict__ target, int32_t V, int32_t P,
-    int32_t items, const NormPart* __restrict__ part, float* __restrict__ l1part, StatsOut o) {
+    int32_t items, const NormPart* __restrict__ part, float* __restrict__ l1part,
+    PairK* __restrict__ pk, StatsOut o) {
   constexpr int SEG = stat_seg<T>();
   const int lane = threadIdx.x & 63;
-  const int nwaves = gridDim.x * kWaves;
   const int npairs = items / P;
-  for (int item = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6); item < items;
-       item += nwaves) {
-    const int it_ = uniform_i(item);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t per = (items + nwaves - 1) / nwaves;
+  int item = uniform_i(static_cast<int>(std::min<int64_t>(items, wv * per)));
+  const int end = static_cast<int>(std::min<int64_t>(items, wv * per + per));
+  if (item >= end) return;
+  // two register buffers: an item's segment (and, for the first item of a
+  // pair in the run, its pair_r5 and the lane's first part record) travel
+  // together, one item ahead
+  uint4 ad[kSegIters], at[kSegIters], bd[kSegIters], bt[kSegIters];
+  float ra = 0.0f, rb = 0.0f;
+  NormPart pa = np_empty(), pb = np_empty();
+  const int first = item;
+  auto load = [&](int it_, uint4* ud, uint4* ut, float& r5, NormPart& pr) {
     const int pair = it_ / P, seg = it_ - pair * P;
     const size_t off = static_cast<size_t>(pair) * V;
-    uint4 ud[kSegIters], ut[kSegIters];
-    const float r5 = pair_r5(draft + off, target + off, V, lane);
+    if (seg == 0 || it_ == first) {
+      r5 = pair_r5(draft + off, target + off, V, lane);
+      pr = lane < P ? part[static_cast<size_t>(pair) * P + lane] : np_empty();
+    }
     seg_load<T, true>(draft + off, target + off, V, seg * SEG, lane, ud, ut);
-    PairK k = pair_k(pair_merge(part + static_cast<size_t>(pair) * P, P, lane));
-    k.K = pair_k5(r5);
+  };
+  PairK k{};
+  int kpair = -1;
+  auto reduce = [&](uint4* ud, uint4* ut, float r5, NormPart pr, int it_) {
+    const int pair = it_ / P, seg = it_ - pair * P;
+    if (pair != kpair) {
+      for (int i = lane + 64; i < P; i += 64) pr = np_merge(pr, part[static_cast<size_t>(pair) * P + i]);
+      k = pair_k(np_wave_merge(pr));
+      k.K = pair_k5(r5);
+      kpair = pair;
+    }
     seg_mask<T, true>(V, seg * SEG, lane, ud, ut);
     float a = 0.0f;
     seg_l1<T>(ud, ut, k, a);
     a = wave_sum(a);
-    uint32_t ticket = 0;
     if (lane == 0) {
       store_coherent(l1part + it_, a);
-      ticket = publish(o.counters + static_cast<size_t>(pair) * kTicketStride);
+      if (seg == 0) {
+        const uint32_t* kd = reinterpret_cast<const uint32_t*>(&k);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(pk + pair);
+#pragma unroll
+        for (int w = 0; w < static_cast<int>(sizeof(PairK) / 4); ++w) store_coherent(dst + w, kd[w]);
+      }
     }
-    ticket = uniform_i(static_cast<int>(ticket));
-    if (ticket != static_cast<uint32_t>(P - 1)) continue;
-    // the pair's last item: its L1 from the item shares (fixed order)
-    float A = 0.0f;
-    for (int i = lane; i < P; i += 64) A += load_coherent(l1part + static_cast<size_t>(pair) * P + i);
-    A = wave_sum(A);
-    uint32_t last = 0;
+  };
+  load(item, ad, at, ra, pa);
+  while (true) {
+    const int n1 = item + 1;
+    load(n1 < end ? n1 : item, bd, bt, rb, pb);
+    reduce(ad, at, ra, pa, item);
+    if (n1 >= end) break;
+    const int n2 = n1 + 1;
+    load(n2 < end ? n2 : n1, ad, at, ra, pa);
+    reduce(bd, bt, rb, pb, n1);
+    if (n2 >= end) break;
+    item = n2;
+  }
+  // the pairs of the run: add this wave's item count to each pair's ticket
+  for (int pair = first / P; pair <= (end - 1) / P; ++pair) {
+    const int lo = std::max(first, pair * P), hi = std::min(end, pair * P + P);
+    uint32_t done = 0;
     if (lane == 0) {
-      const float L1 = l1_final(k, A);
-      const float av = fminf(1.0f, fmaxf(0.0f, 1.0f - 0.5f * L1));
-      const int32_t tch = clamp_token(o.teacher[pair], V);
-      store_coherent(o.l1 + pair, L1);
-      store_coherent(o.accept_rate + pair, av);
-      store_coherent(o.ce + pair, k.lse_d - load_logit(draft + off, tch));
-      store_coherent(o.bce + pair, bce_of(o.conf_logits[pair], av));
-      last = publish(o.counters + static_cast<size_t>(npairs) * kTicketStride) ==
-                     static_cast<uint32_t>(npairs - 1)
-                 ? 1u
-                 : 0u;
+      __builtin_amdgcn_s_waitcnt(0);
+      done = __hip_atomic_fetch_add(o.counters + static_cast<size_t>(pair) * kTicketStride,
+                                    static_cast<uint32_t>(hi - lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+             static_cast<uint32_t>(hi - lo);
     }
-    if (uniform_i(static_cast<int>(last)))
-      wave_batch_reduce(o.l1, o.accept_rate, o.ce, o.bce, o.block_mask, o.N, o.gamma, o.w_ce,
-                        o.w_l1, o.w_conf, o.tau, o.sums);
+    if (uniform_i(static_cast<int>(done)) == P) stats_finish_pair<T>(draft, V, P, npairs, pair, l1part, pk, o);
   }
 }
 
@@ -845,6 +928,24 @@ int device_cus_cached() {
   return cus;
 }
 
+// Workgroups of kThreads of an item kernel resident per compute unit (a
+// property of the code object), cached per kernel; at least 1.
+int resident_blocks(const void* fn, std::atomic<int>& cache) {
+  int nb = cache.load(std::memory_order_relaxed);
+  if (nb > 0) return nb;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb <= 0) nb = 1;
+  cache.store(nb, std::memory_order_relaxed);
+  return nb;
+}
+
+// Grid of an item kernel: every wave resident at once (each then walks its
+// items with the next one's loads in flight), no more waves than items.
+int item_grid(int items, const void* fn, std::atomic<int>& cache) {
+  const int64_t res = static_cast<int64_t>(device_cus_cached()) * resident_blocks(fn, cache);
+  const int64_t need = (static_cast<int64_t>(items) + kWaves - 1) / kWaves;
+  return static_cast<int>(std::max<int64_t>(1, std::min(need, res)));
+}
+
 template <typename T>
 hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
                         const float* conf_logits, const uint8_t* block_mask, int32_t N,
@@ -859,15 +960,18 @@ hipError_t launch_typed(const T* draft, const T* target, const int32_t* teacher,
     char* w = static_cast<char*>(ws);
     NormPart* part = reinterpret_cast<NormPart*>(w + pl.off_part);
     float* l1part = reinterpret_cast<float*>(w + pl.off_l1);
+    PairK* pk = reinterpret_cast<PairK*>(w + pl.off_pk);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(w + pl.off_cnt);
     const int items = npairs * pl.P;
-    const int wgs = std::min(kItemMaxWGs, (items + kWaves - 1) / kWaves);
-    DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
-                  target, V, pl.P, items, part, cnt, npairs + 1);
+    static std::atomic<int> occ1{0}, occ2{0};
+    const int wg1 = item_grid(items, reinterpret_cast<const void*>(&stats_part1_kernel<T>), occ1);
+    const int wg2 = item_grid(items, reinterpret_cast<const void*>(&stats_part2_kernel<T>), occ2);
     const StatsOut o{teacher, conf_logits, block_mask, N, gamma, w_ce, w_l1, w_conf,
                      l1, accept_rate, ce, bce, tau, sums, cnt};
-    DSPARK_LAUNCH("stats_part2", (stats_part2_kernel<T>), dim3(wgs), dim3(kThreads), 0, st, draft,
-                  target, V, pl.P, items, part, l1part, o);
+    DSPARK_LAUNCH("stats_part1", (stats_part1_kernel<T>), dim3(wg1), dim3(kThreads), 0, st, draft,
+                  target, V, pl.P, items, part, cnt, npairs + 1);
+    DSPARK_LAUNCH("stats_part2", (stats_part2_kernel<T>), dim3(wg2), dim3(kThreads), 0, st, draft,
+                  target, V, pl.P, items, part, l1part, pk, o);
     return hipGetLastError();
   } else if (npairs > 0) {
     const dim3 grid(static_cast<unsigned>(std::min(npairs, device_cus_cached())));
@@ -989,7 +1093,9 @@ StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V) {
     off = align_up(off + items * sizeof(NormPart), 256);
     p.off_l1 = off;  // per item: share of the L1 sum
     off = align_up(off + items * sizeof(float), 256);
-    p.off_cnt = off;
+    p.off_pk = off;  // per pair: the constants of look 2 and the final
+    off = align_up(off + static_cast<size_t>(npairs) * sizeof(PairK), 256);
+    p.off_cnt = off;  // per pair: items done; then pairs done (cleared by stats_part1)
     off = align_up(off + (static_cast<size_t>(npairs) + 1) * kTicketStride * sizeof(uint32_t), 256);
   }
   p.bytes = off;
