@@ -104,6 +104,12 @@ StatsPlan plan_stats(int32_t N, int32_t gamma, int32_t V);
 // Compute units of the current device (cached per device; stats.hip).
 int device_cus();
 
+// Grid of a kernel (workgroups of `threads`) whose waves each walk a run of
+// items: every workgroup resident at once, at most one wave per item.  The
+// resident count per compute unit is a property of the code object, cached
+// in `cache` (stats.hip).
+int resident_grid(const void* fn, int threads, int64_t items, std::atomic<int>& cache);
+
 // Batch reduction of the per-position statistics (tau and the sums), shared by
 // the statistics calls (stats.hip).
 hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,

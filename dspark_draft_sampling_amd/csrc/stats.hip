@@ -928,22 +928,11 @@ int device_cus_cached() {
   return cus;
 }
 
-// Workgroups of kThreads of an item kernel resident per compute unit (a
-// property of the code object), cached per kernel; at least 1.
-int resident_blocks(const void* fn, std::atomic<int>& cache) {
-  int nb = cache.load(std::memory_order_relaxed);
-  if (nb > 0) return nb;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb <= 0) nb = 1;
-  cache.store(nb, std::memory_order_relaxed);
-  return nb;
-}
-
-// Grid of an item kernel: every wave resident at once (each then walks its
-// items with the next one's loads in flight), no more waves than items.
+// Grid of an item kernel of kThreads: every wave resident at once (each then
+// walks its items with the next one's loads in flight), no more waves than
+// items.
 int item_grid(int items, const void* fn, std::atomic<int>& cache) {
-  const int64_t res = static_cast<int64_t>(device_cus_cached()) * resident_blocks(fn, cache);
-  const int64_t need = (static_cast<int64_t>(items) + kWaves - 1) / kWaves;
-  return static_cast<int>(std::max<int64_t>(1, std::min(need, res)));
+  return resident_grid(fn, kThreads, items, cache);
 }
 
 template <typename T>
@@ -1028,6 +1017,18 @@ hipError_t launch_backward_typed(const T* draft, const T* target, int32_t N, int
 }  // namespace
 
 int device_cus() { return device_cus_cached(); }
+
+int resident_grid(const void* fn, int threads, int64_t items, std::atomic<int>& cache) {
+  int nb = cache.load(std::memory_order_relaxed);
+  if (nb <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess || nb <= 0) nb = 1;
+    cache.store(nb, std::memory_order_relaxed);
+  }
+  const int64_t res = static_cast<int64_t>(device_cus_cached()) * nb;
+  const int64_t wpb = threads / 64;
+  const int64_t need = (items + wpb - 1) / wpb;
+  return static_cast<int>(std::max<int64_t>(1, std::min(need, res)));
+}
 
 hipError_t launch_stats_reduce(const float* l1, const float* accept_rate, const float* ce, const float* bce,
                                const uint8_t* block_mask, int32_t N, int32_t gamma, float w_ce, float w_l1,

@@ -14,13 +14,13 @@
 //     argmax, sum) with DPP only (no LDS, no barrier); the next item's loads
 //     are in flight while the current one is reduced.
 //  2. verify_decide grid (chunk slices, B).  Every workgroup of a request
-//     combines the segment partials of its rows and replays the accept scan
-//     (one thread per proposal, first reject by ballot), so all of them agree
-//     on the row to sample from.  Each then scores its slice of 256-token
-//     chunks (level 1 of the library's three-level Gumbel-max draw); the last
-//     workgroup to finish (atomic ticket, armed by launch 1) picks the chunk,
-//     then the 16-token sub-chunk and the token inside it (levels 2 and 3),
-//     and writes the outputs.
+//     combines the segment partials of its rows (all records loaded at once)
+//     and replays the accept scan (one thread per proposal, first reject by
+//     ballot), so all of them agree on the row to sample from.  Each then
+//     scores its slice of 256-token chunks (level 1 of the library's
+//     three-level Gumbel-max draw); the last workgroup to finish (atomic
+//     ticket, armed by launch 1) picks the chunk, then the 16-token sub-chunk
+//     and the token inside it (levels 2 and 3), and writes the outputs.
 //
 // Sums use an integer base-2 shift: s = sum 2^(l cT - M2), cT = log2(e) / T,
 // M2 = floor(max(l) cT).  Partials with different shifts combine by exact
@@ -42,6 +42,8 @@ constexpr int kScalarIters = 32;   // scalar loads per lane per segment
 constexpr int kChunksPerWave = 8;  // chunks one wave scores in the decide pass
 constexpr int kChunksPerWG = kChunksPerWave * kWaves;
 constexpr int kRowsMaxWGs = 4096;  // grid of the row pass: up to 16 waves per SIMD
+constexpr int kRowsPerWave = (DSPARK_MAX_GAMMA + 1 + kWaves - 1) / kWaves;  // decide: rows a wave combines
+constexpr int kPartRegs = 2;  // decide: segment records per lane and row held in registers
 
 // One 16-byte load per lane per iteration (vector path: 8 bf16 or 4 fp32
 // logits kept packed in a uint4), or one scalar logit (scalar path).  Lanes
@@ -524,27 +526,10 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
     }
   }
 
-  // 1. combine the segment partials of rows 0..n_d (wave w: rows w, w+4, ...)
-  for (int r = wave; r <= nd; r += kWaves) {
-    const RowPart* p = part + static_cast<size_t>(b * G1 + r) * P;
-    ArgMax am{neg_inf(), INT32_MAX};
-    uint32_t fl = 0;
-    for (int i = lane; i < P; i += 64) {
-      const RowPart q = p[i];
-      am = better(am, ArgMax{q.m, q.arg});
-      fl |= q.flags;
-    }
-    am = wave_argmax(am);
-    fl = wave_or(fl);
-    const float M2 = (am.v > neg_inf() && am.v < pos_inf()) ? shift_of(am.v, cT) : 0.0f;
-    float s = 0.0f;
-    if (sampled && am.v > neg_inf()) {
-      for (int i = lane; i < P; i += 64) {
-        const RowPart q = p[i];
-        if (q.m > neg_inf()) s += q.s * __builtin_amdgcn_exp2f(shift_of(q.m, cT) - M2);
-      }
-      s = wave_sum(s);
-    }
+  // 1. combine the segment partials of rows 0..n_d (wave w: rows w, w+4, ...).
+  // With at most 64 kPartRegs segments a row, every record of the wave's rows
+  // is loaded before any is reduced; longer rows loop over their records.
+  auto row_out = [&](int r, ArgMax am, uint32_t fl, float M2, float s) {
     if (lane == 0) {
       if (!(am.v > neg_inf())) fl |= DSPARK_FLAG_EMPTY_ROW;
       float thr = neg_inf();
@@ -559,6 +544,65 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(
       rM2[r] = M2;
       rarg[r] = am.i;
       rfl[r] = fl;
+    }
+  };
+  if (P <= 64 * kPartRegs) {
+    RowPart q[kRowsPerWave][kPartRegs];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = wave + kWaves * j;
+#pragma unroll
+      for (int h = 0; h < kPartRegs; ++h) {
+        const int i = lane + 64 * h;
+        q[j][h] = (r <= nd && i < P) ? part[static_cast<size_t>(b * G1 + r) * P + i]
+                                     : RowPart{neg_inf(), 0.0f, INT32_MAX, 0u};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = wave + kWaves * j;
+      if (r > nd) break;
+      ArgMax am{neg_inf(), INT32_MAX};
+      uint32_t fl = 0;
+#pragma unroll
+      for (int h = 0; h < kPartRegs; ++h) {
+        am = better(am, ArgMax{q[j][h].m, q[j][h].arg});
+        fl |= q[j][h].flags;
+      }
+      am = wave_argmax(am);
+      fl = wave_or(fl);
+      const float M2 = (am.v > neg_inf() && am.v < pos_inf()) ? shift_of(am.v, cT) : 0.0f;
+      float s = 0.0f;
+      if (sampled && am.v > neg_inf()) {
+#pragma unroll
+        for (int h = 0; h < kPartRegs; ++h)
+          if (q[j][h].m > neg_inf()) s += q[j][h].s * __builtin_amdgcn_exp2f(shift_of(q[j][h].m, cT) - M2);
+        s = wave_sum(s);
+      }
+      row_out(r, am, fl, M2, s);
+    }
+  } else {
+    for (int r = wave; r <= nd; r += kWaves) {
+      const RowPart* p = part + static_cast<size_t>(b * G1 + r) * P;
+      ArgMax am{neg_inf(), INT32_MAX};
+      uint32_t fl = 0;
+      for (int i = lane; i < P; i += 64) {
+        const RowPart q = p[i];
+        am = better(am, ArgMax{q.m, q.arg});
+        fl |= q.flags;
+      }
+      am = wave_argmax(am);
+      fl = wave_or(fl);
+      const float M2 = (am.v > neg_inf() && am.v < pos_inf()) ? shift_of(am.v, cT) : 0.0f;
+      float s = 0.0f;
+      if (sampled && am.v > neg_inf()) {
+        for (int i = lane; i < P; i += 64) {
+          const RowPart q = p[i];
+          if (q.m > neg_inf()) s += q.s * __builtin_amdgcn_exp2f(shift_of(q.m, cT) - M2);
+        }
+        s = wave_sum(s);
+      }
+      row_out(r, am, fl, M2, s);
     }
   }
   __syncthreads();
