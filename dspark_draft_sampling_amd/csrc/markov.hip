@@ -989,7 +989,7 @@ __device__ __forceinline__ void store_z0(const MarkovArgs& a, const FastLds& L, 
     const f32x4 zz = *reinterpret_cast<const f32x4*>(&L.z0[par][n][col]);
     float* dst = a.q_z + (static_cast<size_t>(b0 + n) * a.gamma + (k - 1)) * a.V + v0;
     if (VEC && v0 + 3 < a.V) {
-      *reinterpret_cast<f32x4*>(dst) = zz;
+      __builtin_nontemporal_store(zz, reinterpret_cast<f32x4*>(dst));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -1135,11 +1135,13 @@ __device__ __forceinline__ void fast_tile(const MarkovArgs& a, const bf16x8 (&af
             f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
       } else if (VEC && !EDGE) {
         if (sampled)
-          *reinterpret_cast<f32x4*>(a.q_z + rowoff + v0) = f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+          __builtin_nontemporal_store(f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]},
+                                      reinterpret_cast<f32x4*>(a.q_z + rowoff + v0));
       } else if (sampled) {
         float* dst = a.q_z + rowoff + v0;
         if (VEC && full) {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+          __builtin_nontemporal_store(f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]},
+                                      reinterpret_cast<f32x4*>(dst));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
