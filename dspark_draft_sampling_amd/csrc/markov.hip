@@ -431,7 +431,7 @@ __device__ __forceinline__ void stream_tile(const MarkovArgs& a, const bf16x8 (&
         if (VEC && full) {
           const f32x4 zv{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
           if constexpr (COH) store4_coherent(dst, zv);
-          else *reinterpret_cast<f32x4*>(dst) = zv;
+          else __builtin_nontemporal_store(zv, reinterpret_cast<f32x4*>(dst));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -942,8 +942,9 @@ __device__ __forceinline__ void finalize_request(const MarkovArgs& a, int b, int
 //    argmax, its best and second chunk scores, the candidate and its z), and
 //    one wave of workgroup b mod G finalizes request b: the record with the
 //    best chunk score holds x_k.
-// The q stores of a step are plain stores that drain while the hand-off runs:
-// no record depends on them.  Wave 0 does all the waiting (x_{k-1}, records),
+// The q stores of a step are streaming (non-temporal) stores that drain while
+// the hand-off runs: no record depends on them, and no dirty lines are left
+// for the following kernels to write back.  Wave 0 does all the waiting (x_{k-1}, records),
 // so its loads never queue behind the other waves' stores.
 
 constexpr int kZ0Ld = 68;  // floats per row of wave 0's z tile (64 + 4: bank spread)
