@@ -109,10 +109,17 @@ __device__ __forceinline__ void np_shifts(float md, float mt, float& a2d, float&
 __device__ __forceinline__ float expm1_series(float r) { return r * fmaf(r, fmaf(r, 1.0f / 6.0f, 0.5f), 1.0f); }
 
 // T - D of one element pair under a common shift; d = t = -inf gives 0.
+// SELECT: both forms computed and one selected (no branch); otherwise the
+// compiler may branch and form T - D only where it is taken.  Same value.
+template <bool SELECT>
 __device__ __forceinline__ float np_diff(float d, float t, float D, float T) {
   const float r = t - d;
-  const float near = D * expm1_series(r), far = T - D;
-  return fabsf(r) < kSeriesBand ? near : far;
+  if constexpr (SELECT) {
+    const float near = D * expm1_series(r), far = T - D;
+    return fabsf(r) < kSeriesBand ? near : far;
+  } else {
+    return fabsf(r) < kSeriesBand ? D * expm1_series(r) : T - D;
+  }
 }
 
 // Accumulate one element pair into a part's sums under shifts (a2d, a2t);
@@ -123,7 +130,7 @@ __device__ __forceinline__ void np_elem(float d, float t, float a2d, float a2t, 
   const float T = __builtin_amdgcn_exp2f(fmaf(t, kLog2e, -a2t));
   sd += D;
   if constexpr (COMMON) {
-    const float e = np_diff(d, t, D, T);
+    const float e = np_diff<true>(d, t, D, T);
     x += e;
     ad += fabsf(e);
   } else {
@@ -222,7 +229,7 @@ __device__ __forceinline__ PairK pair_k(const NormPart& p) {
 __device__ __forceinline__ float l1_near(float d, float t, float a2, float kappa) {
   const float D = __builtin_amdgcn_exp2f(fmaf(d, kLog2e, -a2));
   const float T = __builtin_amdgcn_exp2f(fmaf(t, kLog2e, -a2));
-  return fabsf(fmaf(D, kappa, -np_diff(d, t, D, T)));
+  return fabsf(fmaf(D, kappa, -np_diff<false>(d, t, D, T)));
 }
 
 // Far form: one element pair's min(P_v, T_v) Sd.

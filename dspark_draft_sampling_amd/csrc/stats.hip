@@ -697,7 +697,7 @@ __device__ __forceinline__ void seg_l1s(const uint4* ud, const uint4* ut, const 
         const float d = elem16(ud[it], j, T{}), t = elem16(ut[it], j, T{}) - k.K;
         const float D = __builtin_amdgcn_exp2f(fmaf(d, kLog2e, -k.a2d));
         const float Tv = __builtin_amdgcn_exp2f(fmaf(t, kLog2e, -k.a2t));
-        const float e = fmaf(D, k.kappa, -np_diff(d, t, D, Tv));
+        const float e = fmaf(D, k.kappa, -np_diff<false>(d, t, D, Tv));
         acc += fabsf(e);
         s += e > 0.0f ? D : (e < 0.0f ? -D : 0.0f);
       }
@@ -713,7 +713,7 @@ __device__ __forceinline__ float grad_elem(const GradRow& r, float x, float y0, 
     e = u - (fmaf(y, kLog2e, -r.k.a2t) + r.k.lam2);
   } else {
     const float Tv = __builtin_amdgcn_exp2f(fmaf(y, kLog2e, -r.k.a2t));
-    e = fmaf(D, r.k.kappa, -np_diff(x, y, D, Tv));
+    e = fmaf(D, r.k.kappa, -np_diff<false>(x, y, D, Tv));
   }
   const float sg = e > 0.0f ? 1.0f : (e < 0.0f ? -1.0f : 0.0f);
   const float P = D * r.k.isd;

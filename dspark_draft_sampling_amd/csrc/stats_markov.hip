@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kSmThreads) void stats_markov_look1_kernel(SmArgs a
     for (int e = 0; e < 4 * kSmMS; ++e) {
       const float D = __builtin_amdgcn_exp2f(fmaf(d[e], kLog2e, -a2d));
       const float Tv = __builtin_amdgcn_exp2f(fmaf(t[e], kLog2e, -a2t));
-      const float df = np_diff(d[e], t[e], D, Tv);
+      const float df = np_diff<true>(d[e], t[e], D, Tv);
       sd += D;
       x += common ? df : Tv;
       ad += fabsf(df);
