@@ -56,7 +56,7 @@ def parse():
                     default="decode",
                     help="decode (default: the benchmark line); the other configurations "
                          "are measured the same way for reference")
-    ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative"], default="auto",
+    ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative", "request-groups"], default="auto",
                     help="Markov launch plan: one launch for all steps when its grid fits "
                          "(auto), the same through cooperative launch, or two launches per step")
     ap.add_argument("--truncation-arrays", action="store_true",
@@ -87,7 +87,7 @@ def copy_calibration(mib):
 def kernel_bytes(name, B, g, V, r, d, S, R):
     """Algorithmic (compulsory) HBM bytes of one launch of each kernel."""
     C = (V + 255) // 256
-    if name in ("markov_fused", "markov_fast"):  # one launch for all gamma steps: backbone, q, W2 once, A rows
+    if name in ("markov_fused", "markov_fast", "markov_pipe"):  # one launch for all gamma steps: backbone, q, W2 once, A rows
         return 2 * B * g * V + 4 * S * g * V + 2 * r * V + 2 * B * g * r
     if name == "markov_step":      # backbone row + q row written + W2 (once per call) + A rows
         return 2 * B * V + 4 * S * V + (2 * r * V) / g + 2 * B * r
@@ -416,7 +416,7 @@ def main():
     import dspark_draft_sampling_amd as ds
 
     ds.markov_plan({"auto": ds.MARKOV_AUTO, "per-step": ds.MARKOV_PER_STEP,
-                    "cooperative": ds.MARKOV_COOPERATIVE}[args.markov_plan])
+                    "cooperative": ds.MARKOV_COOPERATIVE, "request-groups": ds.MARKOV_REQUEST_GROUPS}[args.markov_plan])
     if args.workload == "markov_stats":
         line = run_markov_stats(args, torch, ds)
     elif args.workload in ("stats", "train"):

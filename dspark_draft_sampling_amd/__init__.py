@@ -451,12 +451,13 @@ def profile_enable(on=True):
     lib().dspark_profile_enable(1 if on else 0)
 
 
-MARKOV_AUTO, MARKOV_PER_STEP, MARKOV_COOPERATIVE = 0, 1, 2
+MARKOV_AUTO, MARKOV_PER_STEP, MARKOV_COOPERATIVE, MARKOV_REQUEST_GROUPS = 0, 1, 2, 3
 
 
 def markov_plan(plan):
-    """Set the Markov launch plan (MARKOV_AUTO, MARKOV_PER_STEP or
-    MARKOV_COOPERATIVE, process-wide); returns the previous one."""
+    """Set the Markov launch plan (MARKOV_AUTO, MARKOV_PER_STEP,
+    MARKOV_COOPERATIVE or MARKOV_REQUEST_GROUPS, process-wide); returns the
+    previous one."""
     prev = lib().dspark_markov_plan(int(plan))
     if prev < 0:
         raise DSparkError(f"unknown Markov plan {plan}")

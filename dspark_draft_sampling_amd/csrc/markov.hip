@@ -23,7 +23,7 @@
 // The confidence head needs only x_{k-1}, so one kernel evaluates it for every
 // row after the last step.
 //
-// Two launch plans run these phases:
+// Three launch plans run these phases:
 //  * fused: one launch for all gamma steps (its whole grid resident at once).
 //    Workgroup g owns the 512 tokens [512 g, 512 g + 512) and keeps their W2
 //    rows in registers (the MFMA A fragments) for the whole call, so the
@@ -40,6 +40,9 @@
 //  * per step: 2 gamma launches (stream kernel over all chunks, finalize
 //    kernel over all requests), used when the fused grid cannot be resident
 //    at once (V above 512 tokens per compute unit).
+//  * request groups (on request, untruncated): the one-launch grid walks
+//    16-request groups step by step, so one group's hand-off overlaps the
+//    other groups' streaming; extra workgroups finalize (markov_pipe).
 #include <algorithm>
 #include <mutex>
 
@@ -95,6 +98,7 @@ struct MarkovArgs {
   // and never depends on more than 64-bit single-copy atomicity
   uint32_t epoch;   // this call's tag (never 0)
   int32_t G;        // workgroups of the one-launch plans (512-token slices)
+  int32_t F;        // pipelined plan: finalizing workgroups after the G streaming ones (else 0)
   uint64_t* tpart;  // truncating plan: chunk records [gamma][B][C][4]
   uint64_t* frec;   // untruncated plan: workgroup records [gamma][B][7][G] (word-major)
   uint64_t* xk;     // x_k hand-off [gamma][B][2]
@@ -1396,6 +1400,401 @@ __device__ __forceinline__ void fast_finalize(const MarkovArgs& a, int b, int k)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined untruncated one-launch plan.
+//
+// Request b's step k depends on nothing but its own x_{k-1}, so the batch is
+// cut into groups of 16 requests (one MFMA N block) and each streaming
+// workgroup walks the passes (step k, group j) in step-major order: pass
+// p = (k - 1) NG + j.  A group's hand-off (records, finalize, x_k, its W1
+// rows) then runs while the other NG - 1 groups of the step stream, instead
+// of stalling the whole batch once per step.
+//  * Workgroups 0 .. G-1 stream (512 tokens each, W2 rows in registers, as in
+//    markov_fast); workgroups G .. G+F-1 hold no W2 and only finalize
+//    (fast_finalize: one wave per request).
+//  * One barrier per pass.  Two waves have a duty besides their tokens and
+//    issue no q stores (their z go to LDS and waves 2, 3, 6, 7 store them one
+//    pass later), so their polls and record stores never queue behind
+//    streaming stores:
+//    - wave 0 polls the next pass's x words before the products, takes them
+//      after, and stages the next pass's W1 rows by LDS DMA into the other
+//      buffer while the epilogue runs;
+//    - wave 1 draws the previous pass's candidates from the LDS partials
+//      (markov_fast's three-level draw, with the level-1 noise of every
+//      request and step drawn once, at the start of the call) and stores the
+//      records.
+//  * Every other wave requests the backbone values of pass p+1 before pass
+//    p's products, so they arrive while pass p runs.
+// The partials (lanes, tokens, reduction orders, noise), the draw and the
+// records are markov_fast's, so every output is equal bit for bit.
+constexpr int kGrp = 16;          // requests per pass (MFMA N block)
+constexpr int kPipeMaxB = 256;    // requests per call (policy held in LDS)
+constexpr int kPipeFin = 2;       // finalizing workgroups, at most
+constexpr int kPipeDma = 9;       // DMA instructions per pass (kGrp rows x kW1Slots slots, rounded up)
+
+struct PipeLds {
+  // W1 rows of a pass by pass parity (kW1Slots 16-byte slots per row, the
+  // last DMA instruction's excess slots land in the padding)
+  __attribute__((aligned(16))) uint16_t a[2][kPipeDma * 64 * 8];
+  float red_m[2][8][kGrp], red_s[2][8][kGrp];
+  uint32_t red_i[2][8][kGrp];
+  float sub_v1[2][8][kGrp], sub_v2[2][8][kGrp];
+  int32_t sub_i1[2][8][kGrp];
+  __attribute__((aligned(16))) float stash[2][8][kGrp][kSub];
+  // waves 0 and 1: z tiles by pass parity, rows of 64 tokens, padded
+  __attribute__((aligned(16))) float z01[2][2][kGrp][kZ0Ld];
+  // level-2 noise of each wave's four sub-chunks for four consecutive groups
+  __attribute__((aligned(16))) float g2[8][4][kGrp][4];
+  // level-1 noise of the workgroup's two chunks per (request, step)
+  float g1[kPipeMaxB][DSPARK_MAX_GAMMA][2];
+  // the batch's policy: 1 / T (sampled), 0 (greedy), -1 (absent); request
+  // ids; positions of the anchors
+  float invT[kPipeMaxB];
+  uint32_t req[kPipeMaxB];
+  int32_t pos0[kPipeMaxB];
+  int32_t xs[kGrp];
+};
+
+// Backbone values of this lane for pass (k, j): tokens vb + 16 ms + 4 (lane >> 4)
+// + i of request 16 j + (lane & 15).
+template <typename T, bool VEC>
+__device__ __forceinline__ void pipe_backbone(QuadRaw<T> (&bb)[kFusedMS], const MarkovArgs& a, int k, int j,
+                                              int vb, int lane) {
+  QuadRaw<T> t[1][kFusedMS];
+  load_backbone<T, VEC, kFusedMS, 1>(t, static_cast<const T*>(a.backbone), a.B, a.gamma, a.V, k, j * kGrp, 0, vb,
+                                     lane);
+#pragma unroll
+  for (int ms = 0; ms < kFusedMS; ++ms) bb[ms] = t[0][ms];
+}
+
+// Waves 2, 3, 6, 7: the z tiles of waves 0 and 1 of pass (k, j) to q, for the
+// sampled requests (thread t of the four waves: one 16-byte piece of each tile).
+template <bool VEC>
+__device__ __forceinline__ void pipe_store_z01(const MarkovArgs& a, const PipeLds& L, int tok0, int k, int j,
+                                               int par, int t) {
+  const int n = t >> 4, col = (t & 15) * 4;
+  const int b = j * kGrp + n;
+  if (!(L.invT[b] > 0.0f)) return;  // absent or greedy request
+  float* row = a.q_z + (static_cast<size_t>(b) * a.gamma + (k - 1)) * a.V;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const int v0 = tok0 + w * 64 + col;
+    const f32x4 zz = *reinterpret_cast<const f32x4*>(&L.z01[par][w][n][col]);
+    if (VEC && v0 + 3 < a.V) {
+      __builtin_nontemporal_store(zz, reinterpret_cast<f32x4*>(row + v0));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v0 + e < a.V) row[v0 + e] = zz[e];
+    }
+  }
+}
+
+// Wave 1: the workgroup's candidate of every request of pass (k, j) (four
+// lanes per request, as markov_fast's draw, with the level-1 noise drawn at
+// the start of the call) and its tagged record, word-major
+// [gamma][B][7][G] as markov_fast's.
+__device__ __forceinline__ void pipe_draw(const MarkovArgs& a, const PipeLds& L, int g, int k, int j, int par) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane >> 2, p = lane & 3;
+  const int b = j * kGrp + n;
+  const int tok0 = g * kFusedTokens;
+  float wm[8], wsum[8];
+  uint32_t wi[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    wm[w] = L.red_m[par][w][n];
+    wsum[w] = L.red_s[par][w][n];
+    wi[w] = L.red_i[par][w][n];
+  }
+  ArgMax am{wm[0], static_cast<int32_t>(wi[0] & 0x7fffffffu)};
+  uint32_t bad = wi[0] >> 31;
+#pragma unroll
+  for (int w = 1; w < 8; ++w) {
+    am = better(am, ArgMax{wm[w], static_cast<int32_t>(wi[w] & 0x7fffffffu)});
+    bad |= wi[w] >> 31;
+  }
+  const bool sampled = L.invT[b] > 0.0f;
+  const uint32_t req = L.req[b];
+  const int32_t pos = L.pos0[b] + k;
+  float sc[2], cmv[2], csv[2];
+#pragma unroll
+  for (int hc = 0; hc < 2; ++hc) {
+    const int c = 2 * g + hc;
+    float cm = wm[4 * hc], cs = wsum[4 * hc];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) lse_merge(cm, cs, wm[4 * hc + w], wsum[4 * hc + w]);
+    cmv[hc] = cm;
+    csv[hc] = cs;
+    sc[hc] = (sampled && c < a.C && cm > neg_inf() && cm < pos_inf() && cs > 0.0f)
+                 ? cm + logf(cs) + L.g1[b][k - 1][hc]
+                 : neg_inf();
+  }
+  float m = cmv[0], s = csv[0];
+  lse_merge(m, s, cmv[1], csv[1]);
+  const int hb = sc[1] > sc[0] ? 1 : 0;
+  Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    t2 = top2_merge(t2, Top2{L.sub_v1[par][4 * hb + w][n], L.sub_i1[par][4 * hb + w][n], L.sub_v2[par][4 * hb + w][n]});
+  // level 3 over the chosen sub-chunk's tokens: lane p takes 4p .. 4p+3
+  const bool draw = sampled && sc[hb] > neg_inf() && t2.i1 != INT32_MAX;
+  Top2 t3{neg_inf(), INT32_MAX, neg_inf()};
+  f32x4 zz = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+  if (draw) {
+    const int wj = (t2.i1 - (tok0 >> 4)) >> 2;  // wave holding the sub-chunk
+    zz = *reinterpret_cast<const f32x4*>(&L.stash[par][wj][n][4 * p]);
+    uint32_t d0 = static_cast<uint32_t>(t2.i1) * 4u + static_cast<uint32_t>(p), d1 = static_cast<uint32_t>(pos),
+             d2 = req, d3 = DSPARK_TAG_DRAFT_TOKEN;
+    philox4x32_10(d0, d1, d2, d3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+    const uint32_t tw[4] = {d0, d1, d2, d3};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (zz[e] > neg_inf()) t3 = top2_merge(t3, Top2{zz[e] + gumbel_of(tw[e]), t2.i1 * kSub + 4 * p + e, neg_inf()});
+  }
+  t3 = quad_top2(t3);
+  float zmine = neg_inf();
+  if (draw && t3.i1 != INT32_MAX && ((t3.i1 - t2.i1 * kSub) >> 2) == p) {
+    const int e = t3.i1 & 3;
+    zmine = e == 0 ? zz[0] : e == 1 ? zz[1] : e == 2 ? zz[2] : zz[3];
+  }
+  const float zc = quad_max(zmine);
+  const bool near23 = (t2.v2 > neg_inf() && near_gap(t2.v1, t2.v2)) ||
+                      (t3.i1 != INT32_MAX && t3.v2 > neg_inf() && near_gap(t3.v1, t3.v2));
+  if (b < a.B) {
+    // the four lanes of a request hold the same record: lane p stores words
+    // p and p + 4
+    uint64_t* R = a.frec + (static_cast<size_t>(k - 1) * a.B + b) * 7 * a.G + g;
+    const uint32_t w0 = p == 0 ? __float_as_uint(m) : p == 1 ? __float_as_uint(s)
+                        : p == 2 ? __float_as_uint(sc[hb]) : __float_as_uint(sc[1 - hb]);
+    const uint32_t w1 = p == 0 ? ((static_cast<uint32_t>(am.i) & 0x7fffffffu) | (bad ? 0x80000000u : 0u))
+                        : p == 1 ? ((draw && t3.i1 != INT32_MAX)
+                                        ? (0x80000000u | (near23 ? 0x40000000u : 0u) | static_cast<uint32_t>(t3.i1))
+                                        : 0u)
+                                 : __float_as_uint(zc);
+    st_tagged(R + static_cast<size_t>(p) * a.G, a.epoch, w0);
+    if (p < 3) st_tagged(R + static_cast<size_t>(p + 4) * a.G, a.epoch, w1);
+  }
+}
+
+// Wave 0: x_{k-1} of pass (k, j)'s requests (lanes 0..15; anchors at k = 1),
+// after a first poll issued earlier (w0, w1: its words).  -1 for absent
+// requests and waits that gave up.
+__device__ __forceinline__ int32_t pipe_x(const MarkovArgs& a, int k, int j, uint64_t w0, uint64_t w1) {
+  const int lane = threadIdx.x & 63;
+  const int b = j * kGrp + lane;
+  if (lane >= kGrp || b >= a.B) return -1;
+  if (k == 1) return clamp_token(a.anchor[b], a.V);
+  if (tag_is(w0, a.epoch) && tag_is(w1, a.epoch) && (payload(w0) ^ kTokenCheck) == payload(w1))
+    return clamp_token(static_cast<int32_t>(payload(w0)), a.V);
+  return clamp_token(wait_token(a, k - 1, b), a.V);
+}
+
+// Wave 0: the W1 rows of the pass whose x values are in L.xs into buffer par
+// (LDS DMA; slot sl = 64 q + lane holds 8 rank elements of row sl / kW1Slots;
+// padding slots, pieces past the rank and absent rows read past the buffer: 0).
+__device__ __forceinline__ void pipe_dma(const MarkovArgs& a, PipeLds& L, int par) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int lane = threadIdx.x & 63;
+  const int r = a.r;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w1), static_cast<short>(0), a.V * r * 2, kBufferWord3);
+#pragma unroll
+  for (int q = 0; q < kPipeDma; ++q) {
+    const int sl = q * 64 + lane, n = sl / kW1Slots, c = sl - n * kW1Slots;
+    const int32_t x = n < kGrp ? L.xs[n] : -1;
+    const bool ok = n < kGrp && c < kW1Slots - 1 && c * 8 < r && x >= 0;
+    const uint32_t off = ok ? static_cast<uint32_t>((x * r + c * 8) * 2) : 0xfffffff0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(L.a[par] + q * 64 * 8), 16, off, 0, 0, 0);
+  }
+}
+
+// Level-2 noise of this wave's four sub-chunks for groups j .. j+3 of step k
+// (lane (n, q): request 16 (j + q) + n, one Philox block).
+__device__ __forceinline__ void pipe_noise2(const MarkovArgs& a, PipeLds& L, int tok0, int wave, int k, int j) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, q = lane >> 4;
+  const int b = (j + q) * kGrp + n;  // < kPipeMaxB (j <= 12 when B <= kPipeMaxB)
+  uint32_t c0 = (static_cast<uint32_t>(tok0) >> 6) + static_cast<uint32_t>(wave),
+           c1 = static_cast<uint32_t>(L.pos0[b] + k), c2 = L.req[b], c3 = DSPARK_TAG_DRAFT_SUB;
+  philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+  *reinterpret_cast<f32x4*>(&L.g2[wave][q][n][0]) = f32x4{gumbel_of(c0), gumbel_of(c1), gumbel_of(c2), gumbel_of(c3)};
+}
+
+// Pass p = (k - 1) NG + j of a streaming workgroup.  bb holds this pass's
+// backbone values (requested during the previous pass); bbn receives the next
+// pass's.  On entry buffer p & 1 holds this pass's W1 rows; on exit (after
+// the barrier) buffer (p + 1) & 1 holds the next pass's, and this pass's
+// partials, stash and z tiles are in LDS for the next pass's draw and stores.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void pipe_pass(const MarkovArgs& a, const bf16x8 (&af)[kFusedMS][kMaxR / 32], int g,
+                                          int p, int P, int NG, PipeLds& L, const QuadRaw<T> (&bb)[kFusedMS],
+                                          QuadRaw<T> (&bbn)[kFusedMS]) {
+  constexpr int MS = kFusedMS;
+  const int tid = opaque_tid(), lane = tid & 63, wave = wave_id();
+  const int gamma = a.gamma, V = a.V;
+  const int k = p / NG + 1, j = p - (k - 1) * NG;
+  const int par = p & 1;
+  const int tok0 = g * kFusedTokens;
+  const int vb = tok0 + wave * 16 * MS;
+  const int ksteps = ((a.r + 31) & ~31) / 32;
+  const bool more = p + 1 < P;
+  const int k1 = (p + 1) / NG + 1, j1 = p + 1 - (k1 - 1) * NG;
+
+  uint64_t w0 = 0, w1 = 0;  // wave 0: the first poll of the next pass's x words
+  if (wave == 0) {
+    if (more && k1 > 1 && lane < kGrp && j1 * kGrp + lane < a.B) {
+      const uint64_t* xp = a.xk + (static_cast<size_t>(k1 - 2) * a.B + j1 * kGrp + lane) * 2;
+      w0 = ld_tagged(xp);
+      w1 = ld_tagged(xp + 1);
+    }
+    if (more) pipe_backbone<T, VEC>(bbn, a, k1, j1, vb, lane);
+  } else if (wave == 1) {
+    if (p > 0) {
+      const int kp = (p - 1) / NG + 1, jp = p - 1 - (kp - 1) * NG;
+      pipe_draw(a, L, g, kp, jp, par ^ 1);
+    }
+    if (more) pipe_backbone<T, VEC>(bbn, a, k1, j1, vb, lane);
+  }
+  if ((j & 3) == 0) pipe_noise2(a, L, tok0, wave, k, j);
+
+  // the bias tile of this pass: W2 rows (A) times the staged W1 rows (B)
+  f32x4 acc[MS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int ld = kMaxR + kPad;
+#pragma unroll
+  for (int ks = 0; ks < kMaxR / 32; ++ks) {
+    if (ks < ksteps) {
+      const bf16x8 bfr = load_frag(L.a[par] + (lane & 15) * ld + ks * 32 + (lane >> 4) * 8);
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+        acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms][ks], bfr, acc[ms], 0, 0, 0);
+    }
+  }
+  if (wave == 0 && more) {
+    // the next pass's x (the poll issued above is back by now, unless the
+    // finalize is late) and its W1 rows, landing while the epilogue runs
+    const int32_t x = pipe_x(a, k1, j1, w0, w1);
+    if (lane < kGrp) L.xs[lane] = x;
+    pipe_dma(a, L, par ^ 1);
+  } else if (wave >= 2) {
+    // the streaming waves' bulk traffic goes out after the duty waves' polls
+    // and record stores of this pass, so those do not queue behind it
+    if (more) pipe_backbone<T, VEC>(bbn, a, k1, j1, vb, lane);
+    if (p > 0 && (wave & 2)) {
+      const int kp = (p - 1) / NG + 1, jp = p - 1 - (kp - 1) * NG;
+      pipe_store_z01<VEC>(a, L, tok0, kp, jp, par ^ 1, ((wave >> 1) & 2 | (wave & 1)) * 64 + lane);
+    }
+  }
+  // epilogue: lane holds tokens vb + ms*16 + 4*(lane>>4) + i of request n
+  const int n = lane & 15;
+  const int b = j * kGrp + n;
+  const int q = lane >> 4;
+  const float pit = L.invT[b];  // 1 / T (sampled), 0 (greedy), -1 (absent)
+  const bool bvalid = pit >= 0.0f;
+  const bool sampled = pit > 0.0f;
+  const float invT = sampled ? pit : 1.0f;
+  const size_t rowoff = (static_cast<size_t>(bvalid ? b : 0) * gamma + (k - 1)) * V;
+  float z[4 * MS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    const int v0 = vb + ms * 16 + 4 * (lane >> 4);
+    const bool full = bvalid && v0 + 3 < V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = (acc[ms][i] + bb[ms].at(i)) * invT;
+      if constexpr (EDGE) z[ms * 4 + i] = (bvalid && v0 + i < V) ? y : neg_inf();
+      else z[ms * 4 + i] = y;
+    }
+    if (wave < 2) {
+      *reinterpret_cast<f32x4*>(&L.z01[par][wave][n][ms * 16 + 4 * (lane >> 4)]) =
+          f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]};
+    } else if (VEC && !EDGE) {
+      if (sampled)
+        __builtin_nontemporal_store(f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]},
+                                    reinterpret_cast<f32x4*>(a.q_z + rowoff + v0));
+    } else if (sampled) {
+      float* dst = a.q_z + rowoff + v0;
+      if (VEC && full) {
+        __builtin_nontemporal_store(f32x4{z[ms * 4], z[ms * 4 + 1], z[ms * 4 + 2], z[ms * 4 + 3]},
+                                    reinterpret_cast<f32x4*>(dst));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v0 + i < V) dst[i] = z[ms * 4 + i];
+      }
+    }
+  }
+  float lm = z[0];
+#pragma unroll
+  for (int e = 1; e < 4 * MS; ++e) lm = fmaxf(lm, z[e]);
+  const float m = rows_max(lm);
+  int32_t arg = INT32_MAX;
+  if (__builtin_amdgcn_ballot_w64(bvalid && !sampled)) {
+#pragma unroll
+    for (int e = 4 * MS - 1; e >= 0; --e)
+      if (z[e] == m && m > neg_inf()) arg = vb + (e >> 2) * 16 + 4 * (lane >> 4) + (e & 3);
+    arg = static_cast<int32_t>(rows_combine(static_cast<uint32_t>(arg), [](uint32_t u, uint32_t v) {
+      return u < v ? u : v;
+    }));
+  }
+  float sj[MS], s;
+  sub_partials<MS>(z, m, sj, s);
+  const bool bad = s != s || m == pos_inf();
+  const uint32_t jbase = static_cast<uint32_t>(vb) >> 4;
+  const float sq = q == 0 ? sj[0] : q == 1 ? sj[1] : q == 2 ? sj[2] : sj[3];
+  Top2 t2{neg_inf(), INT32_MAX, neg_inf()};
+  if (sampled && m > neg_inf() && !bad && sq > 0.0f)
+    t2 = Top2{m + logf(sq) + L.g2[wave][j & 3][n][q], static_cast<int32_t>(jbase + q), neg_inf()};
+  t2 = rows_top2(t2);
+  if (t2.i1 != INT32_MAX) {
+    const int m1 = t2.i1 - static_cast<int32_t>(jbase);
+    const f32x4 zz = m1 == 0   ? f32x4{z[0], z[1], z[2], z[3]}
+                     : m1 == 1 ? f32x4{z[4], z[5], z[6], z[7]}
+                     : m1 == 2 ? f32x4{z[8], z[9], z[10], z[11]}
+                               : f32x4{z[12], z[13], z[14], z[15]};
+    *reinterpret_cast<f32x4*>(&L.stash[par][wave][n][4 * q]) = zz;
+  }
+  if (q == 0) {
+    L.red_m[par][wave][n] = m;
+    L.red_s[par][wave][n] = s;
+    L.red_i[par][wave][n] = (static_cast<uint32_t>(arg) & 0x7fffffffu) | (bad ? 0x80000000u : 0u);
+    L.sub_v1[par][wave][n] = t2.v1;
+    L.sub_i1[par][wave][n] = t2.i1;
+    L.sub_v2[par][wave][n] = t2.v2;
+  }
+  if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // the next pass's W1 rows landed
+  __syncthreads();
+}
+
+// Streaming workgroup g: every pass, then the last pass's draw and z tiles.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void pipe_stream(const MarkovArgs& a, const bf16x8 (&af)[kFusedMS][kMaxR / 32], int g,
+                                            PipeLds& L) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int NG = (a.B + kGrp - 1) / kGrp, P = a.gamma * NG;
+  const int vb = g * kFusedTokens + wave * 16 * kFusedMS;
+  QuadRaw<T> bbA[kFusedMS], bbB[kFusedMS];
+  // pass 0: x_0 = the anchors, its W1 rows and backbone values
+  if (wave == 0) {
+    const int32_t x = pipe_x(a, 1, 0, 0, 0);
+    if (lane < kGrp) L.xs[lane] = x;
+    pipe_dma(a, L, 0);
+  }
+  pipe_backbone<T, VEC>(bbA, a, 1, 0, vb, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int p = 0; p < P; p += 2) {
+    pipe_pass<T, VEC, EDGE>(a, af, g, p, P, NG, L, bbA, bbB);
+    if (p + 1 < P) pipe_pass<T, VEC, EDGE>(a, af, g, p + 1, P, NG, L, bbB, bbA);
+  }
+  const int kp = (P - 1) / NG + 1, jp = P - 1 - (kp - 1) * NG;
+  if (wave == 1) pipe_draw(a, L, g, kp, jp, (P - 1) & 1);
+  if (wave & 2)
+    pipe_store_z01<VEC>(a, L, g * kFusedTokens, kp, jp, (P - 1) & 1, ((wave >> 1) & 2 | (wave & 1)) * 64 + lane);
+}
+
 // Confidence head of every draft row (b, k): c = sigmoid(w . [h_k ;
 // embed(x_{k-1})]), one workgroup per row, run after the last step (x_{k-1}
 // is the anchor for k = 1, else draft token k-1).  8 elements per 16-byte
@@ -1526,6 +1925,61 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fast_kernel(MarkovArgs a
   if (threadIdx.x >= 4 * kTile && a.B <= kTile) store_z0<VEC>(a, L, g * kFusedTokens, 0, a.gamma);
 }
 
+// Pipelined untruncated one-launch plan (see pipe_pass): G streaming
+// workgroups, then F finalizing ones.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kFusedThreads) void markov_pipe_kernel(MarkovArgs a) {
+  __shared__ PipeLds L;
+  const int g = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int NG = (a.B + kGrp - 1) / kGrp, P = a.gamma * NG;
+  if (g >= a.G) {
+    // finalizing workgroup: wave fw takes requests fw, fw + FW, ... of every
+    // group, pass by pass (the order in which their records complete)
+    const int FW = a.F * 8, fw = (g - a.G) * 8 + wave;
+    for (int p = 0; p < P; ++p) {
+      const int k = p / NG + 1, j = p - (k - 1) * NG;
+      for (int i = fw; i < kGrp; i += FW) {
+        const int b = j * kGrp + i;
+        if (b < a.B) fast_finalize(a, b, k);
+      }
+    }
+    return;
+  }
+  for (int t = threadIdx.x; t < kPipeMaxB; t += kFusedThreads) {
+    float it = -1.0f;
+    uint32_t req = 0;
+    int32_t pos = 0;
+    if (t < a.B) {
+      const float Tb = a.pol.temperature[t];
+      it = (a.pol.mode[t] != 0 && !bad_temperature(Tb)) ? 1.0f / Tb : 0.0f;
+      req = a.pol.request_id[t];
+      pos = a.pol.position[t];
+    }
+    L.invT[t] = it;
+    L.req[t] = req;
+    L.pos0[t] = pos;
+  }
+  bf16x8 af[kFusedMS][kMaxR / 32];  // resident for the whole call
+  load_w2<kFusedMS>(af, a.w2, g * kFusedTokens + wave * 16 * kFusedMS, a.V, a.r, lane);
+  // the level-1 noise of chunks 2g, 2g + 1 for every (request, step): one
+  // Philox block each, while the W2 rows arrive
+  __syncthreads();
+  for (int t = threadIdx.x; t < a.B * a.gamma; t += kFusedThreads) {
+    const int b = t / a.gamma, k = t - b * a.gamma + 1;
+    uint32_t d0 = static_cast<uint32_t>(2 * g) >> 2, d1 = static_cast<uint32_t>(L.pos0[b] + k), d2 = L.req[b],
+             d3 = DSPARK_TAG_DRAFT_CHUNK;
+    philox4x32_10(d0, d1, d2, d3, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32));
+    const uint32_t cw[4] = {d0, d1, d2, d3};
+    L.g1[b][k - 1][0] = gumbel_of(cw[(2 * g) & 3]);
+    L.g1[b][k - 1][1] = gumbel_of(cw[(2 * g + 1) & 3]);
+  }
+  // element-wise checks only where the slice runs past the vocabulary or the
+  // last group is partly absent
+  if ((g + 1) * kFusedTokens > a.V || a.B % kGrp != 0) pipe_stream<T, VEC, true>(a, af, g, L);
+  else pipe_stream<T, VEC, false>(a, af, g, L);
+}
+
 // Resident workgroups per compute unit of a one-launch kernel, the device's
 // compute units and whether it offers cooperative launch, cached per device
 // and kernel: a property of the device and the code object only.
@@ -1535,7 +1989,17 @@ struct FusedFit {
   bool coop;
 };
 
-template <typename T, bool VEC, bool FAST>
+// Kernels of the one-launch plans.
+enum { kKindFused = 0, kKindFast = 1, kKindPipe = 2 };
+template <typename T, bool VEC, int KIND>
+const void* one_launch_fn() {
+  return KIND == kKindPipe   ? reinterpret_cast<const void*>(markov_pipe_kernel<T, VEC>)
+         : KIND == kKindFast ? reinterpret_cast<const void*>(markov_fast_kernel<T, VEC>)
+                             : reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>);
+}
+constexpr const char* kKindName[3] = {"markov_fused", "markov_fast", "markov_pipe"};
+
+template <typename T, bool VEC, int KIND>
 FusedFit fused_fit() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];  // (coop << 30 | blocks << 16 | cus) + 1; 0 = unknown
@@ -1548,9 +2012,9 @@ FusedFit fused_fit() {
   int coop = 0, cus = 0, nb = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
-  const void* fn = FAST ? reinterpret_cast<const void*>(markov_fast_kernel<T, VEC>)
-                        : reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kFusedThreads, 0) != hipSuccess) nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, one_launch_fn<T, VEC, KIND>(), kFusedThreads, 0) !=
+      hipSuccess)
+    nb = 0;
   FusedFit f{nb, cus, coop != 0};
   if (f.blocks_per_cu < 0 || f.blocks_per_cu > 0x3fff || cus < 0 || cus > 0xffff) f = FusedFit{0, 0, false};
   if (dev < kMaxDev)
@@ -1593,7 +2057,7 @@ uint32_t next_epoch() {
 
 // One ordinary (or cooperative) launch of a one-launch kernel, chained.
 hipError_t launch_one(const void* fn, const char* name, const MarkovArgs& a, bool coop, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.G)), block(kFusedThreads);
+  const dim3 grid(static_cast<unsigned>(a.G + a.F)), block(kFusedThreads);
   MarkovArgs arg = a;
   void* params[] = {&arg};
   if (coop) {
@@ -1638,13 +2102,15 @@ hipError_t launch_one(const void* fn, const char* name, const MarkovArgs& a, boo
 }
 
 // plan: 0 per-step kernels, 1 one ordinary launch, 2 one cooperative launch
+// of the one-launch kernel KIND
 template <typename T, bool VEC>
-hipError_t launch_plan(MarkovArgs a, int plan, bool fast, hipStream_t st) {
+hipError_t launch_plan(MarkovArgs a, int plan, int kind, hipStream_t st) {
   if (plan) {
     a.epoch = next_epoch();
-    const void* fn = fast ? reinterpret_cast<const void*>(markov_fast_kernel<T, VEC>)
-                          : reinterpret_cast<const void*>(markov_fused_kernel<T, VEC>);
-    hipError_t e = launch_one(fn, fast ? "markov_fast" : "markov_fused", a, plan == 2, st);
+    const void* fn = kind == kKindPipe   ? one_launch_fn<T, VEC, kKindPipe>()
+                     : kind == kKindFast ? one_launch_fn<T, VEC, kKindFast>()
+                                         : one_launch_fn<T, VEC, kKindFused>();
+    hipError_t e = launch_one(fn, kKindName[kind], a, plan == 2, st);
     if (e != hipSuccess) return e;
   } else {
     a.epoch = 0;
@@ -1666,21 +2132,35 @@ hipError_t launch_plan(MarkovArgs a, int plan, bool fast, hipStream_t st) {
 }
 
 template <typename T, bool VEC>
-hipError_t launch_typed(const MarkovArgs& a, int plan_mode, hipStream_t st) {
-  // the untruncated kernel when the call passes no truncation arrays; a
-  // one-launch plan when its grid (one workgroup per 512 tokens) is resident
-  // at once
+hipError_t launch_typed(MarkovArgs a, int plan_mode, hipStream_t st) {
+  // the untruncated kernels when the call passes no truncation arrays; a
+  // one-launch plan when its grid (one workgroup per 512 tokens, plus the
+  // pipelined plan's finalizing workgroups) is resident at once
   const bool fast = !a.pol.top_k && !a.pol.top_p;
-  const FusedFit f = fast ? fused_fit<T, VEC, true>() : fused_fit<T, VEC, false>();
-  int plan = 0;
+  a.F = 0;
   if (fast && a.G > kFastMaxG) {
     // the untruncated finalize reads at most kFastMaxG records per request
-  } else if (plan_mode == DSPARK_MARKOV_AUTO) {
+    return launch_plan<T, VEC>(a, 0, kKindFast, st);
+  }
+  // the request-group plan on request (with fewer than three groups a
+  // group's hand-off has no other group's streaming to hide behind)
+  if (plan_mode == DSPARK_MARKOV_REQUEST_GROUPS && fast && a.B > 2 * kGrp && a.B <= kPipeMaxB) {
+    const FusedFit f = fused_fit<T, VEC, kKindPipe>();
+    const int room = f.blocks_per_cu * stream_cus(st, f.cus) - a.G;
+    if (f.blocks_per_cu > 0 && room >= 1) {
+      a.F = std::min(room, kPipeFin);
+      return launch_plan<T, VEC>(a, 1, kKindPipe, st);
+    }
+  }
+  const int kind = fast ? kKindFast : kKindFused;
+  const FusedFit f = fast ? fused_fit<T, VEC, kKindFast>() : fused_fit<T, VEC, kKindFused>();
+  int plan = 0;
+  if (plan_mode == DSPARK_MARKOV_AUTO || plan_mode == DSPARK_MARKOV_REQUEST_GROUPS) {
     if (f.blocks_per_cu > 0 && a.G <= f.blocks_per_cu * stream_cus(st, f.cus)) plan = 1;
   } else if (plan_mode == DSPARK_MARKOV_COOPERATIVE) {
     if (f.coop && f.blocks_per_cu > 0 && a.G <= f.blocks_per_cu * f.cus) plan = 2;
   }
-  return launch_plan<T, VEC>(a, plan, fast, st);
+  return launch_plan<T, VEC>(a, plan, kind, st);
 }
 
 }  // namespace
@@ -1707,7 +2187,7 @@ MarkovPlan plan_markov(int32_t B, int32_t gamma, int32_t V, int32_t r, int32_t d
   p.C = (V + kChunk - 1) / kChunk;
   p.G = (V + kFusedTokens - 1) / kFusedTokens;
   // one record area, used by whichever plan runs: per-step chunk records
-  // (16 B), tagged chunk records (32 B) or tagged workgroup records (64 B)
+  // (16 B), tagged chunk records (32 B) or tagged workgroup records (56 B)
   const size_t rows = static_cast<size_t>(gamma) * B;
   const size_t rec = std::max({rows * p.C * sizeof(ChunkPart), rows * p.C * 4 * sizeof(uint64_t),
                                rows * p.G * 7 * sizeof(uint64_t)});

@@ -60,7 +60,8 @@ ProfScope::~ProfScope() {
 extern "C" {
 
 int dspark_markov_plan(int plan) {
-  if (plan != DSPARK_MARKOV_AUTO && plan != DSPARK_MARKOV_PER_STEP && plan != DSPARK_MARKOV_COOPERATIVE)
+  if (plan != DSPARK_MARKOV_AUTO && plan != DSPARK_MARKOV_PER_STEP && plan != DSPARK_MARKOV_COOPERATIVE &&
+      plan != DSPARK_MARKOV_REQUEST_GROUPS)
     return -1;
   return dspark::g_markov_plan.exchange(plan);
 }

@@ -235,26 +235,36 @@ int dspark_release(void);
  *   DSPARK_MARKOV_AUTO (default): one launch for all gamma steps whenever its
  *     grid (one workgroup per 512 tokens of the vocabulary) fits the compute
  *     units the stream may use, resident at once; each workgroup then keeps
- *     its slice of markov_w2 in registers for the whole call, and the steps
- *     hand their results to one another through the workspace (polled, no
- *     device-wide barrier; every hand-off word carries a per-call tag, so
- *     the workspace needs no clearing and a stale word is never read as
- *     this call's).  It is an ordinary launch: the library
- *     chains its own such launches on a device (each waits for the previous
- *     one's completion event, whatever the stream; not inside a stream
- *     capture), and residency otherwise relies on no other kernel holding
- *     compute units indefinitely.  Every such wait is bounded: on expiry
- *     the call ends and flags its rows DSPARK_FLAG_SYNC_TIMEOUT.  Otherwise
- *     2 gamma launches as below.
+ *     its slice of markov_w2 in registers for the whole call, the whole
+ *     batch takes each step together, and the steps hand their results to
+ *     one another through the workspace (polled, no device-wide barrier;
+ *     every hand-off word carries a per-call tag, so the workspace needs no
+ *     clearing and a stale word is never read as this call's).  It is an
+ *     ordinary launch: the library chains its own such launches on a device
+ *     (each waits for the previous one's completion event, whatever the
+ *     stream; not inside a stream capture), and residency otherwise relies
+ *     on no other kernel holding compute units indefinitely.  Every such
+ *     wait is bounded: on expiry the call ends and flags its rows
+ *     DSPARK_FLAG_SYNC_TIMEOUT.  Otherwise 2 gamma launches as below.
  *   DSPARK_MARKOV_PER_STEP: 2 gamma launches (one stream kernel over all
  *     chunks and one finalize kernel over all requests per step).
  *   DSPARK_MARKOV_COOPERATIVE: as AUTO, but through cooperative launch (the
  *     runtime guarantees residency, at the price of synchronising its
  *     separate queue with the stream before and after the launch).
  *     Without cooperative launch, as PER_STEP.
+ *   DSPARK_MARKOV_REQUEST_GROUPS: as AUTO, but without truncation arrays,
+ *     with 33 to 256 requests and at least one compute unit to spare, the
+ *     requests are taken in groups of 16 whose steps interleave (a group's
+ *     hand-off runs while the other groups stream), with one or two extra
+ *     workgroups that only combine the records.  Otherwise as AUTO.
  * All plans compute identical results.  Returns the previous plan, or -1
  * (leaving it unchanged) for an unknown value. */
-enum { DSPARK_MARKOV_AUTO = 0, DSPARK_MARKOV_PER_STEP = 1, DSPARK_MARKOV_COOPERATIVE = 2 };
+enum {
+  DSPARK_MARKOV_AUTO = 0,
+  DSPARK_MARKOV_PER_STEP = 1,
+  DSPARK_MARKOV_COOPERATIVE = 2,
+  DSPARK_MARKOV_REQUEST_GROUPS = 3
+};
 int dspark_markov_plan(int plan);
 
 /* ---------------------------------------------------------------------------

@@ -418,22 +418,56 @@ def test_markov_plans_agree(config, decode_full, truncated_full):
         fused_arrays = G.markov(inp, arrays=True)
         ds.markov_plan(ds.MARKOV_COOPERATIVE)
         coop = G.markov(inp)
+        ds.markov_plan(ds.MARKOV_REQUEST_GROUPS)
+        groups = G.markov(inp)
         ds.markov_plan(ds.MARKOV_PER_STEP)
         step = G.markov(inp)
     finally:
         ds.markov_plan(prev)
     samp = inp["mode"] != 0
-    for k in ("draft_tokens", "q_thr", "confidence", "flags", "q_lse", "q_tok"):
-        assert np.array_equal(fused[k], coop[k]), k  # the same kernel
+    for other in (coop, groups):
+        # the whole-step kernel (ordinary and cooperative launch) and the
+        # request-group kernel (decode batch) form the same records and
+        # combine them alike
+        for k in ("draft_tokens", "q_thr", "confidence", "flags", "q_lse", "q_tok"):
+            assert np.array_equal(fused[k], other[k]), k
+        assert np.array_equal(fused["q_logits"][samp], other["q_logits"][samp])
     for other in (step, fused_arrays):
         for k in ("draft_tokens", "q_thr", "confidence", "flags"):
             assert np.array_equal(fused[k], other[k]), k
         for k in ("q_lse", "q_tok"):
             assert np.allclose(fused[k], other[k], rtol=1e-6, atol=0), k
         assert np.array_equal(fused["q_logits"][samp], other["q_logits"][samp])
-    assert np.array_equal(fused["q_logits"][samp], coop["q_logits"][samp])
-    for o in (fused, fused_arrays, coop, step):
+    for o in (fused, fused_arrays, coop, groups, step):
         assert not np.any(o["flags"] & (1 << 5))  # no wait gave up
+
+
+@pytest.mark.parametrize("B,V,dtype", [(33, 5000, "f32"), (48, 4096, "bf16"), (100, 2049, "bf16"),
+                                       (256, 1536, "f32")])
+def test_markov_request_groups(B, V, dtype):
+    """The request-group one-launch kernel (MARKOV_REQUEST_GROUPS without
+    truncation arrays, 33..256 requests) against the oracle on every request,
+    and bit for bit against the whole-step kernel (AUTO): full and partly
+    absent groups (B % 16), slices past the vocabulary, greedy and sampled
+    requests side by side, per-request temperatures."""
+    cfg = dict(seed=91 + B, B=B, gamma=5, V=V, r=32, d=24, dtype=dtype, draft_std=2.0,
+               noise_std=0.5, w_std=0.3, mode="mixed")
+    inp = decode_inputs(cfg)
+    inp["temperature"] = np.random.default_rng(B).uniform(0.5, 1.5, B).astype(np.float32)
+    ref = O.markov_sample(inp)
+    prev = ds.markov_plan(ds.MARKOV_REQUEST_GROUPS)
+    try:
+        got = G.markov(inp)
+        ds.markov_plan(ds.MARKOV_AUTO)
+        whole = G.markov(inp)
+    finally:
+        ds.markov_plan(prev)
+    assert check_markov(inp, got, ref) >= B * inp["gamma"] // 2
+    samp = inp["mode"] != 0
+    for k in ("draft_tokens", "q_lse", "q_thr", "q_tok", "confidence", "flags"):
+        assert np.array_equal(got[k], whole[k]), k
+    assert np.array_equal(got["q_logits"][samp], whole["q_logits"][samp])
+    assert not np.any(got["flags"] & (1 << 5))  # no wait gave up
 
 
 def test_markov_stale_workspace(decode_full):
