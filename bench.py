@@ -359,6 +359,48 @@ def _step_percentiles(step, args, torch):
                 p50_us=round(float(np.percentile(us, 50)), 2), p90_us=round(float(np.percentile(us, 90)), 2))
 
 
+def _graph_step(step, nsteps, args, torch, ds):
+    """The step captured in a HIP graph (nsteps eager steps, one per rotated
+    input set, recorded once) and replayed: microseconds per step, next to the
+    same steps run eagerly with the plan a capture uses (Markov per step)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2 * nsteps):  # the stream's workspaces exist before the capture
+            step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(nsteps):
+            step()
+    torch.cuda.synchronize()
+    reps = max(10, min(args.steps, 50))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+    torch.cuda.synchronize()
+    graph_us = ev0.elapsed_time(ev1) * 1e3 / (reps * nsteps)
+    prev = ds.markov_plan(ds.MARKOV_PER_STEP)
+    try:
+        with torch.cuda.stream(s):
+            step()
+            ev0.record()
+            for _ in range(reps * nsteps):
+                step()
+            ev1.record()
+        torch.cuda.synchronize()
+    finally:
+        ds.markov_plan(prev)
+    eager_us = ev0.elapsed_time(ev1) * 1e3 / (reps * nsteps)
+    del g
+    return dict(step_us=round(graph_us, 2), eager_same_plan_step_us=round(eager_us, 2),
+                markov_plan="per-step (a capture runs every plan as per-step)")
+
+
 def _kernels(step, args, torch, ds, bytes_of):
     """Per-kernel launch durations over a second pass in the same launch
     configuration (HIP events on the launch stream)."""
@@ -523,6 +565,7 @@ def run_decode(args, torch, ds):
     roofline = _roofline(kernels, args.workload)
     step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
     pct = _step_percentiles(step, args, torch)
+    graph = _graph_step(step, len(sets), args, torch, ds)
     # decode-path rates from the per-kernel event times: verify alone, and
     # Markov + verify (the statistics are the training side of the path)
     t_of = lambda pre: sum(k["avg_us"] * k["launches_per_step"] for n, k in kernels.items()
@@ -549,6 +592,7 @@ def run_decode(args, torch, ds):
                 step_rows_s=round(B * (g + 1) / ((t_markov + t_verify) * 1e-6), 1),
                 step_us=dict(**pct, markov_us=round(t_markov, 2), verify_us=round(t_verify, 2),
                              stats_us=round(t_stats, 2), width_us=round(t_of("select_width"), 2)),
+                hip_graph=graph,
                 acceptance=dict(mean_accept_len=round(float(acc.mean()), 4),
                                 accepted_per_proposal=round(float(acc.mean()) / g, 4),
                                 per_position_accept_rate=round(float(acc.sum() / max(reached.sum(), 1)), 4),

@@ -2142,6 +2142,12 @@ hipError_t launch_typed(MarkovArgs a, int plan_mode, hipStream_t st) {
     // the untruncated finalize reads at most kFastMaxG records per request
     return launch_plan<T, VEC>(a, 0, kKindFast, st);
   }
+  // a captured one-launch kernel would keep its call's hand-off tag for every
+  // replay and take the previous replay's words for its own: under stream
+  // capture the steps meet at launch boundaries instead
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+  if (cs != hipStreamCaptureStatusNone) return launch_plan<T, VEC>(a, 0, fast ? kKindFast : kKindFused, st);
   // the request-group plan on request (with fewer than three groups a
   // group's hand-off has no other group's streaming to hide behind)
   if (plan_mode == DSPARK_MARKOV_REQUEST_GROUPS && fast && a.B > 2 * kGrp && a.B <= kPipeMaxB) {

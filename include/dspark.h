@@ -257,6 +257,8 @@ int dspark_release(void);
  *     requests are taken in groups of 16 whose steps interleave (a group's
  *     hand-off runs while the other groups stream), with one or two extra
  *     workgroups that only combine the records.  Otherwise as AUTO.
+ * Inside a stream capture every plan runs as PER_STEP: a captured one-launch
+ * grid would keep one call's hand-off tag for all of its replays.
  * All plans compute identical results.  Returns the previous plan, or -1
  * (leaving it unchanged) for an unknown value. */
 enum {
