@@ -98,3 +98,36 @@ def chisq_pvalue(samples, probs, min_expected=5.0):
 
 def binom_pvalue(k, n, p):
     return float(stats.binomtest(int(k), int(n), float(p)).pvalue)
+
+
+# Per-request arrays of the decode input dicts (leading axis B); every other
+# key is shared by all requests.
+_PER_REQUEST = ("backbone", "target", "anchor", "hidden", "mode", "temperature", "top_k", "top_p",
+                "request_id", "position")
+
+
+def request_subset(inp, reqs):
+    """The input dict restricted to the requests reqs (in that order)."""
+    reqs = np.asarray(reqs)
+    out = {k: (v[reqs] if k in _PER_REQUEST else v) for k, v in inp.items()}
+    out["B"] = len(reqs)
+    return out
+
+
+def per_request_threaded(fn, inp, extra=(), nthreads=None, chunk=8):
+    """fn(sub, *extra_sub) over request chunks of inp on a thread pool (the
+    oracle's calls release the GIL); the per-request outputs concatenated.
+    extra holds per-request arrays (leading axis B) sliced alongside."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    B = inp["B"]
+    parts = [list(range(s, min(s + chunk, B))) for s in range(0, B, chunk)]
+    nthreads = nthreads or min(16, os.cpu_count() or 1)
+
+    def run(reqs):
+        return fn(request_subset(inp, reqs), *[np.asarray(x)[reqs] for x in extra])
+
+    with ThreadPoolExecutor(max_workers=nthreads) as ex:
+        outs = list(ex.map(run, parts))
+    return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}
