@@ -141,6 +141,20 @@ def test_verify_wide_greedy_full_size():
     assert np.all((emitted >= 1) & (emitted <= 8))
 
 
+def test_markov_wide_greedy_full_size():
+    """The wide greedy tile (64 requests x gamma 7, V = 129280, rank 256):
+    the Markov draft of every request against the oracle (greedy draws are
+    argmaxes: bit-exact), then the verify of those proposals."""
+    inp = decode_inputs("wide_greedy")
+    got = G.markov(inp)
+    ref = per_request_threaded(O.markov_sample, inp)
+    assert check_markov(inp, got, ref, strict=True) == inp["B"] * inp["gamma"]
+    assert np.all(got["q_tok"] == 1.0) and np.all(got["flags"] == 0)
+    vref = O.verify(inp, ref["draft_tokens"])
+    vgot = G.verify(inp, got["draft_tokens"])
+    assert check_verify(vgot, vref) == 0
+
+
 def test_stats_full_vocab():
     si = stats_inputs(blocks=list(range(16)), mask_every=8)
     ref = O.accept_stats(si)
