@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative", "request-groups"], default="auto",
                     help="Markov launch plan: one launch for all steps when its grid fits "
                          "(auto), the same through cooperative launch, or two launches per step")
+    ap.add_argument("--concurrent-stats", action="store_true",
+                    help="run the accept stats on a second stream, after the Markov call and beside "
+                         "the verify (they read neither's outputs)")
     ap.add_argument("--truncation-arrays", action="store_true",
                     help="pass the top-k / top-p arrays even when no request truncates (the "
                          "library then takes its truncating kernels)")
@@ -538,6 +541,11 @@ def run_decode(args, torch, ds):
                                             for w in range(g + 1)], dtype=torch.float32, device=dev)
         wd_out = ds.dspark_select_width(mk_out[0]["confidence"], cost)
     it = [0]
+    side = torch.cuda.Stream() if args.concurrent_stats else None
+    if side is not None:
+        with torch.cuda.stream(side):  # the side stream's workspace exists before timing
+            ds.dspark_accept_stats(s0["backbone"], s0["tgt_rows"], teacher, conf_logits, out=st_out)
+        torch.cuda.synchronize()
 
     def step():
         i = it[0] % len(sets)
@@ -545,13 +553,22 @@ def run_decode(args, torch, ds):
         x, mo = sets[i], mk_out[i]
         ds.dspark_markov_sample(x["backbone"], anchor, x["w1"], x["w2"], x["hidden"], x["embed"],
                                 conf_w, pol, seed=0, out=mo)
+        if side is not None:
+            # after the Markov grid (which holds every compute unit), beside the verify
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
         nd = None
         if adaptive:
             ds.dspark_select_width(mo["confidence"], cost, out=wd_out)
             nd = wd_out["n_draft"]
         ds.dspark_verify(x["target"], mo["draft_tokens"], pol, mo["q_logits"], mo["q_lse"],
                          mo["q_thr"], mo["q_tok"], n_draft=nd, seed=0, out=vf_out)
-        ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
+        if side is not None:
+            main.wait_stream(side)
+        else:
+            ds.dspark_accept_stats(x["backbone"], x["tgt_rows"], teacher, conf_logits, out=st_out)
 
     ms_total, wall = _timed(step, args, torch)
     ms_per_step = ms_total / args.steps
@@ -586,7 +603,9 @@ def run_decode(args, torch, ds):
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload=desc, B=B, gamma=g, V=V, r=r, d=d, logits="bf16",
                             temperature=1.0 if headline else "per request", truncation=truncation,
-                            mode=modes, rotated_batches=len(sets), markov_plan=args.markov_plan),
+                            mode=modes, rotated_batches=len(sets), markov_plan=args.markov_plan,
+                            schedule="stats on a second stream beside the verify" if side is not None
+                            else "one stream"),
                 roofline=roofline, cpu_baseline=cpu,
                 verified_rows_s=round(B * (g + 1) / (t_verify * 1e-6), 1),
                 step_rows_s=round(B * (g + 1) / ((t_markov + t_verify) * 1e-6), 1),
