@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--markov-plan", choices=["auto", "per-step", "cooperative", "request-groups"], default="auto",
                     help="Markov launch plan: one launch for all steps when its grid fits "
                          "(auto), the same through cooperative launch, or two launches per step")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (profiling runs)")
     ap.add_argument("--concurrent-stats", action="store_true",
                     help="run the accept stats on a second stream, after the Markov call and beside "
                          "the verify (they read neither's outputs)")
@@ -232,7 +234,9 @@ def summarize_profile(base, workload="decode"):
     true_kib = 256 * 1024
     sf, sw = true_kib / cf, true_kib / cw
     cmd = "python3 bench.py" + wl
-    steps = " --steps 50 --warmup 5" if workload in ("decode", "truncated", "wide_greedy") else " --steps 10 --warmup 2"
+    decode_like = workload in ("decode", "truncated", "wide_greedy")
+    steps = " --steps 50 --warmup 5" if decode_like else " --steps 10 --warmup 2"
+    ng = " --no-graph" if decode_like else ""
     lines = [
         f"# {title}",
         "",
@@ -241,12 +245,12 @@ def summarize_profile(base, workload="decode"):
         "wrote this file):",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats -T -f csv -d $OUT/prof_kt -o kt -- {cmd}{steps} --no-cpu",
-        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
-        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu",
+        f"rocprofv3 --kernel-trace --stats -T -f csv -d $OUT/prof_kt -o kt -- {cmd}{steps} --no-cpu{ng}",
+        f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_FETCH_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu{ng}",
+        f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_WRITE_SIZE -o p -- {cmd} --steps 2 --warmup 1 --no-cpu{ng}",
         f"rocprofv3 --pmc FETCH_SIZE -T -f csv -d $OUT/prof_copy_FETCH_SIZE -o p -- {cmd} --copy-calibration 256",
         f"rocprofv3 --pmc WRITE_SIZE -T -f csv -d $OUT/prof_copy_WRITE_SIZE -o p -- {cmd} --copy-calibration 256",
-        *[f"rocprofv3 --pmc {' '.join(ps)} -T -f csv -d $OUT/prof_SQ{i} -o p -- {cmd} --steps 2 --warmup 1 --no-cpu"
+        *[f"rocprofv3 --pmc {' '.join(ps)} -T -f csv -d $OUT/prof_SQ{i} -o p -- {cmd} --steps 2 --warmup 1 --no-cpu{ng}"
           for i, ps in enumerate(SQ_PASSES)],
         "```",
         "",
@@ -582,7 +586,7 @@ def run_decode(args, torch, ds):
     roofline = _roofline(kernels, args.workload)
     step_bytes = sum(k["alg_bytes"] * k["launches_per_step"] for k in kernels.values())
     pct = _step_percentiles(step, args, torch)
-    graph = _graph_step(step, len(sets), args, torch, ds)
+    graph = None if args.no_graph else _graph_step(step, len(sets), args, torch, ds)
     # decode-path rates from the per-kernel event times: verify alone, and
     # Markov + verify (the statistics are the training side of the path)
     t_of = lambda pre: sum(k["avg_us"] * k["launches_per_step"] for n, k in kernels.items()
