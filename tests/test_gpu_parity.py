@@ -23,7 +23,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import dspark_draft_sampling_amd as ds  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import _gpu as G  # noqa: E402
-from tests._cases import decode_case, per_request_threaded, stats_case  # noqa: E402
+from tests._cases import decode_case, per_request_threaded, request_subset, stats_case  # noqa: E402
 from workloads import STATS_CONFIG, bf16_to_f32, decode_inputs, stats_inputs, to_bf16  # noqa: E402
 
 RTOL = 1e-4
@@ -479,6 +479,36 @@ def test_markov_request_groups(B, V, dtype):
         assert np.array_equal(got[k], whole[k]), k
     assert np.array_equal(got["q_logits"][samp], whole["q_logits"][samp])
     assert not np.any(got["flags"] & (1 << 5))  # no wait gave up
+
+
+def test_markov_untruncated_256_full_size(truncated_full):
+    """256 requests at full size (V = 129280, rank 256, the truncated
+    workload's policies with truncation switched off, so no truncation
+    arrays): the whole-step kernel's four 64-request tiles and the
+    request-group kernel's sixteen groups.  Requests in every tile and at
+    the tile and group edges against the oracle, and the two plans bit for
+    bit on every request."""
+    inp = dict(truncated_full)
+    inp["top_k"] = np.zeros_like(inp["top_k"])
+    inp["top_p"] = np.ones_like(inp["top_p"])
+    assert not G.truncates(inp)
+    prev = ds.markov_plan(ds.MARKOV_AUTO)
+    try:
+        whole = G.markov(inp)
+        ds.markov_plan(ds.MARKOV_REQUEST_GROUPS)
+        groups = G.markov(inp)
+    finally:
+        ds.markov_plan(prev)
+    reqs = np.array([0, 5, 15, 16, 63, 64, 100, 127, 128, 150, 191, 192, 224, 255])
+    sub = request_subset(inp, reqs)
+    ref = per_request_threaded(O.markov_sample, sub)
+    got = {k: v[reqs] for k, v in whole.items()}
+    assert check_markov(sub, got, ref) >= len(reqs) * inp["gamma"] - 2
+    samp = inp["mode"] != 0
+    for k in ("draft_tokens", "q_lse", "q_thr", "q_tok", "confidence", "flags"):
+        assert np.array_equal(groups[k], whole[k]), k
+    assert np.array_equal(groups["q_logits"][samp], whole["q_logits"][samp])
+    assert not np.any(whole["flags"] & (1 << 5)) and not np.any(groups["flags"] & (1 << 5))
 
 
 def test_markov_stale_workspace(decode_full):
