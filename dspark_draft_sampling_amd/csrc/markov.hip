@@ -32,7 +32,8 @@
 //    stored (polled, no grid barrier) and hands x_k to the next stream phase
 //    through tagged words in the workspace: every word that crosses
 //    workgroups carries the call's epoch, so nothing is cleared before the
-//    launch.  Everything that crosses workgroups inside the launch (records,
+//    launch (a captured call derives its epoch from the workspace:
+//    dev_epoch_begin).  Everything that crosses workgroups inside the launch (records,
 //    z rows read by the draw, x_k) is stored and loaded at device scope
 //    (sc1), so no L2 writeback or invalidate is needed.  Without truncation
 //    arrays the untruncated kernel (markov_fast) draws a candidate in every
@@ -96,13 +97,14 @@ struct MarkovArgs {
   // one-launch plans: everything that crosses workgroups is a 64-bit word
   // (epoch << 32 | payload), so a reader accepts a word only from this call
   // and never depends on more than 64-bit single-copy atomicity
-  uint32_t epoch;   // this call's tag (never 0)
+  uint32_t epoch;   // this call's tag (never 0); eager calls keep the top bit clear
+  int32_t dev_epoch;  // captured call: the kernels derive the tag from the workspace
   int32_t G;        // workgroups of the one-launch plans (512-token slices)
   int32_t F;        // pipelined plan: finalizing workgroups after the G streaming ones (else 0)
   uint64_t* tpart;  // truncating plan: chunk records [gamma][B][C][4]
   uint64_t* frec;   // untruncated plan: workgroup records [gamma][B][7][G] (word-major)
   uint64_t* xk;     // x_k hand-off [gamma][B][2]
-  uint64_t* sync;   // timeout mark [2]
+  uint64_t* sync;   // timeout mark [2], then the captured calls' epoch word
 };
 
 // Four consecutive logits starting at a multiple of 4, kept packed (bf16:
@@ -187,6 +189,25 @@ __device__ __forceinline__ bool timed_out(const MarkovArgs& a) {
   return tag_is(w0, a.epoch) && tag_is(w1, a.epoch) && payload(w0) == kTimeoutMark &&
          payload(w1) == ~kTimeoutMark;
 }
+// A captured call cannot take its tag from the host (a graph replays its
+// launch arguments), so the one-launch kernels derive it from the
+// workspace's epoch word: the word + 1, with the top bit set (host tags keep
+// it clear, so the two never meet).  Workgroup 0 stores the tag back when it
+// finishes; by then every workgroup has read the word, since workgroup 0's
+// last finalize needs records of every workgroup.  The kernels that follow
+// in the call read the stored tag.
+constexpr uint32_t kDevEpochBit = 0x80000000u;
+__device__ __forceinline__ void dev_epoch_begin(MarkovArgs& a) {
+  if (a.dev_epoch)
+    a.epoch = ((static_cast<uint32_t>(ld_tagged(a.sync + 2)) + 1u) & ~kDevEpochBit) | kDevEpochBit;
+}
+__device__ __forceinline__ void dev_epoch_end(const MarkovArgs& a) {
+  if (a.dev_epoch && blockIdx.x == 0 && threadIdx.x == 0) st_tagged(a.sync + 2, 0u, a.epoch & ~kDevEpochBit);
+}
+__device__ __forceinline__ void dev_epoch_after(MarkovArgs& a) {
+  if (a.dev_epoch) a.epoch = (static_cast<uint32_t>(ld_tagged(a.sync + 2)) & ~kDevEpochBit) | kDevEpochBit;
+}
+
 // True (after marking the timeout) once a wait begun at t0 should give up.
 __device__ __forceinline__ bool give_up(const MarkovArgs& a, uint64_t t0) {
   if (now_ticks() - t0 > kWaitTicks || timed_out(a)) {
@@ -1802,6 +1823,7 @@ __device__ __forceinline__ void pipe_stream(const MarkovArgs& a, const bf16x8 (&
 constexpr int kConfThreads = 256;
 
 __global__ __launch_bounds__(kConfThreads) void markov_confidence_kernel(MarkovArgs a) {
+  dev_epoch_after(a);
   __shared__ float sh[kConfThreads / 64];
   const int row = blockIdx.x;
   const int b = row / a.gamma, k = row - b * a.gamma + 1;
@@ -1889,6 +1911,7 @@ __global__ __launch_bounds__(kFinThreads) void markov_finalize_kernel(MarkovArgs
 // the confidence kernel.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs a) {
+  dev_epoch_begin(a);
   __shared__ StreamLds<kFusedThreads> SL;
   __shared__ FinLds<kFusedThreads> FL;
   const int g = blockIdx.x, G = gridDim.x;
@@ -1901,11 +1924,13 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fused_kernel(MarkovArgs 
       stream_tile<T, VEC, kFusedThreads, kFusedMS, 4, true>(a, af, tok0, b0, k, SL);
     for (int b = g; b < a.B; b += G) finalize_request<kFusedThreads, VEC, true>(a, b, k, FL);
   }
+  dev_epoch_end(a);
 }
 
 // Untruncated one-launch plan (see fast_tile / fast_finalize).
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void markov_fast_kernel(MarkovArgs a) {
+  dev_epoch_begin(a);
   __shared__ FastLds L;
   const int g = blockIdx.x, G = gridDim.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1923,12 +1948,14 @@ __global__ __launch_bounds__(kFusedThreads) void markov_fast_kernel(MarkovArgs a
   // a one-tile batch's last wave-0 z tile (the barrier after the last draw
   // ordered its LDS writes)
   if (threadIdx.x >= 4 * kTile && a.B <= kTile) store_z0<VEC>(a, L, g * kFusedTokens, 0, a.gamma);
+  dev_epoch_end(a);
 }
 
 // Pipelined untruncated one-launch plan (see pipe_pass): G streaming
 // workgroups, then F finalizing ones.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void markov_pipe_kernel(MarkovArgs a) {
+  dev_epoch_begin(a);
   __shared__ PipeLds L;
   const int g = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1978,6 +2005,7 @@ __global__ __launch_bounds__(kFusedThreads) void markov_pipe_kernel(MarkovArgs a
   // last group is partly absent
   if ((g + 1) * kFusedTokens > a.V || a.B % kGrp != 0) pipe_stream<T, VEC, true>(a, af, g, L);
   else pipe_stream<T, VEC, false>(a, af, g, L);
+  dev_epoch_end(a);
 }
 
 // Resident workgroups per compute unit of a one-launch kernel, the device's
@@ -2047,11 +2075,13 @@ struct FusedChain {
 };
 FusedChain g_chain;
 
-// The epoch of a one-launch call: a process-wide counter, never 0.
+// The epoch of an eager one-launch call: a process-wide counter, never 0,
+// top bit clear (captured calls' tags have it set).
 std::atomic<uint32_t> g_epoch{0};
 uint32_t next_epoch() {
-  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  uint32_t e;
+  do e = (g_epoch.fetch_add(1, std::memory_order_relaxed) + 1) & ~kDevEpochBit;
+  while (e == 0);
   return e;
 }
 
@@ -2106,7 +2136,7 @@ hipError_t launch_one(const void* fn, const char* name, const MarkovArgs& a, boo
 template <typename T, bool VEC>
 hipError_t launch_plan(MarkovArgs a, int plan, int kind, hipStream_t st) {
   if (plan) {
-    a.epoch = next_epoch();
+    a.epoch = a.dev_epoch ? 0u : next_epoch();
     const void* fn = kind == kKindPipe   ? one_launch_fn<T, VEC, kKindPipe>()
                      : kind == kKindFast ? one_launch_fn<T, VEC, kKindFast>()
                                          : one_launch_fn<T, VEC, kKindFused>();
@@ -2114,6 +2144,7 @@ hipError_t launch_plan(MarkovArgs a, int plan, int kind, hipStream_t st) {
     if (e != hipSuccess) return e;
   } else {
     a.epoch = 0;
+    a.dev_epoch = 0;
     const dim3 g_step(a.C, (a.B + kTile - 1) / kTile);
     for (int k = 1; k <= a.gamma; ++k) {
       DSPARK_LAUNCH("markov_step", (markov_step_kernel<T, VEC>), g_step, dim3(kStepThreads), 0, st,
@@ -2142,12 +2173,15 @@ hipError_t launch_typed(MarkovArgs a, int plan_mode, hipStream_t st) {
     // the untruncated finalize reads at most kFastMaxG records per request
     return launch_plan<T, VEC>(a, 0, kKindFast, st);
   }
-  // a captured one-launch kernel would keep its call's hand-off tag for every
-  // replay and take the previous replay's words for its own: under stream
-  // capture the steps meet at launch boundaries instead
+  // a graph replays its launch arguments, so a captured one-launch kernel
+  // takes its hand-off tag from the workspace (dev_epoch_begin); the
+  // cross-stream chaining of one-launch grids is not recorded, and the
+  // cooperative plan runs as an ordinary launch
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
-  if (cs != hipStreamCaptureStatusNone) return launch_plan<T, VEC>(a, 0, fast ? kKindFast : kKindFused, st);
+  const bool captured = cs != hipStreamCaptureStatusNone;
+  a.dev_epoch = captured ? 1 : 0;
+  if (captured && plan_mode == DSPARK_MARKOV_COOPERATIVE) plan_mode = DSPARK_MARKOV_AUTO;
   // the request-group plan on request (with fewer than three groups a
   // group's hand-off has no other group's streaming to hide behind)
   if (plan_mode == DSPARK_MARKOV_REQUEST_GROUPS && fast && a.B > 2 * kGrp && a.B <= kPipeMaxB) {

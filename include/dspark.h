@@ -257,8 +257,15 @@ int dspark_release(void);
  *     requests are taken in groups of 16 whose steps interleave (a group's
  *     hand-off runs while the other groups stream), with one or two extra
  *     workgroups that only combine the records.  Otherwise as AUTO.
- * Inside a stream capture every plan runs as PER_STEP: a captured one-launch
- * grid would keep one call's hand-off tag for all of its replays.
+ * Inside a stream capture the plans run as outside it (COOPERATIVE as an
+ * ordinary launch).  A graph replays its launch arguments, so a captured
+ * one-launch kernel takes its hand-off tag from a counter in the workspace
+ * instead of the host (advanced by each replay; tags of captured and of
+ * eager calls never coincide).  The chaining of one-launch launches is not
+ * recorded in the graph: a replay must not run at the same time as another
+ * one-launch Markov call on the same GPU (if it does, the bounded waits end
+ * the call with DSPARK_FLAG_SYNC_TIMEOUT rows), and replays of graphs that
+ * share a workspace must not overlap.
  * All plans compute identical results.  Returns the previous plan, or -1
  * (leaving it unchanged) for an unknown value. */
 enum {

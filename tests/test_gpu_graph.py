@@ -1,11 +1,14 @@
 """The decode step (Markov sample, verify, accept stats) captured in a HIP
 graph and replayed: every replay gives the eager step's outputs bit for bit.
 
-A captured Markov call runs the per-step plan (a one-launch grid would keep
-one call's hand-off tag for all of its replays), so the eager reference runs
-that plan too.  Eager steps with the default plan, on the same stream and
-workspaces, run between the replays, with synchronisations, as a caller's
-own work would.
+A captured Markov call runs its one-launch kernel (whole-step, request-group
+or truncating) with the hand-off tag taken from its workspace, since a graph
+replays its launch arguments; the eager reference runs the same kernel with
+a host tag (the one-launch kernels agree bit for bit; the per-step plan sums
+its records in another order).  Eager steps with the default
+plan, on the same stream and workspaces, run between the replays, with
+synchronisations, as a caller's own work would: their words (host tags) and
+the replays' (workspace tags) meet in one workspace.
 """
 
 from __future__ import annotations
@@ -28,8 +31,9 @@ def _host(d):
     return {k: v.cpu().numpy().copy() for k, v in d.items()}
 
 
-@pytest.mark.parametrize("mode", ["sampled", "mixed"])
-def test_decode_step_graph_replays(mode):
+@pytest.mark.parametrize("mode,plan,arrays", [("sampled", "auto", False), ("mixed", "auto", False),
+                                               ("mixed", "groups", False), ("mixed", "auto", True)])
+def test_decode_step_graph_replays(mode, plan, arrays):
     cfg = dict(seed=404, B=48, gamma=5, V=4096, r=32, d=32, dtype="bf16", draft_std=3.0,
                noise_std=1.0, w_std=0.05, mode=mode)
     inp = decode_inputs(cfg)
@@ -38,7 +42,11 @@ def test_decode_step_graph_replays(mode):
     tgt_rows = target[:, :g].contiguous()
     anchor, w1, w2 = G.i32(inp["anchor"]), G.bf(inp["w1"]), G.bf(inp["w2"])
     hidden, embed, conf_w = G.bf(inp["hidden"]), G.bf(inp["embed"]), G.f32(inp["conf_w"])
-    pol = G.policy(inp)
+    # a second set of draft logits: replays alternate between the two, so a
+    # replay that took the previous replay's hand-off words for its own would
+    # show it
+    srcs = [backbone.clone(), G.logits(decode_inputs(dict(cfg, seed=405))["backbone"], "bf16")]
+    pol = G.policy(inp, arrays)  # arrays: the truncating kernel (no request truncates)
     rng = np.random.default_rng(5)
     teacher = G.i32(rng.integers(0, inp["V"], (inp["B"], g)))
     conf_logits = G.f32(rng.standard_normal((inp["B"], g)))
@@ -52,23 +60,28 @@ def test_decode_step_graph_replays(mode):
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    prev = ds.markov_plan(ds.MARKOV_PER_STEP)
+    prev = ds.markov_plan(ds.MARKOV_REQUEST_GROUPS if plan == "groups" else ds.MARKOV_AUTO)
     try:
-        with torch.cuda.stream(s):
-            ref = [_host(x) for x in step()]  # eager, the plan a capture runs
+        refs = []
+        for src in srcs:  # eager, the same plan (host tag)
+            with torch.cuda.stream(s):
+                backbone.copy_(src)
+                refs.append([_host(x) for x in step()])
+            torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=s):
+            outs = step()
     finally:
         ds.markov_plan(prev)
-    torch.cuda.synchronize()
-    gr = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gr, stream=s):
-        outs = step()
     samp = inp["mode"] != 0
-    for rep in range(3):
+    assert not np.array_equal(refs[0][0]["draft_tokens"], refs[1][0]["draft_tokens"])
+    for rep in range(4):
         with torch.cuda.stream(s):
+            backbone.copy_(srcs[rep % 2])
             gr.replay()
         torch.cuda.synchronize()
         got = [_host(x) for x in outs]
-        for r, o in zip(ref, got):
+        for r, o in zip(refs[rep % 2], got):
             for k in r:
                 if k == "q_logits":
                     assert np.array_equal(r[k][samp], o[k][samp]), (rep, k)
