@@ -192,29 +192,21 @@ __device__ __forceinline__ bool timed_out(const MarkovArgs& a) {
 // A captured call cannot take its tag from the host (a graph replays its
 // launch arguments), so the one-launch kernels derive it from the
 // workspace's epoch word: the word + 1, with the top bit set (host tags keep
-// it clear, so the two never meet).  Every workgroup counts itself on a
-// ticket word tagged with the call's tag once all its threads have read the
-// epoch word (a ticket with another tag, left by an earlier call, counts as
-// 0); the last one stores the tag back.  The kernels that follow in the call
-// read the stored tag.
+// it clear, so the two never meet).  Workgroup 0 stores the tag back at its
+// end, once every workgroup has read the word: in the whole-step and
+// truncating kernels its last finalize needs records of every workgroup; in
+// the request-group kernel it first waits for the last step's x of every
+// request, which needs every streaming and finalizing workgroup.  (A ticket
+// counted by every workgroup would need no such argument, but 250-odd
+// workgroups ending together on one compare-and-swap word cost about 250 us.)
+// The kernels that follow in the call read the stored tag.
 constexpr uint32_t kDevEpochBit = 0x80000000u;
 __device__ __forceinline__ void dev_epoch_begin(MarkovArgs& a) {
   if (a.dev_epoch)
     a.epoch = ((static_cast<uint32_t>(ld_tagged(a.sync + 2)) + 1u) & ~kDevEpochBit) | kDevEpochBit;
 }
-// Every thread of every workgroup, at the end of the kernel.
 __device__ __forceinline__ void dev_epoch_end(const MarkovArgs& a) {
-  if (!a.dev_epoch) return;
-  __syncthreads();  // every thread of the workgroup has read the epoch word
-  if (threadIdx.x != 0) return;
-  uint64_t* t = a.sync + 3;
-  uint64_t w = ld_tagged(t), nw;
-  do {
-    const uint32_t c = tag_is(w, a.epoch) ? payload(w) + 1u : 1u;
-    nw = (static_cast<uint64_t>(a.epoch) << 32) | c;
-  } while (!__hip_atomic_compare_exchange_strong(t, &w, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT));
-  if (payload(nw) == gridDim.x) st_tagged(a.sync + 2, 0u, a.epoch & ~kDevEpochBit);
+  if (a.dev_epoch && blockIdx.x == 0 && threadIdx.x == 0) st_tagged(a.sync + 2, 0u, a.epoch & ~kDevEpochBit);
 }
 __device__ __forceinline__ void dev_epoch_after(MarkovArgs& a) {
   if (a.dev_epoch) a.epoch = (static_cast<uint32_t>(ld_tagged(a.sync + 2)) & ~kDevEpochBit) | kDevEpochBit;
@@ -1983,7 +1975,6 @@ __global__ __launch_bounds__(kFusedThreads) void markov_pipe_kernel(MarkovArgs a
         if (b < a.B) fast_finalize(a, b, k);
       }
     }
-    dev_epoch_end(a);
     return;
   }
   for (int t = threadIdx.x; t < kPipeMaxB; t += kFusedThreads) {
@@ -2018,7 +2009,11 @@ __global__ __launch_bounds__(kFusedThreads) void markov_pipe_kernel(MarkovArgs a
   // last group is partly absent
   if ((g + 1) * kFusedTokens > a.V || a.B % kGrp != 0) pipe_stream<T, VEC, true>(a, af, g, L);
   else pipe_stream<T, VEC, false>(a, af, g, L);
-  dev_epoch_end(a);
+  if (a.dev_epoch && g == 0 && wave == 0) {
+    // the last step's x of every request: every workgroup has run
+    for (int b = lane; b < a.B; b += 64) (void)wait_token(a, a.gamma, b);
+    dev_epoch_end(a);
+  }
 }
 
 // Resident workgroups per compute unit of a one-launch kernel, the device's
