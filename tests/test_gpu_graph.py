@@ -24,11 +24,13 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 import dspark_draft_sampling_amd as ds  # noqa: E402
 from tests import _gpu as G  # noqa: E402
-from workloads import decode_inputs  # noqa: E402
+from workloads import decode_inputs, stats_markov_inputs  # noqa: E402
 
 
 def _host(d):
-    return {k: v.cpu().numpy().copy() for k, v in d.items()}
+    # bf16 tensors as their bit patterns (numpy has no bfloat16)
+    return {k: (v.view(torch.int16) if v.dtype == torch.bfloat16 else v).cpu().numpy().copy()
+            for k, v in d.items()}
 
 
 @pytest.mark.parametrize("mode,plan,arrays", [("sampled", "auto", False), ("mixed", "auto", False),
@@ -91,3 +93,58 @@ def test_decode_step_graph_replays(mode, plan, arrays):
             step()  # the caller's own eager work between replays (default plan)
         torch.cuda.synchronize()
     assert not np.any(got[0]["flags"] & (1 << 5))  # no wait gave up
+
+
+@pytest.mark.parametrize("N", [24, 2100])
+def test_training_calls_graph_replays(N):
+    """The training-side calls captured in one HIP graph: the statistics,
+    their backward, the teacher-forced Markov statistics and the width
+    choice.  Replays alternate between two sets of logits (copied into the
+    captured tensors) and match the eager calls bit for bit.  N = 24 takes
+    the sliced statistics kernels, N = 2100 (above 2048 row pairs at gamma
+    1) the row kernels."""
+    g = 5 if N < 2048 else 1
+    sets = [stats_markov_inputs(dict(seed=60 + i, N=N, gamma=g, V=2048, dtype="bf16", draft_std=2.0,
+                                     noise_std=0.6), r=32, w_std=0.1, mask_every=3) for i in range(2)]
+    inp = sets[0]
+    draft = G.logits(inp["backbone"], "bf16")
+    target = G.logits(inp["target"], "bf16")
+    srcs = [(G.logits(s["backbone"], "bf16"), G.logits(s["target"], "bf16")) for s in sets]
+    teacher, conf = G.i32(inp["teacher"]), G.f32(inp["conf_logits"])
+    anchor, w1, w2 = G.i32(inp["anchor"]), G.bf(inp["w1"]), G.bf(inp["w2"])
+    mask = torch.from_numpy(np.ascontiguousarray(inp["block_mask"], np.uint8)).to(G.DEV)
+    cost = G.f32(np.array([3.0] + [1.0 + 0.2 * k for k in range(g + 1)], np.float32))
+
+    def calls():
+        st = ds.dspark_accept_stats(draft, target, teacher, conf, mask)
+        gr_ = ds.dspark_accept_stats_backward(draft, target, teacher, conf, mask)
+        sm = ds.dspark_accept_stats_markov(draft, target, anchor, w1, w2, teacher, conf, mask)
+        wd = ds.dspark_select_width(torch.sigmoid(conf), cost)
+        return st, gr_, sm, wd
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    refs = []
+    for d_, t_ in srcs:
+        with torch.cuda.stream(s):
+            draft.copy_(d_)
+            target.copy_(t_)
+            refs.append([_host({k: v for k, v in x.items() if v is not None}) for x in calls()])
+        torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        outs = calls()
+    for rep in range(4):
+        d_, t_ = srcs[rep % 2]
+        with torch.cuda.stream(s):
+            draft.copy_(d_)
+            target.copy_(t_)
+            graph.replay()
+        torch.cuda.synchronize()
+        got = [_host({k: v for k, v in x.items() if v is not None}) for x in outs]
+        for r, o in zip(refs[rep % 2], got):
+            for k in r:
+                assert np.array_equal(r[k], o[k], equal_nan=True), (rep, k)
+        with torch.cuda.stream(s):
+            calls()  # eager work between replays
+        torch.cuda.synchronize()
