@@ -148,3 +148,44 @@ def test_training_calls_graph_replays(N):
         with torch.cuda.stream(s):
             calls()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_verify_noalloc_graph_replays():
+    """dspark_verify_noalloc, for callers that cannot allocate, captured in a
+    HIP graph (caller-owned outputs, the library's static scratch): replays
+    alternating between two sets of target logits match dspark_verify run
+    eagerly on each set, bit for bit."""
+    cfg = dict(seed=808, B=48, gamma=5, V=4096, r=32, d=32, dtype="bf16", draft_std=3.0,
+               noise_std=1.0, w_std=0.05, mode="mixed")
+    inp = decode_inputs(cfg)
+    pol = G.policy(inp)
+    mk = ds.dspark_markov_sample(G.logits(inp["backbone"], "bf16"), G.i32(inp["anchor"]), G.bf(inp["w1"]),
+                                 G.bf(inp["w2"]), G.bf(inp["hidden"]), G.bf(inp["embed"]), G.f32(inp["conf_w"]),
+                                 pol, seed=3)
+    q = dict(q_logits=mk["q_logits"], q_lse=mk["q_lse"], q_thr=mk["q_thr"], q_tok=mk["q_tok"])
+    srcs = [G.logits(inp["target"], "bf16"), G.logits(decode_inputs(dict(cfg, seed=809))["target"], "bf16")]
+    target = srcs[0].clone()
+    B, g1 = target.shape[0], target.shape[1]
+    outs = dict(accept_len=torch.zeros((B,), dtype=torch.int32, device=G.DEV),
+                out_tokens=torch.zeros((B, g1), dtype=torch.int32, device=G.DEV),
+                flags=torch.zeros((B, g1), dtype=torch.uint8, device=G.DEV))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    refs = []
+    for src in srcs:
+        with torch.cuda.stream(s):
+            refs.append(_host(ds.dspark_verify(src, mk["draft_tokens"], pol, seed=3, **q)))
+            ds.dspark_verify_noalloc(target, mk["draft_tokens"], pol, outs, seed=3, **q)  # warm
+        torch.cuda.synchronize()
+    assert not np.array_equal(refs[0]["out_tokens"], refs[1]["out_tokens"])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        ds.dspark_verify_noalloc(target, mk["draft_tokens"], pol, outs, seed=3, **q)
+    for rep in range(4):
+        with torch.cuda.stream(s):
+            target.copy_(srcs[rep % 2])
+            graph.replay()
+        torch.cuda.synchronize()
+        got = _host(outs)
+        for k, v in refs[rep % 2].items():
+            assert np.array_equal(got[k], v), (rep, k)
